@@ -1,0 +1,316 @@
+"""fp64 CPU oracle of the SparseGPT layer solver (test infrastructure only).
+
+Every function below is the plain definition, or the algorithm's steps in the
+pages' order, in float64 with numpy/scipy library primitives as steps.  No
+blocking, batching or reordering beyond what the method itself states.
+
+Notation: W is m x n (rows = output channels, columns = input channels, Y = WX);
+calibration inputs are given token-major, X[t, c] (the transpose of the pages'
+n x N matrix, i.e. the same bytes as a framework's activation tensor).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Iterable, Optional
+
+import numpy as np
+import scipy.linalg
+
+
+# ----------------------------------------------------------------------------
+# Sparsity patterns
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Pattern:
+    """A sparsity target.
+
+    kind == "unstructured": prune a fraction ``sparsity`` of the weights
+    ([SGR] section 11 step 5, "prune the specified fraction").
+    kind == "nm": keep ``n_keep`` of every ``m_group`` consecutive input
+    columns of each row ([SFT] section 8.4: 2:4 keeps 2 of every 4, 16:64 keeps
+    16 of every 64; [G24] 2:4 section: the zeros lie along the reduction axis).
+    """
+
+    kind: str
+    sparsity: float = 0.0
+    n_keep: int = 0
+    m_group: int = 0
+
+    def __post_init__(self):
+        if self.kind == "unstructured":
+            if not (0.0 <= self.sparsity <= 1.0):
+                raise ValueError("sparsity must lie in [0, 1]")
+        elif self.kind == "nm":
+            if not (self.m_group >= 1 and 0 <= self.n_keep <= self.m_group):
+                raise ValueError("N:M needs 0 <= N <= M and M >= 1")
+        else:
+            raise ValueError(f"unknown pattern kind {self.kind!r}")
+
+
+def parse_pattern(p) -> Pattern:
+    """``0.5`` -> 50% unstructured; ``"2:4"`` -> keep 2 of every 4."""
+    if isinstance(p, Pattern):
+        return p
+    if isinstance(p, str) and ":" in p:
+        a, b = p.split(":")
+        return Pattern("nm", n_keep=int(a), m_group=int(b))
+    return Pattern("unstructured", sparsity=float(p))
+
+
+def unstructured_k(sparsity: float, rows: int, width: int) -> int:
+    """Number of weights pruned in one column block of ``rows`` x ``width``.
+
+    Reading (pages silent on rounding): floor(p * rows * width) evaluated in
+    IEEE double exactly in this order, ((p * rows) * width).
+    """
+    return int(math.floor(sparsity * float(rows) * float(width)))
+
+
+# ----------------------------------------------------------------------------
+# a1: Hessian proxy
+# ----------------------------------------------------------------------------
+
+def hessian(x_chunks: Iterable[np.ndarray]) -> np.ndarray:
+    """H = X X^T summed over all calibration tokens ([SGR] section 7, and
+    section 10: calibration samples are used to estimate H = X X^T).
+
+    Reading: the raw sum over tokens (no 1/N, no factor 2).  With token-major
+    chunks Xc[t, c] this is sum_chunks Xc^T Xc.
+    """
+    H = None
+    for xc in x_chunks:
+        xd = np.asarray(xc, dtype=np.float64)
+        part = xd.T @ xd
+        H = part if H is None else H + part
+    if H is None:
+        raise ValueError("no calibration chunks")
+    return H
+
+
+# ----------------------------------------------------------------------------
+# a2 + a3: damping and the inverse factor
+# ----------------------------------------------------------------------------
+
+def dampen(H: np.ndarray, damp: float):
+    """H_d = H + lambda I with lambda = damp * mean(diag H).
+
+    The pages do not mention damping.  Reading: a fraction ``damp`` of the mean
+    diagonal added to every diagonal entry; lambda must be finite and > 0.
+    Returns (H_d, lambda).
+    """
+    n = H.shape[0]
+    lam = damp * (float(np.trace(H)) / n)
+    if not math.isfinite(lam) or lam <= 0.0:
+        raise np.linalg.LinAlgError("damping term is not finite and positive")
+    return H + lam * np.eye(n), lam
+
+
+def inverse_upper_factor(Hd: np.ndarray) -> np.ndarray:
+    """U = the upper-triangular Cholesky factor of H_d^{-1} (H_d^{-1} = U^T U).
+
+    The pages only say the error is estimated from the inverse Hessian ([SGR]
+    section 8).  Textbook route, three library steps: Cholesky of H_d, the
+    inverse from it, Cholesky of the inverse, transposed to upper form.
+    Row j of U satisfies U_jj * U[j, j:] = first row of (H_d[j:, j:])^{-1},
+    i.e. it carries the inverse Hessian of the still-unprocessed columns.
+    """
+    n = Hd.shape[0]
+    L = np.linalg.cholesky(Hd)
+    Linv = scipy.linalg.solve_triangular(L, np.eye(n), lower=True)
+    Hinv = Linv.T @ Linv
+    Hinv = 0.5 * (Hinv + Hinv.T)
+    return np.linalg.cholesky(Hinv).T
+
+
+# ----------------------------------------------------------------------------
+# a4 - a7: selection, OBS prune-and-compensate, finalize (unbatched)
+# ----------------------------------------------------------------------------
+
+def _select_block_unstructured(s: np.ndarray, row0_index: np.ndarray, k: int):
+    """Boolean mask of the k smallest keys (s, linear index) of a block."""
+    flat_s = s.ravel()
+    flat_i = row0_index.ravel()
+    order = np.lexsort((flat_i, flat_s))  # primary s, then index
+    sel = np.zeros(flat_s.size, dtype=bool)
+    sel[order[:k]] = True
+    return sel.reshape(s.shape)
+
+
+def prune(W: np.ndarray, U: np.ndarray, pattern, blocksize: int,
+          mask_in: Optional[np.ndarray] = None, return_trace: bool = False):
+    """Column-by-column OBS pruning with immediate (unbatched) compensation.
+
+    [SGR] section 8: pick a weight, estimate the error of removing it from the
+    inverse Hessian, set it to zero and update the other not-yet-pruned weights
+    of the same row to compensate.  [SGR] section 11 steps 4-5 and [VSG] 02:
+    columns are processed block by block in order, the chosen fraction is
+    pruned and the rest updated, the error being passed on to later columns.
+
+    Readings where the pages are silent:
+      * saliency of weight (r, c) when it is chosen: Ŵ[r,c]^2 / U_cc^2, the
+        OBS error of removing it with columns >= c still free;
+      * compensation reaches only columns not yet processed (to the right);
+      * unstructured: at each block start, prune exactly
+        floor(p * m * w) weights of the whole m x w block, the smallest keys
+        (saliency, r*n + c) in lexicographic order (lower index first on ties);
+      * N:M: at each group start (column = 0 mod M), per row, prune the M-N
+        smallest keys (saliency, c) of the group;
+      * ``mask_in`` (m x n, True = prune) replaces selection;
+      * a pruned weight is written as +0.0.
+
+    Returns (W_hat, mask, eps) with eps[r] = sum of e^2 over row r's pruned
+    weights, e = Ŵ[r,j] / U_jj at prune time.  With ``return_trace`` also a
+    dict with the saliency of every weight at its selection point and, per
+    unstructured block, the k-th and (k+1)-th smallest saliency.
+    """
+    pat = parse_pattern(pattern)
+    Wh = np.array(W, dtype=np.float64, copy=True)
+    m, n = Wh.shape
+    U = np.asarray(U, dtype=np.float64)
+    if U.shape != (n, n):
+        raise ValueError("U must be n x n")
+    if blocksize < 1:
+        raise ValueError("blocksize must be >= 1")
+    if pat.kind == "nm" and n % pat.m_group != 0:
+        raise ValueError("N:M needs M to divide n")
+    mask = np.zeros((m, n), dtype=bool)
+    eps = np.zeros(m, dtype=np.float64)
+    d = np.diag(U).copy()
+    sal = np.full((m, n), np.nan)
+    block_thresholds = []
+    lin = np.arange(m, dtype=np.int64)[:, None] * n
+
+    for j in range(n):
+        if mask_in is not None:
+            mask[:, j] = np.asarray(mask_in[:, j], dtype=bool)
+        elif pat.kind == "unstructured" and j % blocksize == 0:
+            w = min(blocksize, n - j)
+            s = Wh[:, j:j + w] ** 2 / d[j:j + w] ** 2
+            sal[:, j:j + w] = s
+            k = unstructured_k(pat.sparsity, m, w)
+            idx = lin + np.arange(j, j + w, dtype=np.int64)[None, :]
+            mask[:, j:j + w] = _select_block_unstructured(s, idx, k)
+            ss = np.sort(s.ravel())
+            kth = ss[k - 1] if k >= 1 else -np.inf
+            nxt = ss[k] if k < ss.size else np.inf
+            block_thresholds.append((j, w, k, kth, nxt))
+        elif pat.kind == "nm" and j % pat.m_group == 0:
+            M = pat.m_group
+            s = Wh[:, j:j + M] ** 2 / d[j:j + M] ** 2
+            sal[:, j:j + M] = s
+            order = np.argsort(s, axis=1, kind="stable")  # ties: lower column
+            grp = np.zeros((m, M), dtype=bool)
+            np.put_along_axis(grp, order[:, :M - pat.n_keep], True, axis=1)
+            mask[:, j:j + M] = grp
+
+        rows = np.nonzero(mask[:, j])[0]
+        if rows.size:
+            e = Wh[rows, j] / U[j, j]
+            Wh[rows, j:] -= np.outer(e, U[j, j:])
+            Wh[rows, j] = 0.0
+            eps[rows] += e * e
+
+    if return_trace:
+        return Wh, mask, eps, {"saliency": sal, "blocks": block_thresholds}
+    return Wh, mask, eps
+
+
+def prune_free_set(W: np.ndarray, Hd: np.ndarray, pattern, blocksize: int,
+                   mask_in: Optional[np.ndarray] = None):
+    """The same procedure without any Cholesky factor (cross-check route).
+
+    Keeps G = (H_d[F, F])^{-1} for the free set F = {j, ..., n-1} and removes
+    column j from it by the elimination downdate G <- G - G[:,0] G[0,:]/G_00
+    after each step.  The OBS quantities are read from G directly: the error of
+    removing w_j is w_j^2 / G_00 and the compensation of the free weights is
+    -(w_j / G_00) * G[0, :] ([SGR] section 8).  Intended for n <= ~1024.
+    """
+    pat = parse_pattern(pattern)
+    Wh = np.array(W, dtype=np.float64, copy=True)
+    m, n = Wh.shape
+    G = np.linalg.inv(np.asarray(Hd, dtype=np.float64))
+    mask = np.zeros((m, n), dtype=bool)
+    eps = np.zeros(m)
+    lin = np.arange(m, dtype=np.int64)[:, None] * n
+    def downdate(Gj):
+        return Gj[1:, 1:] - np.outer(Gj[1:, 0], Gj[0, 1:]) / Gj[0, 0]
+
+    diag_at = np.zeros(n)  # G_00 of the free set that starts at column j
+    Gj = G.copy()
+    for j in range(n):
+        diag_at[j] = Gj[0, 0]
+        if j + 1 < n:
+            Gj = downdate(Gj)
+
+    Gj = G.copy()
+    for j in range(n):
+        if j > 0:
+            Gj = downdate(Gj)
+        if mask_in is not None:
+            mask[:, j] = np.asarray(mask_in[:, j], dtype=bool)
+        elif pat.kind == "unstructured" and j % blocksize == 0:
+            w = min(blocksize, n - j)
+            s = Wh[:, j:j + w] ** 2 / diag_at[j:j + w]
+            k = unstructured_k(pat.sparsity, m, w)
+            idx = lin + np.arange(j, j + w, dtype=np.int64)[None, :]
+            mask[:, j:j + w] = _select_block_unstructured(s, idx, k)
+        elif pat.kind == "nm" and j % pat.m_group == 0:
+            M = pat.m_group
+            s = Wh[:, j:j + M] ** 2 / diag_at[j:j + M]
+            order = np.argsort(s, axis=1, kind="stable")
+            grp = np.zeros((m, M), dtype=bool)
+            np.put_along_axis(grp, order[:, :M - pat.n_keep], True, axis=1)
+            mask[:, j:j + M] = grp
+        rows = np.nonzero(mask[:, j])[0]
+        if rows.size:
+            wq = Wh[rows, j]
+            Wh[rows, j:] -= np.outer(wq / Gj[0, 0], Gj[0, :])
+            Wh[rows, j] = 0.0
+            eps[rows] += wq * wq / Gj[0, 0]
+    return Wh, mask, eps
+
+
+# ----------------------------------------------------------------------------
+# a8: reconstruction error
+# ----------------------------------------------------------------------------
+
+def reconstruction_error(W: np.ndarray, W_hat: np.ndarray,
+                         x_chunks: Iterable[np.ndarray]) -> float:
+    """E = ||W X - Ŵ X||_F^2 summed over all tokens ([SGR] section 6: keep Ŵ X
+    as close as possible to W X).  W is the original (undamped problem)."""
+    D = np.asarray(W, dtype=np.float64) - np.asarray(W_hat, dtype=np.float64)
+    E = 0.0
+    for xc in x_chunks:
+        Y = D @ np.asarray(xc, dtype=np.float64).T
+        E += float(np.sum(Y * Y))
+    return E
+
+
+def reconstruction_error_from_hessian(W, W_hat, H) -> float:
+    """Same quantity through H: sum over rows of d H d^T with d = w - ŵ."""
+    D = np.asarray(W, dtype=np.float64) - np.asarray(W_hat, dtype=np.float64)
+    return float(np.sum((D @ np.asarray(H, dtype=np.float64)) * D))
+
+
+# ----------------------------------------------------------------------------
+# Whole layer
+# ----------------------------------------------------------------------------
+
+def solve_layer(W, x_chunks, pattern, blocksize: int, damp: float = 0.01,
+                mask_in=None):
+    """a1 .. a7 in order ([SGR] section 11 steps 3-5) for one linear layer.
+
+    Returns a dict with H, lambda, U, W_hat, mask, eps and E (the
+    reconstruction error of Ŵ over the same chunks).
+    """
+    chunks = list(x_chunks)
+    H = hessian(chunks)
+    Hd, lam = dampen(H, damp)
+    U = inverse_upper_factor(Hd)
+    Wh, mask, eps = prune(W, U, pattern, blocksize, mask_in=mask_in)
+    E = reconstruction_error(W, Wh, chunks)
+    return {"H": H, "lam": lam, "U": U, "W_hat": Wh, "mask": mask,
+            "eps": eps, "E": E}
