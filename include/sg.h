@@ -1,0 +1,223 @@
+/*
+ * sg.h -- C ABI of the SparseGPT layer solver for AMD Instinct MI355X (gfx950).
+ *
+ * One linear layer Y = W X (W: m x n, rows = output channels, columns = input
+ * channels).  The four calls follow the method's own order:
+ *
+ *   1. sg_hessian_accumulate    H += Xc^T Xc over calibration chunks
+ *   2. sg_prepare_hinv          U = upper Cholesky factor of (H + lambda I)^{-1}
+ *   3. sg_prune_layer           column sweep: select mask, zero, compensate
+ *   4. sg_reconstruction_error  ||W X - W_hat X||_F^2 (validation)
+ *
+ * Sources, cited by page title and section:
+ *   [SGR] "SparseGPT: Massive Language Models Can Be Accurately Pruned in
+ *         One-Shot" -- review on devpress.csdn.net (sections 6, 7, 8, 11, 14.4)
+ *   [SFT] "Sparse Fine-tuning for Inference Acceleration of LLMs" -- review on
+ *         tqpw.cn (section 8.4: N:M groups)
+ *   [G24] "LLM 2:4 structured sparsity production guide" -- oh-bug.com (2:4
+ *         core mechanism: zeros along the reduction axis)
+ * The pages do not give damping, the Cholesky route to the inverse, the
+ * saliency formula or lazy batching; the readings adopted are stated below.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Memory:  every array argument is DEVICE memory owned by the caller, except
+ *          the strings returned by sg_status_string / sg_last_error_message.
+ *          The library never allocates or frees device memory: scratch space
+ *          comes from the caller's `workspace` (size from sg_workspace_bytes,
+ *          alignment 256 bytes).  Matrices are row-major with the stated
+ *          leading dimension (in elements).
+ * Streams: `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *          only enqueues work on it and returns; results are valid once the
+ *          stream is synchronised.  No call synchronises the device.
+ * Errors:  host-detectable problems (null pointers, bad sizes or patterns,
+ *          small workspace, unsupported dtype or alignment, a device that is
+ *          not gfx950) return a non-zero sg_status BEFORE anything is
+ *          enqueued; sg_last_error_message() then holds a thread-local
+ *          explanation.  A failed launch returns SG_ERR_HIP.
+ * Threads: calls are stateless apart from the thread-local message; calls on
+ *          different streams with disjoint buffers may run concurrently.
+ * Dtypes:  SG_F32 = IEEE binary32, SG_BF16 = bfloat16 (upper 16 bits of a
+ *          binary32), both read and widened exactly to fp32.
+ */
+#ifndef SG_H_
+#define SG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SG_ABI_VERSION 1
+
+typedef int32_t sg_status;
+
+enum {
+  SG_OK = 0,
+  SG_ERR_INVALID_ARGUMENT = 1,
+  SG_ERR_UNSUPPORTED = 2,
+  SG_ERR_WORKSPACE = 3,
+  SG_ERR_HIP = 4
+};
+
+/* element types */
+enum { SG_F32 = 0, SG_BF16 = 1 };
+
+/* sparsity pattern kinds */
+enum { SG_UNSTRUCTURED = 0, SG_NM = 1 };
+
+/* operations, for sg_workspace_bytes */
+enum {
+  SG_OP_HESSIAN = 0,
+  SG_OP_PREPARE_HINV = 1,
+  SG_OP_PRUNE = 2,
+  SG_OP_RECON = 3
+};
+
+/* Largest supported column block of sg_prune_layer. */
+#define SG_MAX_BLOCKSIZE 128
+
+/*
+ * sg_hessian_accumulate -- H += Xc^T Xc.
+ *
+ * [SGR] section 7 (the Hessian proxy H = X X^T of the layer inputs) and
+ * section 10 (calibration samples serve to estimate H).  Reading: a raw sum
+ * over tokens, no 1/N normalisation; call once per chunk of tokens.
+ *
+ *   H      [n x n] fp32, leading dimension n, in/out.  Must hold a symmetric
+ *          matrix on entry (zero it once before the first chunk); on return
+ *          it is again fully symmetric (both triangles written).
+ *   n      number of input channels, 1 <= n <= 65536.
+ *   X      token-major chunk Xc[t, c] (t < T, c < n) with leading dimension
+ *          ldx >= n; x_dtype SG_BF16 or SG_F32.  For SG_BF16 the pointer must
+ *          be 16-byte aligned and ldx a multiple of 8.
+ *   T      tokens in the chunk, T >= 1.
+ *   workspace / ws_bytes: scratch for the token-split partial tiles; the size
+ *          from sg_workspace_bytes(SG_OP_HESSIAN, 0, n, T, 0) gives the
+ *          intended split.  A smaller workspace (even 0 bytes) is accepted: the
+ *          call then splits the tokens less (results stay deterministic for a
+ *          given workspace size).
+ * Accumulation is fp32 (bf16 x bf16 products are exact in fp32).  The result
+ * is bitwise reproducible for the same inputs and workspace size.
+ */
+sg_status sg_hessian_accumulate(float* H, int64_t n, const void* X,
+                                int32_t x_dtype, int64_t T, int64_t ldx,
+                                void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sg_prepare_hinv -- Hinv = U, the upper-triangular Cholesky factor of
+ * (H + lambda I)^{-1}, lambda = damp * mean(diag H).
+ *
+ * [SGR] section 8: the error of removing a weight and the compensation of the
+ * others come from the inverse Hessian.  The pages name no damping and no
+ * factor; reading: dampen by a fraction of the mean diagonal, then
+ * U^T U = (H + lambda I)^{-1} with U upper triangular, positive diagonal.
+ * Row j of U then holds the inverse Hessian of the columns j..n-1 that are
+ * still free when column j is processed (U_jj U[j, j:] = first row of
+ * ((H + lambda I)[j:, j:])^{-1}).
+ * Computed in fp32 as L = chol(J H_d J), U = J L^{-1} J (J reverses indices),
+ * with a blocked factorisation whose trailing updates run on MFMA.
+ *
+ *   Hinv   [n x n] fp32 out, leading dimension n: upper triangle = U, strictly
+ *          lower triangle = 0.
+ *   H      [n x n] fp32 in (symmetric, e.g. from sg_hessian_accumulate); not
+ *          modified.  Hinv must not alias H.
+ *   damp   fraction of mean(diag H) added to the diagonal, finite, >= 0.
+ *   info   one device int32, written by the call: 0 = success; j+1 = the
+ *          factorisation broke down (non-positive or non-finite pivot) at
+ *          original column j; n+1 = mean(diag H) is not finite and positive
+ *          (e.g. H is zero).  When info != 0 the contents of Hinv are
+ *          unspecified.
+ *   workspace: sg_workspace_bytes(SG_OP_PREPARE_HINV, 0, n, 0, 0) bytes
+ *          (two n_pad x n_pad fp32 matrices, n_pad = n rounded up to 128).
+ */
+sg_status sg_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp,
+                          int32_t* info, void* workspace, size_t ws_bytes,
+                          void* stream);
+
+/*
+ * sg_prune_layer -- sparse W_hat with W_hat X ~ W X.
+ *
+ * [SGR] section 8 (OBS: choose a weight, estimate its error from the inverse
+ * Hessian, set it to zero, update the other not-yet-pruned weights of the same
+ * row) and section 11 steps 4-5 (columns processed in blocks; prune the given
+ * fraction and update the rest); [SFT] section 8.4 and [G24] (N:M keeps N of
+ * every M consecutive input columns).  Readings where the pages are silent:
+ *   - saliency of weight (r, c) at its selection point: W_hat[r,c]^2 / U_cc^2;
+ *   - compensation reaches only columns to the right of the pruned one;
+ *   - SG_UNSTRUCTURED: at the start of each column block of width w (the last
+ *     block may be narrower) exactly floor(sparsity * m * w) weights of the
+ *     whole m x w block are pruned: the smallest keys (saliency, r*n + c),
+ *     lower index first on equal saliency;
+ *   - SG_NM: at each group start (column = 0 mod m_group), per row, the
+ *     m_group - n_keep smallest keys (saliency, c) of the group are pruned;
+ *   - the compensation of each block reaches the columns after it through one
+ *     batched product W[:, i2:] -= Err * U[i1:i2, i2:] (lazy batching, the
+ *     same values as the unbatched procedure up to rounding);
+ *   - a pruned weight is stored as +0.0.
+ *
+ *   W_out    [m x n] fp32 out, contiguous (leading dimension n).  May alias W
+ *            only if w_dtype == SG_F32 and ldw == n.
+ *   mask_out [m x n] uint8 out, contiguous: 1 = pruned (W_out is then +0.0),
+ *            0 = kept.  May be NULL.
+ *   W        [m x ldw] in, SG_F32 or SG_BF16, not modified (unless aliased).
+ *   Hinv     [n x n] fp32 in: the factor from sg_prepare_hinv for this n.
+ *   pattern_kind SG_UNSTRUCTURED (uses sparsity in [0, 1]) or SG_NM (uses
+ *            n_keep, m_group with 0 <= n_keep <= m_group, m_group dividing
+ *            both n and blocksize).
+ *   blocksize 1 <= blocksize <= SG_MAX_BLOCKSIZE.
+ *   mask_in  optional [m x n] uint8 (contiguous, 1 = prune): when not NULL it
+ *            replaces the selection (the pattern is still validated).
+ *   workspace: sg_workspace_bytes(SG_OP_PRUNE, m, n, 0, blocksize) bytes.
+ * Limits: m * n < 2^32 (linear indices are 32-bit tie-break keys).
+ */
+sg_status sg_prune_layer(float* W_out, uint8_t* mask_out, const void* W,
+                         int32_t w_dtype, int64_t m, int64_t n, int64_t ldw,
+                         const float* Hinv, int32_t pattern_kind,
+                         double sparsity, int32_t n_keep, int32_t m_group,
+                         int32_t blocksize, const uint8_t* mask_in,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sg_reconstruction_error -- *err = (accumulate ? *err : 0)
+ *                                   + ||(W - W_hat) Xc^T||_F^2.
+ *
+ * [SGR] section 6: the layer objective keeps W_hat X as close as possible to
+ * W X.  Call per calibration chunk with accumulate = 1 after the first.
+ *
+ *   err      one device double, in/out.
+ *   W        [m x ldw] original weights (SG_F32 or SG_BF16).
+ *   W_hat    [m x n] fp32 contiguous (e.g. W_out of sg_prune_layer).
+ *   X        token-major chunk [T x ldx] (SG_F32 or SG_BF16, ldx >= n).
+ *   workspace: sg_workspace_bytes(SG_OP_RECON, m, n, T, 0) bytes.
+ * Products run in fp32 on MFMA; the final sum is fp64 in a fixed order.
+ */
+sg_status sg_reconstruction_error(double* err, int32_t accumulate,
+                                  const void* W, int32_t w_dtype, int64_t ldw,
+                                  const float* W_hat, int64_t m, int64_t n,
+                                  const void* X, int32_t x_dtype, int64_t T,
+                                  int64_t ldx, void* workspace,
+                                  size_t ws_bytes, void* stream);
+
+/* Workspace bytes for an operation (m, n, T, blocksize as in its call; pass 0
+ * for arguments the operation does not take).  Pure host arithmetic: touches
+ * no device.  Returns 0 for invalid arguments. */
+size_t sg_workspace_bytes(int32_t op, int64_t m, int64_t n, int64_t T,
+                          int32_t blocksize);
+
+/* Static description of a status code. */
+const char* sg_status_string(sg_status s);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* sg_last_error_message(void);
+
+/* SG_ABI_VERSION of the loaded library. */
+int32_t sg_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SG_H_ */

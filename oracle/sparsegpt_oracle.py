@@ -97,14 +97,18 @@ def hessian(x_chunks: Iterable[np.ndarray]) -> np.ndarray:
 def dampen(H: np.ndarray, damp: float):
     """H_d = H + lambda I with lambda = damp * mean(diag H).
 
-    The pages do not mention damping.  Reading: a fraction ``damp`` of the mean
-    diagonal added to every diagonal entry; lambda must be finite and > 0.
+    The pages do not mention damping.  Reading: a fraction ``damp`` >= 0 of the
+    mean diagonal added to every diagonal entry.  The mean diagonal must be
+    finite and positive (an all-zero or non-finite H is an error).
     Returns (H_d, lambda).
     """
     n = H.shape[0]
-    lam = damp * (float(np.trace(H)) / n)
-    if not math.isfinite(lam) or lam <= 0.0:
-        raise np.linalg.LinAlgError("damping term is not finite and positive")
+    if not (damp >= 0.0 and math.isfinite(damp)):
+        raise ValueError("damp must be finite and >= 0")
+    mean = float(np.trace(H)) / n
+    if not math.isfinite(mean) or mean <= 0.0:
+        raise np.linalg.LinAlgError("mean(diag H) is not finite and positive")
+    lam = damp * mean
     return H + lam * np.eye(n), lam
 
 
@@ -163,7 +167,8 @@ def prune(W: np.ndarray, U: np.ndarray, pattern, blocksize: int,
 
     Returns (W_hat, mask, eps) with eps[r] = sum of e^2 over row r's pruned
     weights, e = Ŵ[r,j] / U_jj at prune time.  With ``return_trace`` also a
-    dict with the saliency of every weight at its selection point and, per
+    dict with the saliency of every weight at its selection point (computed
+    along the actual trajectory also when ``mask_in`` forces the mask) and, per
     unstructured block, the k-th and (k+1)-th smallest saliency.
     """
     pat = parse_pattern(pattern)
@@ -184,27 +189,29 @@ def prune(W: np.ndarray, U: np.ndarray, pattern, blocksize: int,
     lin = np.arange(m, dtype=np.int64)[:, None] * n
 
     for j in range(n):
-        if mask_in is not None:
-            mask[:, j] = np.asarray(mask_in[:, j], dtype=bool)
-        elif pat.kind == "unstructured" and j % blocksize == 0:
+        if pat.kind == "unstructured" and j % blocksize == 0:
             w = min(blocksize, n - j)
             s = Wh[:, j:j + w] ** 2 / d[j:j + w] ** 2
             sal[:, j:j + w] = s
-            k = unstructured_k(pat.sparsity, m, w)
-            idx = lin + np.arange(j, j + w, dtype=np.int64)[None, :]
-            mask[:, j:j + w] = _select_block_unstructured(s, idx, k)
-            ss = np.sort(s.ravel())
-            kth = ss[k - 1] if k >= 1 else -np.inf
-            nxt = ss[k] if k < ss.size else np.inf
-            block_thresholds.append((j, w, k, kth, nxt))
+            if mask_in is None:
+                k = unstructured_k(pat.sparsity, m, w)
+                idx = lin + np.arange(j, j + w, dtype=np.int64)[None, :]
+                mask[:, j:j + w] = _select_block_unstructured(s, idx, k)
+                ss = np.sort(s.ravel())
+                kth = ss[k - 1] if k >= 1 else -np.inf
+                nxt = ss[k] if k < ss.size else np.inf
+                block_thresholds.append((j, w, k, kth, nxt))
         elif pat.kind == "nm" and j % pat.m_group == 0:
             M = pat.m_group
             s = Wh[:, j:j + M] ** 2 / d[j:j + M] ** 2
             sal[:, j:j + M] = s
-            order = np.argsort(s, axis=1, kind="stable")  # ties: lower column
-            grp = np.zeros((m, M), dtype=bool)
-            np.put_along_axis(grp, order[:, :M - pat.n_keep], True, axis=1)
-            mask[:, j:j + M] = grp
+            if mask_in is None:
+                order = np.argsort(s, axis=1, kind="stable")  # ties: lower column
+                grp = np.zeros((m, M), dtype=bool)
+                np.put_along_axis(grp, order[:, :M - pat.n_keep], True, axis=1)
+                mask[:, j:j + M] = grp
+        if mask_in is not None:
+            mask[:, j] = np.asarray(mask_in[:, j], dtype=bool)
 
         rows = np.nonzero(mask[:, j])[0]
         if rows.size:

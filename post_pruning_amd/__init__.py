@@ -1,0 +1,245 @@
+"""SparseGPT layer solver for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over the C ABI of ``libsg.so`` (declared in include/sg.h).
+The functions carry the same names as the C entry points; they only marshal
+torch tensors (device memory and the current HIP stream) into the calls.  All
+arithmetic runs in the library's HIP kernels: there is no fallback, and every
+call raises if the library is missing or the device is not gfx950.
+
+Pipeline for one linear layer (W: m x n, calibration X token-major [N, n]):
+
+    H = torch.zeros(n, n, device="cuda")
+    for Xc in chunks: sg_hessian_accumulate(H, Xc)
+    Hinv, info = sg_prepare_hinv(H, damp=0.01)
+    W_hat, mask = sg_prune_layer(W, Hinv, 0.5 or "2:4", blocksize=128)
+    err = sg_reconstruction_error(W, W_hat, Xc)      # optional validation
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple, Union
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsg.so")
+
+SG_OK, SG_ERR_INVALID_ARGUMENT, SG_ERR_UNSUPPORTED, SG_ERR_WORKSPACE, SG_ERR_HIP = range(5)
+SG_F32, SG_BF16 = 0, 1
+SG_UNSTRUCTURED, SG_NM = 0, 1
+SG_OP_HESSIAN, SG_OP_PREPARE_HINV, SG_OP_PRUNE, SG_OP_RECON = range(4)
+SG_MAX_BLOCKSIZE = 128
+
+_lib = None
+
+
+class SGError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: {message} (status {status})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsg.so (built by __graft_entry__.build()); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    c_i32, c_i64, c_sz, c_vp, c_dbl = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                        ctypes.c_void_p, ctypes.c_double)
+    lib.sg_hessian_accumulate.argtypes = [c_vp, c_i64, c_vp, c_i32, c_i64, c_i64, c_vp, c_sz, c_vp]
+    lib.sg_prepare_hinv.argtypes = [c_vp, c_vp, c_i64, c_dbl, c_vp, c_vp, c_sz, c_vp]
+    lib.sg_prune_layer.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_i32,
+                                   c_dbl, c_i32, c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]
+    lib.sg_reconstruction_error.argtypes = [c_vp, c_i32, c_vp, c_i32, c_i64, c_vp, c_i64, c_i64,
+                                            c_vp, c_i32, c_i64, c_i64, c_vp, c_sz, c_vp]
+    for f in ("sg_hessian_accumulate", "sg_prepare_hinv", "sg_prune_layer",
+              "sg_reconstruction_error"):
+        getattr(lib, f).restype = c_i32
+    lib.sg_workspace_bytes.argtypes = [c_i32, c_i64, c_i64, c_i64, c_i32]
+    lib.sg_workspace_bytes.restype = c_sz
+    lib.sg_status_string.argtypes = [c_i32]
+    lib.sg_status_string.restype = ctypes.c_char_p
+    lib.sg_last_error_message.argtypes = []
+    lib.sg_last_error_message.restype = ctypes.c_char_p
+    lib.sg_abi_version.argtypes = []
+    lib.sg_abi_version.restype = c_i32
+    _lib = lib
+    return lib
+
+
+def sg_abi_version() -> int:
+    return int(load_library().sg_abi_version())
+
+
+def sg_status_string(s: int) -> str:
+    return load_library().sg_status_string(int(s)).decode()
+
+
+def sg_last_error_message() -> str:
+    return load_library().sg_last_error_message().decode()
+
+
+def sg_workspace_bytes(op: int, m: int = 0, n: int = 0, T: int = 0, blocksize: int = 0) -> int:
+    return int(load_library().sg_workspace_bytes(op, m, n, T, blocksize))
+
+
+def _check(status: int, where: str):
+    if status != SG_OK:
+        raise SGError(status, where, sg_last_error_message() or sg_status_string(status))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SG_F32
+    if t.dtype == torch.bfloat16:
+        return SG_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def _row_major(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D row-major tensor (unit column stride)")
+    return t.stride(0)
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace of {nbytes} bytes needed")
+        return workspace, workspace.numel() * workspace.element_size()
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    return ws, nbytes
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def sg_hessian_accumulate(H: torch.Tensor, X: torch.Tensor,
+                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """H += X^T X for a token-major chunk X [T, n] (bf16 or fp32); H is [n, n] fp32."""
+    lib = load_library()
+    _require_cuda(H, X)
+    if H.dtype != torch.float32 or not H.is_contiguous() or H.dim() != 2 or H.shape[0] != H.shape[1]:
+        raise ValueError("H must be a contiguous square float32 tensor")
+    n = H.shape[0]
+    if X.dim() != 2 or X.shape[1] != n:
+        raise ValueError("X must be [T, n]")
+    ldx = _row_major(X, "X")
+    T = X.shape[0]
+    need = sg_workspace_bytes(SG_OP_HESSIAN, 0, n, T, 0)
+    ws, nb = _workspace(need, H.device, workspace)
+    _check(lib.sg_hessian_accumulate(_ptr(H), n, _ptr(X), _dtype_code(X), T, ldx, _ptr(ws), nb,
+                                     ctypes.c_void_p(_stream(H.device))), "sg_hessian_accumulate")
+    return H
+
+
+def sg_prepare_hinv(H: torch.Tensor, damp: float = 0.01, Hinv: Optional[torch.Tensor] = None,
+                    info: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Upper Cholesky factor of (H + damp*mean(diag H) I)^{-1}; returns (Hinv, info)."""
+    lib = load_library()
+    _require_cuda(H)
+    n = H.shape[0]
+    if H.dtype != torch.float32 or not H.is_contiguous() or H.shape != (n, n):
+        raise ValueError("H must be a contiguous square float32 tensor")
+    if Hinv is None:
+        Hinv = torch.empty_like(H)
+    if info is None:
+        info = torch.empty(1, dtype=torch.int32, device=H.device)
+    need = sg_workspace_bytes(SG_OP_PREPARE_HINV, 0, n, 0, 0)
+    ws, nb = _workspace(need, H.device, workspace)
+    _check(lib.sg_prepare_hinv(_ptr(Hinv), _ptr(H), n, float(damp), _ptr(info), _ptr(ws), nb,
+                               ctypes.c_void_p(_stream(H.device))), "sg_prepare_hinv")
+    return Hinv, info
+
+
+def parse_pattern(pattern: Union[float, str]):
+    """0.5 -> (SG_UNSTRUCTURED, 0.5, 0, 1); "2:4" -> (SG_NM, 0.0, 2, 4)."""
+    if isinstance(pattern, str) and ":" in pattern:
+        a, b = pattern.split(":")
+        return SG_NM, 0.0, int(a), int(b)
+    return SG_UNSTRUCTURED, float(pattern), 0, 1
+
+
+def sg_prune_layer(W: torch.Tensor, Hinv: torch.Tensor, pattern: Union[float, str],
+                   blocksize: int = 128, mask_in: Optional[torch.Tensor] = None,
+                   W_out: Optional[torch.Tensor] = None, mask_out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None):
+    """Prune W ([m, n] bf16/fp32) with the factor Hinv; returns (W_hat fp32, mask uint8)."""
+    lib = load_library()
+    _require_cuda(W, Hinv, mask_in)
+    m, n = W.shape
+    ldw = _row_major(W, "W")
+    if Hinv.shape != (n, n) or Hinv.dtype != torch.float32 or not Hinv.is_contiguous():
+        raise ValueError("Hinv must be a contiguous [n, n] float32 tensor")
+    if mask_in is not None:
+        if mask_in.shape != (m, n) or not mask_in.is_contiguous():
+            raise ValueError("mask_in must be a contiguous [m, n] tensor")
+        mask_in = mask_in.to(torch.uint8)
+    if W_out is None:
+        W_out = torch.empty(m, n, dtype=torch.float32, device=W.device)
+    if mask_out is None:
+        mask_out = torch.empty(m, n, dtype=torch.uint8, device=W.device)
+    kind, sp, nk, mg = parse_pattern(pattern)
+    need = sg_workspace_bytes(SG_OP_PRUNE, m, n, 0, blocksize)
+    ws, nb = _workspace(need, W.device, workspace)
+    _check(lib.sg_prune_layer(_ptr(W_out), _ptr(mask_out), _ptr(W), _dtype_code(W), m, n, ldw,
+                              _ptr(Hinv), kind, sp, nk, mg, int(blocksize), _ptr(mask_in), _ptr(ws),
+                              nb, ctypes.c_void_p(_stream(W.device))), "sg_prune_layer")
+    return W_out, mask_out
+
+
+def sg_reconstruction_error(W: torch.Tensor, W_hat: torch.Tensor, X: torch.Tensor,
+                            err: Optional[torch.Tensor] = None, accumulate: bool = False,
+                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """||(W - W_hat) X^T||_F^2 over a token-major chunk X; returns a device float64 scalar."""
+    lib = load_library()
+    _require_cuda(W, W_hat, X)
+    m, n = W.shape
+    ldw = _row_major(W, "W")
+    ldx = _row_major(X, "X")
+    if W_hat.shape != (m, n) or W_hat.dtype != torch.float32 or not W_hat.is_contiguous():
+        raise ValueError("W_hat must be a contiguous [m, n] float32 tensor")
+    if X.shape[1] != n:
+        raise ValueError("X must be [T, n]")
+    if err is None:
+        err = torch.zeros(1, dtype=torch.float64, device=W.device)
+    T = X.shape[0]
+    need = sg_workspace_bytes(SG_OP_RECON, m, n, T, 0)
+    ws, nb = _workspace(need, W.device, workspace)
+    _check(lib.sg_reconstruction_error(_ptr(err), int(bool(accumulate)), _ptr(W), _dtype_code(W),
+                                       ldw, _ptr(W_hat), m, n, _ptr(X), _dtype_code(X), T, ldx,
+                                       _ptr(ws), nb, ctypes.c_void_p(_stream(W.device))),
+           "sg_reconstruction_error")
+    return err
+
+
+def solve_layer(W: torch.Tensor, x_chunks, pattern, blocksize: int = 128, damp: float = 0.01):
+    """a1..a7 for one layer: Hessian over all chunks, factor, prune."""
+    n = W.shape[1]
+    H = torch.zeros(n, n, dtype=torch.float32, device=W.device)
+    for Xc in x_chunks:
+        sg_hessian_accumulate(H, Xc)
+    Hinv, info = sg_prepare_hinv(H, damp)
+    W_hat, mask = sg_prune_layer(W, Hinv, pattern, blocksize)
+    return {"H": H, "Hinv": Hinv, "info": info, "W_hat": W_hat, "mask": mask}

@@ -1,0 +1,219 @@
+// C ABI entry points: argument validation, workspace carving, gfx950 check.
+// Every host-detectable problem is reported before anything is enqueued.
+#include "sg_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+namespace sg {
+
+static thread_local std::string g_last_error;
+
+sg_status set_error(sg_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+sg_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return set_error(SG_ERR_HIP, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+  return SG_OK;
+}
+
+namespace {
+
+constexpr int kMaxDev = 64;
+std::mutex g_dev_mu;
+int g_dev_ok[kMaxDev];  // 0 unknown, 1 gfx950, -1 other
+
+sg_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return set_error(SG_ERR_HIP, "no current HIP device");
+  if (dev >= kMaxDev) return set_error(SG_ERR_UNSUPPORTED, "device index %d too large", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return set_error(SG_ERR_HIP, "hipGetDeviceProperties failed");
+    g_dev_ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  if (g_dev_ok[dev] != 1)
+    return set_error(SG_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X/MI350X)", dev);
+  return SG_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+}  // namespace sg
+
+using namespace sg;
+
+extern "C" {
+
+int32_t sg_abi_version(void) { return SG_ABI_VERSION; }
+
+const char* sg_status_string(sg_status s) {
+  switch (s) {
+    case SG_OK: return "SG_OK";
+    case SG_ERR_INVALID_ARGUMENT: return "SG_ERR_INVALID_ARGUMENT";
+    case SG_ERR_UNSUPPORTED: return "SG_ERR_UNSUPPORTED";
+    case SG_ERR_WORKSPACE: return "SG_ERR_WORKSPACE";
+    case SG_ERR_HIP: return "SG_ERR_HIP";
+    default: return "SG_ERR_UNKNOWN";
+  }
+}
+
+const char* sg_last_error_message(void) { return g_last_error.c_str(); }
+
+size_t sg_workspace_bytes(int32_t op, int64_t m, int64_t n, int64_t T, int32_t blocksize) {
+  switch (op) {
+    case SG_OP_HESSIAN:
+      if (n < 1 || T < 1) return 0;
+      return hessian_plan(n, T, 0, false).ws_bytes;
+    case SG_OP_PREPARE_HINV:
+      if (n < 1) return 0;
+      return factor_ws_bytes(n);
+    case SG_OP_PRUNE:
+      if (m < 1 || n < 1 || blocksize < 1 || blocksize > SG_MAX_BLOCKSIZE) return 0;
+      return prune_ws_bytes(m, n, blocksize);
+    case SG_OP_RECON:
+      if (m < 1 || n < 1 || T < 1) return 0;
+      return recon_ws_bytes(m, T);
+    default:
+      return 0;
+  }
+}
+
+sg_status sg_hessian_accumulate(float* H, int64_t n, const void* X, int32_t x_dtype, int64_t T,
+                                int64_t ldx, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!H || !X) return set_error(SG_ERR_INVALID_ARGUMENT, "H and X must not be NULL");
+  if (n < 1 || n > 65536) return set_error(SG_ERR_INVALID_ARGUMENT, "n=%lld out of [1, 65536]", (long long)n);
+  if (T < 1) return set_error(SG_ERR_INVALID_ARGUMENT, "T=%lld must be >= 1", (long long)T);
+  if (ldx < n) return set_error(SG_ERR_INVALID_ARGUMENT, "ldx=%lld < n=%lld", (long long)ldx, (long long)n);
+  if (x_dtype != SG_BF16 && x_dtype != SG_F32)
+    return set_error(SG_ERR_UNSUPPORTED, "x_dtype %d not supported", x_dtype);
+  if (x_dtype == SG_BF16 && (!aligned(X, 16) || (ldx % 8) != 0))
+    return set_error(SG_ERR_UNSUPPORTED, "bf16 X must be 16-byte aligned with ldx %% 8 == 0");
+  if (ws_bytes > 0 && !workspace)
+    return set_error(SG_ERR_INVALID_ARGUMENT, "workspace is NULL but ws_bytes > 0");
+  if (workspace && !aligned(workspace, 256))
+    return set_error(SG_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (sg_status e = check_device()) return e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (x_dtype == SG_BF16) {
+    const HessPlan plan = hessian_plan(n, T, workspace ? ws_bytes : 0, true);
+    return launch_hessian_bf16(H, n, static_cast<const uint16_t*>(X), T, ldx, plan, workspace, st);
+  }
+  return launch_hessian_f32(H, n, static_cast<const float*>(X), T, ldx, st);
+}
+
+sg_status sg_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp, int32_t* info,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!Hinv || !H || !info) return set_error(SG_ERR_INVALID_ARGUMENT, "Hinv, H and info must not be NULL");
+  if (n < 1 || n > 65536) return set_error(SG_ERR_INVALID_ARGUMENT, "n=%lld out of [1, 65536]", (long long)n);
+  if (!(damp >= 0.0) || !isfinite(damp))
+    return set_error(SG_ERR_INVALID_ARGUMENT, "damp must be finite and >= 0");
+  if (static_cast<const void*>(Hinv) == static_cast<const void*>(H))
+    return set_error(SG_ERR_INVALID_ARGUMENT, "Hinv must not alias H");
+  const size_t need = factor_ws_bytes(n);
+  if (!workspace || ws_bytes < need)
+    return set_error(SG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (!aligned(workspace, 256))
+    return set_error(SG_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (sg_status e = check_device()) return e;
+  return launch_prepare_hinv(Hinv, H, n, damp, info, workspace, static_cast<hipStream_t>(stream));
+}
+
+sg_status sg_prune_layer(float* W_out, uint8_t* mask_out, const void* W, int32_t w_dtype, int64_t m,
+                         int64_t n, int64_t ldw, const float* Hinv, int32_t pattern_kind,
+                         double sparsity, int32_t n_keep, int32_t m_group, int32_t blocksize,
+                         const uint8_t* mask_in, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!W_out || !W || !Hinv) return set_error(SG_ERR_INVALID_ARGUMENT, "W_out, W and Hinv must not be NULL");
+  if (m < 1 || n < 1) return set_error(SG_ERR_INVALID_ARGUMENT, "m and n must be >= 1");
+  if ((unsigned long long)m * (unsigned long long)n >= (1ull << 32))
+    return set_error(SG_ERR_UNSUPPORTED, "m*n must be < 2^32");
+  if (ldw < n) return set_error(SG_ERR_INVALID_ARGUMENT, "ldw=%lld < n=%lld", (long long)ldw, (long long)n);
+  if (w_dtype != SG_F32 && w_dtype != SG_BF16)
+    return set_error(SG_ERR_UNSUPPORTED, "w_dtype %d not supported", w_dtype);
+  if (static_cast<const void*>(W_out) == W && !(w_dtype == SG_F32 && ldw == n))
+    return set_error(SG_ERR_INVALID_ARGUMENT, "W_out may alias W only for fp32 W with ldw == n");
+  if (blocksize < 1 || blocksize > SG_MAX_BLOCKSIZE)
+    return set_error(SG_ERR_UNSUPPORTED, "blocksize %d out of [1, %d]", blocksize, SG_MAX_BLOCKSIZE);
+  if (pattern_kind == SG_UNSTRUCTURED) {
+    if (!(sparsity >= 0.0 && sparsity <= 1.0))
+      return set_error(SG_ERR_INVALID_ARGUMENT, "sparsity must lie in [0, 1]");
+  } else if (pattern_kind == SG_NM) {
+    if (m_group < 1 || n_keep < 0 || n_keep > m_group)
+      return set_error(SG_ERR_INVALID_ARGUMENT, "N:M needs 0 <= N <= M, M >= 1");
+    if (n % m_group != 0)
+      return set_error(SG_ERR_INVALID_ARGUMENT, "M=%d must divide n=%lld", m_group, (long long)n);
+    if (blocksize % m_group != 0)
+      return set_error(SG_ERR_INVALID_ARGUMENT, "M=%d must divide blocksize=%d", m_group, blocksize);
+    if (!((m_group <= 16 && 16 % m_group == 0) || m_group % 16 == 0))
+      return set_error(SG_ERR_UNSUPPORTED, "M=%d: groups must divide 16 or be a multiple of 16", m_group);
+  } else {
+    return set_error(SG_ERR_INVALID_ARGUMENT, "unknown pattern kind %d", pattern_kind);
+  }
+  const size_t need = prune_ws_bytes(m, n, blocksize);
+  if (!workspace || ws_bytes < need)
+    return set_error(SG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (!aligned(workspace, 256))
+    return set_error(SG_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (sg_status e = check_device()) return e;
+  PruneArgs a;
+  a.W_out = W_out;
+  a.mask_out = mask_out;
+  a.W = W;
+  a.w_dtype = w_dtype;
+  a.m = m;
+  a.n = n;
+  a.ldw = ldw;
+  a.U = Hinv;
+  a.kind = pattern_kind;
+  a.sparsity = sparsity;
+  a.n_keep = pattern_kind == SG_NM ? n_keep : 0;
+  a.m_group = pattern_kind == SG_NM ? m_group : 1;
+  a.blocksize = blocksize;
+  a.mask_in = mask_in;
+  return launch_prune(a, workspace, static_cast<hipStream_t>(stream));
+}
+
+sg_status sg_reconstruction_error(double* err, int32_t accumulate, const void* W, int32_t w_dtype,
+                                  int64_t ldw, const float* W_hat, int64_t m, int64_t n,
+                                  const void* X, int32_t x_dtype, int64_t T, int64_t ldx,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!err || !W || !W_hat || !X)
+    return set_error(SG_ERR_INVALID_ARGUMENT, "err, W, W_hat and X must not be NULL");
+  if (m < 1 || n < 1 || T < 1) return set_error(SG_ERR_INVALID_ARGUMENT, "m, n, T must be >= 1");
+  if (ldw < n || ldx < n) return set_error(SG_ERR_INVALID_ARGUMENT, "ldw and ldx must be >= n");
+  if ((w_dtype != SG_F32 && w_dtype != SG_BF16) || (x_dtype != SG_F32 && x_dtype != SG_BF16))
+    return set_error(SG_ERR_UNSUPPORTED, "dtype not supported");
+  if (ceil_div(m, kRecTile) > 65535) return set_error(SG_ERR_UNSUPPORTED, "m too large");
+  const size_t need = recon_ws_bytes(m, T);
+  if (!workspace || ws_bytes < need)
+    return set_error(SG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (!aligned(workspace, 256))
+    return set_error(SG_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (sg_status e = check_device()) return e;
+  return launch_recon(err, accumulate, W, w_dtype, ldw, W_hat, m, n, X, x_dtype, T, ldx, workspace,
+                      static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// Reconstruction error ||(W - W_hat) Xc^T||_F^2 of one calibration chunk.
+//
+// "SparseGPT ... Pruned in One-Shot" review (devpress), section 6: the layer
+// objective is to keep W_hat X as close as possible to W X.  With token-major
+// Xc[t, c], Y[r][t] = sum_c (W - W_hat)[r][c] Xc[t][c] is an NT contraction
+// over the input channels; it runs on fp32 MFMA in 128x128 (rows x tokens)
+// tiles, each tile squares and sums its outputs, and a single workgroup adds
+// the per-tile partials in tile order in fp64 (reproducible).
+#include "gemm_f32.h"
+
+namespace sg {
+namespace {
+
+__device__ inline float load_elem(const void* p, int dtype, int64_t idx) {
+  if (dtype == SG_BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[idx]);
+  return static_cast<const float*>(p)[idx];
+}
+
+__global__ __launch_bounds__(256) void recon_tile_kernel(const void* __restrict__ W, int wdt,
+                                                         int64_t ldw, const float* __restrict__ Wh,
+                                                         int64_t m, int64_t n,
+                                                         const void* __restrict__ X, int xdt,
+                                                         int64_t T, int64_t ldx,
+                                                         double* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) float Pl[GT * GS];
+  __shared__ __attribute__((aligned(16))) float Ql[GT * GS];
+  __shared__ double red[4];
+  const int64_t t0 = (int64_t)blockIdx.x * GT;
+  const int64_t r0 = (int64_t)blockIdx.y * GT;
+  const int rows = (int)min<int64_t>(GT, m - r0);
+  const int toks = (int)min<int64_t>(GT, T - t0);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kk = threadIdx.x & 31, rsub = threadIdx.x >> 5;
+  TileAcc acc;
+  tile_zero(acc);
+  for (int64_t kc = 0; kc < n; kc += GBK) {
+    const int64_t k = kc + kk;
+#pragma unroll 4
+    for (int rr = 0; rr < GT / 8; ++rr) {
+      const int r = rsub + rr * 8;
+      float dv = 0.f, xv = 0.f;
+      if (k < n) {
+        if (r < rows)
+          dv = load_elem(W, wdt, (r0 + r) * ldw + k) - Wh[(r0 + r) * n + k];
+        if (r < toks) xv = load_elem(X, xdt, (t0 + r) * ldx + k);
+      }
+      Pl[r * GS + kk] = dv;
+      Ql[r * GS + kk] = xv;
+    }
+    __syncthreads();
+    tile_mma_chunk(acc, Pl, Ql, wave, lane);
+    __syncthreads();
+  }
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float y = acc.v[i][jj][v];
+        s += (double)y * (double)y;
+      }
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_down(s, off, 64);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    partial[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+__global__ __launch_bounds__(256) void recon_reduce_kernel(const double* __restrict__ partial,
+                                                           int64_t cnt, double* err, int accumulate) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < cnt; i += 256) s += partial[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *err = (accumulate ? *err : 0.0) + red[0];
+}
+
+}  // namespace
+
+size_t recon_ws_bytes(int64_t m, int64_t T) {
+  return round_up((size_t)ceil_div(m, GT) * ceil_div(T, GT) * sizeof(double), 256);
+}
+
+sg_status launch_recon(double* err, int accumulate, const void* W, int w_dtype, int64_t ldw,
+                       const float* W_hat, int64_t m, int64_t n, const void* X, int x_dtype,
+                       int64_t T, int64_t ldx, void* ws, hipStream_t st) {
+  double* partial = static_cast<double*>(ws);
+  dim3 grid((unsigned)ceil_div(T, GT), (unsigned)ceil_div(m, GT));
+  hipLaunchKernelGGL(recon_tile_kernel, grid, dim3(256), 0, st, W, w_dtype, ldw, W_hat, m, n, X,
+                     x_dtype, T, ldx, partial);
+  if (sg_status e = check_launch("recon tiles")) return e;
+  hipLaunchKernelGGL(recon_reduce_kernel, dim3(1), dim3(256), 0, st, partial,
+                     (int64_t)grid.x * grid.y, err, accumulate);
+  return check_launch("recon reduce");
+}
+
+}  // namespace sg

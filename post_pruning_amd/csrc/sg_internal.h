@@ -1,0 +1,87 @@
+// Internal declarations of the gfx950 SparseGPT layer solver library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sg.h"
+
+namespace sg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kNumCU = 256;       // MI355X compute units (launch sizing only)
+constexpr int kHessTile = 256;    // Hessian output tile edge
+constexpr int kFactorNB = 128;    // factorisation panel width
+constexpr int kGemmTile = 128;    // fp32 MFMA update tile edge
+constexpr int kSelBins = 2048;    // radix-select histogram bins
+constexpr int kRecTile = 128;     // reconstruction-error output tile edge
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+__device__ inline float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Host-side error reporting (thread-local message).
+// ---------------------------------------------------------------------------
+sg_status set_error(sg_status s, const char* fmt, ...);
+sg_status check_launch(const char* what);
+
+// ---------------------------------------------------------------------------
+// Hessian
+// ---------------------------------------------------------------------------
+struct HessPlan {
+  int64_t tiles;       // lower-triangle 256x256 tiles
+  int splits;          // token splits
+  int64_t tok_per_split;
+  size_t ws_bytes;     // partials + counters
+};
+HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws);
+sg_status launch_hessian_bf16(float* H, int64_t n, const uint16_t* X, int64_t T,
+                              int64_t ldx, const HessPlan& plan, void* ws,
+                              hipStream_t st);
+sg_status launch_hessian_f32(float* H, int64_t n, const float* X, int64_t T,
+                             int64_t ldx, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Factorisation
+// ---------------------------------------------------------------------------
+size_t factor_ws_bytes(int64_t n);
+sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp,
+                              int32_t* info, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Prune
+// ---------------------------------------------------------------------------
+struct PruneArgs {
+  float* W_out;
+  uint8_t* mask_out;
+  const void* W;
+  int w_dtype;
+  int64_t m, n, ldw;
+  const float* U;
+  int kind;
+  double sparsity;
+  int n_keep, m_group;
+  int blocksize;
+  const uint8_t* mask_in;
+};
+size_t prune_ws_bytes(int64_t m, int64_t n, int blocksize);
+sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Reconstruction error
+// ---------------------------------------------------------------------------
+size_t recon_ws_bytes(int64_t m, int64_t T);
+sg_status launch_recon(double* err, int accumulate, const void* W, int w_dtype,
+                       int64_t ldw, const float* W_hat, int64_t m, int64_t n,
+                       const void* X, int x_dtype, int64_t T, int64_t ldx,
+                       void* ws, hipStream_t st);
+
+}  // namespace sg

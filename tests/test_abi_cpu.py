@@ -1,0 +1,163 @@
+"""C ABI contract checks that need no GPU.
+
+The library must load without a device, export every function declared in
+include/sg.h, and reject bad arguments before touching HIP.  No compute call is
+made here: every call below fails validation first.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sg.h")
+LIB = os.path.join(ROOT, "post_pruning_amd", "libsg.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libsg.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sg_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def sg():
+    import post_pruning_amd as sg
+    sg.load_library()
+    return sg
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for f in ("sg_hessian_accumulate", "sg_prepare_hinv", "sg_prune_layer",
+              "sg_reconstruction_error"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(sg):
+    assert sg.sg_abi_version() == 1
+    assert sg.sg_status_string(0) == "SG_OK"
+    assert sg.sg_status_string(3) == "SG_ERR_WORKSPACE"
+    assert sg.sg_status_string(99) == "SG_ERR_UNKNOWN"
+
+
+def test_workspace_sizes_pure_host(sg):
+    # Factorisation: two padded n_pad^2 fp32 matrices (+ a small tail).
+    assert sg.sg_workspace_bytes(sg.SG_OP_PREPARE_HINV, 0, 4096) >= 2 * 4096 * 4096 * 4
+    assert sg.sg_workspace_bytes(sg.SG_OP_PREPARE_HINV, 0, 1000) >= 2 * 1024 * 1024 * 4
+    # Prune: select state + an m x 128 fp32 error block.
+    assert sg.sg_workspace_bytes(sg.SG_OP_PRUNE, 4096, 4096, 0, 128) >= 4096 * 128 * 4
+    # Hessian: the small-n, many-token case splits the tokens.
+    assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 4096, 262144, 0) > 0
+    # ... and the large-n case needs no split.
+    assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 28672, 32768, 0) == 0
+    assert sg.sg_workspace_bytes(sg.SG_OP_RECON, 64, 128, 512, 0) >= 8
+    # invalid arguments give 0
+    assert sg.sg_workspace_bytes(sg.SG_OP_PRUNE, 10, 10, 0, 0) == 0
+    assert sg.sg_workspace_bytes(sg.SG_OP_PRUNE, 10, 10, 0, 129) == 0
+    assert sg.sg_workspace_bytes(77, 1, 1, 1, 1) == 0
+
+
+def _lib(sg):
+    return sg.load_library()
+
+
+def test_null_pointers_rejected_before_device(sg):
+    lib = _lib(sg)
+    st = lib.sg_hessian_accumulate(None, 16, None, sg.SG_BF16, 8, 16, None, 0, None)
+    assert st == sg.SG_ERR_INVALID_ARGUMENT
+    assert "NULL" in sg.sg_last_error_message()
+    st = lib.sg_prepare_hinv(None, None, 16, 0.01, None, None, 0, None)
+    assert st == sg.SG_ERR_INVALID_ARGUMENT
+    st = lib.sg_prune_layer(None, None, None, 0, 4, 4, 4, None, 0, 0.5, 0, 1, 4, None, None, 0, None)
+    assert st == sg.SG_ERR_INVALID_ARGUMENT
+    st = lib.sg_reconstruction_error(None, 0, None, 0, 4, None, 4, 4, None, 0, 4, 4, None, 0, None)
+    assert st == sg.SG_ERR_INVALID_ARGUMENT
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation first
+
+
+@pytest.mark.parametrize("args,code", [
+    # n out of range, T < 1, ldx < n, unknown dtype, misaligned bf16 pointer
+    (dict(n=0), 1), (dict(T=0), 1), (dict(ldx=8), 1), (dict(dt=7), 2),
+    (dict(X=ctypes.c_void_p(0x1002)), 2), (dict(ldx=20), 2),
+])
+def test_hessian_validation(sg, args, code):
+    a = dict(H=FAKE, n=16, X=FAKE, dt=sg.SG_BF16, T=8, ldx=16)
+    a.update(args)
+    st = _lib(sg).sg_hessian_accumulate(a["H"], a["n"], a["X"], a["dt"], a["T"], a["ldx"], None, 0,
+                                        None)
+    assert st == code, sg.sg_last_error_message()
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(damp=-0.1), 1), (dict(damp=float("nan")), 1), (dict(alias=True), 1),
+    (dict(ws=0), 3),
+])
+def test_prepare_validation(sg, args, code):
+    a = dict(damp=0.01, alias=False, ws=10 ** 9)
+    a.update(args)
+    Hinv = FAKE if a["alias"] else ctypes.c_void_p(0x2000)
+    st = _lib(sg).sg_prepare_hinv(Hinv, FAKE, 64, a["damp"], FAKE, ctypes.c_void_p(0x10000),
+                                  a["ws"], None)
+    assert st == code, sg.sg_last_error_message()
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(kind=0, sp=1.5), 1),            # sparsity out of [0, 1]
+    (dict(kind=1, nk=3, mg=2), 1),        # N > M
+    (dict(kind=1, nk=2, mg=3, n=96, bs=96), 2),  # M neither divides nor is a multiple of 16
+    (dict(kind=1, nk=2, mg=4, n=130), 1),  # M does not divide n
+    (dict(kind=1, nk=2, mg=8, bs=12), 1),  # M does not divide blocksize
+    (dict(bs=0), 2), (dict(bs=129), 2),   # blocksize range
+    (dict(kind=5), 1),                    # unknown kind
+    (dict(ldw=10), 1),                    # ldw < n
+    (dict(m=70000, n=70000), 2),          # m*n >= 2^32
+    (dict(ws=0), 3),                      # workspace too small
+    (dict(alias=True, dt=1), 1),          # aliasing a bf16 W
+])
+def test_prune_validation(sg, args, code):
+    a = dict(kind=0, sp=0.5, nk=0, mg=1, bs=128, m=64, n=128, ldw=None, ws=10 ** 9, alias=False,
+             dt=0)
+    a.update(args)
+    ldw = a["ldw"] if a["ldw"] is not None else a["n"]
+    Wout = FAKE if a["alias"] else ctypes.c_void_p(0x3000)
+    st = _lib(sg).sg_prune_layer(Wout, None, FAKE, a["dt"], a["m"], a["n"], ldw, FAKE, a["kind"],
+                                 a["sp"], a["nk"], a["mg"], a["bs"], None, ctypes.c_void_p(0x10000),
+                                 a["ws"], None)
+    assert st == code, sg.sg_last_error_message()
+
+
+def test_recon_validation(sg):
+    lib = _lib(sg)
+    st = lib.sg_reconstruction_error(FAKE, 0, FAKE, 0, 4, FAKE, 4, 8, FAKE, 0, 4, 8, None, 0, None)
+    assert st == sg.SG_ERR_INVALID_ARGUMENT  # ldw < n
+    st = lib.sg_reconstruction_error(FAKE, 0, FAKE, 0, 8, FAKE, 4, 8, FAKE, 0, 4, 8, None, 0, None)
+    assert st == sg.SG_ERR_WORKSPACE
+
+
+def test_product_path_imports_no_oracle():
+    # The library binding must not import, call or read the oracle.
+    src_dir = os.path.join(ROOT, "post_pruning_amd")
+    for dirpath, _, files in os.walk(src_dir):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
+
+
+def test_pattern_parsing(sg):
+    assert sg.parse_pattern(0.5) == (sg.SG_UNSTRUCTURED, 0.5, 0, 1)
+    assert sg.parse_pattern("2:4") == (sg.SG_NM, 0.0, 2, 4)
+    assert sg.parse_pattern("16:64") == (sg.SG_NM, 0.0, 16, 64)
