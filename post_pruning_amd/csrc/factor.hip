@@ -37,8 +37,6 @@ namespace sg {
 namespace {
 
 constexpr int NB = kFactorNB;  // 128
-constexpr int LKS = 129;       // row stride of the scalar L_kk tile
-constexpr int LIS = 132;       // row stride of L_kk^{-1} (16-byte aligned rows)
 
 // ---- damping --------------------------------------------------------------
 __global__ __launch_bounds__(256) void damp_lambda_kernel(const float* __restrict__ H, int64_t n,
@@ -94,13 +92,29 @@ __global__ __launch_bounds__(256) void flip_init_kernel(const float* __restrict_
 }
 
 // ---- panel ---------------------------------------------------------------
+// The diagonal block A_kk (128 x 128) is factored and inverted inside one
+// workgroup with a blocked algorithm of 16-column sub-panels:
+//   * wave 0 factors sub-panel p (rows 16p..127, 16 columns) in registers, the
+//     pivot row's entries broadcast with readlane (no LDS round trip);
+//   * all waves apply its rank-16 update to the trailing lower triangle with
+//     v_mfma_f32_16x16x4_f32 directly out of LDS;
+//   * the 16x16 diagonal blocks of L_kk^{-1} are formed by forward
+//     substitution (one lane per column), the off-diagonal blocks by block
+//     forward substitution X[P][Q] = -D_P sum_{R=Q}^{P-1} L[P][R] X[R][Q] on
+//     MFMA (the D-layout of the sum is directly the B operand of the product
+//     with D_P).
+constexpr int PS = 132;  // LDS row stride (floats): 16-byte rows, conflict-free b128 reads
+
 struct PanelLds {
-  float Lk[NB * LKS];
-  float Li[NB * LIS];
-  float Ld[NB];
+  float As[NB * PS];
+  float Li[NB * PS];
   float Pst[GT * GS];
   int fail;
 };
+
+__device__ __forceinline__ float rdlane(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 
 __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float* __restrict__ Y,
                                                     int64_t n_pad, int k, int64_t n,
@@ -108,63 +122,128 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   PanelLds& S = *reinterpret_cast<PanelLds*>(smem);
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int b = blockIdx.x;
   const int64_t k0 = (int64_t)k * NB;
 
-  // 1. load A_kk (lower part is all that is used)
+  // 0. load the lower part of A_kk, clear L_kk^{-1}
   for (int e = tid; e < NB * NB; e += 256) {
     const int i = e >> 7, c = e & 127;
-    S.Lk[i * LKS + c] = (c <= i) ? A[(k0 + i) * n_pad + k0 + c] : 0.f;
+    S.As[i * PS + c] = (c <= i) ? A[(k0 + i) * n_pad + k0 + c] : 0.f;
+    S.Li[i * PS + c] = 0.f;
   }
   if (tid == 0) S.fail = -1;
   __syncthreads();
 
-  // 2. unblocked right-looking Cholesky of A_kk in LDS
-  const int tx = tid & 63, ty = tid >> 6;
-  for (int j = 0; j < NB; ++j) {
-    const float d2 = S.Lk[j * LKS + j];
-    const float d = sqrtf(d2);
-    const float r = 1.f / d;
-    if (tid == 0) {
-      S.Ld[j] = d;
-      if (S.fail < 0 && !(d2 > 0.f && isfinite(d2))) S.fail = j;
+  // 1. blocked Cholesky, 16-column sub-panels
+  for (int p = 0; p < 8; ++p) {
+    const int c0 = p * 16;
+    if (wave == 0) {
+      const int r0 = c0 + lane, r1 = c0 + 64 + lane;
+      float a0[16], a1[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        a0[c] = (r0 < NB) ? S.As[r0 * PS + c0 + c] : 0.f;
+        a1[c] = (r1 < NB) ? S.As[r1 * PS + c0 + c] : 0.f;
+      }
+      int fail = -1;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float d2 = rdlane(a0[j], j);
+        if (fail < 0 && !(d2 > 0.f && isfinite(d2))) fail = j;
+        const float d = sqrtf(d2);
+        const float rd = 1.f / d;
+        a0[j] = (lane > j) ? a0[j] * rd : (lane == j ? d : a0[j]);
+        a1[j] *= rd;
+#pragma unroll
+        for (int c = j + 1; c < 16; ++c) {
+          const float lcj = rdlane(a0[j], c);
+          a0[c] = fmaf(-a0[j], lcj, a0[c]);
+          a1[c] = fmaf(-a1[j], lcj, a1[c]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        if (r0 < NB) S.As[r0 * PS + c0 + c] = (c <= lane) ? a0[c] : 0.f;
+        if (r1 < NB) S.As[r1 * PS + c0 + c] = a1[c];
+      }
+      if (lane == 0 && fail >= 0 && S.fail < 0) S.fail = c0 + fail;
     }
-    if (tid > j && tid < NB) S.Lk[tid * LKS + j] *= r;
     __syncthreads();
-    for (int i = j + 1 + ty; i < NB; i += 4) {
-      const float lij = S.Lk[i * LKS + j];
-      for (int c = j + 1 + tx; c <= i; c += 64) S.Lk[i * LKS + c] -= lij * S.Lk[c * LKS + j];
+    // rank-16 update of the trailing lower triangle, 16x16 tiles (I >= C > p)
+    const int t = 7 - p;
+    const int ntiles = t * (t + 1) / 2;
+    for (int idx = wave; idx < ntiles; idx += 4) {
+      int ii = 0;
+      while ((ii + 1) * (ii + 2) / 2 <= idx) ++ii;
+      const int cc = idx - ii * (ii + 1) / 2;
+      const int I = p + 1 + ii, C = p + 1 + cc;
+      floatx4 acc;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] = S.As[(I * 16 + (lane >> 4) * 4 + v) * PS + C * 16 + (lane & 15)];
+      const floatx4 fa = *reinterpret_cast<const floatx4*>(&S.As[(I * 16 + (lane & 15)) * PS + c0 + (lane >> 4) * 4]);
+      const floatx4 fb = *reinterpret_cast<const floatx4*>(&S.As[(C * 16 + (lane & 15)) * PS + c0 + (lane >> 4) * 4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-fa[e], fb[e], acc, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) S.As[(I * 16 + (lane >> 4) * 4 + v) * PS + C * 16 + (lane & 15)] = acc[v];
     }
     __syncthreads();
   }
   if (b == 0 && tid == 0 && S.fail >= 0) {
-    const int64_t p = k0 + S.fail;  // column in the flipped order
-    if (p < n) atomicCAS(info, 0, (int32_t)(n - p));
+    const int64_t pcol = k0 + S.fail;  // column in the flipped order
+    if (pcol < n) atomicCAS(info, 0, (int32_t)(n - pcol));
   }
 
-  // 3. Li = L_kk^{-1} by right-looking forward substitution of L X = I.
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e >> 7, c = e & 127;
-    S.Li[i * LIS + c] = (i == c) ? 1.f : 0.f;
+  // 2a. inverses of the 16x16 diagonal blocks: lane -> (block, column)
+  if (lane < 32) {
+    const int P = wave * 2 + (lane >> 4);
+    const int c = lane & 15;
+    const int b0 = P * 16;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int q = 0; q < i; ++q) acc = fmaf(S.As[(b0 + i) * PS + b0 + q], x[q], acc);
+      const float lii = S.As[(b0 + i) * PS + b0 + i];
+      x[i] = (i < c) ? 0.f : ((i == c) ? 1.f / lii : -acc / lii);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S.Li[(b0 + i) * PS + b0 + c] = x[i];
   }
   __syncthreads();
-  for (int i = 0; i < NB; ++i) {
-    const float rd = 1.f / S.Ld[i];
-    if (tid <= i) S.Li[i * LIS + tid] *= rd;
-    __syncthreads();
-    for (int rr = i + 1 + ty; rr < NB; rr += 4) {
-      const float lri = S.Lk[rr * LKS + i];
-      for (int c = tx; c <= i; c += 64) S.Li[rr * LIS + c] -= lri * S.Li[i * LIS + c];
+  // 2b. block forward substitution for the off-diagonal blocks
+  for (int P = 1; P < 8; ++P) {
+    for (int Q = wave; Q < P; Q += 4) {
+      floatx4 T = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int R = Q; R < P; ++R) {
+        const floatx4 fa =
+            *reinterpret_cast<const floatx4*>(&S.As[(P * 16 + (lane & 15)) * PS + R * 16 + (lane >> 4) * 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float bv = S.Li[(R * 16 + (lane >> 4) * 4 + e) * PS + Q * 16 + (lane & 15)];
+          T = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[e], bv, T, 0, 0, 0);
+        }
+      }
+      // X[P][Q] = -D_P T; T in D-layout is the B operand (k = 4*(lane/16) + e)
+      const floatx4 fd =
+          *reinterpret_cast<const floatx4*>(&S.Li[(P * 16 + (lane & 15)) * PS + P * 16 + (lane >> 4) * 4]);
+      floatx4 Xq = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Xq = __builtin_amdgcn_mfma_f32_16x16x4f32(-fd[e], T[e], Xq, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) S.Li[(P * 16 + (lane >> 4) * 4 + v) * PS + Q * 16 + (lane & 15)] = Xq[v];
     }
     __syncthreads();
   }
 
-  // 4. apply
+  // 3. apply
   if (b == k) {
     // Y[k,k] = L_kk^{-T}
     for (int e = tid; e < NB * NB; e += 256) {
       const int i = e >> 7, c = e & 127;
-      Y[(k0 + i) * n_pad + k0 + c] = S.Li[c * LIS + i];
+      Y[(k0 + i) * n_pad + k0 + c] = S.Li[c * PS + i];
     }
     return;
   }
@@ -173,25 +252,24 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
     blk = A + (int64_t)b * NB * n_pad + k0;  // L[l,k] = A[l,k] L_kk^{-T}
   else
     blk = Y + (int64_t)b * NB * n_pad + k0;  // Y[c,k] = R[c,k] L_kk^{-T}
-  const int wave = tid >> 6, lane = tid & 63;
   TileAcc acc;
   tile_zero(acc);
   for (int kc = 0; kc < NB; kc += GBK) {
     stage_rows_f32(S.Pst, blk, n_pad, NB, kc, NB);
     __syncthreads();
-    // Q rows = rows of Li (k contiguous), taken straight from the inverse tile
+    // Q rows = rows of L_kk^{-1} (k contiguous), read straight from LDS
     const int prow = (wave >> 1) * 64 + (lane & 15);
     const int qrow = (wave & 1) * 64 + (lane & 15);
 #pragma unroll
     for (int g = 0; g < GBK / 16; ++g) {
       const int kl = g * 16 + (lane >> 4) * 4;
-      floatx4 p[4], q[4];
+      floatx4 pp[4], qq[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        p[i] = *reinterpret_cast<const floatx4*>(S.Pst + (prow + i * 16) * GS + kl);
+        pp[i] = *reinterpret_cast<const floatx4*>(S.Pst + (prow + i * 16) * GS + kl);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        q[jj] = *reinterpret_cast<const floatx4*>(S.Li + (qrow + jj * 16) * LIS + kc + kl);
+        qq[jj] = *reinterpret_cast<const floatx4*>(S.Li + (qrow + jj * 16) * PS + kc + kl);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -199,7 +277,7 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
             acc.v[i][jj] =
-                __builtin_amdgcn_mfma_f32_16x16x4f32(p[i][e], q[jj][e], acc.v[i][jj], 0, 0, 0);
+                __builtin_amdgcn_mfma_f32_16x16x4f32(pp[i][e], qq[jj][e], acc.v[i][jj], 0, 0, 0);
     }
     __syncthreads();
   }
