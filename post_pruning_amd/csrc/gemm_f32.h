@@ -62,35 +62,48 @@ __device__ inline void tile_mma_chunk(TileAcc& acc, const float* Pl, const float
   }
 }
 
-// Stage rows of a k-contiguous fp32 matrix: lds[r][kk] = src[r*ld + k0 + kk]
-// for r < rows, k0 + kk < kend (zero elsewhere).  Optional negation.
+// Stage rows of a k-contiguous fp32 matrix: lds[r][kk] = scale * src[r*ld + k0 + kk]
+// for r < rows, k0 + kk < kend (zero elsewhere; rows >= 1 and kend > k0).
+// All loads are issued first from clamped in-bounds addresses, then the
+// out-of-range values are zeroed as they are written, so the loads overlap.
 __device__ inline void stage_rows_f32(float* lds, const float* __restrict__ src, int64_t ld,
                                       int rows, int64_t k0, int64_t kend, float scale = 1.f) {
   const int kk = threadIdx.x & 31;
   const int r0 = threadIdx.x >> 5;
   const int64_t k = k0 + kk;
-#pragma unroll 4
+  const int64_t kc = k < kend ? k : kend - 1;
+  float v[GT / 8];
+#pragma unroll
   for (int rr = 0; rr < GT / 8; ++rr) {
     const int r = r0 + rr * 8;
-    float v = 0.f;
-    if (r < rows && k < kend) v = src[(int64_t)r * ld + k] * scale;
-    lds[r * GS + kk] = v;
+    const int rc = r < rows ? r : rows - 1;
+    v[rr] = src[(int64_t)rc * ld + kc];
+  }
+#pragma unroll
+  for (int rr = 0; rr < GT / 8; ++rr) {
+    const int r = r0 + rr * 8;
+    lds[r * GS + kk] = (r < rows && k < kend) ? v[rr] * scale : 0.f;
   }
 }
 
 // Stage a row-major [k][j] fp32 matrix transposed: lds[j][kk] = src[(k0+kk)*ld + j]
-// for j < cols, k0 + kk < kend (zero elsewhere).
+// for j < cols, k0 + kk < kend (zero elsewhere; cols >= 1 and kend > k0).
 __device__ inline void stage_cols_f32(float* lds, const float* __restrict__ src, int64_t ld,
                                       int cols, int64_t k0, int64_t kend) {
   const int j = threadIdx.x & 127;
   const int kh = threadIdx.x >> 7;
-#pragma unroll 4
+  const int jc = j < cols ? j : cols - 1;
+  float v[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int64_t k = k0 + kh * 16 + u;
+    const int64_t kc = k < kend ? k : kend - 1;
+    v[u] = src[kc * ld + jc];
+  }
+#pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int kk = kh * 16 + u;
-    const int64_t k = k0 + kk;
-    float v = 0.f;
-    if (j < cols && k < kend) v = src[k * ld + j];
-    lds[j * GS + kk] = v;
+    lds[j * GS + kk] = (j < cols && k0 + kk < kend) ? v[u] : 0.f;
   }
 }
 

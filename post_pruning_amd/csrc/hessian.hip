@@ -6,9 +6,8 @@
 // rank-T update whose reduction axis (tokens) is the strided one.
 //
 // bf16 path: 256x256 output tiles of the lower triangle only (the symmetric
-// result is mirrored on store), 4 waves per workgroup, each wave a 128x128
-// sub-tile of v_mfma_f32_16x16x32_bf16 (accumulators in AGPRs, one wave per
-// SIMD).  X tiles are staged through LDS in
+// result is mirrored on store), 8 waves per workgroup, each wave a 128x64
+// sub-tile of v_mfma_f32_16x16x32_bf16 (two waves per SIMD).  X tiles are staged through LDS in
 // column-major form (each LDS row = one channel, 64 consecutive tokens) by an
 // in-register 8x8 transpose, so every MFMA operand is one 16-byte LDS read.
 // When there are too few tiles to fill the 256 CUs the tokens are split; every
@@ -26,7 +25,7 @@ namespace {
 constexpr int HT = kHessTile;          // 256
 constexpr int HBK = 64;                // tokens per LDS stage
 constexpr int HROWB = HBK * 2 + 16;    // LDS bytes per channel row (padded)
-constexpr int HTHREADS = 256;
+constexpr int HTHREADS = 512;
 constexpr int kMinTokPerSplit = 4096;
 
 __device__ inline int64_t xcd_remap(int64_t bid, int64_t nb) {
@@ -54,11 +53,13 @@ __device__ inline float agent_load(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <bool RAGGED>
 __global__ __launch_bounds__(HTHREADS) void hess_bf16_kernel(
     float* __restrict__ H, int n, const uint16_t* __restrict__ X, int64_t T,
     int64_t ldx, int64_t tiles, int splits, int64_t tps,
     float* __restrict__ part, unsigned* __restrict__ counters) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * HT * HROWB];
+  // Two LDS stages (double buffer), each holding the I-block and the J-block.
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][2 * HT * HROWB];
   __shared__ int s_last;
 
   const int64_t item = xcd_remap(blockIdx.x, gridDim.x);
@@ -74,105 +75,131 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wi = wave >> 1;  // 128-row half of the tile
-  const int wj = wave & 1;   // 128-column half
+  const int wi = wave >> 2;  // 128-row half of the tile
+  const int wj = wave & 3;   // 64-column quarter
 
-  // Loader role: each thread stages one 8 tokens x 8 channels block of the
-  // I-block and one of the J-block (the J-block only for off-diagonal tiles).
-  const int tb = tid & 7;   // 8-token group inside the stage
-  const int cb = tid >> 3;  // 8-channel group inside the tile
-  const unsigned char* lds_a = lds;
-  const unsigned char* lds_b = diag ? lds : lds + HT * HROWB;
+  // Loader role: threads 0..255 stage the I-block, 256..511 the J-block (only
+  // for off-diagonal tiles), one 8 tokens x 8 channels block each per stage.
+  const int op = tid >> 8;
+  const int tb = tid & 7;          // 8-token group inside the stage
+  const int cb = (tid & 255) >> 3; // 8-channel group inside the tile
+  const bool loader = !(diag && op == 1);
 
-  floatx4 acc[8][8];
+  floatx4 acc[8][4];
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[a][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 4; ++c) acc[a][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 r[2][8];
+  u32x4 r[8];
 
+  // All loads of a stage are issued back to back from clamped, always
+  // in-bounds addresses (rows past the token range re-read the last row,
+  // channel groups past n re-read the last group); out-of-range data is
+  // zeroed only when the stage is written to LDS, so no load waits on another.
+  // Per stage one uniform base pointer (row t0) and 32-bit per-lane byte
+  // offsets: SGPR-base addressing, no 64-bit address registers.
+  // RAGGED (n not a multiple of 8) takes a per-element path instead.
   auto gload = [&](int64_t t0) {
+    if (!loader) return;
+    const char* base = reinterpret_cast<const char*>(X + t0 * ldx);
+    const bool partial = t0 + HBK > t_end;
+    const int last = (int)(t_end - 1 - t0);
+    const int colbase = (op == 0 ? i0 : j0) + cb * 8;
 #pragma unroll
-    for (int op = 0; op < 2; ++op) {
-      const int colbase = (op == 0 ? i0 : j0) + cb * 8;
-      const bool active = (op == 0) || !diag;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t t = t0 + tb * 8 + i;
+    for (int i = 0; i < 8; ++i) {
+      int tr = tb * 8 + i;
+      if (partial) tr = tr < last ? tr : last;
+      if constexpr (!RAGGED) {
+        const int colc = colbase < n ? colbase : n - 8;
+        const uint32_t off = (uint32_t)tr * (uint32_t)(ldx * 2) + (uint32_t)colc * 2u;
+        r[i] = *reinterpret_cast<const u32x4*>(base + off);
+      } else {
         u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (active && t < t_end) {
-          const uint16_t* src = X + t * ldx + colbase;
-          if (colbase + 8 <= n) {
-            v = *reinterpret_cast<const u32x4*>(src);
-          } else {
+        const uint16_t* src =
+            reinterpret_cast<const uint16_t*>(base + (uint32_t)tr * (uint32_t)(ldx * 2));
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (colbase + e < n) v[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
-          }
-        }
-        r[op][i] = v;
+        for (int e = 0; e < 8; ++e)
+          if (colbase + e < n) v[e >> 1] |= (uint32_t)src[colbase + e] << (16 * (e & 1));
+        r[i] = v;
       }
     }
   };
 
-  auto lstore = [&]() {
+  // Transpose the 8x8 block in registers and store it channel-major.
+  auto lstore = [&](int64_t t0, unsigned char* buf) {
+    if (!loader) return;
+    unsigned char* dst = buf + op * HT * HROWB;
+    const bool colok = ((op == 0 ? i0 : j0) + cb * 8) < n;
 #pragma unroll
-    for (int op = 0; op < 2; ++op) {
-      if (op == 1 && diag) break;
-      unsigned char* dst = lds + op * HT * HROWB;
+    for (int i = 0; i < 8; ++i) {
+      const bool ok = colok && (t0 + tb * 8 + i) < t_end;
+      if (!ok) r[i] = u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        u32x4 lo, hi;
+    for (int d = 0; d < 4; ++d) {
+      u32x4 lo, hi;
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const uint32_t a0 = r[op][2 * qq][d], a1 = r[op][2 * qq + 1][d];
-          lo[qq] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-          hi[qq] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-        }
-        *reinterpret_cast<u32x4*>(dst + (cb * 8 + 2 * d) * HROWB + tb * 16) = lo;
-        *reinterpret_cast<u32x4*>(dst + (cb * 8 + 2 * d + 1) * HROWB + tb * 16) = hi;
+      for (int qq = 0; qq < 4; ++qq) {
+        const uint32_t a0 = r[2 * qq][d], a1 = r[2 * qq + 1][d];
+        lo[qq] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+        hi[qq] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
       }
+      *reinterpret_cast<u32x4*>(dst + (cb * 8 + 2 * d) * HROWB + tb * 16) = lo;
+      *reinterpret_cast<u32x4*>(dst + (cb * 8 + 2 * d + 1) * HROWB + tb * 16) = hi;
     }
   };
 
+  auto compute = [&](const unsigned char* buf, int ks) {
+    const unsigned char* la = buf;
+    const unsigned char* lb = diag ? buf : buf + HT * HROWB;
+    const int koff = ks * 64 + (lane >> 4) * 16;
+    bf16x8 fb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      fb[c] = *reinterpret_cast<const bf16x8*>(lb + (wj * 64 + c * 16 + (lane & 15)) * HROWB + koff);
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const bf16x8 fa =
+          *reinterpret_cast<const bf16x8*>(la + (wi * 128 + a * 16 + (lane & 15)) * HROWB + koff);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[c], acc[a][c], 0, 0, 0);
+    }
+  };
+
+  // Software pipeline: stage s is computed from LDS buffer s%2 while stage
+  // s+1 (already in registers) is written to the other buffer half-way
+  // through, and stage s+2 is then fetched into registers.  One barrier per
+  // stage.
   const int64_t ntok = t_end > t_begin ? t_end - t_begin : 0;
   const int64_t nsteps = ceil_div(ntok, HBK);
-  if (nsteps > 0) gload(t_begin);
+  if (nsteps > 0) {
+    gload(t_begin);
+    lstore(t_begin, lds[0]);
+    if (nsteps > 1) gload(t_begin + HBK);
+    __syncthreads();
+  }
   for (int64_t step = 0; step < nsteps; ++step) {
-    __syncthreads();
-    lstore();
-    __syncthreads();
-    if (step + 1 < nsteps) gload(t_begin + (step + 1) * HBK);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int koff = ks * 64 + (lane >> 4) * 16;
-      bf16x8 fb[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        fb[c] = *reinterpret_cast<const bf16x8*>(
-            lds_b + (wj * 128 + c * 16 + (lane & 15)) * HROWB + koff);
-#pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        const bf16x8 fa = *reinterpret_cast<const bf16x8*>(
-            lds_a + (wi * 128 + a * 16 + (lane & 15)) * HROWB + koff);
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[c], acc[a][c], 0, 0, 0);
-      }
+    unsigned char* cur = lds[step & 1];
+    unsigned char* nxt = lds[(step + 1) & 1];
+    compute(cur, 0);
+    if (step + 1 < nsteps) {
+      lstore(t_begin + (step + 1) * HBK, nxt);
+      if (step + 2 < nsteps) gload(t_begin + (step + 2) * HBK);
     }
+    compute(cur, 1);
+    __syncthreads();
   }
 
   // ---- epilogue -----------------------------------------------------------
   if (splits > 1) {
-    float* mine = part + (size_t)item * (HT * HT);
+    // Partial tile layout: per (wave, a, c) slot, 64 lanes x float4.
+    floatx4* mine = reinterpret_cast<floatx4*>(part + (size_t)item * (HT * HT));
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          mine[(size_t)(((wave * 64 + a * 8 + c) * 4 + v) * 64 + lane)] = acc[a][c][v];
+      for (int c = 0; c < 4; ++c) mine[(wave * 32 + a * 4 + c) * 64 + lane] = acc[a][c];
     __threadfence();
     __syncthreads();
     if (tid == 0) {
@@ -182,34 +209,31 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_kernel(
     __syncthreads();
     if (!s_last) return;
     __threadfence();
-    // Sum the partials of every split of this tile in split order.
+    // Sum the partials of every split of this tile in split order (the own
+    // partial is re-read too, so the order and the result do not depend on
+    // which split finished last).
+    for (int sp = 0; sp < splits; ++sp) {
+      const floatx4* other =
+          reinterpret_cast<const floatx4*>(part + ((size_t)sp * tiles + ti) * (HT * HT));
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+      for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const size_t off = (size_t)(((wave * 64 + a * 8 + c) * 4 + v) * 64 + lane);
-          float sum = 0.f;
-          for (int sp = 0; sp < splits; ++sp) {
-            const float pv = (sp == split)
-                                 ? acc[a][c][v]
-                                 : agent_load(part + ((size_t)sp * tiles + ti) * (HT * HT) + off);
-            sum = (sp == 0) ? pv : sum + pv;
-          }
-          acc[a][c][v] = sum;
+        for (int c = 0; c < 4; ++c) {
+          const floatx4 pv = other[(wave * 32 + a * 4 + c) * 64 + lane];
+          acc[a][c] = (sp == 0) ? pv : acc[a][c] + pv;
         }
+    }
     if (tid == 0) counters[ti] = 0u;
   }
 
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = i0 + wi * 128 + a * 16 + (lane >> 4) * 4 + v;
-        const int col = j0 + wj * 128 + c * 16 + (lane & 15);
+        const int col = j0 + wj * 64 + c * 16 + (lane & 15);
         if (row >= n || col >= n) continue;
         if (diag && row < col) continue;
         const size_t lo = (size_t)row * n + col;
@@ -319,8 +343,12 @@ sg_status launch_hessian_bf16(float* H, int64_t n, const uint16_t* X, int64_t T,
     if (sg_status e = check_launch("hessian counters")) return e;
   }
   const int64_t grid = plan.tiles * plan.splits;
-  hipLaunchKernelGGL(hess_bf16_kernel, dim3((unsigned)grid), dim3(HTHREADS), 0, st, H, (int)n,
-                     X, T, ldx, plan.tiles, plan.splits, plan.tok_per_split, part, counters);
+  if (n % 8 == 0)
+    hipLaunchKernelGGL(hess_bf16_kernel<false>, dim3((unsigned)grid), dim3(HTHREADS), 0, st, H,
+                       (int)n, X, T, ldx, plan.tiles, plan.splits, plan.tok_per_split, part, counters);
+  else
+    hipLaunchKernelGGL(hess_bf16_kernel<true>, dim3((unsigned)grid), dim3(HTHREADS), 0, st, H,
+                       (int)n, X, T, ldx, plan.tiles, plan.splits, plan.tok_per_split, part, counters);
   return check_launch("hessian bf16");
 }
 
