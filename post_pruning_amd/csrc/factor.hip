@@ -106,9 +106,8 @@ __global__ __launch_bounds__(256) void flip_init_kernel(const float* __restrict_
 constexpr int PS = 132;  // LDS row stride (floats): 16-byte rows, conflict-free b128 reads
 
 struct PanelLds {
-  float As[NB * PS];
+  float As[NB * PS];  // A_kk / L_kk, later the block to transform
   float Li[NB * PS];
-  float Pst[GT * GS];
   int fail;
 };
 
@@ -126,11 +125,36 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
   const int b = blockIdx.x;
   const int64_t k0 = (int64_t)k * NB;
 
-  // 0. load the lower part of A_kk, clear L_kk^{-1}
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e >> 7, c = e & 127;
-    S.As[i * PS + c] = (c <= i) ? A[(k0 + i) * n_pad + k0 + c] : 0.f;
-    S.Li[i * PS + c] = 0.f;
+  // The 128x128 block this workgroup transforms at the end is fetched into
+  // registers right away, so its latency hides behind the factorisation.
+  float* blk = nullptr;
+  if (b > k)
+    blk = A + (int64_t)b * NB * n_pad + k0;  // L[l,k] = A[l,k] L_kk^{-T}
+  else if (b < k)
+    blk = Y + (int64_t)b * NB * n_pad + k0;  // Y[c,k] = R[c,k] L_kk^{-T}
+  const int brow = tid >> 1, bcol = (tid & 1) * 64;
+  floatx4 bv[16];
+  if (blk) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      bv[u] = *reinterpret_cast<const floatx4*>(blk + (int64_t)brow * n_pad + bcol + 4 * u);
+  }
+
+  // 0. load the lower part of A_kk (all loads issued together), clear L_kk^{-1}
+  {
+    floatx4 av[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      av[u] = *reinterpret_cast<const floatx4*>(A + (k0 + brow) * n_pad + k0 + bcol + 4 * u);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      floatx4 v = av[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (bcol + 4 * u + e > brow) v[e] = 0.f;
+      *reinterpret_cast<floatx4*>(&S.As[brow * PS + bcol + 4 * u]) = v;
+      *reinterpret_cast<floatx4*>(&S.Li[brow * PS + bcol + 4 * u]) = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
   }
   if (tid == 0) S.fail = -1;
   __syncthreads();
@@ -151,8 +175,10 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
       for (int j = 0; j < 16; ++j) {
         const float d2 = rdlane(a0[j], j);
         if (fail < 0 && !(d2 > 0.f && isfinite(d2))) fail = j;
-        const float d = sqrtf(d2);
-        const float rd = 1.f / d;
+        // hardware sqrt / reciprocal (about 1 ulp): the pivot chain is the
+        // latency-critical path of the whole factorisation
+        const float d = __builtin_amdgcn_sqrtf(d2);
+        const float rd = __builtin_amdgcn_rcpf(d);
         a0[j] = (lane > j) ? a0[j] * rd : (lane == j ? d : a0[j]);
         a1[j] *= rd;
 #pragma unroll
@@ -206,8 +232,8 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
       float acc = 0.f;
 #pragma unroll
       for (int q = 0; q < i; ++q) acc = fmaf(S.As[(b0 + i) * PS + b0 + q], x[q], acc);
-      const float lii = S.As[(b0 + i) * PS + b0 + i];
-      x[i] = (i < c) ? 0.f : ((i == c) ? 1.f / lii : -acc / lii);
+      const float rlii = __builtin_amdgcn_rcpf(S.As[(b0 + i) * PS + b0 + i]);
+      x[i] = (i < c) ? 0.f : ((i == c) ? rlii : -acc * rlii);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) S.Li[(b0 + i) * PS + b0 + c] = x[i];
@@ -247,39 +273,30 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
     }
     return;
   }
-  float* blk;
-  if (b > k)
-    blk = A + (int64_t)b * NB * n_pad + k0;  // L[l,k] = A[l,k] L_kk^{-T}
-  else
-    blk = Y + (int64_t)b * NB * n_pad + k0;  // Y[c,k] = R[c,k] L_kk^{-T}
+  // stage the prefetched block into the (now free) A_kk area
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    *reinterpret_cast<floatx4*>(&S.As[brow * PS + bcol + 4 * u]) = bv[u];
+  __syncthreads();
   TileAcc acc;
   tile_zero(acc);
-  for (int kc = 0; kc < NB; kc += GBK) {
-    stage_rows_f32(S.Pst, blk, n_pad, NB, kc, NB);
-    __syncthreads();
-    // Q rows = rows of L_kk^{-1} (k contiguous), read straight from LDS
-    const int prow = (wave >> 1) * 64 + (lane & 15);
-    const int qrow = (wave & 1) * 64 + (lane & 15);
+  const int prow = (wave >> 1) * 64 + (lane & 15);
+  const int qrow = (wave & 1) * 64 + (lane & 15);
+#pragma unroll 2
+  for (int kc = 0; kc < NB; kc += 16) {
+    const int kl = kc + (lane >> 4) * 4;
+    floatx4 pp[4], qq[4];
 #pragma unroll
-    for (int g = 0; g < GBK / 16; ++g) {
-      const int kl = g * 16 + (lane >> 4) * 4;
-      floatx4 pp[4], qq[4];
+    for (int i = 0; i < 4; ++i) pp[i] = *reinterpret_cast<const floatx4*>(&S.As[(prow + i * 16) * PS + kl]);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) qq[jj] = *reinterpret_cast<const floatx4*>(&S.Li[(qrow + jj * 16) * PS + kl]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        pp[i] = *reinterpret_cast<const floatx4*>(S.Pst + (prow + i * 16) * GS + kl);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        qq[jj] = *reinterpret_cast<const floatx4*>(S.Li + (qrow + jj * 16) * PS + kc + kl);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            acc.v[i][jj] =
-                __builtin_amdgcn_mfma_f32_16x16x4f32(pp[i][e], qq[jj][e], acc.v[i][jj], 0, 0, 0);
-    }
-    __syncthreads();
+        for (int jj = 0; jj < 4; ++jj)
+          acc.v[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(pp[i][e], qq[jj][e], acc.v[i][jj], 0, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -300,12 +317,11 @@ __device__ inline int64_t isqrt_floor(int64_t x) {
 
 __global__ __launch_bounds__(256) void update_kernel(float* __restrict__ A, float* __restrict__ Y,
                                                      int64_t n_pad, int k, int nblk) {
-  __shared__ __attribute__((aligned(16))) float Pl[GT * GS];
-  __shared__ __attribute__((aligned(16))) float Ql[GT * GS];
+  __shared__ __attribute__((aligned(16))) float lds[4 * GBUF];
   const int64_t t = nblk - k - 1;  // trailing block count
   const int64_t nsyrk = t * (t + 1) / 2;
   int64_t idx = blockIdx.x;
-  float *C;
+  float* C;
   const float *P, *Q;
   if (idx < nsyrk) {
     // lower-triangle tile (l, m) of the trailing matrix, m <= l
@@ -326,24 +342,12 @@ __global__ __launch_bounds__(256) void update_kernel(float* __restrict__ A, floa
     Q = A + lb * NB * n_pad + (int64_t)k * NB;
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  RowsF32 pl{P, n_pad, NB, NB, 1.f};
+  RowsF32 ql{Q, n_pad, NB, NB, 1.f};
   TileAcc acc;
   tile_zero(acc);
-  for (int kc = 0; kc < NB; kc += GBK) {
-    stage_rows_f32(Pl, P, n_pad, NB, kc, NB);
-    stage_rows_f32(Ql, Q, n_pad, NB, kc, NB);
-    __syncthreads();
-    tile_mma_chunk(acc, Pl, Ql, wave, lane);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float* dst = C + (int64_t)tile_row(wave, lane, i, v) * n_pad + tile_col(wave, lane, jj);
-        *dst -= acc.v[i][jj][v];
-      }
+  tile_gemm_pipelined(acc, pl, ql, NB, lds);
+  tile_sub_from(C, n_pad, NB, NB, acc, lds);
 }
 
 // ---- flip out: U[i][j] = Y[n-1-j][n-1-i] (i <= j), 0 below ------------------

@@ -9,6 +9,12 @@
 // 16-byte fragment reads), so a lane fetches 4 consecutive k-values of its
 // row with one ds_read_b128 and feeds them to 4 MFMAs.  A and B use the same
 // lane -> k assignment, so the k permutation inside a 16-wide group cancels.
+//
+// The k loop is software-pipelined: chunk c+1 is loaded into registers while
+// chunk c is multiplied out of one of two LDS buffers, so global-memory latency
+// hides behind the MFMAs.  Loads always use clamped in-bounds addresses and
+// out-of-range values are zeroed when they are written to LDS, so a chunk's
+// loads are issued back to back without waits in between.
 #pragma once
 
 #include "sg_internal.h"
@@ -19,6 +25,7 @@ constexpr int GT = kGemmTile;  // 128
 constexpr int GBK = 32;
 constexpr int GS = GBK + 4;    // LDS row stride in floats
 constexpr int GTHREADS = 256;
+constexpr int GBUF = GT * GS;  // floats per operand buffer
 
 struct TileAcc {
   floatx4 v[4][4];
@@ -62,48 +69,141 @@ __device__ inline void tile_mma_chunk(TileAcc& acc, const float* Pl, const float
   }
 }
 
-// Stage rows of a k-contiguous fp32 matrix: lds[r][kk] = scale * src[r*ld + k0 + kk]
-// for r < rows, k0 + kk < kend (zero elsewhere; rows >= 1 and kend > k0).
-// All loads are issued first from clamped in-bounds addresses, then the
-// out-of-range values are zeroed as they are written, so the loads overlap.
-__device__ inline void stage_rows_f32(float* lds, const float* __restrict__ src, int64_t ld,
-                                      int rows, int64_t k0, int64_t kend, float scale = 1.f) {
-  const int kk = threadIdx.x & 31;
-  const int r0 = threadIdx.x >> 5;
-  const int64_t k = k0 + kk;
-  const int64_t kc = k < kend ? k : kend - 1;
+// Rows of a k-contiguous fp32 matrix: element (r, k) = scale * src[r*ld + k],
+// valid for r < rows, k < kend (rows >= 1, kend >= 1).
+struct RowsF32 {
+  const float* src;
+  int64_t ld;
+  int rows;
+  int64_t kend;
+  float scale;
   float v[GT / 8];
+  __device__ inline void load(int64_t k0) {
+    const int kk = threadIdx.x & 31, r0 = threadIdx.x >> 5;
+    const int64_t k = k0 + kk;
+    const int64_t kc = k < kend ? k : kend - 1;
 #pragma unroll
-  for (int rr = 0; rr < GT / 8; ++rr) {
-    const int r = r0 + rr * 8;
-    const int rc = r < rows ? r : rows - 1;
-    v[rr] = src[(int64_t)rc * ld + kc];
+    for (int rr = 0; rr < GT / 8; ++rr) {
+      const int r = r0 + rr * 8;
+      const int rc = r < rows ? r : rows - 1;
+      v[rr] = src[(int64_t)rc * ld + kc];
+    }
   }
+  __device__ inline void store(float* lds, int64_t k0) {
+    const int kk = threadIdx.x & 31, r0 = threadIdx.x >> 5;
+    const bool kok = k0 + kk < kend;
 #pragma unroll
-  for (int rr = 0; rr < GT / 8; ++rr) {
-    const int r = r0 + rr * 8;
-    lds[r * GS + kk] = (r < rows && k < kend) ? v[rr] * scale : 0.f;
+    for (int rr = 0; rr < GT / 8; ++rr) {
+      const int r = r0 + rr * 8;
+      lds[r * GS + kk] = (r < rows && kok) ? v[rr] * scale : 0.f;
+    }
+  }
+};
+
+// A row-major [k][j] fp32 matrix read transposed: element (j, k) = src[k*ld + j],
+// valid for j < cols, k < kend (cols >= 1, kend >= 1).
+struct ColsF32 {
+  const float* src;
+  int64_t ld;
+  int cols;
+  int64_t kend;
+  float v[16];
+  __device__ inline void load(int64_t k0) {
+    const int j = threadIdx.x & 127, kh = threadIdx.x >> 7;
+    const int jc = j < cols ? j : cols - 1;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int64_t k = k0 + kh * 16 + u;
+      const int64_t kc = k < kend ? k : kend - 1;
+      v[u] = src[kc * ld + jc];
+    }
+  }
+  __device__ inline void store(float* lds, int64_t k0) {
+    const int j = threadIdx.x & 127, kh = threadIdx.x >> 7;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int kk = kh * 16 + u;
+      lds[j * GS + kk] = (j < cols && k0 + kk < kend) ? v[u] : 0.f;
+    }
+  }
+};
+
+// acc += P * Q^T over k in [0, K): P and Q loaders with the load/store
+// interface above; lds holds 4 * GBUF floats (two buffers per operand).
+template <class PL, class QL>
+__device__ inline void tile_gemm_pipelined(TileAcc& acc, PL& pl, QL& ql, int64_t K, float* lds) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t nch = ceil_div(K, GBK);
+  if (nch <= 0) return;
+  pl.load(0);
+  ql.load(0);
+  pl.store(lds, 0);
+  ql.store(lds + GBUF, 0);
+  __syncthreads();
+  for (int64_t c = 0; c < nch; ++c) {
+    float* cur = lds + (c & 1) * 2 * GBUF;
+    float* nxt = lds + ((c + 1) & 1) * 2 * GBUF;
+    const bool more = c + 1 < nch;
+    if (more) {
+      pl.load((c + 1) * GBK);
+      ql.load((c + 1) * GBK);
+    }
+    tile_mma_chunk(acc, cur, cur + GBUF, wave, lane);
+    if (more) {
+      pl.store(nxt, (c + 1) * GBK);
+      ql.store(nxt + GBUF, (c + 1) * GBK);
+    }
+    __syncthreads();
   }
 }
 
-// Stage a row-major [k][j] fp32 matrix transposed: lds[j][kk] = src[(k0+kk)*ld + j]
-// for j < cols, k0 + kk < kend (zero elsewhere; cols >= 1 and kend > k0).
-__device__ inline void stage_cols_f32(float* lds, const float* __restrict__ src, int64_t ld,
-                                      int cols, int64_t k0, int64_t kend) {
-  const int j = threadIdx.x & 127;
-  const int kh = threadIdx.x >> 7;
-  const int jc = j < cols ? j : cols - 1;
-  float v[16];
+// C[0:rows, 0:cols] -= acc (C row-major with leading dimension ldc), staged
+// through LDS (which must hold GT * (GT + 4) floats and be free) so that the
+// read-modify-write of C is done with float4 accesses, 32 lanes per row.
+__device__ inline void tile_sub_from(float* __restrict__ C, int64_t ldc, int rows, int cols,
+                                     const TileAcc& acc, float* lds) {
+  constexpr int TS = GT + 4;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int64_t k = k0 + kh * 16 + u;
-    const int64_t kc = k < kend ? k : kend - 1;
-    v[u] = src[kc * ld + jc];
-  }
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int kk = kh * 16 + u;
-    lds[j * GS + kk] = (j < cols && k0 + kk < kend) ? v[u] : 0.f;
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        lds[tile_row(wave, lane, i, v) * TS + tile_col(wave, lane, jj)] = acc.v[i][jj][v];
+  __syncthreads();
+  const int c4 = (threadIdx.x & 31) * 4;
+  const int r0 = threadIdx.x >> 5;
+  const bool vec = (cols == GT) && ((ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
+  if (vec) {
+    // all loads first (C may alias nothing else, but the compiler cannot know
+    // that a store does not feed a later load), then subtract and store
+    floatx4 cv[GT / 8];
+#pragma unroll
+    for (int rr = 0; rr < GT / 8; ++rr) {
+      const int r = r0 + rr * 8;
+      const int rc = r < rows ? r : rows - 1;
+      cv[rr] = *reinterpret_cast<const floatx4*>(C + (int64_t)rc * ldc + c4);
+    }
+#pragma unroll
+    for (int rr = 0; rr < GT / 8; ++rr) {
+      const int r = r0 + rr * 8;
+      if (r < rows) {
+        const floatx4 t = *reinterpret_cast<const floatx4*>(&lds[r * TS + c4]);
+        *reinterpret_cast<floatx4*>(C + (int64_t)r * ldc + c4) = cv[rr] - t;
+      }
+    }
+  } else {
+    for (int rr = 0; rr < GT / 8; ++rr) {
+      const int r = r0 + rr * 8;
+      if (r >= rows) break;
+      const floatx4 t = *reinterpret_cast<const floatx4*>(&lds[r * TS + c4]);
+      float* crow = C + (int64_t)r * ldc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c4 + e < cols) crow[c4 + e] -= t[e];
+    }
   }
 }
 

@@ -24,9 +24,12 @@
 //   lazy     W[:, i2:] -= Err * U[i1:i2, i2:] on fp32 MFMA (K = w).
 #include "gemm_f32.h"
 
+#include <hip/hip_cooperative_groups.h>
+
 #include <math.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace sg {
 namespace {
@@ -38,12 +41,10 @@ constexpr int SEL_EPT = 16;           // keys per thread per select pass
 enum { MODE_THRESH = 0, MODE_NM = 1, MODE_FORCED = 2 };
 
 struct SelState {
-  unsigned long long prefix;
   unsigned long long thresh;
-  long long krem;
-  unsigned done;  // 0 searching, 1 thresh valid, 2 none selected, 3 all selected
-  unsigned counter;
-  unsigned hist[kSelBins];
+  unsigned done;  // 1 thresh valid, 2 none selected, 3 all selected
+  unsigned pad;
+  unsigned hist[3][kSelBins];  // per-pass merged histograms, used round-robin
 };
 
 __device__ inline float saliency(float w, float ucc) {
@@ -70,96 +71,127 @@ __global__ void convert_kernel(float* __restrict__ out, const void* __restrict__
   }
 }
 
-__global__ void sel_init_kernel(SelState* st, long long k, long long total) {
-  for (int b = threadIdx.x; b < kSelBins; b += blockDim.x) st->hist[b] = 0u;
-  if (threadIdx.x == 0) {
-    st->prefix = 0ull;
-    st->thresh = 0ull;
-    st->krem = k;
-    st->counter = 0u;
-    st->done = (k <= 0) ? 2u : (k >= total ? 3u : 0u);
-  }
+__global__ void sel_clear_kernel(SelState* st) {
+  for (int b = threadIdx.x; b < 3 * kSelBins; b += blockDim.x) (&st->hist[0][0])[b] = 0u;
 }
 
-__global__ __launch_bounds__(256) void sel_pass_kernel(SelState* st, const float* __restrict__ W,
-                                                       const float* __restrict__ U, int64_t m,
-                                                       int64_t n, int64_t i1, int w, int shift,
-                                                       int width) {
-  __shared__ unsigned h[kSelBins];
+// Exact k-th smallest 64-bit key of the m x w block by radix select, all
+// passes in one cooperative launch: each pass histograms one digit of the keys
+// that match the prefix fixed so far (per-wave LDS histograms merged into a
+// global one), then, after a grid-wide sync, every workgroup scans the merged
+// histogram itself and fixes the same digit.  hist[p % 3] is used by pass p;
+// workgroup 0 clears the next pass's buffer during the current pass (the
+// readers of that buffer finished two syncs earlier).  hist[0] must be zero on
+// entry; the sweep kernel that follows re-clears all three.
+__global__ __launch_bounds__(256) void select_kernel(SelState* st, const float* __restrict__ W,
+                                                    const float* __restrict__ U, int64_t m,
+                                                    int64_t n, int64_t i1, int w, long long k) {
+  namespace cg = cooperative_groups;
+  cg::grid_group grid = cg::this_grid();
+  __shared__ unsigned h[4][kSelBins];
   __shared__ unsigned scan[256];
-  __shared__ int s_last;
-  if (st->done != 0u) return;
-  const int tid = threadIdx.x;
-  for (int b = tid; b < kSelBins; b += 256) h[b] = 0u;
-  __syncthreads();
-  const unsigned long long prefix = st->prefix;
-  const int hi = shift + width;
-  const unsigned dmask = (1u << width) - 1u;
-  const int64_t total = m * (int64_t)w;
-  const int64_t base = (int64_t)blockIdx.x * 256 * SEL_EPT;
-  for (int u = 0; u < SEL_EPT; ++u) {
-    const int64_t e = base + (int64_t)u * 256 + tid;
-    if (e >= total) break;
-    const int64_t r = e / w;
-    const int c = (int)(e - r * w);
-    const int64_t col = i1 + c;
-    const unsigned long long key = sal_key(W[r * n + col], U[col * n + col], (uint32_t)(r * n + col));
-    if (hi >= 64 || (key >> hi) == (prefix >> hi))
-      atomicAdd(&h[(unsigned)(key >> shift) & dmask], 1u);
+  __shared__ unsigned long long s_prefix;
+  __shared__ long long s_krem;
+  __shared__ unsigned s_done;
+  __shared__ unsigned long long s_thresh;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const long long total = m * (long long)w;
+  if (tid == 0) {
+    s_prefix = 0ull;
+    s_krem = k;
+    s_done = (k <= 0) ? 2u : (k >= total ? 3u : 0u);
+    s_thresh = 0ull;
   }
   __syncthreads();
-  for (int b = tid; b < kSelBins; b += 256)
-    if (h[b]) atomicAdd(&st->hist[b], h[b]);
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&st->counter, 1u) == gridDim.x - 1) ? 1 : 0;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // Last workgroup: locate the digit holding the krem-th smallest key.
-  const int per = kSelBins / 256;
-  unsigned local = 0;
-  for (int i = 0; i < per; ++i) {
-    const unsigned v = __hip_atomic_load(&st->hist[tid * per + i], __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    h[tid * per + i] = v;
-    local += v;
-  }
-  scan[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
-    const unsigned v = (tid >= off) ? scan[tid - off] : 0u;
+  static const int shifts[6] = {53, 42, 32, 21, 10, 0};
+  static const int widths[6] = {11, 11, 10, 11, 11, 10};
+  for (int p = 0; p < 6; ++p) {
+    if (s_done != 0u) break;  // uniform across the grid
+    const int shift = shifts[p], width = widths[p];
+    const int hi = shift + width;
+    const unsigned dmask = (1u << width) - 1u;
+    const unsigned long long prefix = s_prefix;
+    unsigned* gh = st->hist[p % 3];
+    if (blockIdx.x == 0)
+      for (int b = tid; b < kSelBins; b += 256) st->hist[(p + 1) % 3][b] = 0u;
+    for (int b = tid; b < 4 * kSelBins; b += 256) (&h[0][0])[b] = 0u;
     __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  const long long krem = st->krem;
-  const unsigned long long before = (tid == 0) ? 0ull : scan[tid - 1];
-  if ((long long)before < krem && krem <= (long long)scan[tid]) {
-    unsigned long long cum = before;
-    for (int i = 0; i < per; ++i) {
-      const unsigned cnt = h[tid * per + i];
-      if ((long long)(cum + cnt) >= krem) {
-        const unsigned d = (unsigned)(tid * per + i);
-        const unsigned long long np = prefix | ((unsigned long long)d << shift);
-        const long long nk = krem - (long long)cum;
-        st->prefix = np;
-        st->krem = nk;
-        if ((long long)cnt == nk) {
-          st->thresh = np | ((shift > 0) ? ((1ull << shift) - 1ull) : 0ull);
-          st->done = 1u;
-        } else if (shift == 0) {
-          st->thresh = np;
-          st->done = 1u;
-        }
-        break;
+    // rows are spread over the grid, 2 rows per pass of the workgroup, one
+    // column per thread (w <= 128)
+    const int c = tid & 127;
+    const int cc = c < w ? c : w - 1;
+    const int64_t col = i1 + cc;
+    const float ucc = U[col * n + col];
+    const int64_t rstep = (int64_t)gridDim.x * 2;
+    for (int64_t rb = (int64_t)blockIdx.x * 2 + (tid >> 7); rb < m; rb += 8 * rstep) {
+      // 8 rows' values fetched together, then hashed
+      float wv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t r = rb + u * rstep;
+        wv[u] = W[(r < m ? r : m - 1) * n + col];
       }
-      cum += cnt;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t r = rb + u * rstep;
+        if (r < m && c < w) {
+          const unsigned long long key = sal_key(wv[u], ucc, (uint32_t)(r * n + col));
+          if (hi >= 64 || (key >> hi) == (prefix >> hi))
+            atomicAdd(&h[wave][(unsigned)(key >> shift) & dmask], 1u);
+        }
+      }
     }
+    __syncthreads();
+    for (int b = tid; b < kSelBins; b += 256) {
+      const unsigned v = h[0][b] + h[1][b] + h[2][b] + h[3][b];
+      if (v) atomicAdd(&gh[b], v);
+    }
+    grid.sync();
+    // every workgroup: locate the digit holding the krem-th smallest key
+    const int per = kSelBins / 256;
+    unsigned local = 0;
+    for (int i = 0; i < per; ++i) {
+      const unsigned v = gh[tid * per + i];
+      h[0][tid * per + i] = v;
+      local += v;
+    }
+    scan[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
+      const unsigned v = (tid >= off) ? scan[tid - off] : 0u;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const long long krem = s_krem;
+    const unsigned long long before = (tid == 0) ? 0ull : scan[tid - 1];
+    __syncthreads();
+    if ((long long)before < krem && krem <= (long long)scan[tid]) {
+      unsigned long long cum = before;
+      for (int i = 0; i < per; ++i) {
+        const unsigned cnt = h[0][tid * per + i];
+        if ((long long)(cum + cnt) >= krem) {
+          const unsigned d = (unsigned)(tid * per + i);
+          const unsigned long long np = prefix | ((unsigned long long)d << shift);
+          const long long nk = krem - (long long)cum;
+          s_prefix = np;
+          s_krem = nk;
+          if ((long long)cnt == nk || shift == 0) {
+            // the bucket is taken whole: every key up to the end of its range
+            s_thresh = np | ((shift > 0) ? ((1ull << shift) - 1ull) : 0ull);
+            s_done = 1u;
+          }
+          break;
+        }
+        cum += cnt;
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int b = tid; b < kSelBins; b += 256) st->hist[b] = 0u;
-  if (tid == 0) st->counter = 0u;
+  if (blockIdx.x == 0 && tid == 0) {
+    st->done = s_done;
+    st->thresh = s_thresh;
+  }
 }
 
 template <int L>
@@ -173,14 +205,6 @@ struct SweepLds {
   float Sc[SW_ROWS * SB];
 };
 
-template <int J, int END, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (J < END) {
-    f(std::integral_constant<int, J>{});
-    static_for<J + 1, END>(f);
-  }
-}
-
 // Rank of key (my, me) among the group's keys sal[0..cnt) -- lexicographic
 // (saliency, position), so equal saliencies prune the lower column first.
 __device__ __forceinline__ int group_rank(const float* sal, int cnt, float my, int me) {
@@ -192,11 +216,60 @@ __device__ __forceinline__ int group_rank(const float* sal, int cnt, float my, i
   return rank;
 }
 
+struct SweepCtx {
+  float* sc;       // per-row scratch of the N:M ranking
+  const float* Ub; // U block in LDS
+  const float* Rd; // reciprocal diagonal in LDS
+  int q, w, mgroup, nkeep, sb;
+  bool rv, nm_small;
+};
+
+// Column J = 16*sb + QJ of the in-block sweep.  Register slot s holds column
+// q + 16*(sb + s) (the slots rotate down after every 16 columns), so the owner
+// of column J is lane QJ, slot 0: QJ is a compile-time constant, making the
+// DPP broadcast and every register index static.
+template <int QJ, bool NM>
+__device__ __forceinline__ void sweep_col(const SweepCtx& cx, float (&Wv)[8], float (&E)[8],
+                                          bool (&P)[8]) {
+  const int J = cx.sb * 16 + QJ;
+  if (J >= cx.w) return;
+  const int q = cx.q;
+  if (NM && cx.nm_small && (J % cx.mgroup) == 0) {
+    // the group is columns J..J+M-1 = lanes QJ..QJ+M-1 of slot 0
+    const int c = q + 16 * cx.sb;
+    const float sal = saliency(Wv[0], cx.Ub[c * SB + c]);
+    cx.sc[q] = sal;
+    __syncthreads();
+    if (q >= QJ && q < QJ + cx.mgroup)
+      P[0] = cx.rv && group_rank(cx.sc + QJ, cx.mgroup, sal, q - QJ) < cx.mgroup - cx.nkeep;
+    __syncthreads();
+  }
+  const float eo = (q == QJ && P[0]) ? Wv[0] * cx.Rd[J] : 0.f;
+  const float e = bcast16_c<QJ>(eo);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int as = s + cx.sb;  // absolute slot; past the block the U row is zero
+    const float u = cx.Ub[J * SB + q + 16 * (as < 8 ? as : 7)];
+    Wv[s] = fmaf(-e, as < 8 ? u : 0.f, Wv[s]);
+  }
+  if (q == QJ) {
+    E[0] = eo;
+    if (P[0]) Wv[0] = 0.f;
+  }
+}
+
+template <bool NM, int... Qs>
+__device__ __forceinline__ void sweep_16(std::integer_sequence<int, Qs...>, const SweepCtx& cx,
+                                         float (&Wv)[8], float (&E)[8], bool (&P)[8]) {
+  (sweep_col<Qs, NM>(cx, Wv, E, P), ...);
+}
+
+template <int MODE>
 __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8_t* __restrict__ mask_out,
                                                     float* __restrict__ Err, const float* __restrict__ U,
                                                     const uint8_t* __restrict__ mask_in,
                                                     const SelState* __restrict__ st, int64_t m,
-                                                    int64_t n, int64_t i1, int w, int mode, int nkeep,
+                                                    int64_t n, int64_t i1, int w, int nkeep,
                                                     int mgroup) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   SweepLds& S = *reinterpret_cast<SweepLds*>(smem);
@@ -206,11 +279,31 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   const int64_t r = (int64_t)blockIdx.x * SW_ROWS + rl;
   const bool rv = r < m;
 
-  for (int e = tid; e < SB * SB; e += 256) {
-    const int j = e >> 7, c = e & (SB - 1);
-    S.Ub[e] = (j < w && c < w && c >= j) ? U[(i1 + j) * n + i1 + c] : 0.f;
+  {
+    // U block: row j = tid/2, 64 columns per thread; all loads issued together
+    // from clamped in-bounds addresses, out-of-block entries zeroed on store
+    const int j = tid >> 1, c0 = (tid & 1) * 64;
+    const int jc = j < w ? j : w - 1;
+    const float* urow = U + (i1 + jc) * n + i1;
+    float uv[64];
+#pragma unroll
+    for (int u = 0; u < 64; ++u) {
+      const int c = c0 + u;
+      uv[u] = urow[c < w ? c : w - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 64; ++u) {
+      const int c = c0 + u;
+      S.Ub[j * SB + c] = (j < w && c < w && c >= j) ? uv[u] : 0.f;
+    }
   }
   if (tid < SB) S.Rd[tid] = (tid < w) ? 1.f / U[(i1 + tid) * n + i1 + tid] : 0.f;
+  if (MODE == MODE_THRESH && blockIdx.x == 0) {
+    // leave the select histograms zeroed for the next block (the select
+    // launch of this block has completed)
+    SelState* sw = const_cast<SelState*>(st);
+    for (int b = tid; b < 3 * kSelBins; b += 256) (&sw->hist[0][0])[b] = 0u;
+  }
   float Wv[8], E[8];
   bool P[8];
   const int64_t rowoff = r * n + i1;
@@ -223,13 +316,13 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   }
   __syncthreads();
 
-  if (mode == MODE_FORCED) {
+  if (MODE == MODE_FORCED) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int c = q + 16 * s;
       P[s] = rv && c < w && mask_in[rowoff + c] != 0;
     }
-  } else if (mode == MODE_THRESH) {
+  } else if (MODE == MODE_THRESH) {
     const unsigned done = st->done;
     const unsigned long long thr = st->thresh;
 #pragma unroll
@@ -241,61 +334,55 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
       }
     }
   }
-  const bool nm_small = (mode == MODE_NM) && mgroup <= 16;
-  const bool nm_large = (mode == MODE_NM) && mgroup > 16;
-  float* sc = S.Sc + rl * SB;
 
-  static_for<0, SB>([&](auto Jc) {
-    constexpr int J = decltype(Jc)::value;
-    constexpr int qJ = J & 15, sJ = J >> 4;
-    if (J >= w) return;
-    if (nm_small && (J % mgroup) == 0) {
-      // the group is columns J..J+M-1 = lanes qJ..qJ+M-1 of slot sJ
-      const int c = q + 16 * sJ;
-      const float sal = saliency(Wv[sJ], S.Ub[c * SB + c]);
-      sc[q] = sal;
-      __syncthreads();
-      if (q >= qJ && q < qJ + mgroup)
-        P[sJ] = rv && group_rank(sc + qJ, mgroup, sal, q - qJ) < mgroup - nkeep;
-      __syncthreads();
-    }
-    if constexpr (qJ == 0) {
-      if (nm_large && (J % mgroup) == 0) {
+  SweepCtx cx;
+  cx.sc = S.Sc + rl * SB;
+  cx.Ub = S.Ub;
+  cx.Rd = S.Rd;
+  cx.q = q;
+  cx.w = w;
+  cx.mgroup = mgroup;
+  cx.nkeep = nkeep;
+  cx.rv = rv;
+  cx.nm_small = (MODE == MODE_NM) && mgroup <= 16;
+  const bool nm_large = (MODE == MODE_NM) && mgroup > 16;
+  for (int sb = 0; sb < 8; ++sb) {
+    if (sb * 16 >= w) break;
+    cx.sb = sb;
+    if (MODE == MODE_NM && nm_large && ((sb * 16) % mgroup) == 0) {
+      // group of M >= 16 columns starting here: slots 0 .. M/16-1, all lanes
+      const int J = sb * 16;
 #pragma unroll
-        for (int s = sJ; s < 8; ++s) {
-          const int c = q + 16 * s;
-          if (c < J + mgroup) sc[c - J] = saliency(Wv[s], S.Ub[c * SB + c]);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int s = sJ; s < 8; ++s) {
-          const int c = q + 16 * s;
-          if (c < J + mgroup)
-            P[s] = rv && group_rank(sc, mgroup, sc[c - J], c - J) < mgroup - nkeep;
-        }
-        __syncthreads();
+      for (int s = 0; s < 8; ++s) {
+        const int c = q + 16 * (s + sb);
+        if (s + sb < 8 && c < J + mgroup) cx.sc[c - J] = saliency(Wv[s], S.Ub[c * SB + c]);
       }
-    }
-    const float eo = (q == qJ && P[sJ]) ? Wv[sJ] * S.Rd[J] : 0.f;
-    const float e = bcast16_c<qJ>(eo);
+      __syncthreads();
 #pragma unroll
-    for (int s = sJ; s < 8; ++s) Wv[s] = fmaf(-e, S.Ub[J * SB + q + 16 * s], Wv[s]);
-    if (q == qJ) {
-      E[sJ] = eo;
-      if (P[sJ]) Wv[sJ] = 0.f;
-    }
-  });
-
-  if (rv) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int c = q + 16 * s;
-      if (c < w) {
-        W[rowoff + c] = P[s] ? 0.f : Wv[s];
-        if (mask_out) mask_out[rowoff + c] = P[s] ? 1 : 0;
-        Err[r * SB + c] = E[s];
+      for (int s = 0; s < 8; ++s) {
+        const int c = q + 16 * (s + sb);
+        if (s + sb < 8 && c < J + mgroup)
+          P[s] = rv && group_rank(cx.sc, mgroup, cx.sc[c - J], c - J) < mgroup - nkeep;
       }
+      __syncthreads();
     }
+    sweep_16<MODE == MODE_NM>(std::make_integer_sequence<int, 16>{}, cx, Wv, E, P);
+    // retire slot 0 (column q + 16*sb) and rotate the slots down
+    const int c = q + 16 * sb;
+    if (rv && c < w) {
+      W[rowoff + c] = P[0] ? 0.f : Wv[0];
+      if (mask_out) mask_out[rowoff + c] = P[0] ? 1 : 0;
+      Err[r * SB + c] = E[0];
+    }
+#pragma unroll
+    for (int s = 0; s < 7; ++s) {
+      Wv[s] = Wv[s + 1];
+      E[s] = E[s + 1];
+      P[s] = P[s + 1];
+    }
+    Wv[7] = 0.f;
+    E[7] = 0.f;
+    P[7] = false;
   }
 }
 
@@ -303,32 +390,19 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
 __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ W, const float* __restrict__ Err,
                                                    const float* __restrict__ U, int64_t m, int64_t n,
                                                    int64_t i1, int w) {
-  __shared__ __attribute__((aligned(16))) float Pl[GT * GS];
-  __shared__ __attribute__((aligned(16))) float Ql[GT * GS];
+  __shared__ __attribute__((aligned(16))) float lds[4 * GBUF];
   const int64_t i2 = i1 + w;
   const int64_t r0 = (int64_t)blockIdx.y * GT;
   const int64_t c0 = i2 + (int64_t)blockIdx.x * GT;
   const int rows = (int)min<int64_t>(GT, m - r0);
   const int cols = (int)min<int64_t>(GT, n - c0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  RowsF32 pl{Err + r0 * SB, SB, rows, w, 1.f};
+  ColsF32 ql{U + i1 * n + c0, n, cols, w};
   TileAcc acc;
   tile_zero(acc);
-  for (int kc = 0; kc < w; kc += GBK) {
-    stage_rows_f32(Pl, Err + r0 * SB, SB, rows, kc, w);
-    stage_cols_f32(Ql, U + i1 * n + c0, n, cols, kc, w);
-    __syncthreads();
-    tile_mma_chunk(acc, Pl, Ql, wave, lane);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int rr = tile_row(wave, lane, i, v), cc = tile_col(wave, lane, jj);
-        if (rr < rows && cc < cols) W[(r0 + rr) * n + c0 + cc] -= acc.v[i][jj][v];
-      }
+  tile_gemm_pipelined(acc, pl, ql, w, lds);
+  tile_sub_from(W + r0 * n + c0, n, rows, cols, acc, lds);
 }
 
 }  // namespace
@@ -351,32 +425,56 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
                        n, a.ldw);
     if (sg_status e = check_launch("prune convert")) return e;
   }
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(sweep_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)sizeof(SweepLds)) != hipSuccess)
-    return set_error(SG_ERR_HIP, "hipFuncSetAttribute(sweep_kernel) failed");
+  const void* sweep_fns[3] = {reinterpret_cast<const void*>(sweep_kernel<MODE_THRESH>),
+                              reinterpret_cast<const void*>(sweep_kernel<MODE_NM>),
+                              reinterpret_cast<const void*>(sweep_kernel<MODE_FORCED>)};
+  for (const void* f : sweep_fns)
+    if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SweepLds)) !=
+        hipSuccess)
+      return set_error(SG_ERR_HIP, "hipFuncSetAttribute(sweep_kernel) failed");
 
   const int mode = a.mask_in ? MODE_FORCED : (a.kind == SG_NM ? MODE_NM : MODE_THRESH);
   const int B = a.blocksize;
+  int64_t sel_grid_cap = 0;
+  if (mode == MODE_THRESH) {
+    int dev = 0, ncu = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(select_kernel),
+                                                     256, 0) != hipSuccess || per_cu < 1)
+      return set_error(SG_ERR_HIP, "select kernel occupancy query failed");
+    sel_grid_cap = (int64_t)ncu * per_cu;
+    hipLaunchKernelGGL(sel_clear_kernel, dim3(1), dim3(256), 0, st, sel);
+    if (sg_status e = check_launch("select clear")) return e;
+  }
   for (int64_t i1 = 0; i1 < n; i1 += B) {
     const int w = (int)std::min<int64_t>(B, n - i1);
     if (mode == MODE_THRESH) {
-      const long long total = (long long)m * w;
       const long long k = (long long)floor(a.sparsity * (double)m * (double)w);
-      hipLaunchKernelGGL(sel_init_kernel, dim3(1), dim3(256), 0, st, sel, k, total);
-      if (sg_status e = check_launch("select init")) return e;
-      const unsigned g = (unsigned)ceil_div(total, 256 * SEL_EPT);
-      static const int shifts[6] = {53, 42, 32, 21, 10, 0};
-      static const int widths[6] = {11, 11, 10, 11, 11, 10};
-      for (int p = 0; p < 6; ++p) {
-        hipLaunchKernelGGL(sel_pass_kernel, dim3(g), dim3(256), 0, st, sel, a.W_out, a.U, m, n, i1,
-                           w, shifts[p], widths[p]);
-        if (sg_status e = check_launch("select pass")) return e;
-      }
+      const long long total = (long long)m * w;
+      const unsigned g = (unsigned)std::max<int64_t>(
+          1, std::min<int64_t>(std::min<int64_t>(ceil_div(total, 256 * SEL_EPT), 128), sel_grid_cap));
+      void* args[] = {&sel, const_cast<float**>(&a.W_out), const_cast<float**>(&a.U),
+                      const_cast<int64_t*>(&a.m), const_cast<int64_t*>(&a.n), &i1,
+                      const_cast<int*>(&w), const_cast<long long*>(&k)};
+      if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(select_kernel), dim3(g), dim3(256),
+                                     args, 0, st) != hipSuccess)
+        return set_error(SG_ERR_HIP, "cooperative launch of the select kernel failed");
+      if (sg_status e = check_launch("select")) return e;
     }
-    hipLaunchKernelGGL(sweep_kernel, dim3((unsigned)ceil_div(m, SW_ROWS)), dim3(256),
-                       sizeof(SweepLds), st, a.W_out, a.mask_out, Err, a.U, a.mask_in, sel, m, n,
-                       i1, w, mode, a.n_keep, a.m_group);
+    {
+      const dim3 sg_grid((unsigned)ceil_div(m, SW_ROWS)), sg_block(256);
+      const size_t shm = sizeof(SweepLds);
+      if (mode == MODE_THRESH)
+        hipLaunchKernelGGL(sweep_kernel<MODE_THRESH>, sg_grid, sg_block, shm, st, a.W_out, a.mask_out,
+                           Err, a.U, a.mask_in, sel, m, n, i1, w, a.n_keep, a.m_group);
+      else if (mode == MODE_NM)
+        hipLaunchKernelGGL(sweep_kernel<MODE_NM>, sg_grid, sg_block, shm, st, a.W_out, a.mask_out, Err,
+                           a.U, a.mask_in, sel, m, n, i1, w, a.n_keep, a.m_group);
+      else
+        hipLaunchKernelGGL(sweep_kernel<MODE_FORCED>, sg_grid, sg_block, shm, st, a.W_out, a.mask_out,
+                           Err, a.U, a.mask_in, sel, m, n, i1, w, a.n_keep, a.m_group);
+    }
     if (sg_status e = check_launch("prune sweep")) return e;
     const int64_t i2 = i1 + w;
     if (i2 < n) {

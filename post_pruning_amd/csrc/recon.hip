@@ -16,41 +16,87 @@ __device__ inline float load_elem(const void* p, int dtype, int64_t idx) {
   return static_cast<const float*>(p)[idx];
 }
 
+// P rows: D[r][k] = W[r][k] - W_hat[r][k]
+struct DiffRows {
+  const void* W;
+  int wdt;
+  int64_t ldw;
+  const float* Wh;
+  int64_t n;
+  int rows;
+  float w[GT / 8], h[GT / 8];
+  __device__ inline void load(int64_t k0) {
+    const int kk = threadIdx.x & 31, r0 = threadIdx.x >> 5;
+    const int64_t k = k0 + kk;
+    const int64_t kc = k < n ? k : n - 1;
+#pragma unroll
+    for (int rr = 0; rr < GT / 8; ++rr) {
+      const int r = r0 + rr * 8;
+      const int rc = r < rows ? r : rows - 1;
+      w[rr] = load_elem(W, wdt, (int64_t)rc * ldw + kc);
+      h[rr] = Wh[(int64_t)rc * n + kc];
+    }
+  }
+  __device__ inline void store(float* lds, int64_t k0) {
+    const int kk = threadIdx.x & 31, r0 = threadIdx.x >> 5;
+    const bool kok = k0 + kk < n;
+#pragma unroll
+    for (int rr = 0; rr < GT / 8; ++rr) {
+      const int r = r0 + rr * 8;
+      lds[r * GS + kk] = (r < rows && kok) ? w[rr] - h[rr] : 0.f;
+    }
+  }
+};
+
+// Q rows: the token-major activations X[t][k]
+struct XRows {
+  const void* X;
+  int xdt;
+  int64_t ldx;
+  int64_t n;
+  int rows;
+  float v[GT / 8];
+  __device__ inline void load(int64_t k0) {
+    const int kk = threadIdx.x & 31, r0 = threadIdx.x >> 5;
+    const int64_t k = k0 + kk;
+    const int64_t kc = k < n ? k : n - 1;
+#pragma unroll
+    for (int rr = 0; rr < GT / 8; ++rr) {
+      const int r = r0 + rr * 8;
+      const int rc = r < rows ? r : rows - 1;
+      v[rr] = load_elem(X, xdt, (int64_t)rc * ldx + kc);
+    }
+  }
+  __device__ inline void store(float* lds, int64_t k0) {
+    const int kk = threadIdx.x & 31, r0 = threadIdx.x >> 5;
+    const bool kok = k0 + kk < n;
+#pragma unroll
+    for (int rr = 0; rr < GT / 8; ++rr) {
+      const int r = r0 + rr * 8;
+      lds[r * GS + kk] = (r < rows && kok) ? v[rr] : 0.f;
+    }
+  }
+};
+
 __global__ __launch_bounds__(256) void recon_tile_kernel(const void* __restrict__ W, int wdt,
                                                          int64_t ldw, const float* __restrict__ Wh,
                                                          int64_t m, int64_t n,
                                                          const void* __restrict__ X, int xdt,
                                                          int64_t T, int64_t ldx,
                                                          double* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) float Pl[GT * GS];
-  __shared__ __attribute__((aligned(16))) float Ql[GT * GS];
+  __shared__ __attribute__((aligned(16))) float lds[4 * GBUF];
   __shared__ double red[4];
   const int64_t t0 = (int64_t)blockIdx.x * GT;
   const int64_t r0 = (int64_t)blockIdx.y * GT;
   const int rows = (int)min<int64_t>(GT, m - r0);
   const int toks = (int)min<int64_t>(GT, T - t0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int kk = threadIdx.x & 31, rsub = threadIdx.x >> 5;
+  const size_t wsz = wdt == SG_BF16 ? 2 : 4, xsz = xdt == SG_BF16 ? 2 : 4;
+  DiffRows pl{static_cast<const char*>(W) + r0 * ldw * wsz, wdt, ldw, Wh + r0 * n, n, rows};
+  XRows ql{static_cast<const char*>(X) + t0 * ldx * xsz, xdt, ldx, n, toks};
   TileAcc acc;
   tile_zero(acc);
-  for (int64_t kc = 0; kc < n; kc += GBK) {
-    const int64_t k = kc + kk;
-#pragma unroll 4
-    for (int rr = 0; rr < GT / 8; ++rr) {
-      const int r = rsub + rr * 8;
-      float dv = 0.f, xv = 0.f;
-      if (k < n) {
-        if (r < rows)
-          dv = load_elem(W, wdt, (r0 + r) * ldw + k) - Wh[(r0 + r) * n + k];
-        if (r < toks) xv = load_elem(X, xdt, (t0 + r) * ldx + k);
-      }
-      Pl[r * GS + kk] = dv;
-      Ql[r * GS + kk] = xv;
-    }
-    __syncthreads();
-    tile_mma_chunk(acc, Pl, Ql, wave, lane);
-    __syncthreads();
-  }
+  tile_gemm_pipelined(acc, pl, ql, n, lds);
   double s = 0.0;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
