@@ -36,7 +36,6 @@ namespace {
 
 constexpr int SB = SG_MAX_BLOCKSIZE;  // 128
 constexpr int SW_ROWS = 16;           // rows per sweep workgroup
-constexpr int SEL_EPT = 16;           // keys per thread per select pass
 
 enum { MODE_THRESH = 0, MODE_NM = 1, MODE_FORCED = 2 };
 
@@ -76,25 +75,30 @@ __global__ void sel_clear_kernel(SelState* st) {
 }
 
 // Exact k-th smallest 64-bit key of the m x w block by radix select, all
-// passes in one cooperative launch: each pass histograms one digit of the keys
-// that match the prefix fixed so far (per-wave LDS histograms merged into a
-// global one), then, after a grid-wide sync, every workgroup scans the merged
-// histogram itself and fixes the same digit.  hist[p % 3] is used by pass p;
-// workgroup 0 clears the next pass's buffer during the current pass (the
-// readers of that buffer finished two syncs earlier).  hist[0] must be zero on
-// entry; the sweep kernel that follows re-clears all three.
+// passes in one cooperative launch.  Every thread computes the keys of its
+// (at most SEL_KPT) elements once and keeps them in registers.  Each pass
+// histograms one digit of the keys that still match the prefix fixed so far
+// (eight lane-interleaved LDS sub-histograms against atomic contention on
+// hot bins, merged into a global one); after a grid-wide sync every
+// workgroup scans the merged histogram itself and fixes the same digit.
+// hist[p % 3] is used by pass p; workgroup 0 clears the next pass's buffer
+// during the current pass (its readers finished two syncs earlier).  hist[0]
+// must be zero on entry; the sweep kernel that follows re-clears all three.
+constexpr int SEL_KPT = 32;   // keys per thread held in registers
+constexpr int SEL_SUB = 8;    // LDS sub-histograms
+
 __global__ __launch_bounds__(256) void select_kernel(SelState* st, const float* __restrict__ W,
                                                     const float* __restrict__ U, int64_t m,
                                                     int64_t n, int64_t i1, int w, long long k) {
   namespace cg = cooperative_groups;
   cg::grid_group grid = cg::this_grid();
-  __shared__ unsigned h[4][kSelBins];
-  __shared__ unsigned scan[256];
+  __shared__ unsigned h[SEL_SUB][kSelBins];
+  __shared__ unsigned wsum[4];
   __shared__ unsigned long long s_prefix;
   __shared__ long long s_krem;
   __shared__ unsigned s_done;
   __shared__ unsigned long long s_thresh;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const long long total = m * (long long)w;
   if (tid == 0) {
     s_prefix = 0ull;
@@ -102,9 +106,32 @@ __global__ __launch_bounds__(256) void select_kernel(SelState* st, const float* 
     s_done = (k <= 0) ? 2u : (k >= total ? 3u : 0u);
     s_thresh = 0ull;
   }
+  // keys of this thread: column c, rows rb + u * rstep (u < SEL_KPT)
+  const int c = tid & 127;
+  const int cc = c < w ? c : w - 1;
+  const int64_t col = i1 + cc;
+  const float ucc = U[col * n + col];
+  const int64_t rstep = (int64_t)gridDim.x * 2;
+  const int64_t rb = (int64_t)blockIdx.x * 2 + (tid >> 7);
+  unsigned long long keys[SEL_KPT];
+  {
+    float wv[SEL_KPT];
+#pragma unroll
+    for (int u = 0; u < SEL_KPT; ++u) {
+      const int64_t r = rb + u * rstep;
+      wv[u] = W[(r < m ? r : m - 1) * n + col];
+    }
+#pragma unroll
+    for (int u = 0; u < SEL_KPT; ++u) {
+      const int64_t r = rb + u * rstep;
+      // out-of-range slots get the largest key, which never matches a prefix
+      keys[u] = (r < m && c < w) ? sal_key(wv[u], ucc, (uint32_t)(r * n + col)) : ~0ull;
+    }
+  }
   __syncthreads();
   static const int shifts[6] = {53, 42, 32, 21, 10, 0};
   static const int widths[6] = {11, 11, 10, 11, 11, 10};
+  unsigned* hsub = h[lane & (SEL_SUB - 1)];
   for (int p = 0; p < 6; ++p) {
     if (s_done != 0u) break;  // uniform across the grid
     const int shift = shifts[p], width = widths[p];
@@ -114,76 +141,64 @@ __global__ __launch_bounds__(256) void select_kernel(SelState* st, const float* 
     unsigned* gh = st->hist[p % 3];
     if (blockIdx.x == 0)
       for (int b = tid; b < kSelBins; b += 256) st->hist[(p + 1) % 3][b] = 0u;
-    for (int b = tid; b < 4 * kSelBins; b += 256) (&h[0][0])[b] = 0u;
+    for (int b = tid; b < SEL_SUB * kSelBins; b += 256) (&h[0][0])[b] = 0u;
     __syncthreads();
-    // rows are spread over the grid, 2 rows per pass of the workgroup, one
-    // column per thread (w <= 128)
-    const int c = tid & 127;
-    const int cc = c < w ? c : w - 1;
-    const int64_t col = i1 + cc;
-    const float ucc = U[col * n + col];
-    const int64_t rstep = (int64_t)gridDim.x * 2;
-    for (int64_t rb = (int64_t)blockIdx.x * 2 + (tid >> 7); rb < m; rb += 8 * rstep) {
-      // 8 rows' values fetched together, then hashed
-      float wv[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t r = rb + u * rstep;
-        wv[u] = W[(r < m ? r : m - 1) * n + col];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t r = rb + u * rstep;
-        if (r < m && c < w) {
-          const unsigned long long key = sal_key(wv[u], ucc, (uint32_t)(r * n + col));
-          if (hi >= 64 || (key >> hi) == (prefix >> hi))
-            atomicAdd(&h[wave][(unsigned)(key >> shift) & dmask], 1u);
-        }
-      }
+    for (int u = 0; u < SEL_KPT; ++u) {
+      const unsigned long long key = keys[u];
+      if (key != ~0ull && (hi >= 64 || (key >> hi) == (prefix >> hi)))
+        atomicAdd(&hsub[(unsigned)(key >> shift) & dmask], 1u);
     }
     __syncthreads();
     for (int b = tid; b < kSelBins; b += 256) {
-      const unsigned v = h[0][b] + h[1][b] + h[2][b] + h[3][b];
+      unsigned v = 0;
+#pragma unroll
+      for (int sh = 0; sh < SEL_SUB; ++sh) v += h[sh][b];
       if (v) atomicAdd(&gh[b], v);
     }
     grid.sync();
-    // every workgroup: locate the digit holding the krem-th smallest key
+    // every workgroup: locate the digit holding the krem-th smallest key;
+    // thread t owns bins 8t..8t+7, prefix sums by wave shuffles
     const int per = kSelBins / 256;
+    unsigned cnt[per];
     unsigned local = 0;
+#pragma unroll
     for (int i = 0; i < per; ++i) {
-      const unsigned v = gh[tid * per + i];
-      h[0][tid * per + i] = v;
-      local += v;
+      cnt[i] = gh[tid * per + i];
+      local += cnt[i];
     }
-    scan[tid] = local;
+    unsigned incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
-      const unsigned v = (tid >= off) ? scan[tid - off] : 0u;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
+    unsigned wbase = 0;
+    for (int wv2 = 0; wv2 < wave; ++wv2) wbase += wsum[wv2];
     const long long krem = s_krem;
-    const unsigned long long before = (tid == 0) ? 0ull : scan[tid - 1];
+    const unsigned long long before = (unsigned long long)(wbase + incl - local);
+    const unsigned long long after = (unsigned long long)(wbase + incl);
     __syncthreads();
-    if ((long long)before < krem && krem <= (long long)scan[tid]) {
+    if ((long long)before < krem && krem <= (long long)after) {
       unsigned long long cum = before;
+#pragma unroll
       for (int i = 0; i < per; ++i) {
-        const unsigned cnt = h[0][tid * per + i];
-        if ((long long)(cum + cnt) >= krem) {
+        const unsigned cn = cnt[i];
+        if ((long long)cum < krem && (long long)(cum + cn) >= krem) {
           const unsigned d = (unsigned)(tid * per + i);
           const unsigned long long np = prefix | ((unsigned long long)d << shift);
           const long long nk = krem - (long long)cum;
           s_prefix = np;
           s_krem = nk;
-          if ((long long)cnt == nk || shift == 0) {
+          if ((long long)cn == nk || shift == 0) {
             // the bucket is taken whole: every key up to the end of its range
             s_thresh = np | ((shift > 0) ? ((1ull << shift) - 1ull) : 0ull);
             s_done = 1u;
           }
-          break;
         }
-        cum += cnt;
+        cum += cn;
       }
     }
     __syncthreads();
@@ -232,30 +247,39 @@ template <int QJ, bool NM>
 __device__ __forceinline__ void sweep_col(const SweepCtx& cx, float (&Wv)[8], float (&E)[8],
                                           bool (&P)[8]) {
   const int J = cx.sb * 16 + QJ;
-  if (J >= cx.w) return;
   const int q = cx.q;
-  if (NM && cx.nm_small && (J % cx.mgroup) == 0) {
-    // the group is columns J..J+M-1 = lanes QJ..QJ+M-1 of slot 0
-    const int c = q + 16 * cx.sb;
-    const float sal = saliency(Wv[0], cx.Ub[c * SB + c]);
-    cx.sc[q] = sal;
-    __syncthreads();
-    if (q >= QJ && q < QJ + cx.mgroup)
-      P[0] = cx.rv && group_rank(cx.sc + QJ, cx.mgroup, sal, q - QJ) < cx.mgroup - cx.nkeep;
-    __syncthreads();
+  if constexpr (NM) {
+    if (J < cx.w && cx.nm_small && (J % cx.mgroup) == 0) {
+      // the group is columns J..J+M-1 = lanes QJ..QJ+M-1 of slot 0
+      const int c = q + 16 * cx.sb;
+      const float sal = saliency(Wv[0], cx.Ub[c * SB + c]);
+      cx.sc[q] = sal;
+      __syncthreads();
+      if (q >= QJ && q < QJ + cx.mgroup)
+        P[0] = cx.rv && group_rank(cx.sc + QJ, cx.mgroup, sal, q - QJ) < cx.mgroup - cx.nkeep;
+      __syncthreads();
+    }
   }
-  const float eo = (q == QJ && P[0]) ? Wv[0] * cx.Rd[J] : 0.f;
-  const float e = bcast16_c<QJ>(eo);
+  // Branch-free step (columns past the block are no-ops: P is false there and
+  // the U block is zero), so 16 steps form one basic block and the scheduler
+  // can issue the U-row reads of later steps early.
+  const int Jr = J < SB ? J : SB - 1;
+  const float rdj = cx.Rd[Jr];
+  float u[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const int as = s + cx.sb;  // absolute slot; past the block the U row is zero
-    const float u = cx.Ub[J * SB + q + 16 * (as < 8 ? as : 7)];
-    Wv[s] = fmaf(-e, as < 8 ? u : 0.f, Wv[s]);
+    const float uv = cx.Ub[Jr * SB + q + 16 * (as < 8 ? as : 7)];
+    u[s] = as < 8 ? uv : 0.f;
   }
-  if (q == QJ) {
-    E[0] = eo;
-    if (P[0]) Wv[0] = 0.f;
-  }
+  const bool own = (q == QJ) && (J < cx.w);
+  const bool prune = own && P[0];
+  const float eo = prune ? Wv[0] * rdj : 0.f;
+  const float e = bcast16_c<QJ>(eo);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) Wv[s] = fmaf(-e, u[s], Wv[s]);
+  E[0] = own ? eo : E[0];
+  Wv[0] = prune ? 0.f : Wv[0];
 }
 
 template <bool NM, int... Qs>
@@ -452,8 +476,12 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
     if (mode == MODE_THRESH) {
       const long long k = (long long)floor(a.sparsity * (double)m * (double)w);
       const long long total = (long long)m * w;
-      const unsigned g = (unsigned)std::max<int64_t>(
-          1, std::min<int64_t>(std::min<int64_t>(ceil_div(total, 256 * SEL_EPT), 128), sel_grid_cap));
+      // enough workgroups that every thread holds at most SEL_KPT keys
+      const int64_t need = ceil_div(m, (int64_t)2 * SEL_KPT);
+      if (need > sel_grid_cap)
+        return set_error(SG_ERR_UNSUPPORTED, "m=%lld too large for the single-launch select",
+                         (long long)m);
+      const unsigned g = (unsigned)std::max<int64_t>(1, need);
       void* args[] = {&sel, const_cast<float**>(&a.W_out), const_cast<float**>(&a.U),
                       const_cast<int64_t*>(&a.m), const_cast<int64_t*>(&a.n), &i1,
                       const_cast<int*>(&w), const_cast<long long*>(&k)};
