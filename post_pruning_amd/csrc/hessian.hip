@@ -28,14 +28,6 @@ constexpr int HROWB = HBK * 2 + 16;    // LDS bytes per channel row (padded)
 constexpr int HTHREADS = 512;
 constexpr int kMinTokPerSplit = 4096;
 
-__device__ inline int64_t xcd_remap(int64_t bid, int64_t nb) {
-  // Hardware deals consecutive workgroups round-robin over the 8 XCDs.  Give
-  // each XCD a contiguous run of work items so tiles that share X column
-  // blocks and token ranges meet in the same L2.
-  if (nb % 8 != 0) return bid;
-  return (bid % 8) * (nb / 8) + bid / 8;
-}
-
 __device__ inline void tri_decode(int64_t ti, int& I, int& J) {
   int64_t r = (int64_t)((sqrt(8.0 * (double)ti + 1.0) - 1.0) * 0.5);
   while ((r + 1) * (r + 2) / 2 <= ti) ++r;
@@ -62,7 +54,12 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][2 * HT * HROWB];
   __shared__ int s_last;
 
-  const int64_t item = xcd_remap(blockIdx.x, gridDim.x);
+  // Work items are split-major (item = split * tiles + tile) and taken in
+  // launch order: the workgroups resident at any time all stream the same
+  // token range, spread over all 8 XCDs, so each X slice is fetched from HBM
+  // once into the shared Infinity Cache.  (Grouping tiles per XCD to favour
+  // the per-XCD L2 measured slower.)
+  const int64_t item = blockIdx.x;
   const int split = (int)(item / tiles);
   const int64_t ti = item - (int64_t)split * tiles;
   int I, J;

@@ -1,0 +1,273 @@
+"""Full-size checks in the benchmark's launch configuration (one Hessian call
+over all resident tokens, one factor call, one prune call per pattern).
+
+4096-wide layers: the fp64 oracle H and U are computed in full on the host.
+Unstructured masks couple all rows, so on sampled rows the check is that the
+GPU mask is a valid selection under the oracle's saliencies along the GPU's
+own trajectory (near-ties allowed) and that W_hat matches the oracle with that
+mask forced.  N:M rows are independent: sampled rows are run through the
+oracle free and compared directly.
+
+11008- and 28672-wide layers (the oracle cannot factor them in seconds):
+  * H on a random channel sample against the definition from X's columns;
+  * the trailing 512x512 block of U against an oracle factor of H's trailing
+    block computed from X's trailing columns (U's trailing block depends only
+    on that block of H_d);
+  * exact per-block counts / N:M groups, pruned entries exactly +0.0;
+  * error support: with d = w - w_hat, e = d U^{-1} must vanish on kept
+    columns (the compensation is a combination of U's pruned rows only);
+  * selection consistency on sampled rows, saliencies rebuilt from e.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TAU = 1e-3
+_state = {}
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.stderr.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.stderr.flush()
+    yield
+
+
+@pytest.fixture(scope="module")
+def sg():
+    import post_pruning_amd as sg
+    sg.load_library()
+    return sg
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def _run_layer(sg, name):
+    """GPU pipeline for one workload, cached per module."""
+    if name in _state:
+        return _state[name]
+    cfg = synth.CONFIGS[name]
+    xsrc = cfg.x_source or name
+    if xsrc in _state and "X" in _state[xsrc]:
+        X = _state[xsrc]["X"]
+    else:
+        X = synth.make_x(cfg, "cuda")
+    W = synth.make_weight(cfg, "cuda")
+    H = torch.zeros(cfg.n, cfg.n, device="cuda")
+    sg.sg_hessian_accumulate(H, X)
+    Hinv, info = sg.sg_prepare_hinv(H, cfg.damp)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    res = {"cfg": cfg, "X": X, "W": W, "H": H, "Hinv": Hinv, "prune": {}}
+    for p in cfg.patterns:
+        Wh, mask = sg.sg_prune_layer(W, Hinv, p, cfg.blocksize)
+        torch.cuda.synchronize()
+        res["prune"][p] = (Wh, mask)
+    _state[name] = res
+    return res
+
+
+def _oracle_H_full(X):
+    H = None
+    for t in range(0, X.shape[0], 32768):
+        xc = X[t:t + 32768].double().cpu().numpy()
+        part = xc.T @ xc
+        H = part if H is None else H + part
+    return H
+
+
+def _check_counts_and_zeros(W_hat, mask, pattern, B):
+    m, n = mask.shape
+    gm = mask.cpu().numpy().astype(bool)
+    Wh = W_hat.cpu().numpy()
+    assert np.all(Wh[gm] == 0.0) and not np.any(np.signbit(Wh[gm]))
+    if ":" in pattern:
+        N, M = map(int, pattern.split(":"))
+        assert np.all(gm.reshape(m, -1, M).sum(axis=2) == M - N)
+    else:
+        p = float(pattern)
+        for j in range(0, n, B):
+            w = min(B, n - j)
+            assert int(gm[:, j:j + w].sum()) == math.floor(p * m * w)
+    return gm, Wh
+
+
+def _consistency(S, gmask, pattern, B, across_rows):
+    """Pruned saliencies never exceed kept ones (relative gap TAU)."""
+    m, n = gmask.shape
+    if ":" in pattern:
+        M = int(pattern.split(":")[1])
+        for j in range(0, n, M):
+            s, g = S[:, j:j + M], gmask[:, j:j + M]
+            hi = np.where(g, s, -np.inf).max(axis=1)
+            lo = np.where(~g, s, np.inf).min(axis=1)
+            assert not np.any(hi > lo * (1 + TAU) + 1e-300), f"group {j}"
+    else:
+        for j in range(0, n, B):
+            s, g = S[:, j:j + B], gmask[:, j:j + B]
+            if across_rows and g.any() and (~g).any():
+                assert s[g].max() <= s[~g].min() * (1 + TAU) + 1e-300, f"block {j}"
+
+
+# ---------------------------------------------------------------------------
+# 4096-wide layers: full oracle H and U
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def attn_oracle(sg):
+    res = _run_layer(sg, "attn_4096")
+    if "oracle" not in res:
+        H = _oracle_H_full(res["X"])
+        Hd, lam = oracle.dampen(H, res["cfg"].damp)
+        res["oracle"] = {"H": H, "U": oracle.inverse_upper_factor(Hd), "lam": lam}
+    return res
+
+
+def test_attn_4096_hessian_and_factor(attn_oracle):
+    res = attn_oracle
+    Hg = res["H"].cpu().double().numpy()
+    assert np.array_equal(Hg, Hg.T)
+    assert _rel(Hg, res["oracle"]["H"]) <= 1e-5
+    Ug = res["Hinv"].cpu().double().numpy()
+    assert np.all(np.tril(Ug, -1) == 0.0)
+    assert _rel(Ug, res["oracle"]["U"]) <= 1e-4
+
+
+def test_attn_4096_unstructured_rows(attn_oracle):
+    res = attn_oracle
+    cfg = res["cfg"]
+    p = cfg.patterns[0]
+    Wh, mask = res["prune"][p]
+    gm, Whg = _check_counts_and_zeros(Wh, mask, p, cfg.blocksize)
+    rows = np.random.default_rng(7).choice(cfg.m, 48, replace=False)
+    Wd = res["W"].cpu().double().numpy()[rows]
+    U = res["oracle"]["U"]
+    Who, _, _, tr = oracle.prune(Wd, U, p, cfg.blocksize, mask_in=gm[rows], return_trace=True)
+    _consistency(tr["saliency"], gm[rows], p, cfg.blocksize, across_rows=True)
+    assert _rel(Whg[rows], Who) <= 1e-4
+
+
+def test_mlp_up_11008_nm_rows(sg, attn_oracle):
+    res = _run_layer(sg, "mlp_up_11008")
+    cfg = res["cfg"]
+    p = cfg.patterns[0]
+    Wh, mask = res["prune"][p]
+    gm, Whg = _check_counts_and_zeros(Wh, mask, p, cfg.blocksize)
+    U = attn_oracle["oracle"]["U"]  # same activations, same H and U
+    rows = np.random.default_rng(8).choice(cfg.m, 64, replace=False)
+    Wd = res["W"].cpu().double().numpy()[rows]
+    Who, Mo, _ = oracle.prune(Wd, U, p, cfg.blocksize)
+    agree = (gm[rows] == Mo).mean(axis=1)
+    assert agree.min() >= 0.995
+    Whf, _, _, tr = oracle.prune(Wd, U, p, cfg.blocksize, mask_in=gm[rows], return_trace=True)
+    _consistency(tr["saliency"], gm[rows], p, cfg.blocksize, across_rows=False)
+    assert _rel(Whg[rows], Whf) <= 1e-4
+    # reconstruction error of the sampled rows against the oracle's own W_hat
+    Hd_full = attn_oracle["oracle"]["H"]
+    E_gpu = oracle.reconstruction_error_from_hessian(Wd, Whg[rows], Hd_full)
+    E_o = oracle.reconstruction_error_from_hessian(Wd, Who, Hd_full)
+    assert abs(E_gpu - E_o) <= 1e-3 * E_o
+
+
+# ---------------------------------------------------------------------------
+# wide layers: properties that hold at any size
+# ---------------------------------------------------------------------------
+
+def _support_and_selection(Wd, Whg, g, U, pattern, B):
+    """Properties of a pruned row set that hold at any size (U from the GPU).
+
+    d = w - w_hat and e = d U^{-1}: the compensation applied to a row is a
+    combination of U's rows at its pruned columns, so e vanishes (to rounding)
+    on kept columns.  The value of weight j when its group or block was chosen
+    is w_j - sum_{i < j0} e_i U_ij = w_hat_j + sum_{j0 <= i <= j} e_i U_ij
+    (j0 = start of j's block or group), and its saliency is that squared over
+    U_jj^2; pruned saliencies must not exceed kept ones."""
+    d = Wd - Whg
+    e = scipy.linalg.solve_triangular(U, d.T, trans="T", lower=False).T
+    leak = np.linalg.norm(e[~g]) / np.linalg.norm(e[g])
+    assert leak <= 1e-3, f"compensation leaks onto kept columns: {leak:.2e}"
+    n = Wd.shape[1]
+    M = int(pattern.split(":")[1]) if ":" in pattern else B
+    diag = np.diag(U)
+    S_sel = np.empty_like(Wd)
+    for j0 in range(0, n, M):
+        j1 = min(n, j0 + M)
+        Ug = np.triu(U[j0:j1, j0:j1])
+        cur = Whg[:, j0:j1] + e[:, j0:j1] @ Ug
+        S_sel[:, j0:j1] = cur ** 2 / diag[j0:j1] ** 2
+    _consistency(S_sel, g, pattern, B, across_rows=":" not in pattern)
+
+
+def _diag_fp64(X):
+    """sum_t x_tc^2 in fp64 (plain torch reduction, chunked)."""
+    acc = torch.zeros(X.shape[1], dtype=torch.float64, device=X.device)
+    for t in range(0, X.shape[0], 16384):
+        acc += X[t:t + 16384].double().square().sum(0)
+    return acc.cpu().numpy()
+
+
+def _wide_checks(sg, name, trail=512, nrows=8):
+    res = _run_layer(sg, name)
+    cfg = res["cfg"]
+    X, n = res["X"], cfg.n
+    rng = np.random.default_rng(11)
+    # H on a channel sample
+    S = np.sort(rng.choice(n - trail, 40, replace=False))
+    idx = torch.from_numpy(S).cuda()
+    Hs = None
+    for t in range(0, X.shape[0], 65536):
+        xs = X[t:t + 65536].index_select(1, idx).double().cpu().numpy()
+        part = xs.T @ xs
+        Hs = part if Hs is None else Hs + part
+    Hg = res["H"].index_select(0, idx).index_select(1, idx).cpu().double().numpy()
+    assert _rel(Hg, Hs) <= 1e-5
+    # trailing block of U against the oracle factor of H_d's trailing block;
+    # lambda from the full diagonal, summed in fp64 from X
+    Ht = None
+    for t in range(0, X.shape[0], 65536):
+        xt = X[t:t + 65536, n - trail:].double().cpu().numpy()
+        part = xt.T @ xt
+        Ht = part if Ht is None else Ht + part
+    lam = cfg.damp * float(np.mean(_diag_fp64(X)))
+    Ut_o = oracle.inverse_upper_factor(Ht + lam * np.eye(trail))
+    Ut_g = res["Hinv"][n - trail:, n - trail:].cpu().double().numpy()
+    assert _rel(Ut_g, Ut_o) <= 1e-4
+    # prune properties on sampled rows
+    U = res["Hinv"].cpu().double().numpy()
+    rows = rng.choice(cfg.m, nrows, replace=False)
+    Wd = res["W"].cpu().double().numpy()[rows]
+    for p in cfg.patterns:
+        sys.stderr.write(f"[gpu-case] {name} pattern {p}\n")
+        sys.stderr.flush()
+        Wh, mask = res["prune"][p]
+        gm, Whg = _check_counts_and_zeros(Wh, mask, p, cfg.blocksize)
+        _support_and_selection(Wd, Whg[rows].astype(np.float64), gm[rows], U, p, cfg.blocksize)
+    return res
+
+
+def test_mlp_down_11008_properties(sg):
+    _wide_checks(sg, "mlp_down_11008")
+    _state.pop("mlp_down_11008", None)
+
+
+def test_mlp_down_28672_properties(sg):
+    for k in list(_state):
+        _state.pop(k)
+    torch.cuda.empty_cache()
+    _wide_checks(sg, "mlp_down_28672", nrows=4)
+    _state.pop("mlp_down_28672", None)
+    torch.cuda.empty_cache()
