@@ -13,6 +13,14 @@
 // When there are too few tiles to fill the 256 CUs the tokens are split; every
 // split writes its partial tile to the workspace and the last split to finish
 // sums all partials in split order (bitwise reproducible), then adds into H.
+//
+// Tile order: the hardware deals workgroups round-robin over the 8 XCDs, each
+// with its own L2.  Tiles are enumerated in g x g groups of panels (panel =
+// 256 channels), and XCD x takes a contiguous eighth of that order, split-major:
+// the workgroups resident on one XCD then work on a compact set of tiles that
+// share few panels, over the same token range, so most X re-reads hit its L2;
+// the XCDs run the same token range at the same time, which the shared
+// Infinity Cache serves once.
 #include "sg_internal.h"
 
 #include <math.h>
@@ -36,6 +44,36 @@ __device__ inline void tri_decode(int64_t ti, int& I, int& J) {
   J = (int)(ti - r * (r + 1) / 2);
 }
 
+// k-th tile of the grouped order: panel rows in blocks of g; inside a block
+// row BI, the off-diagonal g x g groups (BJ < BI) row-major, then the
+// diagonal group's lower triangle.
+__device__ inline void grouped_decode(int64_t k, int nt, int g, int& I, int& J) {
+  int64_t base = 0;
+  for (int BI = 0;; ++BI) {
+    const int r0 = BI * g;
+    const int gi = min(g, nt - r0);
+    const int64_t off = (int64_t)BI * gi * g;
+    const int64_t row = off + (int64_t)gi * (gi + 1) / 2;
+    if (k < base + row || r0 + gi >= nt) {
+      const int64_t rem = k - base;
+      if (rem < off) {
+        const int64_t per = (int64_t)gi * g;
+        const int BJ = (int)(rem / per);
+        const int r2 = (int)(rem - BJ * per);
+        I = r0 + r2 / g;
+        J = BJ * g + r2 % g;
+      } else {
+        int a, b;
+        tri_decode(rem - off, a, b);
+        I = r0 + a;
+        J = r0 + b;
+      }
+      return;
+    }
+    base += row;
+  }
+}
+
 __global__ void zero_u32_kernel(unsigned* p, int64_t cnt) {
   int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i < cnt) p[i] = 0u;
@@ -48,22 +86,28 @@ __device__ inline float agent_load(const float* p) {
 template <bool RAGGED>
 __global__ __launch_bounds__(HTHREADS) void hess_bf16_kernel(
     float* __restrict__ H, int n, const uint16_t* __restrict__ X, int64_t T,
-    int64_t ldx, int64_t tiles, int splits, int64_t tps,
+    int64_t ldx, int64_t tiles, int splits, int64_t tps, int group,
     float* __restrict__ part, unsigned* __restrict__ counters) {
   // Two LDS stages (double buffer), each holding the I-block and the J-block.
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][2 * HT * HROWB];
+  // Separate arrays, so the compiler can tell the stage being written from the
+  // stage being read and interleave the two.
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[2 * HT * HROWB];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[2 * HT * HROWB];
   __shared__ int s_last;
 
-  // Work items are split-major (item = split * tiles + tile) and taken in
-  // launch order: the workgroups resident at any time all stream the same
-  // token range, spread over all 8 XCDs, so each X slice is fetched from HBM
-  // once into the shared Infinity Cache.  (Grouping tiles per XCD to favour
-  // the per-XCD L2 measured slower.)
-  const int64_t item = blockIdx.x;
-  const int split = (int)(item / tiles);
-  const int64_t ti = item - (int64_t)split * tiles;
+  // XCD share: tiles [k0, k1) of the grouped order, times all splits,
+  // split-major.  Shares differ by at most one tile; the few workgroups past
+  // a short share exit at once.
+  const int xcd = blockIdx.x & 7;
+  const int64_t jx = blockIdx.x >> 3;
+  const int64_t k0 = tiles * xcd / 8, k1 = tiles * (xcd + 1) / 8;
+  const int64_t cnt = k1 - k0;
+  if (jx >= cnt * splits) return;
+  const int split = (int)(jx / cnt);
+  const int64_t ti = k0 + (jx - (int64_t)split * cnt);
+  const int64_t item = (int64_t)split * tiles + ti;
   int I, J;
-  tri_decode(ti, I, J);
+  grouped_decode(ti, (int)ceil_div((int64_t)n, HT), group, I, J);
   const bool diag = (I == J);
   const int i0 = I * HT, j0 = J * HT;
   const int64_t t_begin = (int64_t)split * tps;
@@ -75,12 +119,14 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_kernel(
   const int wi = wave >> 2;  // 128-row half of the tile
   const int wj = wave & 3;   // 64-column quarter
 
-  // Loader role: threads 0..255 stage the I-block, 256..511 the J-block (only
-  // for off-diagonal tiles), one 8 tokens x 8 channels block each per stage.
+  // Loader role: threads 0..255 stage the I-block, 256..511 the J-block (a
+  // second copy of the I-block on diagonal tiles, which keeps every step
+  // free of branches), one 8 tokens x 8 channels block each per stage.
   const int op = tid >> 8;
   const int tb = tid & 7;          // 8-token group inside the stage
   const int cb = (tid & 255) >> 3; // 8-channel group inside the tile
-  const bool loader = !(diag && op == 1);
+  const int colbase = (op == 0 ? i0 : j0) + cb * 8;
+  const bool colok = colbase < n;
 
   floatx4 acc[8][4];
 #pragma unroll
@@ -90,25 +136,19 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_kernel(
 
   u32x4 r[8];
 
-  // All loads of a stage are issued back to back from clamped, always
-  // in-bounds addresses (rows past the token range re-read the last row,
-  // channel groups past n re-read the last group); out-of-range data is
-  // zeroed only when the stage is written to LDS, so no load waits on another.
-  // Per stage one uniform base pointer (row t0) and 32-bit per-lane byte
-  // offsets: SGPR-base addressing, no 64-bit address registers.
-  // RAGGED (n not a multiple of 8) takes a per-element path instead.
+  // Generic stage load (first and last stages): clamped, always in-bounds
+  // addresses (rows past the token range re-read the last row, channel groups
+  // past n re-read the last group); out-of-range data is zeroed when the stage
+  // is written to LDS.  RAGGED (n not a multiple of 8) loads per element.
   auto gload = [&](int64_t t0) {
-    if (!loader) return;
     const char* base = reinterpret_cast<const char*>(X + t0 * ldx);
-    const bool partial = t0 + HBK > t_end;
-    const int last = (int)(t_end - 1 - t0);
-    const int colbase = (op == 0 ? i0 : j0) + cb * 8;
+    const int last = (int)min<int64_t>(HBK - 1, t_end - 1 - t0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       int tr = tb * 8 + i;
-      if (partial) tr = tr < last ? tr : last;
+      tr = tr < last ? tr : last;
       if constexpr (!RAGGED) {
-        const int colc = colbase < n ? colbase : n - 8;
+        const int colc = colok ? colbase : n - 8;
         const uint32_t off = (uint32_t)tr * (uint32_t)(ldx * 2) + (uint32_t)colc * 2u;
         r[i] = *reinterpret_cast<const u32x4*>(base + off);
       } else {
@@ -123,63 +163,119 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_kernel(
     }
   };
 
-  // Transpose the 8x8 block in registers and store it channel-major.
+  // Transpose the 8x8 block in registers and store it channel-major: one
+  // 16-byte LDS write per pair of channels (d selects channels 2d, 2d+1).
+  auto lstore_pair = [&](unsigned char* dst, int d) {
+    u32x4 lo, hi;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const uint32_t a0 = r[2 * qq][d], a1 = r[2 * qq + 1][d];
+      lo[qq] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+      hi[qq] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+    }
+    *reinterpret_cast<u32x4*>(dst + (cb * 8 + 2 * d) * HROWB + tb * 16) = lo;
+    *reinterpret_cast<u32x4*>(dst + (cb * 8 + 2 * d + 1) * HROWB + tb * 16) = hi;
+  };
+
   auto lstore = [&](int64_t t0, unsigned char* buf) {
-    if (!loader) return;
     unsigned char* dst = buf + op * HT * HROWB;
-    const bool colok = ((op == 0 ? i0 : j0) + cb * 8) < n;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const bool ok = colok && (t0 + tb * 8 + i) < t_end;
       if (!ok) r[i] = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      u32x4 lo, hi;
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const uint32_t a0 = r[2 * qq][d], a1 = r[2 * qq + 1][d];
-        lo[qq] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-        hi[qq] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-      }
-      *reinterpret_cast<u32x4*>(dst + (cb * 8 + 2 * d) * HROWB + tb * 16) = lo;
-      *reinterpret_cast<u32x4*>(dst + (cb * 8 + 2 * d + 1) * HROWB + tb * 16) = hi;
-    }
+    for (int d = 0; d < 4; ++d) lstore_pair(dst, d);
   };
 
+  // MFMA operands: lane l reads 16 bytes (8 tokens) of channel row l%16 at
+  // token offset 8*(l/16) inside the 32-token half ks of the stage.
+  const int koff = (lane >> 4) * 16;
+  const int arow = (wi * 128 + (lane & 15)) * HROWB + koff;
+  const int brow = HT * HROWB + (wj * 64 + (lane & 15)) * HROWB + koff;
+
   auto compute = [&](const unsigned char* buf, int ks) {
-    const unsigned char* la = buf;
-    const unsigned char* lb = diag ? buf : buf + HT * HROWB;
-    const int koff = ks * 64 + (lane >> 4) * 16;
     bf16x8 fb[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      fb[c] = *reinterpret_cast<const bf16x8*>(lb + (wj * 64 + c * 16 + (lane & 15)) * HROWB + koff);
+      fb[c] = *reinterpret_cast<const bf16x8*>(buf + brow + c * 16 * HROWB + ks * 64);
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
-      const bf16x8 fa =
-          *reinterpret_cast<const bf16x8*>(la + (wi * 128 + a * 16 + (lane & 15)) * HROWB + koff);
+      const bf16x8 fa = *reinterpret_cast<const bf16x8*>(buf + arow + a * 16 * HROWB + ks * 64);
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[c], acc[a][c], 0, 0, 0);
     }
   };
 
+  // Steady-state step (all tokens of the stages involved valid): compute
+  // stage s from `cur`, write stage s+1 (in registers) to `nxt`, fetch stage
+  // s+2 into registers.  No branches and no bounds selects; the scheduling
+  // groups interleave the LDS writes, the transposes and the global loads
+  // with the 64 MFMAs of the step so that they issue while the matrix core
+  // is busy.
+  const uint32_t loff =
+      (uint32_t)(tb * 8) * (uint32_t)(ldx * 2) + (uint32_t)(colok ? colbase : n - 8) * 2u;
+  auto fast_step = [&](const unsigned char* cur, unsigned char* nxt, int64_t t_load) {
+    // half 1: 32 MFMA (k = 0..31 of the stage) with their 12 operand reads,
+    // interleaved with the 32 transposes and 8 LDS writes of the next stage
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, 0);
+    unsigned char* dst = nxt + op * HT * HROWB;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) lstore_pair(dst, d);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (g < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // half 2: 32 MFMA (k = 32..63) with their operand reads, interleaved with
+    // the 8 global loads of stage s+2 (into the registers just written out)
+    const char* base = reinterpret_cast<const char*>(X + t_load * ldx);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      r[i] = *reinterpret_cast<const u32x4*>(base + (size_t)i * (size_t)(ldx * 2) + loff);
+    compute(cur, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      if (g < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  };
+
   // Software pipeline: stage s is computed from LDS buffer s%2 while stage
-  // s+1 (already in registers) is written to the other buffer half-way
-  // through, and stage s+2 is then fetched into registers.  One barrier per
-  // stage.
+  // s+1 (already in registers) is written to the other buffer, and stage s+2
+  // is fetched into registers.  One barrier per stage.
   const int64_t ntok = t_end > t_begin ? t_end - t_begin : 0;
   const int64_t nsteps = ceil_div(ntok, HBK);
+  const int64_t nfull = ntok / HBK;
   if (nsteps > 0) {
     gload(t_begin);
-    lstore(t_begin, lds[0]);
+    lstore(t_begin, lds0);
     if (nsteps > 1) gload(t_begin + HBK);
     __syncthreads();
   }
-  for (int64_t step = 0; step < nsteps; ++step) {
-    unsigned char* cur = lds[step & 1];
-    unsigned char* nxt = lds[(step + 1) & 1];
+  int64_t step = 0;
+  if constexpr (!RAGGED) {
+    // pairs of steady-state steps: step s + 2 (and s + 3) must be full stages
+    for (; step + 3 < nfull; step += 2) {
+      fast_step(lds0, lds1, t_begin + (step + 2) * HBK);
+      fast_step(lds1, lds0, t_begin + (step + 3) * HBK);
+    }
+  }
+  for (; step < nsteps; ++step) {
+    unsigned char* cur = (step & 1) ? lds1 : lds0;
+    unsigned char* nxt = (step & 1) ? lds0 : lds1;
     compute(cur, 0);
     if (step + 1 < nsteps) {
       lstore(t_begin + (step + 1) * HBK, nxt);
@@ -237,6 +333,241 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_kernel(
         const float val = H[lo] + acc[a][c][v];
         H[lo] = val;
         if (row != col) H[(size_t)col * n + row] = val;
+      }
+}
+
+// bf16 path for n % 8 == 0: the same tiles and wave layout, with the X
+// stages copied straight from global memory into LDS by the LDS-DMA loads
+// (no register staging, no transposes in VALU).  A stage is 32 tokens; in
+// LDS each token is one 1040-byte row holding the tile's I-panel (256
+// channels) and J-panel (256 channels) as they lie in X, plus 16 bytes of
+// padding so that consecutive tokens start 16 bytes apart in the LDS banks.
+// MFMA operands (8 consecutive tokens of one channel per lane) are read with
+// the transposing LDS read, which gathers 4 tokens x 4 channels across 16
+// lanes.  Four stages rotate, three in flight while the fourth is multiplied.
+constexpr int DK = 32;                       // tokens per stage
+constexpr int DROW = 2 * HT * 2 + 16;        // LDS bytes per token row
+constexpr int DSTAGE = DK * DROW;            // 33280 bytes per stage
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+
+// s_waitcnt immediates that wait for the vector-memory counter only.
+constexpr unsigned kWaitVm0 = 0x0F70u;
+constexpr unsigned kWaitVm4 = 0x0F74u;
+constexpr unsigned kWaitVm8 = 0x0F78u;
+
+// Workgroup barrier without a memory fence: a fence would also wait for the
+// stages still in flight.  LDS visibility is ordered by hand (each wave waits
+// for its own copies of a stage before the barrier that publishes it); the
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ inline void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
+    float* __restrict__ H, int n, const uint16_t* __restrict__ X, int64_t T,
+    int64_t ldx, int64_t tiles, int splits, int64_t tps, int group,
+    float* __restrict__ part, unsigned* __restrict__ counters) {
+  // One array per stage, so the compiler can tell which stage a read touches
+  // and waits only for the copies into that stage.
+  __shared__ __attribute__((aligned(16))) unsigned char st0[DSTAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[DSTAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st2[DSTAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char st3[DSTAGE];
+  __shared__ int s_last;
+
+  const int xcd = blockIdx.x & 7;
+  const int64_t jx = blockIdx.x >> 3;
+  const int64_t k0 = tiles * xcd / 8, k1 = tiles * (xcd + 1) / 8;
+  const int64_t cnt = k1 - k0;
+  if (jx >= cnt * splits) return;
+  const int split = (int)(jx / cnt);
+  const int64_t ti = k0 + (jx - (int64_t)split * cnt);
+  const int64_t item = (int64_t)split * tiles + ti;
+  int I, J;
+  grouped_decode(ti, (int)ceil_div((int64_t)n, HT), group, I, J);
+  const bool diag = (I == J);
+  const int i0 = I * HT, j0 = J * HT;
+  const int64_t t_begin = (int64_t)split * tps;
+  const int64_t t_end = min(T, t_begin + tps);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wi = wave >> 2;
+  const int wj = wave & 3;
+
+  floatx4 acc[8][4];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[a][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // Copy role: wave w copies token rows 4w..4w+3 of every stage, one row per
+  // instruction; lanes 0..31 fetch the I-panel's 32 16-byte chunks, lanes
+  // 32..63 the J-panel's (on diagonal tiles a second copy of the I-panel).
+  // Channel chunks past n re-read the last chunk: those channels only feed
+  // outputs beyond n, which are never stored.
+  int col = ((lane >> 5) ? j0 : i0) + (lane & 31) * 8;
+  col = col < n ? col : n - 8;
+  const uint32_t dcol = (uint32_t)col * 2u;
+  auto copy_stage = [&](unsigned char* buf, int64_t s) {
+    const int64_t tok0 = t_begin + s * DK + wave * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int64_t t = tok0 + j;
+      t = t < t_end ? t : t_end - 1;  // rows past the end are zeroed later
+      const char* src = reinterpret_cast<const char*>(X) + t * ldx * 2 + dcol;
+      __builtin_amdgcn_global_load_lds((const global_void*)src,
+                                       (lds_void*)(buf + (wave * 4 + j) * DROW), 16, 0, 0);
+    }
+  };
+
+  // Operand addresses: lane l of a transposing read points at token row
+  // 8*(l/16) + (l%16)/4 (+4 for the second read) and channel quad l%4 of the
+  // 16-channel fragment; lane i of the result then holds channel i of the
+  // fragment over those 4 tokens.
+  const int s16 = lane & 15;
+  const int trow = 8 * (lane >> 4) + (s16 >> 2);
+  const int q4 = 4 * (s16 & 3);
+  const uint32_t a_off = (uint32_t)(trow * DROW + (wi * 128 + q4) * 2);
+  const uint32_t b_off = (uint32_t)(trow * DROW + HT * 2 + (wj * 64 + q4) * 2);
+
+  auto frag = [&](const unsigned char* buf, uint32_t off) {
+    const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(buf + off));
+    const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(buf + off + 4 * DROW));
+    const shortx8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  auto compute = [&](const unsigned char* buf) {
+    bf16x8 fb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) fb[c] = frag(buf, b_off + c * 32);
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const bf16x8 fa = frag(buf, a_off + a * 32);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[c], acc[a][c], 0, 0, 0);
+    }
+  };
+
+  const int64_t ntok = t_end > t_begin ? t_end - t_begin : 0;
+  const int64_t nsteps = ceil_div(ntok, DK);
+  if (nsteps > 0) copy_stage(st0, 0);
+  if (nsteps > 1) copy_stage(st1, 1);
+  if (nsteps > 2) copy_stage(st2, 2);
+
+  // Step s: wait for this wave's copies of stage s (stages s+1 and s+2 may
+  // stay in flight), barrier (stage s complete in LDS; every wave is done
+  // with stage s-1), start copying stage s+3 into the buffer of stage s-1,
+  // multiply stage s.
+  auto step = [&](const unsigned char* cur, unsigned char* refill, int64_t s) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    stage_barrier();
+    copy_stage(refill, s + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur);
+    // operand reads two fragments ahead of the MFMAs that use them
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (g < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int64_t s = 0;
+  // Unrolled by 8 so that every read names its stage array; at the loop
+  // head the compiler loses track of which copies are still in flight and
+  // waits for all of them once per iteration.
+  for (; s + 10 < nsteps; s += 8) {
+    step(st0, st3, s);
+    step(st1, st0, s + 1);
+    step(st2, st1, s + 2);
+    step(st3, st2, s + 3);
+    step(st0, st3, s + 4);
+    step(st1, st0, s + 5);
+    step(st2, st1, s + 6);
+    step(st3, st2, s + 7);
+  }
+  for (; s < nsteps; ++s) {
+    const int b = (int)(s & 3);
+    unsigned char* cur = b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3;
+    unsigned char* refill = b == 0 ? st3 : b == 1 ? st0 : b == 2 ? st1 : st2;
+    const int64_t later = nsteps - 1 - s;
+    if (later >= 2)
+      __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    stage_barrier();
+    const int valid = (int)min<int64_t>(DK, ntok - s * DK);
+    if (valid < DK) {
+      // last, partial stage: zero the token rows past the end
+      for (int e = tid; e < (DK - valid) * (DROW / 16); e += HTHREADS) {
+        const int row = valid + e / (DROW / 16);
+        *reinterpret_cast<u32x4*>(cur + row * DROW + (e % (DROW / 16)) * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    }
+    if (s + 3 < nsteps) copy_stage(refill, s + 3);
+    compute(cur);
+  }
+
+  // ---- epilogue (same layout as the register-staged kernel) ---------------
+  if (splits > 1) {
+    floatx4* mine = reinterpret_cast<floatx4*>(part + (size_t)item * (HT * HT));
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mine[(wave * 32 + a * 4 + c) * 64 + lane] = acc[a][c];
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned old = atomicAdd(&counters[ti], 1u);
+      s_last = (old == (unsigned)(splits - 1)) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    for (int sp = 0; sp < splits; ++sp) {
+      const floatx4* other =
+          reinterpret_cast<const floatx4*>(part + ((size_t)sp * tiles + ti) * (HT * HT));
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        floatx4 pv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) pv[c] = other[(wave * 32 + a * 4 + c) * 64 + lane];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = (sp == 0) ? pv[c] : acc[a][c] + pv[c];
+      }
+    }
+    if (tid == 0) counters[ti] = 0u;
+  }
+
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = i0 + wi * 128 + a * 16 + (lane >> 4) * 4 + v;
+        const int col2 = j0 + wj * 64 + c * 16 + (lane & 15);
+        if (row >= n || col2 >= n) continue;
+        if (diag && row < col2) continue;
+        const size_t lo = (size_t)row * n + col2;
+        const float val = H[lo] + acc[a][c][v];
+        H[lo] = val;
+        if (row != col2) H[(size_t)col2 * n + row] = val;
       }
 }
 
@@ -323,6 +654,12 @@ HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws) {
   // Recompute the split count actually needed with the rounded split size.
   p.splits = (int)std::max<int64_t>(1, ceil_div(T, p.tok_per_split));
   p.ws_bytes = p.splits > 1 ? cnt_bytes + tile_bytes * (size_t)p.tiles * p.splits : 0;
+  // Group edge: about the square root of the tiles an XCD has resident at once
+  // (its 32 CUs, or its whole share when that is smaller).
+  const double per_xcd = std::min<double>(32.0, (double)p.tiles * p.splits / 8.0) /
+                         std::max(1, std::min(p.splits, 2));
+  p.group = (int)std::max<int64_t>(1, std::min<int64_t>(nt, (int64_t)std::lround(std::sqrt(per_xcd))));
+  p.grid = 8 * ceil_div(p.tiles, 8) * p.splits;
   return p;
 }
 
@@ -339,13 +676,15 @@ sg_status launch_hessian_bf16(float* H, int64_t n, const uint16_t* X, int64_t T,
                        0, st, counters, plan.tiles);
     if (sg_status e = check_launch("hessian counters")) return e;
   }
-  const int64_t grid = plan.tiles * plan.splits;
+  const int64_t grid = plan.grid;
   if (n % 8 == 0)
-    hipLaunchKernelGGL(hess_bf16_kernel<false>, dim3((unsigned)grid), dim3(HTHREADS), 0, st, H,
-                       (int)n, X, T, ldx, plan.tiles, plan.splits, plan.tok_per_split, part, counters);
+    hipLaunchKernelGGL(hess_bf16_dma_kernel, dim3((unsigned)grid), dim3(HTHREADS), 0, st, H,
+                       (int)n, X, T, ldx, plan.tiles, plan.splits, plan.tok_per_split, plan.group,
+                       part, counters);
   else
     hipLaunchKernelGGL(hess_bf16_kernel<true>, dim3((unsigned)grid), dim3(HTHREADS), 0, st, H,
-                       (int)n, X, T, ldx, plan.tiles, plan.splits, plan.tok_per_split, part, counters);
+                       (int)n, X, T, ldx, plan.tiles, plan.splits, plan.tok_per_split, plan.group,
+                       part, counters);
   return check_launch("hessian bf16");
 }
 

@@ -40,6 +40,8 @@ struct HessPlan {
   int64_t tiles;       // lower-triangle 256x256 tiles
   int splits;          // token splits
   int64_t tok_per_split;
+  int group;           // tile-panel group edge of the per-XCD tile order
+  int64_t grid;        // workgroups launched (8 equal per-XCD shares)
   size_t ws_bytes;     // partials + counters
 };
 HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws);

@@ -36,10 +36,14 @@ TAU = 1e-3
 _state = {}
 
 
+def _say(msg):
+    sys.stderr.write(f"[gpu-case] {msg}\n")
+    sys.stderr.flush()
+
+
 @pytest.fixture(autouse=True)
 def _announce(request):
-    sys.stderr.write(f"\n[gpu-case] {request.node.nodeid}\n")
-    sys.stderr.flush()
+    _say(request.node.nodeid)
     yield
 
 
@@ -67,6 +71,7 @@ def _run_layer(sg, name):
     else:
         X = synth.make_x(cfg, "cuda")
     W = synth.make_weight(cfg, "cuda")
+    _say(f"{name}: m={cfg.m} n={cfg.n} T={X.shape[0]} H / factor / prune")
     H = torch.zeros(cfg.n, cfg.n, device="cuda")
     sg.sg_hessian_accumulate(H, X)
     Hinv, info = sg.sg_prepare_hinv(H, cfg.damp)
@@ -131,6 +136,7 @@ def _consistency(S, gmask, pattern, B, across_rows):
 def attn_oracle(sg):
     res = _run_layer(sg, "attn_4096")
     if "oracle" not in res:
+        _say("attn_4096: fp64 oracle H and U on the host")
         H = _oracle_H_full(res["X"])
         Hd, lam = oracle.dampen(H, res["cfg"].damp)
         res["oracle"] = {"H": H, "U": oracle.inverse_upper_factor(Hd), "lam": lam}
@@ -235,6 +241,7 @@ def _wide_checks(sg, name, trail=512, nrows=8):
         Hs = part if Hs is None else Hs + part
     Hg = res["H"].index_select(0, idx).index_select(1, idx).cpu().double().numpy()
     assert _rel(Hg, Hs) <= 1e-5
+    _say(f"{name}: trailing block of U")
     # trailing block of U against the oracle factor of H_d's trailing block;
     # lambda from the full diagonal, summed in fp64 from X
     Ht = None
@@ -251,8 +258,7 @@ def _wide_checks(sg, name, trail=512, nrows=8):
     rows = rng.choice(cfg.m, nrows, replace=False)
     Wd = res["W"].cpu().double().numpy()[rows]
     for p in cfg.patterns:
-        sys.stderr.write(f"[gpu-case] {name} pattern {p}\n")
-        sys.stderr.flush()
+        _say(f"{name} pattern {p} properties")
         Wh, mask = res["prune"][p]
         gm, Whg = _check_counts_and_zeros(Wh, mask, p, cfg.blocksize)
         _support_and_selection(Wd, Whg[rows].astype(np.float64), gm[rows], U, p, cfg.blocksize)
