@@ -24,8 +24,6 @@
 //   lazy     W[:, i2:] -= Err * U[i1:i2, i2:] on fp32 MFMA (K = w).
 #include "gemm_f32.h"
 
-#include <hip/hip_cooperative_groups.h>
-
 #include <math.h>
 
 #include <type_traits>
@@ -35,15 +33,19 @@ namespace sg {
 namespace {
 
 constexpr int SB = SG_MAX_BLOCKSIZE;  // 128
-constexpr int SW_ROWS = 16;           // rows per sweep workgroup
 
 enum { MODE_THRESH = 0, MODE_NM = 1, MODE_FORCED = 2 };
 
+// Radix-select buffers, double-buffered by block parity: the sweep of block b
+// clears the set block b + 1 will use while nobody reads it.
+struct SelSet {
+  unsigned hist0[kSelBins];   // top 11 bits of every key
+  unsigned hist1[kSelBins];   // next 11 bits of the keys under the top digit
+  unsigned ncand;             // keys gathered under the top digit
+  unsigned pad[63];
+};
 struct SelState {
-  unsigned long long thresh;
-  unsigned done;  // 1 thresh valid, 2 none selected, 3 all selected
-  unsigned pad;
-  unsigned hist[3][kSelBins];  // per-pass merged histograms, used round-robin
+  SelSet set[2];
 };
 
 __device__ inline float saliency(float w, float ucc) {
@@ -70,159 +72,278 @@ __global__ void convert_kernel(float* __restrict__ out, const void* __restrict__
   }
 }
 
-__global__ void sel_clear_kernel(SelState* st) {
-  for (int b = threadIdx.x; b < 3 * kSelBins; b += blockDim.x) (&st->hist[0][0])[b] = 0u;
+__device__ inline void sel_clear_set(SelSet& s, int tid, int nthreads) {
+  for (int b = tid; b < kSelBins; b += nthreads) {
+    s.hist0[b] = 0u;
+    s.hist1[b] = 0u;
+  }
+  if (tid == 0) s.ncand = 0u;
 }
 
-// Exact k-th smallest 64-bit key of the m x w block by radix select, all
-// passes in one cooperative launch.  Every thread computes the keys of its
-// (at most SEL_KPT) elements once and keeps them in registers.  Each pass
-// histograms one digit of the keys that still match the prefix fixed so far
-// (eight lane-interleaved LDS sub-histograms against atomic contention on
-// hot bins, merged into a global one); after a grid-wide sync every
-// workgroup scans the merged histogram itself and fixes the same digit.
-// hist[p % 3] is used by pass p; workgroup 0 clears the next pass's buffer
-// during the current pass (its readers finished two syncs earlier).  hist[0]
-// must be zero on entry; the sweep kernel that follows re-clears all three.
-constexpr int SEL_KPT = 32;   // keys per thread held in registers
-constexpr int SEL_SUB = 8;    // LDS sub-histograms
+__global__ void sel_clear_kernel(SelState* st) {
+  sel_clear_set(st->set[0], threadIdx.x, blockDim.x);
+  sel_clear_set(st->set[1], threadIdx.x, blockDim.x);
+}
 
-__global__ __launch_bounds__(256) void select_kernel(SelState* st, const float* __restrict__ W,
-                                                    const float* __restrict__ U, int64_t m,
-                                                    int64_t n, int64_t i1, int w, long long k) {
-  namespace cg = cooperative_groups;
-  cg::grid_group grid = cg::this_grid();
-  __shared__ unsigned h[SEL_SUB][kSelBins];
-  __shared__ unsigned wsum[4];
-  __shared__ unsigned long long s_prefix;
-  __shared__ long long s_krem;
-  __shared__ unsigned s_done;
-  __shared__ unsigned long long s_thresh;
+// Exact k-th smallest 64-bit key (bits(W^2 / U_cc^2) << 32 | r*n + c) of the
+// m x w block, radix select with 11-bit digits, saliency bits first:
+//   pass 0  every workgroup histograms the top digit of its keys (eight
+//           lane-interleaved LDS sub-histograms against contention on hot
+//           bins) and adds it into the block's global histogram;
+//   pass 1  every workgroup scans that histogram itself (2048 bins), fixes the
+//           top digit, histograms the next digit of the keys under it and
+//           gathers those keys into a candidate list;
+//   sweep   every sweep workgroup scans the second histogram, fixes the second
+//           digit, and either takes the whole bucket or sorts the keys under
+//           both digits (gathered from the candidate list) in LDS and reads
+//           off the one of the remaining rank.
+// No workgroup waits for another: each kernel consumes what the previous one
+// completed.
+constexpr int SEL_KPT = 32;    // keys per thread
+constexpr int SEL_SUB = 8;     // LDS sub-histograms
+constexpr int SEL_SORT = 8192; // keys sorted in LDS
+
+// Scan of a 2048-bin histogram (256 threads, thread t owns bins 8t..8t+7):
+// the bin holding the krem-th key, the keys before it and its count, in LDS.
+struct HistPick {
+  unsigned digit, cnt;
+  unsigned long long before;
+  unsigned wsum[4];
+};
+
+__device__ void hist_locate(const unsigned* hist, long long krem, HistPick& P) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long long total = m * (long long)w;
-  if (tid == 0) {
-    s_prefix = 0ull;
-    s_krem = k;
-    s_done = (k <= 0) ? 2u : (k >= total ? 3u : 0u);
-    s_thresh = 0ull;
+  constexpr int per = kSelBins / 256;
+  unsigned cnt[per];
+  unsigned local = 0;
+#pragma unroll
+  for (int i = 0; i < per; ++i) {
+    cnt[i] = hist[tid * per + i];
+    local += cnt[i];
   }
-  // keys of this thread: column c, rows rb + u * rstep (u < SEL_KPT)
+  unsigned incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) P.wsum[wave] = incl;
+  __syncthreads();
+  unsigned wbase = 0;
+  for (int wv = 0; wv < wave; ++wv) wbase += P.wsum[wv];
+  unsigned long long cum = (unsigned long long)(wbase + incl - local);
+  const unsigned long long after = (unsigned long long)(wbase + incl);
+  if ((long long)cum < krem && krem <= (long long)after) {
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      const unsigned cn = cnt[i];
+      if ((long long)cum < krem && (long long)(cum + cn) >= krem) {
+        P.digit = (unsigned)(tid * per + i);
+        P.before = cum;
+        P.cnt = cn;
+      }
+      cum += cn;
+    }
+  }
+  __syncthreads();
+}
+
+struct SelLds {
+  unsigned h[SEL_SUB][kSelBins];
+  unsigned long long stage[SEL_SORT];
+  unsigned nstage;
+  unsigned gbase;
+  HistPick pick;
+};
+
+__global__ __launch_bounds__(256) void select_pass_kernel(SelSet* ss, unsigned long long* cand,
+                                                         const float* __restrict__ W,
+                                                         const float* __restrict__ U, int64_t m,
+                                                         int64_t n, int64_t i1, int w, long long k,
+                                                         int pass) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  SelLds& L = *reinterpret_cast<SelLds*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int b = tid; b < SEL_SUB * kSelBins; b += 256) (&L.h[0][0])[b] = 0u;
+  if (tid == 0) L.nstage = 0u;
+  unsigned top = 0;
+  if (pass == 1) {
+    hist_locate(ss->hist0, k, L.pick);  // (includes a barrier)
+    top = L.pick.digit;
+  }
+  const int shift = pass == 0 ? 53 : 42;
+  const unsigned dmask = (1u << 11) - 1u;
   const int c = tid & 127;
   const int cc = c < w ? c : w - 1;
   const int64_t col = i1 + cc;
   const float ucc = U[col * n + col];
   const int64_t rstep = (int64_t)gridDim.x * 2;
   const int64_t rb = (int64_t)blockIdx.x * 2 + (tid >> 7);
-  unsigned long long keys[SEL_KPT];
-  {
-    float wv[SEL_KPT];
+  float wv[SEL_KPT];
 #pragma unroll
-    for (int u = 0; u < SEL_KPT; ++u) {
-      const int64_t r = rb + u * rstep;
-      wv[u] = W[(r < m ? r : m - 1) * n + col];
-    }
+  for (int u = 0; u < SEL_KPT; ++u) {
+    const int64_t r = rb + u * rstep;
+    wv[u] = W[(r < m ? r : m - 1) * n + col];
+  }
+  __syncthreads();
+  unsigned* hsub = L.h[lane & (SEL_SUB - 1)];
 #pragma unroll
-    for (int u = 0; u < SEL_KPT; ++u) {
-      const int64_t r = rb + u * rstep;
-      // out-of-range slots get the largest key, which never matches a prefix
-      keys[u] = (r < m && c < w) ? sal_key(wv[u], ucc, (uint32_t)(r * n + col)) : ~0ull;
+  for (int u = 0; u < SEL_KPT; ++u) {
+    const int64_t r = rb + u * rstep;
+    if (r < m && c < w) {
+      const unsigned long long key = sal_key(wv[u], ucc, (uint32_t)(r * n + col));
+      if (pass == 0 || (unsigned)(key >> 53) == top) {
+        atomicAdd(&hsub[(unsigned)(key >> shift) & dmask], 1u);
+        if (pass == 1) L.stage[atomicAdd(&L.nstage, 1u)] = key;
+      }
     }
   }
   __syncthreads();
-  static const int shifts[6] = {53, 42, 32, 21, 10, 0};
-  static const int widths[6] = {11, 11, 10, 11, 11, 10};
-  unsigned* hsub = h[lane & (SEL_SUB - 1)];
-  for (int p = 0; p < 6; ++p) {
-    if (s_done != 0u) break;  // uniform across the grid
-    const int shift = shifts[p], width = widths[p];
-    const int hi = shift + width;
-    const unsigned dmask = (1u << width) - 1u;
-    const unsigned long long prefix = s_prefix;
-    unsigned* gh = st->hist[p % 3];
-    if (blockIdx.x == 0)
-      for (int b = tid; b < kSelBins; b += 256) st->hist[(p + 1) % 3][b] = 0u;
-    for (int b = tid; b < SEL_SUB * kSelBins; b += 256) (&h[0][0])[b] = 0u;
+  unsigned* gh = pass == 0 ? ss->hist0 : ss->hist1;
+  for (int b = tid; b < kSelBins; b += 256) {
+    unsigned v = 0;
+#pragma unroll
+    for (int sh = 0; sh < SEL_SUB; ++sh) v += L.h[sh][b];
+    if (v) atomicAdd(&gh[b], v);
+  }
+  if (pass == 1) {
+    // this workgroup's gathered keys to the candidate list (one reservation)
+    if (tid == 0) L.gbase = atomicAdd(&ss->ncand, L.nstage);
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < SEL_KPT; ++u) {
-      const unsigned long long key = keys[u];
-      if (key != ~0ull && (hi >= 64 || (key >> hi) == (prefix >> hi)))
-        atomicAdd(&hsub[(unsigned)(key >> shift) & dmask], 1u);
-    }
+    for (unsigned i = tid; i < L.nstage; i += 256) cand[L.gbase + i] = L.stage[i];
+  }
+}
+
+// Threshold key of the block from the two histograms and the candidates
+// (run by every sweep workgroup; `scratch` holds SEL_SORT keys of LDS).
+__device__ unsigned long long select_finish(const SelSet& ss, const unsigned long long* cand,
+                                            long long k, unsigned long long* scratch,
+                                            unsigned* s_cnt, HistPick& P) {
+  const int tid = threadIdx.x;
+  hist_locate(ss.hist0, k, P);
+  const unsigned d0 = P.digit;
+  const long long k1 = k - (long long)P.before;
+  hist_locate(ss.hist1, k1, P);
+  const unsigned long long pf = ((unsigned long long)d0 << 53) | ((unsigned long long)P.digit << 42);
+  long long kr = k1 - (long long)P.before;
+  const unsigned cnt = P.cnt;
+  if ((long long)cnt == kr) return pf | ((1ull << 42) - 1ull);  // the bucket is taken whole
+  const unsigned ncand = ss.ncand;
+  const unsigned long long fmask2 = ~((1ull << 42) - 1ull);
+  if (cnt <= (unsigned)SEL_SORT) {
+    if (tid == 0) *s_cnt = 0u;
     __syncthreads();
-    for (int b = tid; b < kSelBins; b += 256) {
-      unsigned v = 0;
+    // candidates read 16 per thread at a time, all loads in flight together
+    for (unsigned base = 0; base < ncand; base += 256 * 16) {
+      unsigned long long kv[16];
 #pragma unroll
-      for (int sh = 0; sh < SEL_SUB; ++sh) v += h[sh][b];
-      if (v) atomicAdd(&gh[b], v);
-    }
-    grid.sync();
-    // every workgroup: locate the digit holding the krem-th smallest key;
-    // thread t owns bins 8t..8t+7, prefix sums by wave shuffles
-    const int per = kSelBins / 256;
-    unsigned cnt[per];
-    unsigned local = 0;
+      for (int u = 0; u < 16; ++u) {
+        const unsigned i = base + u * 256 + tid;
+        kv[u] = cand[i < ncand ? i : ncand - 1];
+      }
 #pragma unroll
-    for (int i = 0; i < per; ++i) {
-      cnt[i] = gh[tid * per + i];
-      local += cnt[i];
-    }
-    unsigned incl = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const unsigned v = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += v;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    unsigned wbase = 0;
-    for (int wv2 = 0; wv2 < wave; ++wv2) wbase += wsum[wv2];
-    const long long krem = s_krem;
-    const unsigned long long before = (unsigned long long)(wbase + incl - local);
-    const unsigned long long after = (unsigned long long)(wbase + incl);
-    __syncthreads();
-    if ((long long)before < krem && krem <= (long long)after) {
-      unsigned long long cum = before;
-#pragma unroll
-      for (int i = 0; i < per; ++i) {
-        const unsigned cn = cnt[i];
-        if ((long long)cum < krem && (long long)(cum + cn) >= krem) {
-          const unsigned d = (unsigned)(tid * per + i);
-          const unsigned long long np = prefix | ((unsigned long long)d << shift);
-          const long long nk = krem - (long long)cum;
-          s_prefix = np;
-          s_krem = nk;
-          if ((long long)cn == nk || shift == 0) {
-            // the bucket is taken whole: every key up to the end of its range
-            s_thresh = np | ((shift > 0) ? ((1ull << shift) - 1ull) : 0ull);
-            s_done = 1u;
-          }
-        }
-        cum += cn;
+      for (int u = 0; u < 16; ++u) {
+        const unsigned i = base + u * 256 + tid;
+        if (i < ncand && (kv[u] & fmask2) == pf) scratch[atomicAdd(s_cnt, 1u)] = kv[u];
       }
     }
     __syncthreads();
+    const unsigned got = *s_cnt;
+    unsigned sz = 1;
+    while (sz < got) sz <<= 1;
+    for (unsigned i = got + tid; i < sz; i += 256) scratch[i] = ~0ull;
+    __syncthreads();
+    for (unsigned kk = 2; kk <= sz; kk <<= 1) {
+      for (unsigned j = kk >> 1; j > 0; j >>= 1) {
+        for (unsigned i = tid; i < sz; i += 256) {
+          const unsigned ixj = i ^ j;
+          if (ixj > i) {
+            const unsigned long long a = scratch[i], b = scratch[ixj];
+            if ((a > b) == ((i & kk) == 0)) {
+              scratch[i] = b;
+              scratch[ixj] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    const unsigned long long t = scratch[kr - 1];
+    __syncthreads();
+    return t;
   }
-  if (blockIdx.x == 0 && tid == 0) {
-    st->done = s_done;
-    st->thresh = s_thresh;
+  // too many keys under both digits to sort: radix passes over the list,
+  // with the first 2048 words of scratch as the histogram
+  unsigned* h = reinterpret_cast<unsigned*>(scratch);
+  unsigned long long p2 = pf;
+  static constexpr int kShift[4] = {32, 21, 10, 0};
+  static constexpr int kWidth[4] = {10, 11, 11, 10};
+  for (int p = 0; p < 4; ++p) {
+    const int sh = kShift[p];
+    const unsigned dm = (1u << kWidth[p]) - 1u;
+    const unsigned long long fm = ~((1ull << (sh + kWidth[p])) - 1ull);
+    for (int b = tid; b < kSelBins; b += 256) h[b] = 0u;
+    __syncthreads();
+    for (unsigned base = 0; base < ncand; base += 256 * 16) {
+      unsigned long long kv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const unsigned i = base + u * 256 + tid;
+        kv[u] = cand[i < ncand ? i : ncand - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const unsigned i = base + u * 256 + tid;
+        if (i < ncand && (kv[u] & fm) == p2) atomicAdd(&h[(unsigned)(kv[u] >> sh) & dm], 1u);
+      }
+    }
+    __syncthreads();
+    hist_locate(h, kr, P);
+    p2 |= (unsigned long long)P.digit << sh;
+    kr -= (long long)P.before;
+    if ((long long)P.cnt == kr || sh == 0) {
+      const unsigned long long t = p2 | ((sh > 0) ? ((1ull << sh) - 1ull) : 0ull);
+      __syncthreads();
+      return t;
+    }
+    __syncthreads();
   }
+  return ~0ull;  // not reached
 }
 
-template <int L>
-__device__ inline float bcast16_c(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + L, 0xF, 0xF, false));
-}
+// ---- in-block sweep ---------------------------------------------------------
+// One wave per 16 rows; the block's columns are held in registers as eight
+// 16x16 tiles in the fp32 MFMA accumulator layout (lane l, register v: row
+// 4*(l/16) + v, column l%16 of the tile).  Per 16-column chunk c:
+//   * the 16 columns are swept in order: the owner lanes (column j of the
+//     chunk) compute e = W[r,J] / U_JJ for pruned entries, a DPP row
+//     broadcast hands e to the other 15 lanes of the row, which subtract
+//     e * U[J, col] (U is zero left of the diagonal, so earlier columns are
+//     untouched);
+//   * the chunk's errors E_c (16 x 16) then update every later chunk at once,
+//     W[:, c'] -= E_c U[c, c'], on v_mfma_f32_16x16x4_f32 (E_c goes through a
+//     small per-wave LDS tile to reach the A-operand layout).
+// This is the same computation as the column-by-column OBS sweep, with the
+// updates of later chunks batched (they only add into columns not yet
+// reached).  The U block (upper triangle, zero elsewhere) sits in LDS.
+constexpr int SWS = SB + 4;  // LDS row stride of the U block (floats)
+constexpr int ESS = 20;      // per-wave E tile row stride (floats)
 
 struct SweepLds {
-  float Ub[SB * SB];
-  float Rd[SB];
-  float Sc[SW_ROWS * SB];
+  float Ub[SB * SWS];
+  float Rd[SB];          // 1 / U_JJ (0 past the block)
+  float Es[4][16 * ESS];
+  float Tw[4][16 * SWS]; // per-wave 16 x 128 staging tile (row-major), N:M scratch
 };
 
-// Rank of key (my, me) among the group's keys sal[0..cnt) -- lexicographic
-// (saliency, position), so equal saliencies prune the lower column first.
-__device__ __forceinline__ int group_rank(const float* sal, int cnt, float my, int me) {
+// Lane L of every 16-lane row to the whole row (DPP row_newbcast).
+template <int L>
+__device__ inline float bcast16_c(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + L, 0xF, 0xF, true));
+}
+
+// lexicographic (saliency, position) rank among cnt values
+__device__ __forceinline__ int rank_of(const float* sal, int cnt, float my, int me) {
   int rank = 0;
   for (int t = 0; t < cnt; ++t) {
     const float o = sal[t];
@@ -231,182 +352,364 @@ __device__ __forceinline__ int group_rank(const float* sal, int cnt, float my, i
   return rank;
 }
 
-struct SweepCtx {
-  float* sc;       // per-row scratch of the N:M ranking
-  const float* Ub; // U block in LDS
-  const float* Rd; // reciprocal diagonal in LDS
-  int q, w, mgroup, nkeep, sb;
-  bool rv, nm_small;
+// Per-chunk constants of one lane (its column col = 16c + lc of the chunk):
+//   g[j] = U[16c + j][col] / U_JJ for j != lc, 0 for j == lc;
+// the owner lane of column J keeps its value frozen from step J on, so the
+// chunk's errors can be formed at its end from the registers.
+struct ChunkCtx {
+  float g[16];
+  float rd;      // 1 / U_col,col
+  float ucc;     // U_col,col
 };
 
-// Column J = 16*sb + QJ of the in-block sweep.  Register slot s holds column
-// q + 16*(sb + s) (the slots rotate down after every 16 columns), so the owner
-// of column J is lane QJ, slot 0: QJ is a compile-time constant, making the
-// DPP broadcast and every register index static.
-template <int QJ, bool NM>
-__device__ __forceinline__ void sweep_col(const SweepCtx& cx, float (&Wv)[8], float (&E)[8],
-                                          bool (&P)[8]) {
-  const int J = cx.sb * 16 + QJ;
-  const int q = cx.q;
-  if constexpr (NM) {
-    if (J < cx.w && cx.nm_small && (J % cx.mgroup) == 0) {
-      // the group is columns J..J+M-1 = lanes QJ..QJ+M-1 of slot 0
-      const int c = q + 16 * cx.sb;
-      const float sal = saliency(Wv[0], cx.Ub[c * SB + c]);
-      cx.sc[q] = sal;
-      __syncthreads();
-      if (q >= QJ && q < QJ + cx.mgroup)
-        P[0] = cx.rv && group_rank(cx.sc + QJ, cx.mgroup, sal, q - QJ) < cx.mgroup - cx.nkeep;
-      __syncthreads();
+// Sweep column j of the chunk (compile-time j: static DPP lane and indices).
+// Chain per step and row: select (pruned ? W_J : 0) on the owner lane, DPP
+// broadcast over the 16 lanes of the row, fused multiply-add.
+template <int J, bool NM_SMALL>
+__device__ __forceinline__ void sweep_step(floatx4& Wc, unsigned& Pc, const ChunkCtx& cx, int lc,
+                                           int mgroup, int nkeep, unsigned rowbits) {
+  if constexpr (NM_SMALL) {
+    if ((J % mgroup) == 0) {
+      // rank the group's M columns (lanes J..J+M-1 of the row) at its start
+      const bool in = lc >= J && lc < J + mgroup;
+      const int base = (threadIdx.x & 63) & ~15;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float my = saliency(Wc[v], cx.ucc);
+        int rank = 0;
+        for (int t = 0; t < mgroup; ++t) {
+          const float o = __shfl(my, base + J + t, 64);
+          rank += (o < my || (o == my && t < lc - J)) ? 1 : 0;
+        }
+        if (in && ((rowbits >> v) & 1u) && rank < mgroup - nkeep) Pc |= 1u << v;
+      }
     }
   }
-  // Branch-free step (columns past the block are no-ops: P is false there and
-  // the U block is zero), so 16 steps form one basic block and the scheduler
-  // can issue the U-row reads of later steps early.
-  const int Jr = J < SB ? J : SB - 1;
-  const float rdj = cx.Rd[Jr];
-  float u[8];
+  float e[4];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int as = s + cx.sb;  // absolute slot; past the block the U row is zero
-    const float uv = cx.Ub[Jr * SB + q + 16 * (as < 8 ? as : 7)];
-    u[s] = as < 8 ? uv : 0.f;
-  }
-  const bool own = (q == QJ) && (J < cx.w);
-  const bool prune = own && P[0];
-  const float eo = prune ? Wv[0] * rdj : 0.f;
-  const float e = bcast16_c<QJ>(eo);
+  for (int v = 0; v < 4; ++v) e[v] = bcast16_c<J>(((Pc >> v) & 1u) ? Wc[v] : 0.f);
 #pragma unroll
-  for (int s = 0; s < 8; ++s) Wv[s] = fmaf(-e, u[s], Wv[s]);
-  E[0] = own ? eo : E[0];
-  Wv[0] = prune ? 0.f : Wv[0];
+  for (int v = 0; v < 4; ++v) Wc[v] = fmaf(-e[v], cx.g[J], Wc[v]);
 }
 
-template <bool NM, int... Qs>
-__device__ __forceinline__ void sweep_16(std::integer_sequence<int, Qs...>, const SweepCtx& cx,
-                                         float (&Wv)[8], float (&E)[8], bool (&P)[8]) {
-  (sweep_col<Qs, NM>(cx, Wv, E, P), ...);
+template <bool NM_SMALL, int... Js>
+__device__ __forceinline__ void sweep_chunk(std::integer_sequence<int, Js...>, floatx4& Wc, unsigned& Pc,
+                                            const ChunkCtx& cx, int lc, int mgroup, int nkeep,
+                                            unsigned rowbits) {
+  (sweep_step<Js, NM_SMALL>(Wc, Pc, cx, lc, mgroup, nkeep, rowbits), ...);
 }
 
 template <int MODE>
 __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8_t* __restrict__ mask_out,
                                                     float* __restrict__ Err, const float* __restrict__ U,
                                                     const uint8_t* __restrict__ mask_in,
-                                                    const SelState* __restrict__ st, int64_t m,
-                                                    int64_t n, int64_t i1, int w, int nkeep,
+                                                    SelState* __restrict__ st,
+                                                    const unsigned long long* __restrict__ cand,
+                                                    int parity, long long ksel, int sel_fixed,
+                                                    int64_t m, int64_t n, int64_t i1, int w, int nkeep,
                                                     int mgroup) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   SweepLds& S = *reinterpret_cast<SweepLds*>(smem);
   const int tid = threadIdx.x;
-  const int q = tid & 15;
-  const int rl = tid >> 4;
-  const int64_t r = (int64_t)blockIdx.x * SW_ROWS + rl;
-  const bool rv = r < m;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lc = lane & 15;       // column inside a chunk
+  const int lg = lane >> 4;       // row group: rows 4*lg .. 4*lg+3 of the wave's 16
+  const int64_t r0 = (int64_t)blockIdx.x * 64 + wave * 16 + 4 * lg;
+  const int nch = (w + 15) >> 4;
+
+  // threshold key of the block (the LDS of the U block serves as scratch)
+  __shared__ unsigned s_cnt;
+  __shared__ HistPick s_pick;
+  unsigned long long thr = 0ull;
+  if (MODE == MODE_THRESH && sel_fixed == 0)
+    thr = select_finish(st->set[parity], cand, ksel, reinterpret_cast<unsigned long long*>(S.Ub), &s_cnt,
+                        s_pick);
+  if (MODE == MODE_THRESH && blockIdx.x == 0) sel_clear_set(st->set[parity ^ 1], tid, 256);
 
   {
-    // U block: row j = tid/2, 64 columns per thread; all loads issued together
-    // from clamped in-bounds addresses, out-of-block entries zeroed on store
-    const int j = tid >> 1, c0 = (tid & 1) * 64;
-    const int jc = j < w ? j : w - 1;
-    const float* urow = U + (i1 + jc) * n + i1;
-    float uv[64];
+    // U block, 16-byte loads: pass u covers rows 8u .. 8u+7, one wave
+    // instruction reads two whole 512-byte rows.  Clamped in-bounds
+    // addresses (rows/columns past the block re-read the last one); entries
+    // outside the upper triangle of the w x w block are stored as zero.
+    const bool vec = ((n & 3) == 0) && ((i1 & 3) == 0);  // 16-byte aligned rows
+    floatx4 uv[16];
 #pragma unroll
-    for (int u = 0; u < 64; ++u) {
-      const int c = c0 + u;
-      uv[u] = urow[c < w ? c : w - 1];
+    for (int u = 0; u < 16; ++u) {
+      const int f = u * 256 + tid;
+      const int j = f >> 5, c4 = (f & 31) * 4;
+      const int jc = j < w ? j : w - 1;
+      const float* urow = U + (i1 + jc) * n + i1;
+      if (vec && c4 + 4 <= w) {
+        uv[u] = *reinterpret_cast<const floatx4*>(urow + c4);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) uv[u][e] = urow[c4 + e < w ? c4 + e : w - 1];
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 64; ++u) {
-      const int c = c0 + u;
-      S.Ub[j * SB + c] = (j < w && c < w && c >= j) ? uv[u] : 0.f;
+    for (int u = 0; u < 16; ++u) {
+      const int f = u * 256 + tid;
+      const int j = f >> 5, c4 = (f & 31) * 4;
+      floatx4 t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = c4 + e;
+        t[e] = (j < w && c < w && c >= j) ? uv[u][e] : 0.f;
+      }
+      *reinterpret_cast<floatx4*>(&S.Ub[j * SWS + c4]) = t;
     }
   }
   if (tid < SB) S.Rd[tid] = (tid < w) ? 1.f / U[(i1 + tid) * n + i1 + tid] : 0.f;
-  if (MODE == MODE_THRESH && blockIdx.x == 0) {
-    // leave the select histograms zeroed for the next block (the select
-    // launch of this block has completed)
-    SelState* sw = const_cast<SelState*>(st);
-    for (int b = tid; b < 3 * kSelBins; b += 256) (&sw->hist[0][0])[b] = 0u;
-  }
-  float Wv[8], E[8];
-  bool P[8];
-  const int64_t rowoff = r * n + i1;
+
+  // Block columns in registers; rows past m read row m-1 and stay unwritten.
+  // With 16-byte aligned rows the tile goes through the wave's LDS staging
+  // area: coalesced 16-byte global accesses (one wave instruction = two
+  // 512-byte rows), accumulator layout on the LDS side.
+  const bool vio = ((n & 3) == 0) && ((i1 & 3) == 0) && ((w & 3) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(W) & 15) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(mask_in) & 3) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(mask_out) & 3) == 0);
+  float* Tw = S.Tw[wave];
+  const int64_t rw0 = (int64_t)blockIdx.x * 64 + wave * 16;
+  bool rowok[4];
+  floatx4 Wt[8], Et[8];
+  unsigned Pm[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int c = q + 16 * s;
-    Wv[s] = (rv && c < w) ? W[rowoff + c] : 0.f;
-    E[s] = 0.f;
-    P[s] = false;
+  for (int v = 0; v < 4; ++v) rowok[v] = r0 + v < m;
+  if (vio) {
+    floatx4 t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
+      const int64_t r = rw0 + rr < m ? rw0 + rr : m - 1;
+      t[u] = *reinterpret_cast<const floatx4*>(W + r * n + i1 + (c4 < w ? c4 : w - 4));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
+      *reinterpret_cast<floatx4*>(&Tw[rr * SWS + c4]) = c4 < w ? t[u] : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Wt[c][v] = Tw[(4 * lg + v) * SWS + 16 * c + lc];
+    __builtin_amdgcn_wave_barrier();
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int col = 16 * c + lc;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t r = rowok[v] ? r0 + v : m - 1;
+        Wt[c][v] = (col < w) ? W[r * n + i1 + (col < w ? col : 0)] : 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    Et[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    Pm[c] = 0u;
   }
   __syncthreads();
 
+  // masks known at the block start
   if (MODE == MODE_FORCED) {
+    if (vio) {
+      // the wave's 16 x w mask bytes, 4 bytes per access, through the staging tile
+      unsigned* Tb = reinterpret_cast<unsigned*>(Tw);
+      unsigned mw[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int c = q + 16 * s;
-      P[s] = rv && c < w && mask_in[rowoff + c] != 0;
+      for (int u = 0; u < 8; ++u) {
+        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
+        const int64_t r = rw0 + rr < m ? rw0 + rr : m - 1;
+        mw[u] = *reinterpret_cast<const unsigned*>(mask_in + r * n + i1 + (c4 < w ? c4 : w - 4));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
+        Tb[rr * 32 + (c4 >> 2)] = c4 < w ? mw[u] : 0u;
+      }
+      __builtin_amdgcn_wave_barrier();
+      const unsigned char* Tm = reinterpret_cast<const unsigned char*>(Tw);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (rowok[v] && Tm[(4 * lg + v) * 128 + 16 * c + lc] != 0) Pm[c] |= 1u << v;
+      __builtin_amdgcn_wave_barrier();
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int col = 16 * c + lc;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (rowok[v] && col < w && mask_in[(r0 + v) * n + i1 + col] != 0) Pm[c] |= 1u << v;
+      }
     }
   } else if (MODE == MODE_THRESH) {
-    const unsigned done = st->done;
-    const unsigned long long thr = st->thresh;
+    const unsigned done = sel_fixed ? (unsigned)sel_fixed : 1u;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int c = q + 16 * s;
-      if (rv && c < w) {
-        const unsigned long long key = sal_key(Wv[s], S.Ub[c * SB + c], (uint32_t)(rowoff + c));
-        P[s] = (done == 3u) || (done == 1u && key <= thr);
+    for (int c = 0; c < 8; ++c) {
+      const int col = 16 * c + lc;
+      if (col < w) {
+        const float ucc = S.Ub[col * SWS + col];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if (!rowok[v]) continue;
+          const unsigned long long key = sal_key(Wt[c][v], ucc, (uint32_t)((r0 + v) * n + i1 + col));
+          if (done == 3u || (done == 1u && key <= thr)) Pm[c] |= 1u << v;
+        }
       }
     }
   }
 
-  SweepCtx cx;
-  cx.sc = S.Sc + rl * SB;
-  cx.Ub = S.Ub;
-  cx.Rd = S.Rd;
-  cx.q = q;
-  cx.w = w;
-  cx.mgroup = mgroup;
-  cx.nkeep = nkeep;
-  cx.rv = rv;
-  cx.nm_small = (MODE == MODE_NM) && mgroup <= 16;
-  const bool nm_large = (MODE == MODE_NM) && mgroup > 16;
-  for (int sb = 0; sb < 8; ++sb) {
-    if (sb * 16 >= w) break;
-    cx.sb = sb;
-    if (MODE == MODE_NM && nm_large && ((sb * 16) % mgroup) == 0) {
-      // group of M >= 16 columns starting here: slots 0 .. M/16-1, all lanes
-      const int J = sb * 16;
+  float* Es = S.Es[wave];
+  const bool nm_small = MODE == MODE_NM && mgroup <= 16;
+  const bool nm_large = MODE == MODE_NM && mgroup > 16;
+  const unsigned rowbits = (rowok[0] ? 1u : 0u) | (rowok[1] ? 2u : 0u) | (rowok[2] ? 4u : 0u) |
+                           (rowok[3] ? 8u : 0u);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int c = q + 16 * (s + sb);
-        if (s + sb < 8 && c < J + mgroup) cx.sc[c - J] = saliency(Wv[s], S.Ub[c * SB + c]);
+  for (int c = 0; c < 8; ++c) {
+    if (c >= nch) break;
+    ChunkCtx cx;
+    {
+      const int col = 16 * c + lc;
+      cx.ucc = S.Ub[col * SWS + col];
+      cx.rd = (col < w) ? 1.f / cx.ucc : 0.f;
+      float rdj[16];
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const floatx4 t = *reinterpret_cast<const floatx4*>(&S.Rd[16 * c + 4 * j4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rdj[4 * j4 + e] = t[e];
       }
-      __syncthreads();
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int c = q + 16 * (s + sb);
-        if (s + sb < 8 && c < J + mgroup)
-          P[s] = rv && group_rank(cx.sc, mgroup, cx.sc[c - J], c - J) < mgroup - nkeep;
+      for (int j = 0; j < 16; ++j)
+        cx.g[j] = (j == lc) ? 0.f : S.Ub[(16 * c + j) * SWS + col] * rdj[j];
+    }
+    if (nm_large && ((16 * c) % mgroup) == 0) {
+      // group of M >= 32 columns = chunks c .. c + M/16 - 1 (all current)
+      float* sc = Tw;
+      const int nchg = mgroup >> 4;
+      for (int g = 0; g < nchg && c + g < 8; ++g) {
+        const int col = 16 * (c + g) + lc;
+        const float ucg = S.Ub[col * SWS + col];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[(4 * lg + v) * SWS + 16 * g + lc] = saliency(Wt[c + g][v], ucg);
       }
-      __syncthreads();
-    }
-    sweep_16<MODE == MODE_NM>(std::make_integer_sequence<int, 16>{}, cx, Wv, E, P);
-    // retire slot 0 (column q + 16*sb) and rotate the slots down
-    const int c = q + 16 * sb;
-    if (rv && c < w) {
-      W[rowoff + c] = P[0] ? 0.f : Wv[0];
-      if (mask_out) mask_out[rowoff + c] = P[0] ? 1 : 0;
-      Err[r * SB + c] = E[0];
-    }
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      for (int g = 0; g < nchg && c + g < 8; ++g) {
 #pragma unroll
-    for (int s = 0; s < 7; ++s) {
-      Wv[s] = Wv[s + 1];
-      E[s] = E[s + 1];
-      P[s] = P[s + 1];
+        for (int v = 0; v < 4; ++v) {
+          const float* row = sc + (4 * lg + v) * SWS;
+          const int me = 16 * g + lc;
+          if (rowok[v] && rank_of(row, mgroup, row[me], me) < mgroup - nkeep) Pm[c + g] |= 1u << v;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    Wv[7] = 0.f;
-    E[7] = 0.f;
-    P[7] = false;
+    if (nm_small)
+      sweep_chunk<true>(std::make_integer_sequence<int, 16>{}, Wt[c], Pm[c], cx, lc, mgroup, nkeep,
+                        rowbits);
+    else
+      sweep_chunk<false>(std::make_integer_sequence<int, 16>{}, Wt[c], Pm[c], cx, lc, mgroup, nkeep,
+                         rowbits);
+    // errors of the chunk: e = W_J / U_JJ for pruned entries, from the frozen
+    // owner values; pruned entries become +0.0
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const bool p = (Pm[c] >> v) & 1u;
+      Et[c][v] = p ? Wt[c][v] * cx.rd : 0.f;
+      Wt[c][v] = p ? 0.f : Wt[c][v];
+    }
+    if (c + 1 < nch) {
+      // E_c to the A-operand layout: Es[row][4*(k%4) + k/4] so that lane l
+      // reads E[l%16][4*i + l/16] for i = 0..3 as one 16-byte value
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Es[(4 * lg + v) * ESS + 4 * (lc & 3) + (lc >> 2)] = Et[c][v];
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      const floatx4 ea = *reinterpret_cast<const floatx4*>(&Es[lc * ESS + 4 * lg]);
+      __builtin_amdgcn_wave_barrier();
+      // B operands first (one wait), then the MFMAs with independent
+      // accumulators back to back
+      float bv[8][4];
+#pragma unroll
+      for (int c2 = 1; c2 < 8; ++c2) {
+        if (c2 <= c) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          bv[c2][i] = c2 < nch ? S.Ub[(16 * c + 4 * i + lg) * SWS + 16 * c2 + lc] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c2 = 1; c2 < 8; ++c2) {
+          if (c2 <= c) continue;
+          Wt[c2] = __builtin_amdgcn_mfma_f32_16x16x4f32(-ea[i], bv[c2][i], Wt[c2], 0, 0, 0);
+        }
+    }
+  }
+
+  // retire the block: W (pruned entries +0.0), errors, mask
+  if (vio) {
+    __builtin_amdgcn_wave_barrier();
+    // W, then the errors, then the mask bytes through the staging tile
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          Tw[(4 * lg + v) * SWS + 16 * c + lc] = pass == 0 ? Wt[c][v] : Et[c][v];
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
+        const int64_t r = rw0 + rr;
+        const floatx4 t = *reinterpret_cast<const floatx4*>(&Tw[rr * SWS + c4]);
+        if (r < m) {
+          if (pass == 0) {
+            if (c4 < w) *reinterpret_cast<floatx4*>(W + r * n + i1 + c4) = t;
+          } else {
+            *reinterpret_cast<floatx4*>(Err + r * SB + c4) = t;
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (mask_out) {
+      unsigned char* Tm = reinterpret_cast<unsigned char*>(Tw);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Tm[(4 * lg + v) * 128 + 16 * c + lc] = (Pm[c] >> v) & 1u;
+      __builtin_amdgcn_wave_barrier();
+      const unsigned* Tb = reinterpret_cast<const unsigned*>(Tw);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
+        const int64_t r = rw0 + rr;
+        if (r < m && c4 < w) *reinterpret_cast<unsigned*>(mask_out + r * n + i1 + c4) = Tb[rr * 32 + (c4 >> 2)];
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int col = 16 * c + lc;
+    if (col >= w) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if (!rowok[v]) continue;
+      const int64_t r = r0 + v;
+      const bool p = (Pm[c] >> v) & 1u;
+      W[r * n + i1 + col] = Wt[c][v];
+      if (mask_out) mask_out[r * n + i1 + col] = p ? 1 : 0;
+      Err[r * SB + col] = Et[c][v];
+    }
   }
 }
 
@@ -434,13 +737,16 @@ __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ W, const 
 size_t prune_ws_bytes(int64_t m, int64_t n, int blocksize) {
   (void)n;
   (void)blocksize;
-  return round_up(sizeof(SelState), 256) + round_up((size_t)m * SB * sizeof(float), 256);
+  return round_up(sizeof(SelState), 256) + round_up((size_t)m * SB * sizeof(float), 256) +
+         round_up((size_t)m * SB * sizeof(unsigned long long), 256);
 }
 
 sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
   SelState* sel = static_cast<SelState*>(ws);
   float* Err = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(sizeof(SelState), 256));
   const int64_t m = a.m, n = a.n;
+  unsigned long long* cand = reinterpret_cast<unsigned long long*>(
+      reinterpret_cast<char*>(Err) + round_up((size_t)m * SB * sizeof(float), 256));
 
   if (!(a.w_dtype == SG_F32 && static_cast<const void*>(a.W_out) == a.W)) {
     const int64_t total = m * n;
@@ -449,6 +755,9 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
                        n, a.ldw);
     if (sg_status e = check_launch("prune convert")) return e;
   }
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(select_pass_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SelLds)) != hipSuccess)
+    return set_error(SG_ERR_HIP, "hipFuncSetAttribute(select_pass_kernel) failed");
   const void* sweep_fns[3] = {reinterpret_cast<const void*>(sweep_kernel<MODE_THRESH>),
                               reinterpret_cast<const void*>(sweep_kernel<MODE_NM>),
                               reinterpret_cast<const void*>(sweep_kernel<MODE_FORCED>)};
@@ -459,50 +768,45 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
 
   const int mode = a.mask_in ? MODE_FORCED : (a.kind == SG_NM ? MODE_NM : MODE_THRESH);
   const int B = a.blocksize;
-  int64_t sel_grid_cap = 0;
   if (mode == MODE_THRESH) {
-    int dev = 0, ncu = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(select_kernel),
-                                                     256, 0) != hipSuccess || per_cu < 1)
-      return set_error(SG_ERR_HIP, "select kernel occupancy query failed");
-    sel_grid_cap = (int64_t)ncu * per_cu;
     hipLaunchKernelGGL(sel_clear_kernel, dim3(1), dim3(256), 0, st, sel);
     if (sg_status e = check_launch("select clear")) return e;
   }
-  for (int64_t i1 = 0; i1 < n; i1 += B) {
+  // select: enough workgroups that every thread holds at most SEL_KPT keys
+  const unsigned sel_grid = (unsigned)std::max<int64_t>(1, ceil_div(m, (int64_t)2 * SEL_KPT));
+  const dim3 sw_grid((unsigned)ceil_div(m, 64)), sw_block(256);
+  const size_t shm = sizeof(SweepLds);
+  int parity = 0;
+  for (int64_t i1 = 0; i1 < n; i1 += B, parity ^= 1) {
     const int w = (int)std::min<int64_t>(B, n - i1);
+    int sel_fixed = 0;
+    long long k = 0;
     if (mode == MODE_THRESH) {
-      const long long k = (long long)floor(a.sparsity * (double)m * (double)w);
+      k = (long long)floor(a.sparsity * (double)m * (double)w);
       const long long total = (long long)m * w;
-      // enough workgroups that every thread holds at most SEL_KPT keys
-      const int64_t need = ceil_div(m, (int64_t)2 * SEL_KPT);
-      if (need > sel_grid_cap)
-        return set_error(SG_ERR_UNSUPPORTED, "m=%lld too large for the single-launch select",
-                         (long long)m);
-      const unsigned g = (unsigned)std::max<int64_t>(1, need);
-      void* args[] = {&sel, const_cast<float**>(&a.W_out), const_cast<float**>(&a.U),
-                      const_cast<int64_t*>(&a.m), const_cast<int64_t*>(&a.n), &i1,
-                      const_cast<int*>(&w), const_cast<long long*>(&k)};
-      if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(select_kernel), dim3(g), dim3(256),
-                                     args, 0, st) != hipSuccess)
-        return set_error(SG_ERR_HIP, "cooperative launch of the select kernel failed");
-      if (sg_status e = check_launch("select")) return e;
+      if (k <= 0) {
+        sel_fixed = 2;
+      } else if (k >= total) {
+        sel_fixed = 3;
+      } else {
+        for (int p = 0; p < 2; ++p) {
+          hipLaunchKernelGGL(select_pass_kernel, dim3(sel_grid), dim3(256), sizeof(SelLds), st,
+                             &sel->set[parity], cand, static_cast<const float*>(a.W_out), a.U, m, n,
+                             i1, w, k, p);
+          if (sg_status e = check_launch("select pass")) return e;
+        }
+      }
     }
-    {
-      const dim3 sg_grid((unsigned)ceil_div(m, SW_ROWS)), sg_block(256);
-      const size_t shm = sizeof(SweepLds);
-      if (mode == MODE_THRESH)
-        hipLaunchKernelGGL(sweep_kernel<MODE_THRESH>, sg_grid, sg_block, shm, st, a.W_out, a.mask_out,
-                           Err, a.U, a.mask_in, sel, m, n, i1, w, a.n_keep, a.m_group);
-      else if (mode == MODE_NM)
-        hipLaunchKernelGGL(sweep_kernel<MODE_NM>, sg_grid, sg_block, shm, st, a.W_out, a.mask_out, Err,
-                           a.U, a.mask_in, sel, m, n, i1, w, a.n_keep, a.m_group);
-      else
-        hipLaunchKernelGGL(sweep_kernel<MODE_FORCED>, sg_grid, sg_block, shm, st, a.W_out, a.mask_out,
-                           Err, a.U, a.mask_in, sel, m, n, i1, w, a.n_keep, a.m_group);
-    }
+    if (mode == MODE_THRESH)
+      hipLaunchKernelGGL(sweep_kernel<MODE_THRESH>, sw_grid, sw_block, shm, st, a.W_out, a.mask_out,
+                         Err, a.U, a.mask_in, sel, cand, parity, k, sel_fixed, m, n, i1, w, a.n_keep,
+                         a.m_group);
+    else if (mode == MODE_NM)
+      hipLaunchKernelGGL(sweep_kernel<MODE_NM>, sw_grid, sw_block, shm, st, a.W_out, a.mask_out, Err,
+                         a.U, a.mask_in, sel, cand, 0, 0ll, 0, m, n, i1, w, a.n_keep, a.m_group);
+    else
+      hipLaunchKernelGGL(sweep_kernel<MODE_FORCED>, sw_grid, sw_block, shm, st, a.W_out, a.mask_out,
+                         Err, a.U, a.mask_in, sel, cand, 0, 0ll, 0, m, n, i1, w, a.n_keep, a.m_group);
     if (sg_status e = check_launch("prune sweep")) return e;
     const int64_t i2 = i1 + w;
     if (i2 < n) {
