@@ -360,6 +360,20 @@ constexpr unsigned kWaitVm0 = 0x0F70u;
 constexpr unsigned kWaitVm4 = 0x0F74u;
 constexpr unsigned kWaitVm8 = 0x0F78u;
 
+// One LDS-DMA copy: lane l moves 16 bytes from gbase + voff (its own offset)
+// to LDS byte address lds_addr + 16 * l.  Issued from inline assembly so that
+// the compiler does not add waits of its own for the copies (it cannot tell
+// which stage a later LDS read touches at the head of the software-pipelined
+// loop and would wait for every copy in flight); all ordering of the copies
+// is explicit (s_waitcnt vmcnt before the barrier that publishes a stage).
+// The instruction has no register results; M0 is used by nothing else here.
+__device__ __forceinline__ void lds_dma16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // Workgroup barrier without a memory fence: a fence would also wait for the
 // stages still in flight.  LDS visibility is ordered by hand (each wave waits
 // for its own copies of a stage before the barrier that publishes it); the
@@ -374,8 +388,7 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
     float* __restrict__ H, int n, const uint16_t* __restrict__ X, int64_t T,
     int64_t ldx, int64_t tiles, int splits, int64_t tps, int group,
     float* __restrict__ part, unsigned* __restrict__ counters) {
-  // One array per stage, so the compiler can tell which stage a read touches
-  // and waits only for the copies into that stage.
+  // One array per stage.
   __shared__ __attribute__((aligned(16))) unsigned char st0[DSTAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st1[DSTAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st2[DSTAGE];
@@ -419,13 +432,13 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
   const uint32_t dcol = (uint32_t)col * 2u;
   auto copy_stage = [&](unsigned char* buf, int64_t s) {
     const int64_t tok0 = t_begin + s * DK + wave * 4;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)buf + (uint32_t)(wave * 4 * DROW);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       int64_t t = tok0 + j;
       t = t < t_end ? t : t_end - 1;  // rows past the end are zeroed later
-      const char* src = reinterpret_cast<const char*>(X) + t * ldx * 2 + dcol;
-      __builtin_amdgcn_global_load_lds((const global_void*)src,
-                                       (lds_void*)(buf + (wave * 4 + j) * DROW), 16, 0, 0);
+      const char* row = reinterpret_cast<const char*>(X) + t * ldx * 2;
+      lds_dma16(row, dcol, __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(j * DROW)));
     }
   };
 
@@ -465,38 +478,59 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
   if (nsteps > 1) copy_stage(st1, 1);
   if (nsteps > 2) copy_stage(st2, 2);
 
-  // Step s: wait for this wave's copies of stage s (stages s+1 and s+2 may
-  // stay in flight), barrier (stage s complete in LDS; every wave is done
-  // with stage s-1), start copying stage s+3 into the buffer of stage s-1,
-  // multiply stage s.
-  auto step = [&](const unsigned char* cur, unsigned char* refill, int64_t s) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm8);
+  // Steady-state step s (fragments of stage s already in registers, stage s
+  // complete in LDS): wait for this wave's copies of stage s+1 (stage s+2 may
+  // stay in flight), barrier (stage s+1 complete; every wave is done with
+  // stage s-1), start copying stage s+3 into the buffer of stage s-1,
+  // multiply stage s, and read the first fragments of stage s+1, so that the
+  // next step's MFMAs start right after its barrier.
+  struct Frags {
+    bf16x8 fb[4];
+    bf16x8 fa0;
+  };
+  auto prefetch = [&](const unsigned char* buf, Frags& f) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) f.fb[c] = frag(buf, b_off + c * 32);
+    f.fa0 = frag(buf, a_off);
+  };
+  auto step = [&](const unsigned char* cur, const unsigned char* nxt, unsigned char* refill,
+                  int64_t s, Frags& f) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm4);
     stage_barrier();
     copy_stage(refill, s + 3);
     __builtin_amdgcn_sched_barrier(0);
-    compute(cur);
-    // operand reads two fragments ahead of the MFMAs that use them
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    bf16x8 fa = f.fa0;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const bf16x8 fan = a < 7 ? frag(cur, a_off + (a + 1) * 32) : fa;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f.fb[c], acc[a][c], 0, 0, 0);
+      fa = fan;
+    }
+    prefetch(nxt, f);
+    // two operand reads ahead of the MFMAs; the next stage's fragments are
+    // read during the last MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      if (g < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
   int64_t s = 0;
-  // Unrolled by 8 so that every read names its stage array; at the loop
-  // head the compiler loses track of which copies are still in flight and
-  // waits for all of them once per iteration.
-  for (; s + 10 < nsteps; s += 8) {
-    step(st0, st3, s);
-    step(st1, st0, s + 1);
-    step(st2, st1, s + 2);
-    step(st3, st2, s + 3);
-    step(st0, st3, s + 4);
-    step(st1, st0, s + 5);
-    step(st2, st1, s + 6);
-    step(st3, st2, s + 7);
+  if (nsteps > 6) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm4);  // stages 0 and 1
+    stage_barrier();
+    Frags f;
+    prefetch(st0, f);
+    for (; s + 6 < nsteps; s += 4) {
+      step(st0, st1, st3, s, f);
+      step(st1, st2, st0, s + 1, f);
+      step(st2, st3, st1, s + 2, f);
+      step(st3, st0, st2, s + 3, f);
+    }
   }
   for (; s < nsteps; ++s) {
     const int b = (int)(s & 3);
