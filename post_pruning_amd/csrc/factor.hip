@@ -342,8 +342,8 @@ __global__ __launch_bounds__(256) void update_kernel(float* __restrict__ A, floa
     Q = A + lb * NB * n_pad + (int64_t)k * NB;
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  RowsF32 pl{P, n_pad, NB, NB, 1.f};
-  RowsF32 ql{Q, n_pad, NB, NB, 1.f};
+  RowsF32V pl{P, n_pad, NB, NB};
+  RowsF32V ql{Q, n_pad, NB, NB};
   TileAcc acc;
   tile_zero(acc);
   tile_gemm_pipelined(acc, pl, ql, NB, lds);

@@ -128,6 +128,71 @@ struct ColsF32 {
   }
 };
 
+// Rows of a k-contiguous fp32 matrix with 16-byte aligned rows (ld % 4 == 0,
+// aligned base): four 16-byte loads per thread per chunk (8 threads per row,
+// rows r0, r0 + 32, ...), written to LDS with 16-byte stores.  Element (r, k)
+// = src[r*ld + k], valid for r < rows, k < kend (kend % 4 == 0).
+struct RowsF32V {
+  const float* src;
+  int64_t ld;
+  int rows;
+  int64_t kend;
+  floatx4 v[4];
+  __device__ inline void load(int64_t k0) {
+    const int k4 = (threadIdx.x & 7) * 4, r0 = threadIdx.x >> 3;
+    const int64_t k = k0 + k4;
+    const int64_t kc = k < kend ? k : kend - 4;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = r0 + 32 * u;
+      const int rc = r < rows ? r : rows - 1;
+      v[u] = *reinterpret_cast<const floatx4*>(src + (int64_t)rc * ld + kc);
+    }
+  }
+  __device__ inline void store(float* lds, int64_t k0) {
+    const int k4 = (threadIdx.x & 7) * 4, r0 = threadIdx.x >> 3;
+    const bool kok = k0 + k4 < kend;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = r0 + 32 * u;
+      *reinterpret_cast<floatx4*>(&lds[r * GS + k4]) =
+          (r < rows && kok) ? v[u] : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+};
+
+// Row-major [k][j] fp32 read transposed with 16-byte aligned rows (ld % 4 ==
+// 0, aligned base, cols % 4 == 0): thread t loads columns 4*(t%32) .. +3 of
+// rows k = t/32 + 8u (u < 4) with four 16-byte loads; element (j, k) =
+// src[k*ld + j], valid for j < cols, k < kend.
+struct ColsF32V {
+  const float* src;
+  int64_t ld;
+  int cols;
+  int64_t kend;
+  floatx4 v[4];
+  __device__ inline void load(int64_t k0) {
+    const int j4 = (threadIdx.x & 31) * 4, kh = threadIdx.x >> 5;
+    const int jc = j4 < cols ? j4 : cols - 4;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t k = k0 + kh + 8 * u;
+      const int64_t kc = k < kend ? k : kend - 1;
+      v[u] = *reinterpret_cast<const floatx4*>(src + kc * ld + jc);
+    }
+  }
+  __device__ inline void store(float* lds, int64_t k0) {
+    const int j4 = (threadIdx.x & 31) * 4, kh = threadIdx.x >> 5;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kk = kh + 8 * u;
+      const bool ok = j4 < cols && k0 + kk < kend;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lds[(j4 + e) * GS + kk] = ok ? v[u][e] : 0.f;
+    }
+  }
+};
+
 // acc += P * Q^T over k in [0, K): P and Q loaders with the load/store
 // interface above; lds holds 4 * GBUF floats (two buffers per operand).
 template <class PL, class QL>

@@ -33,6 +33,7 @@ namespace sg {
 namespace {
 
 constexpr int SB = SG_MAX_BLOCKSIZE;  // 128
+constexpr int EGK = 512;              // columns of a lazy-update group (error buffer width)
 
 enum { MODE_THRESH = 0, MODE_NM = 1, MODE_FORCED = 2 };
 
@@ -468,7 +469,8 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   const bool vio = ((n & 3) == 0) && ((i1 & 3) == 0) && ((w & 3) == 0) &&
                    ((reinterpret_cast<uintptr_t>(W) & 15) == 0) &&
                    ((reinterpret_cast<uintptr_t>(mask_in) & 3) == 0) &&
-                   ((reinterpret_cast<uintptr_t>(mask_out) & 3) == 0);
+                   ((reinterpret_cast<uintptr_t>(mask_out) & 3) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(Err) & 15) == 0);
   float* Tw = S.Tw[wave];
   const int64_t rw0 = (int64_t)blockIdx.x * 64 + wave * 16;
   bool rowok[4];
@@ -674,7 +676,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
           if (pass == 0) {
             if (c4 < w) *reinterpret_cast<floatx4*>(W + r * n + i1 + c4) = t;
           } else {
-            *reinterpret_cast<floatx4*>(Err + r * SB + c4) = t;
+            if (c4 < w) *reinterpret_cast<floatx4*>(Err + r * EGK + c4) = t;
           }
         }
       }
@@ -708,36 +710,52 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
       const bool p = (Pm[c] >> v) & 1u;
       W[r * n + i1 + col] = Wt[c][v];
       if (mask_out) mask_out[r * n + i1 + col] = p ? 1 : 0;
-      Err[r * SB + col] = Et[c][v];
+      Err[r * EGK + col] = Et[c][v];
     }
   }
 }
 
-// W[:, i2:] -= Err[:, 0:w] * U[i1:i2, i2:]
-__global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ W, const float* __restrict__ Err,
+// W[:, c_begin:c_end] -= E[:, 0:K] * U[k0:k0+K, c_begin:c_end]; E has row stride
+// EGK.  The lazy update of the column sweep, in two levels: after each block
+// its errors update the rest of the current group of columns (K = block
+// width); after the last block of a group, the errors of the whole group
+// update every column beyond it at once (K = group width).
+template <bool VEC>
+__global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ W, const float* __restrict__ E,
                                                    const float* __restrict__ U, int64_t m, int64_t n,
-                                                   int64_t i1, int w) {
+                                                   int64_t k0, int K, int64_t c_begin, int64_t c_end) {
   __shared__ __attribute__((aligned(16))) float lds[4 * GBUF];
-  const int64_t i2 = i1 + w;
   const int64_t r0 = (int64_t)blockIdx.y * GT;
-  const int64_t c0 = i2 + (int64_t)blockIdx.x * GT;
+  const int64_t c0 = c_begin + (int64_t)blockIdx.x * GT;
   const int rows = (int)min<int64_t>(GT, m - r0);
-  const int cols = (int)min<int64_t>(GT, n - c0);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  RowsF32 pl{Err + r0 * SB, SB, rows, w, 1.f};
-  ColsF32 ql{U + i1 * n + c0, n, cols, w};
+  const int cols = (int)min<int64_t>(GT, c_end - c0);
   TileAcc acc;
   tile_zero(acc);
-  tile_gemm_pipelined(acc, pl, ql, w, lds);
+  if constexpr (VEC) {
+    RowsF32V pl{E + r0 * EGK, EGK, rows, K};
+    ColsF32V ql{U + k0 * n + c0, n, cols, K};
+    tile_gemm_pipelined(acc, pl, ql, K, lds);
+  } else {
+    RowsF32 pl{E + r0 * EGK, EGK, rows, K, 1.f};
+    ColsF32 ql{U + k0 * n + c0, n, cols, K};
+    tile_gemm_pipelined(acc, pl, ql, K, lds);
+  }
   tile_sub_from(W + r0 * n + c0, n, rows, cols, acc, lds);
 }
 
 }  // namespace
 
+// 16-byte loaders apply when every row segment they read is 16-byte aligned
+// and the K and column extents are multiples of 4.
+bool lazy_vec(const float* E, const float* U, int64_t n, int64_t c_begin, int64_t c_end, int K) {
+  return (reinterpret_cast<uintptr_t>(E) % 16) == 0 && (reinterpret_cast<uintptr_t>(U) % 16) == 0 &&
+         (n % 4) == 0 && (c_begin % 4) == 0 && ((c_end - c_begin) % 4) == 0 && (K % 4) == 0;
+}
+
 size_t prune_ws_bytes(int64_t m, int64_t n, int blocksize) {
   (void)n;
   (void)blocksize;
-  return round_up(sizeof(SelState), 256) + round_up((size_t)m * SB * sizeof(float), 256) +
+  return round_up(sizeof(SelState), 256) + round_up((size_t)m * EGK * sizeof(float), 256) +
          round_up((size_t)m * SB * sizeof(unsigned long long), 256);
 }
 
@@ -746,7 +764,7 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
   float* Err = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(sizeof(SelState), 256));
   const int64_t m = a.m, n = a.n;
   unsigned long long* cand = reinterpret_cast<unsigned long long*>(
-      reinterpret_cast<char*>(Err) + round_up((size_t)m * SB * sizeof(float), 256));
+      reinterpret_cast<char*>(Err) + round_up((size_t)m * EGK * sizeof(float), 256));
 
   if (!(a.w_dtype == SG_F32 && static_cast<const void*>(a.W_out) == a.W)) {
     const int64_t total = m * n;
@@ -776,9 +794,14 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
   const unsigned sel_grid = (unsigned)std::max<int64_t>(1, ceil_div(m, (int64_t)2 * SEL_KPT));
   const dim3 sw_grid((unsigned)ceil_div(m, 64)), sw_block(256);
   const size_t shm = sizeof(SweepLds);
+  // lazy-update groups: GK columns (a multiple of the block width, at most EGK)
+  const int64_t GK = (EGK / B) * B;
   int parity = 0;
   for (int64_t i1 = 0; i1 < n; i1 += B, parity ^= 1) {
     const int w = (int)std::min<int64_t>(B, n - i1);
+    const int64_t g0 = (i1 / GK) * GK;
+    const int64_t g_end = std::min<int64_t>(n, g0 + GK);
+    float* Eb = Err + (i1 - g0);  // this block's columns of the group's error buffer
     int sel_fixed = 0;
     long long k = 0;
     if (mode == MODE_THRESH) {
@@ -799,20 +822,36 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
     }
     if (mode == MODE_THRESH)
       hipLaunchKernelGGL(sweep_kernel<MODE_THRESH>, sw_grid, sw_block, shm, st, a.W_out, a.mask_out,
-                         Err, a.U, a.mask_in, sel, cand, parity, k, sel_fixed, m, n, i1, w, a.n_keep,
+                         Eb, a.U, a.mask_in, sel, cand, parity, k, sel_fixed, m, n, i1, w, a.n_keep,
                          a.m_group);
     else if (mode == MODE_NM)
-      hipLaunchKernelGGL(sweep_kernel<MODE_NM>, sw_grid, sw_block, shm, st, a.W_out, a.mask_out, Err,
+      hipLaunchKernelGGL(sweep_kernel<MODE_NM>, sw_grid, sw_block, shm, st, a.W_out, a.mask_out, Eb,
                          a.U, a.mask_in, sel, cand, 0, 0ll, 0, m, n, i1, w, a.n_keep, a.m_group);
     else
       hipLaunchKernelGGL(sweep_kernel<MODE_FORCED>, sw_grid, sw_block, shm, st, a.W_out, a.mask_out,
-                         Err, a.U, a.mask_in, sel, cand, 0, 0ll, 0, m, n, i1, w, a.n_keep, a.m_group);
+                         Eb, a.U, a.mask_in, sel, cand, 0, 0ll, 0, m, n, i1, w, a.n_keep, a.m_group);
     if (sg_status e = check_launch("prune sweep")) return e;
     const int64_t i2 = i1 + w;
-    if (i2 < n) {
-      dim3 grid((unsigned)ceil_div(n - i2, GT), (unsigned)ceil_div(m, GT));
-      hipLaunchKernelGGL(lazy_kernel, grid, dim3(256), 0, st, a.W_out, Err, a.U, m, n, i1, w);
-      if (sg_status e = check_launch("prune lazy")) return e;
+    if (i2 < g_end) {
+      // rest of the group, K = block width
+      dim3 grid((unsigned)ceil_div(g_end - i2, GT), (unsigned)ceil_div(m, GT));
+      if (lazy_vec(Eb, a.U, n, i2, g_end, w))
+        hipLaunchKernelGGL(lazy_kernel<true>, grid, dim3(256), 0, st, a.W_out, Eb, a.U, m, n, i1, w, i2,
+                           g_end);
+      else
+        hipLaunchKernelGGL(lazy_kernel<false>, grid, dim3(256), 0, st, a.W_out, Eb, a.U, m, n, i1, w, i2,
+                           g_end);
+      if (sg_status e = check_launch("prune lazy (group)")) return e;
+    } else if (g_end < n) {
+      // last block of the group: every column beyond it, K = group width
+      dim3 grid((unsigned)ceil_div(n - g_end, GT), (unsigned)ceil_div(m, GT));
+      if (lazy_vec(Err, a.U, n, g_end, n, (int)(g_end - g0)))
+        hipLaunchKernelGGL(lazy_kernel<true>, grid, dim3(256), 0, st, a.W_out, Err, a.U, m, n, g0,
+                           (int)(g_end - g0), g_end, n);
+      else
+        hipLaunchKernelGGL(lazy_kernel<false>, grid, dim3(256), 0, st, a.W_out, Err, a.U, m, n, g0,
+                           (int)(g_end - g0), g_end, n);
+      if (sg_status e = check_launch("prune lazy (trailing)")) return e;
     }
   }
   return SG_OK;
