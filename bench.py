@@ -249,7 +249,7 @@ def main():
             "prune_tflops": (work["lazy"] + work["inblock"]) / (ph["prune"] * 1e-3) / 1e12,
         },
         "roofline": {
-            "kernel": "hess_bf16_kernel (sg_hessian_accumulate, one launch per step)",
+            "kernel": "hess_bf16_dma_kernel (sg_hessian_accumulate, one launch per step)",
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
