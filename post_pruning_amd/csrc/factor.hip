@@ -111,6 +111,15 @@ struct PanelLds {
   int fail;
 };
 
+// Empty asm that takes the 16 values as read-write operands: they must be
+// computed at this point (no instructions are emitted).
+__device__ __forceinline__ void pin16(float (&a)[16]) {
+  asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
+               "+v"(a[6]), "+v"(a[7]));
+  asm volatile("" : "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]), "+v"(a[13]),
+               "+v"(a[14]), "+v"(a[15]));
+}
+
 __device__ __forceinline__ float rdlane(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
@@ -164,22 +173,32 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
     const int c0 = p * 16;
     if (wave == 0) {
       const int r0 = c0 + lane, r1 = c0 + 64 + lane;
+      // 16-byte reads from clamped rows, out-of-range rows zeroed afterwards
+      const int r0c = r0 < NB ? r0 : NB - 1, r1c = r1 < NB ? r1 : NB - 1;
+      floatx4 t0[4], t1[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        t0[q] = *reinterpret_cast<const floatx4*>(&S.As[r0c * PS + c0 + 4 * q]);
+        t1[q] = *reinterpret_cast<const floatx4*>(&S.As[r1c * PS + c0 + 4 * q]);
+      }
       float a0[16], a1[16];
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
-        a0[c] = (r0 < NB) ? S.As[r0 * PS + c0 + c] : 0.f;
-        a1[c] = (r1 < NB) ? S.As[r1 * PS + c0 + c] : 0.f;
+        a0[c] = (r0 < NB) ? t0[c >> 2][c & 3] : 0.f;
+        a1[c] = (r1 < NB) ? t1[c >> 2][c & 3] : 0.f;
       }
-      int fail = -1;
+      // No lane masks: entries above the diagonal start as zero, so scaling
+      // column j on every lane leaves them zero and turns the pivot into
+      // d2/d = d; the updates below only dirty entries (row j, column > j)
+      // above the diagonal, which are never read again and are dropped when
+      // the sub-panel is written back.
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const float d2 = rdlane(a0[j], j);
-        if (fail < 0 && !(d2 > 0.f && isfinite(d2))) fail = j;
-        // hardware sqrt / reciprocal (about 1 ulp): the pivot chain is the
+        // hardware reciprocal square root (about 1 ulp): the pivot chain is the
         // latency-critical path of the whole factorisation
-        const float d = __builtin_amdgcn_sqrtf(d2);
-        const float rd = __builtin_amdgcn_rcpf(d);
-        a0[j] = (lane > j) ? a0[j] * rd : (lane == j ? d : a0[j]);
+        const float rd = __builtin_amdgcn_rsqf(d2);
+        a0[j] *= rd;
         a1[j] *= rd;
 #pragma unroll
         for (int c = j + 1; c < 16; ++c) {
@@ -187,13 +206,30 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
           a0[c] = fmaf(-a0[j], lcj, a0[c]);
           a1[c] = fmaf(-a1[j], lcj, a1[c]);
         }
+        // right-looking order: the updated columns are materialised after
+        // every step, so each broadcast is consumed in its own step (left to
+        // itself the compiler sinks the updates to their first use and keeps
+        // every broadcast value live in scalar registers, which spill)
+        pin16(a0);
+        pin16(a1);
       }
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        if (r0 < NB) S.As[r0 * PS + c0 + c] = (c <= lane) ? a0[c] : 0.f;
-        if (r1 < NB) S.As[r1 * PS + c0 + c] = a1[c];
+      for (int q = 0; q < 4; ++q) {
+        floatx4 w0, w1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w0[e] = (4 * q + e <= lane) ? a0[4 * q + e] : 0.f;
+          w1[e] = a1[4 * q + e];
+        }
+        if (r0 < NB) *reinterpret_cast<floatx4*>(&S.As[r0 * PS + c0 + 4 * q]) = w0;
+        if (r1 < NB) *reinterpret_cast<floatx4*>(&S.As[r1 * PS + c0 + 4 * q]) = w1;
       }
-      if (lane == 0 && fail >= 0 && S.fail < 0) S.fail = c0 + fail;
+      // breakdown: a pivot that was not positive and finite leaves a diagonal
+      // entry that is not (0 * inf, NaN or inf), and every later one follows;
+      // the first such column of the sub-panel is recorded
+      const float dj = S.As[(c0 + (lane & 15)) * PS + c0 + (lane & 15)];
+      const unsigned long long bad = __ballot(lane < 16 && !(dj > 0.f && isfinite(dj)));
+      if (lane == 0 && bad != 0ull && S.fail < 0) S.fail = c0 + __builtin_ctzll(bad);
     }
     __syncthreads();
     // rank-16 update of the trailing lower triangle, 16x16 tiles (I >= C > p)
