@@ -124,14 +124,10 @@ __device__ __forceinline__ float rdlane(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-__global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float* __restrict__ Y,
-                                                    int64_t n_pad, int k, int64_t n,
-                                                    int32_t* info) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  PanelLds& S = *reinterpret_cast<PanelLds*>(smem);
+__device__ __forceinline__ void panel_body(PanelLds& S, float* __restrict__ A, float* __restrict__ Y,
+                                           int64_t n_pad, int k, int64_t n, int32_t* info, int b) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int b = blockIdx.x;
   const int64_t k0 = (int64_t)k * NB;
 
   // The 128x128 block this workgroup transforms at the end is fetched into
@@ -351,39 +347,91 @@ __device__ inline int64_t isqrt_floor(int64_t x) {
   return r;
 }
 
-__global__ __launch_bounds__(256) void update_kernel(float* __restrict__ A, float* __restrict__ Y,
-                                                     int64_t n_pad, int k, int nblk) {
-  __shared__ __attribute__((aligned(16))) float lds[4 * GBUF];
+// Trailing-update tiles of panel k (K = 128 each), in three subsets:
+//   UPD_ALL   every tile;
+//   UPD_COL   the tiles of block column k+1 only (what panel k+1 needs);
+//   UPD_REST  every other tile (run while panel k+1 factors).
+enum { UPD_ALL = 0, UPD_COL = 1, UPD_REST = 2 };
+
+__host__ __device__ inline int64_t update_tiles(int k, int nblk, int mode) {
   const int64_t t = nblk - k - 1;  // trailing block count
-  const int64_t nsyrk = t * (t + 1) / 2;
-  int64_t idx = blockIdx.x;
+  if (t <= 0) return 0;
+  if (mode == UPD_COL) return t + (k + 1);
+  if (mode == UPD_REST) return (t - 1) * t / 2 + (int64_t)(k + 1) * (t - 1);
+  return t * (t + 1) / 2 + (int64_t)(k + 1) * t;
+}
+
+__device__ __forceinline__ void update_body(float* lds, float* __restrict__ A, float* __restrict__ Y,
+                                            int64_t n_pad, int k, int nblk, int mode, int64_t idx) {
+  const int64_t t = nblk - k - 1;
+  // SYRK tiles: lower triangle over trailing blocks [s0, nblk); inverse
+  // tiles: rows c <= k, block columns [s0, nblk)
+  const int64_t s0 = mode == UPD_REST ? k + 2 : k + 1;
+  const int64_t ts = nblk - s0;
+  const int64_t nsyrk = mode == UPD_COL ? t : ts * (ts + 1) / 2;
   float* C;
   const float *P, *Q;
   if (idx < nsyrk) {
-    // lower-triangle tile (l, m) of the trailing matrix, m <= l
-    int64_t l = (isqrt_floor(8 * idx + 1) - 1) / 2;
-    while ((l + 1) * (l + 2) / 2 <= idx) ++l;
-    while (l * (l + 1) / 2 > idx) --l;
-    const int64_t m = idx - l * (l + 1) / 2;
-    const int64_t lb = k + 1 + l, mb = k + 1 + m;
+    int64_t l, m;
+    if (mode == UPD_COL) {
+      l = idx;
+      m = 0;
+    } else {
+      l = (isqrt_floor(8 * idx + 1) - 1) / 2;
+      while ((l + 1) * (l + 2) / 2 <= idx) ++l;
+      while (l * (l + 1) / 2 > idx) --l;
+      m = idx - l * (l + 1) / 2;
+    }
+    const int64_t lb = s0 + l, mb = s0 + m;
     C = A + lb * NB * n_pad + mb * NB;
     P = A + lb * NB * n_pad + (int64_t)k * NB;
     Q = A + mb * NB * n_pad + (int64_t)k * NB;
   } else {
     idx -= nsyrk;
-    const int64_t c = idx % (k + 1);
-    const int64_t lb = k + 1 + idx / (k + 1);
+    int64_t c, lb;
+    if (mode == UPD_COL) {
+      c = idx;
+      lb = k + 1;
+    } else {
+      c = idx % (k + 1);
+      lb = s0 + idx / (k + 1);
+    }
     C = Y + c * NB * n_pad + lb * NB;
     P = Y + c * NB * n_pad + (int64_t)k * NB;
     Q = A + lb * NB * n_pad + (int64_t)k * NB;
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   RowsF32V pl{P, n_pad, NB, NB};
   RowsF32V ql{Q, n_pad, NB, NB};
   TileAcc acc;
   tile_zero(acc);
   tile_gemm_pipelined(acc, pl, ql, NB, lds);
   tile_sub_from(C, n_pad, NB, NB, acc, lds);
+}
+
+__global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float* __restrict__ Y,
+                                                    int64_t n_pad, int k, int64_t n, int32_t* info) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  panel_body(*reinterpret_cast<PanelLds*>(smem), A, Y, n_pad, k, n, info, blockIdx.x);
+}
+
+__global__ __launch_bounds__(256) void update_kernel(float* __restrict__ A, float* __restrict__ Y,
+                                                     int64_t n_pad, int k, int nblk, int mode) {
+  __shared__ __attribute__((aligned(16))) float lds[4 * GBUF];
+  update_body(lds, A, Y, n_pad, k, nblk, mode, blockIdx.x);
+}
+
+// Look-ahead step: workgroups [0, nblk) factor panel k+1 and transform its
+// blocks while the others apply the rest of panel k's trailing update (the
+// tiles outside block column k+1, which panel k+1 does not read).
+__global__ __launch_bounds__(256) void panel_rest_kernel(float* __restrict__ A, float* __restrict__ Y,
+                                                         int64_t n_pad, int k, int nblk, int64_t n,
+                                                         int32_t* info) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  if ((int)blockIdx.x < nblk)
+    panel_body(*reinterpret_cast<PanelLds*>(smem), A, Y, n_pad, k + 1, n, info, blockIdx.x);
+  else
+    update_body(reinterpret_cast<float*>(smem), A, Y, n_pad, k, nblk, UPD_REST,
+                (int64_t)blockIdx.x - nblk);
 }
 
 // ---- flip out: U[i][j] = Y[n-1-j][n-1-i] (i <= j), 0 below ------------------
@@ -431,10 +479,11 @@ sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double dam
 
   static bool attr_done = false;
   if (!attr_done) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(panel_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sizeof(PanelLds)) != hipSuccess)
-      return set_error(SG_ERR_HIP, "hipFuncSetAttribute(panel_kernel) failed");
+    for (const void* f : {reinterpret_cast<const void*>(panel_kernel),
+                          reinterpret_cast<const void*>(panel_rest_kernel)})
+      if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PanelLds)) !=
+          hipSuccess)
+        return set_error(SG_ERR_HIP, "hipFuncSetAttribute(panel kernels) failed");
     attr_done = true;
   }
 
@@ -443,17 +492,19 @@ sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double dam
   const unsigned t64 = (unsigned)(n_pad / 64);
   hipLaunchKernelGGL(flip_init_kernel, dim3(t64, t64), dim3(256), 0, st, H, n, n_pad, lam, A, Y);
   if (sg_status e = check_launch("flip/init")) return e;
-  for (int k = 0; k < nblk; ++k) {
-    hipLaunchKernelGGL(panel_kernel, dim3(nblk), dim3(256), sizeof(PanelLds), st, A, Y, n_pad, k,
-                       n, info);
-    if (sg_status e = check_launch("factor panel")) return e;
-    const int64_t t = nblk - k - 1;
-    const int64_t tiles = t * (t + 1) / 2 + (int64_t)(k + 1) * t;
-    if (tiles > 0) {
-      hipLaunchKernelGGL(update_kernel, dim3((unsigned)tiles), dim3(256), 0, st, A, Y, n_pad, k,
-                         nblk);
-      if (sg_status e = check_launch("factor update")) return e;
-    }
+  // panel 0; then per k: block column k+1 of panel k's update, and panel
+  // k+1 together with the rest of panel k's update
+  hipLaunchKernelGGL(panel_kernel, dim3(nblk), dim3(256), sizeof(PanelLds), st, A, Y, n_pad, 0, n,
+                     info);
+  if (sg_status e = check_launch("factor panel")) return e;
+  for (int k = 0; k + 1 < nblk; ++k) {
+    hipLaunchKernelGGL(update_kernel, dim3((unsigned)update_tiles(k, nblk, UPD_COL)), dim3(256), 0, st,
+                       A, Y, n_pad, k, nblk, (int)UPD_COL);
+    if (sg_status e = check_launch("factor update (next column)")) return e;
+    const int64_t rest = update_tiles(k, nblk, UPD_REST);
+    hipLaunchKernelGGL(panel_rest_kernel, dim3((unsigned)(nblk + rest)), dim3(256), sizeof(PanelLds),
+                       st, A, Y, n_pad, k, nblk, n, info);
+    if (sg_status e = check_launch("factor panel + rest of update")) return e;
   }
   const unsigned tn = (unsigned)ceil_div(n, 64);
   hipLaunchKernelGGL(finalize_kernel, dim3(tn, tn), dim3(256), 0, st, Y, n, n_pad, Hinv);
