@@ -44,5 +44,7 @@ from .sparsegpt_oracle import (  # noqa: F401
     reconstruction_error,
     reconstruction_error_from_hessian,
     solve_layer,
+    pack_two_four,
+    unpack_two_four,
     unstructured_k,
 )

@@ -28,7 +28,10 @@ class Pattern:
     """A sparsity target.
 
     kind == "unstructured": prune a fraction ``sparsity`` of the weights
-    ([SGR] section 11 step 5, "prune the specified fraction").
+    ([SGR] section 11 step 5: the given fraction is pruned within each column
+    block).  ``per_row`` False: the count is taken over the whole m x w block;
+    ``per_row`` True: every row of the block prunes the same count on its own
+    (the pages do not say which; both readings are offered).
     kind == "nm": keep ``n_keep`` of every ``m_group`` consecutive input
     columns of each row ([SFT] section 8.4: 2:4 keeps 2 of every 4, 16:64 keeps
     16 of every 64; [G24] 2:4 section: the zeros lie along the reduction axis).
@@ -38,6 +41,7 @@ class Pattern:
     sparsity: float = 0.0
     n_keep: int = 0
     m_group: int = 0
+    per_row: bool = False
 
     def __post_init__(self):
         if self.kind == "unstructured":
@@ -51,12 +55,15 @@ class Pattern:
 
 
 def parse_pattern(p) -> Pattern:
-    """``0.5`` -> 50% unstructured; ``"2:4"`` -> keep 2 of every 4."""
+    """``0.5`` -> 50% unstructured over each whole block; ``"0.5/row"`` -> 50%
+    of every row of each block; ``"2:4"`` -> keep 2 of every 4."""
     if isinstance(p, Pattern):
         return p
     if isinstance(p, str) and ":" in p:
         a, b = p.split(":")
         return Pattern("nm", n_keep=int(a), m_group=int(b))
+    if isinstance(p, str) and p.endswith("/row"):
+        return Pattern("unstructured", sparsity=float(p[:-4]), per_row=True)
     return Pattern("unstructured", sparsity=float(p))
 
 
@@ -143,6 +150,14 @@ def _select_block_unstructured(s: np.ndarray, row0_index: np.ndarray, k: int):
     return sel.reshape(s.shape)
 
 
+def _select_rows(s: np.ndarray, k: int):
+    """Boolean mask of the k smallest keys (s, column) of every row."""
+    order = np.argsort(s, axis=1, kind="stable")  # ties: lower column first
+    sel = np.zeros(s.shape, dtype=bool)
+    np.put_along_axis(sel, order[:, :k], True, axis=1)
+    return sel
+
+
 def prune(W: np.ndarray, U: np.ndarray, pattern, blocksize: int,
           mask_in: Optional[np.ndarray] = None, return_trace: bool = False):
     """Column-by-column OBS pruning with immediate (unbatched) compensation.
@@ -160,6 +175,8 @@ def prune(W: np.ndarray, U: np.ndarray, pattern, blocksize: int,
       * unstructured: at each block start, prune exactly
         floor(p * m * w) weights of the whole m x w block, the smallest keys
         (saliency, r*n + c) in lexicographic order (lower index first on ties);
+        per row (``"p/row"``): floor(p * w) weights of each row of the block,
+        the smallest keys (saliency, c);
       * N:M: at each group start (column = 0 mod M), per row, prune the M-N
         smallest keys (saliency, c) of the group;
       * ``mask_in`` (m x n, True = prune) replaces selection;
@@ -193,7 +210,9 @@ def prune(W: np.ndarray, U: np.ndarray, pattern, blocksize: int,
             w = min(blocksize, n - j)
             s = Wh[:, j:j + w] ** 2 / d[j:j + w] ** 2
             sal[:, j:j + w] = s
-            if mask_in is None:
+            if mask_in is None and pat.per_row:
+                mask[:, j:j + w] = _select_rows(s, unstructured_k(pat.sparsity, 1, w))
+            elif mask_in is None:
                 k = unstructured_k(pat.sparsity, m, w)
                 idx = lin + np.arange(j, j + w, dtype=np.int64)[None, :]
                 mask[:, j:j + w] = _select_block_unstructured(s, idx, k)
@@ -206,10 +225,7 @@ def prune(W: np.ndarray, U: np.ndarray, pattern, blocksize: int,
             s = Wh[:, j:j + M] ** 2 / d[j:j + M] ** 2
             sal[:, j:j + M] = s
             if mask_in is None:
-                order = np.argsort(s, axis=1, kind="stable")  # ties: lower column
-                grp = np.zeros((m, M), dtype=bool)
-                np.put_along_axis(grp, order[:, :M - pat.n_keep], True, axis=1)
-                mask[:, j:j + M] = grp
+                mask[:, j:j + M] = _select_rows(s, M - pat.n_keep)
         if mask_in is not None:
             mask[:, j] = np.asarray(mask_in[:, j], dtype=bool)
 
@@ -261,16 +277,16 @@ def prune_free_set(W: np.ndarray, Hd: np.ndarray, pattern, blocksize: int,
         elif pat.kind == "unstructured" and j % blocksize == 0:
             w = min(blocksize, n - j)
             s = Wh[:, j:j + w] ** 2 / diag_at[j:j + w]
-            k = unstructured_k(pat.sparsity, m, w)
-            idx = lin + np.arange(j, j + w, dtype=np.int64)[None, :]
-            mask[:, j:j + w] = _select_block_unstructured(s, idx, k)
+            if pat.per_row:
+                mask[:, j:j + w] = _select_rows(s, unstructured_k(pat.sparsity, 1, w))
+            else:
+                k = unstructured_k(pat.sparsity, m, w)
+                idx = lin + np.arange(j, j + w, dtype=np.int64)[None, :]
+                mask[:, j:j + w] = _select_block_unstructured(s, idx, k)
         elif pat.kind == "nm" and j % pat.m_group == 0:
             M = pat.m_group
             s = Wh[:, j:j + M] ** 2 / diag_at[j:j + M]
-            order = np.argsort(s, axis=1, kind="stable")
-            grp = np.zeros((m, M), dtype=bool)
-            np.put_along_axis(grp, order[:, :M - pat.n_keep], True, axis=1)
-            mask[:, j:j + M] = grp
+            mask[:, j:j + M] = _select_rows(s, M - pat.n_keep)
         rows = np.nonzero(mask[:, j])[0]
         if rows.size:
             wq = Wh[rows, j]
@@ -300,6 +316,67 @@ def reconstruction_error_from_hessian(W, W_hat, H) -> float:
     """Same quantity through H: sum over rows of d H d^T with d = w - ŵ."""
     D = np.asarray(W, dtype=np.float64) - np.asarray(W_hat, dtype=np.float64)
     return float(np.sum((D @ np.asarray(H, dtype=np.float64)) * D))
+
+
+# ----------------------------------------------------------------------------
+# 2:4 compressed export
+# ----------------------------------------------------------------------------
+
+def pack_two_four(W_hat: np.ndarray, mask: np.ndarray):
+    """The 2:4 compressed form of a pruned matrix: the kept values plus a
+    2-bit position index per kept value ([G24] 2:4 core-mechanism section: two
+    of every four consecutive values along the reduction axis are kept and
+    their positions are recorded in 2-bit metadata).
+
+    Readings (the page fixes no byte layout):
+      * group g of row r = columns 4g .. 4g+3; its two slots hold the kept
+        positions in increasing order; a group with fewer than two kept
+        positions fills the remaining slots with its lowest pruned positions
+        (value +0.0), so the slot indices are always two distinct positions
+        i0 < i1;
+      * values[r, 2g + s] = W_hat at slot s (0.0 for a pruned slot);
+      * meta[r, g // 2] holds group g in its low nibble (g even) or high nibble
+        (g odd); the nibble is i0 | (i1 << 2);
+      * a group with more than two kept positions cannot be represented: it
+        is counted in ``bad`` and its two lowest kept positions are stored.
+
+    Returns (values [m, n/2] float64, meta [m, ceil(n/8)] uint8, bad).
+    """
+    W_hat = np.asarray(W_hat, dtype=np.float64)
+    mask = np.asarray(mask, dtype=bool)
+    m, n = W_hat.shape
+    if n % 4 != 0:
+        raise ValueError("2:4 export needs 4 | n")
+    ng = n // 4
+    values = np.zeros((m, 2 * ng), dtype=np.float64)
+    meta = np.zeros((m, (ng + 1) // 2), dtype=np.uint8)
+    bad = 0
+    for r in range(m):
+        for g in range(ng):
+            kept = [i for i in range(4) if not mask[r, 4 * g + i]]
+            pruned = [i for i in range(4) if mask[r, 4 * g + i]]
+            if len(kept) > 2:
+                bad += 1
+            i0, i1 = sorted((kept + pruned)[:2])
+            for slot, i in enumerate((i0, i1)):
+                if not mask[r, 4 * g + i]:
+                    values[r, 2 * g + slot] = W_hat[r, 4 * g + i]
+            meta[r, g // 2] |= (i0 | (i1 << 2)) << (4 * (g % 2))
+    return values, meta, bad
+
+
+def unpack_two_four(values: np.ndarray, meta: np.ndarray, n: int) -> np.ndarray:
+    """Dense m x n matrix from its 2:4 compressed form (inverse of
+    pack_two_four for masks with at most two kept positions per group)."""
+    values = np.asarray(values, dtype=np.float64)
+    m = values.shape[0]
+    out = np.zeros((m, n), dtype=np.float64)
+    for r in range(m):
+        for g in range(n // 4):
+            nib = (int(meta[r, g // 2]) >> (4 * (g % 2))) & 0xF
+            out[r, 4 * g + (nib & 3)] = values[r, 2 * g]
+            out[r, 4 * g + (nib >> 2)] = values[r, 2 * g + 1]
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -227,6 +227,134 @@ def test_unstructured_counts_ragged_and_exact_zeros():
     assert np.all(Wh[~M] != 0.0)
 
 
+# ----------------------------------------------------------------------------
+# a4 per-row unstructured granularity
+# ----------------------------------------------------------------------------
+
+def test_per_row_counts_ragged_and_exact_zeros():
+    W, _, _, _, _, U = _layer(31, 11, 50, 200)
+    B, p = 16, 0.55
+    Wh, M, _ = oracle.prune(W, U, f"{p}/row", B)
+    for j in range(0, W.shape[1], B):
+        w = min(B, W.shape[1] - j)
+        assert np.all(M[:, j:j + w].sum(axis=1) == math.floor(p * w))
+    assert np.all(Wh[M] == 0.0) and not np.any(np.signbit(Wh[M]))
+
+
+def test_per_row_identity_hessian_is_row_magnitude_pruning():
+    # H proportional to I: saliency is w^2 times a constant and nothing is
+    # compensated, so each row of each block drops its floor(p w) smallest
+    # magnitudes (lower column first on ties); brute force per row.
+    r = rng0(32)
+    W = np.round(r.standard_normal((5, 37)), 1)  # rounding creates ties
+    Hd, _ = oracle.dampen(2.0 * np.eye(37), 0.01)
+    U = oracle.inverse_upper_factor(Hd)
+    B, p = 12, 0.4
+    Wh, M, _ = oracle.prune(W, U, f"{p}/row", B)
+    for j in range(0, 37, B):
+        w = min(B, 37 - j)
+        k = math.floor(p * w)
+        for row in range(5):
+            keyed = sorted((abs(W[row, j + c]), c) for c in range(w))
+            want = np.zeros(w, dtype=bool)
+            for _, c in keyed[:k]:
+                want[c] = True
+            assert np.array_equal(M[row, j:j + w], want)
+    assert np.array_equal(Wh[~M], W[~M])
+
+
+def test_per_row_exhaustive_single_weight_choice_n8():
+    # one pruned weight per row of an 8-wide block: each row's pick is the
+    # argmin over its 8 single-weight masks of the exact damped error
+    # min_v (w - v) H_d (w - v)^T with v_q = 0 (textbook least squares)
+    W, _, _, Hd, _, U = _layer(33, 6, 8, 60)
+    _, M, _ = oracle.prune(W, U, "0.125/row", 8)
+    for row in range(6):
+        w = W[row]
+        errs = []
+        for q in range(8):
+            K = [c for c in range(8) if c != q]
+            v = np.zeros(8)
+            v[K] = np.linalg.solve(Hd[np.ix_(K, K)], Hd[K, :] @ w)
+            errs.append(_quad(w - v, Hd))
+        assert M[row].sum() == 1 and int(np.argmax(M[row])) == int(np.argmin(errs))
+
+
+def test_per_row_rows_independent_and_one_row_equals_block_global():
+    W, _, _, _, _, U = _layer(34, 7, 40, 150)
+    Wa, Ma, _ = oracle.prune(W, U, "0.6/row", 16)
+    for row in range(7):
+        Wb, Mb, _ = oracle.prune(W[row:row + 1], U, "0.6/row", 16)
+        Wc, Mc, _ = oracle.prune(W[row:row + 1], U, 0.6, 16)
+        assert np.array_equal(Ma[row], Mb[0]) and np.array_equal(Wa[row], Wb[0])
+        assert np.array_equal(Mb, Mc) and np.array_equal(Wb, Wc)
+
+
+def test_per_row_with_block_m_equals_nm():
+    # keeping N of every M per row with B = M is the per-row rule with
+    # p = (M - N) / M (exact in binary for these fractions)
+    W, _, _, _, _, U = _layer(35, 6, 64, 200)
+    for N, M in ((2, 4), (16, 64), (4, 8)):
+        a = oracle.prune(W, U, f"{N}:{M}", M)
+        b = oracle.prune(W, U, f"{(M - N) / M}/row", M)
+        assert np.array_equal(a[1], b[1]) and np.array_equal(a[0], b[0])
+
+
+# ----------------------------------------------------------------------------
+# 2:4 compressed export
+# ----------------------------------------------------------------------------
+
+def test_two_four_pack_golden():
+    with open(os.path.join(GOLDEN, "two_four_packed.json")) as f:
+        fx = json.load(f)
+    for row in fx["rows"]:
+        dense = np.array([row["dense"]])
+        pruned = np.array([row["pruned"]], dtype=bool)
+        Wh = np.where(pruned, 0.0, dense)
+        vals, meta, bad = oracle.pack_two_four(Wh, pruned)
+        assert bad == 0
+        assert np.array_equal(vals[0], np.array(row["values"]))
+        assert list(meta[0]) == row["meta"]
+
+
+def test_two_four_pack_of_pruned_layer_round_trips():
+    W, _, _, _, _, U = _layer(36, 9, 48, 200)
+    Wh, M, _ = oracle.prune(W, U, "2:4", 16)
+    vals, meta, bad = oracle.pack_two_four(Wh, M)
+    assert bad == 0 and vals.shape == (9, 24) and meta.shape == (9, 6)
+    assert np.array_equal(oracle.unpack_two_four(vals, meta, 48), Wh)
+    # every slot index is a kept position, in increasing order
+    for r in range(9):
+        for g in range(12):
+            nib = (int(meta[r, g // 2]) >> (4 * (g % 2))) & 0xF
+            i0, i1 = nib & 3, nib >> 2
+            assert i0 < i1 and not M[r, 4 * g + i0] and not M[r, 4 * g + i1]
+            assert vals[r, 2 * g] == Wh[r, 4 * g + i0] and vals[r, 2 * g + 1] == Wh[r, 4 * g + i1]
+
+
+def test_two_four_pack_sparse_groups_and_unrepresentable_count():
+    r = rng0(37)
+    m, n = 6, 40
+    Wd = r.standard_normal((m, n))
+    # per group: 0..4 pruned positions chosen at random
+    M = np.zeros((m, n), dtype=bool)
+    want_bad = 0
+    for row in range(m):
+        for g in range(n // 4):
+            k = int(r.integers(0, 5))
+            M[row, 4 * g + r.permutation(4)[:k]] = True
+            want_bad += int(4 - k > 2)
+    Wh = np.where(M, 0.0, Wd)
+    vals, meta, bad = oracle.pack_two_four(Wh, M)
+    assert bad == want_bad
+    back = oracle.unpack_two_four(vals, meta, n)
+    for row in range(m):
+        for g in range(n // 4):
+            sl = slice(4 * g, 4 * g + 4)
+            if (~M[row, sl]).sum() <= 2:
+                assert np.array_equal(back[row, sl], Wh[row, sl])
+
+
 @pytest.mark.parametrize("nm", ["2:4", "4:8", "16:32", "16:64", "3:8"])
 def test_nm_exact_groups(nm):
     W, _, _, _, _, U = _layer(12, 9, 64, 300)
@@ -326,7 +454,7 @@ def test_row_permutation_equivariance_nm():
     assert np.array_equal(Ma[perm], Mb) and np.array_equal(Wa[perm], Wb)
 
 
-@pytest.mark.parametrize("pat", [0.5, "2:4", "4:8"])
+@pytest.mark.parametrize("pat", [0.5, "0.5/row", "2:4", "4:8"])
 def test_free_set_route_matches_cholesky_route(pat):
     W, _, _, Hd, _, U = _layer(20, 7, 48, 200)
     a = oracle.prune(W, U, pat, 16)
