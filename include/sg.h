@@ -66,7 +66,7 @@ enum {
 enum { SG_F32 = 0, SG_BF16 = 1 };
 
 /* sparsity pattern kinds */
-enum { SG_UNSTRUCTURED = 0, SG_NM = 1 };
+enum { SG_UNSTRUCTURED = 0, SG_NM = 1, SG_UNSTRUCTURED_ROW = 2 };
 
 /* operations, for sg_workspace_bytes */
 enum {
@@ -151,6 +151,10 @@ sg_status sg_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp,
  *     block may be narrower) exactly floor(sparsity * m * w) weights of the
  *     whole m x w block are pruned: the smallest keys (saliency, r*n + c),
  *     lower index first on equal saliency;
+ *   - SG_UNSTRUCTURED_ROW: at the start of each column block of width w,
+ *     every row prunes floor(sparsity * w) of its own w weights, the smallest
+ *     keys (saliency, c) of the row (the per-row reading of the same
+ *     fraction-per-block rule);
  *   - SG_NM: at each group start (column = 0 mod m_group), per row, the
  *     m_group - n_keep smallest keys (saliency, c) of the group are pruned;
  *   - the compensation of each block reaches the columns after it through one
@@ -164,9 +168,10 @@ sg_status sg_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp,
  *            0 = kept.  May be NULL.
  *   W        [m x ldw] in, SG_F32 or SG_BF16, not modified (unless aliased).
  *   Hinv     [n x n] fp32 in: the factor from sg_prepare_hinv for this n.
- *   pattern_kind SG_UNSTRUCTURED (uses sparsity in [0, 1]) or SG_NM (uses
- *            n_keep, m_group with 0 <= n_keep <= m_group, m_group dividing
- *            both n and blocksize).
+ *   pattern_kind SG_UNSTRUCTURED or SG_UNSTRUCTURED_ROW (use sparsity in
+ *            [0, 1]) or SG_NM (uses n_keep, m_group with 0 <= n_keep <=
+ *            m_group, m_group dividing both n and blocksize, and either
+ *            dividing 16 or a multiple of 16).
  *   blocksize 1 <= blocksize <= SG_MAX_BLOCKSIZE.
  *   mask_in  optional [m x n] uint8 (contiguous, 1 = prune): when not NULL it
  *            replaces the selection (the pattern is still validated).
@@ -200,6 +205,37 @@ sg_status sg_reconstruction_error(double* err, int32_t accumulate,
                                   const void* X, int32_t x_dtype, int64_t T,
                                   int64_t ldx, void* workspace,
                                   size_t ws_bytes, void* stream);
+
+/*
+ * sg_pack_two_four -- the 2:4 compressed form of a pruned matrix: its kept
+ * values and a 2-bit position for each.
+ *
+ * [G24] 2:4 core-mechanism section: two of every four consecutive values
+ * along the reduction axis are kept, and 2-bit metadata records where they
+ * sit.  The page fixes no byte layout; this one is:
+ *   - group g of row r is columns 4g .. 4g+3; its two slots hold two distinct
+ *     positions i0 < i1: the kept positions, and if fewer than two are kept,
+ *     the lowest pruned positions (stored value +0.0);
+ *   - values[r * (n/2) + 2g + s] = W_hat at slot s, in v_dtype (SG_F32: the
+ *     fp32 value; SG_BF16: rounded to nearest, ties to even);
+ *   - meta[r * ceil(n/8) + g/2] holds the nibble i0 | (i1 << 2) of group g,
+ *     in the low half of the byte for even g and the high half for odd g;
+ *   - a group with more than two kept positions cannot be represented: its
+ *     two lowest kept positions are stored and it is counted in *bad.
+ *
+ *   values  [m x n/2] out, v_dtype, contiguous.
+ *   meta    [m x ceil(n/8)] uint8 out, contiguous.
+ *   bad     one device int32 out: the number of unrepresentable groups (0
+ *           for every mask sg_prune_layer returns with pattern 2:4).
+ *   W_hat   [m x n] fp32 in, contiguous (e.g. W_out of sg_prune_layer).
+ *   mask    [m x n] uint8 in, contiguous, 1 = pruned.
+ *   n       a multiple of 4; m >= 1.
+ * Entries of W_hat at pruned positions are not read.
+ */
+sg_status sg_pack_two_four(void* values, int32_t v_dtype, uint8_t* meta,
+                           int32_t* bad, const float* W_hat,
+                           const uint8_t* mask, int64_t m, int64_t n,
+                           void* stream);
 
 /* Workspace bytes for an operation (m, n, T, blocksize as in its call; pass 0
  * for arguments the operation does not take).  Pure host arithmetic: touches

@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libsg.so")
 
 SG_OK, SG_ERR_INVALID_ARGUMENT, SG_ERR_UNSUPPORTED, SG_ERR_WORKSPACE, SG_ERR_HIP = range(5)
 SG_F32, SG_BF16 = 0, 1
-SG_UNSTRUCTURED, SG_NM = 0, 1
+SG_UNSTRUCTURED, SG_NM, SG_UNSTRUCTURED_ROW = 0, 1, 2
 SG_OP_HESSIAN, SG_OP_PREPARE_HINV, SG_OP_PRUNE, SG_OP_RECON = range(4)
 SG_MAX_BLOCKSIZE = 128
 
@@ -59,8 +59,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    c_dbl, c_i32, c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]
     lib.sg_reconstruction_error.argtypes = [c_vp, c_i32, c_vp, c_i32, c_i64, c_vp, c_i64, c_i64,
                                             c_vp, c_i32, c_i64, c_i64, c_vp, c_sz, c_vp]
+    lib.sg_pack_two_four.argtypes = [c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp]
     for f in ("sg_hessian_accumulate", "sg_prepare_hinv", "sg_prune_layer",
-              "sg_reconstruction_error"):
+              "sg_reconstruction_error", "sg_pack_two_four"):
         getattr(lib, f).restype = c_i32
     lib.sg_workspace_bytes.argtypes = [c_i32, c_i64, c_i64, c_i64, c_i32]
     lib.sg_workspace_bytes.restype = c_sz
@@ -174,10 +175,13 @@ def sg_prepare_hinv(H: torch.Tensor, damp: float = 0.01, Hinv: Optional[torch.Te
 
 
 def parse_pattern(pattern: Union[float, str]):
-    """0.5 -> (SG_UNSTRUCTURED, 0.5, 0, 1); "2:4" -> (SG_NM, 0.0, 2, 4)."""
+    """0.5 -> (SG_UNSTRUCTURED, 0.5, 0, 1); "0.5/row" -> (SG_UNSTRUCTURED_ROW,
+    0.5, 0, 1); "2:4" -> (SG_NM, 0.0, 2, 4)."""
     if isinstance(pattern, str) and ":" in pattern:
         a, b = pattern.split(":")
         return SG_NM, 0.0, int(a), int(b)
+    if isinstance(pattern, str) and pattern.endswith("/row"):
+        return SG_UNSTRUCTURED_ROW, float(pattern[:-4]), 0, 1
     return SG_UNSTRUCTURED, float(pattern), 0, 1
 
 
@@ -232,6 +236,41 @@ def sg_reconstruction_error(W: torch.Tensor, W_hat: torch.Tensor, X: torch.Tenso
                                        _ptr(ws), nb, ctypes.c_void_p(_stream(W.device))),
            "sg_reconstruction_error")
     return err
+
+
+def sg_pack_two_four(W_hat: torch.Tensor, mask: torch.Tensor,
+                     value_dtype: torch.dtype = torch.float32,
+                     values: Optional[torch.Tensor] = None, meta: Optional[torch.Tensor] = None):
+    """2:4 compressed form of a pruned [m, n] matrix.
+
+    Returns (values [m, n/2] of ``value_dtype`` (float32 or bfloat16),
+    meta [m, ceil(n/8)] uint8, bad: device int32 count of groups with more than
+    two kept positions)."""
+    lib = load_library()
+    _require_cuda(W_hat, mask)
+    m, n = W_hat.shape
+    if W_hat.dtype != torch.float32 or not W_hat.is_contiguous():
+        raise ValueError("W_hat must be a contiguous float32 tensor")
+    if mask.shape != (m, n) or not mask.is_contiguous():
+        raise ValueError("mask must be a contiguous [m, n] tensor")
+    mask = mask.to(torch.uint8)
+    if value_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("value_dtype must be float32 or bfloat16")
+    if values is None:
+        values = torch.empty(m, n // 2, dtype=value_dtype, device=W_hat.device)
+    elif (values.shape != (m, n // 2) or values.dtype != value_dtype or not values.is_contiguous()
+          or not values.is_cuda):
+        raise ValueError("values must be a contiguous [m, n/2] GPU tensor of value_dtype")
+    if meta is None:
+        meta = torch.empty(m, (n + 7) // 8, dtype=torch.uint8, device=W_hat.device)
+    elif meta.shape != (m, (n + 7) // 8) or meta.dtype != torch.uint8 or not meta.is_contiguous() \
+            or not meta.is_cuda:
+        raise ValueError("meta must be a contiguous [m, ceil(n/8)] uint8 GPU tensor")
+    bad = torch.empty(1, dtype=torch.int32, device=W_hat.device)
+    _check(lib.sg_pack_two_four(_ptr(values), _dtype_code(values), _ptr(meta), _ptr(bad),
+                                _ptr(W_hat), _ptr(mask), m, n,
+                                ctypes.c_void_p(_stream(W_hat.device))), "sg_pack_two_four")
+    return values, meta, bad
 
 
 def solve_layer(W: torch.Tensor, x_chunks, pattern, blocksize: int = 128, damp: float = 0.01):

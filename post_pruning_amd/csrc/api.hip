@@ -155,7 +155,7 @@ sg_status sg_prune_layer(float* W_out, uint8_t* mask_out, const void* W, int32_t
     return set_error(SG_ERR_INVALID_ARGUMENT, "W_out may alias W only for fp32 W with ldw == n");
   if (blocksize < 1 || blocksize > SG_MAX_BLOCKSIZE)
     return set_error(SG_ERR_UNSUPPORTED, "blocksize %d out of [1, %d]", blocksize, SG_MAX_BLOCKSIZE);
-  if (pattern_kind == SG_UNSTRUCTURED) {
+  if (pattern_kind == SG_UNSTRUCTURED || pattern_kind == SG_UNSTRUCTURED_ROW) {
     if (!(sparsity >= 0.0 && sparsity <= 1.0))
       return set_error(SG_ERR_INVALID_ARGUMENT, "sparsity must lie in [0, 1]");
   } else if (pattern_kind == SG_NM) {
@@ -214,6 +214,23 @@ sg_status sg_reconstruction_error(double* err, int32_t accumulate, const void* W
   if (sg_status e = check_device()) return e;
   return launch_recon(err, accumulate, W, w_dtype, ldw, W_hat, m, n, X, x_dtype, T, ldx, workspace,
                       static_cast<hipStream_t>(stream));
+}
+
+sg_status sg_pack_two_four(void* values, int32_t v_dtype, uint8_t* meta, int32_t* bad,
+                           const float* W_hat, const uint8_t* mask, int64_t m, int64_t n,
+                           void* stream) {
+  g_last_error.clear();
+  if (!values || !meta || !bad || !W_hat || !mask)
+    return set_error(SG_ERR_INVALID_ARGUMENT, "values, meta, bad, W_hat and mask must not be NULL");
+  if (m < 1 || n < 4) return set_error(SG_ERR_INVALID_ARGUMENT, "m must be >= 1 and n >= 4");
+  if (n % 4 != 0) return set_error(SG_ERR_INVALID_ARGUMENT, "n=%lld is not a multiple of 4", (long long)n);
+  if ((unsigned long long)m * (unsigned long long)n >= (1ull << 40))
+    return set_error(SG_ERR_UNSUPPORTED, "m*n too large");
+  if (v_dtype != SG_F32 && v_dtype != SG_BF16)
+    return set_error(SG_ERR_UNSUPPORTED, "v_dtype %d not supported", v_dtype);
+  if (sg_status e = check_device()) return e;
+  return launch_pack_two_four(values, v_dtype, meta, bad, W_hat, mask, m, n,
+                              static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -35,7 +35,7 @@ namespace {
 constexpr int SB = SG_MAX_BLOCKSIZE;  // 128
 constexpr int EGK = 512;              // columns of a lazy-update group (error buffer width)
 
-enum { MODE_THRESH = 0, MODE_NM = 1, MODE_FORCED = 2 };
+enum { MODE_THRESH = 0, MODE_NM = 1, MODE_FORCED = 2, MODE_ROW = 3 };
 
 // Radix-select buffers, double-buffered by block parity: the sweep of block b
 // clears the set block b + 1 will use while nobody reads it.
@@ -567,8 +567,10 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   }
 
   float* Es = S.Es[wave];
+  // groups ranked from registers (M <= 16) or through the staging tile (M >
+  // 16, and the per-row mode, whose group is the whole block: mgroup = w)
   const bool nm_small = MODE == MODE_NM && mgroup <= 16;
-  const bool nm_large = MODE == MODE_NM && mgroup > 16;
+  const bool nm_large = (MODE == MODE_NM && mgroup > 16) || MODE == MODE_ROW;
   const unsigned rowbits = (rowok[0] ? 1u : 0u) | (rowok[1] ? 2u : 0u) | (rowok[2] ? 4u : 0u) |
                            (rowok[3] ? 8u : 0u);
 #pragma unroll
@@ -591,9 +593,9 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
         cx.g[j] = (j == lc) ? 0.f : S.Ub[(16 * c + j) * SWS + col] * rdj[j];
     }
     if (nm_large && ((16 * c) % mgroup) == 0) {
-      // group of M >= 32 columns = chunks c .. c + M/16 - 1 (all current)
+      // group of mgroup columns = chunks c .. c + ceil(mgroup/16) - 1 (all current)
       float* sc = Tw;
-      const int nchg = mgroup >> 4;
+      const int nchg = (mgroup + 15) >> 4;
       for (int g = 0; g < nchg && c + g < 8; ++g) {
         const int col = 16 * (c + g) + lc;
         const float ucg = S.Ub[col * SWS + col];
@@ -607,7 +609,8 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
         for (int v = 0; v < 4; ++v) {
           const float* row = sc + (4 * lg + v) * SWS;
           const int me = 16 * g + lc;
-          if (rowok[v] && rank_of(row, mgroup, row[me], me) < mgroup - nkeep) Pm[c + g] |= 1u << v;
+          if (rowok[v] && me < mgroup && rank_of(row, mgroup, row[me], me) < mgroup - nkeep)
+            Pm[c + g] |= 1u << v;
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -776,15 +779,17 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(select_pass_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SelLds)) != hipSuccess)
     return set_error(SG_ERR_HIP, "hipFuncSetAttribute(select_pass_kernel) failed");
-  const void* sweep_fns[3] = {reinterpret_cast<const void*>(sweep_kernel<MODE_THRESH>),
+  const void* sweep_fns[4] = {reinterpret_cast<const void*>(sweep_kernel<MODE_THRESH>),
                               reinterpret_cast<const void*>(sweep_kernel<MODE_NM>),
-                              reinterpret_cast<const void*>(sweep_kernel<MODE_FORCED>)};
+                              reinterpret_cast<const void*>(sweep_kernel<MODE_FORCED>),
+                              reinterpret_cast<const void*>(sweep_kernel<MODE_ROW>)};
   for (const void* f : sweep_fns)
     if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SweepLds)) !=
         hipSuccess)
       return set_error(SG_ERR_HIP, "hipFuncSetAttribute(sweep_kernel) failed");
 
-  const int mode = a.mask_in ? MODE_FORCED : (a.kind == SG_NM ? MODE_NM : MODE_THRESH);
+  const int mode = a.mask_in ? MODE_FORCED
+                             : (a.kind == SG_NM ? MODE_NM : (a.kind == SG_UNSTRUCTURED_ROW ? MODE_ROW : MODE_THRESH));
   const int B = a.blocksize;
   if (mode == MODE_THRESH) {
     hipLaunchKernelGGL(sel_clear_kernel, dim3(1), dim3(256), 0, st, sel);
@@ -827,6 +832,11 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
     else if (mode == MODE_NM)
       hipLaunchKernelGGL(sweep_kernel<MODE_NM>, sw_grid, sw_block, shm, st, a.W_out, a.mask_out, Eb,
                          a.U, a.mask_in, sel, cand, 0, 0ll, 0, m, n, i1, w, a.n_keep, a.m_group);
+    else if (mode == MODE_ROW)
+      // one group per row spanning the block: keep w - floor(p * w)
+      hipLaunchKernelGGL(sweep_kernel<MODE_ROW>, sw_grid, sw_block, shm, st, a.W_out, a.mask_out, Eb,
+                         a.U, a.mask_in, sel, cand, 0, 0ll, 0, m, n, i1, w,
+                         w - (int)floor(a.sparsity * (double)w), w);
     else
       hipLaunchKernelGGL(sweep_kernel<MODE_FORCED>, sw_grid, sw_block, shm, st, a.W_out, a.mask_out,
                          Eb, a.U, a.mask_in, sel, cand, 0, 0ll, 0, m, n, i1, w, a.n_keep, a.m_group);

@@ -78,6 +78,13 @@ size_t prune_ws_bytes(int64_t m, int64_t n, int blocksize);
 sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st);
 
 // ---------------------------------------------------------------------------
+// 2:4 compressed export
+// ---------------------------------------------------------------------------
+sg_status launch_pack_two_four(void* values, int v_dtype, uint8_t* meta, int32_t* bad,
+                               const float* W_hat, const uint8_t* mask, int64_t m, int64_t n,
+                               hipStream_t st);
+
+// ---------------------------------------------------------------------------
 // Reconstruction error
 // ---------------------------------------------------------------------------
 size_t recon_ws_bytes(int64_t m, int64_t T);

@@ -83,6 +83,8 @@ def test_null_pointers_rejected_before_device(sg):
     assert st == sg.SG_ERR_INVALID_ARGUMENT
     st = lib.sg_reconstruction_error(None, 0, None, 0, 4, None, 4, 4, None, 0, 4, 4, None, 0, None)
     assert st == sg.SG_ERR_INVALID_ARGUMENT
+    st = lib.sg_pack_two_four(None, 0, None, None, None, None, 4, 8, None)
+    assert st == sg.SG_ERR_INVALID_ARGUMENT
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation first
@@ -116,6 +118,7 @@ def test_prepare_validation(sg, args, code):
 
 @pytest.mark.parametrize("args,code", [
     (dict(kind=0, sp=1.5), 1),            # sparsity out of [0, 1]
+    (dict(kind=2, sp=-0.1), 1),           # per-row sparsity out of [0, 1]
     (dict(kind=1, nk=3, mg=2), 1),        # N > M
     (dict(kind=1, nk=2, mg=3, n=96, bs=96), 2),  # M neither divides nor is a multiple of 16
     (dict(kind=1, nk=2, mg=4, n=130), 1),  # M does not divide n
@@ -147,6 +150,17 @@ def test_recon_validation(sg):
     assert st == sg.SG_ERR_WORKSPACE
 
 
+@pytest.mark.parametrize("m,n,dt,code", [
+    (4, 10, 0, 1),   # n not a multiple of 4
+    (0, 8, 0, 1),    # m < 1
+    (4, 0, 0, 1),    # n < 4
+    (4, 8, 7, 2),    # value dtype
+])
+def test_pack_validation(sg, m, n, dt, code):
+    st = _lib(sg).sg_pack_two_four(FAKE, dt, FAKE, FAKE, FAKE, FAKE, m, n, None)
+    assert st == code, sg.sg_last_error_message()
+
+
 def test_product_path_imports_no_oracle():
     # The library binding must not import, call or read the oracle.
     src_dir = os.path.join(ROOT, "post_pruning_amd")
@@ -161,3 +175,5 @@ def test_pattern_parsing(sg):
     assert sg.parse_pattern(0.5) == (sg.SG_UNSTRUCTURED, 0.5, 0, 1)
     assert sg.parse_pattern("2:4") == (sg.SG_NM, 0.0, 2, 4)
     assert sg.parse_pattern("16:64") == (sg.SG_NM, 0.0, 16, 64)
+    assert sg.parse_pattern("16:128") == (sg.SG_NM, 0.0, 16, 128)
+    assert sg.parse_pattern("0.5/row") == (sg.SG_UNSTRUCTURED_ROW, 0.5, 0, 1)

@@ -187,6 +187,20 @@ def test_mlp_up_11008_nm_rows(sg, attn_oracle):
     E_gpu = oracle.reconstruction_error_from_hessian(Wd, Whg[rows], Hd_full)
     E_o = oracle.reconstruction_error_from_hessian(Wd, Who, Hd_full)
     assert abs(E_gpu - E_o) <= 1e-3 * E_o
+    # 2:4 compressed export of the whole layer; sampled rows against the oracle
+    _say("mlp_up_11008: 2:4 export")
+    vo, mo, bo = oracle.pack_two_four(Whg[rows], gm[rows])
+    assert bo == 0
+    for vdt in (torch.float32, torch.bfloat16):
+        vals, meta, bad = sg.sg_pack_two_four(Wh, mask, value_dtype=vdt)
+        torch.cuda.synchronize()
+        assert int(bad.item()) == 0
+        ri = torch.from_numpy(rows).cuda()
+        vg = vals.index_select(0, ri).cpu()
+        want = torch.from_numpy(vo.astype(np.float32)).to(vdt)
+        iv = torch.int16 if vdt == torch.bfloat16 else torch.int32
+        assert torch.equal(vg.view(iv), want.view(iv))
+        assert np.array_equal(meta.index_select(0, ri).cpu().numpy(), mo)
 
 
 # ---------------------------------------------------------------------------

@@ -54,11 +54,12 @@ def _rel(a, b):
 CASES = [
     # name, m, n, tokens, dtype, act, outliers, factor, patterns, blocksize, chunk
     ("tiny", 64, 128, 512, "f32", "linear", 0, 1.0, ("0.5",), 32, 512),
-    ("attn_s", 256, 512, 16384, "bf16", "linear", 8, 20.0, ("0.5",), 128, 8192),
-    ("mlpup_s", 384, 512, 8192, "bf16", "linear", 8, 20.0, ("2:4",), 128, 8192),
+    ("attn_s", 256, 512, 16384, "bf16", "linear", 8, 20.0, ("0.5", "16:128"), 128, 8192),
+    ("mlpup_s", 384, 512, 8192, "bf16", "linear", 8, 20.0, ("2:4", "0.5/row"), 128, 8192),
     ("mlpdown_s", 256, 640, 8192, "bf16", "relu", 6, 10.0, ("0.6", "4:8"), 128, 4096),
-    ("ragged", 200, 1000, 3000, "bf16", "linear", 4, 20.0, ("0.5",), 128, 1700),
-    ("ragged_b64", 130, 384, 2000, "f32", "relu", 3, 10.0, ("0.55", "2:4", "16:64"), 64, 2000),
+    ("ragged", 200, 1000, 3000, "bf16", "linear", 4, 20.0, ("0.5", "0.6/row"), 128, 1700),
+    ("ragged_b64", 130, 384, 2000, "f32", "relu", 3, 10.0, ("0.55", "2:4", "16:64", "0.55/row"), 64,
+     2000),
     ("b32", 96, 256, 4096, "bf16", "linear", 2, 20.0, ("0.5", "1:4", "16:32"), 32, 4096),
 ]
 
@@ -156,6 +157,11 @@ def _check_counts(mask, pattern, B):
         N, M = map(int, pattern.split(":"))
         g = mask.reshape(m, -1, M).sum(axis=2)
         assert np.all(g == M - N)
+    elif pattern.endswith("/row"):
+        p = float(pattern[:-4])
+        for j in range(0, n, B):
+            w = min(B, n - j)
+            assert np.all(mask[:, j:j + w].sum(axis=1) == math.floor(p * w))
     else:
         p = float(pattern)
         for j in range(0, n, B):
@@ -178,6 +184,15 @@ def _check_selection_consistency(Wd, U, pattern, B, gmask):
             lo = np.where(~g, s, np.inf).min(axis=1)
             bad = hi > lo * (1 + TAU) + 1e-300
             assert not bad.any(), f"group at column {j}: rows {np.nonzero(bad)[0][:5]}"
+    elif pattern.endswith("/row"):
+        for j in range(0, n, B):
+            w = min(B, n - j)
+            s = S[:, j:j + w]
+            g = gmask[:, j:j + w]
+            hi = np.where(g, s, -np.inf).max(axis=1)
+            lo = np.where(~g, s, np.inf).min(axis=1)
+            bad = hi > lo * (1 + TAU) + 1e-300
+            assert not bad.any(), f"block at column {j}: rows {np.nonzero(bad)[0][:5]}"
     else:
         for j in range(0, n, B):
             w = min(B, n - j)
@@ -230,6 +245,52 @@ def test_prune_parity(sg, case):
         assert abs(E_gpu - E_o) <= 1e-3 * E_o
         E_same = oracle.reconstruction_error(ref["Wd"], Whg, ref["chunks"])
         assert abs(E_gpu - E_same) <= 1e-5 * E_same
+
+
+def _oracle_pack_check(sg, Wh, mask, rows=None):
+    """GPU 2:4 export of (Wh, mask) against the oracle's, bit for bit, in fp32
+    and bf16 (the oracle's fp32 values rounded by torch's CPU conversion)."""
+    Wh_h = Wh.cpu().numpy()
+    M_h = mask.cpu().numpy().astype(bool)
+    if rows is not None:
+        Wh_h, M_h = Wh_h[rows], M_h[rows]
+    vo, mo, bo = oracle.pack_two_four(Wh_h, M_h)
+    for vdt in (torch.float32, torch.bfloat16):
+        vals, meta, bad = sg.sg_pack_two_four(Wh, mask, value_dtype=vdt)
+        torch.cuda.synchronize()
+        vg, mg = vals.cpu(), meta.cpu().numpy()
+        if rows is not None:
+            vg, mg = vg[rows], mg[rows]
+        want = torch.from_numpy(vo.astype(np.float32)).to(vdt)
+        assert torch.equal(vg.view(torch.int16 if vdt == torch.bfloat16 else torch.int32),
+                           want.view(torch.int16 if vdt == torch.bfloat16 else torch.int32))
+        assert np.array_equal(mg, mo)
+        if rows is None:
+            assert int(bad.item()) == bo
+    return bo
+
+
+def test_two_four_export_of_pruned_layer(sg):
+    ref = _oracle_layer(CASES[2])  # mlpup_s, 2:4
+    cfg = ref["cfg"]
+    _, Hinv = _gpu_factor(sg, ref)
+    Wh, mask = sg.sg_prune_layer(ref["W"].cuda(), Hinv, "2:4", cfg.blocksize)
+    torch.cuda.synchronize()
+    assert _oracle_pack_check(sg, Wh, mask) == 0
+    vals, meta, _ = sg.sg_pack_two_four(Wh, mask)
+    back = oracle.unpack_two_four(vals.cpu().double().numpy(), meta.cpu().numpy(), cfg.n)
+    assert np.array_equal(back, Wh.cpu().double().numpy())
+
+
+@pytest.mark.parametrize("m,n", [(37, 44), (64, 512), (5, 4)])
+def test_two_four_export_any_mask(sg, m, n):
+    # random masks with 0..4 pruned per group (unrepresentable groups counted);
+    # n = 44 and n = 4 take the unaligned path with a half-filled metadata byte
+    g = torch.Generator().manual_seed(m * 1000 + n)
+    Wd = torch.randn(m, n, generator=g)
+    mask = (torch.rand(m, n, generator=g) < torch.rand(m, 1, generator=g)).to(torch.uint8)
+    Wh = torch.where(mask.bool(), torch.zeros_like(Wd), Wd)
+    _oracle_pack_check(sg, Wh.cuda(), mask.cuda())
 
 
 def test_sparsity_zero_and_one(sg):
