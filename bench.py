@@ -216,6 +216,32 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
 
+    export = None
+    if pattern == "2:4":
+        # 2:4 compressed export of the step's result (not part of the step):
+        # HBM-bound, algorithmic bytes per weight 4 + 1 in, value bytes / 2 +
+        # 1/8 out
+        export = {}
+        for vdt, vb in ((torch.float32, 4), (torch.bfloat16, 2)):
+            vals = torch.empty(m, n // 2, dtype=vdt, device=dev)
+            meta = torch.empty(m, (n + 7) // 8, dtype=torch.uint8, device=dev)
+            for _ in range(2):
+                sg.sg_pack_two_four(W_out, mask, value_dtype=vdt, values=vals, meta=meta)
+            reps = 20
+            e0, e1 = ev(), ev()
+            e0.record()
+            for _ in range(reps):
+                sg.sg_pack_two_four(W_out, mask, value_dtype=vdt, values=vals, meta=meta)
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / reps
+            nbytes = m * n * 5.0 + m * (n // 2) * vb + m * ((n + 7) // 8)
+            gbs = nbytes / (t * 1e-3) / 1e9
+            export["values_" + ("f32" if vb == 4 else "bf16")] = {
+                "kernel": "pack24_kernel (sg_pack_two_four)", "bound": "hbm", "ms": t,
+                "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                "algorithmic_bytes": nbytes}
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a host sample", file=sys.stderr, flush=True)
@@ -261,6 +287,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if export is not None:
+        line["two_four_export"] = export
     print(json.dumps(line))
 
 

@@ -353,6 +353,16 @@ __device__ __forceinline__ int rank_of(const float* sal, int cnt, float my, int 
   return rank;
 }
 
+// Sum of x over the 16 lanes of a DPP row, returned in every lane of the row
+// (Hillis-Steele scan by row_shr 1, 2, 4, 8, then lane 15 broadcast).
+__device__ __forceinline__ int rowsum16(int x) {
+  x += __builtin_amdgcn_mov_dpp(x, 0x111, 0xF, 0xF, true);
+  x += __builtin_amdgcn_mov_dpp(x, 0x112, 0xF, 0xF, true);
+  x += __builtin_amdgcn_mov_dpp(x, 0x114, 0xF, 0xF, true);
+  x += __builtin_amdgcn_mov_dpp(x, 0x118, 0xF, 0xF, true);
+  return __builtin_amdgcn_mov_dpp(x, 0x15F, 0xF, 0xF, true);
+}
+
 // Per-chunk constants of one lane (its column col = 16c + lc of the chunk):
 //   g[j] = U[16c + j][col] / U_JJ for j != lc, 0 for j == lc;
 // the owner lane of column J keeps its value frozen from step J on, so the
@@ -366,23 +376,34 @@ struct ChunkCtx {
 // Sweep column j of the chunk (compile-time j: static DPP lane and indices).
 // Chain per step and row: select (pruned ? W_J : 0) on the owner lane, DPP
 // broadcast over the 16 lanes of the row, fused multiply-add.
-template <int J, bool NM_SMALL>
+// 1 if member T of the group starting at lane J precedes this lane's value
+// in (saliency, position) order
+template <int J, int T>
+__device__ __forceinline__ int ahead_of(float my, int me) {
+  const float o = bcast16_c<J + T>(my);
+  return (o < my || (o == my && T < me)) ? 1 : 0;
+}
+
+template <int J, int... Ts>
+__device__ __forceinline__ int group_rank(std::integer_sequence<int, Ts...>, float my, int me) {
+  return (ahead_of<J, Ts>(my, me) + ... + 0);
+}
+
+template <int J, int MGS>
 __device__ __forceinline__ void sweep_step(floatx4& Wc, unsigned& Pc, const ChunkCtx& cx, int lc,
-                                           int mgroup, int nkeep, unsigned rowbits) {
-  if constexpr (NM_SMALL) {
-    if ((J % mgroup) == 0) {
-      // rank the group's M columns (lanes J..J+M-1 of the row) at its start
-      const bool in = lc >= J && lc < J + mgroup;
-      const int base = (threadIdx.x & 63) & ~15;
+                                           int nkeep, unsigned rowbits) {
+  if constexpr (MGS > 0) {
+    if constexpr ((J % MGS) == 0) {
+      // N:M group of MGS <= 16 columns = lanes J .. J+MGS-1 of the row: rank
+      // the current saliencies at the group start; the group's values reach
+      // every lane of the row by DPP row broadcasts
+      const int me = lc - J;
+      const bool in = me >= 0 && me < MGS;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const float my = saliency(Wc[v], cx.ucc);
-        int rank = 0;
-        for (int t = 0; t < mgroup; ++t) {
-          const float o = __shfl(my, base + J + t, 64);
-          rank += (o < my || (o == my && t < lc - J)) ? 1 : 0;
-        }
-        if (in && ((rowbits >> v) & 1u) && rank < mgroup - nkeep) Pc |= 1u << v;
+        const int rank = group_rank<J>(std::make_integer_sequence<int, MGS>{}, my, me);
+        if (in && ((rowbits >> v) & 1u) && rank < MGS - nkeep) Pc |= 1u << v;
       }
     }
   }
@@ -393,14 +414,13 @@ __device__ __forceinline__ void sweep_step(floatx4& Wc, unsigned& Pc, const Chun
   for (int v = 0; v < 4; ++v) Wc[v] = fmaf(-e[v], cx.g[J], Wc[v]);
 }
 
-template <bool NM_SMALL, int... Js>
+template <int MGS, int... Js>
 __device__ __forceinline__ void sweep_chunk(std::integer_sequence<int, Js...>, floatx4& Wc, unsigned& Pc,
-                                            const ChunkCtx& cx, int lc, int mgroup, int nkeep,
-                                            unsigned rowbits) {
-  (sweep_step<Js, NM_SMALL>(Wc, Pc, cx, lc, mgroup, nkeep, rowbits), ...);
+                                            const ChunkCtx& cx, int lc, int nkeep, unsigned rowbits) {
+  (sweep_step<Js, MGS>(Wc, Pc, cx, lc, nkeep, rowbits), ...);
 }
 
-template <int MODE>
+template <int MODE, int MGS>
 __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8_t* __restrict__ mask_out,
                                                     float* __restrict__ Err, const float* __restrict__ U,
                                                     const uint8_t* __restrict__ mask_in,
@@ -567,10 +587,10 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   }
 
   float* Es = S.Es[wave];
-  // groups ranked from registers (M <= 16) or through the staging tile (M >
-  // 16, and the per-row mode, whose group is the whole block: mgroup = w)
-  const bool nm_small = MODE == MODE_NM && mgroup <= 16;
-  const bool nm_large = (MODE == MODE_NM && mgroup > 16) || MODE == MODE_ROW;
+  // groups of M <= 16 are ranked inside the column steps (MGS = M); larger
+  // groups (and the per-row mode, whose group is the whole block: mgroup = w)
+  // at their first chunk, from the saliencies of all their chunks
+  const bool nm_large = (MODE == MODE_NM && MGS == 0) || MODE == MODE_ROW;
   const unsigned rowbits = (rowok[0] ? 1u : 0u) | (rowok[1] ? 2u : 0u) | (rowok[2] ? 4u : 0u) |
                            (rowok[3] ? 8u : 0u);
 #pragma unroll
@@ -594,33 +614,65 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
     }
     if (nm_large && ((16 * c) % mgroup) == 0) {
       // group of mgroup columns = chunks c .. c + ceil(mgroup/16) - 1 (all current)
-      float* sc = Tw;
       const int nchg = (mgroup + 15) >> 4;
-      for (int g = 0; g < nchg && c + g < 8; ++g) {
-        const int col = 16 * (c + g) + lc;
-        const float ucg = S.Ub[col * SWS + col];
+      const int kp = mgroup - nkeep;  // pruned per row
+      if (mgroup > 64) {
+        // k-th smallest 39-bit key (saliency bits, position) per row by a
+        // bitwise search: counts over the 16 lanes of the row by DPP sums
+        unsigned long long key[8][4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) sc[(4 * lg + v) * SWS + 16 * g + lc] = saliency(Wt[c + g][v], ucg);
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __builtin_amdgcn_wave_barrier();
-      for (int g = 0; g < nchg && c + g < 8; ++g) {
+        for (int g = 0; g < 8; ++g) {
+          const int pos = 16 * g + lc;
+          const int col = 16 * (c + g) + lc;
+          const bool ok = g < nchg && c + g < 8 && pos < mgroup;
+          const float ucg = S.Ub[(ok ? col : 0) * SWS + (ok ? col : 0)];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float* row = sc + (4 * lg + v) * SWS;
-          const int me = 16 * g + lc;
-          if (rowok[v] && me < mgroup && rank_of(row, mgroup, row[me], me) < mgroup - nkeep)
-            Pm[c + g] |= 1u << v;
+          for (int v = 0; v < 4; ++v)
+            key[g][v] = ok ? (((unsigned long long)__float_as_uint(saliency(Wt[c + g < 8 ? c + g : 7][v], ucg))
+                               << 7) | (unsigned)pos)
+                           : ~0ull;
         }
+        unsigned long long T[4] = {0ull, 0ull, 0ull, 0ull};
+        for (int b = 38; b >= 0; --b) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const unsigned long long cand = T[v] | (1ull << b);
+            int cnt = 0;
+#pragma unroll
+            for (int g = 0; g < 8; ++g) cnt += key[g][v] < cand ? 1 : 0;
+            if (rowsum16(cnt) < kp) T[v] = cand;
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          if (c + g >= 8) continue;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (rowok[v] && kp > 0 && key[g][v] <= T[v]) Pm[c + g] |= 1u << v;
+        }
+      } else {
+        float* sc = Tw;
+        for (int g = 0; g < nchg && c + g < 8; ++g) {
+          const int col = 16 * (c + g) + lc;
+          const float ucg = S.Ub[col * SWS + col];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sc[(4 * lg + v) * SWS + 16 * g + lc] = saliency(Wt[c + g][v], ucg);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        for (int g = 0; g < nchg && c + g < 8; ++g) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float* row = sc + (4 * lg + v) * SWS;
+            const int me = 16 * g + lc;
+            if (rowok[v] && me < mgroup && rank_of(row, mgroup, row[me], me) < kp)
+              Pm[c + g] |= 1u << v;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
       }
-      __builtin_amdgcn_wave_barrier();
     }
-    if (nm_small)
-      sweep_chunk<true>(std::make_integer_sequence<int, 16>{}, Wt[c], Pm[c], cx, lc, mgroup, nkeep,
-                        rowbits);
-    else
-      sweep_chunk<false>(std::make_integer_sequence<int, 16>{}, Wt[c], Pm[c], cx, lc, mgroup, nkeep,
-                         rowbits);
+    sweep_chunk<MGS>(std::make_integer_sequence<int, 16>{}, Wt[c], Pm[c], cx, lc, nkeep, rowbits);
     // errors of the chunk: e = W_J / U_JJ for pruned entries, from the frozen
     // owner values; pruned entries become +0.0
 #pragma unroll
@@ -779,10 +831,15 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(select_pass_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SelLds)) != hipSuccess)
     return set_error(SG_ERR_HIP, "hipFuncSetAttribute(select_pass_kernel) failed");
-  const void* sweep_fns[4] = {reinterpret_cast<const void*>(sweep_kernel<MODE_THRESH>),
-                              reinterpret_cast<const void*>(sweep_kernel<MODE_NM>),
-                              reinterpret_cast<const void*>(sweep_kernel<MODE_FORCED>),
-                              reinterpret_cast<const void*>(sweep_kernel<MODE_ROW>)};
+  const void* sweep_fns[] = {reinterpret_cast<const void*>(sweep_kernel<MODE_THRESH, 0>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_FORCED, 0>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_ROW, 0>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 0>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 1>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 2>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 4>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 8>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 16>)};
   for (const void* f : sweep_fns)
     if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SweepLds)) !=
         hipSuccess)
@@ -825,21 +882,27 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
         }
       }
     }
-    if (mode == MODE_THRESH)
-      hipLaunchKernelGGL(sweep_kernel<MODE_THRESH>, sw_grid, sw_block, shm, st, a.W_out, a.mask_out,
-                         Eb, a.U, a.mask_in, sel, cand, parity, k, sel_fixed, m, n, i1, w, a.n_keep,
-                         a.m_group);
-    else if (mode == MODE_NM)
-      hipLaunchKernelGGL(sweep_kernel<MODE_NM>, sw_grid, sw_block, shm, st, a.W_out, a.mask_out, Eb,
-                         a.U, a.mask_in, sel, cand, 0, 0ll, 0, m, n, i1, w, a.n_keep, a.m_group);
-    else if (mode == MODE_ROW)
+#define SG_SWEEP(MD, MG, PAR, K, FIX, NK, MGRP)                                                    \
+  hipLaunchKernelGGL((sweep_kernel<MD, MG>), sw_grid, sw_block, shm, st, a.W_out, a.mask_out, Eb, a.U, \
+                     a.mask_in, sel, cand, PAR, K, FIX, m, n, i1, w, NK, MGRP)
+    if (mode == MODE_THRESH) {
+      SG_SWEEP(MODE_THRESH, 0, parity, k, sel_fixed, a.n_keep, a.m_group);
+    } else if (mode == MODE_NM) {
+      switch (a.m_group) {
+        case 1: SG_SWEEP(MODE_NM, 1, 0, 0ll, 0, a.n_keep, a.m_group); break;
+        case 2: SG_SWEEP(MODE_NM, 2, 0, 0ll, 0, a.n_keep, a.m_group); break;
+        case 4: SG_SWEEP(MODE_NM, 4, 0, 0ll, 0, a.n_keep, a.m_group); break;
+        case 8: SG_SWEEP(MODE_NM, 8, 0, 0ll, 0, a.n_keep, a.m_group); break;
+        case 16: SG_SWEEP(MODE_NM, 16, 0, 0ll, 0, a.n_keep, a.m_group); break;
+        default: SG_SWEEP(MODE_NM, 0, 0, 0ll, 0, a.n_keep, a.m_group); break;
+      }
+    } else if (mode == MODE_ROW) {
       // one group per row spanning the block: keep w - floor(p * w)
-      hipLaunchKernelGGL(sweep_kernel<MODE_ROW>, sw_grid, sw_block, shm, st, a.W_out, a.mask_out, Eb,
-                         a.U, a.mask_in, sel, cand, 0, 0ll, 0, m, n, i1, w,
-                         w - (int)floor(a.sparsity * (double)w), w);
-    else
-      hipLaunchKernelGGL(sweep_kernel<MODE_FORCED>, sw_grid, sw_block, shm, st, a.W_out, a.mask_out,
-                         Eb, a.U, a.mask_in, sel, cand, 0, 0ll, 0, m, n, i1, w, a.n_keep, a.m_group);
+      SG_SWEEP(MODE_ROW, 0, 0, 0ll, 0, w - (int)floor(a.sparsity * (double)w), w);
+    } else {
+      SG_SWEEP(MODE_FORCED, 0, 0, 0ll, 0, a.n_keep, a.m_group);
+    }
+#undef SG_SWEEP
     if (sg_status e = check_launch("prune sweep")) return e;
     const int64_t i2 = i1 + w;
     if (i2 < g_end) {
