@@ -45,6 +45,9 @@ from .sparsegpt_oracle import (  # noqa: F401
     reconstruction_error_from_hessian,
     solve_layer,
     pack_two_four,
+    quant_grid,
+    quant_code,
+    prune_quantized,
     unpack_two_four,
     unstructured_k,
 )

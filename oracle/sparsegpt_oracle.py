@@ -241,6 +241,115 @@ def prune(W: np.ndarray, U: np.ndarray, pattern, blocksize: int,
     return Wh, mask, eps
 
 
+# ----------------------------------------------------------------------------
+# Joint sparse + quantized sweep
+# ----------------------------------------------------------------------------
+
+def quant_grid(W: np.ndarray, bits: int):
+    """Per-row uniform grid with 2^bits levels spanning the row's original
+    weights and 0 (the pages name 4- and 8-bit weights but no grid).
+
+    Reading: lo = min(0, min_j w_j), hi = max(0, max_j w_j),
+    scale = (hi - lo) / (2^bits - 1) (1 for an all-zero row), integer zero
+    point z = round(-lo / scale), rounding half to even throughout.  Returns
+    (scale[m], zero[m]) as float64.
+    """
+    if not (2 <= bits <= 8):
+        raise ValueError("bits must lie in [2, 8]")
+    W = np.asarray(W, dtype=np.float64)
+    lo = np.minimum(W.min(axis=1), 0.0)
+    hi = np.maximum(W.max(axis=1), 0.0)
+    levels = float(2 ** bits - 1)
+    scale = np.where(hi > lo, (hi - lo) / levels, 1.0)
+    zero = np.rint(-lo / scale)
+    return scale, zero
+
+
+def quant_code(x, scale, zero, bits: int):
+    """Integer code of x on the grid: clamp(round(x / scale) + z, 0, 2^bits - 1)."""
+    return np.clip(np.rint(x / scale) + zero, 0.0, float(2 ** bits - 1))
+
+
+def prune_quantized(W: np.ndarray, U: np.ndarray, pattern, blocksize: int, bits: int,
+                    mask_in: Optional[np.ndarray] = None,
+                    codes_in: Optional[np.ndarray] = None, return_trace: bool = False):
+    """Pruning and quantization in one column sweep ([SGR] section 15: the
+    kept weights of a pruned layer can also be quantized to few bits;
+    section 17: GPTQ quantizes weight by weight and compensates the rounding
+    error through the inverse Hessian, the same second-order step SparseGPT
+    uses for pruning).
+
+    Same column order, selection points and saliencies as ``prune``.  At
+    column j every row's weight is either pruned (target 0) or kept and
+    rounded to its row's grid (target scale * (code - z)); in both cases
+    e = (Ŵ[r,j] - target) / U_jj, the not-yet-processed weights of the row
+    take Ŵ[r, j:] -= e * U[j, j:], and Ŵ[r,j] = target exactly.
+
+    ``codes_in`` (m x n) replaces the rounding decisions (for comparisons
+    along another implementation's trajectory).  Returns (W_hat, mask, eps,
+    codes, scale, zero); codes of pruned weights are z (their value is 0).
+    With ``return_trace`` also a dict with the saliency of every weight at
+    its selection point, the value of every weight when it was quantized and
+    the error e of every column step.
+    """
+    pat = parse_pattern(pattern)
+    Wh = np.array(W, dtype=np.float64, copy=True)
+    m, n = Wh.shape
+    U = np.asarray(U, dtype=np.float64)
+    if U.shape != (n, n):
+        raise ValueError("U must be n x n")
+    if pat.kind == "nm" and n % pat.m_group != 0:
+        raise ValueError("N:M needs M to divide n")
+    scale, zero = quant_grid(Wh, bits)
+    mask = np.zeros((m, n), dtype=bool)
+    codes = np.zeros((m, n), dtype=np.float64)
+    eps = np.zeros(m)
+    d = np.diag(U).copy()
+    sal = np.full((m, n), np.nan)
+    at_quant = np.full((m, n), np.nan)
+    errs = np.zeros((m, n))
+    lin = np.arange(m, dtype=np.int64)[:, None] * n
+
+    for j in range(n):
+        if pat.kind == "unstructured" and j % blocksize == 0:
+            w = min(blocksize, n - j)
+            s = Wh[:, j:j + w] ** 2 / d[j:j + w] ** 2
+            sal[:, j:j + w] = s
+            if mask_in is None and pat.per_row:
+                mask[:, j:j + w] = _select_rows(s, unstructured_k(pat.sparsity, 1, w))
+            elif mask_in is None:
+                idx = lin + np.arange(j, j + w, dtype=np.int64)[None, :]
+                mask[:, j:j + w] = _select_block_unstructured(s, idx, unstructured_k(pat.sparsity, m, w))
+        elif pat.kind == "nm" and j % pat.m_group == 0:
+            M = pat.m_group
+            s = Wh[:, j:j + M] ** 2 / d[j:j + M] ** 2
+            sal[:, j:j + M] = s
+            if mask_in is None:
+                mask[:, j:j + M] = _select_rows(s, M - pat.n_keep)
+        if mask_in is not None:
+            mask[:, j] = np.asarray(mask_in[:, j], dtype=bool)
+
+        x = Wh[:, j].copy()
+        at_quant[:, j] = x
+        if codes_in is not None:
+            c = np.asarray(codes_in[:, j], dtype=np.float64)
+        else:
+            c = quant_code(x, scale, zero, bits)
+        c = np.where(mask[:, j], zero, c)
+        target = scale * (c - zero)
+        e = (x - target) / U[j, j]
+        Wh[:, j:] -= np.outer(e, U[j, j:])
+        Wh[:, j] = np.where(mask[:, j], 0.0, target)
+        codes[:, j] = c
+        errs[:, j] = e
+        eps += e * e
+
+    out = (Wh, mask, eps, codes.astype(np.uint8), scale, zero)
+    if return_trace:
+        return out + ({"saliency": sal, "at_quant": at_quant, "errors": errs},)
+    return out
+
+
 def prune_free_set(W: np.ndarray, Hd: np.ndarray, pattern, blocksize: int,
                    mask_in: Optional[np.ndarray] = None):
     """The same procedure without any Cholesky factor (cross-check route).

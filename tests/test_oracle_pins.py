@@ -301,6 +301,94 @@ def test_per_row_with_block_m_equals_nm():
 
 
 # ----------------------------------------------------------------------------
+# joint sparse + quantized sweep
+# ----------------------------------------------------------------------------
+
+def test_quant_grid_hand_examples():
+    # worked by hand: [-1, 0.5, 2] at 2 bits spans [-1, 2]: scale 1, zero 1;
+    # 0.5 / 1 is a tie that rounds to the even 0 -> code 1 -> value 0.
+    # [0.25, 0.75, 1.75] at 3 bits spans [0, 1.75]: scale 0.25, zero 0.
+    # [-0.5, 0.25, 1.0] at 2 bits spans [-0.5, 1]: scale 0.5, zero 1; 0.25 /
+    # 0.5 = 0.5 ties to 0 -> code 1 -> value 0.
+    for row, bits, sc, z, codes in (([-1.0, 0.5, 2.0], 2, 1.0, 1.0, [0, 1, 3]),
+                                    ([0.25, 0.75, 1.75], 3, 0.25, 0.0, [1, 3, 7]),
+                                    ([-0.5, 0.25, 1.0], 2, 0.5, 1.0, [0, 1, 3])):
+        W = np.array([row])
+        scale, zero = oracle.quant_grid(W, bits)
+        assert scale[0] == sc and zero[0] == z
+        got = oracle.quant_code(W[0], scale[0], zero[0], bits)
+        assert list(got) == codes
+
+
+def _nearest_level(x, scale, zero, bits):
+    # brute force over all 2^bits levels; ties go to the even offset code - z
+    best = None
+    for c in range(2 ** bits):
+        v = scale * (c - zero)
+        key = (abs(x - v), (c - zero) % 2)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def test_quantized_sweep_identity_hessian_is_round_to_nearest():
+    # H ~ I: no compensation reaches other columns, so every kept weight is
+    # simply its nearest grid level and the mask is magnitude pruning
+    r = rng0(41)
+    W = r.standard_normal((4, 24))
+    Hd, _ = oracle.dampen(5.0 * np.eye(24), 0.01)
+    U = oracle.inverse_upper_factor(Hd)
+    for pat in (0.0, 0.5, "2:4"):
+        Wh, M, _, C, scale, zero = oracle.prune_quantized(W, U, pat, 8, 3)
+        _, Mp, _ = oracle.prune(W, U, pat, 8)
+        assert np.array_equal(M, Mp)
+        for i in range(4):
+            for j in range(24):
+                if M[i, j]:
+                    assert Wh[i, j] == 0.0 and C[i, j] == zero[i]
+                else:
+                    c = _nearest_level(W[i, j], scale[i], zero[i], 3)
+                    assert C[i, j] == c
+                    assert Wh[i, j] == pytest.approx(scale[i] * (c - zero[i]), abs=1e-15)
+
+
+def test_quantized_sweep_prefix_values_are_least_squares():
+    # the value a weight has when it is quantized equals the textbook
+    # constrained least-squares optimum with every earlier column fixed at
+    # its final value: v_K = w_K + H_KK^-1 H_KP (w_P - t_P)
+    W, _, _, Hd, _, U = _layer(42, 3, 20, 120)
+    Wh, M, eps, C, _, _, tr = oracle.prune_quantized(W, U, 0.3, 5, 4, return_trace=True)
+    for j in (1, 6, 13, 19):
+        P = list(range(j))
+        K = list(range(j, 20))
+        for i in range(3):
+            vK = W[i, K] + np.linalg.solve(Hd[np.ix_(K, K)], Hd[np.ix_(K, P)] @ (W[i, P] - Wh[i, P]))
+            assert tr["at_quant"][i, j] == pytest.approx(vK[0], rel=1e-9, abs=1e-12)
+
+
+def test_quantized_sweep_error_structure():
+    # w - w_hat = e U row by row (each step moves the row along U's row j),
+    # and the damped error equals the sum of e^2
+    W, _, _, Hd, _, U = _layer(43, 5, 32, 150)
+    for pat in (0.5, "4:8", "0.5/row"):
+        Wh, M, eps, C, scale, zero, tr = oracle.prune_quantized(W, U, pat, 10, 3, return_trace=True)
+        d = W - Wh
+        assert np.abs(d - tr["errors"] @ U).max() < 1e-12
+        for i in range(5):
+            assert _quad(d[i], Hd) == pytest.approx(eps[i], rel=1e-9)
+        # every value is on its row's grid, pruned ones exactly +0.0
+        assert np.allclose(Wh, scale[:, None] * (C.astype(float) - zero[:, None]), atol=1e-15)
+        assert np.all(Wh[M] == 0.0) and not np.any(np.signbit(Wh[M]))
+
+
+def test_quantized_sweep_forced_decisions_reproduce():
+    W, _, _, _, _, U = _layer(44, 4, 16, 80)
+    a = oracle.prune_quantized(W, U, "2:4", 8, 4)
+    b = oracle.prune_quantized(W, U, "2:4", 8, 4, mask_in=a[1], codes_in=a[3])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[3], b[3])
+
+
+# ----------------------------------------------------------------------------
 # 2:4 compressed export
 # ----------------------------------------------------------------------------
 
