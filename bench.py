@@ -64,7 +64,7 @@ def load_traffic(workload):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, pattern, W_host, X_host_sample, n_tok_total, rows_sample):
+def cpu_baseline(cfg, pattern, W_host, X_host_sample, n_tok_total, rows_sample, bits=0):
     """The oracle as it stands, timed on host cores on a bounded sample of the
     same layer, scaled to one whole layer: Hessian on a token sample (scaled by
     tokens), the full n x n factor, the column sweep on a row sample (scaled
@@ -88,7 +88,10 @@ def cpu_baseline(cfg, pattern, W_host, X_host_sample, n_tok_total, rows_sample):
     t_u = time.perf_counter() - t0
     Ws = W_host[:rows_sample].double().numpy()
     t0 = time.perf_counter()
-    oracle.prune(Ws, U, pattern, cfg.blocksize)
+    if bits:
+        oracle.prune_quantized(Ws, U, pattern, cfg.blocksize, bits)
+    else:
+        oracle.prune(Ws, U, pattern, cfg.blocksize)
     t_p = time.perf_counter() - t0
     total = t_h * (n_tok_total / xs.shape[0]) + t_u + t_p * (cfg.m / rows_sample)
     return {
@@ -109,6 +112,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="attn_4096")
     ap.add_argument("--pattern", default=None)
+    ap.add_argument("--bits", type=int, default=0,
+                    help="also round the kept weights to a per-row grid of 2^bits levels in the sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this size (for counter scaling)")
@@ -146,6 +151,14 @@ def main():
     ws_f = torch.empty(sg.sg_workspace_bytes(sg.SG_OP_PREPARE_HINV, 0, n, 0, 0), dtype=torch.uint8,
                        device=dev)
     ws_p = torch.empty(sg.sg_workspace_bytes(sg.SG_OP_PRUNE, m, n, 0, B), dtype=torch.uint8, device=dev)
+    codes = torch.empty(m, n, dtype=torch.uint8, device=dev) if args.bits else None
+
+    def prune():
+        if args.bits:
+            sg.sg_prune_quantize_layer(W, Hinv, pattern, args.bits, B, W_out=W_out, mask_out=mask,
+                                       codes_out=codes, workspace=ws_p)
+        else:
+            sg.sg_prune_layer(W, Hinv, pattern, B, W_out=W_out, mask_out=mask, workspace=ws_p)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
@@ -159,7 +172,7 @@ def main():
         sg.sg_prepare_hinv(H, cfg.damp, Hinv=Hinv, info=info, workspace=ws_f)
         if marks is not None:
             marks[2].record()
-        sg.sg_prune_layer(W, Hinv, pattern, B, W_out=W_out, mask_out=mask, workspace=ws_p)
+        prune()
         if marks is not None:
             marks[3].record()
 
@@ -186,7 +199,7 @@ def main():
         mk[1].record()
         sg.sg_prepare_hinv(H, cfg.damp, Hinv=Hinv, info=info, workspace=ws_f)
         mk[2].record()
-        sg.sg_prune_layer(W, Hinv, pattern, B, W_out=W_out, mask_out=mask, workspace=ws_p)
+        prune()
         mk[3].record()
     t_end.record()
     torch.cuda.synchronize()
@@ -247,7 +260,7 @@ def main():
         print("[bench] timing the oracle on a host sample", file=sys.stderr, flush=True)
         tok_sample = min(N, 8192)
         rows = min(m, 256)
-        cpu = cpu_baseline(cfg, pattern, W.cpu(), X[:tok_sample].cpu(), N, rows)
+        cpu = cpu_baseline(cfg, pattern, W.cpu(), X[:tok_sample].cpu(), N, rows, args.bits)
 
     line = {
         "metric": "per-layer prune wall-time (s) + TFLOP/s & % MFMA/HBM roofline, 4096² → 28672×8192",
@@ -264,8 +277,10 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the layer)",
         "config": {
             "workload": f"{args.config}: W {m}x{n} {cfg.dtype}, X {N}x{n} {cfg.dtype}, "
-                        f"pattern {pattern}, blocksize {B}, damp {cfg.damp}",
+                        f"pattern {pattern}, blocksize {B}, damp {cfg.damp}"
+                        + (f", kept weights on a {args.bits}-bit grid" if args.bits else ""),
             "m": m, "n": n, "tokens": N, "pattern": pattern, "blocksize": B,
+            "quant_bits": args.bits or None,
         },
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
         "tflops_algorithmic": total_flops / (ms * 1e-3) / 1e12,

@@ -186,6 +186,42 @@ sg_status sg_prune_layer(float* W_out, uint8_t* mask_out, const void* W,
                          void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * sg_prune_quantize_layer -- sg_prune_layer with the kept weights also
+ * rounded to a per-row grid of 2^bits levels inside the same column sweep.
+ *
+ * [SGR] section 15 (a pruned layer's remaining weights can also be quantized
+ * to 4 or 8 bits) and section 17 (GPTQ quantizes weights one at a time and
+ * compensates each rounding error through the inverse Hessian, the step
+ * SparseGPT applies to pruning).  Readings where the pages are silent:
+ *   - each row's grid spans its original weights and 0: lo = min(0, min w),
+ *     hi = max(0, max w), scale = (hi - lo) / (2^bits - 1) (1 for an all-zero
+ *     row), zero point z = round(-lo / scale);
+ *   - selection is exactly that of sg_prune_layer (same saliencies, taken on
+ *     the current weights); at column j a kept weight x becomes
+ *     scale * (clamp(round(x / scale) + z, 0, 2^bits - 1) - z), rounding half
+ *     to even, and its error (x - that) / U_jj is compensated on the row's
+ *     later columns exactly like the error of a pruned weight.
+ *
+ *   codes_out [m x n] uint8 out, contiguous, may be NULL: the grid index of
+ *             every weight (W_out = scale * (code - zero)); a pruned weight
+ *             holds the row's zero point.
+ *   scale_out, zero_out [m] fp32 out (not NULL): each row's grid.
+ *   bits      2 <= bits <= 8.
+ * Every other argument, the workspace and the error behaviour are those of
+ * sg_prune_layer.
+ */
+sg_status sg_prune_quantize_layer(float* W_out, uint8_t* mask_out,
+                                  uint8_t* codes_out, float* scale_out,
+                                  float* zero_out, int32_t bits, const void* W,
+                                  int32_t w_dtype, int64_t m, int64_t n,
+                                  int64_t ldw, const float* Hinv,
+                                  int32_t pattern_kind, double sparsity,
+                                  int32_t n_keep, int32_t m_group,
+                                  int32_t blocksize, const uint8_t* mask_in,
+                                  void* workspace, size_t ws_bytes,
+                                  void* stream);
+
+/*
  * sg_reconstruction_error -- *err = (accumulate ? *err : 0)
  *                                   + ||(W - W_hat) Xc^T||_F^2.
  *

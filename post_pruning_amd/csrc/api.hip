@@ -139,11 +139,11 @@ sg_status sg_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp, i
   return launch_prepare_hinv(Hinv, H, n, damp, info, workspace, static_cast<hipStream_t>(stream));
 }
 
-sg_status sg_prune_layer(float* W_out, uint8_t* mask_out, const void* W, int32_t w_dtype, int64_t m,
-                         int64_t n, int64_t ldw, const float* Hinv, int32_t pattern_kind,
-                         double sparsity, int32_t n_keep, int32_t m_group, int32_t blocksize,
-                         const uint8_t* mask_in, void* workspace, size_t ws_bytes, void* stream) {
-  g_last_error.clear();
+static sg_status prune_common(float* W_out, uint8_t* mask_out, uint8_t* codes_out, float* scale_out,
+                              float* zero_out, int32_t bits, const void* W, int32_t w_dtype, int64_t m,
+                              int64_t n, int64_t ldw, const float* Hinv, int32_t pattern_kind,
+                              double sparsity, int32_t n_keep, int32_t m_group, int32_t blocksize,
+                              const uint8_t* mask_in, void* workspace, size_t ws_bytes, void* stream) {
   if (!W_out || !W || !Hinv) return set_error(SG_ERR_INVALID_ARGUMENT, "W_out, W and Hinv must not be NULL");
   if (m < 1 || n < 1) return set_error(SG_ERR_INVALID_ARGUMENT, "m and n must be >= 1");
   if ((unsigned long long)m * (unsigned long long)n >= (1ull << 32))
@@ -191,7 +191,35 @@ sg_status sg_prune_layer(float* W_out, uint8_t* mask_out, const void* W, int32_t
   a.m_group = pattern_kind == SG_NM ? m_group : 1;
   a.blocksize = blocksize;
   a.mask_in = mask_in;
+  a.bits = bits;
+  a.codes_out = codes_out;
+  a.qscale = scale_out;
+  a.qzero = zero_out;
   return launch_prune(a, workspace, static_cast<hipStream_t>(stream));
+}
+
+sg_status sg_prune_layer(float* W_out, uint8_t* mask_out, const void* W, int32_t w_dtype, int64_t m,
+                         int64_t n, int64_t ldw, const float* Hinv, int32_t pattern_kind,
+                         double sparsity, int32_t n_keep, int32_t m_group, int32_t blocksize,
+                         const uint8_t* mask_in, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  return prune_common(W_out, mask_out, nullptr, nullptr, nullptr, 0, W, w_dtype, m, n, ldw, Hinv,
+                      pattern_kind, sparsity, n_keep, m_group, blocksize, mask_in, workspace, ws_bytes,
+                      stream);
+}
+
+sg_status sg_prune_quantize_layer(float* W_out, uint8_t* mask_out, uint8_t* codes_out, float* scale_out,
+                                  float* zero_out, int32_t bits, const void* W, int32_t w_dtype,
+                                  int64_t m, int64_t n, int64_t ldw, const float* Hinv,
+                                  int32_t pattern_kind, double sparsity, int32_t n_keep,
+                                  int32_t m_group, int32_t blocksize, const uint8_t* mask_in,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!scale_out || !zero_out) return set_error(SG_ERR_INVALID_ARGUMENT, "scale_out and zero_out must not be NULL");
+  if (bits < 2 || bits > 8) return set_error(SG_ERR_INVALID_ARGUMENT, "bits=%d out of [2, 8]", bits);
+  return prune_common(W_out, mask_out, codes_out, scale_out, zero_out, bits, W, w_dtype, m, n, ldw, Hinv,
+                      pattern_kind, sparsity, n_keep, m_group, blocksize, mask_in, workspace, ws_bytes,
+                      stream);
 }
 
 sg_status sg_reconstruction_error(double* err, int32_t accumulate, const void* W, int32_t w_dtype,

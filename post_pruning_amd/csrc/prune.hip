@@ -373,6 +373,19 @@ struct ChunkCtx {
   float ucc;     // U_col,col
 };
 
+// Grid of the joint sparse + quantized sweep for the lane's four rows:
+// value = s * (code - z), code = clamp(round(x / s) + z, 0, L), rounding half
+// to even (x / s taken as x * (1 / s)).
+struct RowQuant {
+  float s[4], inv[4], z[4];
+  float L;
+};
+
+__device__ __forceinline__ float quant_value(float x, const RowQuant& q, int v) {
+  const float c = fminf(fmaxf(rintf(x * q.inv[v]) + q.z[v], 0.f), q.L);
+  return q.s[v] * (c - q.z[v]);
+}
+
 // Sweep column j of the chunk (compile-time j: static DPP lane and indices).
 // Chain per step and row: select (pruned ? W_J : 0) on the owner lane, DPP
 // broadcast over the 16 lanes of the row, fused multiply-add.
@@ -389,9 +402,9 @@ __device__ __forceinline__ int group_rank(std::integer_sequence<int, Ts...>, flo
   return (ahead_of<J, Ts>(my, me) + ... + 0);
 }
 
-template <int J, int MGS>
+template <int J, int MGS, bool QUANT>
 __device__ __forceinline__ void sweep_step(floatx4& Wc, unsigned& Pc, const ChunkCtx& cx, int lc,
-                                           int nkeep, unsigned rowbits) {
+                                           int nkeep, unsigned rowbits, const RowQuant& q) {
   if constexpr (MGS > 0) {
     if constexpr ((J % MGS) == 0) {
       // N:M group of MGS <= 16 columns = lanes J .. J+MGS-1 of the row: rank
@@ -407,20 +420,30 @@ __device__ __forceinline__ void sweep_step(floatx4& Wc, unsigned& Pc, const Chun
       }
     }
   }
+  // owner lane's deviation from its target (0 if pruned, the grid value if
+  // kept and quantized), times U_JJ: the DPP broadcast hands it to the row
   float e[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) e[v] = bcast16_c<J>(((Pc >> v) & 1u) ? Wc[v] : 0.f);
+  for (int v = 0; v < 4; ++v) {
+    float d;
+    if constexpr (QUANT)
+      d = ((Pc >> v) & 1u) ? Wc[v] : Wc[v] - quant_value(Wc[v], q, v);
+    else
+      d = ((Pc >> v) & 1u) ? Wc[v] : 0.f;
+    e[v] = bcast16_c<J>(d);
+  }
 #pragma unroll
   for (int v = 0; v < 4; ++v) Wc[v] = fmaf(-e[v], cx.g[J], Wc[v]);
 }
 
-template <int MGS, int... Js>
+template <int MGS, bool QUANT, int... Js>
 __device__ __forceinline__ void sweep_chunk(std::integer_sequence<int, Js...>, floatx4& Wc, unsigned& Pc,
-                                            const ChunkCtx& cx, int lc, int nkeep, unsigned rowbits) {
-  (sweep_step<Js, MGS>(Wc, Pc, cx, lc, nkeep, rowbits), ...);
+                                            const ChunkCtx& cx, int lc, int nkeep, unsigned rowbits,
+                                            const RowQuant& q) {
+  (sweep_step<Js, MGS, QUANT>(Wc, Pc, cx, lc, nkeep, rowbits, q), ...);
 }
 
-template <int MODE, int MGS>
+template <int MODE, int MGS, bool QUANT>
 __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8_t* __restrict__ mask_out,
                                                     float* __restrict__ Err, const float* __restrict__ U,
                                                     const uint8_t* __restrict__ mask_in,
@@ -428,7 +451,9 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
                                                     const unsigned long long* __restrict__ cand,
                                                     int parity, long long ksel, int sel_fixed,
                                                     int64_t m, int64_t n, int64_t i1, int w, int nkeep,
-                                                    int mgroup) {
+                                                    int mgroup, uint8_t* __restrict__ codes_out,
+                                                    const float* __restrict__ qscale,
+                                                    const float* __restrict__ qzero, float qlevels) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   SweepLds& S = *reinterpret_cast<SweepLds*>(smem);
   const int tid = threadIdx.x;
@@ -437,6 +462,17 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   const int lg = lane >> 4;       // row group: rows 4*lg .. 4*lg+3 of the wave's 16
   const int64_t r0 = (int64_t)blockIdx.x * 64 + wave * 16 + 4 * lg;
   const int nch = (w + 15) >> 4;
+  RowQuant q;
+  if constexpr (QUANT) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t r = r0 + v < m ? r0 + v : m - 1;
+      q.s[v] = qscale[r];
+      q.inv[v] = 1.f / q.s[v];
+      q.z[v] = qzero[r];
+    }
+    q.L = qlevels;
+  }
 
   // threshold key of the block (the LDS of the U block serves as scratch)
   __shared__ unsigned s_cnt;
@@ -490,6 +526,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
                    ((reinterpret_cast<uintptr_t>(W) & 15) == 0) &&
                    ((reinterpret_cast<uintptr_t>(mask_in) & 3) == 0) &&
                    ((reinterpret_cast<uintptr_t>(mask_out) & 3) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(codes_out) & 3) == 0) &&
                    ((reinterpret_cast<uintptr_t>(Err) & 15) == 0);
   float* Tw = S.Tw[wave];
   const int64_t rw0 = (int64_t)blockIdx.x * 64 + wave * 16;
@@ -672,14 +709,20 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
         __builtin_amdgcn_wave_barrier();
       }
     }
-    sweep_chunk<MGS>(std::make_integer_sequence<int, 16>{}, Wt[c], Pm[c], cx, lc, nkeep, rowbits);
-    // errors of the chunk: e = W_J / U_JJ for pruned entries, from the frozen
-    // owner values; pruned entries become +0.0
+    sweep_chunk<MGS, QUANT>(std::make_integer_sequence<int, 16>{}, Wt[c], Pm[c], cx, lc, nkeep, rowbits, q);
+    // errors of the chunk: e = (W_J - target) / U_JJ, from the frozen owner
+    // values; pruned entries become +0.0, quantized ones their grid value
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const bool p = (Pm[c] >> v) & 1u;
-      Et[c][v] = p ? Wt[c][v] * cx.rd : 0.f;
-      Wt[c][v] = p ? 0.f : Wt[c][v];
+      if constexpr (QUANT) {
+        const float t = quant_value(Wt[c][v], q, v);
+        Et[c][v] = (p ? Wt[c][v] : Wt[c][v] - t) * cx.rd;
+        Wt[c][v] = p ? 0.f : t;
+      } else {
+        Et[c][v] = p ? Wt[c][v] * cx.rd : 0.f;
+        Wt[c][v] = p ? 0.f : Wt[c][v];
+      }
     }
     if (c + 1 < nch) {
       // E_c to the A-operand layout: Es[row][4*(k%4) + k/4] so that lane l
@@ -752,6 +795,25 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
         if (r < m && c4 < w) *reinterpret_cast<unsigned*>(mask_out + r * n + i1 + c4) = Tb[rr * 32 + (c4 >> 2)];
       }
     }
+    if (QUANT && codes_out) {
+      // grid codes, recovered from the final values (pruned: 0 -> z)
+      __builtin_amdgcn_wave_barrier();
+      unsigned char* Tm = reinterpret_cast<unsigned char*>(Tw);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          Tm[(4 * lg + v) * 128 + 16 * c + lc] =
+              (unsigned char)fminf(fmaxf(rintf(Wt[c][v] * q.inv[v]) + q.z[v], 0.f), q.L);
+      __builtin_amdgcn_wave_barrier();
+      const unsigned* Tb = reinterpret_cast<const unsigned*>(Tw);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
+        const int64_t r = rw0 + rr;
+        if (r < m && c4 < w) *reinterpret_cast<unsigned*>(codes_out + r * n + i1 + c4) = Tb[rr * 32 + (c4 >> 2)];
+      }
+    }
     return;
   }
 #pragma unroll
@@ -765,8 +827,46 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
       const bool p = (Pm[c] >> v) & 1u;
       W[r * n + i1 + col] = Wt[c][v];
       if (mask_out) mask_out[r * n + i1 + col] = p ? 1 : 0;
+      if (QUANT && codes_out)
+        codes_out[r * n + i1 + col] =
+            (unsigned char)fminf(fmaxf(rintf(Wt[c][v] * q.inv[v]) + q.z[v], 0.f), q.L);
       Err[r * EGK + col] = Et[c][v];
     }
+  }
+}
+
+// Per-row grid of the joint sparse + quantized sweep, from the row's original
+// weights: lo = min(0, min w), hi = max(0, max w), scale = (hi - lo) / L
+// (1 for an all-zero row), zero = round(-lo / scale).  One workgroup per row.
+// scale and the zero point are formed in fp64 (lo and hi are exact): bf16
+// rows often have hi = -lo, where -lo / scale sits on a half-way point and
+// the rounding of fp32 intermediates would decide the zero point.
+__global__ __launch_bounds__(256) void qgrid_kernel(const float* __restrict__ W, int64_t n, float L,
+                                                    float* __restrict__ scale, float* __restrict__ zero) {
+  __shared__ float red[2][4];
+  const float* row = W + (int64_t)blockIdx.x * n;
+  float lo = 0.f, hi = 0.f;
+  for (int64_t c = threadIdx.x; c < n; c += 256) {
+    const float x = row[c];
+    lo = fminf(lo, x);
+    hi = fmaxf(hi, x);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o, 64));
+    hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = lo;
+    red[1][threadIdx.x >> 6] = hi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    lo = fminf(fminf(red[0][0], red[0][1]), fminf(red[0][2], red[0][3]));
+    hi = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    const double s = hi > lo ? ((double)hi - (double)lo) / (double)L : 1.0;
+    scale[blockIdx.x] = (float)s;
+    zero[blockIdx.x] = (float)rint(-(double)lo / s);
   }
 }
 
@@ -831,19 +931,36 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(select_pass_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SelLds)) != hipSuccess)
     return set_error(SG_ERR_HIP, "hipFuncSetAttribute(select_pass_kernel) failed");
-  const void* sweep_fns[] = {reinterpret_cast<const void*>(sweep_kernel<MODE_THRESH, 0>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_FORCED, 0>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_ROW, 0>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 0>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 1>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 2>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 4>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 8>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 16>)};
+  const void* sweep_fns[] = {reinterpret_cast<const void*>(sweep_kernel<MODE_THRESH, 0, false>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_FORCED, 0, false>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_ROW, 0, false>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 0, false>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 1, false>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 2, false>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 4, false>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 8, false>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 16, false>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_THRESH, 0, true>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_FORCED, 0, true>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_ROW, 0, true>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 0, true>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 1, true>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 2, true>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 4, true>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 8, true>),
+                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 16, true>)};
   for (const void* f : sweep_fns)
     if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SweepLds)) !=
         hipSuccess)
       return set_error(SG_ERR_HIP, "hipFuncSetAttribute(sweep_kernel) failed");
+  const bool quant = a.bits > 0;
+  const float qlevels = quant ? (float)((1 << a.bits) - 1) : 0.f;
+  if (quant) {
+    // grid from the original weights (W_out holds their fp32 copy)
+    hipLaunchKernelGGL(qgrid_kernel, dim3((unsigned)m), dim3(256), 0, st, a.W_out, n, qlevels, a.qscale,
+                       a.qzero);
+    if (sg_status e = check_launch("quantization grid")) return e;
+  }
 
   const int mode = a.mask_in ? MODE_FORCED
                              : (a.kind == SG_NM ? MODE_NM : (a.kind == SG_UNSTRUCTURED_ROW ? MODE_ROW : MODE_THRESH));
@@ -882,9 +999,17 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
         }
       }
     }
-#define SG_SWEEP(MD, MG, PAR, K, FIX, NK, MGRP)                                                    \
-  hipLaunchKernelGGL((sweep_kernel<MD, MG>), sw_grid, sw_block, shm, st, a.W_out, a.mask_out, Eb, a.U, \
-                     a.mask_in, sel, cand, PAR, K, FIX, m, n, i1, w, NK, MGRP)
+#define SG_SWEEP(MD, MG, PAR, K, FIX, NK, MGRP)                                                     \
+  do {                                                                                            \
+    if (quant)                                                                                    \
+      hipLaunchKernelGGL((sweep_kernel<MD, MG, true>), sw_grid, sw_block, shm, st, a.W_out,          \
+                         a.mask_out, Eb, a.U, a.mask_in, sel, cand, PAR, K, FIX, m, n, i1, w, NK,   \
+                         MGRP, a.codes_out, a.qscale, a.qzero, qlevels);                           \
+    else                                                                                          \
+      hipLaunchKernelGGL((sweep_kernel<MD, MG, false>), sw_grid, sw_block, shm, st, a.W_out,         \
+                         a.mask_out, Eb, a.U, a.mask_in, sel, cand, PAR, K, FIX, m, n, i1, w, NK,   \
+                         MGRP, nullptr, nullptr, nullptr, 0.f);                                    \
+  } while (0)
     if (mode == MODE_THRESH) {
       SG_SWEEP(MODE_THRESH, 0, parity, k, sel_fixed, a.n_keep, a.m_group);
     } else if (mode == MODE_NM) {

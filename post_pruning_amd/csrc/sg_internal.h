@@ -73,6 +73,11 @@ struct PruneArgs {
   int n_keep, m_group;
   int blocksize;
   const uint8_t* mask_in;
+  // joint quantization (bits == 0: pruning only)
+  int bits;
+  uint8_t* codes_out;
+  float* qscale;
+  float* qzero;
 };
 size_t prune_ws_bytes(int64_t m, int64_t n, int blocksize);
 sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st);

@@ -85,6 +85,18 @@ def test_null_pointers_rejected_before_device(sg):
     assert st == sg.SG_ERR_INVALID_ARGUMENT
     st = lib.sg_pack_two_four(None, 0, None, None, None, None, 4, 8, None)
     assert st == sg.SG_ERR_INVALID_ARGUMENT
+    st = lib.sg_prune_quantize_layer(None, None, None, None, None, 4, None, 0, 4, 4, 4, None, 0, 0.5,
+                                     0, 1, 4, None, None, 0, None)
+    assert st == sg.SG_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("bits,code", [(1, 1), (9, 1), (4, 3)])
+def test_prune_quantize_validation(sg, bits, code):
+    # bits out of range, then (valid bits) a workspace that is too small
+    st = _lib(sg).sg_prune_quantize_layer(ctypes.c_void_p(0x3000), None, None, FAKE, FAKE, bits, FAKE,
+                                          0, 64, 128, 128, FAKE, 0, 0.5, 0, 1, 128, None,
+                                          ctypes.c_void_p(0x10000), 0, None)
+    assert st == code, sg.sg_last_error_message()
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation first
