@@ -65,6 +65,7 @@ def load_traffic(workload):
 
 
 def cpu_baseline(cfg, pattern, W_host, X_host_sample, n_tok_total, rows_sample, bits=0):
+    m_rows = W_host.shape[0]
     """The oracle as it stands, timed on host cores on a bounded sample of the
     same layer, scaled to one whole layer: Hessian on a token sample (scaled by
     tokens), the full n x n factor, the column sweep on a row sample (scaled
@@ -93,15 +94,15 @@ def cpu_baseline(cfg, pattern, W_host, X_host_sample, n_tok_total, rows_sample, 
     else:
         oracle.prune(Ws, U, pattern, cfg.blocksize)
     t_p = time.perf_counter() - t0
-    total = t_h * (n_tok_total / xs.shape[0]) + t_u + t_p * (cfg.m / rows_sample)
+    total = t_h * (n_tok_total / xs.shape[0]) + t_u + t_p * (m_rows / rows_sample)
     return {
         "value": total,
         "unit": "s",
         "cores": int(threads),
         "kind": "oracle",
         "sample": (f"Hessian on {xs.shape[0]} of {n_tok_total} tokens (x{n_tok_total // xs.shape[0]}), "
-                   f"full {cfg.n}x{cfg.n} fp64 factor, sweep on {rows_sample} of {cfg.m} rows "
-                   f"(x{cfg.m // rows_sample}); measured {t_h:.2f}+{t_u:.2f}+{t_p:.2f} s"),
+                   f"full {cfg.n}x{cfg.n} fp64 factor, sweep on {rows_sample} of {m_rows} rows "
+                   f"(x{m_rows // rows_sample}); measured {t_h:.2f}+{t_u:.2f}+{t_p:.2f} s"),
     }
 
 
@@ -112,6 +113,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="attn_4096")
     ap.add_argument("--pattern", default=None)
+    ap.add_argument("--shared", type=int, default=1,
+                    help="prune this many matrices of the layer's shape that share its input "
+                         "(stacked, one call with the shared factor)")
     ap.add_argument("--bits", type=int, default=0,
                     help="also round the kept weights to a per-row grid of 2^bits levels in the sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -137,7 +141,14 @@ def main():
     m, n, N, B = cfg.m, cfg.n, cfg.tokens, cfg.blocksize
     print(f"[bench] generating {args.config}: W {m}x{n}, X {N}x{n} ({cfg.dtype})", file=sys.stderr,
           flush=True)
-    W = synth.make_weight(cfg, dev)
+    if args.shared > 1:
+        import dataclasses
+        W = torch.cat([synth.make_weight(dataclasses.replace(cfg, config_id=cfg.config_id + 500 + i), dev)
+                       for i in range(args.shared)])
+        m = W.shape[0]
+    else:
+        W = synth.make_weight(cfg, dev)
+    splits = [i * cfg.m for i in range(args.shared + 1)]
     X = synth.make_x(cfg, dev)
     torch.cuda.synchronize()
 
@@ -154,7 +165,10 @@ def main():
     codes = torch.empty(m, n, dtype=torch.uint8, device=dev) if args.bits else None
 
     def prune():
-        if args.bits:
+        if args.shared > 1:
+            sg.sg_prune_layers_shared(W, splits, Hinv, pattern, B, bits=args.bits, W_out=W_out,
+                                      mask_out=mask, codes_out=codes, workspace=ws_p)
+        elif args.bits:
             sg.sg_prune_quantize_layer(W, Hinv, pattern, args.bits, B, W_out=W_out, mask_out=mask,
                                        codes_out=codes, workspace=ws_p)
         else:
@@ -281,6 +295,7 @@ def main():
                         + (f", kept weights on a {args.bits}-bit grid" if args.bits else ""),
             "m": m, "n": n, "tokens": N, "pattern": pattern, "blocksize": B,
             "quant_bits": args.bits or None,
+            "shared_matrices": args.shared,
         },
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
         "tflops_algorithmic": total_flops / (ms * 1e-3) / 1e12,
@@ -304,6 +319,8 @@ def main():
     }
     if export is not None:
         line["two_four_export"] = export
+    if args.shared > 1:
+        line["matrices_per_s"] = args.shared / (ms * 1e-3)
     print(json.dumps(line))
 
 

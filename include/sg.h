@@ -79,6 +79,9 @@ enum {
 /* Largest supported column block of sg_prune_layer. */
 #define SG_MAX_BLOCKSIZE 128
 
+/* Most matrices one sg_prune_layers_shared call can stack. */
+#define SG_MAX_SEGMENTS 16
+
 /*
  * sg_hessian_accumulate -- H += Xc^T Xc.
  *
@@ -220,6 +223,43 @@ sg_status sg_prune_quantize_layer(float* W_out, uint8_t* mask_out,
                                   int32_t blocksize, const uint8_t* mask_in,
                                   void* workspace, size_t ws_bytes,
                                   void* stream);
+
+/*
+ * sg_prune_layers_shared -- prune several weight matrices that read the same
+ * input (the query/key/value projections, or gate and up) in one call with
+ * their one shared factor Hinv.
+ *
+ * [SGR] section 7: H depends only on a layer's inputs, so matrices fed by the
+ * same activations share H and U.  The result for each matrix is exactly
+ * that of its own sg_prune_layer (or sg_prune_quantize_layer) call; the
+ * matrices are only processed together, so that every launch covers all of
+ * their rows.
+ *
+ *   W, W_out, mask_out, mask_in, codes_out: the nseg matrices stacked by
+ *             rows (each n columns wide) into one m_total x n matrix, in the
+ *             layouts of sg_prune_layer.
+ *   row_splits host array of nseg + 1 row offsets: 0 = row_splits[0] <
+ *             row_splits[1] < ... < row_splits[nseg] = m_total; matrix p is
+ *             rows [row_splits[p], row_splits[p+1]).
+ *   nseg      1 <= nseg <= SG_MAX_SEGMENTS.
+ *   bits      0 for pruning only (codes_out, scale_out and zero_out unused),
+ *             or 2..8 for the joint sweep of sg_prune_quantize_layer
+ *             (scale_out and zero_out [m_total] then required).
+ *   Unstructured selection counts floor(sparsity * m_p * w) per block of
+ *   each matrix p; every other pattern decides row by row.
+ * Workspace: sg_workspace_bytes(SG_OP_PRUNE, m_total, n, 0, blocksize).
+ */
+sg_status sg_prune_layers_shared(float* W_out, uint8_t* mask_out,
+                                 uint8_t* codes_out, float* scale_out,
+                                 float* zero_out, int32_t bits, const void* W,
+                                 int32_t w_dtype, int64_t m_total, int64_t n,
+                                 int64_t ldw, const int64_t* row_splits,
+                                 int32_t nseg, const float* Hinv,
+                                 int32_t pattern_kind, double sparsity,
+                                 int32_t n_keep, int32_t m_group,
+                                 int32_t blocksize, const uint8_t* mask_in,
+                                 void* workspace, size_t ws_bytes,
+                                 void* stream);
 
 /*
  * sg_reconstruction_error -- *err = (accumulate ? *err : 0)

@@ -31,6 +31,7 @@ SG_F32, SG_BF16 = 0, 1
 SG_UNSTRUCTURED, SG_NM, SG_UNSTRUCTURED_ROW = 0, 1, 2
 SG_OP_HESSIAN, SG_OP_PREPARE_HINV, SG_OP_PRUNE, SG_OP_RECON = range(4)
 SG_MAX_BLOCKSIZE = 128
+SG_MAX_SEGMENTS = 16
 
 _lib = None
 
@@ -63,8 +64,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sg_prune_quantize_layer.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
                                             c_i64, c_i64, c_vp, c_i32, c_dbl, c_i32, c_i32, c_i32,
                                             c_vp, c_vp, c_sz, c_vp]
+    lib.sg_prune_layers_shared.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
+                                           c_i64, c_i64, c_vp, c_i32, c_vp, c_i32, c_dbl, c_i32,
+                                           c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]
     for f in ("sg_hessian_accumulate", "sg_prepare_hinv", "sg_prune_layer",
-              "sg_reconstruction_error", "sg_pack_two_four", "sg_prune_quantize_layer"):
+              "sg_reconstruction_error", "sg_pack_two_four", "sg_prune_quantize_layer",
+              "sg_prune_layers_shared"):
         getattr(lib, f).restype = c_i32
     lib.sg_workspace_bytes.argtypes = [c_i32, c_i64, c_i64, c_i64, c_i32]
     lib.sg_workspace_bytes.restype = c_sz
@@ -252,6 +257,55 @@ def sg_prune_quantize_layer(W: torch.Tensor, Hinv: torch.Tensor, pattern: Union[
                                        _ptr(ws), nb, ctypes.c_void_p(_stream(W.device))),
            "sg_prune_quantize_layer")
     return W_out, mask_out, codes_out, scale, zero
+
+
+def sg_prune_layers_shared(W: torch.Tensor, row_splits, Hinv: torch.Tensor,
+                           pattern: Union[float, str], blocksize: int = 128, bits: int = 0,
+                           mask_in: Optional[torch.Tensor] = None,
+                           W_out: Optional[torch.Tensor] = None,
+                           mask_out: Optional[torch.Tensor] = None,
+                           codes_out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None):
+    """Prune matrices that share one input (stacked by rows in W, matrix p =
+    rows row_splits[p]:row_splits[p+1]) with their shared factor in one call.
+
+    Returns (W_hat, mask), or (W_hat, mask, codes, scale, zero) for bits > 0;
+    each matrix's rows equal its own sg_prune_layer / sg_prune_quantize_layer
+    result."""
+    lib = load_library()
+    _require_cuda(W, Hinv, mask_in)
+    m, n = W.shape
+    ldw = _row_major(W, "W")
+    splits = [int(x) for x in row_splits]
+    nseg = len(splits) - 1
+    if Hinv.shape != (n, n) or Hinv.dtype != torch.float32 or not Hinv.is_contiguous():
+        raise ValueError("Hinv must be a contiguous [n, n] float32 tensor")
+    if mask_in is not None:
+        if mask_in.shape != (m, n) or not mask_in.is_contiguous():
+            raise ValueError("mask_in must be a contiguous [m, n] tensor")
+        mask_in = mask_in.to(torch.uint8)
+    if W_out is None:
+        W_out = torch.empty(m, n, dtype=torch.float32, device=W.device)
+    if mask_out is None:
+        mask_out = torch.empty(m, n, dtype=torch.uint8, device=W.device)
+    scale = zero = None
+    if bits:
+        if codes_out is None:
+            codes_out = torch.empty(m, n, dtype=torch.uint8, device=W.device)
+        scale = torch.empty(m, dtype=torch.float32, device=W.device)
+        zero = torch.empty(m, dtype=torch.float32, device=W.device)
+    kind, sp, nk, mg = parse_pattern(pattern)
+    need = sg_workspace_bytes(SG_OP_PRUNE, m, n, 0, blocksize)
+    ws, nb = _workspace(need, W.device, workspace)
+    arr = (ctypes.c_int64 * max(1, len(splits)))(*splits)
+    _check(lib.sg_prune_layers_shared(_ptr(W_out), _ptr(mask_out), _ptr(codes_out), _ptr(scale),
+                                      _ptr(zero), int(bits), _ptr(W), _dtype_code(W), m, n, ldw,
+                                      ctypes.cast(arr, ctypes.c_void_p), nseg, _ptr(Hinv), kind, sp,
+                                      nk, mg, int(blocksize), _ptr(mask_in), _ptr(ws), nb,
+                                      ctypes.c_void_p(_stream(W.device))), "sg_prune_layers_shared")
+    if bits:
+        return W_out, mask_out, codes_out, scale, zero
+    return W_out, mask_out
 
 
 def sg_reconstruction_error(W: torch.Tensor, W_hat: torch.Tensor, X: torch.Tensor,

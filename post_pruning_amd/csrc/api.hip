@@ -141,7 +141,8 @@ sg_status sg_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp, i
 
 static sg_status prune_common(float* W_out, uint8_t* mask_out, uint8_t* codes_out, float* scale_out,
                               float* zero_out, int32_t bits, const void* W, int32_t w_dtype, int64_t m,
-                              int64_t n, int64_t ldw, const float* Hinv, int32_t pattern_kind,
+                              int64_t n, int64_t ldw, const int64_t* row_splits, int32_t nseg,
+                              const float* Hinv, int32_t pattern_kind,
                               double sparsity, int32_t n_keep, int32_t m_group, int32_t blocksize,
                               const uint8_t* mask_in, void* workspace, size_t ws_bytes, void* stream) {
   if (!W_out || !W || !Hinv) return set_error(SG_ERR_INVALID_ARGUMENT, "W_out, W and Hinv must not be NULL");
@@ -191,6 +192,9 @@ static sg_status prune_common(float* W_out, uint8_t* mask_out, uint8_t* codes_ou
   a.m_group = pattern_kind == SG_NM ? m_group : 1;
   a.blocksize = blocksize;
   a.mask_in = mask_in;
+  a.nseg = nseg;
+  a.seg_rows[0] = 0;
+  for (int p = 1; p <= nseg; ++p) a.seg_rows[p] = row_splits ? row_splits[p] : m;
   a.bits = bits;
   a.codes_out = codes_out;
   a.qscale = scale_out;
@@ -203,9 +207,9 @@ sg_status sg_prune_layer(float* W_out, uint8_t* mask_out, const void* W, int32_t
                          double sparsity, int32_t n_keep, int32_t m_group, int32_t blocksize,
                          const uint8_t* mask_in, void* workspace, size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  return prune_common(W_out, mask_out, nullptr, nullptr, nullptr, 0, W, w_dtype, m, n, ldw, Hinv,
-                      pattern_kind, sparsity, n_keep, m_group, blocksize, mask_in, workspace, ws_bytes,
-                      stream);
+  return prune_common(W_out, mask_out, nullptr, nullptr, nullptr, 0, W, w_dtype, m, n, ldw, nullptr, 1,
+                      Hinv, pattern_kind, sparsity, n_keep, m_group, blocksize, mask_in, workspace,
+                      ws_bytes, stream);
 }
 
 sg_status sg_prune_quantize_layer(float* W_out, uint8_t* mask_out, uint8_t* codes_out, float* scale_out,
@@ -217,9 +221,36 @@ sg_status sg_prune_quantize_layer(float* W_out, uint8_t* mask_out, uint8_t* code
   g_last_error.clear();
   if (!scale_out || !zero_out) return set_error(SG_ERR_INVALID_ARGUMENT, "scale_out and zero_out must not be NULL");
   if (bits < 2 || bits > 8) return set_error(SG_ERR_INVALID_ARGUMENT, "bits=%d out of [2, 8]", bits);
-  return prune_common(W_out, mask_out, codes_out, scale_out, zero_out, bits, W, w_dtype, m, n, ldw, Hinv,
-                      pattern_kind, sparsity, n_keep, m_group, blocksize, mask_in, workspace, ws_bytes,
-                      stream);
+  return prune_common(W_out, mask_out, codes_out, scale_out, zero_out, bits, W, w_dtype, m, n, ldw,
+                      nullptr, 1, Hinv, pattern_kind, sparsity, n_keep, m_group, blocksize, mask_in,
+                      workspace, ws_bytes, stream);
+}
+
+sg_status sg_prune_layers_shared(float* W_out, uint8_t* mask_out, uint8_t* codes_out, float* scale_out,
+                                 float* zero_out, int32_t bits, const void* W, int32_t w_dtype,
+                                 int64_t m_total, int64_t n, int64_t ldw, const int64_t* row_splits,
+                                 int32_t nseg, const float* Hinv, int32_t pattern_kind, double sparsity,
+                                 int32_t n_keep, int32_t m_group, int32_t blocksize,
+                                 const uint8_t* mask_in, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  g_last_error.clear();
+  if (!row_splits) return set_error(SG_ERR_INVALID_ARGUMENT, "row_splits must not be NULL");
+  if (nseg < 1 || nseg > SG_MAX_SEGMENTS)
+    return set_error(SG_ERR_INVALID_ARGUMENT, "nseg=%d out of [1, %d]", nseg, SG_MAX_SEGMENTS);
+  if (row_splits[0] != 0 || row_splits[nseg] != m_total)
+    return set_error(SG_ERR_INVALID_ARGUMENT, "row_splits must run from 0 to m_total");
+  for (int p = 0; p < nseg; ++p)
+    if (row_splits[p + 1] <= row_splits[p])
+      return set_error(SG_ERR_INVALID_ARGUMENT, "row_splits must increase strictly");
+  if (bits != 0) {
+    if (bits < 2 || bits > 8) return set_error(SG_ERR_INVALID_ARGUMENT, "bits=%d: 0 or [2, 8]", bits);
+    if (!scale_out || !zero_out)
+      return set_error(SG_ERR_INVALID_ARGUMENT, "scale_out and zero_out must not be NULL when bits > 0");
+  }
+  return prune_common(W_out, mask_out, bits ? codes_out : nullptr, bits ? scale_out : nullptr,
+                      bits ? zero_out : nullptr, bits, W, w_dtype, m_total, n, ldw, row_splits, nseg,
+                      Hinv, pattern_kind, sparsity, n_keep, m_group, blocksize, mask_in, workspace,
+                      ws_bytes, stream);
 }
 
 sg_status sg_reconstruction_error(double* err, int32_t accumulate, const void* W, int32_t w_dtype,

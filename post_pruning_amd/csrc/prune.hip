@@ -49,6 +49,18 @@ struct SelState {
   SelSet set[2];
 };
 
+// Row segments of one prune call (kernel argument): segment p is rows
+// [row0[p], row0[p+1]); its sweep workgroups are [wg0[p], wg0[p+1]) (64 rows
+// each); k[p] keys of each block are pruned under block-global selection
+// (fixed[p]: 2 none, 3 all, 0 selected by the radix passes).
+struct Segs {
+  int n;
+  int64_t row0[SG_MAX_SEGMENTS + 1];
+  int wg0[SG_MAX_SEGMENTS + 1];
+  long long k[SG_MAX_SEGMENTS];
+  int fixed[SG_MAX_SEGMENTS];
+};
+
 __device__ inline float saliency(float w, float ucc) {
   const float q = w / ucc;
   return q * q;
@@ -81,9 +93,9 @@ __device__ inline void sel_clear_set(SelSet& s, int tid, int nthreads) {
   if (tid == 0) s.ncand = 0u;
 }
 
-__global__ void sel_clear_kernel(SelState* st) {
-  sel_clear_set(st->set[0], threadIdx.x, blockDim.x);
-  sel_clear_set(st->set[1], threadIdx.x, blockDim.x);
+__global__ void sel_clear_kernel(SelState* st) {  // one workgroup per segment
+  sel_clear_set(st[blockIdx.x].set[0], threadIdx.x, blockDim.x);
+  sel_clear_set(st[blockIdx.x].set[1], threadIdx.x, blockDim.x);
 }
 
 // Exact k-th smallest 64-bit key (bits(W^2 / U_cc^2) << 32 | r*n + c) of the
@@ -157,11 +169,18 @@ struct SelLds {
   HistPick pick;
 };
 
-__global__ __launch_bounds__(256) void select_pass_kernel(SelSet* ss, unsigned long long* cand,
+__global__ __launch_bounds__(256) void select_pass_kernel(SelState* st, int parity,
+                                                         unsigned long long* cand,
                                                          const float* __restrict__ W,
-                                                         const float* __restrict__ U, int64_t m,
-                                                         int64_t n, int64_t i1, int w, long long k,
-                                                         int pass) {
+                                                         const float* __restrict__ U, const Segs segs,
+                                                         int64_t n, int64_t i1, int w, int pass) {
+  // blockIdx.y = segment; its keys only, into its own histograms and list
+  const int seg = blockIdx.y;
+  if (segs.fixed[seg] != 0) return;  // whole workgroup: nothing to select
+  const long long k = segs.k[seg];
+  SelSet* ss = &st[seg].set[parity];
+  cand += segs.row0[seg] * SB;
+  const int64_t rlo = segs.row0[seg], m = segs.row0[seg + 1];
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   SelLds& L = *reinterpret_cast<SelLds*>(smem);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -179,7 +198,7 @@ __global__ __launch_bounds__(256) void select_pass_kernel(SelSet* ss, unsigned l
   const int64_t col = i1 + cc;
   const float ucc = U[col * n + col];
   const int64_t rstep = (int64_t)gridDim.x * 2;
-  const int64_t rb = (int64_t)blockIdx.x * 2 + (tid >> 7);
+  const int64_t rb = rlo + (int64_t)blockIdx.x * 2 + (tid >> 7);
   float wv[SEL_KPT];
 #pragma unroll
   for (int u = 0; u < SEL_KPT; ++u) {
@@ -449,8 +468,8 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
                                                     const uint8_t* __restrict__ mask_in,
                                                     SelState* __restrict__ st,
                                                     const unsigned long long* __restrict__ cand,
-                                                    int parity, long long ksel, int sel_fixed,
-                                                    int64_t m, int64_t n, int64_t i1, int w, int nkeep,
+                                                    int parity, const Segs segs,
+                                                    int64_t n, int64_t i1, int w, int nkeep,
                                                     int mgroup, uint8_t* __restrict__ codes_out,
                                                     const float* __restrict__ qscale,
                                                     const float* __restrict__ qzero, float qlevels) {
@@ -460,7 +479,16 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   const int wave = tid >> 6, lane = tid & 63;
   const int lc = lane & 15;       // column inside a chunk
   const int lg = lane >> 4;       // row group: rows 4*lg .. 4*lg+3 of the wave's 16
-  const int64_t r0 = (int64_t)blockIdx.x * 64 + wave * 16 + 4 * lg;
+  // this workgroup's segment (matrix): its rows end at m
+  int seg = 0;
+  while (seg + 1 < segs.n && (int)blockIdx.x >= segs.wg0[seg + 1]) ++seg;
+  const int64_t m = segs.row0[seg + 1];
+  const int64_t rbase = segs.row0[seg] + ((int64_t)blockIdx.x - segs.wg0[seg]) * 64;
+  const long long ksel = segs.k[seg];
+  const int sel_fixed = segs.fixed[seg];
+  SelState* const stp = st + seg;
+  const unsigned long long* const candp = cand + segs.row0[seg] * SB;
+  const int64_t r0 = rbase + wave * 16 + 4 * lg;
   const int nch = (w + 15) >> 4;
   RowQuant q;
   if constexpr (QUANT) {
@@ -479,9 +507,9 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   __shared__ HistPick s_pick;
   unsigned long long thr = 0ull;
   if (MODE == MODE_THRESH && sel_fixed == 0)
-    thr = select_finish(st->set[parity], cand, ksel, reinterpret_cast<unsigned long long*>(S.Ub), &s_cnt,
-                        s_pick);
-  if (MODE == MODE_THRESH && blockIdx.x == 0) sel_clear_set(st->set[parity ^ 1], tid, 256);
+    thr = select_finish(stp->set[parity], candp, ksel, reinterpret_cast<unsigned long long*>(S.Ub),
+                        &s_cnt, s_pick);
+  if (MODE == MODE_THRESH && (int)blockIdx.x == segs.wg0[seg]) sel_clear_set(stp->set[parity ^ 1], tid, 256);
 
   {
     // U block, 16-byte loads: pass u covers rows 8u .. 8u+7, one wave
@@ -529,7 +557,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
                    ((reinterpret_cast<uintptr_t>(codes_out) & 3) == 0) &&
                    ((reinterpret_cast<uintptr_t>(Err) & 15) == 0);
   float* Tw = S.Tw[wave];
-  const int64_t rw0 = (int64_t)blockIdx.x * 64 + wave * 16;
+  const int64_t rw0 = rbase + wave * 16;
   bool rowok[4];
   floatx4 Wt[8], Et[8];
   unsigned Pm[8];
@@ -910,13 +938,14 @@ bool lazy_vec(const float* E, const float* U, int64_t n, int64_t c_begin, int64_
 size_t prune_ws_bytes(int64_t m, int64_t n, int blocksize) {
   (void)n;
   (void)blocksize;
-  return round_up(sizeof(SelState), 256) + round_up((size_t)m * EGK * sizeof(float), 256) +
+  return round_up(sizeof(SelState) * SG_MAX_SEGMENTS, 256) + round_up((size_t)m * EGK * sizeof(float), 256) +
          round_up((size_t)m * SB * sizeof(unsigned long long), 256);
 }
 
 sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
   SelState* sel = static_cast<SelState*>(ws);
-  float* Err = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up(sizeof(SelState), 256));
+  float* Err = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                        round_up(sizeof(SelState) * SG_MAX_SEGMENTS, 256));
   const int64_t m = a.m, n = a.n;
   unsigned long long* cand = reinterpret_cast<unsigned long long*>(
       reinterpret_cast<char*>(Err) + round_up((size_t)m * EGK * sizeof(float), 256));
@@ -965,13 +994,25 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
   const int mode = a.mask_in ? MODE_FORCED
                              : (a.kind == SG_NM ? MODE_NM : (a.kind == SG_UNSTRUCTURED_ROW ? MODE_ROW : MODE_THRESH));
   const int B = a.blocksize;
+  // segments: block-global selection runs per stacked matrix; every other
+  // mode decides row by row, so the rows form one segment
+  Segs segs = {};
+  segs.n = mode == MODE_THRESH ? a.nseg : 1;
+  int64_t max_rows = 0;
+  for (int p = 0; p < segs.n; ++p) {
+    segs.row0[p] = mode == MODE_THRESH ? a.seg_rows[p] : 0;
+    segs.row0[p + 1] = mode == MODE_THRESH ? a.seg_rows[p + 1] : m;
+    segs.wg0[p + 1] = segs.wg0[p] + (int)ceil_div(segs.row0[p + 1] - segs.row0[p], 64);
+    max_rows = std::max<int64_t>(max_rows, segs.row0[p + 1] - segs.row0[p]);
+  }
   if (mode == MODE_THRESH) {
-    hipLaunchKernelGGL(sel_clear_kernel, dim3(1), dim3(256), 0, st, sel);
+    hipLaunchKernelGGL(sel_clear_kernel, dim3((unsigned)segs.n), dim3(256), 0, st, sel);
     if (sg_status e = check_launch("select clear")) return e;
   }
   // select: enough workgroups that every thread holds at most SEL_KPT keys
-  const unsigned sel_grid = (unsigned)std::max<int64_t>(1, ceil_div(m, (int64_t)2 * SEL_KPT));
-  const dim3 sw_grid((unsigned)ceil_div(m, 64)), sw_block(256);
+  const dim3 sel_grid((unsigned)std::max<int64_t>(1, ceil_div(max_rows, (int64_t)2 * SEL_KPT)),
+                      (unsigned)segs.n);
+  const dim3 sw_grid((unsigned)segs.wg0[segs.n]), sw_block(256);
   const size_t shm = sizeof(SweepLds);
   // lazy-update groups: GK columns (a multiple of the block width, at most EGK)
   const int64_t GK = (EGK / B) * B;
@@ -981,51 +1022,50 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
     const int64_t g0 = (i1 / GK) * GK;
     const int64_t g_end = std::min<int64_t>(n, g0 + GK);
     float* Eb = Err + (i1 - g0);  // this block's columns of the group's error buffer
-    int sel_fixed = 0;
-    long long k = 0;
     if (mode == MODE_THRESH) {
-      k = (long long)floor(a.sparsity * (double)m * (double)w);
-      const long long total = (long long)m * w;
-      if (k <= 0) {
-        sel_fixed = 2;
-      } else if (k >= total) {
-        sel_fixed = 3;
-      } else {
-        for (int p = 0; p < 2; ++p) {
-          hipLaunchKernelGGL(select_pass_kernel, dim3(sel_grid), dim3(256), sizeof(SelLds), st,
-                             &sel->set[parity], cand, static_cast<const float*>(a.W_out), a.U, m, n,
-                             i1, w, k, p);
+      bool any = false;
+      for (int p = 0; p < segs.n; ++p) {
+        const int64_t mp = segs.row0[p + 1] - segs.row0[p];
+        const long long k = (long long)floor(a.sparsity * (double)mp * (double)w);
+        segs.k[p] = k;
+        segs.fixed[p] = k <= 0 ? 2 : (k >= (long long)mp * w ? 3 : 0);
+        any = any || segs.fixed[p] == 0;
+      }
+      if (any) {
+        for (int pass = 0; pass < 2; ++pass) {
+          hipLaunchKernelGGL(select_pass_kernel, sel_grid, dim3(256), sizeof(SelLds), st, sel, parity,
+                             cand, static_cast<const float*>(a.W_out), a.U, segs, n, i1, w, pass);
           if (sg_status e = check_launch("select pass")) return e;
         }
       }
     }
-#define SG_SWEEP(MD, MG, PAR, K, FIX, NK, MGRP)                                                     \
+#define SG_SWEEP(MD, MG, NK, MGRP)                                                                  \
   do {                                                                                            \
     if (quant)                                                                                    \
       hipLaunchKernelGGL((sweep_kernel<MD, MG, true>), sw_grid, sw_block, shm, st, a.W_out,          \
-                         a.mask_out, Eb, a.U, a.mask_in, sel, cand, PAR, K, FIX, m, n, i1, w, NK,   \
+                         a.mask_out, Eb, a.U, a.mask_in, sel, cand, parity, segs, n, i1, w, NK,     \
                          MGRP, a.codes_out, a.qscale, a.qzero, qlevels);                           \
     else                                                                                          \
       hipLaunchKernelGGL((sweep_kernel<MD, MG, false>), sw_grid, sw_block, shm, st, a.W_out,         \
-                         a.mask_out, Eb, a.U, a.mask_in, sel, cand, PAR, K, FIX, m, n, i1, w, NK,   \
+                         a.mask_out, Eb, a.U, a.mask_in, sel, cand, parity, segs, n, i1, w, NK,     \
                          MGRP, nullptr, nullptr, nullptr, 0.f);                                    \
   } while (0)
     if (mode == MODE_THRESH) {
-      SG_SWEEP(MODE_THRESH, 0, parity, k, sel_fixed, a.n_keep, a.m_group);
+      SG_SWEEP(MODE_THRESH, 0, a.n_keep, a.m_group);
     } else if (mode == MODE_NM) {
       switch (a.m_group) {
-        case 1: SG_SWEEP(MODE_NM, 1, 0, 0ll, 0, a.n_keep, a.m_group); break;
-        case 2: SG_SWEEP(MODE_NM, 2, 0, 0ll, 0, a.n_keep, a.m_group); break;
-        case 4: SG_SWEEP(MODE_NM, 4, 0, 0ll, 0, a.n_keep, a.m_group); break;
-        case 8: SG_SWEEP(MODE_NM, 8, 0, 0ll, 0, a.n_keep, a.m_group); break;
-        case 16: SG_SWEEP(MODE_NM, 16, 0, 0ll, 0, a.n_keep, a.m_group); break;
-        default: SG_SWEEP(MODE_NM, 0, 0, 0ll, 0, a.n_keep, a.m_group); break;
+        case 1: SG_SWEEP(MODE_NM, 1, a.n_keep, a.m_group); break;
+        case 2: SG_SWEEP(MODE_NM, 2, a.n_keep, a.m_group); break;
+        case 4: SG_SWEEP(MODE_NM, 4, a.n_keep, a.m_group); break;
+        case 8: SG_SWEEP(MODE_NM, 8, a.n_keep, a.m_group); break;
+        case 16: SG_SWEEP(MODE_NM, 16, a.n_keep, a.m_group); break;
+        default: SG_SWEEP(MODE_NM, 0, a.n_keep, a.m_group); break;
       }
     } else if (mode == MODE_ROW) {
       // one group per row spanning the block: keep w - floor(p * w)
-      SG_SWEEP(MODE_ROW, 0, 0, 0ll, 0, w - (int)floor(a.sparsity * (double)w), w);
+      SG_SWEEP(MODE_ROW, 0, w - (int)floor(a.sparsity * (double)w), w);
     } else {
-      SG_SWEEP(MODE_FORCED, 0, 0, 0ll, 0, a.n_keep, a.m_group);
+      SG_SWEEP(MODE_FORCED, 0, a.n_keep, a.m_group);
     }
 #undef SG_SWEEP
     if (sg_status e = check_launch("prune sweep")) return e;

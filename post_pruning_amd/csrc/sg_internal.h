@@ -73,6 +73,10 @@ struct PruneArgs {
   int n_keep, m_group;
   int blocksize;
   const uint8_t* mask_in;
+  // row segments: W stacks nseg matrices that share the input (and U);
+  // unstructured selection is per segment
+  int nseg;
+  int64_t seg_rows[SG_MAX_SEGMENTS + 1];
   // joint quantization (bits == 0: pruning only)
   int bits;
   uint8_t* codes_out;

@@ -173,6 +173,24 @@ def test_pack_validation(sg, m, n, dt, code):
     assert st == code, sg.sg_last_error_message()
 
 
+@pytest.mark.parametrize("splits,nseg", [
+    (None, 2),            # no splits
+    ([0, 64, 128], 0),    # nseg < 1
+    ([0, 64, 128], 17),   # nseg > SG_MAX_SEGMENTS
+    ([0, 64, 100], 2),    # does not end at m_total
+    ([0, 80, 64, 128], 3),  # not increasing
+    ([4, 64, 128], 2),    # does not start at 0
+])
+def test_shared_validation(sg, splits, nseg):
+    arr = None
+    if splits is not None:
+        arr = ctypes.cast((ctypes.c_int64 * 18)(*(splits + [128] * (18 - len(splits)))), ctypes.c_void_p)
+    st = _lib(sg).sg_prune_layers_shared(ctypes.c_void_p(0x3000), None, None, None, None, 0, FAKE, 0,
+                                         128, 128, 128, arr, nseg, FAKE, 0, 0.5, 0, 1, 128, None,
+                                         ctypes.c_void_p(0x10000), 10 ** 9, None)
+    assert st == sg.SG_ERR_INVALID_ARGUMENT, sg.sg_last_error_message()
+
+
 def test_product_path_imports_no_oracle():
     # The library binding must not import, call or read the oracle.
     src_dir = os.path.join(ROOT, "post_pruning_amd")

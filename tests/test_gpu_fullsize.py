@@ -203,6 +203,33 @@ def test_mlp_up_11008_nm_rows(sg, attn_oracle):
         assert np.array_equal(meta.index_select(0, ri).cpu().numpy(), mo)
 
 
+def test_mlp_up_11008_quantized_rows(sg, attn_oracle):
+    # joint 2:4 + 4-bit sweep at full size; rows are independent under N:M, so
+    # sampled rows go through the oracle along the GPU's own trajectory
+    res = _run_layer(sg, "mlp_up_11008")
+    cfg = res["cfg"]
+    Wh, mask, codes, scale, zero = sg.sg_prune_quantize_layer(res["W"], res["Hinv"], "2:4", 4,
+                                                              cfg.blocksize)
+    torch.cuda.synchronize()
+    gm, Whg = _check_counts_and_zeros(Wh, mask, "2:4", cfg.blocksize)
+    rows = np.random.default_rng(9).choice(cfg.m, 48, replace=False)
+    Wd = res["W"].cpu().double().numpy()[rows]
+    U = attn_oracle["oracle"]["U"]
+    so, zo = oracle.quant_grid(Wd, 4)
+    sc = scale.cpu().numpy()[rows]
+    assert np.abs(sc - so).max() <= 1e-6 * np.abs(so).max()
+    assert np.array_equal(zero.cpu().numpy()[rows].astype(np.float64), zo)
+    cg = codes.cpu().numpy()[rows]
+    Whf, _, _, _, _, _, tr = oracle.prune_quantized(Wd, U, "2:4", cfg.blocksize, 4, mask_in=gm[rows],
+                                                    codes_in=cg, return_trace=True)
+    _consistency(tr["saliency"], gm[rows], "2:4", cfg.blocksize, across_rows=False)
+    y = tr["at_quant"] / so[:, None]
+    near = np.abs(y - np.floor(y) - 0.5) <= 1e-4
+    want = oracle.quant_code(tr["at_quant"], so[:, None], zo[:, None], 4)
+    assert not np.any((~gm[rows]) & (cg != want) & ~near)
+    assert _rel(Whg[rows], Whf) <= 1e-4
+
+
 # ---------------------------------------------------------------------------
 # wide layers: properties that hold at any size
 # ---------------------------------------------------------------------------
