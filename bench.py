@@ -44,7 +44,7 @@ def algorithmic_work(m, n, N, B):
 
 def hessian_source_hash():
     h = hashlib.sha256()
-    for f in ("hessian.hip", "sg_internal.h"):
+    for f in ("hessian.hip", "hessian.h"):
         with open(os.path.join(ROOT, "post_pruning_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

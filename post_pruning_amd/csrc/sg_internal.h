@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "../../include/sg.h"
+#include "hessian.h"
 
 namespace sg {
 
@@ -14,7 +15,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kNumCU = 256;       // MI355X compute units (launch sizing only)
-constexpr int kHessTile = 256;    // Hessian output tile edge
 constexpr int kFactorNB = 128;    // factorisation panel width
 constexpr int kGemmTile = 128;    // fp32 MFMA update tile edge
 constexpr int kSelBins = 2048;    // radix-select histogram bins
@@ -32,24 +32,6 @@ __device__ inline float bf16_to_f32(uint16_t h) {
 // ---------------------------------------------------------------------------
 sg_status set_error(sg_status s, const char* fmt, ...);
 sg_status check_launch(const char* what);
-
-// ---------------------------------------------------------------------------
-// Hessian
-// ---------------------------------------------------------------------------
-struct HessPlan {
-  int64_t tiles;       // lower-triangle 256x256 tiles
-  int splits;          // token splits
-  int64_t tok_per_split;
-  int group;           // tile-panel group edge of the per-XCD tile order
-  int64_t grid;        // workgroups launched (8 equal per-XCD shares)
-  size_t ws_bytes;     // partials + counters
-};
-HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws);
-sg_status launch_hessian_bf16(float* H, int64_t n, const uint16_t* X, int64_t T,
-                              int64_t ldx, const HessPlan& plan, void* ws,
-                              hipStream_t st);
-sg_status launch_hessian_f32(float* H, int64_t n, const float* X, int64_t T,
-                             int64_t ldx, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Factorisation
