@@ -17,6 +17,9 @@ Sources (cited by page title and section throughout):
 * [VSG] "Vector-Based SparseGPT" -- press article on voc.com.cn, parts 01-02
   (SparseGPT processes weights in order and compensates the rest; block-wise
   processing passes the error on to later parts).
+* [VSG] parts 01-02 also describe vector-level joint compensation: the
+  weights chosen within a range are removed together and the kept ones
+  adjusted jointly (prune_vector).
 * [G24] "LLM 2:4 structured sparsity production guide" -- oh-bug.com, section
   on the 2:4 core mechanism (two zeros in every four consecutive values along
   the reduction axis; the worked example [0.42,-0.18,0.07,0.31]).
@@ -48,6 +51,7 @@ from .sparsegpt_oracle import (  # noqa: F401
     quant_grid,
     quant_code,
     prune_quantized,
+    prune_vector,
     unpack_two_four,
     unstructured_k,
 )

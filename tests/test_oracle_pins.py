@@ -389,6 +389,79 @@ def test_quantized_sweep_forced_decisions_reproduce():
 
 
 # ----------------------------------------------------------------------------
+# vector-level joint compensation
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("pat", [0.5, "0.5/row", "2:4"])
+def test_vector_range_one_is_column_by_column(pat):
+    W, _, _, _, _, U = _layer(51, 6, 32, 150)
+    a = oracle.prune(W, U, pat, 8)
+    b = oracle.prune_vector(W, U, pat, 8, 1)
+    assert np.array_equal(a[1], b[1])
+    assert np.abs(a[0] - b[0]).max() < 1e-12
+    assert np.allclose(a[2], b[2], rtol=1e-10)
+
+
+def test_vector_single_range_is_least_squares_optimum():
+    # one block, one range: the result is the textbook constrained least
+    # squares optimum v_K = H_KK^-1 H_K,: w for the chosen mask, from H_d
+    W, _, _, Hd, _, U = _layer(52, 5, 16, 100)
+    Wh, M, eps = oracle.prune_vector(W, U, 0.5, 16, 16)
+    for r in range(5):
+        K = np.nonzero(~M[r])[0]
+        v = np.zeros(16)
+        v[K] = np.linalg.solve(Hd[np.ix_(K, K)], Hd[K, :] @ W[r])
+        assert np.abs(Wh[r] - v).max() < 1e-10
+        assert _quad(W[r] - v, Hd) == pytest.approx(eps[r], rel=1e-9)
+    # and it is never worse than removing the same weights one at a time
+    _, _, eps_seq = oracle.prune(W, U, 0.5, 16, mask_in=M)
+    assert np.all(eps <= eps_seq * (1 + 1e-12))
+
+
+def test_vector_last_range_is_least_squares_given_prefix():
+    # after the last range's joint step nothing changes any more: its kept
+    # weights are the least-squares optimum with every earlier column fixed at
+    # its final value and the range's chosen weights at zero
+    W, _, _, Hd, _, U = _layer(53, 4, 32, 160)
+    Wh, M, _ = oracle.prune_vector(W, U, "0.5/row", 16, 8)
+    j0 = 24
+    for r in range(4):
+        Q = list(range(j0)) + [j for j in range(j0, 32) if M[r, j]]
+        K = [j for j in range(j0, 32) if not M[r, j]]
+        t = np.where(M[r], 0.0, Wh[r])[Q]
+        vK = W[r, K] + np.linalg.solve(Hd[np.ix_(K, K)], Hd[np.ix_(K, Q)] @ (W[r, Q] - t))
+        assert np.abs(Wh[r, K] - vK).max() < 1e-10
+
+
+@pytest.mark.parametrize("pat,vec", [(0.5, 8), ("4:8", 16), ("16:32", 16), ("0.6/row", 4)])
+def test_vector_error_structure(pat, vec):
+    W, _, _, Hd, _, U = _layer(54, 5, 64, 200)
+    Wh, M, eps, tr = oracle.prune_vector(W, U, pat, 16, vec, return_trace=True)
+    d = W - Wh
+    assert np.abs(d - tr["errors"] @ U).max() < 1e-12
+    for r in range(5):
+        assert _quad(d[r], Hd) == pytest.approx(eps[r], rel=1e-9)
+    assert np.all(Wh[M] == 0.0) and not np.any(np.signbit(Wh[M]))
+    _, Mp, _ = oracle.prune(W, U, pat, 16)
+    if vec == 1:
+        assert np.array_equal(M, Mp)
+
+
+def test_vector_prefix_masks_equal_column_by_column():
+    # chosen sets that are prefixes of each range: removing them one at a time
+    # with the later columns free is already the joint optimum
+    W, _, _, _, _, U = _layer(55, 6, 32, 150)
+    r = rng0(5)
+    M = np.zeros((6, 32), dtype=bool)
+    for i in range(6):
+        for j0 in range(0, 32, 8):
+            M[i, j0:j0 + int(r.integers(0, 9))] = True
+    a = oracle.prune(W, U, 0.5, 8, mask_in=M)
+    b = oracle.prune_vector(W, U, 0.5, 8, 8, mask_in=M)
+    assert np.abs(a[0] - b[0]).max() < 1e-12
+
+
+# ----------------------------------------------------------------------------
 # 2:4 compressed export
 # ----------------------------------------------------------------------------
 
