@@ -116,6 +116,8 @@ def main():
     ap.add_argument("--shared", type=int, default=1,
                     help="prune this many matrices of the layer's shape that share its input "
                          "(stacked, one call with the shared factor)")
+    ap.add_argument("--vec", type=int, default=1,
+                    help="16: remove the chosen weights of each 16-column range together")
     ap.add_argument("--bits", type=int, default=0,
                     help="also round the kept weights to a per-row grid of 2^bits levels in the sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -168,6 +170,9 @@ def main():
         if args.shared > 1:
             sg.sg_prune_layers_shared(W, splits, Hinv, pattern, B, bits=args.bits, W_out=W_out,
                                       mask_out=mask, codes_out=codes, workspace=ws_p)
+        elif args.vec != 1:
+            sg.sg_prune_layer_vector(W, Hinv, pattern, args.vec, B, W_out=W_out, mask_out=mask,
+                                     workspace=ws_p)
         elif args.bits:
             sg.sg_prune_quantize_layer(W, Hinv, pattern, args.bits, B, W_out=W_out, mask_out=mask,
                                        codes_out=codes, workspace=ws_p)
@@ -292,10 +297,12 @@ def main():
         "config": {
             "workload": f"{args.config}: W {m}x{n} {cfg.dtype}, X {N}x{n} {cfg.dtype}, "
                         f"pattern {pattern}, blocksize {B}, damp {cfg.damp}"
-                        + (f", kept weights on a {args.bits}-bit grid" if args.bits else ""),
+                        + (f", kept weights on a {args.bits}-bit grid" if args.bits else "")
+                        + (f", chosen weights removed {args.vec} columns at a time" if args.vec != 1 else ""),
             "m": m, "n": n, "tokens": N, "pattern": pattern, "blocksize": B,
             "quant_bits": args.bits or None,
             "shared_matrices": args.shared,
+            "joint_range": args.vec,
         },
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
         "tflops_algorithmic": total_flops / (ms * 1e-3) / 1e12,

@@ -225,6 +225,38 @@ sg_status sg_prune_quantize_layer(float* W_out, uint8_t* mask_out,
                                   void* stream);
 
 /*
+ * sg_prune_layer_vector -- sg_prune_layer with the chosen weights of each
+ * range of vec consecutive columns removed together (vector-level joint
+ * compensation).
+ *
+ * [VSG] parts 01-02: rather than removing weights one after another with a
+ * compensation after each, the weights chosen within a range are set to
+ * zero together and the kept weights are adjusted jointly.  Readings where
+ * the article is silent:
+ *   - ranges are [j0, j0 + vec); vec = 1 is exactly sg_prune_layer, vec = 16
+ *     removes each row's chosen weights of a 16-column range at once;
+ *   - selection rules, counts and saliencies are those of sg_prune_layer; a
+ *     selection point inside a range sees the values at the range start;
+ *   - at a range start, a row with chosen set P takes the exact multi-weight
+ *     OBS update over the free columns F = [j0, n): delta_F =
+ *     -w_P (G_PP)^-1 G_P,F with G = (H_d[F,F])^-1 = U_FF^T U_FF; the chosen
+ *     weights become +0.0, earlier columns stay as they are.
+ *
+ *   vec       1 or 16; with 16 the block size must be a multiple of 16 and,
+ *             under N:M, M must divide 16 or be a multiple of it.
+ * Every other argument, the workspace and the error behaviour are those of
+ * sg_prune_layer.
+ */
+sg_status sg_prune_layer_vector(float* W_out, uint8_t* mask_out, const void* W,
+                                int32_t w_dtype, int64_t m, int64_t n,
+                                int64_t ldw, const float* Hinv,
+                                int32_t pattern_kind, double sparsity,
+                                int32_t n_keep, int32_t m_group,
+                                int32_t blocksize, int32_t vec,
+                                const uint8_t* mask_in, void* workspace,
+                                size_t ws_bytes, void* stream);
+
+/*
  * sg_prune_layers_shared -- prune several weight matrices that read the same
  * input (the query/key/value projections, or gate and up) in one call with
  * their one shared factor Hinv.

@@ -67,9 +67,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sg_prune_layers_shared.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
                                            c_i64, c_i64, c_vp, c_i32, c_vp, c_i32, c_dbl, c_i32,
                                            c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]
+    lib.sg_prune_layer_vector.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_i32,
+                                          c_dbl, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]
     for f in ("sg_hessian_accumulate", "sg_prepare_hinv", "sg_prune_layer",
               "sg_reconstruction_error", "sg_pack_two_four", "sg_prune_quantize_layer",
-              "sg_prune_layers_shared"):
+              "sg_prune_layers_shared", "sg_prune_layer_vector"):
         getattr(lib, f).restype = c_i32
     lib.sg_workspace_bytes.argtypes = [c_i32, c_i64, c_i64, c_i64, c_i32]
     lib.sg_workspace_bytes.restype = c_sz
@@ -218,6 +220,36 @@ def sg_prune_layer(W: torch.Tensor, Hinv: torch.Tensor, pattern: Union[float, st
     _check(lib.sg_prune_layer(_ptr(W_out), _ptr(mask_out), _ptr(W), _dtype_code(W), m, n, ldw,
                               _ptr(Hinv), kind, sp, nk, mg, int(blocksize), _ptr(mask_in), _ptr(ws),
                               nb, ctypes.c_void_p(_stream(W.device))), "sg_prune_layer")
+    return W_out, mask_out
+
+
+def sg_prune_layer_vector(W: torch.Tensor, Hinv: torch.Tensor, pattern: Union[float, str], vec: int = 16,
+                          blocksize: int = 128, mask_in: Optional[torch.Tensor] = None,
+                          W_out: Optional[torch.Tensor] = None, mask_out: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None):
+    """Prune W with the chosen weights of each range of ``vec`` columns removed
+    together (vec = 16; vec = 1 is sg_prune_layer); returns (W_hat, mask)."""
+    lib = load_library()
+    _require_cuda(W, Hinv, mask_in)
+    m, n = W.shape
+    ldw = _row_major(W, "W")
+    if Hinv.shape != (n, n) or Hinv.dtype != torch.float32 or not Hinv.is_contiguous():
+        raise ValueError("Hinv must be a contiguous [n, n] float32 tensor")
+    if mask_in is not None:
+        if mask_in.shape != (m, n) or not mask_in.is_contiguous():
+            raise ValueError("mask_in must be a contiguous [m, n] tensor")
+        mask_in = mask_in.to(torch.uint8)
+    if W_out is None:
+        W_out = torch.empty(m, n, dtype=torch.float32, device=W.device)
+    if mask_out is None:
+        mask_out = torch.empty(m, n, dtype=torch.uint8, device=W.device)
+    kind, sp, nk, mg = parse_pattern(pattern)
+    need = sg_workspace_bytes(SG_OP_PRUNE, m, n, 0, blocksize)
+    ws, nb = _workspace(need, W.device, workspace)
+    _check(lib.sg_prune_layer_vector(_ptr(W_out), _ptr(mask_out), _ptr(W), _dtype_code(W), m, n, ldw,
+                                     _ptr(Hinv), kind, sp, nk, mg, int(blocksize), int(vec),
+                                     _ptr(mask_in), _ptr(ws), nb, ctypes.c_void_p(_stream(W.device))),
+           "sg_prune_layer_vector")
     return W_out, mask_out
 
 

@@ -13,7 +13,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsg.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "hessian.hip", "factor.hip", "prune.hip", "recon.hip", "export.hip"]
+SOURCES = ["api.hip", "hessian.hip", "factor.hip", "prune.hip", "sweep_plain.hip", "sweep_quant.hip",
+           "sweep_joint.hip", "recon.hip", "export.hip"]
 
 HIPCC_FLAGS = [
     "-std=c++17",

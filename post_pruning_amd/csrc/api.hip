@@ -144,7 +144,8 @@ static sg_status prune_common(float* W_out, uint8_t* mask_out, uint8_t* codes_ou
                               int64_t n, int64_t ldw, const int64_t* row_splits, int32_t nseg,
                               const float* Hinv, int32_t pattern_kind,
                               double sparsity, int32_t n_keep, int32_t m_group, int32_t blocksize,
-                              const uint8_t* mask_in, void* workspace, size_t ws_bytes, void* stream) {
+                              const uint8_t* mask_in, void* workspace, size_t ws_bytes, void* stream,
+                              int32_t vec = 1) {
   if (!W_out || !W || !Hinv) return set_error(SG_ERR_INVALID_ARGUMENT, "W_out, W and Hinv must not be NULL");
   if (m < 1 || n < 1) return set_error(SG_ERR_INVALID_ARGUMENT, "m and n must be >= 1");
   if ((unsigned long long)m * (unsigned long long)n >= (1ull << 32))
@@ -192,6 +193,7 @@ static sg_status prune_common(float* W_out, uint8_t* mask_out, uint8_t* codes_ou
   a.m_group = pattern_kind == SG_NM ? m_group : 1;
   a.blocksize = blocksize;
   a.mask_in = mask_in;
+  a.vec = vec;
   a.nseg = nseg;
   a.seg_rows[0] = 0;
   for (int p = 1; p <= nseg; ++p) a.seg_rows[p] = row_splits ? row_splits[p] : m;
@@ -224,6 +226,25 @@ sg_status sg_prune_quantize_layer(float* W_out, uint8_t* mask_out, uint8_t* code
   return prune_common(W_out, mask_out, codes_out, scale_out, zero_out, bits, W, w_dtype, m, n, ldw,
                       nullptr, 1, Hinv, pattern_kind, sparsity, n_keep, m_group, blocksize, mask_in,
                       workspace, ws_bytes, stream);
+}
+
+sg_status sg_prune_layer_vector(float* W_out, uint8_t* mask_out, const void* W, int32_t w_dtype,
+                                int64_t m, int64_t n, int64_t ldw, const float* Hinv,
+                                int32_t pattern_kind, double sparsity, int32_t n_keep,
+                                int32_t m_group, int32_t blocksize, int32_t vec,
+                                const uint8_t* mask_in, void* workspace, size_t ws_bytes,
+                                void* stream) {
+  g_last_error.clear();
+  if (vec != 1 && vec != 16) return set_error(SG_ERR_UNSUPPORTED, "vec=%d: 1 or 16 supported", vec);
+  if (vec == 16) {
+    if (blocksize % 16 != 0)
+      return set_error(SG_ERR_INVALID_ARGUMENT, "vec=16 needs a block size that is a multiple of 16");
+    if (pattern_kind == SG_NM && 16 % m_group != 0 && m_group % 16 != 0)
+      return set_error(SG_ERR_INVALID_ARGUMENT, "vec=16 needs M | 16 or 16 | M");
+  }
+  return prune_common(W_out, mask_out, nullptr, nullptr, nullptr, 0, W, w_dtype, m, n, ldw, nullptr, 1,
+                      Hinv, pattern_kind, sparsity, n_keep, m_group, blocksize, mask_in, workspace,
+                      ws_bytes, stream, vec);
 }
 
 sg_status sg_prune_layers_shared(float* W_out, uint8_t* mask_out, uint8_t* codes_out, float* scale_out,

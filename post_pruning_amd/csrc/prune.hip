@@ -22,7 +22,7 @@
 //            of the block start without predication.  N:M groups are ranked at
 //            their first column through a small per-row LDS scratch.
 //   lazy     W[:, i2:] -= Err * U[i1:i2, i2:] on fp32 MFMA (K = w).
-#include "gemm_f32.h"
+#include "sweep.h"
 
 #include <math.h>
 
@@ -31,44 +31,6 @@
 
 namespace sg {
 namespace {
-
-constexpr int SB = SG_MAX_BLOCKSIZE;  // 128
-constexpr int EGK = 512;              // columns of a lazy-update group (error buffer width)
-
-enum { MODE_THRESH = 0, MODE_NM = 1, MODE_FORCED = 2, MODE_ROW = 3 };
-
-// Radix-select buffers, double-buffered by block parity: the sweep of block b
-// clears the set block b + 1 will use while nobody reads it.
-struct SelSet {
-  unsigned hist0[kSelBins];   // top 11 bits of every key
-  unsigned hist1[kSelBins];   // next 11 bits of the keys under the top digit
-  unsigned ncand;             // keys gathered under the top digit
-  unsigned pad[63];
-};
-struct SelState {
-  SelSet set[2];
-};
-
-// Row segments of one prune call (kernel argument): segment p is rows
-// [row0[p], row0[p+1]); its sweep workgroups are [wg0[p], wg0[p+1]) (64 rows
-// each); k[p] keys of each block are pruned under block-global selection
-// (fixed[p]: 2 none, 3 all, 0 selected by the radix passes).
-struct Segs {
-  int n;
-  int64_t row0[SG_MAX_SEGMENTS + 1];
-  int wg0[SG_MAX_SEGMENTS + 1];
-  long long k[SG_MAX_SEGMENTS];
-  int fixed[SG_MAX_SEGMENTS];
-};
-
-__device__ inline float saliency(float w, float ucc) {
-  const float q = w / ucc;
-  return q * q;
-}
-
-__device__ inline unsigned long long sal_key(float w, float ucc, uint32_t lin) {
-  return ((unsigned long long)__float_as_uint(saliency(w, ucc)) << 32) | lin;
-}
 
 __global__ void convert_kernel(float* __restrict__ out, const void* __restrict__ W, int dtype,
                                int64_t m, int64_t n, int64_t ldw) {
@@ -85,82 +47,10 @@ __global__ void convert_kernel(float* __restrict__ out, const void* __restrict__
   }
 }
 
-__device__ inline void sel_clear_set(SelSet& s, int tid, int nthreads) {
-  for (int b = tid; b < kSelBins; b += nthreads) {
-    s.hist0[b] = 0u;
-    s.hist1[b] = 0u;
-  }
-  if (tid == 0) s.ncand = 0u;
-}
-
 __global__ void sel_clear_kernel(SelState* st) {  // one workgroup per segment
   sel_clear_set(st[blockIdx.x].set[0], threadIdx.x, blockDim.x);
   sel_clear_set(st[blockIdx.x].set[1], threadIdx.x, blockDim.x);
 }
-
-// Exact k-th smallest 64-bit key (bits(W^2 / U_cc^2) << 32 | r*n + c) of the
-// m x w block, radix select with 11-bit digits, saliency bits first:
-//   pass 0  every workgroup histograms the top digit of its keys (eight
-//           lane-interleaved LDS sub-histograms against contention on hot
-//           bins) and adds it into the block's global histogram;
-//   pass 1  every workgroup scans that histogram itself (2048 bins), fixes the
-//           top digit, histograms the next digit of the keys under it and
-//           gathers those keys into a candidate list;
-//   sweep   every sweep workgroup scans the second histogram, fixes the second
-//           digit, and either takes the whole bucket or sorts the keys under
-//           both digits (gathered from the candidate list) in LDS and reads
-//           off the one of the remaining rank.
-// No workgroup waits for another: each kernel consumes what the previous one
-// completed.
-constexpr int SEL_KPT = 32;    // keys per thread
-constexpr int SEL_SUB = 8;     // LDS sub-histograms
-constexpr int SEL_SORT = 8192; // keys sorted in LDS
-
-// Scan of a 2048-bin histogram (256 threads, thread t owns bins 8t..8t+7):
-// the bin holding the krem-th key, the keys before it and its count, in LDS.
-struct HistPick {
-  unsigned digit, cnt;
-  unsigned long long before;
-  unsigned wsum[4];
-};
-
-__device__ void hist_locate(const unsigned* hist, long long krem, HistPick& P) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int per = kSelBins / 256;
-  unsigned cnt[per];
-  unsigned local = 0;
-#pragma unroll
-  for (int i = 0; i < per; ++i) {
-    cnt[i] = hist[tid * per + i];
-    local += cnt[i];
-  }
-  unsigned incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
-  }
-  if (lane == 63) P.wsum[wave] = incl;
-  __syncthreads();
-  unsigned wbase = 0;
-  for (int wv = 0; wv < wave; ++wv) wbase += P.wsum[wv];
-  unsigned long long cum = (unsigned long long)(wbase + incl - local);
-  const unsigned long long after = (unsigned long long)(wbase + incl);
-  if ((long long)cum < krem && krem <= (long long)after) {
-#pragma unroll
-    for (int i = 0; i < per; ++i) {
-      const unsigned cn = cnt[i];
-      if ((long long)cum < krem && (long long)(cum + cn) >= krem) {
-        P.digit = (unsigned)(tid * per + i);
-        P.before = cum;
-        P.cnt = cn;
-      }
-      cum += cn;
-    }
-  }
-  __syncthreads();
-}
-
 struct SelLds {
   unsigned h[SEL_SUB][kSelBins];
   unsigned long long stage[SEL_SORT];
@@ -231,635 +121,6 @@ __global__ __launch_bounds__(256) void select_pass_kernel(SelState* st, int pari
     if (tid == 0) L.gbase = atomicAdd(&ss->ncand, L.nstage);
     __syncthreads();
     for (unsigned i = tid; i < L.nstage; i += 256) cand[L.gbase + i] = L.stage[i];
-  }
-}
-
-// Threshold key of the block from the two histograms and the candidates
-// (run by every sweep workgroup; `scratch` holds SEL_SORT keys of LDS).
-__device__ unsigned long long select_finish(const SelSet& ss, const unsigned long long* cand,
-                                            long long k, unsigned long long* scratch,
-                                            unsigned* s_cnt, HistPick& P) {
-  const int tid = threadIdx.x;
-  hist_locate(ss.hist0, k, P);
-  const unsigned d0 = P.digit;
-  const long long k1 = k - (long long)P.before;
-  hist_locate(ss.hist1, k1, P);
-  const unsigned long long pf = ((unsigned long long)d0 << 53) | ((unsigned long long)P.digit << 42);
-  long long kr = k1 - (long long)P.before;
-  const unsigned cnt = P.cnt;
-  if ((long long)cnt == kr) return pf | ((1ull << 42) - 1ull);  // the bucket is taken whole
-  const unsigned ncand = ss.ncand;
-  const unsigned long long fmask2 = ~((1ull << 42) - 1ull);
-  if (cnt <= (unsigned)SEL_SORT) {
-    if (tid == 0) *s_cnt = 0u;
-    __syncthreads();
-    // candidates read 16 per thread at a time, all loads in flight together
-    for (unsigned base = 0; base < ncand; base += 256 * 16) {
-      unsigned long long kv[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const unsigned i = base + u * 256 + tid;
-        kv[u] = cand[i < ncand ? i : ncand - 1];
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const unsigned i = base + u * 256 + tid;
-        if (i < ncand && (kv[u] & fmask2) == pf) scratch[atomicAdd(s_cnt, 1u)] = kv[u];
-      }
-    }
-    __syncthreads();
-    const unsigned got = *s_cnt;
-    unsigned sz = 1;
-    while (sz < got) sz <<= 1;
-    for (unsigned i = got + tid; i < sz; i += 256) scratch[i] = ~0ull;
-    __syncthreads();
-    for (unsigned kk = 2; kk <= sz; kk <<= 1) {
-      for (unsigned j = kk >> 1; j > 0; j >>= 1) {
-        for (unsigned i = tid; i < sz; i += 256) {
-          const unsigned ixj = i ^ j;
-          if (ixj > i) {
-            const unsigned long long a = scratch[i], b = scratch[ixj];
-            if ((a > b) == ((i & kk) == 0)) {
-              scratch[i] = b;
-              scratch[ixj] = a;
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
-    const unsigned long long t = scratch[kr - 1];
-    __syncthreads();
-    return t;
-  }
-  // too many keys under both digits to sort: radix passes over the list,
-  // with the first 2048 words of scratch as the histogram
-  unsigned* h = reinterpret_cast<unsigned*>(scratch);
-  unsigned long long p2 = pf;
-  static constexpr int kShift[4] = {32, 21, 10, 0};
-  static constexpr int kWidth[4] = {10, 11, 11, 10};
-  for (int p = 0; p < 4; ++p) {
-    const int sh = kShift[p];
-    const unsigned dm = (1u << kWidth[p]) - 1u;
-    const unsigned long long fm = ~((1ull << (sh + kWidth[p])) - 1ull);
-    for (int b = tid; b < kSelBins; b += 256) h[b] = 0u;
-    __syncthreads();
-    for (unsigned base = 0; base < ncand; base += 256 * 16) {
-      unsigned long long kv[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const unsigned i = base + u * 256 + tid;
-        kv[u] = cand[i < ncand ? i : ncand - 1];
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const unsigned i = base + u * 256 + tid;
-        if (i < ncand && (kv[u] & fm) == p2) atomicAdd(&h[(unsigned)(kv[u] >> sh) & dm], 1u);
-      }
-    }
-    __syncthreads();
-    hist_locate(h, kr, P);
-    p2 |= (unsigned long long)P.digit << sh;
-    kr -= (long long)P.before;
-    if ((long long)P.cnt == kr || sh == 0) {
-      const unsigned long long t = p2 | ((sh > 0) ? ((1ull << sh) - 1ull) : 0ull);
-      __syncthreads();
-      return t;
-    }
-    __syncthreads();
-  }
-  return ~0ull;  // not reached
-}
-
-// ---- in-block sweep ---------------------------------------------------------
-// One wave per 16 rows; the block's columns are held in registers as eight
-// 16x16 tiles in the fp32 MFMA accumulator layout (lane l, register v: row
-// 4*(l/16) + v, column l%16 of the tile).  Per 16-column chunk c:
-//   * the 16 columns are swept in order: the owner lanes (column j of the
-//     chunk) compute e = W[r,J] / U_JJ for pruned entries, a DPP row
-//     broadcast hands e to the other 15 lanes of the row, which subtract
-//     e * U[J, col] (U is zero left of the diagonal, so earlier columns are
-//     untouched);
-//   * the chunk's errors E_c (16 x 16) then update every later chunk at once,
-//     W[:, c'] -= E_c U[c, c'], on v_mfma_f32_16x16x4_f32 (E_c goes through a
-//     small per-wave LDS tile to reach the A-operand layout).
-// This is the same computation as the column-by-column OBS sweep, with the
-// updates of later chunks batched (they only add into columns not yet
-// reached).  The U block (upper triangle, zero elsewhere) sits in LDS.
-constexpr int SWS = SB + 4;  // LDS row stride of the U block (floats)
-constexpr int ESS = 20;      // per-wave E tile row stride (floats)
-
-struct SweepLds {
-  float Ub[SB * SWS];
-  float Rd[SB];          // 1 / U_JJ (0 past the block)
-  float Es[4][16 * ESS];
-  float Tw[4][16 * SWS]; // per-wave 16 x 128 staging tile (row-major), N:M scratch
-};
-
-// Lane L of every 16-lane row to the whole row (DPP row_newbcast).
-template <int L>
-__device__ inline float bcast16_c(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + L, 0xF, 0xF, true));
-}
-
-// lexicographic (saliency, position) rank among cnt values
-__device__ __forceinline__ int rank_of(const float* sal, int cnt, float my, int me) {
-  int rank = 0;
-  for (int t = 0; t < cnt; ++t) {
-    const float o = sal[t];
-    rank += (o < my || (o == my && t < me)) ? 1 : 0;
-  }
-  return rank;
-}
-
-// Sum of x over the 16 lanes of a DPP row, returned in every lane of the row
-// (Hillis-Steele scan by row_shr 1, 2, 4, 8, then lane 15 broadcast).
-__device__ __forceinline__ int rowsum16(int x) {
-  x += __builtin_amdgcn_mov_dpp(x, 0x111, 0xF, 0xF, true);
-  x += __builtin_amdgcn_mov_dpp(x, 0x112, 0xF, 0xF, true);
-  x += __builtin_amdgcn_mov_dpp(x, 0x114, 0xF, 0xF, true);
-  x += __builtin_amdgcn_mov_dpp(x, 0x118, 0xF, 0xF, true);
-  return __builtin_amdgcn_mov_dpp(x, 0x15F, 0xF, 0xF, true);
-}
-
-// Per-chunk constants of one lane (its column col = 16c + lc of the chunk):
-//   g[j] = U[16c + j][col] / U_JJ for j != lc, 0 for j == lc;
-// the owner lane of column J keeps its value frozen from step J on, so the
-// chunk's errors can be formed at its end from the registers.
-struct ChunkCtx {
-  float g[16];
-  float rd;      // 1 / U_col,col
-  float ucc;     // U_col,col
-};
-
-// Grid of the joint sparse + quantized sweep for the lane's four rows:
-// value = s * (code - z), code = clamp(round(x / s) + z, 0, L), rounding half
-// to even (x / s taken as x * (1 / s)).
-struct RowQuant {
-  float s[4], inv[4], z[4];
-  float L;
-};
-
-__device__ __forceinline__ float quant_value(float x, const RowQuant& q, int v) {
-  const float c = fminf(fmaxf(rintf(x * q.inv[v]) + q.z[v], 0.f), q.L);
-  return q.s[v] * (c - q.z[v]);
-}
-
-// Sweep column j of the chunk (compile-time j: static DPP lane and indices).
-// Chain per step and row: select (pruned ? W_J : 0) on the owner lane, DPP
-// broadcast over the 16 lanes of the row, fused multiply-add.
-// 1 if member T of the group starting at lane J precedes this lane's value
-// in (saliency, position) order
-template <int J, int T>
-__device__ __forceinline__ int ahead_of(float my, int me) {
-  const float o = bcast16_c<J + T>(my);
-  return (o < my || (o == my && T < me)) ? 1 : 0;
-}
-
-template <int J, int... Ts>
-__device__ __forceinline__ int group_rank(std::integer_sequence<int, Ts...>, float my, int me) {
-  return (ahead_of<J, Ts>(my, me) + ... + 0);
-}
-
-template <int J, int MGS, bool QUANT>
-__device__ __forceinline__ void sweep_step(floatx4& Wc, unsigned& Pc, const ChunkCtx& cx, int lc,
-                                           int nkeep, unsigned rowbits, const RowQuant& q) {
-  if constexpr (MGS > 0) {
-    if constexpr ((J % MGS) == 0) {
-      // N:M group of MGS <= 16 columns = lanes J .. J+MGS-1 of the row: rank
-      // the current saliencies at the group start; the group's values reach
-      // every lane of the row by DPP row broadcasts
-      const int me = lc - J;
-      const bool in = me >= 0 && me < MGS;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float my = saliency(Wc[v], cx.ucc);
-        const int rank = group_rank<J>(std::make_integer_sequence<int, MGS>{}, my, me);
-        if (in && ((rowbits >> v) & 1u) && rank < MGS - nkeep) Pc |= 1u << v;
-      }
-    }
-  }
-  // owner lane's deviation from its target (0 if pruned, the grid value if
-  // kept and quantized), times U_JJ: the DPP broadcast hands it to the row
-  float e[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    float d;
-    if constexpr (QUANT)
-      d = ((Pc >> v) & 1u) ? Wc[v] : Wc[v] - quant_value(Wc[v], q, v);
-    else
-      d = ((Pc >> v) & 1u) ? Wc[v] : 0.f;
-    e[v] = bcast16_c<J>(d);
-  }
-#pragma unroll
-  for (int v = 0; v < 4; ++v) Wc[v] = fmaf(-e[v], cx.g[J], Wc[v]);
-}
-
-template <int MGS, bool QUANT, int... Js>
-__device__ __forceinline__ void sweep_chunk(std::integer_sequence<int, Js...>, floatx4& Wc, unsigned& Pc,
-                                            const ChunkCtx& cx, int lc, int nkeep, unsigned rowbits,
-                                            const RowQuant& q) {
-  (sweep_step<Js, MGS, QUANT>(Wc, Pc, cx, lc, nkeep, rowbits, q), ...);
-}
-
-template <int MODE, int MGS, bool QUANT>
-__global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8_t* __restrict__ mask_out,
-                                                    float* __restrict__ Err, const float* __restrict__ U,
-                                                    const uint8_t* __restrict__ mask_in,
-                                                    SelState* __restrict__ st,
-                                                    const unsigned long long* __restrict__ cand,
-                                                    int parity, const Segs segs,
-                                                    int64_t n, int64_t i1, int w, int nkeep,
-                                                    int mgroup, uint8_t* __restrict__ codes_out,
-                                                    const float* __restrict__ qscale,
-                                                    const float* __restrict__ qzero, float qlevels) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  SweepLds& S = *reinterpret_cast<SweepLds*>(smem);
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int lc = lane & 15;       // column inside a chunk
-  const int lg = lane >> 4;       // row group: rows 4*lg .. 4*lg+3 of the wave's 16
-  // this workgroup's segment (matrix): its rows end at m
-  int seg = 0;
-  while (seg + 1 < segs.n && (int)blockIdx.x >= segs.wg0[seg + 1]) ++seg;
-  const int64_t m = segs.row0[seg + 1];
-  const int64_t rbase = segs.row0[seg] + ((int64_t)blockIdx.x - segs.wg0[seg]) * 64;
-  const long long ksel = segs.k[seg];
-  const int sel_fixed = segs.fixed[seg];
-  SelState* const stp = st + seg;
-  const unsigned long long* const candp = cand + segs.row0[seg] * SB;
-  const int64_t r0 = rbase + wave * 16 + 4 * lg;
-  const int nch = (w + 15) >> 4;
-  RowQuant q;
-  if constexpr (QUANT) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t r = r0 + v < m ? r0 + v : m - 1;
-      q.s[v] = qscale[r];
-      q.inv[v] = 1.f / q.s[v];
-      q.z[v] = qzero[r];
-    }
-    q.L = qlevels;
-  }
-
-  // threshold key of the block (the LDS of the U block serves as scratch)
-  __shared__ unsigned s_cnt;
-  __shared__ HistPick s_pick;
-  unsigned long long thr = 0ull;
-  if (MODE == MODE_THRESH && sel_fixed == 0)
-    thr = select_finish(stp->set[parity], candp, ksel, reinterpret_cast<unsigned long long*>(S.Ub),
-                        &s_cnt, s_pick);
-  if (MODE == MODE_THRESH && (int)blockIdx.x == segs.wg0[seg]) sel_clear_set(stp->set[parity ^ 1], tid, 256);
-
-  {
-    // U block, 16-byte loads: pass u covers rows 8u .. 8u+7, one wave
-    // instruction reads two whole 512-byte rows.  Clamped in-bounds
-    // addresses (rows/columns past the block re-read the last one); entries
-    // outside the upper triangle of the w x w block are stored as zero.
-    const bool vec = ((n & 3) == 0) && ((i1 & 3) == 0);  // 16-byte aligned rows
-    floatx4 uv[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int f = u * 256 + tid;
-      const int j = f >> 5, c4 = (f & 31) * 4;
-      const int jc = j < w ? j : w - 1;
-      const float* urow = U + (i1 + jc) * n + i1;
-      if (vec && c4 + 4 <= w) {
-        uv[u] = *reinterpret_cast<const floatx4*>(urow + c4);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) uv[u][e] = urow[c4 + e < w ? c4 + e : w - 1];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int f = u * 256 + tid;
-      const int j = f >> 5, c4 = (f & 31) * 4;
-      floatx4 t;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = c4 + e;
-        t[e] = (j < w && c < w && c >= j) ? uv[u][e] : 0.f;
-      }
-      *reinterpret_cast<floatx4*>(&S.Ub[j * SWS + c4]) = t;
-    }
-  }
-  if (tid < SB) S.Rd[tid] = (tid < w) ? 1.f / U[(i1 + tid) * n + i1 + tid] : 0.f;
-
-  // Block columns in registers; rows past m read row m-1 and stay unwritten.
-  // With 16-byte aligned rows the tile goes through the wave's LDS staging
-  // area: coalesced 16-byte global accesses (one wave instruction = two
-  // 512-byte rows), accumulator layout on the LDS side.
-  const bool vio = ((n & 3) == 0) && ((i1 & 3) == 0) && ((w & 3) == 0) &&
-                   ((reinterpret_cast<uintptr_t>(W) & 15) == 0) &&
-                   ((reinterpret_cast<uintptr_t>(mask_in) & 3) == 0) &&
-                   ((reinterpret_cast<uintptr_t>(mask_out) & 3) == 0) &&
-                   ((reinterpret_cast<uintptr_t>(codes_out) & 3) == 0) &&
-                   ((reinterpret_cast<uintptr_t>(Err) & 15) == 0);
-  float* Tw = S.Tw[wave];
-  const int64_t rw0 = rbase + wave * 16;
-  bool rowok[4];
-  floatx4 Wt[8], Et[8];
-  unsigned Pm[8];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) rowok[v] = r0 + v < m;
-  if (vio) {
-    floatx4 t[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
-      const int64_t r = rw0 + rr < m ? rw0 + rr : m - 1;
-      t[u] = *reinterpret_cast<const floatx4*>(W + r * n + i1 + (c4 < w ? c4 : w - 4));
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
-      *reinterpret_cast<floatx4*>(&Tw[rr * SWS + c4]) = c4 < w ? t[u] : floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) Wt[c][v] = Tw[(4 * lg + v) * SWS + 16 * c + lc];
-    __builtin_amdgcn_wave_barrier();
-  } else {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int col = 16 * c + lc;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t r = rowok[v] ? r0 + v : m - 1;
-        Wt[c][v] = (col < w) ? W[r * n + i1 + (col < w ? col : 0)] : 0.f;
-      }
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    Et[c] = floatx4{0.f, 0.f, 0.f, 0.f};
-    Pm[c] = 0u;
-  }
-  __syncthreads();
-
-  // masks known at the block start
-  if (MODE == MODE_FORCED) {
-    if (vio) {
-      // the wave's 16 x w mask bytes, 4 bytes per access, through the staging tile
-      unsigned* Tb = reinterpret_cast<unsigned*>(Tw);
-      unsigned mw[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
-        const int64_t r = rw0 + rr < m ? rw0 + rr : m - 1;
-        mw[u] = *reinterpret_cast<const unsigned*>(mask_in + r * n + i1 + (c4 < w ? c4 : w - 4));
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
-        Tb[rr * 32 + (c4 >> 2)] = c4 < w ? mw[u] : 0u;
-      }
-      __builtin_amdgcn_wave_barrier();
-      const unsigned char* Tm = reinterpret_cast<const unsigned char*>(Tw);
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (rowok[v] && Tm[(4 * lg + v) * 128 + 16 * c + lc] != 0) Pm[c] |= 1u << v;
-      __builtin_amdgcn_wave_barrier();
-    } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int col = 16 * c + lc;
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (rowok[v] && col < w && mask_in[(r0 + v) * n + i1 + col] != 0) Pm[c] |= 1u << v;
-      }
-    }
-  } else if (MODE == MODE_THRESH) {
-    const unsigned done = sel_fixed ? (unsigned)sel_fixed : 1u;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int col = 16 * c + lc;
-      if (col < w) {
-        const float ucc = S.Ub[col * SWS + col];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          if (!rowok[v]) continue;
-          const unsigned long long key = sal_key(Wt[c][v], ucc, (uint32_t)((r0 + v) * n + i1 + col));
-          if (done == 3u || (done == 1u && key <= thr)) Pm[c] |= 1u << v;
-        }
-      }
-    }
-  }
-
-  float* Es = S.Es[wave];
-  // groups of M <= 16 are ranked inside the column steps (MGS = M); larger
-  // groups (and the per-row mode, whose group is the whole block: mgroup = w)
-  // at their first chunk, from the saliencies of all their chunks
-  const bool nm_large = (MODE == MODE_NM && MGS == 0) || MODE == MODE_ROW;
-  const unsigned rowbits = (rowok[0] ? 1u : 0u) | (rowok[1] ? 2u : 0u) | (rowok[2] ? 4u : 0u) |
-                           (rowok[3] ? 8u : 0u);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    if (c >= nch) break;
-    ChunkCtx cx;
-    {
-      const int col = 16 * c + lc;
-      cx.ucc = S.Ub[col * SWS + col];
-      cx.rd = (col < w) ? 1.f / cx.ucc : 0.f;
-      float rdj[16];
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const floatx4 t = *reinterpret_cast<const floatx4*>(&S.Rd[16 * c + 4 * j4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rdj[4 * j4 + e] = t[e];
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        cx.g[j] = (j == lc) ? 0.f : S.Ub[(16 * c + j) * SWS + col] * rdj[j];
-    }
-    if (nm_large && ((16 * c) % mgroup) == 0) {
-      // group of mgroup columns = chunks c .. c + ceil(mgroup/16) - 1 (all current)
-      const int nchg = (mgroup + 15) >> 4;
-      const int kp = mgroup - nkeep;  // pruned per row
-      if (mgroup > 64) {
-        // k-th smallest 39-bit key (saliency bits, position) per row by a
-        // bitwise search: counts over the 16 lanes of the row by DPP sums
-        unsigned long long key[8][4];
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
-          const int pos = 16 * g + lc;
-          const int col = 16 * (c + g) + lc;
-          const bool ok = g < nchg && c + g < 8 && pos < mgroup;
-          const float ucg = S.Ub[(ok ? col : 0) * SWS + (ok ? col : 0)];
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            key[g][v] = ok ? (((unsigned long long)__float_as_uint(saliency(Wt[c + g < 8 ? c + g : 7][v], ucg))
-                               << 7) | (unsigned)pos)
-                           : ~0ull;
-        }
-        unsigned long long T[4] = {0ull, 0ull, 0ull, 0ull};
-        for (int b = 38; b >= 0; --b) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const unsigned long long cand = T[v] | (1ull << b);
-            int cnt = 0;
-#pragma unroll
-            for (int g = 0; g < 8; ++g) cnt += key[g][v] < cand ? 1 : 0;
-            if (rowsum16(cnt) < kp) T[v] = cand;
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
-          if (c + g >= 8) continue;
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (rowok[v] && kp > 0 && key[g][v] <= T[v]) Pm[c + g] |= 1u << v;
-        }
-      } else {
-        float* sc = Tw;
-        for (int g = 0; g < nchg && c + g < 8; ++g) {
-          const int col = 16 * (c + g) + lc;
-          const float ucg = S.Ub[col * SWS + col];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) sc[(4 * lg + v) * SWS + 16 * g + lc] = saliency(Wt[c + g][v], ucg);
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_wave_barrier();
-        for (int g = 0; g < nchg && c + g < 8; ++g) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float* row = sc + (4 * lg + v) * SWS;
-            const int me = 16 * g + lc;
-            if (rowok[v] && me < mgroup && rank_of(row, mgroup, row[me], me) < kp)
-              Pm[c + g] |= 1u << v;
-          }
-        }
-        __builtin_amdgcn_wave_barrier();
-      }
-    }
-    sweep_chunk<MGS, QUANT>(std::make_integer_sequence<int, 16>{}, Wt[c], Pm[c], cx, lc, nkeep, rowbits, q);
-    // errors of the chunk: e = (W_J - target) / U_JJ, from the frozen owner
-    // values; pruned entries become +0.0, quantized ones their grid value
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const bool p = (Pm[c] >> v) & 1u;
-      if constexpr (QUANT) {
-        const float t = quant_value(Wt[c][v], q, v);
-        Et[c][v] = (p ? Wt[c][v] : Wt[c][v] - t) * cx.rd;
-        Wt[c][v] = p ? 0.f : t;
-      } else {
-        Et[c][v] = p ? Wt[c][v] * cx.rd : 0.f;
-        Wt[c][v] = p ? 0.f : Wt[c][v];
-      }
-    }
-    if (c + 1 < nch) {
-      // E_c to the A-operand layout: Es[row][4*(k%4) + k/4] so that lane l
-      // reads E[l%16][4*i + l/16] for i = 0..3 as one 16-byte value
-#pragma unroll
-      for (int v = 0; v < 4; ++v) Es[(4 * lg + v) * ESS + 4 * (lc & 3) + (lc >> 2)] = Et[c][v];
-      __builtin_amdgcn_s_waitcnt(0);
-      __builtin_amdgcn_wave_barrier();
-      const floatx4 ea = *reinterpret_cast<const floatx4*>(&Es[lc * ESS + 4 * lg]);
-      __builtin_amdgcn_wave_barrier();
-      // B operands first (one wait), then the MFMAs with independent
-      // accumulators back to back
-      float bv[8][4];
-#pragma unroll
-      for (int c2 = 1; c2 < 8; ++c2) {
-        if (c2 <= c) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          bv[c2][i] = c2 < nch ? S.Ub[(16 * c + 4 * i + lg) * SWS + 16 * c2 + lc] : 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int c2 = 1; c2 < 8; ++c2) {
-          if (c2 <= c) continue;
-          Wt[c2] = __builtin_amdgcn_mfma_f32_16x16x4f32(-ea[i], bv[c2][i], Wt[c2], 0, 0, 0);
-        }
-    }
-  }
-
-  // retire the block: W (pruned entries +0.0), errors, mask
-  if (vio) {
-    __builtin_amdgcn_wave_barrier();
-    // W, then the errors, then the mask bytes through the staging tile
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          Tw[(4 * lg + v) * SWS + 16 * c + lc] = pass == 0 ? Wt[c][v] : Et[c][v];
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
-        const int64_t r = rw0 + rr;
-        const floatx4 t = *reinterpret_cast<const floatx4*>(&Tw[rr * SWS + c4]);
-        if (r < m) {
-          if (pass == 0) {
-            if (c4 < w) *reinterpret_cast<floatx4*>(W + r * n + i1 + c4) = t;
-          } else {
-            if (c4 < w) *reinterpret_cast<floatx4*>(Err + r * EGK + c4) = t;
-          }
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-    if (mask_out) {
-      unsigned char* Tm = reinterpret_cast<unsigned char*>(Tw);
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) Tm[(4 * lg + v) * 128 + 16 * c + lc] = (Pm[c] >> v) & 1u;
-      __builtin_amdgcn_wave_barrier();
-      const unsigned* Tb = reinterpret_cast<const unsigned*>(Tw);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
-        const int64_t r = rw0 + rr;
-        if (r < m && c4 < w) *reinterpret_cast<unsigned*>(mask_out + r * n + i1 + c4) = Tb[rr * 32 + (c4 >> 2)];
-      }
-    }
-    if (QUANT && codes_out) {
-      // grid codes, recovered from the final values (pruned: 0 -> z)
-      __builtin_amdgcn_wave_barrier();
-      unsigned char* Tm = reinterpret_cast<unsigned char*>(Tw);
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          Tm[(4 * lg + v) * 128 + 16 * c + lc] =
-              (unsigned char)fminf(fmaxf(rintf(Wt[c][v] * q.inv[v]) + q.z[v], 0.f), q.L);
-      __builtin_amdgcn_wave_barrier();
-      const unsigned* Tb = reinterpret_cast<const unsigned*>(Tw);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
-        const int64_t r = rw0 + rr;
-        if (r < m && c4 < w) *reinterpret_cast<unsigned*>(codes_out + r * n + i1 + c4) = Tb[rr * 32 + (c4 >> 2)];
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int col = 16 * c + lc;
-    if (col >= w) continue;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      if (!rowok[v]) continue;
-      const int64_t r = r0 + v;
-      const bool p = (Pm[c] >> v) & 1u;
-      W[r * n + i1 + col] = Wt[c][v];
-      if (mask_out) mask_out[r * n + i1 + col] = p ? 1 : 0;
-      if (QUANT && codes_out)
-        codes_out[r * n + i1 + col] =
-            (unsigned char)fminf(fmaxf(rintf(Wt[c][v] * q.inv[v]) + q.z[v], 0.f), q.L);
-      Err[r * EGK + col] = Et[c][v];
-    }
   }
 }
 
@@ -960,29 +221,8 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(select_pass_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SelLds)) != hipSuccess)
     return set_error(SG_ERR_HIP, "hipFuncSetAttribute(select_pass_kernel) failed");
-  const void* sweep_fns[] = {reinterpret_cast<const void*>(sweep_kernel<MODE_THRESH, 0, false>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_FORCED, 0, false>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_ROW, 0, false>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 0, false>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 1, false>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 2, false>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 4, false>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 8, false>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 16, false>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_THRESH, 0, true>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_FORCED, 0, true>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_ROW, 0, true>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 0, true>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 1, true>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 2, true>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 4, true>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 8, true>),
-                             reinterpret_cast<const void*>(sweep_kernel<MODE_NM, 16, true>)};
-  for (const void* f : sweep_fns)
-    if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SweepLds)) !=
-        hipSuccess)
-      return set_error(SG_ERR_HIP, "hipFuncSetAttribute(sweep_kernel) failed");
   const bool quant = a.bits > 0;
+  const bool joint = a.vec == 16;
   const float qlevels = quant ? (float)((1 << a.bits) - 1) : 0.f;
   if (quant) {
     // grid from the original weights (W_out holds their fp32 copy)
@@ -1012,8 +252,7 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
   // select: enough workgroups that every thread holds at most SEL_KPT keys
   const dim3 sel_grid((unsigned)std::max<int64_t>(1, ceil_div(max_rows, (int64_t)2 * SEL_KPT)),
                       (unsigned)segs.n);
-  const dim3 sw_grid((unsigned)segs.wg0[segs.n]), sw_block(256);
-  const size_t shm = sizeof(SweepLds);
+  const dim3 sw_grid((unsigned)segs.wg0[segs.n]);
   // lazy-update groups: GK columns (a multiple of the block width, at most EGK)
   const int64_t GK = (EGK / B) * B;
   int parity = 0;
@@ -1039,36 +278,37 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
         }
       }
     }
-#define SG_SWEEP(MD, MG, NK, MGRP)                                                                  \
-  do {                                                                                            \
-    if (quant)                                                                                    \
-      hipLaunchKernelGGL((sweep_kernel<MD, MG, true>), sw_grid, sw_block, shm, st, a.W_out,          \
-                         a.mask_out, Eb, a.U, a.mask_in, sel, cand, parity, segs, n, i1, w, NK,     \
-                         MGRP, a.codes_out, a.qscale, a.qzero, qlevels);                           \
-    else                                                                                          \
-      hipLaunchKernelGGL((sweep_kernel<MD, MG, false>), sw_grid, sw_block, shm, st, a.W_out,         \
-                         a.mask_out, Eb, a.U, a.mask_in, sel, cand, parity, segs, n, i1, w, NK,     \
-                         MGRP, nullptr, nullptr, nullptr, 0.f);                                    \
-  } while (0)
-    if (mode == MODE_THRESH) {
-      SG_SWEEP(MODE_THRESH, 0, a.n_keep, a.m_group);
-    } else if (mode == MODE_NM) {
-      switch (a.m_group) {
-        case 1: SG_SWEEP(MODE_NM, 1, a.n_keep, a.m_group); break;
-        case 2: SG_SWEEP(MODE_NM, 2, a.n_keep, a.m_group); break;
-        case 4: SG_SWEEP(MODE_NM, 4, a.n_keep, a.m_group); break;
-        case 8: SG_SWEEP(MODE_NM, 8, a.n_keep, a.m_group); break;
-        case 16: SG_SWEEP(MODE_NM, 16, a.n_keep, a.m_group); break;
-        default: SG_SWEEP(MODE_NM, 0, a.n_keep, a.m_group); break;
-      }
-    } else if (mode == MODE_ROW) {
+    SweepArgs sa;
+    sa.W = a.W_out;
+    sa.mask_out = a.mask_out;
+    sa.Err = Eb;
+    sa.U = a.U;
+    sa.mask_in = a.mask_in;
+    sa.st = sel;
+    sa.cand = cand;
+    sa.parity = parity;
+    sa.segs = segs;
+    sa.n = n;
+    sa.i1 = i1;
+    sa.w = w;
+    sa.nkeep = a.n_keep;
+    sa.mgroup = a.m_group;
+    sa.codes_out = a.codes_out;
+    sa.qscale = a.qscale;
+    sa.qzero = a.qzero;
+    sa.qlevels = qlevels;
+    sa.mode = mode;
+    sa.mgs = 0;
+    sa.grid = sw_grid;
+    sa.stream = st;
+    if (mode == MODE_NM && a.m_group <= 16) sa.mgs = a.m_group;
+    if (mode == MODE_ROW) {
       // one group per row spanning the block: keep w - floor(p * w)
-      SG_SWEEP(MODE_ROW, 0, w - (int)floor(a.sparsity * (double)w), w);
-    } else {
-      SG_SWEEP(MODE_FORCED, 0, a.n_keep, a.m_group);
+      sa.nkeep = w - (int)floor(a.sparsity * (double)w);
+      sa.mgroup = w;
     }
-#undef SG_SWEEP
-    if (sg_status e = check_launch("prune sweep")) return e;
+    if (sg_status e = quant ? launch_sweep_quant(sa) : (joint ? launch_sweep_joint(sa) : launch_sweep_plain(sa)))
+      return e;
     const int64_t i2 = i1 + w;
     if (i2 < g_end) {
       // rest of the group, K = block width

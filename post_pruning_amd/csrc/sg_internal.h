@@ -59,6 +59,8 @@ struct PruneArgs {
   // unstructured selection is per segment
   int nseg;
   int64_t seg_rows[SG_MAX_SEGMENTS + 1];
+  // vector-level removal: 1 = column by column, 16 = joint per 16 columns
+  int vec;
   // joint quantization (bits == 0: pruning only)
   int bits;
   uint8_t* codes_out;

@@ -191,6 +191,17 @@ def test_shared_validation(sg, splits, nseg):
     assert st == sg.SG_ERR_INVALID_ARGUMENT, sg.sg_last_error_message()
 
 
+@pytest.mark.parametrize("vec,bs,kind,nk,mg,code", [
+    (8, 128, 0, 0, 1, 2),     # vec not 1 or 16
+    (16, 120, 0, 0, 1, 1),    # block size not a multiple of 16
+    (16, 96, 1, 2, 3, 1),     # M neither divides 16 nor is a multiple of it (caught first here)
+])
+def test_vector_validation(sg, vec, bs, kind, nk, mg, code):
+    st = _lib(sg).sg_prune_layer_vector(ctypes.c_void_p(0x3000), None, FAKE, 0, 64, 96, 96, FAKE, kind, 0.5,
+                                        nk, mg, bs, vec, None, ctypes.c_void_p(0x10000), 10 ** 9, None)
+    assert st == code, sg.sg_last_error_message()
+
+
 def test_product_path_imports_no_oracle():
     # The library binding must not import, call or read the oracle.
     src_dir = os.path.join(ROOT, "post_pruning_amd")
