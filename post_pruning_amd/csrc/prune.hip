@@ -10,18 +10,16 @@
 // of row r removes e = W[r,j] / U_jj and subtracts e * U[j, j:] from the row.
 //
 // Per column block [i1, i1 + w):
-//   select   (unstructured only) exact k-th smallest 64-bit key
-//            (bits(W^2 / U_cc^2) << 32 | r*n + c) over the whole m x w block,
-//            by a 6-pass 11/11/10-bit radix select; each pass builds an LDS
-//            histogram per workgroup, and the last workgroup to finish scans
-//            the merged histogram and fixes the next digit.
-//   sweep    16 lanes per row, lane q owning columns q, q+16, ..., q+112 of the
-//            block in registers; the owner of column j broadcasts e to its
-//            row with a DPP row_newbcast; the U block sits in LDS with its
-//            strictly lower part zero, so every lane updates every slot right
-//            of the block start without predication.  N:M groups are ranked at
-//            their first column through a small per-row LDS scratch.
-//   lazy     W[:, i2:] -= Err * U[i1:i2, i2:] on fp32 MFMA (K = w).
+//   select   (block-global unstructured only) exact k-th smallest 64-bit key
+//            (bits(W^2 / U_cc^2) << 32 | r*n + c) of each stacked matrix's
+//            m x w block: two radix passes (11-bit digits) here, finished by
+//            every sweep workgroup (sweep.h);
+//   sweep    the in-block OBS prune and compensate of sweep.h, instantiated
+//            in sweep_plain.hip, sweep_quant.hip and sweep_joint.hip; N:M and
+//            per-row groups are ranked inside it;
+//   lazy     W[:, i2:] -= Err * U[i1:i2, i2:] on fp32 MFMA, in two levels:
+//            the rest of the 512-column group after each block (K = w), the
+//            columns beyond the group after its last block (K = 512).
 #include "sweep.h"
 
 #include <math.h>
