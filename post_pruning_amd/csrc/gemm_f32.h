@@ -21,69 +21,79 @@
 
 namespace sg {
 
-constexpr int GT = kGemmTile;  // 128
+constexpr int GT = kGemmTile;  // 128 (the default tile; 64 for small contractions)
 constexpr int GBK = 32;
 constexpr int GS = GBK + 4;    // LDS row stride in floats
 constexpr int GTHREADS = 256;
-constexpr int GBUF = GT * GS;  // floats per operand buffer
+constexpr int GBUF = GT * GS;  // floats per operand buffer of a 128-row tile
 
-struct TileAcc {
-  floatx4 v[4][4];
+// T x T output tile: each of the 4 waves owns a (T/2) x (T/2) sub-tile of
+// (T/32) x (T/32) MFMA 16x16 blocks.
+template <int T>
+struct TileAccT {
+  floatx4 v[T / 32][T / 32];
 };
+using TileAcc = TileAccT<GT>;
 
-__device__ inline void tile_zero(TileAcc& a) {
+template <int T>
+__device__ inline void tile_zero(TileAccT<T>& a) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < T / 32; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a.v[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < T / 32; ++j) a.v[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Output element held by (lane, i, j, v): row / column inside the 128x128 tile.
+// Output element held by (lane, i, j, v): row / column inside the T x T tile.
+template <int T = GT>
 __device__ inline int tile_row(int wave, int lane, int i, int v) {
-  return (wave >> 1) * 64 + i * 16 + (lane >> 4) * 4 + v;
+  return (wave >> 1) * (T / 2) + i * 16 + (lane >> 4) * 4 + v;
 }
+template <int T = GT>
 __device__ inline int tile_col(int wave, int lane, int j) {
-  return (wave & 1) * 64 + j * 16 + (lane & 15);
+  return (wave & 1) * (T / 2) + j * 16 + (lane & 15);
 }
 
-// acc += P[0:128, 0:32] * Q[0:128, 0:32]^T from LDS tiles [128][GS].
-__device__ inline void tile_mma_chunk(TileAcc& acc, const float* Pl, const float* Ql, int wave,
+// acc += P[0:T, 0:32] * Q[0:T, 0:32]^T from LDS tiles [T][GS].
+template <int T>
+__device__ inline void tile_mma_chunk(TileAccT<T>& acc, const float* Pl, const float* Ql, int wave,
                                       int lane) {
-  const int prow = (wave >> 1) * 64 + (lane & 15);
-  const int qrow = (wave & 1) * 64 + (lane & 15);
+  constexpr int NI = T / 32;
+  const int prow = (wave >> 1) * (T / 2) + (lane & 15);
+  const int qrow = (wave & 1) * (T / 2) + (lane & 15);
 #pragma unroll
   for (int g = 0; g < GBK / 16; ++g) {
     const int k = g * 16 + (lane >> 4) * 4;
-    floatx4 p[4], q[4];
+    floatx4 p[NI], q[NI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = *reinterpret_cast<const floatx4*>(Pl + (prow + i * 16) * GS + k);
+    for (int i = 0; i < NI; ++i) p[i] = *reinterpret_cast<const floatx4*>(Pl + (prow + i * 16) * GS + k);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) q[j] = *reinterpret_cast<const floatx4*>(Ql + (qrow + j * 16) * GS + k);
+    for (int j = 0; j < NI; ++j) q[j] = *reinterpret_cast<const floatx4*>(Ql + (qrow + j * 16) * GS + k);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NI; ++j)
           acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[i][e], q[j][e], acc.v[i][j], 0, 0, 0);
   }
 }
 
 // Rows of a k-contiguous fp32 matrix: element (r, k) = scale * src[r*ld + k],
 // valid for r < rows, k < kend (rows >= 1, kend >= 1).
-struct RowsF32 {
+template <int T>
+struct RowsF32T {
   const float* src;
   int64_t ld;
   int rows;
   int64_t kend;
   float scale;
-  float v[GT / 8];
+  float v[T / 8];
   __device__ inline void load(int64_t k0) {
     const int kk = threadIdx.x & 31, r0 = threadIdx.x >> 5;
     const int64_t k = k0 + kk;
     const int64_t kc = k < kend ? k : kend - 1;
 #pragma unroll
-    for (int rr = 0; rr < GT / 8; ++rr) {
+    for (int rr = 0; rr < T / 8; ++rr) {
       const int r = r0 + rr * 8;
       const int rc = r < rows ? r : rows - 1;
       v[rr] = src[(int64_t)rc * ld + kc];
@@ -93,57 +103,31 @@ struct RowsF32 {
     const int kk = threadIdx.x & 31, r0 = threadIdx.x >> 5;
     const bool kok = k0 + kk < kend;
 #pragma unroll
-    for (int rr = 0; rr < GT / 8; ++rr) {
+    for (int rr = 0; rr < T / 8; ++rr) {
       const int r = r0 + rr * 8;
       lds[r * GS + kk] = (r < rows && kok) ? v[rr] * scale : 0.f;
     }
   }
 };
-
-// A row-major [k][j] fp32 matrix read transposed: element (j, k) = src[k*ld + j],
-// valid for j < cols, k < kend (cols >= 1, kend >= 1).
-struct ColsF32 {
-  const float* src;
-  int64_t ld;
-  int cols;
-  int64_t kend;
-  float v[16];
-  __device__ inline void load(int64_t k0) {
-    const int j = threadIdx.x & 127, kh = threadIdx.x >> 7;
-    const int jc = j < cols ? j : cols - 1;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int64_t k = k0 + kh * 16 + u;
-      const int64_t kc = k < kend ? k : kend - 1;
-      v[u] = src[kc * ld + jc];
-    }
-  }
-  __device__ inline void store(float* lds, int64_t k0) {
-    const int j = threadIdx.x & 127, kh = threadIdx.x >> 7;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int kk = kh * 16 + u;
-      lds[j * GS + kk] = (j < cols && k0 + kk < kend) ? v[u] : 0.f;
-    }
-  }
-};
+using RowsF32 = RowsF32T<GT>;
 
 // Rows of a k-contiguous fp32 matrix with 16-byte aligned rows (ld % 4 == 0,
-// aligned base): four 16-byte loads per thread per chunk (8 threads per row,
+// aligned base): T/32 16-byte loads per thread per chunk (8 threads per row,
 // rows r0, r0 + 32, ...), written to LDS with 16-byte stores.  Element (r, k)
 // = src[r*ld + k], valid for r < rows, k < kend (kend % 4 == 0).
-struct RowsF32V {
+template <int T>
+struct RowsF32VT {
   const float* src;
   int64_t ld;
   int rows;
   int64_t kend;
-  floatx4 v[4];
+  floatx4 v[T / 32];
   __device__ inline void load(int64_t k0) {
     const int k4 = (threadIdx.x & 7) * 4, r0 = threadIdx.x >> 3;
     const int64_t k = k0 + k4;
     const int64_t kc = k < kend ? k : kend - 4;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < T / 32; ++u) {
       const int r = r0 + 32 * u;
       const int rc = r < rows ? r : rows - 1;
       v[u] = *reinterpret_cast<const floatx4*>(src + (int64_t)rc * ld + kc);
@@ -153,115 +137,124 @@ struct RowsF32V {
     const int k4 = (threadIdx.x & 7) * 4, r0 = threadIdx.x >> 3;
     const bool kok = k0 + k4 < kend;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < T / 32; ++u) {
       const int r = r0 + 32 * u;
       *reinterpret_cast<floatx4*>(&lds[r * GS + k4]) =
           (r < rows && kok) ? v[u] : floatx4{0.f, 0.f, 0.f, 0.f};
     }
   }
 };
+using RowsF32V = RowsF32VT<GT>;
 
-// Row-major [k][j] fp32 read transposed with 16-byte aligned rows (ld % 4 ==
-// 0, aligned base, cols % 4 == 0): thread t loads columns 4*(t%32) .. +3 of
-// rows k = t/32 + 8u (u < 4) with four 16-byte loads; element (j, k) =
-// src[k*ld + j], valid for j < cols, k < kend.
-struct ColsF32V {
+// Row-major [k][j] fp32 read transposed (any alignment): thread t owns column
+// j = t % T and KT = 32 T / 256 consecutive k of the chunk.  Its loads are
+// 4-byte but coalesced across the wave (consecutive j); it writes its k-values
+// to LDS with 16-byte stores into row j, which with the 144-byte row stride
+// land in distinct bank groups for every 16 consecutive lanes.
+// Element (j, k) = src[k*ld + j], valid for j < cols, k < kend.
+template <int T>
+struct ColsF32TT {
+  static constexpr int KT = GBK * T / GTHREADS;  // 16 (T = 128) or 8 (T = 64)
   const float* src;
   int64_t ld;
   int cols;
   int64_t kend;
-  floatx4 v[4];
+  float v[KT];
   __device__ inline void load(int64_t k0) {
-    const int j4 = (threadIdx.x & 31) * 4, kh = threadIdx.x >> 5;
-    const int jc = j4 < cols ? j4 : cols - 4;
+    const int j = threadIdx.x % T, kb = (threadIdx.x / T) * KT;
+    const int jc = j < cols ? j : cols - 1;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t k = k0 + kh + 8 * u;
+    for (int u = 0; u < KT; ++u) {
+      const int64_t k = k0 + kb + u;
       const int64_t kc = k < kend ? k : kend - 1;
-      v[u] = *reinterpret_cast<const floatx4*>(src + kc * ld + jc);
+      v[u] = src[kc * ld + jc];
     }
   }
   __device__ inline void store(float* lds, int64_t k0) {
-    const int j4 = (threadIdx.x & 31) * 4, kh = threadIdx.x >> 5;
+    const int j = threadIdx.x % T, kb = (threadIdx.x / T) * KT;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int kk = kh + 8 * u;
-      const bool ok = j4 < cols && k0 + kk < kend;
+    for (int q = 0; q < KT / 4; ++q) {
+      floatx4 t;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) lds[(j4 + e) * GS + kk] = ok ? v[u][e] : 0.f;
+      for (int e = 0; e < 4; ++e) t[e] = (j < cols && k0 + kb + 4 * q + e < kend) ? v[4 * q + e] : 0.f;
+      *reinterpret_cast<floatx4*>(&lds[j * GS + kb + 4 * q]) = t;
     }
   }
 };
+using ColsF32T = ColsF32TT<GT>;
 
 // acc += P * Q^T over k in [0, K): P and Q loaders with the load/store
-// interface above; lds holds 4 * GBUF floats (two buffers per operand).
-template <class PL, class QL>
-__device__ inline void tile_gemm_pipelined(TileAcc& acc, PL& pl, QL& ql, int64_t K, float* lds) {
+// interface above; lds holds 4 * T * GS floats (two buffers per operand).
+template <int T, class PL, class QL>
+__device__ inline void tile_gemm_pipelined(TileAccT<T>& acc, PL& pl, QL& ql, int64_t K, float* lds) {
+  constexpr int BUF = T * GS;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t nch = ceil_div(K, GBK);
   if (nch <= 0) return;
   pl.load(0);
   ql.load(0);
   pl.store(lds, 0);
-  ql.store(lds + GBUF, 0);
+  ql.store(lds + BUF, 0);
   __syncthreads();
   for (int64_t c = 0; c < nch; ++c) {
-    float* cur = lds + (c & 1) * 2 * GBUF;
-    float* nxt = lds + ((c + 1) & 1) * 2 * GBUF;
+    float* cur = lds + (c & 1) * 2 * BUF;
+    float* nxt = lds + ((c + 1) & 1) * 2 * BUF;
     const bool more = c + 1 < nch;
     if (more) {
       pl.load((c + 1) * GBK);
       ql.load((c + 1) * GBK);
     }
-    tile_mma_chunk(acc, cur, cur + GBUF, wave, lane);
+    tile_mma_chunk(acc, cur, cur + BUF, wave, lane);
     if (more) {
       pl.store(nxt, (c + 1) * GBK);
-      ql.store(nxt + GBUF, (c + 1) * GBK);
+      ql.store(nxt + BUF, (c + 1) * GBK);
     }
     __syncthreads();
   }
 }
 
 // C[0:rows, 0:cols] -= acc (C row-major with leading dimension ldc), staged
-// through LDS (which must hold GT * (GT + 4) floats and be free) so that the
-// read-modify-write of C is done with float4 accesses, 32 lanes per row.
+// through LDS (which must hold T * (T + 4) floats and be free) so that the
+// read-modify-write of C is done with float4 accesses, T/4 lanes per row.
+template <int T>
 __device__ inline void tile_sub_from(float* __restrict__ C, int64_t ldc, int rows, int cols,
-                                     const TileAcc& acc, float* lds) {
-  constexpr int TS = GT + 4;
+                                     const TileAccT<T>& acc, float* lds) {
+  constexpr int TS = T + 4;
+  constexpr int RPP = GTHREADS / (T / 4);  // rows per pass
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < T / 32; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
+    for (int jj = 0; jj < T / 32; ++jj)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        lds[tile_row(wave, lane, i, v) * TS + tile_col(wave, lane, jj)] = acc.v[i][jj][v];
+        lds[tile_row<T>(wave, lane, i, v) * TS + tile_col<T>(wave, lane, jj)] = acc.v[i][jj][v];
   __syncthreads();
-  const int c4 = (threadIdx.x & 31) * 4;
-  const int r0 = threadIdx.x >> 5;
-  const bool vec = (cols == GT) && ((ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
+  const int c4 = (threadIdx.x % (T / 4)) * 4;
+  const int r0 = threadIdx.x / (T / 4);
+  const bool vec = (cols == T) && ((ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
   if (vec) {
     // all loads first (C may alias nothing else, but the compiler cannot know
     // that a store does not feed a later load), then subtract and store
-    floatx4 cv[GT / 8];
+    floatx4 cv[T / RPP];
 #pragma unroll
-    for (int rr = 0; rr < GT / 8; ++rr) {
-      const int r = r0 + rr * 8;
+    for (int rr = 0; rr < T / RPP; ++rr) {
+      const int r = r0 + rr * RPP;
       const int rc = r < rows ? r : rows - 1;
       cv[rr] = *reinterpret_cast<const floatx4*>(C + (int64_t)rc * ldc + c4);
     }
 #pragma unroll
-    for (int rr = 0; rr < GT / 8; ++rr) {
-      const int r = r0 + rr * 8;
+    for (int rr = 0; rr < T / RPP; ++rr) {
+      const int r = r0 + rr * RPP;
       if (r < rows) {
         const floatx4 t = *reinterpret_cast<const floatx4*>(&lds[r * TS + c4]);
         *reinterpret_cast<floatx4*>(C + (int64_t)r * ldc + c4) = cv[rr] - t;
       }
     }
   } else {
-    for (int rr = 0; rr < GT / 8; ++rr) {
-      const int r = r0 + rr * 8;
+    for (int rr = 0; rr < T / RPP; ++rr) {
+      const int r = r0 + rr * RPP;
       if (r >= rows) break;
       const floatx4 t = *reinterpret_cast<const floatx4*>(&lds[r * TS + c4]);
       float* crow = C + (int64_t)r * ldc;

@@ -162,27 +162,49 @@ __global__ __launch_bounds__(256) void qgrid_kernel(const float* __restrict__ W,
 // its errors update the rest of the current group of columns (K = block
 // width); after the last block of a group, the errors of the whole group
 // update every column beyond it at once (K = group width).
-template <bool VEC>
+template <bool VEC, int T>
 __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ W, const float* __restrict__ E,
                                                    const float* __restrict__ U, int64_t m, int64_t n,
                                                    int64_t k0, int K, int64_t c_begin, int64_t c_end) {
-  __shared__ __attribute__((aligned(16))) float lds[4 * GBUF];
-  const int64_t r0 = (int64_t)blockIdx.y * GT;
-  const int64_t c0 = c_begin + (int64_t)blockIdx.x * GT;
-  const int rows = (int)min<int64_t>(GT, m - r0);
-  const int cols = (int)min<int64_t>(GT, c_end - c0);
-  TileAcc acc;
+  __shared__ __attribute__((aligned(16))) float lds[4 * T * GS];
+  const int64_t r0 = (int64_t)blockIdx.y * T;
+  const int64_t c0 = c_begin + (int64_t)blockIdx.x * T;
+  const int rows = (int)min<int64_t>(T, m - r0);
+  const int cols = (int)min<int64_t>(T, c_end - c0);
+  TileAccT<T> acc;
   tile_zero(acc);
   if constexpr (VEC) {
-    RowsF32V pl{E + r0 * EGK, EGK, rows, K};
-    ColsF32V ql{U + k0 * n + c0, n, cols, K};
+    RowsF32VT<T> pl{E + r0 * EGK, EGK, rows, K};
+    ColsF32TT<T> ql{U + k0 * n + c0, n, cols, K};
     tile_gemm_pipelined(acc, pl, ql, K, lds);
   } else {
-    RowsF32 pl{E + r0 * EGK, EGK, rows, K, 1.f};
-    ColsF32 ql{U + k0 * n + c0, n, cols, K};
+    RowsF32T<T> pl{E + r0 * EGK, EGK, rows, K, 1.f};
+    ColsF32TT<T> ql{U + k0 * n + c0, n, cols, K};
     tile_gemm_pipelined(acc, pl, ql, K, lds);
   }
   tile_sub_from(W + r0 * n + c0, n, rows, cols, acc, lds);
+}
+
+// W[:, c_begin:c_end] -= E[:, 0:K] * U[k0:k0+K, c_begin:c_end] with the tile
+// that fills the GPU: 128 x 128 when that grid covers a full round of
+// workgroups (two per CU), else 64 x 64 (four times the workgroups).
+sg_status launch_lazy(float* W, const float* E, const float* U, int64_t m, int64_t n, int64_t k0, int K,
+                      int64_t c_begin, int64_t c_end, bool vec, hipStream_t st) {
+  const int64_t t128 = ceil_div(c_end - c_begin, 128) * ceil_div(m, 128);
+  if (t128 >= 2 * kNumCU) {
+    const dim3 grid((unsigned)ceil_div(c_end - c_begin, 128), (unsigned)ceil_div(m, 128));
+    if (vec)
+      hipLaunchKernelGGL((lazy_kernel<true, 128>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end);
+    else
+      hipLaunchKernelGGL((lazy_kernel<false, 128>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end);
+  } else {
+    const dim3 grid((unsigned)ceil_div(c_end - c_begin, 64), (unsigned)ceil_div(m, 64));
+    if (vec)
+      hipLaunchKernelGGL((lazy_kernel<true, 64>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end);
+    else
+      hipLaunchKernelGGL((lazy_kernel<false, 64>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end);
+  }
+  return check_launch("prune lazy");
 }
 
 }  // namespace
@@ -310,24 +332,13 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
     const int64_t i2 = i1 + w;
     if (i2 < g_end) {
       // rest of the group, K = block width
-      dim3 grid((unsigned)ceil_div(g_end - i2, GT), (unsigned)ceil_div(m, GT));
-      if (lazy_vec(Eb, a.U, n, i2, g_end, w))
-        hipLaunchKernelGGL(lazy_kernel<true>, grid, dim3(256), 0, st, a.W_out, Eb, a.U, m, n, i1, w, i2,
-                           g_end);
-      else
-        hipLaunchKernelGGL(lazy_kernel<false>, grid, dim3(256), 0, st, a.W_out, Eb, a.U, m, n, i1, w, i2,
-                           g_end);
-      if (sg_status e = check_launch("prune lazy (group)")) return e;
+      if (sg_status e = launch_lazy(a.W_out, Eb, a.U, m, n, i1, w, i2, g_end, lazy_vec(Eb, a.U, n, i2, g_end, w), st))
+        return e;
     } else if (g_end < n) {
       // last block of the group: every column beyond it, K = group width
-      dim3 grid((unsigned)ceil_div(n - g_end, GT), (unsigned)ceil_div(m, GT));
-      if (lazy_vec(Err, a.U, n, g_end, n, (int)(g_end - g0)))
-        hipLaunchKernelGGL(lazy_kernel<true>, grid, dim3(256), 0, st, a.W_out, Err, a.U, m, n, g0,
-                           (int)(g_end - g0), g_end, n);
-      else
-        hipLaunchKernelGGL(lazy_kernel<false>, grid, dim3(256), 0, st, a.W_out, Err, a.U, m, n, g0,
-                           (int)(g_end - g0), g_end, n);
-      if (sg_status e = check_launch("prune lazy (trailing)")) return e;
+      if (sg_status e = launch_lazy(a.W_out, Err, a.U, m, n, g0, (int)(g_end - g0), g_end, n,
+                                    lazy_vec(Err, a.U, n, g_end, n, (int)(g_end - g0)), st))
+        return e;
     }
   }
   return SG_OK;

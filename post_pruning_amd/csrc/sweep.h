@@ -72,7 +72,7 @@ __device__ inline void sel_clear_set(SelSet& s, int tid, int nthreads) {
 //           off the one of the remaining rank.
 // No workgroup waits for another: each kernel consumes what the previous one
 // completed.
-constexpr int SEL_KPT = 32;    // keys per thread
+constexpr int SEL_KPT = 16;    // keys per thread
 constexpr int SEL_SUB = 8;     // LDS sub-histograms
 constexpr int SEL_SORT = 8192; // keys sorted in LDS
 
