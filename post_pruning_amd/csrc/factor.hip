@@ -414,10 +414,37 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
   panel_body(*reinterpret_cast<PanelLds*>(smem), A, Y, n_pad, k, n, info, blockIdx.x);
 }
 
-__global__ __launch_bounds__(256) void update_kernel(float* __restrict__ A, float* __restrict__ Y,
-                                                     int64_t n_pad, int k, int nblk, int mode) {
-  __shared__ __attribute__((aligned(16))) float lds[4 * GBUF];
-  update_body(lds, A, Y, n_pad, k, nblk, mode, blockIdx.x);
+// Block column k+1 of panel k's update (what panel k+1 reads first) in 64x64
+// quarters of the 128x128 tiles: four times the workgroups of the tile grid,
+// which is only t + k + 1 tiles, for a short latency-bound launch.
+__global__ __launch_bounds__(256) void col_update_kernel(float* __restrict__ A, float* __restrict__ Y,
+                                                         int64_t n_pad, int k, int nblk) {
+  __shared__ __attribute__((aligned(16))) float lds[4 * 64 * GS];
+  const int64_t t = nblk - k - 1;
+  int64_t idx = blockIdx.x >> 2;
+  const int qr = (blockIdx.x >> 1) & 1, qc = blockIdx.x & 1;
+  float* C;
+  const float *P, *Q;
+  if (idx < t) {
+    // SYRK tile (k+1+idx, k+1); its quarter above the diagonal is not needed
+    if (idx == 0 && qr < qc) return;
+    const int64_t lb = k + 1 + idx, mb = k + 1;
+    C = A + lb * NB * n_pad + mb * NB;
+    P = A + lb * NB * n_pad + (int64_t)k * NB;
+    Q = A + mb * NB * n_pad + (int64_t)k * NB;
+  } else {
+    // inverse tile (c, k+1)
+    const int64_t c = idx - t, lb = k + 1;
+    C = Y + c * NB * n_pad + lb * NB;
+    P = Y + c * NB * n_pad + (int64_t)k * NB;
+    Q = A + lb * NB * n_pad + (int64_t)k * NB;
+  }
+  RowsF32VT<64> pl{P + (int64_t)qr * 64 * n_pad, n_pad, 64, NB};
+  RowsF32VT<64> ql{Q + (int64_t)qc * 64 * n_pad, n_pad, 64, NB};
+  TileAccT<64> acc;
+  tile_zero(acc);
+  tile_gemm_pipelined(acc, pl, ql, NB, lds);
+  tile_sub_from(C + (int64_t)qr * 64 * n_pad + qc * 64, n_pad, 64, 64, acc, lds);
 }
 
 // Look-ahead step: workgroups [0, nblk) factor panel k+1 and transform its
@@ -498,8 +525,8 @@ sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double dam
                      info);
   if (sg_status e = check_launch("factor panel")) return e;
   for (int k = 0; k + 1 < nblk; ++k) {
-    hipLaunchKernelGGL(update_kernel, dim3((unsigned)update_tiles(k, nblk, UPD_COL)), dim3(256), 0, st,
-                       A, Y, n_pad, k, nblk, (int)UPD_COL);
+    hipLaunchKernelGGL(col_update_kernel, dim3((unsigned)(4 * update_tiles(k, nblk, UPD_COL))), dim3(256), 0,
+                       st, A, Y, n_pad, k, nblk);
     if (sg_status e = check_launch("factor update (next column)")) return e;
     const int64_t rest = update_tiles(k, nblk, UPD_REST);
     hipLaunchKernelGGL(panel_rest_kernel, dim3((unsigned)(nblk + rest)), dim3(256), sizeof(PanelLds),
