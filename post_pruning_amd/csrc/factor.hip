@@ -349,7 +349,8 @@ __device__ inline int64_t isqrt_floor(int64_t x) {
 
 // Trailing-update tiles of panel k (K = 128 each), in three subsets:
 //   UPD_ALL   every tile;
-//   UPD_COL   the tiles of block column k+1 only (what panel k+1 needs);
+//   UPD_COL   the tiles of block column k+1 only (what panel k+1 needs; run
+//             by col_update_kernel in 64x64 quarters);
 //   UPD_REST  every other tile (run while panel k+1 factors).
 enum { UPD_ALL = 0, UPD_COL = 1, UPD_REST = 2 };
 
@@ -363,39 +364,26 @@ __host__ __device__ inline int64_t update_tiles(int k, int nblk, int mode) {
 
 __device__ __forceinline__ void update_body(float* lds, float* __restrict__ A, float* __restrict__ Y,
                                             int64_t n_pad, int k, int nblk, int mode, int64_t idx) {
-  const int64_t t = nblk - k - 1;
-  // SYRK tiles: lower triangle over trailing blocks [s0, nblk); inverse
-  // tiles: rows c <= k, block columns [s0, nblk)
+  // UPD_ALL or UPD_REST.  SYRK tiles: lower triangle over trailing blocks
+  // [s0, nblk); inverse tiles: rows c <= k, block columns [s0, nblk)
   const int64_t s0 = mode == UPD_REST ? k + 2 : k + 1;
   const int64_t ts = nblk - s0;
-  const int64_t nsyrk = mode == UPD_COL ? t : ts * (ts + 1) / 2;
+  const int64_t nsyrk = ts * (ts + 1) / 2;
   float* C;
   const float *P, *Q;
   if (idx < nsyrk) {
-    int64_t l, m;
-    if (mode == UPD_COL) {
-      l = idx;
-      m = 0;
-    } else {
-      l = (isqrt_floor(8 * idx + 1) - 1) / 2;
-      while ((l + 1) * (l + 2) / 2 <= idx) ++l;
-      while (l * (l + 1) / 2 > idx) --l;
-      m = idx - l * (l + 1) / 2;
-    }
+    int64_t l = (isqrt_floor(8 * idx + 1) - 1) / 2;
+    while ((l + 1) * (l + 2) / 2 <= idx) ++l;
+    while (l * (l + 1) / 2 > idx) --l;
+    const int64_t m = idx - l * (l + 1) / 2;
     const int64_t lb = s0 + l, mb = s0 + m;
     C = A + lb * NB * n_pad + mb * NB;
     P = A + lb * NB * n_pad + (int64_t)k * NB;
     Q = A + mb * NB * n_pad + (int64_t)k * NB;
   } else {
     idx -= nsyrk;
-    int64_t c, lb;
-    if (mode == UPD_COL) {
-      c = idx;
-      lb = k + 1;
-    } else {
-      c = idx % (k + 1);
-      lb = s0 + idx / (k + 1);
-    }
+    const int64_t c = idx % (k + 1);
+    const int64_t lb = s0 + idx / (k + 1);
     C = Y + c * NB * n_pad + lb * NB;
     P = Y + c * NB * n_pad + (int64_t)k * NB;
     Q = A + lb * NB * n_pad + (int64_t)k * NB;

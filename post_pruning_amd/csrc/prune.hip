@@ -209,11 +209,10 @@ sg_status launch_lazy(float* W, const float* E, const float* U, int64_t m, int64
 
 }  // namespace
 
-// 16-byte loaders apply when every row segment they read is 16-byte aligned
-// and the K and column extents are multiples of 4.
-bool lazy_vec(const float* E, const float* U, int64_t n, int64_t c_begin, int64_t c_end, int K) {
-  return (reinterpret_cast<uintptr_t>(E) % 16) == 0 && (reinterpret_cast<uintptr_t>(U) % 16) == 0 &&
-         (n % 4) == 0 && (c_begin % 4) == 0 && ((c_end - c_begin) % 4) == 0 && (K % 4) == 0;
+// The 16-byte row loader of E applies when E's rows are 16-byte aligned and
+// the K extent is a multiple of 4 (U is read by the 4-byte transposed loader).
+bool lazy_vec(const float* E, int K) {
+  return (reinterpret_cast<uintptr_t>(E) % 16) == 0 && (K % 4) == 0;
 }
 
 size_t prune_ws_bytes(int64_t m, int64_t n, int blocksize) {
@@ -332,12 +331,12 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
     const int64_t i2 = i1 + w;
     if (i2 < g_end) {
       // rest of the group, K = block width
-      if (sg_status e = launch_lazy(a.W_out, Eb, a.U, m, n, i1, w, i2, g_end, lazy_vec(Eb, a.U, n, i2, g_end, w), st))
+      if (sg_status e = launch_lazy(a.W_out, Eb, a.U, m, n, i1, w, i2, g_end, lazy_vec(Eb, w), st))
         return e;
     } else if (g_end < n) {
       // last block of the group: every column beyond it, K = group width
       if (sg_status e = launch_lazy(a.W_out, Err, a.U, m, n, g0, (int)(g_end - g0), g_end, n,
-                                    lazy_vec(Err, a.U, n, g_end, n, (int)(g_end - g0)), st))
+                                    lazy_vec(Err, (int)(g_end - g0)), st))
         return e;
     }
   }

@@ -233,6 +233,10 @@ __device__ inline unsigned long long select_finish(const SelSet& ss, const unsig
 // This is the same computation as the column-by-column OBS sweep, with the
 // updates of later chunks batched (they only add into columns not yet
 // reached).  The U block (upper triangle, zero elsewhere) sits in LDS.
+// Template variants of one kernel: MODE (block-global threshold, N:M,
+// per-row, forced mask), MGS (N:M groups of up to 16 columns, ranked inside
+// the column steps), QUANT (kept weights rounded to their row's grid at their
+// step) and JOINT (each 16-column chunk's chosen weights removed together).
 constexpr int SWS = SB + 4;  // LDS row stride of the U block (floats)
 constexpr int ESS = 20;      // per-wave E tile row stride (floats)
 
