@@ -1,0 +1,190 @@
+// fp32-accurate tile core on bf16 MFMA for the dense contractions of the
+// solver (the lazy trailing update and the factorisation's trailing updates).
+//
+// Every fp32 operand value x is split exactly into three bf16 parts,
+//   h = bf16(x), m = bf16(x - h), l = bf16(x - h - m),   x = h + m + l
+// (round to nearest even at each step; 3 x 8 significand bits hold the 24 of
+// fp32).  A product x*y is formed from the six terms that reach the fp32
+// rounding level, hh + hm + mh + hl + lh + mm (the dropped ml, lm, ll are
+// below 2^-24 relative), each exact in the fp32 accumulator of
+// v_mfma_f32_16x16x32_bf16.  Six bf16 MFMAs of K = 32 replace eight fp32
+// MFMAs of K = 4, at twice the rate each: 2.7x the fp32 MFMA throughput.
+//
+// Layout as in gemm_f32.h (one 256-thread workgroup per T x T output tile,
+// 4 waves in a 2 x 2 grid of (T/2) x (T/2) sub-tiles, 32 k-values per chunk,
+// the MFMA result layout is the same), except that each operand is staged as
+// three bf16 planes [3][T][XS] with k contiguous: a 16-byte LDS read gives a
+// lane its 8 consecutive k-values of one row, which is the bf16 MFMA operand.
+// The split happens when a chunk goes from registers to LDS.  One LDS buffer
+// (so that two workgroups fit on a CU): the next chunk's global loads are in
+// flight while the current chunk is multiplied, then written after a barrier.
+#pragma once
+
+#include "gemm_f32.h"
+
+namespace sg {
+
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+constexpr int XS = GBK + 8;  // LDS row stride in bf16 (80 bytes: conflict-free 16-byte reads)
+
+template <int T>
+struct X6Lds {
+  static constexpr int PLANE = T * XS;                 // bf16 per plane
+  static constexpr int OPER = 3 * PLANE;               // bf16 per operand
+  static constexpr int BYTES = 2 * OPER * 2;           // both operands
+  static constexpr int EPI = T * (T + 4) * 4;          // epilogue staging (fp32)
+  static constexpr int SIZE = BYTES > EPI ? BYTES : EPI;
+};
+
+// x -> (h, m, l), four values at a time
+__device__ inline void split3(const floatx4& x, bf16x4v& h, bf16x4v& m, bf16x4v& l) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 hb = (__bf16)x[e];
+    const float r1 = x[e] - (float)hb;
+    const __bf16 mb = (__bf16)r1;
+    const float r2 = r1 - (float)mb;
+    h[e] = hb;
+    m[e] = mb;
+    l[e] = (__bf16)r2;
+  }
+}
+
+// Rows of a k-contiguous fp32 matrix with 16-byte aligned rows (as
+// RowsF32VT): element (r, k) = src[r*ld + k], valid for r < rows, k < kend
+// (kend % 4 == 0); stored split into the three planes.
+template <int T>
+struct RowsX6V {
+  const float* src;
+  int64_t ld;
+  int rows;
+  int64_t kend;
+  floatx4 v[T / 32];
+  __device__ inline void load(int64_t k0) {
+    const int k4 = (threadIdx.x & 7) * 4, r0 = threadIdx.x >> 3;
+    const int64_t k = k0 + k4;
+    const int64_t kc = k < kend ? k : kend - 4;
+#pragma unroll
+    for (int u = 0; u < T / 32; ++u) {
+      const int r = r0 + 32 * u;
+      const int rc = r < rows ? r : rows - 1;
+      v[u] = *reinterpret_cast<const floatx4*>(src + (int64_t)rc * ld + kc);
+    }
+  }
+  __device__ inline void store(__bf16* lds, int64_t k0) {
+    const int k4 = (threadIdx.x & 7) * 4, r0 = threadIdx.x >> 3;
+    const bool kok = k0 + k4 < kend;
+#pragma unroll
+    for (int u = 0; u < T / 32; ++u) {
+      const int r = r0 + 32 * u;
+      const floatx4 x = (r < rows && kok) ? v[u] : floatx4{0.f, 0.f, 0.f, 0.f};
+      bf16x4v h, m, l;
+      split3(x, h, m, l);
+      *reinterpret_cast<bf16x4v*>(lds + 0 * X6Lds<T>::PLANE + r * XS + k4) = h;
+      *reinterpret_cast<bf16x4v*>(lds + 1 * X6Lds<T>::PLANE + r * XS + k4) = m;
+      *reinterpret_cast<bf16x4v*>(lds + 2 * X6Lds<T>::PLANE + r * XS + k4) = l;
+    }
+  }
+};
+
+// Row-major [k][j] fp32 read transposed (as ColsF32TT): thread t owns column
+// j = t % T and KT = 32 T / 256 consecutive k; element (j, k) = src[k*ld + j],
+// valid for j < cols, k < kend; stored split into the three planes.
+template <int T>
+struct ColsX6T {
+  static constexpr int KT = GBK * T / GTHREADS;  // 16 (T = 128) or 8 (T = 64)
+  const float* src;
+  int64_t ld;
+  int cols;
+  int64_t kend;
+  float v[KT];
+  __device__ inline void load(int64_t k0) {
+    const int j = threadIdx.x % T, kb = (threadIdx.x / T) * KT;
+    const int jc = j < cols ? j : cols - 1;
+#pragma unroll
+    for (int u = 0; u < KT; ++u) {
+      const int64_t k = k0 + kb + u;
+      const int64_t kc = k < kend ? k : kend - 1;
+      v[u] = src[kc * ld + jc];
+    }
+  }
+  __device__ inline void store(__bf16* lds, int64_t k0) {
+    const int j = threadIdx.x % T, kb = (threadIdx.x / T) * KT;
+#pragma unroll
+    for (int q = 0; q < KT / 4; ++q) {
+      floatx4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (j < cols && k0 + kb + 4 * q + e < kend) ? v[4 * q + e] : 0.f;
+      bf16x4v h, m, l;
+      split3(x, h, m, l);
+      *reinterpret_cast<bf16x4v*>(lds + 0 * X6Lds<T>::PLANE + j * XS + kb + 4 * q) = h;
+      *reinterpret_cast<bf16x4v*>(lds + 1 * X6Lds<T>::PLANE + j * XS + kb + 4 * q) = m;
+      *reinterpret_cast<bf16x4v*>(lds + 2 * X6Lds<T>::PLANE + j * XS + kb + 4 * q) = l;
+    }
+  }
+};
+
+// acc += P[0:T, 0:32] * Q[0:T, 0:32]^T from the split planes in LDS.
+template <int T>
+__device__ inline void tile_mma_x6(TileAccT<T>& acc, const __bf16* Pl, const __bf16* Ql, int wave, int lane) {
+  constexpr int NI = T / 32;
+  constexpr int PL = X6Lds<T>::PLANE;
+  const int prow = (wave >> 1) * (T / 2) + (lane & 15);
+  const int qrow = (wave & 1) * (T / 2) + (lane & 15);
+  const int k = (lane >> 4) * 8;
+  bf16x8v p[NI][3], q[NI][3];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      p[i][s] = *reinterpret_cast<const bf16x8v*>(Pl + s * PL + (prow + i * 16) * XS + k);
+      q[i][s] = *reinterpret_cast<const bf16x8v*>(Ql + s * PL + (qrow + i * 16) * XS + k);
+    }
+  // smallest terms first
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      floatx4 a = acc.v[i][j];
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[i][1], q[j][1], a, 0, 0, 0);  // mm
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[i][0], q[j][2], a, 0, 0, 0);  // hl
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[i][2], q[j][0], a, 0, 0, 0);  // lh
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[i][0], q[j][1], a, 0, 0, 0);  // hm
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[i][1], q[j][0], a, 0, 0, 0);  // mh
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[i][0], q[j][0], a, 0, 0, 0);  // hh
+      acc.v[i][j] = a;
+    }
+}
+
+// acc += P * Q^T over k in [0, K); lds holds X6Lds<T>::SIZE bytes.
+template <int T, class PL, class QL>
+__device__ inline void tile_gemm_x6(TileAccT<T>& acc, PL& pl, QL& ql, int64_t K, void* lds) {
+  __bf16* Pl = static_cast<__bf16*>(lds);
+  __bf16* Ql = Pl + X6Lds<T>::OPER;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t nch = ceil_div(K, GBK);
+  if (nch <= 0) return;
+  pl.load(0);
+  ql.load(0);
+  pl.store(Pl, 0);
+  ql.store(Ql, 0);
+  __syncthreads();
+  for (int64_t c = 0; c < nch; ++c) {
+    const bool more = c + 1 < nch;
+    if (more) {
+      pl.load((c + 1) * GBK);
+      ql.load((c + 1) * GBK);
+    }
+    tile_mma_x6(acc, Pl, Ql, wave, lane);
+    if (more) {
+      __syncthreads();
+      pl.store(Pl, (c + 1) * GBK);
+      ql.store(Ql, (c + 1) * GBK);
+      __syncthreads();
+    }
+  }
+}
+
+}  // namespace sg

@@ -20,6 +20,7 @@
 //   lazy     W[:, i2:] -= Err * U[i1:i2, i2:] on fp32 MFMA, in two levels:
 //            the rest of the 512-column group after each block (K = w), the
 //            columns beyond the group after its last block (K = 512).
+#include "gemm_x6.h"
 #include "sweep.h"
 
 #include <math.h>
@@ -166,7 +167,9 @@ template <bool VEC, int T>
 __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ W, const float* __restrict__ E,
                                                    const float* __restrict__ U, int64_t m, int64_t n,
                                                    int64_t k0, int K, int64_t c_begin, int64_t c_end) {
-  __shared__ __attribute__((aligned(16))) float lds[4 * T * GS];
+  constexpr int LDSB = VEC ? X6Lds<T>::SIZE : 4 * T * GS * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char ldsb[LDSB];
+  float* lds = reinterpret_cast<float*>(ldsb);
   const int64_t r0 = (int64_t)blockIdx.y * T;
   const int64_t c0 = c_begin + (int64_t)blockIdx.x * T;
   const int rows = (int)min<int64_t>(T, m - r0);
@@ -174,9 +177,10 @@ __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ W, const 
   TileAccT<T> acc;
   tile_zero(acc);
   if constexpr (VEC) {
-    RowsF32VT<T> pl{E + r0 * EGK, EGK, rows, K};
-    ColsF32TT<T> ql{U + k0 * n + c0, n, cols, K};
-    tile_gemm_pipelined(acc, pl, ql, K, lds);
+    // fp32-accurate products on bf16 MFMA (three-way split, six terms)
+    RowsX6V<T> pl{E + r0 * EGK, EGK, rows, K};
+    ColsX6T<T> ql{U + k0 * n + c0, n, cols, K};
+    tile_gemm_x6(acc, pl, ql, K, ldsb);
   } else {
     RowsF32T<T> pl{E + r0 * EGK, EGK, rows, K, 1.f};
     ColsF32TT<T> ql{U + k0 * n + c0, n, cols, K};
