@@ -29,7 +29,7 @@
 //     R[c,l] -= Y[c,k] L[l,k]^T   for c <= k < l                      (inverse)
 // where R is the running right-hand side of L X = I, kept transposed in the
 // upper block triangle of Y (R starts as I).
-#include "gemm_f32.h"
+#include "gemm_x6.h"
 
 #include <math.h>
 
@@ -388,11 +388,12 @@ __device__ __forceinline__ void update_body(float* lds, float* __restrict__ A, f
     P = Y + c * NB * n_pad + (int64_t)k * NB;
     Q = A + lb * NB * n_pad + (int64_t)k * NB;
   }
-  RowsF32V pl{P, n_pad, NB, NB};
-  RowsF32V ql{Q, n_pad, NB, NB};
+  // fp32-accurate products on bf16 MFMA (three-way split, six terms)
+  RowsX6V<NB> pl{P, n_pad, NB, NB};
+  RowsX6V<NB> ql{Q, n_pad, NB, NB};
   TileAcc acc;
   tile_zero(acc);
-  tile_gemm_pipelined(acc, pl, ql, NB, lds);
+  tile_gemm_x6(acc, pl, ql, NB, lds);
   tile_sub_from(C, n_pad, NB, NB, acc, lds);
 }
 
@@ -407,7 +408,8 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
 // which is only t + k + 1 tiles, for a short latency-bound launch.
 __global__ __launch_bounds__(256) void col_update_kernel(float* __restrict__ A, float* __restrict__ Y,
                                                          int64_t n_pad, int k, int nblk) {
-  __shared__ __attribute__((aligned(16))) float lds[4 * 64 * GS];
+  __shared__ __attribute__((aligned(16))) unsigned char ldsb[X6Lds<64>::SIZE];
+  float* lds = reinterpret_cast<float*>(ldsb);
   const int64_t t = nblk - k - 1;
   int64_t idx = blockIdx.x >> 2;
   const int qr = (blockIdx.x >> 1) & 1, qc = blockIdx.x & 1;
@@ -427,11 +429,11 @@ __global__ __launch_bounds__(256) void col_update_kernel(float* __restrict__ A, 
     P = Y + c * NB * n_pad + (int64_t)k * NB;
     Q = A + lb * NB * n_pad + (int64_t)k * NB;
   }
-  RowsF32VT<64> pl{P + (int64_t)qr * 64 * n_pad, n_pad, 64, NB};
-  RowsF32VT<64> ql{Q + (int64_t)qc * 64 * n_pad, n_pad, 64, NB};
+  RowsX6V<64> pl{P + (int64_t)qr * 64 * n_pad, n_pad, 64, NB};
+  RowsX6V<64> ql{Q + (int64_t)qc * 64 * n_pad, n_pad, 64, NB};
   TileAccT<64> acc;
   tile_zero(acc);
-  tile_gemm_pipelined(acc, pl, ql, NB, lds);
+  tile_gemm_x6(acc, pl, ql, NB, ldsb);
   tile_sub_from(C + (int64_t)qr * 64 * n_pad + qc * 64, n_pad, 64, 64, acc, lds);
 }
 
