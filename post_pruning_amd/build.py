@@ -26,6 +26,12 @@ HIPCC_FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
 ]
 
+# Per-source options.  The column sweep keeps its block tiles in registers and
+# updates them with MFMAs between the column steps: with the MFMA operands in
+# ordinary VGPRs there are no accumulator-register copies in that loop.
+SOURCE_FLAGS = {s: ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+                for s in ("sweep_plain.hip", "sweep_quant.hip", "sweep_joint.hip")}
+
 
 def _hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -36,7 +42,7 @@ def _hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")

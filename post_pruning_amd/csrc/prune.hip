@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void select_pass_kernel(SelState* st, int pari
   const int c = tid & 127;
   const int cc = c < w ? c : w - 1;
   const int64_t col = i1 + cc;
-  const float ucc = U[col * n + col];
+  const float rd = 1.f / U[col * n + col];
   const int64_t rstep = (int64_t)gridDim.x * 2;
   const int64_t rb = rlo + (int64_t)blockIdx.x * 2 + (tid >> 7);
   float wv[SEL_KPT];
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void select_pass_kernel(SelState* st, int pari
   for (int u = 0; u < SEL_KPT; ++u) {
     const int64_t r = rb + u * rstep;
     if (r < m && c < w) {
-      const unsigned long long key = sal_key(wv[u], ucc, (uint32_t)(r * n + col));
+      const unsigned long long key = sal_key(wv[u], rd, (uint32_t)(r * n + col));
       if (pass == 0 || (unsigned)(key >> 53) == top) {
         atomicAdd(&hsub[(unsigned)(key >> shift) & dmask], 1u);
         if (pass == 1) L.stage[atomicAdd(&L.nstage, 1u)] = key;

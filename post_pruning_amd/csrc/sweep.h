@@ -41,13 +41,16 @@ struct Segs {
   int fixed[SG_MAX_SEGMENTS];
 };
 
-__device__ inline float saliency(float w, float ucc) {
-  const float q = w / ucc;
+// OBS saliency w^2 / U_cc^2 as (w * rd)^2 with rd = 1 / U_cc (the IEEE
+// quotient, formed the same way wherever a saliency is taken, so that every
+// kernel ranks the same fp32 values).
+__device__ inline float saliency(float w, float rd) {
+  const float q = w * rd;
   return q * q;
 }
 
-__device__ inline unsigned long long sal_key(float w, float ucc, uint32_t lin) {
-  return ((unsigned long long)__float_as_uint(saliency(w, ucc)) << 32) | lin;
+__device__ inline unsigned long long sal_key(float w, float rd, uint32_t lin) {
+  return ((unsigned long long)__float_as_uint(saliency(w, rd)) << 32) | lin;
 }
 
 __device__ inline void sel_clear_set(SelSet& s, int tid, int nthreads) {
@@ -384,7 +387,7 @@ __device__ __forceinline__ void rank_step(const floatx4& Wc, unsigned& Pc, const
       const bool in = me >= 0 && me < MGS;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float my = saliency(Wc[v], cx.ucc);
+        const float my = saliency(Wc[v], cx.rd);
         const int rank = group_rank<J>(std::make_integer_sequence<int, MGS>{}, my, me);
         if (in && ((rowbits >> v) & 1u) && rank < MGS - nkeep) Pc |= 1u << v;
       }
@@ -450,7 +453,7 @@ __device__ __forceinline__ void sweep_step(floatx4& Wc, unsigned& Pc, const Chun
       const bool in = me >= 0 && me < MGS;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float my = saliency(Wc[v], cx.ucc);
+        const float my = saliency(Wc[v], cx.rd);
         const int rank = group_rank<J>(std::make_integer_sequence<int, MGS>{}, my, me);
         if (in && ((rowbits >> v) & 1u) && rank < MGS - nkeep) Pc |= 1u << v;
       }
@@ -519,49 +522,29 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
     q.L = qlevels;
   }
 
-  // threshold key of the block (the LDS of the U block serves as scratch)
-  __shared__ unsigned s_cnt;
-  __shared__ HistPick s_pick;
-  unsigned long long thr = 0ull;
-  if (MODE == MODE_THRESH && sel_fixed == 0)
-    thr = select_finish(stp->set[parity], candp, ksel, reinterpret_cast<unsigned long long*>(S.Ub),
-                        &s_cnt, s_pick);
-  if (MODE == MODE_THRESH && (int)blockIdx.x == segs.wg0[seg]) sel_clear_set(stp->set[parity ^ 1], tid, 256);
-
-  {
-    // U block, 16-byte loads: pass u covers rows 8u .. 8u+7, one wave
-    // instruction reads two whole 512-byte rows.  Clamped in-bounds
-    // addresses (rows/columns past the block re-read the last one); entries
-    // outside the upper triangle of the w x w block are stored as zero.
-    const bool vec = ((n & 3) == 0) && ((i1 & 3) == 0);  // 16-byte aligned rows
-    floatx4 uv[16];
+  // Every global load of the block is issued before anything waits on one:
+  // the U block (16-byte loads, pass u covers rows 8u .. 8u+7, one wave
+  // instruction reads two whole 512-byte rows; clamped in-bounds addresses,
+  // rows/columns past the block re-read the last one), its diagonal, the
+  // wave's W tile and, for a forced mask, its mask bytes.  Their latencies
+  // overlap each other and the threshold search.
+  const bool uvec = ((n & 3) == 0) && ((i1 & 3) == 0);  // 16-byte aligned rows
+  floatx4 uv[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int f = u * 256 + tid;
-      const int j = f >> 5, c4 = (f & 31) * 4;
-      const int jc = j < w ? j : w - 1;
-      const float* urow = U + (i1 + jc) * n + i1;
-      if (vec && c4 + 4 <= w) {
-        uv[u] = *reinterpret_cast<const floatx4*>(urow + c4);
-      } else {
+  for (int u = 0; u < 16; ++u) {
+    const int f = u * 256 + tid;
+    const int j = f >> 5, c4 = (f & 31) * 4;
+    const int jc = j < w ? j : w - 1;
+    const float* urow = U + (i1 + jc) * n + i1;
+    if (uvec && c4 + 4 <= w) {
+      uv[u] = *reinterpret_cast<const floatx4*>(urow + c4);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) uv[u][e] = urow[c4 + e < w ? c4 + e : w - 1];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int f = u * 256 + tid;
-      const int j = f >> 5, c4 = (f & 31) * 4;
-      floatx4 t;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = c4 + e;
-        t[e] = (j < w && c < w && c >= j) ? uv[u][e] : 0.f;
-      }
-      *reinterpret_cast<floatx4*>(&S.Ub[j * SWS + c4]) = t;
+      for (int e = 0; e < 4; ++e) uv[u][e] = urow[c4 + e < w ? c4 + e : w - 1];
     }
   }
-  if (tid < SB) S.Rd[tid] = (tid < w) ? 1.f / U[(i1 + tid) * n + i1 + tid] : 0.f;
+  const int dj = tid < w ? tid : w - 1;
+  const float udiag = U[(i1 + dj) * n + i1 + dj];
 
   // Block columns in registers; rows past m read row m-1 and stay unwritten.
   // With 16-byte aligned rows the tile goes through the wave's LDS staging
@@ -580,18 +563,55 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   unsigned Pm[8];
 #pragma unroll
   for (int v = 0; v < 4; ++v) rowok[v] = r0 + v < m;
+  floatx4 wt[8];
+  unsigned mw[8];
   if (vio) {
-    floatx4 t[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
       const int64_t r = rw0 + rr < m ? rw0 + rr : m - 1;
-      t[u] = *reinterpret_cast<const floatx4*>(W + r * n + i1 + (c4 < w ? c4 : w - 4));
+      wt[u] = *reinterpret_cast<const floatx4*>(W + r * n + i1 + (c4 < w ? c4 : w - 4));
     }
+    if (MODE == MODE_FORCED) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
+        const int64_t r = rw0 + rr < m ? rw0 + rr : m - 1;
+        mw[u] = *reinterpret_cast<const unsigned*>(mask_in + r * n + i1 + (c4 < w ? c4 : w - 4));
+      }
+    }
+  }
+
+  // threshold key of the block (the LDS of the U block serves as scratch)
+  __shared__ unsigned s_cnt;
+  __shared__ HistPick s_pick;
+  unsigned long long thr = 0ull;
+  if (MODE == MODE_THRESH && sel_fixed == 0)
+    thr = select_finish(stp->set[parity], candp, ksel, reinterpret_cast<unsigned long long*>(S.Ub),
+                        &s_cnt, s_pick);
+  if (MODE == MODE_THRESH && (int)blockIdx.x == segs.wg0[seg]) sel_clear_set(stp->set[parity ^ 1], tid, 256);
+
+  // U block to LDS: entries outside the upper triangle of the w x w block
+  // are stored as zero
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int f = u * 256 + tid;
+    const int j = f >> 5, c4 = (f & 31) * 4;
+    floatx4 t;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = c4 + e;
+      t[e] = (j < w && c < w && c >= j) ? uv[u][e] : 0.f;
+    }
+    *reinterpret_cast<floatx4*>(&S.Ub[j * SWS + c4]) = t;
+  }
+  if (tid < SB) S.Rd[tid] = (tid < w) ? 1.f / udiag : 0.f;
+
+  if (vio) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
-      *reinterpret_cast<floatx4*>(&Tw[rr * SWS + c4]) = c4 < w ? t[u] : floatx4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<floatx4*>(&Tw[rr * SWS + c4]) = c4 < w ? wt[u] : floatx4{0.f, 0.f, 0.f, 0.f};
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -632,15 +652,9 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   // masks known at the block start
   if (MODE == MODE_FORCED) {
     if (vio) {
-      // the wave's 16 x w mask bytes, 4 bytes per access, through the staging tile
+      // the wave's 16 x w mask bytes (loaded in the prologue, 4 bytes per
+      // access) through the staging tile
       unsigned* Tb = reinterpret_cast<unsigned*>(Tw);
-      unsigned mw[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
-        const int64_t r = rw0 + rr < m ? rw0 + rr : m - 1;
-        mw[u] = *reinterpret_cast<const unsigned*>(mask_in + r * n + i1 + (c4 < w ? c4 : w - 4));
-      }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
@@ -668,12 +682,12 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int col = 16 * c + lc;
+      const float rdc = S.Rd[col];
       if (col < w) {
-        const float ucc = S.Ub[col * SWS + col];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           if (!rowok[v]) continue;
-          const unsigned long long key = sal_key(Wt[c][v], ucc, (uint32_t)((r0 + v) * n + i1 + col));
+          const unsigned long long key = sal_key(Wt[c][v], rdc, (uint32_t)((r0 + v) * n + i1 + col));
           if (done == 3u || (done == 1u && key <= thr)) Pm[c] |= 1u << v;
         }
       }
@@ -693,9 +707,10 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
     ChunkCtx cx;
     {
       const int col = 16 * c + lc;
+      // every lane reads all 16 values (no per-lane branch around a read)
       cx.ucc = S.Ub[col * SWS + col];
-      cx.rd = (col < w) ? 1.f / cx.ucc : 0.f;
-      float rdj[16];
+      cx.rd = S.Rd[col];  // 1 / U_col,col, 0 past the block
+      float rdj[16], uj[16];
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
         const floatx4 t = *reinterpret_cast<const floatx4*>(&S.Rd[16 * c + 4 * j4]);
@@ -703,8 +718,9 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
         for (int e = 0; e < 4; ++e) rdj[4 * j4 + e] = t[e];
       }
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        cx.g[j] = (j == lc) ? 0.f : S.Ub[(16 * c + j) * SWS + col] * rdj[j];
+      for (int j = 0; j < 16; ++j) uj[j] = S.Ub[(16 * c + j) * SWS + col];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) cx.g[j] = (j == lc) ? 0.f : uj[j] * rdj[j];
     }
     if (nm_large && ((16 * c) % mgroup) == 0) {
       // group of mgroup columns = chunks c .. c + ceil(mgroup/16) - 1 (all current)
@@ -719,10 +735,10 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
           const int pos = 16 * g + lc;
           const int col = 16 * (c + g) + lc;
           const bool ok = g < nchg && c + g < 8 && pos < mgroup;
-          const float ucg = S.Ub[(ok ? col : 0) * SWS + (ok ? col : 0)];
+          const float rdg = S.Rd[ok ? col : 0];
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            key[g][v] = ok ? (((unsigned long long)__float_as_uint(saliency(Wt[c + g < 8 ? c + g : 7][v], ucg))
+            key[g][v] = ok ? (((unsigned long long)__float_as_uint(saliency(Wt[c + g < 8 ? c + g : 7][v], rdg))
                                << 7) | (unsigned)pos)
                            : ~0ull;
         }
@@ -748,9 +764,9 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
         float* sc = Tw;
         for (int g = 0; g < nchg && c + g < 8; ++g) {
           const int col = 16 * (c + g) + lc;
-          const float ucg = S.Ub[col * SWS + col];
+          const float rdg = S.Rd[col];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) sc[(4 * lg + v) * SWS + 16 * g + lc] = saliency(Wt[c + g][v], ucg);
+          for (int v = 0; v < 4; ++v) sc[(4 * lg + v) * SWS + 16 * g + lc] = saliency(Wt[c + g][v], rdg);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_wave_barrier();
@@ -805,8 +821,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
       for (int c2 = 1; c2 < 8; ++c2) {
         if (c2 <= c) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          bv[c2][i] = c2 < nch ? S.Ub[(16 * c + 4 * i + lg) * SWS + 16 * c2 + lc] : 0.f;
+        for (int i = 0; i < 4; ++i) bv[c2][i] = S.Ub[(16 * c + 4 * i + lg) * SWS + 16 * c2 + lc];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
