@@ -124,26 +124,121 @@ __device__ __forceinline__ float rdlane(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
+// Rank-16 update of the trailing lower triangle after sub-panel p: the 16x16
+// tiles (I, C), p < C <= I < 8, dealt round robin to the 4 waves, MT = the
+// most any wave gets.  A wave issues all its LDS reads, then its MFMA chains
+// interleaved, then its writes (one LDS round trip instead of one per tile);
+// slots past the tile count recompute the first tile and are not written.
+template <int MT>
+__device__ __forceinline__ void rank16_update(PanelLds& S, int p, int wave, int lane) {
+  const int c0 = 16 * p;
+  const int t = 7 - p;
+  const int ntiles = t * (t + 1) / 2;
+  floatx4 acc[MT], fa[MT], fb[MT];
+  int aoff[MT];
+#pragma unroll
+  for (int s = 0; s < MT; ++s) {
+    const int i0 = wave + 4 * s;
+    const int idx = i0 < ntiles ? i0 : 0;
+    int ii = 0;
+    while ((ii + 1) * (ii + 2) / 2 <= idx) ++ii;
+    const int cc = idx - ii * (ii + 1) / 2;
+    const int I = p + 1 + ii, C = p + 1 + cc;
+    aoff[s] = (I * 16 + (lane >> 4) * 4) * PS + C * 16 + (lane & 15);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[s][v] = S.As[aoff[s] + v * PS];
+    fa[s] = *reinterpret_cast<const floatx4*>(&S.As[(I * 16 + (lane & 15)) * PS + c0 + (lane >> 4) * 4]);
+    fb[s] = *reinterpret_cast<const floatx4*>(&S.As[(C * 16 + (lane & 15)) * PS + c0 + (lane >> 4) * 4]);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int s = 0; s < MT; ++s) acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(-fa[s][e], fb[s][e], acc[s], 0, 0, 0);
+#pragma unroll
+  for (int s = 0; s < MT; ++s)
+    if (wave + 4 * s < ntiles) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) S.As[aoff[s] + v * PS] = acc[s][v];
+    }
+}
+
+// Block row P of L_kk^{-1} below the diagonal: X[P][Q] = -D_P sum_R L[P][R]
+// X[R][Q] for Q = wave, wave + 4 (Q < P).  The sum runs over R = 0 .. P-1:
+// the blocks X[R][Q] with R < Q are zero (the inverse is lower triangular and
+// its buffer starts cleared), so the trip count is fixed, every LDS read is
+// issued before the MFMAs, and both blocks of a wave are formed together.
+template <int P>
+__device__ __forceinline__ void inv_block_row(PanelLds& S, int wave, int lane) {
+  constexpr int NQ = P > 4 ? 2 : 1;
+  if (wave >= P) return;
+  floatx4 fa[P];
+  float bv[NQ][P][4];
+#pragma unroll
+  for (int R = 0; R < P; ++R) {
+    fa[R] = *reinterpret_cast<const floatx4*>(&S.As[(P * 16 + (lane & 15)) * PS + R * 16 + (lane >> 4) * 4]);
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) {
+      const int Q = (wave + 4 * h) & 7;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[h][R][e] = S.Li[(R * 16 + (lane >> 4) * 4 + e) * PS + Q * 16 + (lane & 15)];
+    }
+  }
+  const floatx4 fd = *reinterpret_cast<const floatx4*>(&S.Li[(P * 16 + (lane & 15)) * PS + P * 16 + (lane >> 4) * 4]);
+  floatx4 T[NQ];
+#pragma unroll
+  for (int h = 0; h < NQ; ++h) T[h] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int R = 0; R < P; ++R)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int h = 0; h < NQ; ++h) T[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[R][e], bv[h][R][e], T[h], 0, 0, 0);
+  // X[P][Q] = -D_P T; T in D-layout is the B operand (k = 4*(lane/16) + e)
+  floatx4 Xq[NQ];
+#pragma unroll
+  for (int h = 0; h < NQ; ++h) Xq[h] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) Xq[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(-fd[e], T[h][e], Xq[h], 0, 0, 0);
+#pragma unroll
+  for (int h = 0; h < NQ; ++h) {
+    const int Q = wave + 4 * h;
+    if (Q < P) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) S.Li[(P * 16 + (lane >> 4) * 4 + v) * PS + Q * 16 + (lane & 15)] = Xq[h][v];
+    }
+  }
+}
+
+// R = rows of the block this workgroup transforms at the end (128 / R
+// workgroups share each block; every one of them factors A_kk).
+template <int R>
 __device__ __forceinline__ void panel_body(PanelLds& S, float* __restrict__ A, float* __restrict__ Y,
-                                           int64_t n_pad, int k, int64_t n, int32_t* info, int b) {
+                                           int64_t n_pad, int k, int64_t n, int32_t* info, int b, int part) {
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform across the wave: held in a scalar register
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t k0 = (int64_t)k * NB;
 
-  // The 128x128 block this workgroup transforms at the end is fetched into
-  // registers right away, so its latency hides behind the factorisation.
+  // The R x 128 part of the block this workgroup transforms at the end
+  // (rows part * R ..) is fetched into registers right away, so its latency
+  // hides behind the factorisation.
   float* blk = nullptr;
   if (b > k)
-    blk = A + (int64_t)b * NB * n_pad + k0;  // L[l,k] = A[l,k] L_kk^{-T}
+    blk = A + ((int64_t)b * NB + part * R) * n_pad + k0;  // L[l,k] = A[l,k] L_kk^{-T}
   else if (b < k)
-    blk = Y + (int64_t)b * NB * n_pad + k0;  // Y[c,k] = R[c,k] L_kk^{-T}
-  const int brow = tid >> 1, bcol = (tid & 1) * 64;
-  floatx4 bv[16];
+    blk = Y + ((int64_t)b * NB + part * R) * n_pad + k0;  // Y[c,k] = R[c,k] L_kk^{-T}
+  constexpr int TPR = 256 / R;       // threads per row of the part
+  constexpr int CPT = NB / TPR;      // columns per thread
+  const int prow_t = tid / TPR, pcol_t = (tid % TPR) * CPT;
+  floatx4 bv[CPT / 4];
   if (blk) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      bv[u] = *reinterpret_cast<const floatx4*>(blk + (int64_t)brow * n_pad + bcol + 4 * u);
+    for (int u = 0; u < CPT / 4; ++u)
+      bv[u] = *reinterpret_cast<const floatx4*>(blk + (int64_t)prow_t * n_pad + pcol_t + 4 * u);
   }
+  const int brow = tid >> 1, bcol = (tid & 1) * 64;
 
   // 0. load the lower part of A_kk (all loads issued together), clear L_kk^{-1}
   {
@@ -228,27 +323,20 @@ __device__ __forceinline__ void panel_body(PanelLds& S, float* __restrict__ A, f
       if (lane == 0 && bad != 0ull && S.fail < 0) S.fail = c0 + __builtin_ctzll(bad);
     }
     __syncthreads();
-    // rank-16 update of the trailing lower triangle, 16x16 tiles (I >= C > p)
-    const int t = 7 - p;
-    const int ntiles = t * (t + 1) / 2;
-    for (int idx = wave; idx < ntiles; idx += 4) {
-      int ii = 0;
-      while ((ii + 1) * (ii + 2) / 2 <= idx) ++ii;
-      const int cc = idx - ii * (ii + 1) / 2;
-      const int I = p + 1 + ii, C = p + 1 + cc;
-      floatx4 acc;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] = S.As[(I * 16 + (lane >> 4) * 4 + v) * PS + C * 16 + (lane & 15)];
-      const floatx4 fa = *reinterpret_cast<const floatx4*>(&S.As[(I * 16 + (lane & 15)) * PS + c0 + (lane >> 4) * 4]);
-      const floatx4 fb = *reinterpret_cast<const floatx4*>(&S.As[(C * 16 + (lane & 15)) * PS + c0 + (lane >> 4) * 4]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-fa[e], fb[e], acc, 0, 0, 0);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) S.As[(I * 16 + (lane >> 4) * 4 + v) * PS + C * 16 + (lane & 15)] = acc[v];
+    // rank-16 update of the trailing lower triangle (t(t+1)/2 tiles, t = 7 - p)
+    switch (7 - p) {
+      case 7: rank16_update<7>(S, p, wave, lane); break;
+      case 6: rank16_update<6>(S, p, wave, lane); break;
+      case 5: rank16_update<4>(S, p, wave, lane); break;
+      case 4: rank16_update<3>(S, p, wave, lane); break;
+      case 3: rank16_update<2>(S, p, wave, lane); break;
+      case 2:
+      case 1: rank16_update<1>(S, p, wave, lane); break;
+      default: break;
     }
     __syncthreads();
   }
-  if (b == 0 && tid == 0 && S.fail >= 0) {
+  if (b == 0 && part == 0 && tid == 0 && S.fail >= 0) {
     const int64_t pcol = k0 + S.fail;  // column in the flipped order
     if (pcol < n) atomicCAS(info, 0, (int32_t)(n - pcol));
   }
@@ -271,72 +359,67 @@ __device__ __forceinline__ void panel_body(PanelLds& S, float* __restrict__ A, f
     for (int i = 0; i < 16; ++i) S.Li[(b0 + i) * PS + b0 + c] = x[i];
   }
   __syncthreads();
-  // 2b. block forward substitution for the off-diagonal blocks
-  for (int P = 1; P < 8; ++P) {
-    for (int Q = wave; Q < P; Q += 4) {
-      floatx4 T = floatx4{0.f, 0.f, 0.f, 0.f};
-      for (int R = Q; R < P; ++R) {
-        const floatx4 fa =
-            *reinterpret_cast<const floatx4*>(&S.As[(P * 16 + (lane & 15)) * PS + R * 16 + (lane >> 4) * 4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float bv = S.Li[(R * 16 + (lane >> 4) * 4 + e) * PS + Q * 16 + (lane & 15)];
-          T = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[e], bv, T, 0, 0, 0);
-        }
-      }
-      // X[P][Q] = -D_P T; T in D-layout is the B operand (k = 4*(lane/16) + e)
-      const floatx4 fd =
-          *reinterpret_cast<const floatx4*>(&S.Li[(P * 16 + (lane & 15)) * PS + P * 16 + (lane >> 4) * 4]);
-      floatx4 Xq = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Xq = __builtin_amdgcn_mfma_f32_16x16x4f32(-fd[e], T[e], Xq, 0, 0, 0);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) S.Li[(P * 16 + (lane >> 4) * 4 + v) * PS + Q * 16 + (lane & 15)] = Xq[v];
-    }
-    __syncthreads();
-  }
+  // 2b. block forward substitution for the off-diagonal blocks, one block
+  // row at a time
+  inv_block_row<1>(S, wave, lane);
+  __syncthreads();
+  inv_block_row<2>(S, wave, lane);
+  __syncthreads();
+  inv_block_row<3>(S, wave, lane);
+  __syncthreads();
+  inv_block_row<4>(S, wave, lane);
+  __syncthreads();
+  inv_block_row<5>(S, wave, lane);
+  __syncthreads();
+  inv_block_row<6>(S, wave, lane);
+  __syncthreads();
+  inv_block_row<7>(S, wave, lane);
+  __syncthreads();
 
   // 3. apply
   if (b == k) {
-    // Y[k,k] = L_kk^{-T}
-    for (int e = tid; e < NB * NB; e += 256) {
-      const int i = e >> 7, c = e & 127;
+    // Y[k,k] = L_kk^{-T}, rows part * R ..
+    for (int e = tid; e < R * NB; e += 256) {
+      const int i = part * R + (e >> 7), c = e & 127;
       Y[(k0 + i) * n_pad + k0 + c] = S.Li[c * PS + i];
     }
     return;
   }
-  // stage the prefetched block into the (now free) A_kk area
+  // stage the prefetched part into the (now free) A_kk area
 #pragma unroll
-  for (int u = 0; u < 16; ++u)
-    *reinterpret_cast<floatx4*>(&S.As[brow * PS + bcol + 4 * u]) = bv[u];
+  for (int u = 0; u < CPT / 4; ++u)
+    *reinterpret_cast<floatx4*>(&S.As[prow_t * PS + pcol_t + 4 * u]) = bv[u];
   __syncthreads();
-  TileAcc acc;
-  tile_zero(acc);
-  const int prow = (wave >> 1) * 64 + (lane & 15);
-  const int qrow = (wave & 1) * 64 + (lane & 15);
+  // out[r][c] = sum_q part[r][q] Linv[c][q]: wave w owns output columns
+  // 32w .. 32w+31 of all R rows, (R/16) x 2 MFMA blocks
+  constexpr int NI = R / 16;
+  floatx4 acc[NI][2];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) acc[i][0] = acc[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int qrow = wave * 32 + (lane & 15);
 #pragma unroll 2
   for (int kc = 0; kc < NB; kc += 16) {
     const int kl = kc + (lane >> 4) * 4;
-    floatx4 pp[4], qq[4];
+    floatx4 pp[NI], qq[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pp[i] = *reinterpret_cast<const floatx4*>(&S.As[(prow + i * 16) * PS + kl]);
+    for (int i = 0; i < NI; ++i) pp[i] = *reinterpret_cast<const floatx4*>(&S.As[(i * 16 + (lane & 15)) * PS + kl]);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) qq[jj] = *reinterpret_cast<const floatx4*>(&S.Li[(qrow + jj * 16) * PS + kl]);
+    for (int jj = 0; jj < 2; ++jj) qq[jj] = *reinterpret_cast<const floatx4*>(&S.Li[(qrow + jj * 16) * PS + kl]);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          acc.v[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(pp[i][e], qq[jj][e], acc.v[i][jj], 0, 0, 0);
+        for (int jj = 0; jj < 2; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(pp[i][e], qq[jj][e], acc[i][jj], 0, 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
+    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        blk[(int64_t)tile_row(wave, lane, i, v) * n_pad + tile_col(wave, lane, jj)] = acc.v[i][jj][v];
+        blk[(int64_t)(i * 16 + (lane >> 4) * 4 + v) * n_pad + wave * 32 + jj * 16 + (lane & 15)] = acc[i][jj][v];
 }
 
 // ---- trailing update ------------------------------------------------------
@@ -397,10 +480,13 @@ __device__ __forceinline__ void update_body(float* lds, float* __restrict__ A, f
   tile_sub_from(C, n_pad, NB, NB, acc, lds);
 }
 
+template <int R>
 __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float* __restrict__ Y,
                                                     int64_t n_pad, int k, int64_t n, int32_t* info) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  panel_body(*reinterpret_cast<PanelLds*>(smem), A, Y, n_pad, k, n, info, blockIdx.x);
+  constexpr int parts = NB / R;
+  panel_body<R>(*reinterpret_cast<PanelLds*>(smem), A, Y, n_pad, k, n, info, blockIdx.x / parts,
+                blockIdx.x % parts);
 }
 
 // Block column k+1 of panel k's update (what panel k+1 reads first) in 64x64
@@ -408,7 +494,7 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
 // which is only t + k + 1 tiles, for a short latency-bound launch.
 __global__ __launch_bounds__(256) void col_update_kernel(float* __restrict__ A, float* __restrict__ Y,
                                                          int64_t n_pad, int k, int nblk) {
-  __shared__ __attribute__((aligned(16))) unsigned char ldsb[X6Lds<64>::SIZE];
+  __shared__ __attribute__((aligned(16))) unsigned char ldsb[X6Lds<64>::SHORT];
   float* lds = reinterpret_cast<float*>(ldsb);
   const int64_t t = nblk - k - 1;
   int64_t idx = blockIdx.x >> 2;
@@ -429,26 +515,69 @@ __global__ __launch_bounds__(256) void col_update_kernel(float* __restrict__ A, 
     P = Y + c * NB * n_pad + (int64_t)k * NB;
     Q = A + lb * NB * n_pad + (int64_t)k * NB;
   }
+  // the quarter of C and both operands are requested before the first product
+  float* Cq = C + (int64_t)qr * 64 * n_pad + qc * 64;
+  CTileV<64> ct;
+  ct.load(Cq, n_pad, 64);
   RowsX6V<64> pl{P + (int64_t)qr * 64 * n_pad, n_pad, 64, NB};
   RowsX6V<64> ql{Q + (int64_t)qc * 64 * n_pad, n_pad, 64, NB};
   TileAccT<64> acc;
   tile_zero(acc);
-  tile_gemm_x6(acc, pl, ql, NB, ldsb);
-  tile_sub_from(C + (int64_t)qr * 64 * n_pad + qc * 64, n_pad, 64, 64, acc, lds);
+  tile_gemm_x6_short<64, NB / GBK>(acc, pl, ql, NB, ldsb);
+  tile_sub_pre(Cq, n_pad, 64, ct, acc, lds);
 }
 
-// Look-ahead step: workgroups [0, nblk) factor panel k+1 and transform its
-// blocks while the others apply the rest of panel k's trailing update (the
-// tiles outside block column k+1, which panel k+1 does not read).
+// Look-ahead step: workgroups [0, nblk * 128 / R) factor panel k+1 and
+// transform its blocks (R rows each) while the others apply the rest of panel
+// k's trailing update (the tiles outside block column k+1, which panel k+1
+// does not read).
+template <int R>
 __global__ __launch_bounds__(256) void panel_rest_kernel(float* __restrict__ A, float* __restrict__ Y,
                                                          int64_t n_pad, int k, int nblk, int64_t n,
                                                          int32_t* info) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  if ((int)blockIdx.x < nblk)
-    panel_body(*reinterpret_cast<PanelLds*>(smem), A, Y, n_pad, k + 1, n, info, blockIdx.x);
+  constexpr int parts = NB / R;
+  if ((int)blockIdx.x < nblk * parts)
+    panel_body<R>(*reinterpret_cast<PanelLds*>(smem), A, Y, n_pad, k + 1, n, info, blockIdx.x / parts,
+                  blockIdx.x % parts);
   else
     update_body(reinterpret_cast<float*>(smem), A, Y, n_pad, k, nblk, UPD_REST,
-                (int64_t)blockIdx.x - nblk);
+                (int64_t)blockIdx.x - nblk * parts);
+}
+
+// The panel chain (factor A_kk, invert it, transform the block column) is
+// the critical path of the factorisation at moderate n.  The transform is
+// split over 128 / R workgroups per block (each repeats the 128 x 128
+// factorisation, which is latency bound) while that keeps the panel launch
+// within one workgroup per CU.
+template <int R>
+sg_status run_factor_loop(float* A, float* Y, int64_t n_pad, int nblk, int64_t n, int32_t* info,
+                          hipStream_t st) {
+  constexpr int parts = NB / R;
+  static bool attr_done = false;
+  if (!attr_done) {
+    for (const void* f : {reinterpret_cast<const void*>(panel_kernel<R>),
+                          reinterpret_cast<const void*>(panel_rest_kernel<R>)})
+      if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PanelLds)) !=
+          hipSuccess)
+        return set_error(SG_ERR_HIP, "hipFuncSetAttribute(panel kernels) failed");
+    attr_done = true;
+  }
+  // panel 0; then per k: block column k+1 of panel k's update, and panel
+  // k+1 together with the rest of panel k's update
+  hipLaunchKernelGGL(panel_kernel<R>, dim3((unsigned)(nblk * parts)), dim3(256), sizeof(PanelLds), st, A, Y,
+                     n_pad, 0, n, info);
+  if (sg_status e = check_launch("factor panel")) return e;
+  for (int k = 0; k + 1 < nblk; ++k) {
+    hipLaunchKernelGGL(col_update_kernel, dim3((unsigned)(4 * update_tiles(k, nblk, UPD_COL))), dim3(256), 0,
+                       st, A, Y, n_pad, k, nblk);
+    if (sg_status e = check_launch("factor update (next column)")) return e;
+    const int64_t rest = update_tiles(k, nblk, UPD_REST);
+    hipLaunchKernelGGL(panel_rest_kernel<R>, dim3((unsigned)(nblk * parts + rest)), dim3(256),
+                       sizeof(PanelLds), st, A, Y, n_pad, k, nblk, n, info);
+    if (sg_status e = check_launch("factor panel + rest of update")) return e;
+  }
+  return SG_OK;
 }
 
 // ---- flip out: U[i][j] = Y[n-1-j][n-1-i] (i <= j), 0 below ------------------
@@ -494,35 +623,23 @@ sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double dam
   float* Y = A + n_pad * n_pad;
   float* lam = Y + n_pad * n_pad;
 
-  static bool attr_done = false;
-  if (!attr_done) {
-    for (const void* f : {reinterpret_cast<const void*>(panel_kernel),
-                          reinterpret_cast<const void*>(panel_rest_kernel)})
-      if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PanelLds)) !=
-          hipSuccess)
-        return set_error(SG_ERR_HIP, "hipFuncSetAttribute(panel kernels) failed");
-    attr_done = true;
-  }
-
   hipLaunchKernelGGL(damp_lambda_kernel, dim3(1), dim3(256), 0, st, H, n, damp, lam, info);
   if (sg_status e = check_launch("damping")) return e;
   const unsigned t64 = (unsigned)(n_pad / 64);
   hipLaunchKernelGGL(flip_init_kernel, dim3(t64, t64), dim3(256), 0, st, H, n, n_pad, lam, A, Y);
   if (sg_status e = check_launch("flip/init")) return e;
-  // panel 0; then per k: block column k+1 of panel k's update, and panel
-  // k+1 together with the rest of panel k's update
-  hipLaunchKernelGGL(panel_kernel, dim3(nblk), dim3(256), sizeof(PanelLds), st, A, Y, n_pad, 0, n,
-                     info);
-  if (sg_status e = check_launch("factor panel")) return e;
-  for (int k = 0; k + 1 < nblk; ++k) {
-    hipLaunchKernelGGL(col_update_kernel, dim3((unsigned)(4 * update_tiles(k, nblk, UPD_COL))), dim3(256), 0,
-                       st, A, Y, n_pad, k, nblk);
-    if (sg_status e = check_launch("factor update (next column)")) return e;
-    const int64_t rest = update_tiles(k, nblk, UPD_REST);
-    hipLaunchKernelGGL(panel_rest_kernel, dim3((unsigned)(nblk + rest)), dim3(256), sizeof(PanelLds),
-                       st, A, Y, n_pad, k, nblk, n, info);
-    if (sg_status e = check_launch("factor panel + rest of update")) return e;
-  }
+  // Rows per panel workgroup.  Up to n = 4096 the panel chain sets the time
+  // and the panel takes four workgroups per block (128 of the 256 CUs); at
+  // larger n the trailing update dominates, the panel workgroups (one CU
+  // each, for their 135 KB of LDS) would take CUs from it, and one
+  // workgroup per block is kept (measured at n = 11008: 13.8 ms with two per
+  // block against 12.8 ms with one).
+  sg_status e;
+  if (nblk * 8 <= kNumCU)
+    e = run_factor_loop<32>(A, Y, n_pad, nblk, n, info, st);
+  else
+    e = run_factor_loop<128>(A, Y, n_pad, nblk, n, info, st);
+  if (e != SG_OK) return e;
   const unsigned tn = (unsigned)ceil_div(n, 64);
   hipLaunchKernelGGL(finalize_kernel, dim3(tn, tn), dim3(256), 0, st, Y, n, n_pad, Hinv);
   return check_launch("factor finalize");

@@ -216,6 +216,57 @@ __device__ inline void tile_gemm_pipelined(TileAccT<T>& acc, PL& pl, QL& ql, int
 // C[0:rows, 0:cols] -= acc (C row-major with leading dimension ldc), staged
 // through LDS (which must hold T * (T + 4) floats and be free) so that the
 // read-modify-write of C is done with float4 accesses, T/4 lanes per row.
+// A T x T tile of C read ahead of the contraction that updates it (the
+// loads are in flight while the products are formed).  Applies when the tile
+// is full width with 16-byte aligned rows, the layout of tile_sub_from's
+// vector path: thread t holds columns 4 (t % (T/4)) .. +3 of rows
+// t / (T/4) + RPP * rr.
+template <int T>
+struct CTileV {
+  static constexpr int RPP = GTHREADS / (T / 4);
+  floatx4 cv[T / RPP];
+  __device__ static bool ok(const float* C, int64_t ldc, int cols) {
+    return (cols == T) && ((ldc & 3) == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
+  }
+  __device__ inline void load(const float* __restrict__ C, int64_t ldc, int rows) {
+    const int c4 = (threadIdx.x % (T / 4)) * 4, r0 = threadIdx.x / (T / 4);
+#pragma unroll
+    for (int rr = 0; rr < T / RPP; ++rr) {
+      const int r = r0 + rr * RPP;
+      const int rc = r < rows ? r : rows - 1;
+      cv[rr] = *reinterpret_cast<const floatx4*>(C + (int64_t)rc * ldc + c4);
+    }
+  }
+};
+
+// C -= acc with C's values read ahead into ct (CTileV::ok held); the
+// accumulator goes through LDS as in tile_sub_from.
+template <int T>
+__device__ inline void tile_sub_pre(float* __restrict__ C, int64_t ldc, int rows, const CTileV<T>& ct,
+                                    const TileAccT<T>& acc, float* lds) {
+  constexpr int TS = T + 4;
+  constexpr int RPP = CTileV<T>::RPP;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < T / 32; ++i)
+#pragma unroll
+    for (int jj = 0; jj < T / 32; ++jj)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        lds[tile_row<T>(wave, lane, i, v) * TS + tile_col<T>(wave, lane, jj)] = acc.v[i][jj][v];
+  __syncthreads();
+  const int c4 = (threadIdx.x % (T / 4)) * 4, r0 = threadIdx.x / (T / 4);
+#pragma unroll
+  for (int rr = 0; rr < T / RPP; ++rr) {
+    const int r = r0 + rr * RPP;
+    if (r < rows) {
+      const floatx4 t = *reinterpret_cast<const floatx4*>(&lds[r * TS + c4]);
+      *reinterpret_cast<floatx4*>(C + (int64_t)r * ldc + c4) = ct.cv[rr] - t;
+    }
+  }
+}
+
 template <int T>
 __device__ inline void tile_sub_from(float* __restrict__ C, int64_t ldc, int rows, int cols,
                                      const TileAccT<T>& acc, float* lds) {

@@ -36,6 +36,7 @@ struct X6Lds {
   static constexpr int BYTES = 2 * OPER * 2;           // both operands
   static constexpr int EPI = T * (T + 4) * 4;          // epilogue staging (fp32)
   static constexpr int SIZE = BYTES > EPI ? BYTES : EPI;
+  static constexpr int SHORT = 2 * BYTES > EPI ? 2 * BYTES : EPI;  // two chunk buffers
 };
 
 // x -> (h, m, l), four values at a time
@@ -184,6 +185,38 @@ __device__ inline void tile_gemm_x6(TileAccT<T>& acc, PL& pl, QL& ql, int64_t K,
       ql.store(Ql, (c + 1) * GBK);
       __syncthreads();
     }
+  }
+}
+
+// acc += P * Q^T for K <= 32 NCH, every operand load issued up front: the
+// short contractions (one block of errors, one panel) are latency bound, and
+// this takes one global round trip instead of one per chunk.  Two LDS
+// buffers, one barrier per chunk; lds holds X6Lds<T>::SHORT bytes.
+template <int T, int NCH, class PL, class QL>
+__device__ inline void tile_gemm_x6_short(TileAccT<T>& acc, const PL& pl0, const QL& ql0, int64_t K,
+                                          void* lds) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nch = (int)ceil_div(K, GBK);
+  PL pl[NCH];
+  QL ql[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    pl[c] = pl0;
+    ql[c] = ql0;
+    if (c < nch) {
+      pl[c].load(c * GBK);
+      ql[c].load(c * GBK);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c >= nch) break;
+    __bf16* Pl = static_cast<__bf16*>(lds) + (c & 1) * 2 * X6Lds<T>::OPER;
+    __bf16* Ql = Pl + X6Lds<T>::OPER;
+    pl[c].store(Pl, c * GBK);
+    ql[c].store(Ql, c * GBK);
+    __syncthreads();
+    tile_mma_x6(acc, Pl, Ql, wave, lane);
   }
 }
 

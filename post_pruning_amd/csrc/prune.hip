@@ -163,20 +163,34 @@ __global__ __launch_bounds__(256) void qgrid_kernel(const float* __restrict__ W,
 // its errors update the rest of the current group of columns (K = block
 // width); after the last block of a group, the errors of the whole group
 // update every column beyond it at once (K = group width).
-template <bool VEC, int T>
-__global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ W, const float* __restrict__ E,
+template <bool VEC, int T, bool SHORT = false>
+__global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ W, const float* __restrict__ E,
                                                    const float* __restrict__ U, int64_t m, int64_t n,
                                                    int64_t k0, int K, int64_t c_begin, int64_t c_end) {
-  constexpr int LDSB = VEC ? X6Lds<T>::SIZE : 4 * T * GS * 4;
+  constexpr int LDSB = VEC ? (SHORT ? X6Lds<T>::SHORT : X6Lds<T>::SIZE) : 4 * T * GS * 4;
   __shared__ __attribute__((aligned(16))) unsigned char ldsb[LDSB];
   float* lds = reinterpret_cast<float*>(ldsb);
   const int64_t r0 = (int64_t)blockIdx.y * T;
   const int64_t c0 = c_begin + (int64_t)blockIdx.x * T;
   const int rows = (int)min<int64_t>(T, m - r0);
   const int cols = (int)min<int64_t>(T, c_end - c0);
+  float* C = W + r0 * n + c0;
   TileAccT<T> acc;
   tile_zero(acc);
-  if constexpr (VEC) {
+  if constexpr (VEC && SHORT) {
+    // one block's errors (K <= 128): the operands and the W tile are all
+    // requested before the first product
+    CTileV<T> ct;
+    const bool cpre = CTileV<T>::ok(C, n, cols);
+    if (cpre) ct.load(C, n, rows);
+    RowsX6V<T> pl{E + r0 * EGK, EGK, rows, K};
+    ColsX6T<T> ql{U + k0 * n + c0, n, cols, K};
+    tile_gemm_x6_short<T, SB / GBK>(acc, pl, ql, K, ldsb);
+    if (cpre) {
+      tile_sub_pre(C, n, rows, ct, acc, lds);
+      return;
+    }
+  } else if constexpr (VEC) {
     // fp32-accurate products on bf16 MFMA (three-way split, six terms)
     RowsX6V<T> pl{E + r0 * EGK, EGK, rows, K};
     ColsX6T<T> ql{U + k0 * n + c0, n, cols, K};
@@ -186,7 +200,7 @@ __global__ __launch_bounds__(256) void lazy_kernel(float* __restrict__ W, const 
     ColsF32TT<T> ql{U + k0 * n + c0, n, cols, K};
     tile_gemm_pipelined(acc, pl, ql, K, lds);
   }
-  tile_sub_from(W + r0 * n + c0, n, rows, cols, acc, lds);
+  tile_sub_from(C, n, rows, cols, acc, lds);
 }
 
 // W[:, c_begin:c_end] -= E[:, 0:K] * U[k0:k0+K, c_begin:c_end] with the tile
@@ -203,7 +217,10 @@ sg_status launch_lazy(float* W, const float* E, const float* U, int64_t m, int64
       hipLaunchKernelGGL((lazy_kernel<false, 128>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end);
   } else {
     const dim3 grid((unsigned)ceil_div(c_end - c_begin, 64), (unsigned)ceil_div(m, 64));
-    if (vec)
+    if (vec && K <= SB)
+      hipLaunchKernelGGL((lazy_kernel<true, 64, true>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin,
+                         c_end);
+    else if (vec)
       hipLaunchKernelGGL((lazy_kernel<true, 64>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end);
     else
       hipLaunchKernelGGL((lazy_kernel<false, 64>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end);

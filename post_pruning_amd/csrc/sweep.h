@@ -496,7 +496,8 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   SweepLds& S = *reinterpret_cast<SweepLds*>(smem);
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform across the wave: held in a scalar register
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lc = lane & 15;       // column inside a chunk
   const int lg = lane >> 4;       // row group: rows 4*lg .. 4*lg+3 of the wave's 16
   // this workgroup's segment (matrix): its rows end at m
