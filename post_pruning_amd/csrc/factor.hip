@@ -24,14 +24,18 @@
 //     row blocks l > k:  L[l,k] = A[l,k] * L_kk^{-T}                 (TRSM)
 //     col blocks c < k:  Y[c,k] = R[c,k] * L_kk^{-T}                 (inverse)
 //     c == k:            Y[k,k] = L_kk^{-T}
-//   update kernel (fp32 MFMA, K = 128):
+//   trailing update (fp32-accurate products on bf16 MFMA, K = 128):
 //     A[l,m] -= L[l,k] L[m,k]^T   for k < m <= l                     (SYRK)
 //     R[c,l] -= Y[c,k] L[l,k]^T   for c <= k < l                      (inverse)
 // where R is the running right-hand side of L X = I, kept transposed in the
-// upper block triangle of Y (R starts as I).
+// upper block triangle of Y (R starts as I).  Look-ahead: block column k+1
+// of the update goes first (one short launch); panel k+1 then runs on the
+// caller's stream while the rest of the update runs on a second stream.
 #include "gemm_x6.h"
 
 #include <math.h>
+
+#include <mutex>
 
 namespace sg {
 namespace {
@@ -434,7 +438,7 @@ __device__ inline int64_t isqrt_floor(int64_t x) {
 //   UPD_ALL   every tile;
 //   UPD_COL   the tiles of block column k+1 only (what panel k+1 needs; run
 //             by col_update_kernel in 64x64 quarters);
-//   UPD_REST  every other tile (run while panel k+1 factors).
+//   UPD_REST  every other tile (run beside panel k+1).
 enum { UPD_ALL = 0, UPD_COL = 1, UPD_REST = 2 };
 
 __host__ __device__ inline int64_t update_tiles(int k, int nblk, int mode) {
@@ -527,10 +531,11 @@ __global__ __launch_bounds__(256) void col_update_kernel(float* __restrict__ A, 
   tile_sub_pre(Cq, n_pad, 64, ct, acc, lds);
 }
 
-// Look-ahead step: workgroups [0, nblk * 128 / R) factor panel k+1 and
-// transform its blocks (R rows each) while the others apply the rest of panel
-// k's trailing update (the tiles outside block column k+1, which panel k+1
-// does not read).
+// Look-ahead step in one launch: workgroups [0, nblk * 128 / R) factor panel
+// k+1 and transform its blocks (R rows each) while the others apply the rest
+// of panel k's trailing update (the tiles outside block column k+1, which
+// panel k+1 does not read).  The panel's workgroups come first in the grid,
+// so they are dispatched first.
 template <int R>
 __global__ __launch_bounds__(256) void panel_rest_kernel(float* __restrict__ A, float* __restrict__ Y,
                                                          int64_t n_pad, int k, int nblk, int64_t n,
@@ -545,14 +550,57 @@ __global__ __launch_bounds__(256) void panel_rest_kernel(float* __restrict__ A, 
                 (int64_t)blockIdx.x - nblk * parts);
 }
 
+// The rest of panel k's trailing update on its own (the panel launch runs
+// beside it on a second stream): 66 KB of LDS per workgroup, two per CU.
+__global__ __launch_bounds__(256, 2) void rest_update_kernel(float* __restrict__ A, float* __restrict__ Y,
+                                                             int64_t n_pad, int k, int nblk) {
+  __shared__ __attribute__((aligned(16))) unsigned char ldsb[X6Lds<NB>::SIZE];
+  update_body(reinterpret_cast<float*>(ldsb), A, Y, n_pad, k, nblk, UPD_REST, blockIdx.x);
+}
+
+// A second stream per device for the trailing updates, with the two events
+// that order it against the caller's stream; one factorisation at a time
+// per device enqueues on it.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t ev_panel = nullptr, ev_rest = nullptr;
+  std::mutex mu;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_init;
+
+sg_status side_stream(SideStream*& out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(SG_ERR_HIP, "factor: no current device (or device index >= %d)", kMaxDevices);
+  SideStream& ss = g_side[dev];
+  std::lock_guard<std::mutex> g(g_side_init);
+  if (!ss.s) {
+    hipStream_t s = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess)
+      return set_error(SG_ERR_HIP, "factor: creating the update stream or its events failed");
+    ss.ev_panel = a;
+    ss.ev_rest = b;
+    ss.s = s;
+  }
+  out = &ss;
+  return SG_OK;
+}
+
 // The panel chain (factor A_kk, invert it, transform the block column) is
 // the critical path of the factorisation at moderate n.  The transform is
 // split over 128 / R workgroups per block (each repeats the 128 x 128
 // factorisation, which is latency bound) while that keeps the panel launch
 // within one workgroup per CU.
+// One stream: panel 0, then per k the next-column update of panel k and one
+// launch holding panel k+1 and the rest of panel k's update.
 template <int R>
-sg_status run_factor_loop(float* A, float* Y, int64_t n_pad, int nblk, int64_t n, int32_t* info,
-                          hipStream_t st) {
+sg_status run_factor_fused(float* A, float* Y, int64_t n_pad, int nblk, int64_t n, int32_t* info,
+                           hipStream_t st) {
   constexpr int parts = NB / R;
   static bool attr_done = false;
   if (!attr_done) {
@@ -563,8 +611,6 @@ sg_status run_factor_loop(float* A, float* Y, int64_t n_pad, int nblk, int64_t n
         return set_error(SG_ERR_HIP, "hipFuncSetAttribute(panel kernels) failed");
     attr_done = true;
   }
-  // panel 0; then per k: block column k+1 of panel k's update, and panel
-  // k+1 together with the rest of panel k's update
   hipLaunchKernelGGL(panel_kernel<R>, dim3((unsigned)(nblk * parts)), dim3(256), sizeof(PanelLds), st, A, Y,
                      n_pad, 0, n, info);
   if (sg_status e = check_launch("factor panel")) return e;
@@ -577,6 +623,58 @@ sg_status run_factor_loop(float* A, float* Y, int64_t n_pad, int nblk, int64_t n
                        sizeof(PanelLds), st, A, Y, n_pad, k, nblk, n, info);
     if (sg_status e = check_launch("factor panel + rest of update")) return e;
   }
+  return SG_OK;
+}
+
+// Two streams: the rest of each step's update runs on the update stream with
+// two workgroups per CU instead of sharing a launch (and its 135 KB of LDS
+// per workgroup) with the panel.
+template <int R>
+sg_status run_factor_split(float* A, float* Y, int64_t n_pad, int nblk, int64_t n, int32_t* info,
+                           hipStream_t st) {
+  constexpr int parts = NB / R;
+  static bool attr_done = false;
+  if (!attr_done) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(panel_kernel<R>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PanelLds)) != hipSuccess)
+      return set_error(SG_ERR_HIP, "hipFuncSetAttribute(panel kernel) failed");
+    attr_done = true;
+  }
+  SideStream* ss = nullptr;
+  if (sg_status e = side_stream(ss)) return e;
+  std::lock_guard<std::mutex> g(ss->mu);
+  const auto api = [](hipError_t r, const char* what) -> sg_status {
+    return r == hipSuccess ? SG_OK : set_error(SG_ERR_HIP, "factor: %s failed", what);
+  };
+  // Caller's stream: panel 0, then per k the next-column update of panel k
+  // (after the rest of panel k-1's update, which covers that column) and
+  // panel k+1.  Update stream: the rest of panel k's update, after panel k,
+  // beside the next-column update and panel k+1.
+  hipLaunchKernelGGL(panel_kernel<R>, dim3((unsigned)(nblk * parts)), dim3(256), sizeof(PanelLds), st, A, Y,
+                     n_pad, 0, n, info);
+  if (sg_status e = check_launch("factor panel")) return e;
+  if (sg_status e = api(hipEventRecord(ss->ev_panel, st), "event record")) return e;
+  for (int k = 0; k + 1 < nblk; ++k) {
+    if (k > 0)
+      if (sg_status e = api(hipStreamWaitEvent(st, ss->ev_rest, 0), "stream wait")) return e;
+    hipLaunchKernelGGL(col_update_kernel, dim3((unsigned)(4 * update_tiles(k, nblk, UPD_COL))), dim3(256), 0,
+                       st, A, Y, n_pad, k, nblk);
+    if (sg_status e = check_launch("factor update (next column)")) return e;
+    if (sg_status e = api(hipStreamWaitEvent(ss->s, ss->ev_panel, 0), "stream wait")) return e;
+    const int64_t rest = update_tiles(k, nblk, UPD_REST);
+    if (rest > 0) {
+      hipLaunchKernelGGL(rest_update_kernel, dim3((unsigned)rest), dim3(256), 0, ss->s, A, Y, n_pad, k, nblk);
+      if (sg_status e = check_launch("factor update (rest)")) return e;
+    }
+    if (sg_status e = api(hipEventRecord(ss->ev_rest, ss->s), "event record")) return e;
+    hipLaunchKernelGGL(panel_kernel<R>, dim3((unsigned)(nblk * parts)), dim3(256), sizeof(PanelLds), st, A, Y,
+                       n_pad, k + 1, n, info);
+    if (sg_status e = check_launch("factor panel")) return e;
+    if (sg_status e = api(hipEventRecord(ss->ev_panel, st), "event record")) return e;
+  }
+  // join: the caller's stream waits for the last trailing update
+  if (nblk > 1)
+    if (sg_status e = api(hipStreamWaitEvent(st, ss->ev_rest, 0), "stream wait")) return e;
   return SG_OK;
 }
 
@@ -628,17 +726,19 @@ sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double dam
   const unsigned t64 = (unsigned)(n_pad / 64);
   hipLaunchKernelGGL(flip_init_kernel, dim3(t64, t64), dim3(256), 0, st, H, n, n_pad, lam, A, Y);
   if (sg_status e = check_launch("flip/init")) return e;
-  // Rows per panel workgroup.  Up to n = 4096 the panel chain sets the time
-  // and the panel takes four workgroups per block (128 of the 256 CUs); at
-  // larger n the trailing update dominates, the panel workgroups (one CU
-  // each, for their 135 KB of LDS) would take CUs from it, and one
-  // workgroup per block is kept (measured at n = 11008: 13.8 ms with two per
-  // block against 12.8 ms with one).
+  // Up to n = 4096 the panel chain sets the time: the panel takes four
+  // workgroups per block (128 of the 256 CUs) and shares one launch with the
+  // rest of the previous step's update, behind which its workgroups are
+  // dispatched first (1.63 ms at n = 4096 against 1.98 ms on two streams,
+  // where the update's workgroups delay the panel's).  At larger n the
+  // trailing update sets the time: one panel workgroup per block, and the
+  // update on its own stream at two workgroups per CU (n = 28672: 150 ms
+  // against 182 ms in the shared launch).
   sg_status e;
   if (nblk * 8 <= kNumCU)
-    e = run_factor_loop<32>(A, Y, n_pad, nblk, n, info, st);
+    e = run_factor_fused<32>(A, Y, n_pad, nblk, n, info, st);
   else
-    e = run_factor_loop<128>(A, Y, n_pad, nblk, n, info, st);
+    e = run_factor_split<128>(A, Y, n_pad, nblk, n, info, st);
   if (e != SG_OK) return e;
   const unsigned tn = (unsigned)ceil_div(n, 64);
   hipLaunchKernelGGL(finalize_kernel, dim3(tn, tn), dim3(256), 0, st, Y, n, n_pad, Hinv);

@@ -39,23 +39,37 @@ struct X6Lds {
   static constexpr int SHORT = 2 * BYTES > EPI ? 2 * BYTES : EPI;  // two chunk buffers
 };
 
-// x -> (h, m, l), four values at a time
-__device__ inline void split3(const floatx4& x, bf16x4v& h, bf16x4v& m, bf16x4v& l) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const __bf16 hb = (__bf16)x[e];
-    const float r1 = x[e] - (float)hb;
-    const __bf16 mb = (__bf16)r1;
-    const float r2 = r1 - (float)mb;
-    h[e] = hb;
-    m[e] = mb;
-    l[e] = (__bf16)r2;
-  }
+typedef float floatx2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// (a, b) -> their h, m and l parts as packed bf16 pairs (a in the low half):
+// one round-to-nearest-even pair conversion per part; the value of a packed
+// bf16 is its bits moved to the top of an fp32 word.
+__device__ __forceinline__ void split3_pair(float a, float b, uint32_t& hp, uint32_t& mp, uint32_t& lp) {
+  hp = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2v){a, b}, bf16x2v));
+  const float ra = a - __uint_as_float(hp << 16), rb = b - __uint_as_float(hp & 0xffff0000u);
+  mp = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2v){ra, rb}, bf16x2v));
+  const float sa = ra - __uint_as_float(mp << 16), sb = rb - __uint_as_float(mp & 0xffff0000u);
+  lp = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2v){sa, sb}, bf16x2v));
+}
+
+// four values split and written to the three planes (8 bytes each)
+__device__ __forceinline__ void store_split4(__bf16* lds, int plane, int off, const floatx4& x) {
+  uint32_t h0, m0, l0, h1, m1, l1;
+  split3_pair(x[0], x[1], h0, m0, l0);
+  split3_pair(x[2], x[3], h1, m1, l1);
+  typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<u32x2v*>(lds + 0 * plane + off) = u32x2v{h0, h1};
+  *reinterpret_cast<u32x2v*>(lds + 1 * plane + off) = u32x2v{m0, m1};
+  *reinterpret_cast<u32x2v*>(lds + 2 * plane + off) = u32x2v{l0, l1};
 }
 
 // Rows of a k-contiguous fp32 matrix with 16-byte aligned rows (as
 // RowsF32VT): element (r, k) = src[r*ld + k], valid for r < rows, k < kend
-// (kend % 4 == 0); stored split into the three planes.
+// (kend % 4 == 0); stored split into the three planes.  A chunk with every
+// row present and every k below kend is read from a workgroup-uniform base
+// plus a 32-bit per-lane offset (no per-element address arithmetic); other
+// chunks use clamped addresses and zero what lies outside.
 template <int T>
 struct RowsX6V {
   const float* src;
@@ -65,6 +79,15 @@ struct RowsX6V {
   floatx4 v[T / 32];
   __device__ inline void load(int64_t k0) {
     const int k4 = (threadIdx.x & 7) * 4, r0 = threadIdx.x >> 3;
+    if (rows == T && k0 + GBK <= kend && ld < (int64_t(1) << 24)) {
+      const uint32_t voff = (uint32_t)(r0 * ld + k4) * 4u;
+#pragma unroll
+      for (int u = 0; u < T / 32; ++u) {
+        const char* base = reinterpret_cast<const char*>(src + 32 * u * ld + k0);
+        v[u] = *reinterpret_cast<const floatx4*>(base + voff);
+      }
+      return;
+    }
     const int64_t k = k0 + k4;
     const int64_t kc = k < kend ? k : kend - 4;
 #pragma unroll
@@ -81,18 +104,16 @@ struct RowsX6V {
     for (int u = 0; u < T / 32; ++u) {
       const int r = r0 + 32 * u;
       const floatx4 x = (r < rows && kok) ? v[u] : floatx4{0.f, 0.f, 0.f, 0.f};
-      bf16x4v h, m, l;
-      split3(x, h, m, l);
-      *reinterpret_cast<bf16x4v*>(lds + 0 * X6Lds<T>::PLANE + r * XS + k4) = h;
-      *reinterpret_cast<bf16x4v*>(lds + 1 * X6Lds<T>::PLANE + r * XS + k4) = m;
-      *reinterpret_cast<bf16x4v*>(lds + 2 * X6Lds<T>::PLANE + r * XS + k4) = l;
+      store_split4(lds, X6Lds<T>::PLANE, r * XS + k4, x);
     }
   }
 };
 
 // Row-major [k][j] fp32 read transposed (as ColsF32TT): thread t owns column
 // j = t % T and KT = 32 T / 256 consecutive k; element (j, k) = src[k*ld + j],
-// valid for j < cols, k < kend; stored split into the three planes.
+// valid for j < cols, k < kend; stored split into the three planes.  The k
+// range of a thread is the same for its whole wave, so a full chunk is read
+// from uniform row addresses plus the lane's column offset.
 template <int T>
 struct ColsX6T {
   static constexpr int KT = GBK * T / GTHREADS;  // 16 (T = 128) or 8 (T = 64)
@@ -102,7 +123,17 @@ struct ColsX6T {
   int64_t kend;
   float v[KT];
   __device__ inline void load(int64_t k0) {
-    const int j = threadIdx.x % T, kb = (threadIdx.x / T) * KT;
+    const int j = threadIdx.x % T;
+    const int kb = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / T)) * KT;
+    if (cols == T && k0 + GBK <= kend) {
+      const uint32_t voff = (uint32_t)j * 4u;
+#pragma unroll
+      for (int u = 0; u < KT; ++u) {
+        const char* base = reinterpret_cast<const char*>(src + (k0 + kb + u) * ld);
+        v[u] = *reinterpret_cast<const float*>(base + voff);
+      }
+      return;
+    }
     const int jc = j < cols ? j : cols - 1;
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
@@ -118,11 +149,7 @@ struct ColsX6T {
       floatx4 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = (j < cols && k0 + kb + 4 * q + e < kend) ? v[4 * q + e] : 0.f;
-      bf16x4v h, m, l;
-      split3(x, h, m, l);
-      *reinterpret_cast<bf16x4v*>(lds + 0 * X6Lds<T>::PLANE + j * XS + kb + 4 * q) = h;
-      *reinterpret_cast<bf16x4v*>(lds + 1 * X6Lds<T>::PLANE + j * XS + kb + 4 * q) = m;
-      *reinterpret_cast<bf16x4v*>(lds + 2 * X6Lds<T>::PLANE + j * XS + kb + 4 * q) = l;
+      store_split4(lds, X6Lds<T>::PLANE, j * XS + kb + 4 * q, x);
     }
   }
 };

@@ -140,6 +140,29 @@ def test_hessian_and_factor(sg, case):
     assert _rel(Ug, ref["U"]) <= 1e-4
 
 
+def test_factor_update_stream_path(sg):
+    """Above n = 4096 the factorisation runs each step's trailing update on a
+    second stream (the panel and the update in separate launches): U against
+    the oracle as at the smaller sizes, and bit-for-bit repeatable."""
+    n, T = 4224, 6144  # 33 panels of 128
+    rng = np.random.default_rng(4224)
+    X = rng.standard_normal((T, n)) * np.exp(0.5 * rng.standard_normal(n))[None, :]
+    H = X.T @ X
+    Hd, _ = oracle.dampen(H, 0.01)
+    U = oracle.inverse_upper_factor(Hd)
+    Hg = torch.from_numpy(H.astype(np.float32)).cuda()
+    Hinv, info = sg.sg_prepare_hinv(Hg, 0.01)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    Ug = Hinv.cpu().double().numpy()
+    assert np.all(np.tril(Ug, -1) == 0.0)
+    assert np.all(np.diag(Ug) > 0)
+    assert _rel(Ug, U) <= 1e-4
+    Hinv2, _ = sg.sg_prepare_hinv(Hg, 0.01)
+    torch.cuda.synchronize()
+    assert torch.equal(Hinv, Hinv2)
+
+
 def _gpu_factor(sg, ref):
     cfg = ref["cfg"]
     X = ref["X"].cuda()
