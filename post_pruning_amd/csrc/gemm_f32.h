@@ -216,6 +216,12 @@ __device__ inline void tile_gemm_pipelined(TileAccT<T>& acc, PL& pl, QL& ql, int
 // C[0:rows, 0:cols] -= acc (C row-major with leading dimension ldc), staged
 // through LDS (which must hold T * (T + 4) floats and be free) so that the
 // read-modify-write of C is done with float4 accesses, T/4 lanes per row.
+// Epilogue hook: called with (row, column, new value) of every element the
+// epilogue stores; the default does nothing.
+struct NoHook {
+  __device__ void operator()(int, int, float) const {}
+};
+
 // A T x T tile of C read ahead of the contraction that updates it (the
 // loads are in flight while the products are formed).  Applies when the tile
 // is full width with 16-byte aligned rows, the layout of tile_sub_from's
@@ -241,9 +247,9 @@ struct CTileV {
 
 // C -= acc with C's values read ahead into ct (CTileV::ok held); the
 // accumulator goes through LDS as in tile_sub_from.
-template <int T>
+template <int T, class Hook = NoHook>
 __device__ inline void tile_sub_pre(float* __restrict__ C, int64_t ldc, int rows, const CTileV<T>& ct,
-                                    const TileAccT<T>& acc, float* lds) {
+                                    const TileAccT<T>& acc, float* lds, const Hook& hook = Hook()) {
   constexpr int TS = T + 4;
   constexpr int RPP = CTileV<T>::RPP;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -262,14 +268,17 @@ __device__ inline void tile_sub_pre(float* __restrict__ C, int64_t ldc, int rows
     const int r = r0 + rr * RPP;
     if (r < rows) {
       const floatx4 t = *reinterpret_cast<const floatx4*>(&lds[r * TS + c4]);
-      *reinterpret_cast<floatx4*>(C + (int64_t)r * ldc + c4) = ct.cv[rr] - t;
+      const floatx4 nv = ct.cv[rr] - t;
+      *reinterpret_cast<floatx4*>(C + (int64_t)r * ldc + c4) = nv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hook(r, c4 + e, nv[e]);
     }
   }
 }
 
-template <int T>
+template <int T, class Hook = NoHook>
 __device__ inline void tile_sub_from(float* __restrict__ C, int64_t ldc, int rows, int cols,
-                                     const TileAccT<T>& acc, float* lds) {
+                                     const TileAccT<T>& acc, float* lds, const Hook& hook = Hook()) {
   constexpr int TS = T + 4;
   constexpr int RPP = GTHREADS / (T / 4);  // rows per pass
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -300,7 +309,10 @@ __device__ inline void tile_sub_from(float* __restrict__ C, int64_t ldc, int row
       const int r = r0 + rr * RPP;
       if (r < rows) {
         const floatx4 t = *reinterpret_cast<const floatx4*>(&lds[r * TS + c4]);
-        *reinterpret_cast<floatx4*>(C + (int64_t)r * ldc + c4) = cv[rr] - t;
+        const floatx4 nv = cv[rr] - t;
+        *reinterpret_cast<floatx4*>(C + (int64_t)r * ldc + c4) = nv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hook(r, c4 + e, nv[e]);
       }
     }
   } else {
@@ -311,7 +323,11 @@ __device__ inline void tile_sub_from(float* __restrict__ C, int64_t ldc, int row
       float* crow = C + (int64_t)r * ldc;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (c4 + e < cols) crow[c4 + e] -= t[e];
+        if (c4 + e < cols) {
+          const float nv = crow[c4 + e] - t[e];
+          crow[c4 + e] = nv;
+          hook(r, c4 + e, nv);
+        }
     }
   }
 }

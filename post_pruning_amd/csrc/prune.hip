@@ -158,25 +158,58 @@ __global__ __launch_bounds__(256) void qgrid_kernel(const float* __restrict__ W,
   }
 }
 
+// Epilogue hook of the lazy update: the tiles that hold the next block's
+// final values count their saliency keys' top digit into an LDS histogram
+// (the first radix-select pass of that block, taken where the values are
+// produced).  Same digit and same fp32 saliency as select_pass_kernel.
+struct TopDigitHist {
+  unsigned* lh;       // LDS [kSelBins]
+  const float* lrd;   // LDS [T]: 1 / U_cc of the tile's columns
+  int ncols;          // tile columns inside the next block
+  __device__ void operator()(int, int c, float v) const {
+    if (c < ncols) atomicAdd(&lh[__float_as_uint(saliency(v, lrd[c])) >> 21], 1u);
+  }
+};
+
 // W[:, c_begin:c_end] -= E[:, 0:K] * U[k0:k0+K, c_begin:c_end]; E has row stride
 // EGK.  The lazy update of the column sweep, in two levels: after each block
 // its errors update the rest of the current group of columns (K = block
 // width); after the last block of a group, the errors of the whole group
-// update every column beyond it at once (K = group width).
+// update every column beyond it at once (K = group width).  With hist0 set,
+// the tiles over the next block's first hist_w columns also add that
+// block's top-digit histogram into hist0.
+
 template <bool VEC, int T, bool SHORT = false>
 __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ W, const float* __restrict__ E,
-                                                   const float* __restrict__ U, int64_t m, int64_t n,
-                                                   int64_t k0, int K, int64_t c_begin, int64_t c_end) {
+                                                      const float* __restrict__ U, int64_t m, int64_t n,
+                                                      int64_t k0, int K, int64_t c_begin, int64_t c_end,
+                                                      unsigned* __restrict__ hist0, int hist_w) {
   constexpr int LDSB = VEC ? (SHORT ? X6Lds<T>::SHORT : X6Lds<T>::SIZE) : 4 * T * GS * 4;
   __shared__ __attribute__((aligned(16))) unsigned char ldsb[LDSB];
+  __shared__ unsigned lhist[kSelBins];
+  __shared__ float lrd[T];
   float* lds = reinterpret_cast<float*>(ldsb);
   const int64_t r0 = (int64_t)blockIdx.y * T;
   const int64_t c0 = c_begin + (int64_t)blockIdx.x * T;
   const int rows = (int)min<int64_t>(T, m - r0);
   const int cols = (int)min<int64_t>(T, c_end - c0);
   float* C = W + r0 * n + c0;
+  // tiles over the next block's columns [c_begin, c_begin + hist_w)
+  const bool hist = hist0 != nullptr && (int64_t)blockIdx.x * T < hist_w;
+  const TopDigitHist hk{lhist, lrd, (int)min<int64_t>(cols, hist_w - (int64_t)blockIdx.x * T)};
+  // the tile's diagonal entries of U are requested now and stored to LDS
+  // after the products (their latency hides behind them)
+  float ucc = 1.f;
+  if (hist) {
+    for (int b = threadIdx.x; b < kSelBins; b += 256) lhist[b] = 0u;
+    if (threadIdx.x < T) {
+      const int64_t c = c0 + (threadIdx.x < cols ? threadIdx.x : 0);
+      ucc = U[c * n + c];
+    }
+  }
   TileAccT<T> acc;
   tile_zero(acc);
+  bool done = false;
   if constexpr (VEC && SHORT) {
     // one block's errors (K <= 128): the operands and the W tile are all
     // requested before the first product
@@ -186,9 +219,13 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ W, con
     RowsX6V<T> pl{E + r0 * EGK, EGK, rows, K};
     ColsX6T<T> ql{U + k0 * n + c0, n, cols, K};
     tile_gemm_x6_short<T, SB / GBK>(acc, pl, ql, K, ldsb);
+    if (hist && threadIdx.x < T) lrd[threadIdx.x] = 1.f / ucc;
     if (cpre) {
-      tile_sub_pre(C, n, rows, ct, acc, lds);
-      return;
+      if (hist)
+        tile_sub_pre(C, n, rows, ct, acc, lds, hk);
+      else
+        tile_sub_pre(C, n, rows, ct, acc, lds);
+      done = true;
     }
   } else if constexpr (VEC) {
     // fp32-accurate products on bf16 MFMA (three-way split, six terms)
@@ -200,30 +237,48 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ W, con
     ColsF32TT<T> ql{U + k0 * n + c0, n, cols, K};
     tile_gemm_pipelined(acc, pl, ql, K, lds);
   }
-  tile_sub_from(C, n, rows, cols, acc, lds);
+  if (!done) {
+    if (hist && threadIdx.x < T) lrd[threadIdx.x] = 1.f / ucc;
+    if (hist)
+      tile_sub_from(C, n, rows, cols, acc, lds, hk);
+    else
+      tile_sub_from(C, n, rows, cols, acc, lds);
+  }
+  if (hist) {
+    __syncthreads();
+    for (int b = threadIdx.x; b < kSelBins; b += 256) {
+      const unsigned v = lhist[b];
+      if (v) atomicAdd(&hist0[b], v);
+    }
+  }
 }
 
 // W[:, c_begin:c_end] -= E[:, 0:K] * U[k0:k0+K, c_begin:c_end] with the tile
 // that fills the GPU: 128 x 128 when that grid covers a full round of
 // workgroups (two per CU), else 64 x 64 (four times the workgroups).
 sg_status launch_lazy(float* W, const float* E, const float* U, int64_t m, int64_t n, int64_t k0, int K,
-                      int64_t c_begin, int64_t c_end, bool vec, hipStream_t st) {
+                      int64_t c_begin, int64_t c_end, bool vec, hipStream_t st, unsigned* hist0 = nullptr,
+                      int hist_w = 0) {
   const int64_t t128 = ceil_div(c_end - c_begin, 128) * ceil_div(m, 128);
   if (t128 >= 2 * kNumCU) {
     const dim3 grid((unsigned)ceil_div(c_end - c_begin, 128), (unsigned)ceil_div(m, 128));
     if (vec)
-      hipLaunchKernelGGL((lazy_kernel<true, 128>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end);
+      hipLaunchKernelGGL((lazy_kernel<true, 128>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end,
+                         hist0, hist_w);
     else
-      hipLaunchKernelGGL((lazy_kernel<false, 128>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end);
+      hipLaunchKernelGGL((lazy_kernel<false, 128>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin,
+                         c_end, hist0, hist_w);
   } else {
     const dim3 grid((unsigned)ceil_div(c_end - c_begin, 64), (unsigned)ceil_div(m, 64));
     if (vec && K <= SB)
       hipLaunchKernelGGL((lazy_kernel<true, 64, true>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin,
-                         c_end);
+                         c_end, hist0, hist_w);
     else if (vec)
-      hipLaunchKernelGGL((lazy_kernel<true, 64>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end);
+      hipLaunchKernelGGL((lazy_kernel<true, 64>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end,
+                         hist0, hist_w);
     else
-      hipLaunchKernelGGL((lazy_kernel<false, 64>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end);
+      hipLaunchKernelGGL((lazy_kernel<false, 64>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin,
+                         c_end, hist0, hist_w);
   }
   return check_launch("prune lazy");
 }
@@ -296,6 +351,9 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
   // lazy-update groups: GK columns (a multiple of the block width, at most EGK)
   const int64_t GK = (EGK / B) * B;
   int parity = 0;
+  // the first radix pass of a block is taken in the epilogue of the lazy
+  // update that produces its final values when there is one matrix
+  bool pass0_done = false;
   for (int64_t i1 = 0; i1 < n; i1 += B, parity ^= 1) {
     const int w = (int)std::min<int64_t>(B, n - i1);
     const int64_t g0 = (i1 / GK) * GK;
@@ -311,7 +369,7 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
         any = any || segs.fixed[p] == 0;
       }
       if (any) {
-        for (int pass = 0; pass < 2; ++pass) {
+        for (int pass = pass0_done ? 1 : 0; pass < 2; ++pass) {
           hipLaunchKernelGGL(select_pass_kernel, sel_grid, dim3(256), sizeof(SelLds), st, sel, parity,
                              cand, static_cast<const float*>(a.W_out), a.U, segs, n, i1, w, pass);
           if (sg_status e = check_launch("select pass")) return e;
@@ -350,15 +408,30 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
     if (sg_status e = quant ? launch_sweep_quant(sa) : (joint ? launch_sweep_joint(sa) : launch_sweep_plain(sa)))
       return e;
     const int64_t i2 = i1 + w;
+    // next block: histogram its keys' top digit in the lazy update's epilogue?
+    unsigned* hist0 = nullptr;
+    int hist_w = 0;
+    if (mode == MODE_THRESH && segs.n == 1 && i2 < n) {
+      const int w2 = (int)std::min<int64_t>(B, n - i2);
+      const long long k2 = (long long)floor(a.sparsity * (double)m * (double)w2);
+      if (k2 > 0 && k2 < (long long)m * w2) {
+        hist0 = sel[0].set[parity ^ 1].hist0;
+        hist_w = w2;
+      }
+    }
+    pass0_done = hist0 != nullptr;
     if (i2 < g_end) {
       // rest of the group, K = block width
-      if (sg_status e = launch_lazy(a.W_out, Eb, a.U, m, n, i1, w, i2, g_end, lazy_vec(Eb, w), st))
+      if (sg_status e =
+              launch_lazy(a.W_out, Eb, a.U, m, n, i1, w, i2, g_end, lazy_vec(Eb, w), st, hist0, hist_w))
         return e;
     } else if (g_end < n) {
       // last block of the group: every column beyond it, K = group width
       if (sg_status e = launch_lazy(a.W_out, Err, a.U, m, n, g0, (int)(g_end - g0), g_end, n,
-                                    lazy_vec(Err, (int)(g_end - g0)), st))
+                                    lazy_vec(Err, (int)(g_end - g0)), st, hist0, hist_w))
         return e;
+    } else {
+      pass0_done = false;
     }
   }
   return SG_OK;
