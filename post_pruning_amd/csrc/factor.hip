@@ -475,9 +475,10 @@ __device__ __forceinline__ void update_body(float* lds, float* __restrict__ A, f
     P = Y + c * NB * n_pad + (int64_t)k * NB;
     Q = A + lb * NB * n_pad + (int64_t)k * NB;
   }
-  // fp32-accurate products on bf16 MFMA (three-way split, six terms)
-  RowsX6V<NB> pl{P, n_pad, NB, NB};
-  RowsX6V<NB> ql{Q, n_pad, NB, NB};
+  // fp32-accurate products on bf16 MFMA (three-way split, six terms); every
+  // tile is full (n_pad < 2^24: the workspace holds 2 n_pad^2 floats)
+  RowsX6V<NB, true> pl{P, n_pad, NB, NB};
+  RowsX6V<NB, true> ql{Q, n_pad, NB, NB};
   TileAcc acc;
   tile_zero(acc);
   tile_gemm_x6(acc, pl, ql, NB, lds);
@@ -523,8 +524,8 @@ __global__ __launch_bounds__(256) void col_update_kernel(float* __restrict__ A, 
   float* Cq = C + (int64_t)qr * 64 * n_pad + qc * 64;
   CTileV<64> ct;
   ct.load(Cq, n_pad, 64);
-  RowsX6V<64> pl{P + (int64_t)qr * 64 * n_pad, n_pad, 64, NB};
-  RowsX6V<64> ql{Q + (int64_t)qc * 64 * n_pad, n_pad, 64, NB};
+  RowsX6V<64, true> pl{P + (int64_t)qr * 64 * n_pad, n_pad, 64, NB};
+  RowsX6V<64, true> ql{Q + (int64_t)qc * 64 * n_pad, n_pad, 64, NB};
   TileAccT<64> acc;
   tile_zero(acc);
   tile_gemm_x6_short<64, NB / GBK>(acc, pl, ql, NB, ldsb);

@@ -69,8 +69,10 @@ __device__ __forceinline__ void store_split4(__bf16* lds, int plane, int off, co
 // (kend % 4 == 0); stored split into the three planes.  A chunk with every
 // row present and every k below kend is read from a workgroup-uniform base
 // plus a 32-bit per-lane offset (no per-element address arithmetic); other
-// chunks use clamped addresses and zero what lies outside.
-template <int T>
+// chunks use clamped addresses and zero what lies outside.  FULL: the caller
+// guarantees rows == T, kend a multiple of 32 and ld < 2^24 (only the first
+// path is compiled).
+template <int T, bool FULL = false>
 struct RowsX6V {
   const float* src;
   int64_t ld;
@@ -79,7 +81,7 @@ struct RowsX6V {
   floatx4 v[T / 32];
   __device__ inline void load(int64_t k0) {
     const int k4 = (threadIdx.x & 7) * 4, r0 = threadIdx.x >> 3;
-    if (rows == T && k0 + GBK <= kend && ld < (int64_t(1) << 24)) {
+    if (FULL || (rows == T && k0 + GBK <= kend && ld < (int64_t(1) << 24))) {
       const uint32_t voff = (uint32_t)(r0 * ld + k4) * 4u;
 #pragma unroll
       for (int u = 0; u < T / 32; ++u) {
@@ -99,11 +101,11 @@ struct RowsX6V {
   }
   __device__ inline void store(__bf16* lds, int64_t k0) {
     const int k4 = (threadIdx.x & 7) * 4, r0 = threadIdx.x >> 3;
-    const bool kok = k0 + k4 < kend;
+    const bool kok = FULL || k0 + k4 < kend;
 #pragma unroll
     for (int u = 0; u < T / 32; ++u) {
       const int r = r0 + 32 * u;
-      const floatx4 x = (r < rows && kok) ? v[u] : floatx4{0.f, 0.f, 0.f, 0.f};
+      const floatx4 x = (FULL || (r < rows && kok)) ? v[u] : floatx4{0.f, 0.f, 0.f, 0.f};
       store_split4(lds, X6Lds<T>::PLANE, r * XS + k4, x);
     }
   }
@@ -113,8 +115,9 @@ struct RowsX6V {
 // j = t % T and KT = 32 T / 256 consecutive k; element (j, k) = src[k*ld + j],
 // valid for j < cols, k < kend; stored split into the three planes.  The k
 // range of a thread is the same for its whole wave, so a full chunk is read
-// from uniform row addresses plus the lane's column offset.
-template <int T>
+// from uniform row addresses plus the lane's column offset.  FULL: the caller
+// guarantees cols == T and kend a multiple of 32.
+template <int T, bool FULL = false>
 struct ColsX6T {
   static constexpr int KT = GBK * T / GTHREADS;  // 16 (T = 128) or 8 (T = 64)
   const float* src;
@@ -125,7 +128,7 @@ struct ColsX6T {
   __device__ inline void load(int64_t k0) {
     const int j = threadIdx.x % T;
     const int kb = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / T)) * KT;
-    if (cols == T && k0 + GBK <= kend) {
+    if (FULL || (cols == T && k0 + GBK <= kend)) {
       const uint32_t voff = (uint32_t)j * 4u;
 #pragma unroll
       for (int u = 0; u < KT; ++u) {
@@ -148,13 +151,14 @@ struct ColsX6T {
     for (int q = 0; q < KT / 4; ++q) {
       floatx4 x;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (j < cols && k0 + kb + 4 * q + e < kend) ? v[4 * q + e] : 0.f;
+      for (int e = 0; e < 4; ++e) x[e] = (FULL || (j < cols && k0 + kb + 4 * q + e < kend)) ? v[4 * q + e] : 0.f;
       store_split4(lds, X6Lds<T>::PLANE, j * XS + kb + 4 * q, x);
     }
   }
 };
 
-// acc += P[0:T, 0:32] * Q[0:T, 0:32]^T from the split planes in LDS.
+// acc += P[0:T, 0:32] * Q[0:T, 0:32]^T from the split planes in LDS.  The Q
+// fragments are read once; the P fragments one row block at a time.
 template <int T>
 __device__ inline void tile_mma_x6(TileAccT<T>& acc, const __bf16* Pl, const __bf16* Ql, int wave, int lane) {
   constexpr int NI = T / 32;
@@ -162,56 +166,98 @@ __device__ inline void tile_mma_x6(TileAccT<T>& acc, const __bf16* Pl, const __b
   const int prow = (wave >> 1) * (T / 2) + (lane & 15);
   const int qrow = (wave & 1) * (T / 2) + (lane & 15);
   const int k = (lane >> 4) * 8;
-  bf16x8v p[NI][3], q[NI][3];
+  bf16x8v q[NI][3];
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
+  for (int j = 0; j < NI; ++j)
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      p[i][s] = *reinterpret_cast<const bf16x8v*>(Pl + s * PL + (prow + i * 16) * XS + k);
-      q[i][s] = *reinterpret_cast<const bf16x8v*>(Ql + s * PL + (qrow + i * 16) * XS + k);
-    }
-  // smallest terms first
+    for (int s = 0; s < 3; ++s) q[j][s] = *reinterpret_cast<const bf16x8v*>(Ql + s * PL + (qrow + j * 16) * XS + k);
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
+  for (int i = 0; i < NI; ++i) {
+    bf16x8v p[3];
+#pragma unroll
+    for (int s = 0; s < 3; ++s) p[s] = *reinterpret_cast<const bf16x8v*>(Pl + s * PL + (prow + i * 16) * XS + k);
+    // smallest terms first
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       floatx4 a = acc.v[i][j];
-      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[i][1], q[j][1], a, 0, 0, 0);  // mm
-      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[i][0], q[j][2], a, 0, 0, 0);  // hl
-      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[i][2], q[j][0], a, 0, 0, 0);  // lh
-      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[i][0], q[j][1], a, 0, 0, 0);  // hm
-      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[i][1], q[j][0], a, 0, 0, 0);  // mh
-      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[i][0], q[j][0], a, 0, 0, 0);  // hh
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[1], q[j][1], a, 0, 0, 0);  // mm
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[0], q[j][2], a, 0, 0, 0);  // hl
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[2], q[j][0], a, 0, 0, 0);  // lh
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[0], q[j][1], a, 0, 0, 0);  // hm
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[1], q[j][0], a, 0, 0, 0);  // mh
+      a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p[0], q[j][0], a, 0, 0, 0);  // hh
       acc.v[i][j] = a;
     }
+  }
 }
 
-// acc += P * Q^T over k in [0, K); lds holds X6Lds<T>::SIZE bytes.
-template <int T, class PL, class QL>
+// acc += P * Q^T over k in [0, K); lds holds X6Lds<T>::SIZE bytes.  With
+// DEPTH = 2 the global loads run two chunks ahead (two register sets): a
+// chunk's products take less time than a load's round trip under load.
+// DEPTH = 1 loads one chunk ahead (fewer registers).
+template <int T, int DEPTH = 2, class PL, class QL>
 __device__ inline void tile_gemm_x6(TileAccT<T>& acc, PL& pl, QL& ql, int64_t K, void* lds) {
   __bf16* Pl = static_cast<__bf16*>(lds);
   __bf16* Ql = Pl + X6Lds<T>::OPER;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t nch = ceil_div(K, GBK);
   if (nch <= 0) return;
+  if constexpr (DEPTH == 1) {
+    pl.load(0);
+    ql.load(0);
+    pl.store(Pl, 0);
+    ql.store(Ql, 0);
+    __syncthreads();
+    for (int64_t c = 0; c < nch; ++c) {
+      const bool more = c + 1 < nch;
+      if (more) {
+        pl.load((c + 1) * GBK);
+        ql.load((c + 1) * GBK);
+      }
+      tile_mma_x6(acc, Pl, Ql, wave, lane);
+      if (more) {
+        __syncthreads();
+        pl.store(Pl, (c + 1) * GBK);
+        ql.store(Ql, (c + 1) * GBK);
+        __syncthreads();
+      }
+    }
+    return;
+  }
+  PL pl2 = pl;
+  QL ql2 = ql;
   pl.load(0);
   ql.load(0);
+  if (nch > 1) {
+    pl2.load(GBK);
+    ql2.load(GBK);
+  }
   pl.store(Pl, 0);
   ql.store(Ql, 0);
   __syncthreads();
-  for (int64_t c = 0; c < nch; ++c) {
-    const bool more = c + 1 < nch;
-    if (more) {
-      pl.load((c + 1) * GBK);
-      ql.load((c + 1) * GBK);
+  for (int64_t c = 0; c < nch; c += 2) {
+    // chunk c is in LDS, chunk c+1 in (pl2, ql2); (pl, ql) takes chunk c+2
+    if (c + 2 < nch) {
+      pl.load((c + 2) * GBK);
+      ql.load((c + 2) * GBK);
     }
     tile_mma_x6(acc, Pl, Ql, wave, lane);
-    if (more) {
-      __syncthreads();
-      pl.store(Pl, (c + 1) * GBK);
-      ql.store(Ql, (c + 1) * GBK);
-      __syncthreads();
+    if (c + 1 >= nch) break;
+    __syncthreads();
+    pl2.store(Pl, (c + 1) * GBK);
+    ql2.store(Ql, (c + 1) * GBK);
+    __syncthreads();
+    // chunk c+1 is in LDS, chunk c+2 in (pl, ql); (pl2, ql2) takes chunk c+3
+    if (c + 3 < nch) {
+      pl2.load((c + 3) * GBK);
+      ql2.load((c + 3) * GBK);
     }
+    tile_mma_x6(acc, Pl, Ql, wave, lane);
+    if (c + 2 >= nch) break;
+    __syncthreads();
+    pl.store(Pl, (c + 2) * GBK);
+    ql.store(Ql, (c + 2) * GBK);
+    __syncthreads();
   }
 }
 

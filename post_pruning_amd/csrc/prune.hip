@@ -228,10 +228,17 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ W, con
       done = true;
     }
   } else if constexpr (VEC) {
-    // fp32-accurate products on bf16 MFMA (three-way split, six terms)
-    RowsX6V<T> pl{E + r0 * EGK, EGK, rows, K};
-    ColsX6T<T> ql{U + k0 * n + c0, n, cols, K};
-    tile_gemm_x6(acc, pl, ql, K, ldsb);
+    // fp32-accurate products on bf16 MFMA (three-way split, six terms); full
+    // tiles take loaders without the clamped path (fewer live registers)
+    if (rows == T && cols == T && (K % GBK) == 0 && n < (int64_t(1) << 24)) {
+      RowsX6V<T, true> pl{E + r0 * EGK, EGK, rows, K};
+      ColsX6T<T, true> ql{U + k0 * n + c0, n, cols, K};
+      tile_gemm_x6(acc, pl, ql, K, ldsb);
+    } else {
+      RowsX6V<T> pl{E + r0 * EGK, EGK, rows, K};
+      ColsX6T<T> ql{U + k0 * n + c0, n, cols, K};
+      tile_gemm_x6<T, 1>(acc, pl, ql, K, ldsb);
+    }
   } else {
     RowsF32T<T> pl{E + r0 * EGK, EGK, rows, K, 1.f};
     ColsF32TT<T> ql{U + k0 * n + c0, n, cols, K};
