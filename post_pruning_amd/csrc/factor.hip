@@ -166,51 +166,56 @@ __device__ __forceinline__ void rank16_update(PanelLds& S, int p, int wave, int 
     }
 }
 
-// Block row P of L_kk^{-1} below the diagonal: X[P][Q] = -D_P sum_R L[P][R]
-// X[R][Q] for Q = wave, wave + 4 (Q < P).  The sum runs over R = 0 .. P-1:
-// the blocks X[R][Q] with R < Q are zero (the inverse is lower triangular and
-// its buffer starts cleared), so the trip count is fixed, every LDS read is
-// issued before the MFMAs, and both blocks of a wave are formed together.
-template <int P>
-__device__ __forceinline__ void inv_block_row(PanelLds& S, int wave, int lane) {
-  constexpr int NQ = P > 4 ? 2 : 1;
-  if (wave >= P) return;
-  floatx4 fa[P];
-  float bv[NQ][P][4];
+// Column blocks Q1 and Q2 of X = L_kk^{-1} below the diagonal, formed by one
+// wave: X[P][Q] = -D_P sum_{R=Q}^{P-1} L[P][R] X[R][Q] for P = Q+1 .. 7 in
+// order, D_P = X[P][P] (the 16x16 diagonal inverses, already in Li).  A
+// column's blocks depend only on blocks of the same column, so the wave needs
+// no barrier between them: each block stays in registers, where its MFMA
+// result layout (lane l, value v: row 4(l/16)+v, column l%16) is exactly the
+// B operand the later products read (k = 4(l/16)+e for the e-th K=4 MFMA),
+// and is written to Li for the apply.  The two columns' chains interleave.
+template <int Q1, int Q2>
+__device__ __forceinline__ void inv_columns(PanelLds& S, int lane) {
+  floatx4 X1[8], X2[8];
+  const int lr = lane & 15, lk = (lane >> 4) * 4;
 #pragma unroll
-  for (int R = 0; R < P; ++R) {
-    fa[R] = *reinterpret_cast<const floatx4*>(&S.As[(P * 16 + (lane & 15)) * PS + R * 16 + (lane >> 4) * 4]);
-#pragma unroll
-    for (int h = 0; h < NQ; ++h) {
-      const int Q = (wave + 4 * h) & 7;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bv[h][R][e] = S.Li[(R * 16 + (lane >> 4) * 4 + e) * PS + Q * 16 + (lane & 15)];
-    }
+  for (int v = 0; v < 4; ++v) {
+    X1[Q1][v] = S.Li[(Q1 * 16 + lk + v) * PS + Q1 * 16 + lr];
+    X2[Q2][v] = S.Li[(Q2 * 16 + lk + v) * PS + Q2 * 16 + lr];
   }
-  const floatx4 fd = *reinterpret_cast<const floatx4*>(&S.Li[(P * 16 + (lane & 15)) * PS + P * 16 + (lane >> 4) * 4]);
-  floatx4 T[NQ];
 #pragma unroll
-  for (int h = 0; h < NQ; ++h) T[h] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int P = 1; P < 8; ++P) {
+    if (P <= Q1 && P <= Q2) continue;
+    // the row P fragments of L (A operands, 4 consecutive k per lane)
+    floatx4 fa[8];
 #pragma unroll
-  for (int R = 0; R < P; ++R)
+    for (int R = 0; R < P; ++R)
+      if (R >= (Q1 < Q2 ? Q1 : Q2))
+        fa[R] = *reinterpret_cast<const floatx4*>(&S.As[(P * 16 + lr) * PS + R * 16 + lk]);
+    const floatx4 fd = *reinterpret_cast<const floatx4*>(&S.Li[(P * 16 + lr) * PS + P * 16 + lk]);
+    floatx4 T1 = floatx4{0.f, 0.f, 0.f, 0.f}, T2 = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int R = 0; R < P; ++R)
 #pragma unroll
-      for (int h = 0; h < NQ; ++h) T[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[R][e], bv[h][R][e], T[h], 0, 0, 0);
-  // X[P][Q] = -D_P T; T in D-layout is the B operand (k = 4*(lane/16) + e)
-  floatx4 Xq[NQ];
+      for (int e = 0; e < 4; ++e) {
+        if (P > Q1 && R >= Q1) T1 = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[R][e], X1[R][e], T1, 0, 0, 0);
+        if (P > Q2 && R >= Q2) T2 = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[R][e], X2[R][e], T2, 0, 0, 0);
+      }
+    floatx4 Y1 = floatx4{0.f, 0.f, 0.f, 0.f}, Y2 = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int h = 0; h < NQ; ++h) Xq[h] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 4; ++e) {
+      if (P > Q1) Y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(-fd[e], T1[e], Y1, 0, 0, 0);
+      if (P > Q2) Y2 = __builtin_amdgcn_mfma_f32_16x16x4f32(-fd[e], T2[e], Y2, 0, 0, 0);
+    }
+    if (P > Q1) {
+      X1[P] = Y1;
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
+      for (int v = 0; v < 4; ++v) S.Li[(P * 16 + lk + v) * PS + Q1 * 16 + lr] = Y1[v];
+    }
+    if (P > Q2) {
+      X2[P] = Y2;
 #pragma unroll
-    for (int h = 0; h < NQ; ++h) Xq[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(-fd[e], T[h][e], Xq[h], 0, 0, 0);
-#pragma unroll
-  for (int h = 0; h < NQ; ++h) {
-    const int Q = wave + 4 * h;
-    if (Q < P) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) S.Li[(P * 16 + (lane >> 4) * 4 + v) * PS + Q * 16 + (lane & 15)] = Xq[h][v];
+      for (int v = 0; v < 4; ++v) S.Li[(P * 16 + lk + v) * PS + Q2 * 16 + lr] = Y2[v];
     }
   }
 }
@@ -363,21 +368,14 @@ __device__ __forceinline__ void panel_body(PanelLds& S, float* __restrict__ A, f
     for (int i = 0; i < 16; ++i) S.Li[(b0 + i) * PS + b0 + c] = x[i];
   }
   __syncthreads();
-  // 2b. block forward substitution for the off-diagonal blocks, one block
-  // row at a time
-  inv_block_row<1>(S, wave, lane);
-  __syncthreads();
-  inv_block_row<2>(S, wave, lane);
-  __syncthreads();
-  inv_block_row<3>(S, wave, lane);
-  __syncthreads();
-  inv_block_row<4>(S, wave, lane);
-  __syncthreads();
-  inv_block_row<5>(S, wave, lane);
-  __syncthreads();
-  inv_block_row<6>(S, wave, lane);
-  __syncthreads();
-  inv_block_row<7>(S, wave, lane);
+  // 2b. the blocks below the diagonal, column block by column block: wave w
+  // forms columns w and 7 - w (balanced work, no barrier in between)
+  switch (wave) {
+    case 0: inv_columns<0, 7>(S, lane); break;
+    case 1: inv_columns<1, 6>(S, lane); break;
+    case 2: inv_columns<2, 5>(S, lane); break;
+    default: inv_columns<3, 4>(S, lane); break;
+  }
   __syncthreads();
 
   // 3. apply
