@@ -133,6 +133,76 @@ __device__ __forceinline__ float rdlane(float v, int l) {
 // most any wave gets.  A wave issues all its LDS reads, then its MFMA chains
 // interleaved, then its writes (one LDS round trip instead of one per tile);
 // slots past the tile count recompute the first tile and are not written.
+// Sub-panel factorisation in one wave: the 16 columns c0 .. c0+15 of the
+// rows c0 .. 127 (row c0 + lane in a0 and, with TWO, row c0 + 64 + lane in
+// a1), pivot by pivot, the pivot row's entries broadcast with readlane.
+template <bool TWO>
+__device__ __forceinline__ void subpanel_factor(PanelLds& S, int c0, int lane) {
+  const int r0 = c0 + lane, r1 = c0 + 64 + lane;
+  // 16-byte reads from clamped rows, out-of-range rows zeroed afterwards
+  const int r0c = r0 < NB ? r0 : NB - 1, r1c = r1 < NB ? r1 : NB - 1;
+  floatx4 t0[4], t1[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    t0[q] = *reinterpret_cast<const floatx4*>(&S.As[r0c * PS + c0 + 4 * q]);
+    if (TWO) t1[q] = *reinterpret_cast<const floatx4*>(&S.As[r1c * PS + c0 + 4 * q]);
+  }
+  float a0[16], a1[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    a0[c] = (r0 < NB) ? t0[c >> 2][c & 3] : 0.f;
+    a1[c] = (TWO && r1 < NB) ? t1[c >> 2][c & 3] : 0.f;
+  }
+  // No lane masks: entries above the diagonal start as zero, so scaling
+  // column j on every lane leaves them zero and turns the pivot into
+  // d2/d = d; the updates below only dirty entries (row j, column > j)
+  // above the diagonal, which are never read again and are dropped when
+  // the sub-panel is written back.
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float d2 = rdlane(a0[j], j);
+    // hardware reciprocal square root (about 1 ulp): the pivot chain is the
+    // latency-critical path of the whole factorisation
+    const float rd = __builtin_amdgcn_rsqf(d2);
+    a0[j] *= rd;
+    if (TWO) a1[j] *= rd;
+#pragma unroll
+    for (int c = j + 1; c < 16; ++c) {
+      const float lcj = rdlane(a0[j], c);
+      a0[c] = fmaf(-a0[j], lcj, a0[c]);
+      if (TWO) a1[c] = fmaf(-a1[j], lcj, a1[c]);
+    }
+    // right-looking order: the updated columns are materialised after
+    // every step, so each broadcast is consumed in its own step (left to
+    // itself the compiler sinks the updates to their first use and keeps
+    // every broadcast value live in scalar registers, which spill)
+    pin16(a0);
+    if (TWO) pin16(a1);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    floatx4 w0, w1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w0[e] = (4 * q + e <= lane) ? a0[4 * q + e] : 0.f;
+      w1[e] = a1[4 * q + e];
+    }
+    if (r0 < NB) *reinterpret_cast<floatx4*>(&S.As[r0 * PS + c0 + 4 * q]) = w0;
+    if (TWO && r1 < NB) *reinterpret_cast<floatx4*>(&S.As[r1 * PS + c0 + 4 * q]) = w1;
+  }
+  // breakdown: a pivot that was not positive and finite leaves a diagonal
+  // entry that is not (0 * inf, NaN or inf), and every later one follows;
+  // the first such column of the sub-panel is recorded
+  const float dj = S.As[(c0 + (lane & 15)) * PS + c0 + (lane & 15)];
+  const unsigned long long bad = __ballot(lane < 16 && !(dj > 0.f && isfinite(dj)));
+  if (lane == 0 && bad != 0ull && S.fail < 0) S.fail = c0 + __builtin_ctzll(bad);
+}
+
+// Row index ii of triangle tile idx (idx = ii (ii + 1) / 2 + cc, 0 <= cc <= ii),
+// 3 bits per entry: tiles 0..20 in kTriLo, 21..27 in kTriHi.
+constexpr uint64_t kTriLo = 0x5b6db2491b6d2448ull;
+constexpr uint64_t kTriHi = 0x1b6db6ull;
+
 template <int MT>
 __device__ __forceinline__ void rank16_update(PanelLds& S, int p, int wave, int lane) {
   const int c0 = 16 * p;
@@ -144,8 +214,9 @@ __device__ __forceinline__ void rank16_update(PanelLds& S, int p, int wave, int 
   for (int s = 0; s < MT; ++s) {
     const int i0 = wave + 4 * s;
     const int idx = i0 < ntiles ? i0 : 0;
-    int ii = 0;
-    while ((ii + 1) * (ii + 2) / 2 <= idx) ++ii;
+    // tile idx = ii (ii + 1) / 2 + cc of the triangle: ii from a packed
+    // table of 3-bit entries (idx < 28), no search loop
+    const int ii = (int)((idx < 21 ? (kTriLo >> (3 * idx)) : (kTriHi >> (3 * (idx - 21)))) & 7u);
     const int cc = idx - ii * (ii + 1) / 2;
     const int I = p + 1 + ii, C = p + 1 + cc;
     aoff[s] = (I * 16 + (lane >> 4) * 4) * PS + C * 16 + (lane & 15);
@@ -272,64 +343,11 @@ __device__ __forceinline__ void panel_body(PanelLds& S, float* __restrict__ A, f
   for (int p = 0; p < 8; ++p) {
     const int c0 = p * 16;
     if (wave == 0) {
-      const int r0 = c0 + lane, r1 = c0 + 64 + lane;
-      // 16-byte reads from clamped rows, out-of-range rows zeroed afterwards
-      const int r0c = r0 < NB ? r0 : NB - 1, r1c = r1 < NB ? r1 : NB - 1;
-      floatx4 t0[4], t1[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        t0[q] = *reinterpret_cast<const floatx4*>(&S.As[r0c * PS + c0 + 4 * q]);
-        t1[q] = *reinterpret_cast<const floatx4*>(&S.As[r1c * PS + c0 + 4 * q]);
-      }
-      float a0[16], a1[16];
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        a0[c] = (r0 < NB) ? t0[c >> 2][c & 3] : 0.f;
-        a1[c] = (r1 < NB) ? t1[c >> 2][c & 3] : 0.f;
-      }
-      // No lane masks: entries above the diagonal start as zero, so scaling
-      // column j on every lane leaves them zero and turns the pivot into
-      // d2/d = d; the updates below only dirty entries (row j, column > j)
-      // above the diagonal, which are never read again and are dropped when
-      // the sub-panel is written back.
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float d2 = rdlane(a0[j], j);
-        // hardware reciprocal square root (about 1 ulp): the pivot chain is the
-        // latency-critical path of the whole factorisation
-        const float rd = __builtin_amdgcn_rsqf(d2);
-        a0[j] *= rd;
-        a1[j] *= rd;
-#pragma unroll
-        for (int c = j + 1; c < 16; ++c) {
-          const float lcj = rdlane(a0[j], c);
-          a0[c] = fmaf(-a0[j], lcj, a0[c]);
-          a1[c] = fmaf(-a1[j], lcj, a1[c]);
-        }
-        // right-looking order: the updated columns are materialised after
-        // every step, so each broadcast is consumed in its own step (left to
-        // itself the compiler sinks the updates to their first use and keeps
-        // every broadcast value live in scalar registers, which spill)
-        pin16(a0);
-        pin16(a1);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        floatx4 w0, w1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w0[e] = (4 * q + e <= lane) ? a0[4 * q + e] : 0.f;
-          w1[e] = a1[4 * q + e];
-        }
-        if (r0 < NB) *reinterpret_cast<floatx4*>(&S.As[r0 * PS + c0 + 4 * q]) = w0;
-        if (r1 < NB) *reinterpret_cast<floatx4*>(&S.As[r1 * PS + c0 + 4 * q]) = w1;
-      }
-      // breakdown: a pivot that was not positive and finite leaves a diagonal
-      // entry that is not (0 * inf, NaN or inf), and every later one follows;
-      // the first such column of the sub-panel is recorded
-      const float dj = S.As[(c0 + (lane & 15)) * PS + c0 + (lane & 15)];
-      const unsigned long long bad = __ballot(lane < 16 && !(dj > 0.f && isfinite(dj)));
-      if (lane == 0 && bad != 0ull && S.fail < 0) S.fail = c0 + __builtin_ctzll(bad);
+      // rows c0 + lane and, while they exist, c0 + 64 + lane
+      if (c0 + 64 < NB)
+        subpanel_factor<true>(S, c0, lane);
+      else
+        subpanel_factor<false>(S, c0, lane);
     }
     __syncthreads();
     // rank-16 update of the trailing lower triangle (t(t+1)/2 tiles, t = 7 - p)
