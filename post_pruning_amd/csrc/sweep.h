@@ -679,18 +679,21 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
       }
     }
   } else if (MODE == MODE_THRESH) {
+    // key <= thr, the 64-bit key compared as its two 32-bit halves
+    // (saliency bits, then the position r*n + c modulo 2^32 as in sal_key)
     const unsigned done = sel_fixed ? (unsigned)sel_fixed : 1u;
+    const uint32_t thi = (uint32_t)(thr >> 32), tlo = (uint32_t)thr;
+    const uint32_t lin0 = (uint32_t)(r0 * n + i1 + lc), nn = (uint32_t)n;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int col = 16 * c + lc;
       const float rdc = S.Rd[col];
-      if (col < w) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          if (!rowok[v]) continue;
-          const unsigned long long key = sal_key(Wt[c][v], rdc, (uint32_t)((r0 + v) * n + i1 + col));
-          if (done == 3u || (done == 1u && key <= thr)) Pm[c] |= 1u << v;
-        }
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t sb = __float_as_uint(saliency(Wt[c][v], rdc));
+        const uint32_t lin = lin0 + (uint32_t)v * nn + 16u * (uint32_t)c;
+        const bool sel = done == 3u || (done == 1u && (sb < thi || (sb == thi && lin <= tlo)));
+        if (col < w && rowok[v] && sel) Pm[c] |= 1u << v;
       }
     }
   }
@@ -834,66 +837,42 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
     }
   }
 
-  // retire the block: W (pruned entries +0.0), errors, mask
-  if (vio) {
-    __builtin_amdgcn_wave_barrier();
-    // W, then the errors, then the mask bytes through the staging tile
+  // retire the block: W (pruned entries +0.0), errors, mask, straight from
+  // the registers (each store instruction writes 16 consecutive values of
+  // four rows; no staging round trip through LDS).  Full blocks of full
+  // rows store from four row pointers with constant offsets.
+  if (w == SB && rw0 + 16 <= m) {
+    float* wr[4];
+    float* er[4];
+    uint8_t* mr[4];
+    uint8_t* qr[4];
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          Tw[(4 * lg + v) * SWS + 16 * c + lc] = pass == 0 ? Wt[c][v] : Et[c][v];
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
-        const int64_t r = rw0 + rr;
-        const floatx4 t = *reinterpret_cast<const floatx4*>(&Tw[rr * SWS + c4]);
-        if (r < m) {
-          if (pass == 0) {
-            if (c4 < w) *reinterpret_cast<floatx4*>(W + r * n + i1 + c4) = t;
-          } else {
-            if (c4 < w) *reinterpret_cast<floatx4*>(Err + r * EGK + c4) = t;
-          }
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
+    for (int v = 0; v < 4; ++v) {
+      const int64_t r = r0 + v;
+      wr[v] = W + r * n + i1 + lc;
+      er[v] = Err + r * EGK + lc;
+      mr[v] = mask_out ? mask_out + r * n + i1 + lc : nullptr;
+      qr[v] = (QUANT && codes_out) ? codes_out + r * n + i1 + lc : nullptr;
     }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        wr[v][16 * c] = Wt[c][v];
+        er[v][16 * c] = Et[c][v];
+      }
     if (mask_out) {
-      unsigned char* Tm = reinterpret_cast<unsigned char*>(Tw);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) Tm[(4 * lg + v) * 128 + 16 * c + lc] = (Pm[c] >> v) & 1u;
-      __builtin_amdgcn_wave_barrier();
-      const unsigned* Tb = reinterpret_cast<const unsigned*>(Tw);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
-        const int64_t r = rw0 + rr;
-        if (r < m && c4 < w) *reinterpret_cast<unsigned*>(mask_out + r * n + i1 + c4) = Tb[rr * 32 + (c4 >> 2)];
-      }
+        for (int v = 0; v < 4; ++v) mr[v][16 * c] = (uint8_t)((Pm[c] >> v) & 1u);
     }
     if (QUANT && codes_out) {
-      // grid codes, recovered from the final values (pruned: 0 -> z)
-      __builtin_amdgcn_wave_barrier();
-      unsigned char* Tm = reinterpret_cast<unsigned char*>(Tw);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          Tm[(4 * lg + v) * 128 + 16 * c + lc] =
-              (unsigned char)fminf(fmaxf(rintf(Wt[c][v] * q.inv[v]) + q.z[v], 0.f), q.L);
-      __builtin_amdgcn_wave_barrier();
-      const unsigned* Tb = reinterpret_cast<const unsigned*>(Tw);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
-        const int64_t r = rw0 + rr;
-        if (r < m && c4 < w) *reinterpret_cast<unsigned*>(codes_out + r * n + i1 + c4) = Tb[rr * 32 + (c4 >> 2)];
-      }
+          qr[v][16 * c] = (unsigned char)fminf(fmaxf(rintf(Wt[c][v] * q.inv[v]) + q.z[v], 0.f), q.L);
     }
     return;
   }
