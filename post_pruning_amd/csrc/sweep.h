@@ -531,17 +531,28 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   // overlap each other and the threshold search.
   const bool uvec = ((n & 3) == 0) && ((i1 & 3) == 0);  // 16-byte aligned rows
   floatx4 uv[16];
+  if (uvec && w == SB && n < (int64_t(1) << 24)) {
+    // full block: pass u reads rows 8u + tid/32 from a uniform base (row
+    // i1 + 8u) plus the thread's 32-bit offset
+    const uint32_t uoff = (uint32_t)((tid >> 5) * n + (tid & 31) * 4) * 4u;
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int f = u * 256 + tid;
-    const int j = f >> 5, c4 = (f & 31) * 4;
-    const int jc = j < w ? j : w - 1;
-    const float* urow = U + (i1 + jc) * n + i1;
-    if (uvec && c4 + 4 <= w) {
-      uv[u] = *reinterpret_cast<const floatx4*>(urow + c4);
-    } else {
+    for (int u = 0; u < 16; ++u) {
+      const char* base = reinterpret_cast<const char*>(U + (i1 + 8 * u) * n + i1);
+      uv[u] = *reinterpret_cast<const floatx4*>(base + uoff);
+    }
+  } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) uv[u][e] = urow[c4 + e < w ? c4 + e : w - 1];
+    for (int u = 0; u < 16; ++u) {
+      const int f = u * 256 + tid;
+      const int j = f >> 5, c4 = (f & 31) * 4;
+      const int jc = j < w ? j : w - 1;
+      const float* urow = U + (i1 + jc) * n + i1;
+      if (uvec && c4 + 4 <= w) {
+        uv[u] = *reinterpret_cast<const floatx4*>(urow + c4);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) uv[u][e] = urow[c4 + e < w ? c4 + e : w - 1];
+      }
     }
   }
   const int dj = tid < w ? tid : w - 1;
@@ -566,7 +577,23 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   for (int v = 0; v < 4; ++v) rowok[v] = r0 + v < m;
   floatx4 wt[8];
   unsigned mw[8];
-  if (vio) {
+  if (vio && w == SB && rw0 + 16 <= m && n < (int64_t(1) << 24)) {
+    // full tile: pass u reads rows 2u + lane/32 from a uniform base
+    const uint32_t woff = (uint32_t)((lane >> 5) * n + (lane & 31) * 4) * 4u;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const char* base = reinterpret_cast<const char*>(W + (rw0 + 2 * u) * n + i1);
+      wt[u] = *reinterpret_cast<const floatx4*>(base + woff);
+    }
+    if (MODE == MODE_FORCED) {
+      const uint32_t moff = (uint32_t)((lane >> 5) * n + (lane & 31) * 4);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const unsigned char* base = mask_in + (rw0 + 2 * u) * n + i1;
+        mw[u] = *reinterpret_cast<const unsigned*>(base + moff);
+      }
+    }
+  } else if (vio) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
