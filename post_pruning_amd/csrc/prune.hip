@@ -73,7 +73,10 @@ __global__ __launch_bounds__(256) void select_pass_kernel(SelState* st, int pari
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   SelLds& L = *reinterpret_cast<SelLds*>(smem);
   const int tid = threadIdx.x, lane = tid & 63;
-  for (int b = tid; b < SEL_SUB * kSelBins; b += 256) (&L.h[0][0])[b] = 0u;
+  // pass 0 counts every key (lane-interleaved sub-histograms against hot
+  // bins); pass 1 only the few keys under the top digit (one histogram)
+  const int nsub = pass == 0 ? SEL_SUB : 1;
+  for (int b = tid; b < nsub * kSelBins; b += 256) (&L.h[0][0])[b] = 0u;
   if (tid == 0) L.nstage = 0u;
   unsigned top = 0;
   if (pass == 1) {
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(256) void select_pass_kernel(SelState* st, int pari
     wv[u] = W[(r < m ? r : m - 1) * n + col];
   }
   __syncthreads();
-  unsigned* hsub = L.h[lane & (SEL_SUB - 1)];
+  unsigned* hsub = L.h[pass == 0 ? (lane & (SEL_SUB - 1)) : 0];
 #pragma unroll
   for (int u = 0; u < SEL_KPT; ++u) {
     const int64_t r = rb + u * rstep;
@@ -111,8 +114,7 @@ __global__ __launch_bounds__(256) void select_pass_kernel(SelState* st, int pari
   unsigned* gh = pass == 0 ? ss->hist0 : ss->hist1;
   for (int b = tid; b < kSelBins; b += 256) {
     unsigned v = 0;
-#pragma unroll
-    for (int sh = 0; sh < SEL_SUB; ++sh) v += L.h[sh][b];
+    for (int sh = 0; sh < nsub; ++sh) v += L.h[sh][b];
     if (v) atomicAdd(&gh[b], v);
   }
   if (pass == 1) {
