@@ -78,17 +78,14 @@ __global__ __launch_bounds__(256) void select_pass_kernel(SelState* st, int pari
   const int nsub = pass == 0 ? SEL_SUB : 1;
   for (int b = tid; b < nsub * kSelBins; b += 256) (&L.h[0][0])[b] = 0u;
   if (tid == 0) L.nstage = 0u;
-  unsigned top = 0;
-  if (pass == 1) {
-    hist_locate(ss->hist0, k, L.pick);  // (includes a barrier)
-    top = L.pick.digit;
-  }
+  // this thread's keys are requested first: their latency overlaps the scan
+  // of the top-digit histogram
   const int shift = pass == 0 ? 53 : 42;
   const unsigned dmask = (1u << 11) - 1u;
   const int c = tid & 127;
   const int cc = c < w ? c : w - 1;
   const int64_t col = i1 + cc;
-  const float rd = 1.f / U[col * n + col];
+  const float ucol = U[col * n + col];
   const int64_t rstep = (int64_t)gridDim.x * 2;
   const int64_t rb = rlo + (int64_t)blockIdx.x * 2 + (tid >> 7);
   float wv[SEL_KPT];
@@ -97,6 +94,12 @@ __global__ __launch_bounds__(256) void select_pass_kernel(SelState* st, int pari
     const int64_t r = rb + u * rstep;
     wv[u] = W[(r < m ? r : m - 1) * n + col];
   }
+  unsigned top = 0;
+  if (pass == 1) {
+    hist_locate(ss->hist0, k, L.pick);  // (includes a barrier)
+    top = L.pick.digit;
+  }
+  const float rd = 1.f / ucol;
   __syncthreads();
   unsigned* hsub = L.h[pass == 0 ? (lane & (SEL_SUB - 1)) : 0];
 #pragma unroll
