@@ -128,11 +128,13 @@ __device__ __forceinline__ float rdlane(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// Rank-16 update of the trailing lower triangle after sub-panel p: the 16x16
-// tiles (I, C), p < C <= I < 8, dealt round robin to the 4 waves, MT = the
-// most any wave gets.  A wave issues all its LDS reads, then its MFMA chains
-// interleaved, then its writes (one LDS round trip instead of one per tile);
-// slots past the tile count recompute the first tile and are not written.
+// Part of the rank-16 update of the trailing lower triangle after sub-panel
+// p: the 16x16 tiles (I, C) of block column q0 (COL: q0 <= I < 8) or of the
+// triangle q0 <= C <= I < 8, dealt round robin to NW waves (w = this wave's
+// place among them), MT = the most any wave gets.  A wave issues all its LDS
+// reads, then its MFMA chains interleaved, then its writes (one LDS round
+// trip instead of one per tile); slots past the tile count recompute the
+// first tile and are not written.
 // Sub-panel factorisation in one wave: the 16 columns c0 .. c0+15 of the
 // rows c0 .. 127 (row c0 + lane in a0 and, with TWO, row c0 + 64 + lane in
 // a1), pivot by pivot, the pivot row's entries broadcast with readlane.
@@ -203,22 +205,22 @@ __device__ __forceinline__ void subpanel_factor(PanelLds& S, int c0, int lane) {
 constexpr uint64_t kTriLo = 0x5b6db2491b6d2448ull;
 constexpr uint64_t kTriHi = 0x1b6db6ull;
 
-template <int MT>
-__device__ __forceinline__ void rank16_update(PanelLds& S, int p, int wave, int lane) {
+template <int MT, bool COL, int NW>
+__device__ __forceinline__ void rank16_update(PanelLds& S, int p, int q0, int w, int lane) {
   const int c0 = 16 * p;
-  const int t = 7 - p;
-  const int ntiles = t * (t + 1) / 2;
+  const int t = 8 - q0;
+  const int ntiles = COL ? t : t * (t + 1) / 2;
   floatx4 acc[MT], fa[MT], fb[MT];
   int aoff[MT];
 #pragma unroll
   for (int s = 0; s < MT; ++s) {
-    const int i0 = wave + 4 * s;
+    const int i0 = w + NW * s;
     const int idx = i0 < ntiles ? i0 : 0;
     // tile idx = ii (ii + 1) / 2 + cc of the triangle: ii from a packed
     // table of 3-bit entries (idx < 28), no search loop
-    const int ii = (int)((idx < 21 ? (kTriLo >> (3 * idx)) : (kTriHi >> (3 * (idx - 21)))) & 7u);
-    const int cc = idx - ii * (ii + 1) / 2;
-    const int I = p + 1 + ii, C = p + 1 + cc;
+    const int ii = COL ? idx : (int)((idx < 21 ? (kTriLo >> (3 * idx)) : (kTriHi >> (3 * (idx - 21)))) & 7u);
+    const int cc = COL ? 0 : idx - ii * (ii + 1) / 2;
+    const int I = q0 + ii, C = q0 + cc;
     aoff[s] = (I * 16 + (lane >> 4) * 4) * PS + C * 16 + (lane & 15);
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[s][v] = S.As[aoff[s] + v * PS];
@@ -231,7 +233,7 @@ __device__ __forceinline__ void rank16_update(PanelLds& S, int p, int wave, int 
     for (int s = 0; s < MT; ++s) acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(-fa[s][e], fb[s][e], acc[s], 0, 0, 0);
 #pragma unroll
   for (int s = 0; s < MT; ++s)
-    if (wave + 4 * s < ntiles) {
+    if (w + NW * s < ntiles) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) S.As[aoff[s] + v * PS] = acc[s][v];
     }
@@ -339,27 +341,38 @@ __device__ __forceinline__ void panel_body(PanelLds& S, float* __restrict__ A, f
   if (tid == 0) S.fail = -1;
   __syncthreads();
 
-  // 1. blocked Cholesky, 16-column sub-panels
-  for (int p = 0; p < 8; ++p) {
-    const int c0 = p * 16;
+  // 1. blocked Cholesky, 16-column sub-panels, with a look-ahead of one:
+  // after sub-panel p, the four waves first update block column p+1 (what
+  // sub-panel p+1 reads); then wave 0 factors sub-panel p+1 while waves 1..3
+  // update the rest of the trailing triangle (block columns p+2 ..), which
+  // sub-panel p+1 neither reads nor writes.
+  if (wave == 0) subpanel_factor<true>(S, 0, lane);
+  __syncthreads();
+  for (int p = 0; p < 7; ++p) {
+    // block column p+1: 7 - p tiles
+    if (p < 3)
+      rank16_update<2, true, 4>(S, p, p + 1, wave, lane);
+    else
+      rank16_update<1, true, 4>(S, p, p + 1, wave, lane);
+    __syncthreads();
     if (wave == 0) {
       // rows c0 + lane and, while they exist, c0 + 64 + lane
+      const int c0 = (p + 1) * 16;
       if (c0 + 64 < NB)
         subpanel_factor<true>(S, c0, lane);
       else
         subpanel_factor<false>(S, c0, lane);
-    }
-    __syncthreads();
-    // rank-16 update of the trailing lower triangle (t(t+1)/2 tiles, t = 7 - p)
-    switch (7 - p) {
-      case 7: rank16_update<7>(S, p, wave, lane); break;
-      case 6: rank16_update<6>(S, p, wave, lane); break;
-      case 5: rank16_update<4>(S, p, wave, lane); break;
-      case 4: rank16_update<3>(S, p, wave, lane); break;
-      case 3: rank16_update<2>(S, p, wave, lane); break;
-      case 2:
-      case 1: rank16_update<1>(S, p, wave, lane); break;
-      default: break;
+    } else {
+      // the triangle of block columns p+2 .. 7: (6 - p)(7 - p)/2 tiles
+      switch (p) {
+        case 0: rank16_update<7, false, 3>(S, p, p + 2, wave - 1, lane); break;
+        case 1: rank16_update<5, false, 3>(S, p, p + 2, wave - 1, lane); break;
+        case 2: rank16_update<4, false, 3>(S, p, p + 2, wave - 1, lane); break;
+        case 3: rank16_update<2, false, 3>(S, p, p + 2, wave - 1, lane); break;
+        case 4:
+        case 5: rank16_update<1, false, 3>(S, p, p + 2, wave - 1, lane); break;
+        default: break;
+      }
     }
     __syncthreads();
   }
