@@ -706,32 +706,32 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
       }
     }
   } else if (MODE == MODE_THRESH) {
-    // key <= thr, the 64-bit key compared as its two 32-bit halves
-    // (saliency bits, then the position r*n + c modulo 2^32 as in sal_key).
-    // Written with bitwise operations on 0/1 words so that it compiles to
-    // straight-line selects, not one branch per key; the eight 1/U_cc
+    // key <= thr as one 64-bit compare per key (saliency bits, then the
+    // position r*n + c modulo 2^32 as in sal_key); the uniform cases (none
+    // or all selected) branch once, outside the loops.  The eight 1/U_cc
     // values are read before any is used.
-    const unsigned done = sel_fixed ? (unsigned)sel_fixed : 1u;
-    const unsigned all = done == 3u ? 1u : 0u, some = done == 1u ? 1u : 0u;
-    const uint32_t thi = (uint32_t)(thr >> 32), tlo = (uint32_t)thr;
-    const uint32_t lin0 = (uint32_t)(r0 * n + i1 + lc), nn = (uint32_t)n;
-    float rdv[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) rdv[c] = S.Rd[16 * c + lc];
     const unsigned rows = (rowok[0] ? 1u : 0u) | (rowok[1] ? 2u : 0u) | (rowok[2] ? 4u : 0u) |
                           (rowok[3] ? 8u : 0u);
+    if (sel_fixed == 0) {
+      const uint32_t lin0 = (uint32_t)(r0 * n + i1 + lc), nn = (uint32_t)n;
+      float rdv[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const unsigned colok = 16 * c + lc < w ? rows : 0u;
-      unsigned bits = 0u;
+      for (int c = 0; c < 8; ++c) rdv[c] = S.Rd[16 * c + lc];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint32_t sb = __float_as_uint(saliency(Wt[c][v], rdv[c]));
-        const uint32_t lin = lin0 + (uint32_t)v * nn + 16u * (uint32_t)c;
-        const unsigned below = (sb < thi ? 1u : 0u) | ((sb == thi ? 1u : 0u) & (lin <= tlo ? 1u : 0u));
-        bits |= (all | (some & below)) << v;
+      for (int c = 0; c < 8; ++c) {
+        unsigned bits = 0u;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t lin = lin0 + (uint32_t)v * nn + 16u * (uint32_t)c;
+          const unsigned long long key =
+              ((unsigned long long)__float_as_uint(saliency(Wt[c][v], rdv[c])) << 32) | lin;
+          bits |= (key <= thr ? 1u : 0u) << v;
+        }
+        Pm[c] |= bits & (16 * c + lc < w ? rows : 0u);
       }
-      Pm[c] |= bits & colok;
+    } else if (sel_fixed == 3) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) Pm[c] |= 16 * c + lc < w ? rows : 0u;
     }
   }
 
