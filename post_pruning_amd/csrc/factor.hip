@@ -632,15 +632,13 @@ template <int R>
 sg_status run_factor_fused(float* A, float* Y, int64_t n_pad, int nblk, int64_t n, int32_t* info,
                            hipStream_t st) {
   constexpr int parts = NB / R;
-  static bool attr_done = false;
-  if (!attr_done) {
-    for (const void* f : {reinterpret_cast<const void*>(panel_kernel<R>),
-                          reinterpret_cast<const void*>(panel_rest_kernel<R>)})
-      if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PanelLds)) !=
-          hipSuccess)
-        return set_error(SG_ERR_HIP, "hipFuncSetAttribute(panel kernels) failed");
-    attr_done = true;
-  }
+  // the LDS limit is a per-device attribute: set on every call (cheap), so
+  // that a call on another device finds it set too
+  for (const void* f : {reinterpret_cast<const void*>(panel_kernel<R>),
+                        reinterpret_cast<const void*>(panel_rest_kernel<R>)})
+    if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PanelLds)) !=
+        hipSuccess)
+      return set_error(SG_ERR_HIP, "hipFuncSetAttribute(panel kernels) failed");
   hipLaunchKernelGGL(panel_kernel<R>, dim3((unsigned)(nblk * parts)), dim3(256), sizeof(PanelLds), st, A, Y,
                      n_pad, 0, n, info);
   if (sg_status e = check_launch("factor panel")) return e;
@@ -663,13 +661,9 @@ template <int R>
 sg_status run_factor_split(float* A, float* Y, int64_t n_pad, int nblk, int64_t n, int32_t* info,
                            hipStream_t st) {
   constexpr int parts = NB / R;
-  static bool attr_done = false;
-  if (!attr_done) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(panel_kernel<R>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PanelLds)) != hipSuccess)
-      return set_error(SG_ERR_HIP, "hipFuncSetAttribute(panel kernel) failed");
-    attr_done = true;
-  }
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(panel_kernel<R>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PanelLds)) != hipSuccess)
+    return set_error(SG_ERR_HIP, "hipFuncSetAttribute(panel kernel) failed");
   SideStream* ss = nullptr;
   if (sg_status e = side_stream(ss)) return e;
   std::lock_guard<std::mutex> g(ss->mu);
