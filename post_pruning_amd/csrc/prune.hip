@@ -31,18 +31,40 @@
 namespace sg {
 namespace {
 
-__global__ void convert_kernel(float* __restrict__ out, const void* __restrict__ W, int dtype,
-                               int64_t m, int64_t n, int64_t ldw) {
-  const int64_t total = m * n;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = e / n, c = e - r * n;
-    float v;
-    if (dtype == SG_BF16)
-      v = bf16_to_f32(static_cast<const uint16_t*>(W)[r * ldw + c]);
-    else
-      v = static_cast<const float*>(W)[r * ldw + c];
-    out[e] = v;
+// W (bf16 or fp32, row stride ldw) -> out (fp32, row stride n).  Each
+// thread converts 8 consecutive columns of a row (blockIdx.x picks 2048
+// columns, blockIdx.y strides over the rows): 16-byte accesses when every
+// row of both matrices is 16-byte aligned (vec), element by element
+// otherwise and in a row's last partial group.
+__global__ __launch_bounds__(256) void convert_kernel(float* __restrict__ out, const void* __restrict__ W,
+                                                      int dtype, int64_t m, int64_t n, int64_t ldw, int vec) {
+  const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (c0 >= n) return;
+  for (int64_t r = blockIdx.y; r < m; r += gridDim.y) {
+    float* o = out + r * n + c0;
+    if (vec && c0 + 8 <= n) {
+      if (dtype == SG_BF16) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(W) + r * ldw + c0);
+        floatx4 lo, hi;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          lo[2 * q] = __uint_as_float(x[q] << 16);
+          lo[2 * q + 1] = __uint_as_float(x[q] & 0xffff0000u);
+          hi[2 * q] = __uint_as_float(x[q + 2] << 16);
+          hi[2 * q + 1] = __uint_as_float(x[q + 2] & 0xffff0000u);
+        }
+        *reinterpret_cast<floatx4*>(o) = lo;
+        *reinterpret_cast<floatx4*>(o + 4) = hi;
+      } else {
+        const float* src = static_cast<const float*>(W) + r * ldw + c0;
+        *reinterpret_cast<floatx4*>(o) = *reinterpret_cast<const floatx4*>(src);
+        *reinterpret_cast<floatx4*>(o + 4) = *reinterpret_cast<const floatx4*>(src + 4);
+      }
+    } else {
+      for (int e = 0; e < 8 && c0 + e < n; ++e)
+        o[e] = dtype == SG_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(W)[r * ldw + c0 + e])
+                                : static_cast<const float*>(W)[r * ldw + c0 + e];
+    }
   }
 }
 
@@ -319,10 +341,11 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
       reinterpret_cast<char*>(Err) + round_up((size_t)m * EGK * sizeof(float), 256));
 
   if (!(a.w_dtype == SG_F32 && static_cast<const void*>(a.W_out) == a.W)) {
-    const int64_t total = m * n;
-    const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(total, 256), 65536);
-    hipLaunchKernelGGL(convert_kernel, dim3(grid), dim3(256), 0, st, a.W_out, a.W, a.w_dtype, m,
-                       n, a.ldw);
+    const size_t el = a.w_dtype == SG_BF16 ? 2 : 4;
+    const int vec = (reinterpret_cast<uintptr_t>(a.W) % 16) == 0 && ((a.ldw * (int64_t)el) % 16) == 0 &&
+                    (reinterpret_cast<uintptr_t>(a.W_out) % 16) == 0 && (n % 4) == 0;
+    const dim3 grid((unsigned)ceil_div(n, 2048), (unsigned)std::min<int64_t>(m, 8192));
+    hipLaunchKernelGGL(convert_kernel, grid, dim3(256), 0, st, a.W_out, a.W, a.w_dtype, m, n, a.ldw, vec);
     if (sg_status e = check_launch("prune convert")) return e;
   }
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(select_pass_kernel),
