@@ -43,15 +43,26 @@ namespace {
 constexpr int NB = kFactorNB;  // 128
 
 // ---- damping --------------------------------------------------------------
-__global__ __launch_bounds__(256) void damp_lambda_kernel(const float* __restrict__ H, int64_t n,
-                                                          double damp, float* lam_out,
-                                                          int32_t* info) {
-  __shared__ double red[256];
+// One workgroup of 1024 threads; each thread's diagonal entries (one cache
+// line apiece) are requested eight at a time before they are summed.
+__global__ __launch_bounds__(1024) void damp_lambda_kernel(const float* __restrict__ H, int64_t n,
+                                                           double damp, float* lam_out,
+                                                           int32_t* info) {
+  __shared__ double red[1024];
   double s = 0.0;
-  for (int64_t i = threadIdx.x; i < n; i += 256) s += (double)H[i * n + i];
+  for (int64_t i0 = threadIdx.x; i0 < n; i0 += 8 * 1024) {
+    float d[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + u * 1024;
+      d[u] = i < n ? H[i * n + i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += (double)d[u];
+  }
   red[threadIdx.x] = s;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
+  for (int w = 512; w > 0; w >>= 1) {
     if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
@@ -745,7 +756,7 @@ sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double dam
   float* Y = A + n_pad * n_pad;
   float* lam = Y + n_pad * n_pad;
 
-  hipLaunchKernelGGL(damp_lambda_kernel, dim3(1), dim3(256), 0, st, H, n, damp, lam, info);
+  hipLaunchKernelGGL(damp_lambda_kernel, dim3(1), dim3(1024), 0, st, H, n, damp, lam, info);
   if (sg_status e = check_launch("damping")) return e;
   const unsigned t64 = (unsigned)(n_pad / 64);
   hipLaunchKernelGGL(flip_init_kernel, dim3(t64, t64), dim3(256), 0, st, H, n, n_pad, lam, A, Y);
