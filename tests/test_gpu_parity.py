@@ -386,3 +386,28 @@ def test_degenerate_tiny_shapes(sg):
         Who, Mo, _ = oracle.prune(W.double().numpy(), U, 0.5, 4)
         assert np.array_equal(mask.cpu().numpy().astype(bool), Mo)
         assert _rel(Wh.cpu().numpy(), Who) <= 1e-4
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("off", [0, 1])
+def test_prune_padded_row_views(sg, dtype, off):
+    """W given as a row-major view with padded rows (ldw > n; off = 1 starts
+    it one element in, so its rows are not 16-byte aligned) prunes bitwise as
+    its contiguous copy.  n = 132 leaves a partial 8-column group at the end
+    of every row of the fp32 working copy."""
+    m, n, pad = 96, 132, 12
+    gen = torch.Generator().manual_seed(7)
+    X = torch.randn(2048, n, generator=gen).cuda()
+    H = torch.zeros(n, n, device="cuda")
+    sg.sg_hessian_accumulate(H, X)
+    Hinv, info = sg.sg_prepare_hinv(H, 0.01)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    big = torch.randn(m, n + pad, generator=gen).to(tdt).cuda()
+    W = big[:, off:off + n]
+    assert W.stride(0) == n + pad
+    ref_W, ref_mask = sg.sg_prune_layer(W.contiguous(), Hinv, 0.5, 128)
+    got_W, got_mask = sg.sg_prune_layer(W, Hinv, 0.5, 128)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    assert torch.equal(got_W, ref_W) and torch.equal(got_mask, ref_mask)
+    assert 0 < int(got_mask.sum()) < m * n
