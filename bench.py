@@ -65,11 +65,11 @@ def load_traffic(workload):
 
 
 def cpu_baseline(cfg, pattern, W_host, X_host_sample, n_tok_total, rows_sample, bits=0):
-    m_rows = W_host.shape[0]
     """The oracle as it stands, timed on host cores on a bounded sample of the
     same layer, scaled to one whole layer: Hessian on a token sample (scaled by
     tokens), the full n x n factor, the column sweep on a row sample (scaled
     by rows)."""
+    m_rows = W_host.shape[0]
     import numpy as np
 
     import oracle

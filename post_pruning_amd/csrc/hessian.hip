@@ -7,9 +7,14 @@
 //
 // bf16 path: 256x256 output tiles of the lower triangle only (the symmetric
 // result is mirrored on store), 8 waves per workgroup, each wave a 128x64
-// sub-tile of v_mfma_f32_16x16x32_bf16 (two waves per SIMD).  X tiles are staged through LDS in
-// column-major form (each LDS row = one channel, 64 consecutive tokens) by an
-// in-register 8x8 transpose, so every MFMA operand is one 16-byte LDS read.
+// sub-tile of v_mfma_f32_16x16x32_bf16 (two waves per SIMD).  Two kernels
+// stage X through LDS:
+//   * hess_bf16_dma_kernel (n % 8 == 0, the main path): token rows are copied
+//     as they lie in X straight from global memory into LDS by the LDS-DMA
+//     loads, and the operands are gathered by the transposing LDS read;
+//   * hess_bf16_kernel (any n): tiles are transposed in registers (8x8) and
+//     stored channel-major (each LDS row = one channel, 64 consecutive
+//     tokens), so every MFMA operand is one 16-byte LDS read.
 // When there are too few tiles to fill the 256 CUs the tokens are split; every
 // split writes its partial tile to the workspace and the last split to finish
 // sums all partials in split order (bitwise reproducible), then adds into H.
