@@ -57,8 +57,12 @@ def test_workspace_sizes_pure_host(sg):
     assert sg.sg_workspace_bytes(sg.SG_OP_PREPARE_HINV, 0, 1000) >= 2 * 1024 * 1024 * 4
     # Prune: select state + an m x 128 fp32 error block.
     assert sg.sg_workspace_bytes(sg.SG_OP_PRUNE, 4096, 4096, 0, 128) >= 4096 * 128 * 4
-    # Hessian: the small-n, many-token case splits the tokens.
-    assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 4096, 262144, 0) > 0
+    # Hessian: the small-n, many-token case splits the tokens: 136 lower
+    # 256x256 tiles in 7 splits (4 full-ish rounds of 256 workgroups), one
+    # fp32 partial tile per split and tile after a 256-byte aligned counter
+    # array.
+    tiles = 16 * 17 // 2
+    assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 4096, 262144, 0) == 768 + tiles * 7 * 256 * 256 * 4
     # ... and the large-n case needs no split.
     assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 28672, 32768, 0) == 0
     assert sg.sg_workspace_bytes(sg.SG_OP_RECON, 64, 128, 512, 0) >= 8
