@@ -1,7 +1,7 @@
 """fp64 CPU oracle of the SparseGPT layer solver (test infrastructure only).
 
 Every function below is the plain definition, or the algorithm's steps in the
-pages' order, in float64 with numpy/scipy library primitives as steps.  No
+pages' order, in float64 with numpy / PyTorch-CPU library primitives as steps.  No
 blocking, batching or reordering beyond what the method itself states.
 
 Notation: W is m x n (rows = output channels, columns = input channels, Y = WX);
@@ -16,7 +16,7 @@ from dataclasses import dataclass
 from typing import Iterable, Optional
 
 import numpy as np
-import scipy.linalg
+import torch
 
 
 # ----------------------------------------------------------------------------
@@ -123,17 +123,17 @@ def inverse_upper_factor(Hd: np.ndarray) -> np.ndarray:
     """U = the upper-triangular Cholesky factor of H_d^{-1} (H_d^{-1} = U^T U).
 
     The pages only say the error is estimated from the inverse Hessian ([SGR]
-    section 8).  Textbook route, three library steps: Cholesky of H_d, the
-    inverse from it, Cholesky of the inverse, transposed to upper form.
+    section 8).  Textbook route, three library steps (LAPACK through PyTorch's
+    CPU fp64 linear algebra): Cholesky of H_d, the inverse from that factor,
+    Cholesky of the inverse, transposed to upper form.
     Row j of U satisfies U_jj * U[j, j:] = first row of (H_d[j:, j:])^{-1},
     i.e. it carries the inverse Hessian of the still-unprocessed columns.
     """
-    n = Hd.shape[0]
-    L = np.linalg.cholesky(Hd)
-    Linv = scipy.linalg.solve_triangular(L, np.eye(n), lower=True)
-    Hinv = Linv.T @ Linv
+    Hd_t = torch.from_numpy(np.ascontiguousarray(Hd, dtype=np.float64))
+    L = torch.linalg.cholesky(Hd_t)          # H_d = L L^T
+    Hinv = torch.cholesky_inverse(L)         # H_d^{-1} from its Cholesky factor
     Hinv = 0.5 * (Hinv + Hinv.T)
-    return np.linalg.cholesky(Hinv).T
+    return torch.linalg.cholesky(Hinv).T.contiguous().numpy()
 
 
 # ----------------------------------------------------------------------------
