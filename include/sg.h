@@ -28,15 +28,21 @@
  *          alignment 256 bytes).  Matrices are row-major with the stated
  *          leading dimension (in elements).
  * Streams: `stream` is a hipStream_t (NULL = the default stream).  Every call
- *          only enqueues work on it and returns; results are valid once the
- *          stream is synchronised.  No call synchronises the device.
+ *          only enqueues work on it (and, for sg_prepare_hinv, on a second
+ *          stream the caller may pass) and returns; results are valid once
+ *          `stream` is synchronised.  No call synchronises the device, and the
+ *          library creates no stream or event.
  * Errors:  host-detectable problems (null pointers, bad sizes or patterns,
  *          small workspace, unsupported dtype or alignment, a device that is
  *          not gfx950) return a non-zero sg_status BEFORE anything is
  *          enqueued; sg_last_error_message() then holds a thread-local
  *          explanation.  A failed launch returns SG_ERR_HIP.
- * Threads: calls are stateless apart from the thread-local message; calls on
- *          different streams with disjoint buffers may run concurrently.
+ * Threads: the library keeps no state across calls beyond the thread-local
+ *          message and a per-device memo of the architecture check (both
+ *          guarded).  Calls
+ *          on different streams with disjoint buffers (and, for
+ *          sg_prepare_hinv, distinct update streams and events) may run
+ *          concurrently.
  * Dtypes:  SG_F32 = IEEE binary32, SG_BF16 = bfloat16 (upper 16 bits of a
  *          binary32), both read and widened exactly to fp32.
  */
@@ -50,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SG_ABI_VERSION 1
+#define SG_ABI_VERSION 2
 
 typedef int32_t sg_status;
 
@@ -95,7 +101,11 @@ enum {
  *   n      number of input channels, 1 <= n <= 65536.
  *   X      token-major chunk Xc[t, c] (t < T, c < n) with leading dimension
  *          ldx >= n; x_dtype SG_BF16 or SG_F32.  For SG_BF16 the pointer must
- *          be 16-byte aligned and ldx a multiple of 8.
+ *          be 16-byte aligned and ldx a multiple of 8; rows are read in
+ *          16-byte pieces up to n rounded up to a multiple of 8, so the buffer
+ *          must hold (T - 1) * ldx + round_up(n, 8) elements (a [T, ldx]
+ *          tensor or a column view of one does); the values in the padding
+ *          columns do not affect H.
  *   T      tokens in the chunk, T >= 1.
  *   workspace / ws_bytes: scratch for the token-split partial tiles; the size
  *          from sg_workspace_bytes(SG_OP_HESSIAN, 0, n, T, 0) gives the
@@ -135,10 +145,20 @@ sg_status sg_hessian_accumulate(float* H, int64_t n, const void* X,
  *          unspecified.
  *   workspace: sg_workspace_bytes(SG_OP_PREPARE_HINV, 0, n, 0, 0) bytes
  *          (two n_pad x n_pad fp32 matrices, n_pad = n rounded up to 128).
+ *   update_stream, event_a, event_b: optional (all NULL, or all three given):
+ *          a second hipStream_t on the same device, different from `stream`,
+ *          and two distinct hipEvent_t the caller created and owns.  Above
+ *          n = 4096 the trailing updates then run on update_stream beside the
+ *          panel chain on `stream`, ordered by the two events, and `stream`
+ *          waits for update_stream before the call's last kernel; with NULL
+ *          every kernel runs on `stream` (same result, bit for bit; slower at
+ *          large n).  Up to n = 4096 the three are not used.  Concurrent calls
+ *          must not share an update stream or an event.
  */
 sg_status sg_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp,
                           int32_t* info, void* workspace, size_t ws_bytes,
-                          void* stream);
+                          void* stream, void* update_stream, void* event_a,
+                          void* event_b);
 
 /*
  * sg_prune_layer -- sparse W_hat with W_hat X ~ W X.

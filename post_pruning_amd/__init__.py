@@ -55,7 +55,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     c_i32, c_i64, c_sz, c_vp, c_dbl = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
                                         ctypes.c_void_p, ctypes.c_double)
     lib.sg_hessian_accumulate.argtypes = [c_vp, c_i64, c_vp, c_i32, c_i64, c_i64, c_vp, c_sz, c_vp]
-    lib.sg_prepare_hinv.argtypes = [c_vp, c_vp, c_i64, c_dbl, c_vp, c_vp, c_sz, c_vp]
+    lib.sg_prepare_hinv.argtypes = [c_vp, c_vp, c_i64, c_dbl, c_vp, c_vp, c_sz, c_vp, c_vp, c_vp, c_vp]
     lib.sg_prune_layer.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_i32,
                                    c_dbl, c_i32, c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]
     lib.sg_reconstruction_error.argtypes = [c_vp, c_i32, c_vp, c_i32, c_i64, c_vp, c_i64, c_i64,
@@ -164,10 +164,22 @@ def sg_hessian_accumulate(H: torch.Tensor, X: torch.Tensor,
     return H
 
 
+# Above this n the factorisation's trailing updates can run on a second stream
+# (the library's fused single-stream form is used up to it either way).
+FACTOR_SPLIT_MIN_N = 4097
+
+
 def sg_prepare_hinv(H: torch.Tensor, damp: float = 0.01, Hinv: Optional[torch.Tensor] = None,
                     info: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Upper Cholesky factor of (H + damp*mean(diag H) I)^{-1}; returns (Hinv, info)."""
+                    workspace: Optional[torch.Tensor] = None,
+                    update_stream: Union[str, None, "torch.cuda.Stream"] = "auto",
+                    ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Upper Cholesky factor of (H + damp*mean(diag H) I)^{-1}; returns (Hinv, info).
+
+    ``update_stream``: "auto" takes a stream from torch's pool and two fresh
+    events for this call when n > 4096 (the trailing updates then overlap the
+    panel chain); a torch.cuda.Stream uses that stream; None keeps every
+    kernel on the current stream.  The library itself creates no stream."""
     lib = load_library()
     _require_cuda(H)
     n = H.shape[0]
@@ -179,8 +191,25 @@ def sg_prepare_hinv(H: torch.Tensor, damp: float = 0.01, Hinv: Optional[torch.Te
         info = torch.empty(1, dtype=torch.int32, device=H.device)
     need = sg_workspace_bytes(SG_OP_PREPARE_HINV, 0, n, 0, 0)
     ws, nb = _workspace(need, H.device, workspace)
+    side = ev_a = ev_b = None
+    if isinstance(update_stream, str):
+        if update_stream != "auto":
+            raise ValueError("update_stream must be 'auto', None or a torch.cuda.Stream")
+        if n >= FACTOR_SPLIT_MIN_N:
+            side = torch.cuda.Stream(device=H.device)
+    else:
+        side = update_stream
+    if side is not None:
+        # events owned by this call (created by their first record)
+        ev_a, ev_b = torch.cuda.Event(), torch.cuda.Event()
+        ev_a.record(side)
+        ev_b.record(side)
     _check(lib.sg_prepare_hinv(_ptr(Hinv), _ptr(H), n, float(damp), _ptr(info), _ptr(ws), nb,
-                               ctypes.c_void_p(_stream(H.device))), "sg_prepare_hinv")
+                               ctypes.c_void_p(_stream(H.device)),
+                               None if side is None else ctypes.c_void_p(side.cuda_stream),
+                               None if ev_a is None else ctypes.c_void_p(ev_a.cuda_event),
+                               None if ev_b is None else ctypes.c_void_p(ev_b.cuda_event)),
+           "sg_prepare_hinv")
     return Hinv, info
 
 

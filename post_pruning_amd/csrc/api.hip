@@ -122,7 +122,8 @@ sg_status sg_hessian_accumulate(float* H, int64_t n, const void* X, int32_t x_dt
 }
 
 sg_status sg_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp, int32_t* info,
-                          void* workspace, size_t ws_bytes, void* stream) {
+                          void* workspace, size_t ws_bytes, void* stream, void* update_stream,
+                          void* event_a, void* event_b) {
   g_last_error.clear();
   if (!Hinv || !H || !info) return set_error(SG_ERR_INVALID_ARGUMENT, "Hinv, H and info must not be NULL");
   if (n < 1 || n > 65536) return set_error(SG_ERR_INVALID_ARGUMENT, "n=%lld out of [1, 65536]", (long long)n);
@@ -135,8 +136,16 @@ sg_status sg_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp, i
     return set_error(SG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
   if (!aligned(workspace, 256))
     return set_error(SG_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  const int given = (update_stream != nullptr) + (event_a != nullptr) + (event_b != nullptr);
+  if (given != 0 && given != 3)
+    return set_error(SG_ERR_INVALID_ARGUMENT, "update_stream, event_a and event_b go together (all or none)");
+  if (given == 3 && (update_stream == stream || event_a == event_b))
+    return set_error(SG_ERR_INVALID_ARGUMENT,
+                     "update_stream must differ from stream, and event_a from event_b");
   if (sg_status e = check_device()) return e;
-  return launch_prepare_hinv(Hinv, H, n, damp, info, workspace, static_cast<hipStream_t>(stream));
+  return launch_prepare_hinv(Hinv, H, n, damp, info, workspace, static_cast<hipStream_t>(stream),
+                             static_cast<hipStream_t>(update_stream), static_cast<hipEvent_t>(event_a),
+                             static_cast<hipEvent_t>(event_b));
 }
 
 static sg_status prune_common(float* W_out, uint8_t* mask_out, uint8_t* codes_out, float* scale_out,

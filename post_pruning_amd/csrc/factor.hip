@@ -30,12 +30,11 @@
 // where R is the running right-hand side of L X = I, kept transposed in the
 // upper block triangle of Y (R starts as I).  Look-ahead: block column k+1
 // of the update goes first (one short launch); panel k+1 then runs on the
-// caller's stream while the rest of the update runs on a second stream.
+// caller's stream while the rest of the update runs beside it (in the same
+// launch up to n = 4096, else on a second stream the caller provides).
 #include "gemm_x6.h"
 
 #include <math.h>
-
-#include <mutex>
 
 namespace sg {
 namespace {
@@ -599,39 +598,6 @@ __global__ __launch_bounds__(256, 2) void rest_update_kernel(float* __restrict__
   update_body(reinterpret_cast<float*>(ldsb), A, Y, n_pad, k, nblk, UPD_REST, blockIdx.x);
 }
 
-// A second stream per device for the trailing updates, with the two events
-// that order it against the caller's stream; one factorisation at a time
-// per device enqueues on it.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t ev_panel = nullptr, ev_rest = nullptr;
-  std::mutex mu;
-};
-constexpr int kMaxDevices = 64;
-SideStream g_side[kMaxDevices];
-std::mutex g_side_init;
-
-sg_status side_stream(SideStream*& out) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-    return set_error(SG_ERR_HIP, "factor: no current device (or device index >= %d)", kMaxDevices);
-  SideStream& ss = g_side[dev];
-  std::lock_guard<std::mutex> g(g_side_init);
-  if (!ss.s) {
-    hipStream_t s = nullptr;
-    hipEvent_t a = nullptr, b = nullptr;
-    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess)
-      return set_error(SG_ERR_HIP, "factor: creating the update stream or its events failed");
-    ss.ev_panel = a;
-    ss.ev_rest = b;
-    ss.s = s;
-  }
-  out = &ss;
-  return SG_OK;
-}
-
 // The panel chain (factor A_kk, invert it, transform the block column) is
 // the critical path of the factorisation at moderate n.  The transform is
 // split over 128 / R workgroups per block (each repeats the 128 x 128
@@ -665,19 +631,22 @@ sg_status run_factor_fused(float* A, float* Y, int64_t n_pad, int nblk, int64_t 
   return SG_OK;
 }
 
-// Two streams: the rest of each step's update runs on the update stream with
-// two workgroups per CU instead of sharing a launch (and its 135 KB of LDS
-// per workgroup) with the panel.
+// Two streams: the rest of each step's update runs on the caller's update
+// stream with two workgroups per CU instead of sharing a launch (and its
+// 135 KB of LDS per workgroup) with the panel.  The two caller events order
+// the streams: ev_panel after each panel, ev_rest after each rest update.
+struct SideStream {
+  hipStream_t s;
+  hipEvent_t ev_panel, ev_rest;
+};
+
 template <int R>
 sg_status run_factor_split(float* A, float* Y, int64_t n_pad, int nblk, int64_t n, int32_t* info,
-                           hipStream_t st) {
+                           hipStream_t st, const SideStream* ss) {
   constexpr int parts = NB / R;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(panel_kernel<R>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PanelLds)) != hipSuccess)
     return set_error(SG_ERR_HIP, "hipFuncSetAttribute(panel kernel) failed");
-  SideStream* ss = nullptr;
-  if (sg_status e = side_stream(ss)) return e;
-  std::lock_guard<std::mutex> g(ss->mu);
   const auto api = [](hipError_t r, const char* what) -> sg_status {
     return r == hipSuccess ? SG_OK : set_error(SG_ERR_HIP, "factor: %s failed", what);
   };
@@ -749,7 +718,8 @@ size_t factor_ws_bytes(int64_t n) {
 }
 
 sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp, int32_t* info,
-                              void* ws, hipStream_t st) {
+                              void* ws, hipStream_t st, hipStream_t side, hipEvent_t ev_a,
+                              hipEvent_t ev_b) {
   const int64_t n_pad = round_up(n, NB);
   const int nblk = (int)(n_pad / NB);
   float* A = static_cast<float*>(ws);
@@ -768,12 +738,17 @@ sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double dam
   // where the update's workgroups delay the panel's).  At larger n the
   // trailing update sets the time: one panel workgroup per block, and the
   // update on its own stream at two workgroups per CU (n = 28672: 150 ms
-  // against 182 ms in the shared launch).
+  // against 182 ms in the shared launch).  Without a caller update stream
+  // the single-stream fused form serves every n.
   sg_status e;
-  if (nblk * 8 <= kNumCU)
+  if (nblk * 8 <= kNumCU) {
     e = run_factor_fused<32>(A, Y, n_pad, nblk, n, info, st);
-  else
-    e = run_factor_split<128>(A, Y, n_pad, nblk, n, info, st);
+  } else if (side != nullptr) {
+    const SideStream ss{side, ev_a, ev_b};
+    e = run_factor_split<128>(A, Y, n_pad, nblk, n, info, st, &ss);
+  } else {
+    e = run_factor_fused<128>(A, Y, n_pad, nblk, n, info, st);
+  }
   if (e != SG_OK) return e;
   const unsigned tn = (unsigned)ceil_div(n, 64);
   hipLaunchKernelGGL(finalize_kernel, dim3(tn, tn), dim3(256), 0, st, Y, n, n_pad, Hinv);

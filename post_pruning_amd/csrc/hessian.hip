@@ -7,14 +7,12 @@
 //
 // bf16 path: 256x256 output tiles of the lower triangle only (the symmetric
 // result is mirrored on store), 8 waves per workgroup, each wave a 128x64
-// sub-tile of v_mfma_f32_16x16x32_bf16 (two waves per SIMD).  Two kernels
-// stage X through LDS:
-//   * hess_bf16_dma_kernel (n % 8 == 0, the main path): token rows are copied
-//     as they lie in X straight from global memory into LDS by the LDS-DMA
-//     loads, and the operands are gathered by the transposing LDS read;
-//   * hess_bf16_kernel (any n): tiles are transposed in registers (8x8) and
-//     stored channel-major (each LDS row = one channel, 64 consecutive
-//     tokens), so every MFMA operand is one 16-byte LDS read.
+// sub-tile of v_mfma_f32_16x16x32_bf16 (two waves per SIMD).  Token rows are
+// copied as they lie in X straight from global memory into LDS by the LDS-DMA
+// loads, and the operands are gathered by the transposing LDS read.  Rows are
+// read in 16-byte chunks up to n rounded up to 8 channels (inside the row:
+// the ABI asks for ldx % 8 == 0); channels past n only feed outputs past n,
+// which are never stored.
 // When there are too few tiles to fill the 256 CUs the tokens are split; every
 // split writes its partial tile to the workspace and the last split to finish
 // sums all partials in split order (bitwise reproducible), then adds into H.
@@ -36,8 +34,7 @@ namespace sg {
 namespace {
 
 constexpr int HT = kHessTile;          // 256
-constexpr int HBK = 64;                // tokens per LDS stage
-constexpr int HROWB = HBK * 2 + 16;    // LDS bytes per channel row (padded)
+constexpr int HSPLIT_ALIGN = 64;     // tokens: split boundaries are multiples of this
 constexpr int HTHREADS = 512;
 constexpr int kMinTokPerSplit = 4096;
 
@@ -84,266 +81,8 @@ __global__ void zero_u32_kernel(unsigned* p, int64_t cnt) {
   if (i < cnt) p[i] = 0u;
 }
 
-__device__ inline float agent_load(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <bool RAGGED>
-__global__ __launch_bounds__(HTHREADS) void hess_bf16_kernel(
-    float* __restrict__ H, int n, const uint16_t* __restrict__ X, int64_t T,
-    int64_t ldx, int64_t tiles, int splits, int64_t tps, int group,
-    float* __restrict__ part, unsigned* __restrict__ counters) {
-  // Two LDS stages (double buffer), each holding the I-block and the J-block.
-  // Separate arrays, so the compiler can tell the stage being written from the
-  // stage being read and interleave the two.
-  __shared__ __attribute__((aligned(16))) unsigned char lds0[2 * HT * HROWB];
-  __shared__ __attribute__((aligned(16))) unsigned char lds1[2 * HT * HROWB];
-  __shared__ int s_last;
-
-  // XCD share: tiles [k0, k1) of the grouped order, times all splits,
-  // split-major.  Shares differ by at most one tile; the few workgroups past
-  // a short share exit at once.
-  const int xcd = blockIdx.x & 7;
-  const int64_t jx = blockIdx.x >> 3;
-  const int64_t k0 = tiles * xcd / 8, k1 = tiles * (xcd + 1) / 8;
-  const int64_t cnt = k1 - k0;
-  if (jx >= cnt * splits) return;
-  const int split = (int)(jx / cnt);
-  const int64_t ti = k0 + (jx - (int64_t)split * cnt);
-  const int64_t item = (int64_t)split * tiles + ti;
-  int I, J;
-  grouped_decode(ti, (int)ceil_div((int64_t)n, HT), group, I, J);
-  const bool diag = (I == J);
-  const int i0 = I * HT, j0 = J * HT;
-  const int64_t t_begin = (int64_t)split * tps;
-  const int64_t t_end = min(T, t_begin + tps);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wi = wave >> 2;  // 128-row half of the tile
-  const int wj = wave & 3;   // 64-column quarter
-
-  // Loader role: threads 0..255 stage the I-block, 256..511 the J-block (a
-  // second copy of the I-block on diagonal tiles, which keeps every step
-  // free of branches), one 8 tokens x 8 channels block each per stage.
-  const int op = tid >> 8;
-  const int tb = tid & 7;          // 8-token group inside the stage
-  const int cb = (tid & 255) >> 3; // 8-channel group inside the tile
-  const int colbase = (op == 0 ? i0 : j0) + cb * 8;
-  const bool colok = colbase < n;
-
-  floatx4 acc[8][4];
-#pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 r[8];
-
-  // Generic stage load (first and last stages): clamped, always in-bounds
-  // addresses (rows past the token range re-read the last row, channel groups
-  // past n re-read the last group); out-of-range data is zeroed when the stage
-  // is written to LDS.  RAGGED (n not a multiple of 8) loads per element.
-  auto gload = [&](int64_t t0) {
-    const char* base = reinterpret_cast<const char*>(X + t0 * ldx);
-    const int last = (int)min<int64_t>(HBK - 1, t_end - 1 - t0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int tr = tb * 8 + i;
-      tr = tr < last ? tr : last;
-      if constexpr (!RAGGED) {
-        const int colc = colok ? colbase : n - 8;
-        const uint32_t off = (uint32_t)tr * (uint32_t)(ldx * 2) + (uint32_t)colc * 2u;
-        r[i] = *reinterpret_cast<const u32x4*>(base + off);
-      } else {
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        const uint16_t* src =
-            reinterpret_cast<const uint16_t*>(base + (uint32_t)tr * (uint32_t)(ldx * 2));
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (colbase + e < n) v[e >> 1] |= (uint32_t)src[colbase + e] << (16 * (e & 1));
-        r[i] = v;
-      }
-    }
-  };
-
-  // Transpose the 8x8 block in registers and store it channel-major: one
-  // 16-byte LDS write per pair of channels (d selects channels 2d, 2d+1).
-  auto lstore_pair = [&](unsigned char* dst, int d) {
-    u32x4 lo, hi;
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const uint32_t a0 = r[2 * qq][d], a1 = r[2 * qq + 1][d];
-      lo[qq] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-      hi[qq] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-    }
-    *reinterpret_cast<u32x4*>(dst + (cb * 8 + 2 * d) * HROWB + tb * 16) = lo;
-    *reinterpret_cast<u32x4*>(dst + (cb * 8 + 2 * d + 1) * HROWB + tb * 16) = hi;
-  };
-
-  auto lstore = [&](int64_t t0, unsigned char* buf) {
-    unsigned char* dst = buf + op * HT * HROWB;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool ok = colok && (t0 + tb * 8 + i) < t_end;
-      if (!ok) r[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int d = 0; d < 4; ++d) lstore_pair(dst, d);
-  };
-
-  // MFMA operands: lane l reads 16 bytes (8 tokens) of channel row l%16 at
-  // token offset 8*(l/16) inside the 32-token half ks of the stage.
-  const int koff = (lane >> 4) * 16;
-  const int arow = (wi * 128 + (lane & 15)) * HROWB + koff;
-  const int brow = HT * HROWB + (wj * 64 + (lane & 15)) * HROWB + koff;
-
-  auto compute = [&](const unsigned char* buf, int ks) {
-    bf16x8 fb[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      fb[c] = *reinterpret_cast<const bf16x8*>(buf + brow + c * 16 * HROWB + ks * 64);
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      const bf16x8 fa = *reinterpret_cast<const bf16x8*>(buf + arow + a * 16 * HROWB + ks * 64);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[c], acc[a][c], 0, 0, 0);
-    }
-  };
-
-  // Steady-state step (all tokens of the stages involved valid): compute
-  // stage s from `cur`, write stage s+1 (in registers) to `nxt`, fetch stage
-  // s+2 into registers.  No branches and no bounds selects; the scheduling
-  // groups interleave the LDS writes, the transposes and the global loads
-  // with the 64 MFMAs of the step so that they issue while the matrix core
-  // is busy.
-  const uint32_t loff =
-      (uint32_t)(tb * 8) * (uint32_t)(ldx * 2) + (uint32_t)(colok ? colbase : n - 8) * 2u;
-  auto fast_step = [&](const unsigned char* cur, unsigned char* nxt, int64_t t_load) {
-    // half 1: 32 MFMA (k = 0..31 of the stage) with their 12 operand reads,
-    // interleaved with the 32 transposes and 8 LDS writes of the next stage
-    __builtin_amdgcn_sched_barrier(0);
-    compute(cur, 0);
-    unsigned char* dst = nxt + op * HT * HROWB;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) lstore_pair(dst, d);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      if (g < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // half 2: 32 MFMA (k = 32..63) with their operand reads, interleaved with
-    // the 8 global loads of stage s+2 (into the registers just written out)
-    const char* base = reinterpret_cast<const char*>(X + t_load * ldx);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      r[i] = *reinterpret_cast<const u32x4*>(base + (size_t)i * (size_t)(ldx * 2) + loff);
-    compute(cur, 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-      if (g < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-  };
-
-  // Software pipeline: stage s is computed from LDS buffer s%2 while stage
-  // s+1 (already in registers) is written to the other buffer, and stage s+2
-  // is fetched into registers.  One barrier per stage.
-  const int64_t ntok = t_end > t_begin ? t_end - t_begin : 0;
-  const int64_t nsteps = ceil_div(ntok, HBK);
-  const int64_t nfull = ntok / HBK;
-  if (nsteps > 0) {
-    gload(t_begin);
-    lstore(t_begin, lds0);
-    if (nsteps > 1) gload(t_begin + HBK);
-    __syncthreads();
-  }
-  int64_t step = 0;
-  if constexpr (!RAGGED) {
-    // pairs of steady-state steps: step s + 2 (and s + 3) must be full stages
-    for (; step + 3 < nfull; step += 2) {
-      fast_step(lds0, lds1, t_begin + (step + 2) * HBK);
-      fast_step(lds1, lds0, t_begin + (step + 3) * HBK);
-    }
-  }
-  for (; step < nsteps; ++step) {
-    unsigned char* cur = (step & 1) ? lds1 : lds0;
-    unsigned char* nxt = (step & 1) ? lds0 : lds1;
-    compute(cur, 0);
-    if (step + 1 < nsteps) {
-      lstore(t_begin + (step + 1) * HBK, nxt);
-      if (step + 2 < nsteps) gload(t_begin + (step + 2) * HBK);
-    }
-    compute(cur, 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue -----------------------------------------------------------
-  if (splits > 1) {
-    // Partial tile layout: per (wave, a, c) slot, 64 lanes x float4.
-    floatx4* mine = reinterpret_cast<floatx4*>(part + (size_t)item * (HT * HT));
-#pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) mine[(wave * 32 + a * 4 + c) * 64 + lane] = acc[a][c];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned old = atomicAdd(&counters[ti], 1u);
-      s_last = (old == (unsigned)(splits - 1)) ? 1 : 0;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    // Sum the partials of every split of this tile in split order (the own
-    // partial is re-read too, so the order and the result do not depend on
-    // which split finished last).
-    for (int sp = 0; sp < splits; ++sp) {
-      const floatx4* other =
-          reinterpret_cast<const floatx4*>(part + ((size_t)sp * tiles + ti) * (HT * HT));
-#pragma unroll
-      for (int a = 0; a < 8; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const floatx4 pv = other[(wave * 32 + a * 4 + c) * 64 + lane];
-          acc[a][c] = (sp == 0) ? pv : acc[a][c] + pv;
-        }
-    }
-    if (tid == 0) counters[ti] = 0u;
-  }
-
-#pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = i0 + wi * 128 + a * 16 + (lane >> 4) * 4 + v;
-        const int col = j0 + wj * 64 + c * 16 + (lane & 15);
-        if (row >= n || col >= n) continue;
-        if (diag && row < col) continue;
-        const size_t lo = (size_t)row * n + col;
-        const float val = H[lo] + acc[a][c][v];
-        H[lo] = val;
-        if (row != col) H[(size_t)col * n + row] = val;
-      }
-}
-
-// bf16 path for n % 8 == 0: the same tiles and wave layout, with the X
-// stages copied straight from global memory into LDS by the LDS-DMA loads
-// (no register staging, no transposes in VALU).  A stage is 32 tokens; in
+// The X stages are copied straight from global memory into LDS by the
+// LDS-DMA loads (no register staging, no transposes in VALU).  A stage is 32 tokens; in
 // LDS each token is one 1040-byte row holding the tile's I-panel (256
 // channels) and J-panel (256 channels) as they lie in X, plus 16 bytes of
 // padding so that consecutive tokens start 16 bytes apart in the LDS banks.
@@ -430,10 +169,12 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
   // Copy role: wave w copies token rows 4w..4w+3 of every stage, one row per
   // instruction; lanes 0..31 fetch the I-panel's 32 16-byte chunks, lanes
   // 32..63 the J-panel's (on diagonal tiles a second copy of the I-panel).
-  // Channel chunks past n re-read the last chunk: those channels only feed
-  // outputs beyond n, which are never stored.
+  // Chunks past n8 (n rounded up to 8, still inside the row since ldx is a
+  // multiple of 8) re-read the last chunk: channels past n only feed outputs
+  // beyond n, which are never stored.
+  const int n8 = (n + 7) & ~7;
   int col = ((lane >> 5) ? j0 : i0) + (lane & 31) * 8;
-  col = col < n ? col : n - 8;
+  col = col < n8 ? col : n8 - 8;
   const uint32_t dcol = (uint32_t)col * 2u;
   auto copy_stage = [&](unsigned char* buf, int64_t s) {
     const int64_t tok0 = t_begin + s * DK + wave * 4;
@@ -562,7 +303,11 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
     compute(cur);
   }
 
-  // ---- epilogue (same layout as the register-staged kernel) ---------------
+  // ---- epilogue -----------------------------------------------------------
+  // Token splits: each split writes its partial tile (per (wave, a, c) slot,
+  // 64 lanes x float4); the last split to arrive sums every partial in split
+  // order (its own re-read too, so the result does not depend on which split
+  // finished last) and adds into H.
   if (splits > 1) {
     floatx4* mine = reinterpret_cast<floatx4*>(part + (size_t)item * (HT * HT));
 #pragma unroll
@@ -691,7 +436,7 @@ HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws) {
     }
   }
   p.splits = best_s;
-  p.tok_per_split = round_up(ceil_div(T, best_s), HBK);
+  p.tok_per_split = round_up(ceil_div(T, best_s), HSPLIT_ALIGN);
   // Recompute the split count actually needed with the rounded split size.
   p.splits = (int)std::max<int64_t>(1, ceil_div(T, p.tok_per_split));
   p.ws_bytes = p.splits > 1 ? cnt_bytes + tile_bytes * (size_t)p.tiles * p.splits : 0;
@@ -718,14 +463,9 @@ sg_status launch_hessian_bf16(float* H, int64_t n, const uint16_t* X, int64_t T,
     if (sg_status e = check_launch("hessian counters")) return e;
   }
   const int64_t grid = plan.grid;
-  if (n % 8 == 0)
-    hipLaunchKernelGGL(hess_bf16_dma_kernel, dim3((unsigned)grid), dim3(HTHREADS), 0, st, H,
-                       (int)n, X, T, ldx, plan.tiles, plan.splits, plan.tok_per_split, plan.group,
-                       part, counters);
-  else
-    hipLaunchKernelGGL(hess_bf16_kernel<true>, dim3((unsigned)grid), dim3(HTHREADS), 0, st, H,
-                       (int)n, X, T, ldx, plan.tiles, plan.splits, plan.tok_per_split, plan.group,
-                       part, counters);
+  hipLaunchKernelGGL(hess_bf16_dma_kernel, dim3((unsigned)grid), dim3(HTHREADS), 0, st, H,
+                     (int)n, X, T, ldx, plan.tiles, plan.splits, plan.tok_per_split, plan.group,
+                     part, counters);
   return check_launch("hessian bf16");
 }
 

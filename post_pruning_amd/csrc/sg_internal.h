@@ -38,7 +38,8 @@ sg_status check_launch(const char* what);
 // ---------------------------------------------------------------------------
 size_t factor_ws_bytes(int64_t n);
 sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp,
-                              int32_t* info, void* ws, hipStream_t st);
+                              int32_t* info, void* ws, hipStream_t st, hipStream_t side,
+                              hipEvent_t ev_a, hipEvent_t ev_b);
 
 // ---------------------------------------------------------------------------
 // Prune
@@ -69,7 +70,6 @@ struct PruneArgs {
 };
 size_t prune_ws_bytes(int64_t m, int64_t n, int blocksize);
 sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st);
-
 // ---------------------------------------------------------------------------
 // 2:4 compressed export
 // ---------------------------------------------------------------------------

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings(sg):
-    assert sg.sg_abi_version() == 1
+    assert sg.sg_abi_version() == 2
     assert sg.sg_status_string(0) == "SG_OK"
     assert sg.sg_status_string(3) == "SG_ERR_WORKSPACE"
     assert sg.sg_status_string(99) == "SG_ERR_UNKNOWN"
@@ -81,7 +81,7 @@ def test_null_pointers_rejected_before_device(sg):
     st = lib.sg_hessian_accumulate(None, 16, None, sg.SG_BF16, 8, 16, None, 0, None)
     assert st == sg.SG_ERR_INVALID_ARGUMENT
     assert "NULL" in sg.sg_last_error_message()
-    st = lib.sg_prepare_hinv(None, None, 16, 0.01, None, None, 0, None)
+    st = lib.sg_prepare_hinv(None, None, 16, 0.01, None, None, 0, None, None, None, None)
     assert st == sg.SG_ERR_INVALID_ARGUMENT
     st = lib.sg_prune_layer(None, None, None, 0, 4, 4, 4, None, 0, 0.5, 0, 1, 4, None, None, 0, None)
     assert st == sg.SG_ERR_INVALID_ARGUMENT
@@ -119,17 +119,32 @@ def test_hessian_validation(sg, args, code):
     assert st == code, sg.sg_last_error_message()
 
 
+S1, S2, E1, E2 = (ctypes.c_void_p(a) for a in (0x5000, 0x6000, 0x7000, 0x8000))
+
+
 @pytest.mark.parametrize("args,code", [
     (dict(damp=-0.1), 1), (dict(damp=float("nan")), 1), (dict(alias=True), 1),
     (dict(ws=0), 3),
+    # the update stream and its two events go together, all distinct
+    (dict(side=(S2, None, None)), 1), (dict(side=(S2, E1, None)), 1),
+    (dict(side=(None, E1, E2)), 1), (dict(side=(S1, E1, E2)), 1), (dict(side=(S2, E1, E1)), 1),
 ])
 def test_prepare_validation(sg, args, code):
-    a = dict(damp=0.01, alias=False, ws=10 ** 9)
+    a = dict(damp=0.01, alias=False, ws=10 ** 9, side=(None, None, None))
     a.update(args)
     Hinv = FAKE if a["alias"] else ctypes.c_void_p(0x2000)
     st = _lib(sg).sg_prepare_hinv(Hinv, FAKE, 64, a["damp"], FAKE, ctypes.c_void_p(0x10000),
-                                  a["ws"], None)
+                                  a["ws"], S1, *a["side"])
     assert st == code, sg.sg_last_error_message()
+
+
+def test_library_creates_no_stream_or_event():
+    # Every stream and event the library enqueues on is the caller's.
+    csrc = os.path.join(ROOT, "post_pruning_amd", "csrc")
+    for f in os.listdir(csrc):
+        text = open(os.path.join(csrc, f)).read()
+        for call in ("hipStreamCreate", "hipEventCreate", "hipExtStreamCreate"):
+            assert call not in text, (f, call)
 
 
 @pytest.mark.parametrize("args,code", [

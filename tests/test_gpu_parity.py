@@ -140,27 +140,61 @@ def test_hessian_and_factor(sg, case):
     assert _rel(Ug, ref["U"]) <= 1e-4
 
 
-def test_factor_update_stream_path(sg):
-    """Above n = 4096 the factorisation runs each step's trailing update on a
-    second stream (the panel and the update in separate launches): U against
-    the oracle as at the smaller sizes, and bit-for-bit repeatable."""
-    n, T = 4224, 6144  # 33 panels of 128
-    rng = np.random.default_rng(4224)
+def _factor_case(seed, n=4224, T=6144):
+    rng = np.random.default_rng(seed)
     X = rng.standard_normal((T, n)) * np.exp(0.5 * rng.standard_normal(n))[None, :]
     H = X.T @ X
     Hd, _ = oracle.dampen(H, 0.01)
-    U = oracle.inverse_upper_factor(Hd)
-    Hg = torch.from_numpy(H.astype(np.float32)).cuda()
-    Hinv, info = sg.sg_prepare_hinv(Hg, 0.01)
-    torch.cuda.synchronize()
+    return H, oracle.inverse_upper_factor(Hd)
+
+
+def _check_factor(Hinv, info, U):
     assert int(info.item()) == 0
     Ug = Hinv.cpu().double().numpy()
     assert np.all(np.tril(Ug, -1) == 0.0)
     assert np.all(np.diag(Ug) > 0)
     assert _rel(Ug, U) <= 1e-4
+
+
+def test_factor_update_stream_path(sg):
+    """Above n = 4096 the factorisation runs each step's trailing update on a
+    second stream the caller provides (the panel and the update in separate
+    launches), or, without one, in the panel's launch on the caller's stream.
+    Both forms: U against the oracle as at the smaller sizes, bit-for-bit
+    repeatable, and bit-for-bit equal to each other."""
+    H, U = _factor_case(4224)  # 33 panels of 128
+    Hg = torch.from_numpy(H.astype(np.float32)).cuda()
+    Hinv, info = sg.sg_prepare_hinv(Hg, 0.01)  # "auto": a pool stream and two events
+    torch.cuda.synchronize()
+    _check_factor(Hinv, info, U)
     Hinv2, _ = sg.sg_prepare_hinv(Hg, 0.01)
     torch.cuda.synchronize()
     assert torch.equal(Hinv, Hinv2)
+    Hinv1, info1 = sg.sg_prepare_hinv(Hg, 0.01, update_stream=None)  # one stream
+    torch.cuda.synchronize()
+    _check_factor(Hinv1, info1, U)
+    assert torch.equal(Hinv, Hinv1)
+
+
+def test_factor_two_callers_two_streams(sg):
+    """Two factorisations above n = 4096 enqueued back to back on two caller
+    streams, each with its own update stream and events: the library holds
+    no stream of its own, so they overlap freely and each U matches its
+    oracle."""
+    cases = [_factor_case(s) for s in (4225, 4226)]
+    Hs = [torch.from_numpy(H.astype(np.float32)).cuda() for H, _ in cases]
+    mains = [torch.cuda.Stream() for _ in cases]
+    sides = [torch.cuda.Stream() for _ in cases]
+    torch.cuda.synchronize()
+    outs = []
+    for Hg, st, side in zip(Hs, mains, sides):
+        with torch.cuda.stream(st):
+            Hinv = torch.empty_like(Hg)
+            info = torch.empty(1, dtype=torch.int32, device="cuda")
+            outs.append(sg.sg_prepare_hinv(Hg, 0.01, Hinv=Hinv, info=info, update_stream=side))
+    torch.cuda.synchronize()
+    for (Hinv, info), (_, U) in zip(outs, cases):
+        _check_factor(Hinv, info, U)
 
 
 def _gpu_factor(sg, ref):
@@ -411,3 +445,29 @@ def test_prune_padded_row_views(sg, dtype, off):
     assert int(info.item()) == 0
     assert torch.equal(got_W, ref_W) and torch.equal(got_mask, ref_mask)
     assert 0 < int(got_mask.sum()) < m * n
+
+
+@pytest.mark.parametrize("ws", ["split", "none"])
+def test_hessian_bf16_ragged_padded_view(sg, ws):
+    """bf16 X with n % 8 != 0 given as a column view of a wider [T, 1008]
+    tensor (ldx = 1008).  The kernel reads each row in 16-byte pieces up to n
+    rounded up to 8 channels; the padding columns hold NaN, which must not
+    reach H.  Checked against the oracle with the intended token split and
+    with no workspace (no split)."""
+    n, ldx, T = 1001, 1008, 9000
+    gen = torch.Generator().manual_seed(1001)
+    scale = torch.exp(torch.randn(n, generator=gen))
+    Xv = (torch.randn(T, n, generator=gen) * scale).to(torch.bfloat16)
+    big = torch.full((T, ldx), float("nan"), dtype=torch.bfloat16)
+    big[:, :n] = Xv
+    Xg = big.cuda()[:, :n]
+    assert Xg.stride(0) == ldx and not Xg.is_contiguous()
+    need = sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, n, T, 0)
+    assert need > 0  # this shape splits the tokens when it may
+    H = _gpu_hessian(sg, Xg, n, T, workspace_bytes=need if ws == "split" else 0)
+    torch.cuda.synchronize()
+    Hg = H.cpu().double().numpy()
+    assert np.isfinite(Hg).all()
+    assert np.array_equal(Hg, Hg.T)
+    Ho = oracle.hessian([Xv.double().numpy()])
+    assert _rel(Hg, Ho) <= 1e-5
