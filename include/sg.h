@@ -39,7 +39,7 @@
  *          explanation.  A failed launch returns SG_ERR_HIP.
  * Threads: the library keeps no state across calls beyond the thread-local
  *          message and a per-device memo of the architecture check (both
- *          guarded).  Calls
+ *          guarded), plus the scratch array of sg_prune_layer_noalloc.  Calls
  *          on different streams with disjoint buffers (and, for
  *          sg_prepare_hinv, distinct update streams and events) may run
  *          concurrently.
@@ -87,6 +87,10 @@ enum {
 
 /* Most matrices one sg_prune_layers_shared call can stack. */
 #define SG_MAX_SEGMENTS 16
+
+/* Bytes of the device scratch array that sg_prune_layer_noalloc uses in place
+ * of a workspace (64 MiB: sg_prune_layer's workspace for m up to 21,600). */
+#define SG_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /*
  * sg_hessian_accumulate -- H += Xc^T Xc.
@@ -207,6 +211,32 @@ sg_status sg_prune_layer(float* W_out, uint8_t* mask_out, const void* W,
                          double sparsity, int32_t n_keep, int32_t m_group,
                          int32_t blocksize, const uint8_t* mask_in,
                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sg_prune_layer_noalloc -- sg_prune_layer without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments (minus workspace / ws_bytes), same results bit for bit and
+ * same error behaviour as sg_prune_layer.  The scratch comes from a device
+ * array of the library of SG_NOALLOC_SCRATCH_BYTES, one per GPU, held from
+ * the first call on that GPU until the process ends; the call itself
+ * allocates nothing (no hipMalloc, no allocating library routine).
+ * Limit: sg_workspace_bytes(SG_OP_PRUNE, m, n, 0, blocksize) must not exceed
+ * SG_NOALLOC_SCRATCH_BYTES (m <= 21,600 at any n), else SG_ERR_UNSUPPORTED
+ * before anything is enqueued.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (from different streams or threads) race and must be ordered by
+ * the caller.  Each call clears what it needs cleared itself, by kernels on
+ * `stream` (no memset), so consecutive calls need no reset in between.
+ */
+sg_status sg_prune_layer_noalloc(float* W_out, uint8_t* mask_out,
+                                 const void* W, int32_t w_dtype, int64_t m,
+                                 int64_t n, int64_t ldw, const float* Hinv,
+                                 int32_t pattern_kind, double sparsity,
+                                 int32_t n_keep, int32_t m_group,
+                                 int32_t blocksize, const uint8_t* mask_in,
+                                 void* stream);
 
 /*
  * sg_prune_quantize_layer -- sg_prune_layer with the kept weights also

@@ -32,6 +32,7 @@ SG_UNSTRUCTURED, SG_NM, SG_UNSTRUCTURED_ROW = 0, 1, 2
 SG_OP_HESSIAN, SG_OP_PREPARE_HINV, SG_OP_PRUNE, SG_OP_RECON = range(4)
 SG_MAX_BLOCKSIZE = 128
 SG_MAX_SEGMENTS = 16
+SG_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -67,11 +68,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sg_prune_layers_shared.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
                                            c_i64, c_i64, c_vp, c_i32, c_vp, c_i32, c_dbl, c_i32,
                                            c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]
+    lib.sg_prune_layer_noalloc.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_i32,
+                                           c_dbl, c_i32, c_i32, c_i32, c_vp, c_vp]
     lib.sg_prune_layer_vector.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_i32,
                                           c_dbl, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]
     for f in ("sg_hessian_accumulate", "sg_prepare_hinv", "sg_prune_layer",
               "sg_reconstruction_error", "sg_pack_two_four", "sg_prune_quantize_layer",
-              "sg_prune_layers_shared", "sg_prune_layer_vector"):
+              "sg_prune_layers_shared", "sg_prune_layer_vector", "sg_prune_layer_noalloc"):
         getattr(lib, f).restype = c_i32
     lib.sg_workspace_bytes.argtypes = [c_i32, c_i64, c_i64, c_i64, c_i32]
     lib.sg_workspace_bytes.restype = c_sz
@@ -249,6 +252,33 @@ def sg_prune_layer(W: torch.Tensor, Hinv: torch.Tensor, pattern: Union[float, st
     _check(lib.sg_prune_layer(_ptr(W_out), _ptr(mask_out), _ptr(W), _dtype_code(W), m, n, ldw,
                               _ptr(Hinv), kind, sp, nk, mg, int(blocksize), _ptr(mask_in), _ptr(ws),
                               nb, ctypes.c_void_p(_stream(W.device))), "sg_prune_layer")
+    return W_out, mask_out
+
+
+def sg_prune_layer_noalloc(W: torch.Tensor, Hinv: torch.Tensor, pattern: Union[float, str],
+                           blocksize: int = 128, mask_in: Optional[torch.Tensor] = None,
+                           W_out: Optional[torch.Tensor] = None,
+                           mask_out: Optional[torch.Tensor] = None):
+    """sg_prune_layer with the library's per-GPU scratch array in place of a
+    workspace (the C call allocates nothing; pass W_out and mask_out to keep
+    this wrapper from allocating them).  Calls overlapping on one GPU race."""
+    lib = load_library()
+    _require_cuda(W, Hinv, mask_in)
+    m, n = W.shape
+    ldw = _row_major(W, "W")
+    if Hinv.shape != (n, n) or Hinv.dtype != torch.float32 or not Hinv.is_contiguous():
+        raise ValueError("Hinv must be a contiguous [n, n] float32 tensor")
+    if mask_in is not None:
+        if mask_in.shape != (m, n) or not mask_in.is_contiguous() or mask_in.dtype != torch.uint8:
+            raise ValueError("mask_in must be a contiguous [m, n] uint8 tensor")
+    if W_out is None:
+        W_out = torch.empty(m, n, dtype=torch.float32, device=W.device)
+    if mask_out is None:
+        mask_out = torch.empty(m, n, dtype=torch.uint8, device=W.device)
+    kind, sp, nk, mg = parse_pattern(pattern)
+    _check(lib.sg_prune_layer_noalloc(_ptr(W_out), _ptr(mask_out), _ptr(W), _dtype_code(W), m, n, ldw,
+                                      _ptr(Hinv), kind, sp, nk, mg, int(blocksize), _ptr(mask_in),
+                                      ctypes.c_void_p(_stream(W.device))), "sg_prune_layer_noalloc")
     return W_out, mask_out
 
 

@@ -223,6 +223,30 @@ sg_status sg_prune_layer(float* W_out, uint8_t* mask_out, const void* W, int32_t
                       ws_bytes, stream);
 }
 
+sg_status sg_prune_layer_noalloc(float* W_out, uint8_t* mask_out, const void* W, int32_t w_dtype,
+                                 int64_t m, int64_t n, int64_t ldw, const float* Hinv,
+                                 int32_t pattern_kind, double sparsity, int32_t n_keep,
+                                 int32_t m_group, int32_t blocksize, const uint8_t* mask_in,
+                                 void* stream) {
+  g_last_error.clear();
+  if (!W_out || !W || !Hinv) return set_error(SG_ERR_INVALID_ARGUMENT, "W_out, W and Hinv must not be NULL");
+  if (m < 1 || n < 1) return set_error(SG_ERR_INVALID_ARGUMENT, "m and n must be >= 1");
+  if (blocksize < 1 || blocksize > SG_MAX_BLOCKSIZE)
+    return set_error(SG_ERR_UNSUPPORTED, "blocksize %d out of [1, %d]", blocksize, SG_MAX_BLOCKSIZE);
+  const size_t need = prune_ws_bytes(m, n, blocksize);
+  if (need > kNoAllocScratchBytes)
+    return set_error(SG_ERR_UNSUPPORTED,
+                     "m=%lld needs %zu bytes of scratch; sg_prune_layer_noalloc holds %zu "
+                     "(use sg_prune_layer with a workspace)",
+                     (long long)m, need, kNoAllocScratchBytes);
+  if (sg_status e = check_device()) return e;
+  void* ws = nullptr;
+  if (sg_status e = noalloc_scratch(&ws)) return e;
+  return prune_common(W_out, mask_out, nullptr, nullptr, nullptr, 0, W, w_dtype, m, n, ldw, nullptr, 1,
+                      Hinv, pattern_kind, sparsity, n_keep, m_group, blocksize, mask_in, ws,
+                      kNoAllocScratchBytes, stream);
+}
+
 sg_status sg_prune_quantize_layer(float* W_out, uint8_t* mask_out, uint8_t* codes_out, float* scale_out,
                                   float* zero_out, int32_t bits, const void* W, int32_t w_dtype,
                                   int64_t m, int64_t n, int64_t ldw, const float* Hinv,

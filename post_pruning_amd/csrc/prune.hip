@@ -25,6 +25,7 @@
 
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -323,6 +324,36 @@ sg_status launch_lazy(float* W, const float* E, const float* U, int64_t m, int64
 // the K extent is a multiple of 4 (U is read by the 4-byte transposed loader).
 bool lazy_vec(const float* E, int K) {
   return (reinterpret_cast<uintptr_t>(E) % 16) == 0 && (K % 4) == 0;
+}
+
+// Scratch of sg_prune_layer_noalloc: the prune workspace as a device array
+// of the library's own, for callers that cannot allocate.  Every GPU the
+// library runs on holds its own copy (at its own address) until the process
+// ends; host code reaches it only through the address hipGetSymbolAddress
+// returns on that device (the array's name is a host-side stand-in there).
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kScratchDevs = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevs];  // device address of `scratch`, per device
+}  // namespace
+
+sg_status noalloc_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return set_error(SG_ERR_HIP, "no current HIP device");
+  if (dev >= kScratchDevs) return set_error(SG_ERR_UNSUPPORTED, "device index %d too large", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return set_error(SG_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return SG_OK;
 }
 
 size_t prune_ws_bytes(int64_t m, int64_t n, int blocksize) {

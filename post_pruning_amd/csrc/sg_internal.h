@@ -69,7 +69,12 @@ struct PruneArgs {
   float* qzero;
 };
 size_t prune_ws_bytes(int64_t m, int64_t n, int blocksize);
+// The no-allocation prune entry point's scratch array (per device; its size
+// is SG_NOALLOC_SCRATCH_BYTES): its device address on the current device.
+constexpr size_t kNoAllocScratchBytes = SG_NOALLOC_SCRATCH_BYTES;
+sg_status noalloc_scratch(void** ptr);
 sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st);
+
 // ---------------------------------------------------------------------------
 // 2:4 compressed export
 // ---------------------------------------------------------------------------

@@ -237,3 +237,18 @@ def test_pattern_parsing(sg):
     assert sg.parse_pattern("16:64") == (sg.SG_NM, 0.0, 16, 64)
     assert sg.parse_pattern("16:128") == (sg.SG_NM, 0.0, 16, 128)
     assert sg.parse_pattern("0.5/row") == (sg.SG_UNSTRUCTURED_ROW, 0.5, 0, 1)
+
+
+def test_noalloc_validation(sg):
+    lib = _lib(sg)
+    # null pointers and sizes are rejected first
+    st = lib.sg_prune_layer_noalloc(None, None, None, 0, 4, 4, 4, None, 0, 0.5, 0, 1, 4, None, None)
+    assert st == sg.SG_ERR_INVALID_ARGUMENT
+    # a layer whose workspace exceeds the scratch array: rejected before the device is touched
+    need = sg.sg_workspace_bytes(sg.SG_OP_PRUNE, 30000, 256, 0, 128)
+    assert need > sg.SG_NOALLOC_SCRATCH_BYTES
+    st = lib.sg_prune_layer_noalloc(ctypes.c_void_p(0x3000), None, FAKE, 0, 30000, 256, 256, FAKE, 0, 0.5,
+                                    0, 1, 128, None, None)
+    assert st == sg.SG_ERR_UNSUPPORTED and "scratch" in sg.sg_last_error_message()
+    # the largest m the array serves at blocksize 128
+    assert sg.sg_workspace_bytes(sg.SG_OP_PRUNE, 21600, 28672, 0, 128) <= sg.SG_NOALLOC_SCRATCH_BYTES
