@@ -344,6 +344,37 @@ sg_status sg_prune_layers_shared(float* W_out, uint8_t* mask_out,
                                  void* stream);
 
 /*
+ * sg_prune_layers_batched -- prune several layers' weight matrices, each with
+ * the factor of its own inputs, in one call.
+ *
+ * [VSG] part 02 (inter-layer parallel sparsity): with every layer's dense
+ * inputs recorded beforehand, the layers' solves no longer depend on one
+ * another and can be pruned in parallel.  Each matrix's result is exactly
+ * that of its own sg_prune_layer (or sg_prune_quantize_layer) call with its
+ * own Hinv; the matrices are only processed together, so that every launch
+ * of the latency-bound column sweep covers the rows of all of them.
+ *
+ *   W, W_out, mask_out, mask_in, codes_out, row_splits, nseg, bits,
+ *   scale_out, zero_out: as in sg_prune_layers_shared (the matrices stacked
+ *             by rows, each n columns wide).
+ *   Hinv      host array of nseg device pointers: Hinv[p] is the [n x n]
+ *             factor from sg_prepare_hinv of matrix p's inputs.
+ *   Selection counts, patterns, workspace and errors as in
+ *   sg_prune_layers_shared (unstructured counts per matrix and block).
+ */
+sg_status sg_prune_layers_batched(float* W_out, uint8_t* mask_out,
+                                  uint8_t* codes_out, float* scale_out,
+                                  float* zero_out, int32_t bits, const void* W,
+                                  int32_t w_dtype, int64_t m_total, int64_t n,
+                                  int64_t ldw, const int64_t* row_splits,
+                                  int32_t nseg, const float* const* Hinv,
+                                  int32_t pattern_kind, double sparsity,
+                                  int32_t n_keep, int32_t m_group,
+                                  int32_t blocksize, const uint8_t* mask_in,
+                                  void* workspace, size_t ws_bytes,
+                                  void* stream);
+
+/*
  * sg_reconstruction_error -- *err = (accumulate ? *err : 0)
  *                                   + ||(W - W_hat) Xc^T||_F^2.
  *

@@ -154,7 +154,7 @@ static sg_status prune_common(float* W_out, uint8_t* mask_out, uint8_t* codes_ou
                               const float* Hinv, int32_t pattern_kind,
                               double sparsity, int32_t n_keep, int32_t m_group, int32_t blocksize,
                               const uint8_t* mask_in, void* workspace, size_t ws_bytes, void* stream,
-                              int32_t vec = 1) {
+                              int32_t vec = 1, const float* const* Useg = nullptr) {
   if (!W_out || !W || !Hinv) return set_error(SG_ERR_INVALID_ARGUMENT, "W_out, W and Hinv must not be NULL");
   if (m < 1 || n < 1) return set_error(SG_ERR_INVALID_ARGUMENT, "m and n must be >= 1");
   if ((unsigned long long)m * (unsigned long long)n >= (1ull << 32))
@@ -196,6 +196,8 @@ static sg_status prune_common(float* W_out, uint8_t* mask_out, uint8_t* codes_ou
   a.n = n;
   a.ldw = ldw;
   a.U = Hinv;
+  a.seg_u = Useg != nullptr;
+  for (int p = 0; p < SG_MAX_SEGMENTS; ++p) a.Useg[p] = (Useg && p < nseg) ? Useg[p] : Hinv;
   a.kind = pattern_kind;
   a.sparsity = sparsity;
   a.n_keep = pattern_kind == SG_NM ? n_keep : 0;
@@ -305,6 +307,34 @@ sg_status sg_prune_layers_shared(float* W_out, uint8_t* mask_out, uint8_t* codes
                       bits ? zero_out : nullptr, bits, W, w_dtype, m_total, n, ldw, row_splits, nseg,
                       Hinv, pattern_kind, sparsity, n_keep, m_group, blocksize, mask_in, workspace,
                       ws_bytes, stream);
+}
+
+sg_status sg_prune_layers_batched(float* W_out, uint8_t* mask_out, uint8_t* codes_out, float* scale_out,
+                                  float* zero_out, int32_t bits, const void* W, int32_t w_dtype,
+                                  int64_t m_total, int64_t n, int64_t ldw, const int64_t* row_splits,
+                                  int32_t nseg, const float* const* Hinv, int32_t pattern_kind,
+                                  double sparsity, int32_t n_keep, int32_t m_group, int32_t blocksize,
+                                  const uint8_t* mask_in, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!row_splits || !Hinv) return set_error(SG_ERR_INVALID_ARGUMENT, "row_splits and Hinv must not be NULL");
+  if (nseg < 1 || nseg > SG_MAX_SEGMENTS)
+    return set_error(SG_ERR_INVALID_ARGUMENT, "nseg=%d out of [1, %d]", nseg, SG_MAX_SEGMENTS);
+  if (row_splits[0] != 0 || row_splits[nseg] != m_total)
+    return set_error(SG_ERR_INVALID_ARGUMENT, "row_splits must run from 0 to m_total");
+  for (int p = 0; p < nseg; ++p) {
+    if (row_splits[p + 1] <= row_splits[p])
+      return set_error(SG_ERR_INVALID_ARGUMENT, "row_splits must increase strictly");
+    if (!Hinv[p]) return set_error(SG_ERR_INVALID_ARGUMENT, "Hinv[%d] is NULL", p);
+  }
+  if (bits != 0) {
+    if (bits < 2 || bits > 8) return set_error(SG_ERR_INVALID_ARGUMENT, "bits=%d: 0 or [2, 8]", bits);
+    if (!scale_out || !zero_out)
+      return set_error(SG_ERR_INVALID_ARGUMENT, "scale_out and zero_out must not be NULL when bits > 0");
+  }
+  return prune_common(W_out, mask_out, bits ? codes_out : nullptr, bits ? scale_out : nullptr,
+                      bits ? zero_out : nullptr, bits, W, w_dtype, m_total, n, ldw, row_splits, nseg,
+                      Hinv[0], pattern_kind, sparsity, n_keep, m_group, blocksize, mask_in, workspace,
+                      ws_bytes, stream, 1, Hinv);
 }
 
 sg_status sg_reconstruction_error(double* err, int32_t accumulate, const void* W, int32_t w_dtype,

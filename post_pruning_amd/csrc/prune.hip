@@ -83,12 +83,12 @@ struct SelLds {
 
 __global__ __launch_bounds__(256) void select_pass_kernel(SelState* st, int parity,
                                                          unsigned long long* cand,
-                                                         const float* __restrict__ W,
-                                                         const float* __restrict__ U, const Segs segs,
+                                                         const float* __restrict__ W, const Segs segs,
                                                          int64_t n, int64_t i1, int w, int pass) {
   // blockIdx.y = segment; its keys only, into its own histograms and list
   const int seg = blockIdx.y;
   if (segs.fixed[seg] != 0) return;  // whole workgroup: nothing to select
+  const float* __restrict__ U = segs.U[seg];
   const long long k = segs.k[seg];
   SelSet* ss = &st[seg].set[parity];
   cand += segs.row0[seg] * SB;
@@ -203,13 +203,14 @@ struct TopDigitHist {
 // EGK.  The lazy update of the column sweep, in two levels: after each block
 // its errors update the rest of the current group of columns (K = block
 // width); after the last block of a group, the errors of the whole group
-// update every column beyond it at once (K = group width).  With hist0 set,
-// the tiles over the next block's first hist_w columns also add that
-// block's top-digit histogram into hist0.
+// update every column beyond it at once (K = group width).  blockIdx.z picks
+// a row segment (its rows and its factor U).  With hist0 set, the tiles over
+// the next block's first hist_w columns also add that block's top-digit
+// histogram into hist0.
 
 template <bool VEC, int T, bool SHORT = false>
 __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ W, const float* __restrict__ E,
-                                                      const float* __restrict__ U, int64_t m, int64_t n,
+                                                      const Segs segs, int64_t n,
                                                       int64_t k0, int K, int64_t c_begin, int64_t c_end,
                                                       unsigned* __restrict__ hist0, int hist_w) {
   constexpr int LDSB = VEC ? (SHORT ? X6Lds<T>::SHORT : X6Lds<T>::SIZE) : 4 * T * GS * 4;
@@ -217,7 +218,11 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ W, con
   __shared__ unsigned lhist[kSelBins];
   __shared__ float lrd[T];
   float* lds = reinterpret_cast<float*>(ldsb);
-  const int64_t r0 = (int64_t)blockIdx.y * T;
+  const int seg = blockIdx.z;
+  const int64_t m = segs.row0[seg + 1];
+  const int64_t r0 = segs.row0[seg] + (int64_t)blockIdx.y * T;
+  if (r0 >= m) return;  // whole workgroup: past a shorter segment
+  const float* __restrict__ U = segs.U[seg];
   const int64_t c0 = c_begin + (int64_t)blockIdx.x * T;
   const int rows = (int)min<int64_t>(T, m - r0);
   const int cols = (int)min<int64_t>(T, c_end - c0);
@@ -288,31 +293,39 @@ __global__ __launch_bounds__(256, 2) void lazy_kernel(float* __restrict__ W, con
   }
 }
 
-// W[:, c_begin:c_end] -= E[:, 0:K] * U[k0:k0+K, c_begin:c_end] with the tile
-// that fills the GPU: 128 x 128 when that grid covers a full round of
-// workgroups (two per CU), else 64 x 64 (four times the workgroups).
-sg_status launch_lazy(float* W, const float* E, const float* U, int64_t m, int64_t n, int64_t k0, int K,
+// W[:, c_begin:c_end] -= E[:, 0:K] * U[k0:k0+K, c_begin:c_end] (per row
+// segment, with its U) with the tile that fills the GPU: 128 x 128 when that
+// grid covers a full round of workgroups (two per CU), else 64 x 64 (four
+// times the workgroups).
+sg_status launch_lazy(float* W, const float* E, const Segs& segs, int64_t n, int64_t k0, int K,
                       int64_t c_begin, int64_t c_end, bool vec, hipStream_t st, unsigned* hist0 = nullptr,
                       int hist_w = 0) {
-  const int64_t t128 = ceil_div(c_end - c_begin, 128) * ceil_div(m, 128);
+  int64_t t128 = 0, max_rows = 0;
+  for (int p = 0; p < segs.n; ++p) {
+    const int64_t mp = segs.row0[p + 1] - segs.row0[p];
+    t128 += ceil_div(c_end - c_begin, 128) * ceil_div(mp, 128);
+    max_rows = std::max<int64_t>(max_rows, mp);
+  }
   if (t128 >= 2 * kNumCU) {
-    const dim3 grid((unsigned)ceil_div(c_end - c_begin, 128), (unsigned)ceil_div(m, 128));
+    const dim3 grid((unsigned)ceil_div(c_end - c_begin, 128), (unsigned)ceil_div(max_rows, 128),
+                    (unsigned)segs.n);
     if (vec)
-      hipLaunchKernelGGL((lazy_kernel<true, 128>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end,
+      hipLaunchKernelGGL((lazy_kernel<true, 128>), grid, dim3(256), 0, st, W, E, segs, n, k0, K, c_begin, c_end,
                          hist0, hist_w);
     else
-      hipLaunchKernelGGL((lazy_kernel<false, 128>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin,
+      hipLaunchKernelGGL((lazy_kernel<false, 128>), grid, dim3(256), 0, st, W, E, segs, n, k0, K, c_begin,
                          c_end, hist0, hist_w);
   } else {
-    const dim3 grid((unsigned)ceil_div(c_end - c_begin, 64), (unsigned)ceil_div(m, 64));
+    const dim3 grid((unsigned)ceil_div(c_end - c_begin, 64), (unsigned)ceil_div(max_rows, 64),
+                    (unsigned)segs.n);
     if (vec && K <= SB)
-      hipLaunchKernelGGL((lazy_kernel<true, 64, true>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin,
+      hipLaunchKernelGGL((lazy_kernel<true, 64, true>), grid, dim3(256), 0, st, W, E, segs, n, k0, K, c_begin,
                          c_end, hist0, hist_w);
     else if (vec)
-      hipLaunchKernelGGL((lazy_kernel<true, 64>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin, c_end,
+      hipLaunchKernelGGL((lazy_kernel<true, 64>), grid, dim3(256), 0, st, W, E, segs, n, k0, K, c_begin, c_end,
                          hist0, hist_w);
     else
-      hipLaunchKernelGGL((lazy_kernel<false, 64>), grid, dim3(256), 0, st, W, E, U, m, n, k0, K, c_begin,
+      hipLaunchKernelGGL((lazy_kernel<false, 64>), grid, dim3(256), 0, st, W, E, segs, n, k0, K, c_begin,
                          c_end, hist0, hist_w);
   }
   return check_launch("prune lazy");
@@ -395,14 +408,17 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
   const int mode = a.mask_in ? MODE_FORCED
                              : (a.kind == SG_NM ? MODE_NM : (a.kind == SG_UNSTRUCTURED_ROW ? MODE_ROW : MODE_THRESH));
   const int B = a.blocksize;
-  // segments: block-global selection runs per stacked matrix; every other
-  // mode decides row by row, so the rows form one segment
+  // segments: block-global selection runs per stacked matrix, and matrices
+  // with factors of their own need their own segment; otherwise (one shared
+  // factor, a mode that decides row by row) the rows form one segment
+  const bool own = mode == MODE_THRESH || a.seg_u;
   Segs segs = {};
-  segs.n = mode == MODE_THRESH ? a.nseg : 1;
+  segs.n = own ? a.nseg : 1;
   int64_t max_rows = 0;
   for (int p = 0; p < segs.n; ++p) {
-    segs.row0[p] = mode == MODE_THRESH ? a.seg_rows[p] : 0;
-    segs.row0[p + 1] = mode == MODE_THRESH ? a.seg_rows[p + 1] : m;
+    segs.row0[p] = own ? a.seg_rows[p] : 0;
+    segs.row0[p + 1] = own ? a.seg_rows[p + 1] : m;
+    segs.U[p] = a.seg_u ? a.Useg[p] : a.U;
     segs.wg0[p + 1] = segs.wg0[p] + (int)ceil_div(segs.row0[p + 1] - segs.row0[p], 64);
     max_rows = std::max<int64_t>(max_rows, segs.row0[p + 1] - segs.row0[p]);
   }
@@ -437,7 +453,7 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
       if (any) {
         for (int pass = pass0_done ? 1 : 0; pass < 2; ++pass) {
           hipLaunchKernelGGL(select_pass_kernel, sel_grid, dim3(256), sizeof(SelLds), st, sel, parity,
-                             cand, static_cast<const float*>(a.W_out), a.U, segs, n, i1, w, pass);
+                             cand, static_cast<const float*>(a.W_out), segs, n, i1, w, pass);
           if (sg_status e = check_launch("select pass")) return e;
         }
       }
@@ -446,7 +462,6 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
     sa.W = a.W_out;
     sa.mask_out = a.mask_out;
     sa.Err = Eb;
-    sa.U = a.U;
     sa.mask_in = a.mask_in;
     sa.st = sel;
     sa.cand = cand;
@@ -489,11 +504,11 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
     if (i2 < g_end) {
       // rest of the group, K = block width
       if (sg_status e =
-              launch_lazy(a.W_out, Eb, a.U, m, n, i1, w, i2, g_end, lazy_vec(Eb, w), st, hist0, hist_w))
+              launch_lazy(a.W_out, Eb, segs, n, i1, w, i2, g_end, lazy_vec(Eb, w), st, hist0, hist_w))
         return e;
     } else if (g_end < n) {
       // last block of the group: every column beyond it, K = group width
-      if (sg_status e = launch_lazy(a.W_out, Err, a.U, m, n, g0, (int)(g_end - g0), g_end, n,
+      if (sg_status e = launch_lazy(a.W_out, Err, segs, n, g0, (int)(g_end - g0), g_end, n,
                                     lazy_vec(Err, (int)(g_end - g0)), st, hist0, hist_w))
         return e;
     } else {

@@ -51,6 +51,10 @@ struct PruneArgs {
   int w_dtype;
   int64_t m, n, ldw;
   const float* U;
+  // seg_u: every stacked matrix has a factor of its own, Useg[p] (else all
+  // share U)
+  bool seg_u;
+  const float* Useg[SG_MAX_SEGMENTS];
   int kind;
   double sparsity;
   int n_keep, m_group;

@@ -30,15 +30,17 @@ struct SelState {
 };
 
 // Row segments of one prune call (kernel argument): segment p is rows
-// [row0[p], row0[p+1]); its sweep workgroups are [wg0[p], wg0[p+1]) (64 rows
-// each); k[p] keys of each block are pruned under block-global selection
-// (fixed[p]: 2 none, 3 all, 0 selected by the radix passes).
+// [row0[p], row0[p+1]) with the factor U[p]; its sweep workgroups are
+// [wg0[p], wg0[p+1]) (64 rows each); k[p] keys of each block are pruned under
+// block-global selection (fixed[p]: 2 none, 3 all, 0 selected by the radix
+// passes).
 struct Segs {
   int n;
   int64_t row0[SG_MAX_SEGMENTS + 1];
   int wg0[SG_MAX_SEGMENTS + 1];
   long long k[SG_MAX_SEGMENTS];
   int fixed[SG_MAX_SEGMENTS];
+  const float* U[SG_MAX_SEGMENTS];
 };
 
 // OBS saliency w^2 / U_cc^2 as (w * rd)^2 with rd = 1 / U_cc (the IEEE
@@ -484,7 +486,7 @@ __device__ __forceinline__ void sweep_chunk(std::integer_sequence<int, Js...>, f
 
 template <int MODE, int MGS, bool QUANT, bool JOINT = false>
 __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8_t* __restrict__ mask_out,
-                                                    float* __restrict__ Err, const float* __restrict__ U,
+                                                    float* __restrict__ Err,
                                                     const uint8_t* __restrict__ mask_in,
                                                     SelState* __restrict__ st,
                                                     const unsigned long long* __restrict__ cand,
@@ -504,6 +506,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   int seg = 0;
   while (seg + 1 < segs.n && (int)blockIdx.x >= segs.wg0[seg + 1]) ++seg;
   const int64_t m = segs.row0[seg + 1];
+  const float* __restrict__ U = segs.U[seg];
   const int64_t rbase = segs.row0[seg] + ((int64_t)blockIdx.x - segs.wg0[seg]) * 64;
   const long long ksel = segs.k[seg];
   const int sel_fixed = segs.fixed[seg];
@@ -937,7 +940,6 @@ struct SweepArgs {
   float* W;
   uint8_t* mask_out;
   float* Err;
-  const float* U;
   const uint8_t* mask_in;
   SelState* st;
   const unsigned long long* cand;

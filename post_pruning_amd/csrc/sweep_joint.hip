@@ -11,7 +11,7 @@ sg_status go(const SweepArgs& a) {
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SweepLds)) != hipSuccess)
     return set_error(SG_ERR_HIP, "hipFuncSetAttribute(sweep_kernel) failed");
   hipLaunchKernelGGL((sweep_kernel<MODE, MGS, false, true>), a.grid, dim3(256), sizeof(SweepLds), a.stream,
-                     a.W, a.mask_out, a.Err, a.U, a.mask_in, a.st, a.cand, a.parity, a.segs, a.n, a.i1, a.w,
+                     a.W, a.mask_out, a.Err, a.mask_in, a.st, a.cand, a.parity, a.segs, a.n, a.i1, a.w,
                      a.nkeep, a.mgroup, a.codes_out, a.qscale, a.qzero, a.qlevels);
   return check_launch("prune sweep");
 }

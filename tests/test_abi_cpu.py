@@ -252,3 +252,30 @@ def test_noalloc_validation(sg):
     assert st == sg.SG_ERR_UNSUPPORTED and "scratch" in sg.sg_last_error_message()
     # the largest m the array serves at blocksize 128
     assert sg.sg_workspace_bytes(sg.SG_OP_PRUNE, 21600, 28672, 0, 128) <= sg.SG_NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("splits,nseg,hinv", [
+    (None, 2, True),            # no splits
+    ([0, 64, 128], 2, False),   # no factor array
+    ([0, 64, 128], 0, True),    # nseg < 1
+    ([0, 64, 100], 2, True),    # does not end at m_total
+    ([0, 80, 64, 128], 3, True),  # not increasing
+])
+def test_batched_validation(sg, splits, nseg, hinv):
+    arr = None
+    if splits is not None:
+        arr = ctypes.cast((ctypes.c_int64 * 18)(*(splits + [128] * (18 - len(splits)))), ctypes.c_void_p)
+    hv = ctypes.cast((ctypes.c_void_p * 16)(*([0x1000] * 16)), ctypes.c_void_p) if hinv else None
+    st = _lib(sg).sg_prune_layers_batched(ctypes.c_void_p(0x3000), None, None, None, None, 0, FAKE, 0,
+                                          128, 128, 128, arr, nseg, hv, 0, 0.5, 0, 1, 128, None,
+                                          ctypes.c_void_p(0x10000), 10 ** 9, None)
+    assert st == sg.SG_ERR_INVALID_ARGUMENT, sg.sg_last_error_message()
+
+
+def test_batched_null_factor_rejected(sg):
+    arr = ctypes.cast((ctypes.c_int64 * 3)(0, 64, 128), ctypes.c_void_p)
+    hv = ctypes.cast((ctypes.c_void_p * 2)(0x1000, None), ctypes.c_void_p)
+    st = _lib(sg).sg_prune_layers_batched(ctypes.c_void_p(0x3000), None, None, None, None, 0, FAKE, 0,
+                                          128, 128, 128, arr, 2, hv, 0, 0.5, 0, 1, 128, None,
+                                          ctypes.c_void_p(0x10000), 10 ** 9, None)
+    assert st == sg.SG_ERR_INVALID_ARGUMENT and "Hinv[1]" in sg.sg_last_error_message()
