@@ -3,12 +3,17 @@
 One step = the whole hot path for one linear layer with its calibration
 activations already resident in HBM: zero H, H += X^T X over all tokens,
 factor (H + lambda I)^{-1} -> U, prune W (mask selection, OBS compensation,
-lazy updates).  Default workload: the 4096 x 4096 attention-projection layer
-(bf16 W and X, 262,144 calibration tokens, 50% unstructured, block 128).
+lazy updates).  Default workload: the 8192 x 28672 down-projection layer
+(bf16 W and X, 524,288 calibration tokens, 50% unstructured, block 128), the
+largest of the layer shapes; the 4096- and 11008-wide layers are timed in the
+same run after it (key "configs").
 
 Prints ONE JSON line.  ``value`` is the per-layer wall time in seconds (lower
-is better); per-phase times, algorithmic TFLOP/s, the roofline of the dominant
-kernel (the Hessian) and the oracle's CPU time on a bounded sample ride along.
+is better).  Along with it: per-phase times, algorithmic TFLOP/s, each
+phase's fraction of its roofline (the sweep and lazy-update kernels timed by
+the profiler's kernel records over one extra prune call), the roofline of the
+dominant kernel (the Hessian, timed with HIP events around its launch) and
+the oracle's CPU time on a bounded sample.
 """
 
 from __future__ import annotations
@@ -28,8 +33,17 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+METRIC = "per-layer prune wall-time (s) + TFLOP/s & % MFMA/HBM roofline, 4096² → 28672×8192"
+
+# the other layer shapes, timed after the headline workload (name, pattern)
+EXTRA = [("attn_4096", "0.5"), ("mlp_up_11008", "2:4"), ("mlp_down_11008", "0.6"),
+         ("mlp_down_11008", "4:8"), ("mlp_down_28672", "2:4")]
+
 
 def algorithmic_work(m, n, N, B):
+    """Algorithmic flops (and the sweep's bytes) of one layer: H n(n+1)N,
+    factor 2n^3/3, lazy sum 2 m w (n - i2), in-block sum m w (w - 1), sweep
+    13 bytes per weight (W in, W_hat, errors, mask out)."""
     hess = n * (n + 1) * N
     factor = 2.0 * n ** 3 / 3.0
     lazy = 0.0
@@ -64,29 +78,34 @@ def load_traffic(workload):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, pattern, W_host, X_host_sample, n_tok_total, rows_sample, bits=0):
-    """The oracle as it stands, timed on host cores on a bounded sample of the
-    same layer, scaled to one whole layer: Hessian on a token sample (scaled by
-    tokens), the full n x n factor, the column sweep on a row sample (scaled
-    by rows)."""
-    m_rows = W_host.shape[0]
+def cpu_baseline(cfg, pattern, W_host, X_host_sample, n_tok_total, rows_sample, n_factor, bits=0):
+    """The oracle as it stands, timed on the host cores on a bounded sample of
+    the same layer and scaled to one whole layer: the Hessian on a token
+    sample (scaled by tokens), the factor at a smaller n (scaled by n^3), the
+    column sweep on a row sample (scaled by rows)."""
     import numpy as np
+    import torch
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    m_rows, n = W_host.shape
     xs = X_host_sample.double().numpy()
     t0 = time.perf_counter()
     Hs = oracle.hessian([xs])
     t_h = time.perf_counter() - t0
     H_est = Hs * (n_tok_total / xs.shape[0])
+    # the factor on the leading n_factor channels (same distribution)
+    n_factor = min(n, n_factor)
     t0 = time.perf_counter()
-    Hd, _ = oracle.dampen(H_est, cfg.damp)
-    U = oracle.inverse_upper_factor(Hd)
+    Hd_f, _ = oracle.dampen(H_est[:n_factor, :n_factor], cfg.damp)
+    U = oracle.inverse_upper_factor(Hd_f)
     t_u = time.perf_counter() - t0
+    if n > n_factor:
+        # the sweep needs a factor of the full width: the diagonal one of the
+        # damped diagonal (the sweep's cost does not depend on U's values)
+        d = np.diag(H_est)
+        U = np.diag(1.0 / np.sqrt(d + cfg.damp * d.mean()))
     Ws = W_host[:rows_sample].double().numpy()
     t0 = time.perf_counter()
     if bits:
@@ -94,24 +113,324 @@ def cpu_baseline(cfg, pattern, W_host, X_host_sample, n_tok_total, rows_sample, 
     else:
         oracle.prune(Ws, U, pattern, cfg.blocksize)
     t_p = time.perf_counter() - t0
-    total = t_h * (n_tok_total / xs.shape[0]) + t_u + t_p * (m_rows / rows_sample)
+    f_h = n_tok_total / xs.shape[0]
+    f_u = (n / n_factor) ** 3
+    f_p = m_rows / rows_sample
+    total = t_h * f_h + t_u * f_u + t_p * f_p
     return {
         "value": total,
         "unit": "s",
-        "cores": int(threads),
+        "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"Hessian on {xs.shape[0]} of {n_tok_total} tokens (x{n_tok_total // xs.shape[0]}), "
-                   f"full {cfg.n}x{cfg.n} fp64 factor, sweep on {rows_sample} of {m_rows} rows "
-                   f"(x{m_rows // rows_sample}); measured {t_h:.2f}+{t_u:.2f}+{t_p:.2f} s"),
+        "sample": (f"Hessian on {xs.shape[0]} of {n_tok_total} tokens (x{f_h:.0f}), fp64 factor at "
+                   f"n = {n_factor} (x{f_u:.1f} = (n/{n_factor})^3), sweep on {rows_sample} of {m_rows} "
+                   f"rows (x{f_p:.0f}); measured {t_h:.2f} + {t_u:.2f} + {t_p:.2f} s on "
+                   f"{cores} cores (sched_getaffinity)"),
     }
+
+
+def kernel_attribution(fn):
+    """Device time per kernel over one call of fn, from the profiler's kernel
+    records: {kernel name: (calls, total ms)}."""
+    import torch
+    from torch.profiler import ProfilerActivity, profile
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        fn()
+        torch.cuda.synchronize()
+    out = {}
+    for e in prof.key_averages():
+        t = getattr(e, "device_time_total", None)
+        if t is None:
+            t = getattr(e, "cuda_time_total", 0.0)
+        if t and t > 0:
+            out[e.key] = (int(e.count), t / 1e3)
+    return out
+
+
+def _short(name):
+    """'void sg::(anonymous namespace)::sweep_kernel<0, 0>(float*, ...)' ->
+    'sweep_kernel<0, 0>'."""
+    s = name.replace("(anonymous namespace)::", "")
+    s = s.split("(")[0].strip()
+    if s.startswith("void "):
+        s = s[5:]
+    head = s.split("<")[0]
+    if "::" in head:
+        s = s[len(head.rsplit("::", 1)[0]) + 2:]
+    return s
+
+
+def _sum_kernels(attr, base):
+    calls, ms = 0, 0.0
+    for k, (c, t) in attr.items():
+        if _short(k).split("<")[0] == base:
+            calls += c
+            ms += t
+    return calls, ms
+
+
+class Layer:
+    """Device buffers and one step of the path for one workload."""
+
+    def __init__(self, sg, cfg, pattern, dev, args, X=None):
+        import torch
+
+        import synth
+        self.sg, self.cfg, self.pattern, self.args = sg, cfg, pattern, args
+        m, n, N, B = cfg.m, cfg.n, cfg.tokens, cfg.blocksize
+        if args.shared > 1:
+            import dataclasses
+            W = torch.cat([synth.make_weight(dataclasses.replace(cfg, config_id=cfg.config_id + 500 + i), dev)
+                           for i in range(args.shared)])
+            m = W.shape[0]
+        else:
+            W = synth.make_weight(cfg, dev)
+        self.W = W
+        self.m, self.n, self.N, self.B = m, n, N, B
+        self.splits = [i * cfg.m for i in range(args.shared + 1)]
+        self.X = X if X is not None else synth.make_x(cfg, dev)
+        self.H = torch.zeros(n, n, dtype=torch.float32, device=dev)
+        self.Hinv = torch.empty(n, n, dtype=torch.float32, device=dev)
+        self.info = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.W_out = torch.empty(m, n, dtype=torch.float32, device=dev)
+        self.mask = torch.empty(m, n, dtype=torch.uint8, device=dev)
+        self.ws_h = torch.empty(max(1, sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, n, N, 0)),
+                                dtype=torch.uint8, device=dev)
+        self.ws_f = torch.empty(sg.sg_workspace_bytes(sg.SG_OP_PREPARE_HINV, 0, n, 0, 0), dtype=torch.uint8,
+                                device=dev)
+        self.ws_p = torch.empty(sg.sg_workspace_bytes(sg.SG_OP_PRUNE, m, n, 0, B), dtype=torch.uint8,
+                                device=dev)
+        self.codes = torch.empty(m, n, dtype=torch.uint8, device=dev) if args.bits else None
+        # the factor's update stream and events (used above n = 4096)
+        self.side = torch.cuda.Stream(device=dev)
+
+    def hessian(self):
+        self.H.zero_()
+        self.sg.sg_hessian_accumulate(self.H, self.X, workspace=self.ws_h)
+
+    def factor(self):
+        self.sg.sg_prepare_hinv(self.H, self.cfg.damp, Hinv=self.Hinv, info=self.info, workspace=self.ws_f,
+                                update_stream=self.side)
+
+    def prune(self):
+        sg, a = self.sg, self.args
+        if a.shared > 1:
+            sg.sg_prune_layers_shared(self.W, self.splits, self.Hinv, self.pattern, self.B, bits=a.bits,
+                                      W_out=self.W_out, mask_out=self.mask, codes_out=self.codes,
+                                      workspace=self.ws_p)
+        elif a.vec != 1:
+            sg.sg_prune_layer_vector(self.W, self.Hinv, self.pattern, a.vec, self.B, W_out=self.W_out,
+                                     mask_out=self.mask, workspace=self.ws_p)
+        elif a.bits:
+            sg.sg_prune_quantize_layer(self.W, self.Hinv, self.pattern, a.bits, self.B, W_out=self.W_out,
+                                       mask_out=self.mask, codes_out=self.codes, workspace=self.ws_p)
+        else:
+            sg.sg_prune_layer(self.W, self.Hinv, self.pattern, self.B, W_out=self.W_out, mask_out=self.mask,
+                              workspace=self.ws_p)
+
+    def step(self):
+        self.hessian()
+        self.factor()
+        self.prune()
+
+    def timed(self, steps, warmup, label):
+        """warmup + steps; returns (ms per step, phase ms, Hessian launch ms)."""
+        import torch
+        ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        for i in range(warmup):
+            self.step()
+            torch.cuda.synchronize()
+            print(f"[bench] {label}: warmup {i + 1}/{warmup} done", file=sys.stderr, flush=True)
+        if int(self.info.item()) != 0:
+            raise RuntimeError(f"{label}: factorisation failed: info={int(self.info.item())}")
+        marks = [[ev() for _ in range(5)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0, t1 = ev(), ev()
+        t0.record()
+        for i in range(steps):
+            mk = marks[i]
+            mk[0].record()
+            self.H.zero_()
+            mk[1].record()  # the Hessian launch alone, on the stream it runs on
+            self.sg.sg_hessian_accumulate(self.H, self.X, workspace=self.ws_h)
+            mk[2].record()
+            self.factor()
+            mk[3].record()
+            self.prune()
+            mk[4].record()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        ph = {"hessian": 0.0, "factor": 0.0, "prune": 0.0}
+        hk = 0.0
+        for mk in marks:
+            ph["hessian"] += mk[0].elapsed_time(mk[2])
+            hk += mk[1].elapsed_time(mk[2])
+            ph["factor"] += mk[2].elapsed_time(mk[3])
+            ph["prune"] += mk[3].elapsed_time(mk[4])
+        ph = {k: v / steps for k, v in ph.items()}
+        print(f"[bench] {label}: timed {steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+        return ms, ph, hk / steps
+
+    def fractions(self, ph, attr=None):
+        w = algorithmic_work(self.m, self.n, self.N, self.B)
+        out = {
+            "hessian_frac_bf16": w["hessian"] / (ph["hessian"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "factor_frac_fp32": w["factor"] / (ph["factor"] * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+            "prune_tflops": (w["lazy"] + w["inblock"]) / (ph["prune"] * 1e-3) / 1e12,
+        }
+        if attr:
+            c_s, t_s = _sum_kernels(attr, "sweep_kernel")
+            c_l, t_l = _sum_kernels(attr, "lazy_kernel")
+            c_q, t_q = _sum_kernels(attr, "select_pass_kernel")
+            if t_s > 0:
+                out["sweep_hbm_frac"] = w["sweep_bytes"] / (t_s * 1e-3) / 1e9 / PEAK_HBM_GBS
+                out["sweep_kernels_ms"] = t_s
+                out["sweep_launches"] = c_s
+            if t_l > 0:
+                out["lazy_frac_fp32"] = w["lazy"] / (t_l * 1e-3) / 1e12 / PEAK_FP32_TFLOPS
+                out["lazy_kernels_ms"] = t_l
+            if t_q > 0:
+                out["select_kernels_ms"] = t_q
+        return out
+
+
+def measure_peaks(dev):
+    """The machine peaks the roofline fractions are quoted against, measured:
+    MFMA chains on register operands (bf16 16x16x32 and fp32 16x16x4, eight
+    waves per SIMD) and a 4 GiB device copy and read (libsg_peaks.so)."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "post_pruning_amd", "libsg_peaks.so"))
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timeit(call, reps=5):
+        call()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            assert call() == 0
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    blocks, iters = 2048, 20000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    waves = blocks * 4
+    res = {}
+    t = timeit(lambda: lib.sgp_mfma_bf16(iters, blocks, ctypes.c_void_p(out.data_ptr()), st))
+    fl = waves * iters * 8 * 2.0 * 16 * 16 * 32
+    res["mfma_bf16_tflops"] = fl / (t * 1e-3) / 1e12
+    t = timeit(lambda: lib.sgp_mfma_f32(iters, blocks, ctypes.c_void_p(out.data_ptr()), st))
+    fl = waves * iters * 8 * 2.0 * 16 * 16 * 4
+    res["mfma_f32_tflops"] = fl / (t * 1e-3) / 1e12
+    nbytes = 4 << 30
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    n4 = nbytes // 16
+    cb = 256 * 16
+    t = timeit(lambda: lib.sgp_copy(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()),
+                                    ctypes.c_int64(n4), cb, st))
+    res["hbm_copy_gbs"] = 2.0 * nbytes / (t * 1e-3) / 1e9
+    red = torch.empty(cb * 256, dtype=torch.float32, device=dev)
+    t = timeit(lambda: lib.sgp_read(ctypes.c_void_p(a.data_ptr()), ctypes.c_int64(n4), cb,
+                                    ctypes.c_void_p(red.data_ptr()), st))
+    res["hbm_read_gbs"] = nbytes / (t * 1e-3) / 1e9
+    res["datasheet"] = {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "mfma_f32_tflops": PEAK_FP32_TFLOPS,
+                        "hbm_gbs": PEAK_HBM_GBS}
+    res["probe"] = (f"{blocks} workgroups x 4 waves x {iters} rounds of 8 independent MFMAs; "
+                    f"4 GiB float4 copy / read over {cb} workgroups; mean of 5 launches after one warm-up")
+    return res
+
+
+def bench_layers(sg, K, args, dev):
+    """K layers of the 4096 x 4096 attention-projection shape, each with its
+    own weights and calibration activations.  Sequential: per layer Hessian,
+    factor, prune.  Batched: per layer Hessian and factor, then one
+    sg_prune_layers_batched over the K stacked matrices with their own
+    factors.  Returns (batched ms per K layers, sequential ms, phase ms)."""
+    import dataclasses
+
+    import torch
+
+    import synth
+    base = synth.CONFIGS["attn_4096"]
+    pattern = args.pattern or base.patterns[0]
+    cfgs = [dataclasses.replace(base, config_id=600 + i) for i in range(K)]
+    Ls = []
+    for i, c in enumerate(cfgs):
+        print(f"[bench] generating layer {i + 1}/{K}", file=sys.stderr, flush=True)
+        Ls.append(Layer(sg, c, pattern, dev, args))
+    W_all = torch.cat([L.W for L in Ls])
+    splits = [i * base.m for i in range(K + 1)]
+    W_out = torch.empty(K * base.m, base.n, dtype=torch.float32, device=dev)
+    mask = torch.empty(K * base.m, base.n, dtype=torch.uint8, device=dev)
+    ws = torch.empty(sg.sg_workspace_bytes(sg.SG_OP_PRUNE, K * base.m, base.n, 0, base.blocksize),
+                     dtype=torch.uint8, device=dev)
+    Hinvs = [L.Hinv for L in Ls]
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def sequential():
+        for L in Ls:
+            L.step()
+
+    def batched(marks=None):
+        for L in Ls:
+            L.hessian()
+            L.factor()
+        if marks is not None:
+            marks.record()
+        sg.sg_prune_layers_batched(W_all, splits, Hinvs, pattern, base.blocksize, W_out=W_out, mask_out=mask,
+                                   workspace=ws)
+
+    res = {}
+    for name, fn in (("sequential", sequential), ("batched", batched)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = ev(), ev()
+        pm = [ev() for _ in range(args.steps)]
+        t0.record()
+        for i in range(args.steps):
+            if name == "batched":
+                fn(pm[i])
+            else:
+                fn()
+        t1.record()
+        torch.cuda.synchronize()
+        res[name] = t0.elapsed_time(t1) / args.steps
+        print(f"[bench] {K} layers {name}: {res[name]:.3f} ms/step", file=sys.stderr, flush=True)
+    # the batched prune alone
+    e0, e1 = ev(), ev()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        sg.sg_prune_layers_batched(W_all, splits, Hinvs, pattern, base.blocksize, W_out=W_out, mask_out=mask,
+                                   workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    res["batched_prune_ms"] = e0.elapsed_time(e1) / args.steps
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(args.steps):
+        for L in Ls:
+            L.prune()
+    e1.record()
+    torch.cuda.synchronize()
+    res["sequential_prune_ms"] = e0.elapsed_time(e1) / args.steps
+    return res, base, pattern
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="attn_4096")
+    ap.add_argument("--config", default="mlp_down_28672")
     ap.add_argument("--pattern", default=None)
     ap.add_argument("--shared", type=int, default=1,
                     help="prune this many matrices of the layer's shape that share its input "
@@ -121,8 +440,16 @@ def main():
     ap.add_argument("--bits", type=int, default=0,
                     help="also round the kept weights to a per-row grid of 2^bits levels in the sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip timing the other layer shapes")
+    ap.add_argument("--no-attribution", action="store_true",
+                    help="skip the profiler's per-kernel times (e.g. when run under rocprofv3)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this size (for counter scaling)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="K > 1: K attention-shaped layers with their own inputs, pruned sequentially "
+                         "and in one batched call; reports layers/s")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure the machine peaks (MFMA bf16/fp32, HBM copy/read) and print them")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -138,103 +465,50 @@ def main():
     sg.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.peaks:
+        print(json.dumps({"measured_peaks": measure_peaks(dev)}))
+        return
+    if args.layers > 1:
+        K = args.layers
+        res, base, pattern = bench_layers(sg, K, args, dev)
+        ms = res["batched"]
+        print(json.dumps({
+            "metric": METRIC, "value": ms / K / 1e3, "unit": "s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": False, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16 inputs, fp32 accumulate/solve",
+            "data": "synthetic (seeded; shapes and distributions of the layer)",
+            "config": {"workload": f"{K} x attn_4096 layers with their own inputs: W 4096x4096 bf16, "
+                                   f"X 262144x4096 bf16 each, pattern {pattern}, blocksize {base.blocksize}; "
+                                   f"per layer Hessian and factor, one batched prune",
+                       "layers": K, "pattern": pattern},
+            "layers_per_s": K / (ms * 1e-3),
+            "sequential_ms_per_step": res["sequential"],
+            "sequential_layers_per_s": K / (res["sequential"] * 1e-3),
+            "batched_prune_ms": res["batched_prune_ms"],
+            "sequential_prune_ms": res["sequential_prune_ms"],
+        }))
+        return
     cfg = synth.CONFIGS[args.config]
     pattern = args.pattern or cfg.patterns[0]
-    m, n, N, B = cfg.m, cfg.n, cfg.tokens, cfg.blocksize
-    print(f"[bench] generating {args.config}: W {m}x{n}, X {N}x{n} ({cfg.dtype})", file=sys.stderr,
-          flush=True)
-    if args.shared > 1:
-        import dataclasses
-        W = torch.cat([synth.make_weight(dataclasses.replace(cfg, config_id=cfg.config_id + 500 + i), dev)
-                       for i in range(args.shared)])
-        m = W.shape[0]
-    else:
-        W = synth.make_weight(cfg, dev)
-    splits = [i * cfg.m for i in range(args.shared + 1)]
-    X = synth.make_x(cfg, dev)
-    torch.cuda.synchronize()
-
-    H = torch.zeros(n, n, dtype=torch.float32, device=dev)
-    Hinv = torch.empty(n, n, dtype=torch.float32, device=dev)
-    info = torch.zeros(1, dtype=torch.int32, device=dev)
-    W_out = torch.empty(m, n, dtype=torch.float32, device=dev)
-    mask = torch.empty(m, n, dtype=torch.uint8, device=dev)
-    ws_h = torch.empty(max(1, sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, n, N, 0)), dtype=torch.uint8,
-                       device=dev)
-    ws_f = torch.empty(sg.sg_workspace_bytes(sg.SG_OP_PREPARE_HINV, 0, n, 0, 0), dtype=torch.uint8,
-                       device=dev)
-    ws_p = torch.empty(sg.sg_workspace_bytes(sg.SG_OP_PRUNE, m, n, 0, B), dtype=torch.uint8, device=dev)
-    codes = torch.empty(m, n, dtype=torch.uint8, device=dev) if args.bits else None
-
-    def prune():
-        if args.shared > 1:
-            sg.sg_prune_layers_shared(W, splits, Hinv, pattern, B, bits=args.bits, W_out=W_out,
-                                      mask_out=mask, codes_out=codes, workspace=ws_p)
-        elif args.vec != 1:
-            sg.sg_prune_layer_vector(W, Hinv, pattern, args.vec, B, W_out=W_out, mask_out=mask,
-                                     workspace=ws_p)
-        elif args.bits:
-            sg.sg_prune_quantize_layer(W, Hinv, pattern, args.bits, B, W_out=W_out, mask_out=mask,
-                                       codes_out=codes, workspace=ws_p)
-        else:
-            sg.sg_prune_layer(W, Hinv, pattern, B, W_out=W_out, mask_out=mask, workspace=ws_p)
-
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-
-    def step(marks=None):
-        if marks is not None:
-            marks[0].record()
-        H.zero_()
-        sg.sg_hessian_accumulate(H, X, workspace=ws_h)
-        if marks is not None:
-            marks[1].record()
-        sg.sg_prepare_hinv(H, cfg.damp, Hinv=Hinv, info=info, workspace=ws_f)
-        if marks is not None:
-            marks[2].record()
-        prune()
-        if marks is not None:
-            marks[3].record()
-
-    for i in range(args.warmup):
-        step()
-        torch.cuda.synchronize()
-        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
-    if int(info.item()) != 0:
-        raise RuntimeError(f"factorisation failed: info={int(info.item())}")
-
-    phase_marks = [[ev() for _ in range(4)] for _ in range(args.steps)]
-    hess_marks = [[ev(), ev()] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start, t_end = ev(), ev()
-    wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(args.steps):
-        mk = phase_marks[i]
-        mk[0].record()
-        H.zero_()
-        hess_marks[i][0].record()
-        sg.sg_hessian_accumulate(H, X, workspace=ws_h)
-        hess_marks[i][1].record()
-        mk[1].record()
-        sg.sg_prepare_hinv(H, cfg.damp, Hinv=Hinv, info=info, workspace=ws_f)
-        mk[2].record()
-        prune()
-        mk[3].record()
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = t_start.elapsed_time(t_end) / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step (host wall {wall:.2f} s)",
+    print(f"[bench] generating {args.config}: W {cfg.m}x{cfg.n}, X {cfg.tokens}x{cfg.n} ({cfg.dtype})",
           file=sys.stderr, flush=True)
+    L = Layer(sg, cfg, pattern, dev, args)
+    torch.cuda.synchronize()
+    ms, ph, t_hess_kernel_ms = L.timed(args.steps, args.warmup, args.config)
+    m, n, N, B = L.m, L.n, L.N, L.B
 
-    ph = {"hessian": 0.0, "factor": 0.0, "prune": 0.0}
-    for mk in phase_marks:
-        ph["hessian"] += mk[0].elapsed_time(mk[1])
-        ph["factor"] += mk[1].elapsed_time(mk[2])
-        ph["prune"] += mk[2].elapsed_time(mk[3])
-    ph = {k: v / args.steps for k, v in ph.items()}
-    t_hess_kernel_ms = sum(a.elapsed_time(b) for a, b in hess_marks) / args.steps
-
+    attr = None
+    if not args.no_attribution:
+        try:
+            attr = kernel_attribution(L.prune)
+            f_attr = kernel_attribution(L.factor)
+            attr_factor = {k: v for k, v in f_attr.items()}
+        except Exception as e:  # the profiler is context, never the measurement
+            print(f"[bench] kernel attribution unavailable: {e!r}", file=sys.stderr, flush=True)
+            attr, attr_factor = None, None
+    else:
+        attr_factor = None
+    fr = L.fractions(ph, attr)
     work = algorithmic_work(m, n, N, B)
     total_flops = work["hessian"] + work["factor"] + work["lazy"] + work["inblock"]
     achieved = work["hessian"] / (t_hess_kernel_ms * 1e-3) / 1e12
@@ -247,6 +521,7 @@ def main():
         a.fill_(1)
         b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
 
     export = None
     if pattern == "2:4":
@@ -254,16 +529,17 @@ def main():
         # HBM-bound, algorithmic bytes per weight 4 + 1 in, value bytes / 2 +
         # 1/8 out
         export = {}
+        ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
         for vdt, vb in ((torch.float32, 4), (torch.bfloat16, 2)):
             vals = torch.empty(m, n // 2, dtype=vdt, device=dev)
             meta = torch.empty(m, (n + 7) // 8, dtype=torch.uint8, device=dev)
             for _ in range(2):
-                sg.sg_pack_two_four(W_out, mask, value_dtype=vdt, values=vals, meta=meta)
+                sg.sg_pack_two_four(L.W_out, L.mask, value_dtype=vdt, values=vals, meta=meta)
             reps = 20
             e0, e1 = ev(), ev()
             e0.record()
             for _ in range(reps):
-                sg.sg_pack_two_four(W_out, mask, value_dtype=vdt, values=vals, meta=meta)
+                sg.sg_pack_two_four(L.W_out, L.mask, value_dtype=vdt, values=vals, meta=meta)
             e1.record()
             torch.cuda.synchronize()
             t = e0.elapsed_time(e1) / reps
@@ -277,12 +553,57 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a host sample", file=sys.stderr, flush=True)
-        tok_sample = min(N, 8192)
-        rows = min(m, 256)
-        cpu = cpu_baseline(cfg, pattern, W.cpu(), X[:tok_sample].cpu(), N, rows, args.bits)
+        tok_sample = min(N, 4096 if n > 8192 else 8192)
+        rows = min(m, 16 if n > 8192 else 256)
+        n_factor = min(n, 8192)
+        cpu = cpu_baseline(cfg, pattern, L.W.cpu(), L.X[:tok_sample].cpu(), N, rows, n_factor, args.bits)
+
+    main_key = f"{args.config} {pattern}"
+    extra = {}
+    if not args.no_extra and args.shared == 1 and args.vec == 1 and not args.bits:
+        # free the headline layer's buffers, then time the other shapes
+        keepX = L.X if args.config == "mlp_down_28672" else None
+        del L
+        torch.cuda.empty_cache()
+        cache = {}
+        for name, pat in EXTRA:
+            key = f"{name} {pat}"
+            if key == main_key:
+                continue
+            c = synth.CONFIGS[name]
+            xsrc = c.x_source or name
+            if name == "mlp_down_28672" and keepX is not None:
+                X = keepX
+            elif xsrc in cache:
+                X = cache[xsrc]
+            else:
+                cache.clear()
+                torch.cuda.empty_cache()
+                X = synth.make_x(c, dev)
+                cache[xsrc] = X
+            Lx = Layer(sg, c, pat, dev, args, X=X)
+            e_ms, e_ph, e_hk = Lx.timed(3, 1, key)
+            e_attr = None
+            if not args.no_attribution and attr is not None:
+                try:
+                    e_attr = kernel_attribution(Lx.prune)
+                except Exception:
+                    e_attr = None
+            e_fr = Lx.fractions(e_ph, e_attr)
+            w = algorithmic_work(Lx.m, Lx.n, Lx.N, Lx.B)
+            extra[key] = {
+                "ms": e_ms, "phases_ms": {k: round(v, 4) for k, v in e_ph.items()},
+                "tflops_algorithmic": (w["hessian"] + w["factor"] + w["lazy"] + w["inblock"]) / (e_ms * 1e-3) / 1e12,
+                "hessian_launch_ms": e_hk,
+                "phase_roofline": e_fr,
+            }
+            del Lx
+            torch.cuda.empty_cache()
+        keepX = None
+        cache.clear()
 
     line = {
-        "metric": "per-layer prune wall-time (s) + TFLOP/s & % MFMA/HBM roofline, 4096² → 28672×8192",
+        "metric": METRIC,
         "value": ms / 1e3,
         "unit": "s",
         "n_gpus": 1,
@@ -306,11 +627,7 @@ def main():
         },
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
         "tflops_algorithmic": total_flops / (ms * 1e-3) / 1e12,
-        "phase_roofline": {
-            "hessian_frac_bf16": work["hessian"] / (ph["hessian"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "factor_frac_fp32": work["factor"] / (ph["factor"] * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
-            "prune_tflops": (work["lazy"] + work["inblock"]) / (ph["prune"] * 1e-3) / 1e12,
-        },
+        "phase_roofline": fr,
         "roofline": {
             "kernel": "hess_bf16_dma_kernel (sg_hessian_accumulate, one launch per step)",
             "bound": "mfma",
@@ -324,6 +641,14 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if attr:
+        line["prune_kernels_ms"] = {_short(k): round(t, 4)
+                                    for k, (c, t) in sorted(attr.items(), key=lambda kv: -kv[1][1])[:8]}
+    if attr_factor:
+        line["factor_kernels_ms"] = {_short(k): round(t, 4) for k, (c, t) in
+                                     sorted(attr_factor.items(), key=lambda kv: -kv[1][1])[:6]}
+    if extra:
+        line["configs"] = extra
     if export is not None:
         line["two_four_export"] = export
     if args.shared > 1:
