@@ -34,6 +34,10 @@ HIPCC_FLAGS = [
 # ordinary VGPRs there are no accumulator-register copies in that loop.
 SOURCE_FLAGS = {s: ["-mllvm", "-amdgpu-mfma-vgpr-form"]
                 for s in ("sweep_plain.hip", "sweep_quant.hip", "sweep_joint.hip")}
+# The peak probes' MFMA chains: in accumulator registers the compiler shuffles
+# the loop-carried tuples with accvgpr moves between the MFMAs; in VGPRs the
+# loop is the eight MFMAs alone.
+SOURCE_FLAGS["peaks.hip"] = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc() -> str:

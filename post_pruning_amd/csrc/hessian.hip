@@ -355,9 +355,14 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
       }
 }
 
-// fp32 inputs: plain LDS-tiled VALU kernel (64x64 lower tiles, 4x4 outputs
-// per thread).  Each 32-token stage is summed separately before it is added
-// to the running total.
+// fp32 inputs: 64x64 lower-triangle tiles on v_mfma_f32_16x16x4_f32.  A
+// 32-token stage of both 64-channel panels sits in LDS as it lies in X
+// (token rows, channels contiguous); each of the 4 waves owns a 32x32
+// sub-tile (2x2 MFMA blocks), and lane l reads its operand value (channel
+// l % 16 of a block, token l / 16 of a 4-token step) straight from a token
+// row, so consecutive lanes read consecutive words.  Each stage is summed in
+// its own accumulators before it is added to the running total (32-token
+// partial sums): fp32 products, unlike bf16 ones, are rounded.
 constexpr int FT = 64;
 constexpr int FBK = 32;
 
@@ -369,38 +374,74 @@ __global__ __launch_bounds__(256) void hess_f32_kernel(float* __restrict__ H, in
   int I, J;
   tri_decode(blockIdx.x, I, J);
   const int i0 = I * FT, j0 = J * FT;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4] = {};
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wi = wave >> 1, wj = wave & 1;
+  floatx4 tot[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) tot[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // loader: thread t stages channel t % 64 of token rows t / 64 + 4 u
+  const int lc = tid & 63, lr = tid >> 6;
+  const bool aok = i0 + lc < n, bok = j0 + lc < n;
+  const int64_t ca = aok ? i0 + lc : n - 1, cb = bok ? j0 + lc : n - 1;
   for (int64_t t0 = 0; t0 < T; t0 += FBK) {
-    for (int e = threadIdx.x; e < FBK * FT; e += 256) {
-      const int tt = e / FT, c = e % FT;
-      const int64_t t = t0 + tt;
-      As[tt][c] = (t < T && i0 + c < n) ? X[t * ldx + i0 + c] : 0.f;
-      Bs[tt][c] = (t < T && j0 + c < n) ? X[t * ldx + j0 + c] : 0.f;
+    float va[FBK / 4], vb[FBK / 4];
+#pragma unroll
+    for (int u = 0; u < FBK / 4; ++u) {
+      const int64_t t = t0 + lr + 4 * u;
+      const int64_t tc = t < T ? t : T - 1;  // clamped in-bounds address, zeroed below
+      va[u] = X[tc * ldx + ca];
+      vb[u] = X[tc * ldx + cb];
+    }
+#pragma unroll
+    for (int u = 0; u < FBK / 4; ++u) {
+      const bool tok = t0 + lr + 4 * u < T;
+      As[lr + 4 * u][lc] = (tok && aok) ? va[u] : 0.f;
+      Bs[lr + 4 * u][lc] = (tok && bok) ? vb[u] : 0.f;
     }
     __syncthreads();
-    float stage[4][4] = {};
-    for (int k = 0; k < FBK; ++k) {
-      float a[4], bb[4];
-      for (int u = 0; u < 4; ++u) a[u] = As[k][ty * 4 + u];
-      for (int u = 0; u < 4; ++u) bb[u] = Bs[k][tx * 4 + u];
-      for (int u = 0; u < 4; ++u)
-        for (int w = 0; w < 4; ++w) stage[u][w] = fmaf(a[u], bb[w], stage[u][w]);
+    floatx4 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < FBK; k += 4) {
+      const int kr = k + (lane >> 4);
+      float fa[2], fb[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) fa[a] = As[kr][wi * 32 + a * 16 + (lane & 15)];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) fb[b] = Bs[kr][wj * 32 + b * 16 + (lane & 15)];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[a], fb[b], acc[a][b], 0, 0, 0);
     }
-    for (int u = 0; u < 4; ++u)
-      for (int w = 0; w < 4; ++w) acc[u][w] += stage[u][w];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) tot[a][b] += acc[a][b];
     __syncthreads();
   }
-  for (int u = 0; u < 4; ++u)
-    for (int w = 0; w < 4; ++w) {
-      const int row = i0 + ty * 4 + u, col = j0 + tx * 4 + w;
-      if (row >= n || col >= n) continue;
-      if (I == J && row < col) continue;
-      const size_t lo = (size_t)row * n + col;
-      const float val = H[lo] + acc[u][w];
-      H[lo] = val;
-      if (row != col) H[(size_t)col * n + row] = val;
-    }
+  // lane l, register v of block (a, b): row 4 (l / 16) + v, column l % 16
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = i0 + wi * 32 + a * 16 + (lane >> 4) * 4 + v;
+        const int col = j0 + wj * 32 + b * 16 + (lane & 15);
+        if (row >= n || col >= n) continue;
+        if (I == J && row < col) continue;
+        const size_t lo = (size_t)row * n + col;
+        const float val = H[lo] + tot[a][b][v];
+        H[lo] = val;
+        if (row != col) H[(size_t)col * n + row] = val;
+      }
 }
 
 }  // namespace
