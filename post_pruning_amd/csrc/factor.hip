@@ -75,7 +75,8 @@ __global__ __launch_bounds__(1024) void damp_lambda_kernel(const float* __restri
 }
 
 // A = J (H + lam I) J on the lower block triangle (identity tail for padding);
-// Y = I on the upper block triangle.  64x64 tiles.
+// Y = I (zero below the diagonal, so its lower block triangle is zero too:
+// the paired updates read Y[k+1][k]).  64x64 tiles.
 __global__ __launch_bounds__(256) void flip_init_kernel(const float* __restrict__ H, int64_t n,
                                                         int64_t n_pad,
                                                         const float* __restrict__ lam_p,
@@ -88,7 +89,6 @@ __global__ __launch_bounds__(256) void flip_init_kernel(const float* __restrict_
   const int64_t j = tj * 64 + c;
   // block-triangle membership at the 128 granularity of the factorisation
   const bool lower = (ti / 2) >= (tj / 2);
-  const bool upper = (ti / 2) <= (tj / 2);
   for (int rr = r0; rr < 64; rr += 4) {
     const int64_t i = ti * 64 + rr;
     if (lower) {
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void flip_init_kernel(const float* __restrict_
       }
       A[i * n_pad + j] = v;
     }
-    if (upper) Y[i * n_pad + j] = (i == j) ? 1.f : 0.f;
+    Y[i * n_pad + j] = (i == j) ? 1.f : 0.f;
   }
 }
 
@@ -473,26 +473,35 @@ __device__ inline int64_t isqrt_floor(int64_t x) {
   return r;
 }
 
-// Trailing-update tiles of panel k (K = 128 each), in three subsets:
+// Trailing-update tiles of panels k .. kl = k + kw - 1 (kw = 1: K = 128;
+// kw = 2: the two panels' updates in one pass, K = 256), in three subsets:
 //   UPD_ALL   every tile;
-//   UPD_COL   the tiles of block column k+1 only (what panel k+1 needs; run
-//             by col_update_kernel in 64x64 quarters);
-//   UPD_REST  every other tile (run beside panel k+1).
+//   UPD_COL   the tiles of block column kl+1 only (what panel kl+1 needs;
+//             run by col_update_kernel in 64x64 quarters);
+//   UPD_REST  every other tile (run beside panel kl+1).
+// SYRK tiles (l, m), kl < m <= l: A[l,m] -= L[l,k:kl+1] L[m,k:kl+1]^T.
+// Inverse tiles (c, l), c <= kl < l: R[c,l] -= Y[c,k:kl+1] L[l,k:kl+1]^T
+// (for kw = 2 and c = kl, Y[kl][k] lies in Y's lower block triangle, which
+// is zero).  Pairing halves the passes over the trailing matrix, whose
+// read-modify-write bounds the update at large n.
 enum { UPD_ALL = 0, UPD_COL = 1, UPD_REST = 2 };
 
-__host__ __device__ inline int64_t update_tiles(int k, int nblk, int mode) {
-  const int64_t t = nblk - k - 1;  // trailing block count
+__host__ __device__ inline int64_t update_tiles(int k, int kw, int nblk, int mode) {
+  const int kl = k + kw - 1;
+  const int64_t t = nblk - kl - 1;  // trailing block count
   if (t <= 0) return 0;
-  if (mode == UPD_COL) return t + (k + 1);
-  if (mode == UPD_REST) return (t - 1) * t / 2 + (int64_t)(k + 1) * (t - 1);
-  return t * (t + 1) / 2 + (int64_t)(k + 1) * t;
+  if (mode == UPD_COL) return t + (kl + 1);
+  if (mode == UPD_REST) return (t - 1) * t / 2 + (int64_t)(kl + 1) * (t - 1);
+  return t * (t + 1) / 2 + (int64_t)(kl + 1) * t;
 }
 
+template <int KW>
 __device__ __forceinline__ void update_body(float* lds, float* __restrict__ A, float* __restrict__ Y,
                                             int64_t n_pad, int k, int nblk, int mode, int64_t idx) {
   // UPD_ALL or UPD_REST.  SYRK tiles: lower triangle over trailing blocks
-  // [s0, nblk); inverse tiles: rows c <= k, block columns [s0, nblk)
-  const int64_t s0 = mode == UPD_REST ? k + 2 : k + 1;
+  // [s0, nblk); inverse tiles: rows c <= kl, block columns [s0, nblk)
+  const int kl = k + KW - 1;
+  const int64_t s0 = mode == UPD_REST ? kl + 2 : kl + 1;
   const int64_t ts = nblk - s0;
   const int64_t nsyrk = ts * (ts + 1) / 2;
   float* C;
@@ -508,19 +517,19 @@ __device__ __forceinline__ void update_body(float* lds, float* __restrict__ A, f
     Q = A + mb * NB * n_pad + (int64_t)k * NB;
   } else {
     idx -= nsyrk;
-    const int64_t c = idx % (k + 1);
-    const int64_t lb = s0 + idx / (k + 1);
+    const int64_t c = idx % (kl + 1);
+    const int64_t lb = s0 + idx / (kl + 1);
     C = Y + c * NB * n_pad + lb * NB;
     P = Y + c * NB * n_pad + (int64_t)k * NB;
     Q = A + lb * NB * n_pad + (int64_t)k * NB;
   }
   // fp32-accurate products on bf16 MFMA (three-way split, six terms); every
   // tile is full (n_pad < 2^24: the workspace holds 2 n_pad^2 floats)
-  RowsX6V<NB, true> pl{P, n_pad, NB, NB};
-  RowsX6V<NB, true> ql{Q, n_pad, NB, NB};
+  RowsX6V<NB, true> pl{P, n_pad, NB, KW * NB};
+  RowsX6V<NB, true> ql{Q, n_pad, NB, KW * NB};
   TileAcc acc;
   tile_zero(acc);
-  tile_gemm_x6(acc, pl, ql, NB, lds);
+  tile_gemm_x6(acc, pl, ql, KW * NB, lds);
   tile_sub_from(C, n_pad, NB, NB, acc, lds);
 }
 
@@ -533,69 +542,78 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
                 blockIdx.x % parts);
 }
 
-// Block column k+1 of panel k's update (what panel k+1 reads first) in 64x64
-// quarters of the 128x128 tiles: four times the workgroups of the tile grid,
-// which is only t + k + 1 tiles, for a short latency-bound launch.
+// Block column kl+1 of the update of panels k .. kl = k + KW - 1 (what panel
+// kl+1 reads first) in 64x64 quarters of the 128x128 tiles: four times the
+// workgroups of the tile grid, which is only t + kl + 1 tiles, for a short
+// latency-bound launch.
+template <int KW>
 __global__ __launch_bounds__(256) void col_update_kernel(float* __restrict__ A, float* __restrict__ Y,
                                                          int64_t n_pad, int k, int nblk) {
   __shared__ __attribute__((aligned(16))) unsigned char ldsb[X6Lds<64>::SHORT];
   float* lds = reinterpret_cast<float*>(ldsb);
-  const int64_t t = nblk - k - 1;
+  const int kl = k + KW - 1;
+  const int64_t t = nblk - kl - 1;
   int64_t idx = blockIdx.x >> 2;
   const int qr = (blockIdx.x >> 1) & 1, qc = blockIdx.x & 1;
   float* C;
   const float *P, *Q;
   if (idx < t) {
-    // SYRK tile (k+1+idx, k+1); its quarter above the diagonal is not needed
+    // SYRK tile (kl+1+idx, kl+1); its quarter above the diagonal is not needed
     if (idx == 0 && qr < qc) return;
-    const int64_t lb = k + 1 + idx, mb = k + 1;
+    const int64_t lb = kl + 1 + idx, mb = kl + 1;
     C = A + lb * NB * n_pad + mb * NB;
     P = A + lb * NB * n_pad + (int64_t)k * NB;
     Q = A + mb * NB * n_pad + (int64_t)k * NB;
   } else {
-    // inverse tile (c, k+1)
-    const int64_t c = idx - t, lb = k + 1;
+    // inverse tile (c, kl+1)
+    const int64_t c = idx - t, lb = kl + 1;
     C = Y + c * NB * n_pad + lb * NB;
     P = Y + c * NB * n_pad + (int64_t)k * NB;
     Q = A + lb * NB * n_pad + (int64_t)k * NB;
   }
-  // the quarter of C and both operands are requested before the first product
+  // the quarter of C and (K = 128) both operands are requested before the
+  // first product; K = 256 streams its chunks two ahead
   float* Cq = C + (int64_t)qr * 64 * n_pad + qc * 64;
   CTileV<64> ct;
   ct.load(Cq, n_pad, 64);
-  RowsX6V<64, true> pl{P + (int64_t)qr * 64 * n_pad, n_pad, 64, NB};
-  RowsX6V<64, true> ql{Q + (int64_t)qc * 64 * n_pad, n_pad, 64, NB};
+  RowsX6V<64, true> pl{P + (int64_t)qr * 64 * n_pad, n_pad, 64, KW * NB};
+  RowsX6V<64, true> ql{Q + (int64_t)qc * 64 * n_pad, n_pad, 64, KW * NB};
   TileAccT<64> acc;
   tile_zero(acc);
-  tile_gemm_x6_short<64, NB / GBK>(acc, pl, ql, NB, ldsb);
+  if constexpr (KW == 1)
+    tile_gemm_x6_short<64, NB / GBK>(acc, pl, ql, NB, ldsb);
+  else
+    tile_gemm_x6(acc, pl, ql, KW * NB, ldsb);
   tile_sub_pre(Cq, n_pad, 64, ct, acc, lds);
 }
 
 // Look-ahead step in one launch: workgroups [0, nblk * 128 / R) factor panel
-// k+1 and transform its blocks (R rows each) while the others apply the rest
-// of panel k's trailing update (the tiles outside block column k+1, which
-// panel k+1 does not read).  The panel's workgroups come first in the grid,
+// kl+1 and transform its blocks (R rows each) while the others apply the rest
+// of the update of panels k .. kl (the tiles outside block column kl+1, which
+// panel kl+1 does not read).  The panel's workgroups come first in the grid,
 // so they are dispatched first.
-template <int R>
+template <int R, int KW>
 __global__ __launch_bounds__(256) void panel_rest_kernel(float* __restrict__ A, float* __restrict__ Y,
                                                          int64_t n_pad, int k, int nblk, int64_t n,
                                                          int32_t* info) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int parts = NB / R;
   if ((int)blockIdx.x < nblk * parts)
-    panel_body<R>(*reinterpret_cast<PanelLds*>(smem), A, Y, n_pad, k + 1, n, info, blockIdx.x / parts,
+    panel_body<R>(*reinterpret_cast<PanelLds*>(smem), A, Y, n_pad, k + KW, n, info, blockIdx.x / parts,
                   blockIdx.x % parts);
   else
-    update_body(reinterpret_cast<float*>(smem), A, Y, n_pad, k, nblk, UPD_REST,
-                (int64_t)blockIdx.x - nblk * parts);
+    update_body<KW>(reinterpret_cast<float*>(smem), A, Y, n_pad, k, nblk, UPD_REST,
+                    (int64_t)blockIdx.x - nblk * parts);
 }
 
-// The rest of panel k's trailing update on its own (the panel launch runs
-// beside it on a second stream): 66 KB of LDS per workgroup, two per CU.
+// The rest of the update of panels k .. k + KW - 1 on its own (the panel
+// launch runs beside it on a second stream): 66 KB of LDS per workgroup, two
+// per CU.
+template <int KW>
 __global__ __launch_bounds__(256, 2) void rest_update_kernel(float* __restrict__ A, float* __restrict__ Y,
                                                              int64_t n_pad, int k, int nblk) {
   __shared__ __attribute__((aligned(16))) unsigned char ldsb[X6Lds<NB>::SIZE];
-  update_body(reinterpret_cast<float*>(ldsb), A, Y, n_pad, k, nblk, UPD_REST, blockIdx.x);
+  update_body<KW>(reinterpret_cast<float*>(ldsb), A, Y, n_pad, k, nblk, UPD_REST, blockIdx.x);
 }
 
 // The panel chain (factor A_kk, invert it, transform the block column) is
@@ -603,30 +621,52 @@ __global__ __launch_bounds__(256, 2) void rest_update_kernel(float* __restrict__
 // split over 128 / R workgroups per block (each repeats the 128 x 128
 // factorisation, which is latency bound) while that keeps the panel launch
 // within one workgroup per CU.
-// One stream: panel 0, then per k the next-column update of panel k and one
-// launch holding panel k+1 and the rest of panel k's update.
-template <int R>
+//
+// Above n = 4096 the trailing update sets the time, and its read-modify-write
+// of the trailing matrix bounds it: panels go in pairs (PAIRS), so that one
+// pass with K = 256 replaces two with K = 128.  A pair (k, k+1): the update of
+// block column k+1 by panel k, panel k+1 on its own, block column k+2 by both
+// panels, then panel k+2 beside the rest of both panels' update.
+//
+// One stream: panel 0, then per step the next-column update(s) and one launch
+// holding the next panel and the rest of the step's update.
+template <int R, bool PAIRS>
 sg_status run_factor_fused(float* A, float* Y, int64_t n_pad, int nblk, int64_t n, int32_t* info,
                            hipStream_t st) {
   constexpr int parts = NB / R;
   // the LDS limit is a per-device attribute: set on every call (cheap), so
   // that a call on another device finds it set too
   for (const void* f : {reinterpret_cast<const void*>(panel_kernel<R>),
-                        reinterpret_cast<const void*>(panel_rest_kernel<R>)})
+                        reinterpret_cast<const void*>(panel_rest_kernel<R, 1>),
+                        reinterpret_cast<const void*>(panel_rest_kernel<R, 2>)})
     if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PanelLds)) !=
         hipSuccess)
       return set_error(SG_ERR_HIP, "hipFuncSetAttribute(panel kernels) failed");
-  hipLaunchKernelGGL(panel_kernel<R>, dim3((unsigned)(nblk * parts)), dim3(256), sizeof(PanelLds), st, A, Y,
-                     n_pad, 0, n, info);
+  const dim3 pgrid((unsigned)(nblk * parts)), blk(256);
+  hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, 0, n, info);
   if (sg_status e = check_launch("factor panel")) return e;
-  for (int k = 0; k + 1 < nblk; ++k) {
-    hipLaunchKernelGGL(col_update_kernel, dim3((unsigned)(4 * update_tiles(k, nblk, UPD_COL))), dim3(256), 0,
+  for (int k = 0; k + 1 < nblk;) {
+    hipLaunchKernelGGL(col_update_kernel<1>, dim3((unsigned)(4 * update_tiles(k, 1, nblk, UPD_COL))), blk, 0,
                        st, A, Y, n_pad, k, nblk);
     if (sg_status e = check_launch("factor update (next column)")) return e;
-    const int64_t rest = update_tiles(k, nblk, UPD_REST);
-    hipLaunchKernelGGL(panel_rest_kernel<R>, dim3((unsigned)(nblk * parts + rest)), dim3(256),
-                       sizeof(PanelLds), st, A, Y, n_pad, k, nblk, n, info);
-    if (sg_status e = check_launch("factor panel + rest of update")) return e;
+    if (PAIRS && k + 2 < nblk) {
+      hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, k + 1, n, info);
+      if (sg_status e = check_launch("factor panel")) return e;
+      hipLaunchKernelGGL(col_update_kernel<2>, dim3((unsigned)(4 * update_tiles(k, 2, nblk, UPD_COL))), blk,
+                         0, st, A, Y, n_pad, k, nblk);
+      if (sg_status e = check_launch("factor update (next column, two panels)")) return e;
+      const int64_t rest = update_tiles(k, 2, nblk, UPD_REST);
+      hipLaunchKernelGGL((panel_rest_kernel<R, 2>), dim3((unsigned)(nblk * parts + rest)), blk,
+                         sizeof(PanelLds), st, A, Y, n_pad, k, nblk, n, info);
+      if (sg_status e = check_launch("factor panel + rest of update")) return e;
+      k += 2;
+    } else {
+      const int64_t rest = update_tiles(k, 1, nblk, UPD_REST);
+      hipLaunchKernelGGL((panel_rest_kernel<R, 1>), dim3((unsigned)(nblk * parts + rest)), blk,
+                         sizeof(PanelLds), st, A, Y, n_pad, k, nblk, n, info);
+      if (sg_status e = check_launch("factor panel + rest of update")) return e;
+      k += 1;
+    }
   }
   return SG_OK;
 }
@@ -634,7 +674,9 @@ sg_status run_factor_fused(float* A, float* Y, int64_t n_pad, int nblk, int64_t 
 // Two streams: the rest of each step's update runs on the caller's update
 // stream with two workgroups per CU instead of sharing a launch (and its
 // 135 KB of LDS per workgroup) with the panel.  The two caller events order
-// the streams: ev_panel after each panel, ev_rest after each rest update.
+// the streams: ev_panel once the panels a rest update reads are done,
+// ev_rest after each rest update.  Same steps and pairs as the one-stream
+// form, so the same result bit for bit.
 struct SideStream {
   hipStream_t s;
   hipEvent_t ev_panel, ev_rest;
@@ -650,34 +692,50 @@ sg_status run_factor_split(float* A, float* Y, int64_t n_pad, int nblk, int64_t 
   const auto api = [](hipError_t r, const char* what) -> sg_status {
     return r == hipSuccess ? SG_OK : set_error(SG_ERR_HIP, "factor: %s failed", what);
   };
-  // Caller's stream: panel 0, then per k the next-column update of panel k
-  // (after the rest of panel k-1's update, which covers that column) and
-  // panel k+1.  Update stream: the rest of panel k's update, after panel k,
-  // beside the next-column update and panel k+1.
-  hipLaunchKernelGGL(panel_kernel<R>, dim3((unsigned)(nblk * parts)), dim3(256), sizeof(PanelLds), st, A, Y,
-                     n_pad, 0, n, info);
+  const dim3 pgrid((unsigned)(nblk * parts)), blk(256);
+  // Caller's stream: panel 0; per step (after the previous step's rest
+  // update, which covers the next block column) the next-column update(s),
+  // the pair's second panel, and the next panel.  Update stream: the rest of
+  // the step's update, once its panels are done, beside the next panel.
+  hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, 0, n, info);
   if (sg_status e = check_launch("factor panel")) return e;
   if (sg_status e = api(hipEventRecord(ss->ev_panel, st), "event record")) return e;
-  for (int k = 0; k + 1 < nblk; ++k) {
-    if (k > 0)
+  bool pending = false;  // a rest update was enqueued on the update stream
+  for (int k = 0; k + 1 < nblk;) {
+    if (pending)
       if (sg_status e = api(hipStreamWaitEvent(st, ss->ev_rest, 0), "stream wait")) return e;
-    hipLaunchKernelGGL(col_update_kernel, dim3((unsigned)(4 * update_tiles(k, nblk, UPD_COL))), dim3(256), 0,
+    const int kw = (k + 2 < nblk) ? 2 : 1;
+    hipLaunchKernelGGL(col_update_kernel<1>, dim3((unsigned)(4 * update_tiles(k, 1, nblk, UPD_COL))), blk, 0,
                        st, A, Y, n_pad, k, nblk);
     if (sg_status e = check_launch("factor update (next column)")) return e;
-    if (sg_status e = api(hipStreamWaitEvent(ss->s, ss->ev_panel, 0), "stream wait")) return e;
-    const int64_t rest = update_tiles(k, nblk, UPD_REST);
-    if (rest > 0) {
-      hipLaunchKernelGGL(rest_update_kernel, dim3((unsigned)rest), dim3(256), 0, ss->s, A, Y, n_pad, k, nblk);
-      if (sg_status e = check_launch("factor update (rest)")) return e;
+    if (kw == 2) {
+      hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, k + 1, n, info);
+      if (sg_status e = check_launch("factor panel")) return e;
+      if (sg_status e = api(hipEventRecord(ss->ev_panel, st), "event record")) return e;
+      hipLaunchKernelGGL(col_update_kernel<2>, dim3((unsigned)(4 * update_tiles(k, 2, nblk, UPD_COL))), blk,
+                         0, st, A, Y, n_pad, k, nblk);
+      if (sg_status e = check_launch("factor update (next column, two panels)")) return e;
     }
-    if (sg_status e = api(hipEventRecord(ss->ev_rest, ss->s), "event record")) return e;
-    hipLaunchKernelGGL(panel_kernel<R>, dim3((unsigned)(nblk * parts)), dim3(256), sizeof(PanelLds), st, A, Y,
-                       n_pad, k + 1, n, info);
+    const int64_t rest = update_tiles(k, kw, nblk, UPD_REST);
+    if (rest > 0) {
+      if (sg_status e = api(hipStreamWaitEvent(ss->s, ss->ev_panel, 0), "stream wait")) return e;
+      if (kw == 2)
+        hipLaunchKernelGGL(rest_update_kernel<2>, dim3((unsigned)rest), blk, 0, ss->s, A, Y, n_pad, k, nblk);
+      else
+        hipLaunchKernelGGL(rest_update_kernel<1>, dim3((unsigned)rest), blk, 0, ss->s, A, Y, n_pad, k, nblk);
+      if (sg_status e = check_launch("factor update (rest)")) return e;
+      if (sg_status e = api(hipEventRecord(ss->ev_rest, ss->s), "event record")) return e;
+      pending = true;
+    } else {
+      pending = false;
+    }
+    hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, k + kw, n, info);
     if (sg_status e = check_launch("factor panel")) return e;
     if (sg_status e = api(hipEventRecord(ss->ev_panel, st), "event record")) return e;
+    k += kw;
   }
   // join: the caller's stream waits for the last trailing update
-  if (nblk > 1)
+  if (pending)
     if (sg_status e = api(hipStreamWaitEvent(st, ss->ev_rest, 0), "stream wait")) return e;
   return SG_OK;
 }
@@ -742,12 +800,12 @@ sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double dam
   // the single-stream fused form serves every n.
   sg_status e;
   if (nblk * 8 <= kNumCU) {
-    e = run_factor_fused<32>(A, Y, n_pad, nblk, n, info, st);
+    e = run_factor_fused<32, false>(A, Y, n_pad, nblk, n, info, st);
   } else if (side != nullptr) {
     const SideStream ss{side, ev_a, ev_b};
     e = run_factor_split<128>(A, Y, n_pad, nblk, n, info, st, &ss);
   } else {
-    e = run_factor_fused<128>(A, Y, n_pad, nblk, n, info, st);
+    e = run_factor_fused<128, true>(A, Y, n_pad, nblk, n, info, st);
   }
   if (e != SG_OK) return e;
   const unsigned tn = (unsigned)ceil_div(n, 64);

@@ -131,41 +131,84 @@ def check_in(offs, extent, what):
     assert offs.min() >= 0 and offs.max() < extent, (what, int(offs.min()), int(offs.max()), extent)
 
 
+@pytest.mark.parametrize("kw", [1, 2])
 @pytest.mark.parametrize("n", [200, 1000, 4096, 4224, 11008, 28672])
-def test_col_update_offsets(n):
-    """col_update_kernel for every panel step k: C quarter, P and Q loaders
-    (RowsX6V<64, true>, K = 128, four chunks) against the n_pad x n_pad A and
-    Y matrices."""
+def test_col_update_offsets(n, kw):
+    """col_update_kernel<KW> for every panel step k: block column kl + 1 of the
+    update of panels k .. kl = k + kw - 1 (kw = 2 pairs two panels, K = 256,
+    streamed by the pipelined core; kw = 1 is the two-buffer core, K = 128):
+    the C quarter and the P and Q loaders (RowsX6V<64, true>) against the
+    n_pad x n_pad A and Y matrices."""
     n_pad = cdiv(n, NB) * NB
     nblk = n_pad // NB
     ext = n_pad * n_pad
-    ks = range(nblk - 1) if nblk <= 40 else list(range(3)) + list(range(nblk - 4, nblk - 1))
+    ks = [k for k in range(nblk) if k + kw < nblk]
+    if nblk > 40:
+        ks = ks[:3] + ks[-4:]
     for k in ks:
-        t = nblk - k - 1
-        tiles = t + k + 1
+        kl = k + kw - 1
+        t = nblk - kl - 1
+        tiles = t + kl + 1
         for bid in range(4 * tiles):
             idx, qr, qc = bid >> 2, (bid >> 1) & 1, bid & 1
             if idx < t:
                 if idx == 0 and qr < qc:
                     continue
-                lb, mb = k + 1 + idx, k + 1
+                lb, mb = kl + 1 + idx, kl + 1
                 C = lb * NB * n_pad + mb * NB          # into A
                 P = lb * NB * n_pad + k * NB           # into A
                 Q = mb * NB * n_pad + k * NB           # into A
             else:
-                c, lb = idx - t, k + 1
+                c, lb = idx - t, kl + 1
                 C = c * NB * n_pad + lb * NB           # into Y
                 P = c * NB * n_pad + k * NB            # into Y
                 Q = lb * NB * n_pad + k * NB           # into A
+            # the K = kw * 128 columns read stay in the row (and, for kw = 2,
+            # are block columns k and k + 1)
+            assert (P % n_pad) + kw * NB <= n_pad and (Q % n_pad) + kw * NB <= n_pad
             Cq = C + qr * 64 * n_pad + qc * 64
             rd, wr = ctile_rows(64, 64)
             for (r, c4) in rd + wr:
                 check_in(Cq + r[:, None] * n_pad + c4[:, None] + np.arange(4), ext, ("C", n, k, bid))
-            for c in range(NB // GBK):
-                check_in(P + qr * 64 * n_pad + rows_x6v_load(64, True, n_pad, 64, NB, c * GBK), ext,
+            for c in range(kw * NB // GBK):
+                check_in(P + qr * 64 * n_pad + rows_x6v_load(64, True, n_pad, 64, kw * NB, c * GBK), ext,
                          ("P", n, k, bid, c))
-                check_in(Q + qc * 64 * n_pad + rows_x6v_load(64, True, n_pad, 64, NB, c * GBK), ext,
+                check_in(Q + qc * 64 * n_pad + rows_x6v_load(64, True, n_pad, 64, kw * NB, c * GBK), ext,
                          ("Q", n, k, bid, c))
+
+
+@pytest.mark.parametrize("n", [4224, 11008, 28672])
+def test_paired_rest_update_tiles(n):
+    """update_body<2> (UPD_REST) tile map: every SYRK tile lies in A's lower
+    block triangle beyond block column k + 2, every inverse tile in Y's upper
+    block triangle, and both operands' K = 256 columns are block columns k,
+    k + 1 of the same rows."""
+    n_pad = cdiv(n, NB) * NB
+    nblk = n_pad // NB
+    for k in [0, 1, nblk // 2, nblk - 4, nblk - 3]:
+        if k + 2 >= nblk:
+            continue
+        kl = k + 1
+        s0 = kl + 2
+        ts = nblk - s0
+        nsyrk = ts * (ts + 1) // 2
+        t = nblk - kl - 1
+        total = (t - 1) * t // 2 + (kl + 1) * (t - 1)
+        assert total == nsyrk + (kl + 1) * ts
+        seen = set()
+        for idx in range(total):
+            if idx < nsyrk:
+                l = (math.isqrt(8 * idx + 1) - 1) // 2
+                m = idx - l * (l + 1) // 2
+                lb, mb = s0 + l, s0 + m
+                assert s0 <= mb <= lb < nblk
+                seen.add(("A", lb, mb))
+            else:
+                j = idx - nsyrk
+                c, lb = j % (kl + 1), s0 + j // (kl + 1)
+                assert c <= kl < lb < nblk
+                seen.add(("Y", c, lb))
+        assert len(seen) == total  # each tile once
 
 
 def lazy_launches(m, n, B):
