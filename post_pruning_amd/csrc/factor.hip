@@ -36,6 +36,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace sg {
 namespace {
 
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(1024) void damp_lambda_kernel(const float* __restri
 
 // A = J (H + lam I) J on the lower block triangle (identity tail for padding);
 // Y = I (zero below the diagonal, so its lower block triangle is zero too:
-// the paired updates read Y[k+1][k]).  64x64 tiles.
+// the grouped updates read Y[c][k .. c-1]).  64x64 tiles.
 __global__ __launch_bounds__(256) void flip_init_kernel(const float* __restrict__ H, int64_t n,
                                                         int64_t n_pad,
                                                         const float* __restrict__ lam_p,
@@ -473,17 +475,17 @@ __device__ inline int64_t isqrt_floor(int64_t x) {
   return r;
 }
 
-// Trailing-update tiles of panels k .. kl = k + kw - 1 (kw = 1: K = 128;
-// kw = 2: the two panels' updates in one pass, K = 256), in three subsets:
+// Trailing-update tiles of panels k .. kl = k + kw - 1 (K = 128 kw: the
+// group's updates in one pass), in three subsets:
 //   UPD_ALL   every tile;
 //   UPD_COL   the tiles of block column kl+1 only (what panel kl+1 needs;
 //             run by col_update_kernel in 64x64 quarters);
 //   UPD_REST  every other tile (run beside panel kl+1).
 // SYRK tiles (l, m), kl < m <= l: A[l,m] -= L[l,k:kl+1] L[m,k:kl+1]^T.
 // Inverse tiles (c, l), c <= kl < l: R[c,l] -= Y[c,k:kl+1] L[l,k:kl+1]^T
-// (for kw = 2 and c = kl, Y[kl][k] lies in Y's lower block triangle, which
-// is zero).  Pairing halves the passes over the trailing matrix, whose
-// read-modify-write bounds the update at large n.
+// (for c > k the terms Y[c][k .. c-1] lie in Y's lower block triangle,
+// which is zero).  Grouping divides the passes over the trailing matrix,
+// whose read-modify-write bounds the update at large n, by kw.
 enum { UPD_ALL = 0, UPD_COL = 1, UPD_REST = 2 };
 
 __host__ __device__ inline int64_t update_tiles(int k, int kw, int nblk, int mode) {
@@ -572,7 +574,7 @@ __global__ __launch_bounds__(256) void col_update_kernel(float* __restrict__ A, 
     Q = A + lb * NB * n_pad + (int64_t)k * NB;
   }
   // the quarter of C and (K = 128) both operands are requested before the
-  // first product; K = 256 streams its chunks two ahead
+  // first product; K >= 256 streams its chunks two ahead
   float* Cq = C + (int64_t)qr * 64 * n_pad + qc * 64;
   CTileV<64> ct;
   ct.load(Cq, n_pad, 64);
@@ -623,14 +625,56 @@ __global__ __launch_bounds__(256, 2) void rest_update_kernel(float* __restrict__
 // within one workgroup per CU.
 //
 // Above n = 4096 the trailing update sets the time, and its read-modify-write
-// of the trailing matrix bounds it: panels go in pairs (PAIRS), so that one
-// pass with K = 256 replaces two with K = 128.  A pair (k, k+1): the update of
-// block column k+1 by panel k, panel k+1 on its own, block column k+2 by both
-// panels, then panel k+2 beside the rest of both panels' update.
-//
-// One stream: panel 0, then per step the next-column update(s) and one launch
-// holding the next panel and the rest of the step's update.
-template <int R, bool PAIRS>
+// of the trailing matrix bounds it: panels go in groups of up to KWMAX, so
+// that one pass with K = 128 kw replaces kw passes with K = 128.  A group of
+// kw panels from k: for j = 1 .. kw - 1, block column k+j by panels k ..
+// k+j-1 (K = 128 j) and then panel k+j on its own; block column k+kw by the
+// whole group; then panel k+kw beside the rest of the group's update.
+constexpr int KWMAX = 4;
+
+// host launchers of the templates by group width (1 .. KWMAX)
+sg_status launch_col_update(int kw, float* A, float* Y, int64_t n_pad, int k, int nblk, hipStream_t st) {
+  const dim3 grid((unsigned)(4 * update_tiles(k, kw, nblk, UPD_COL))), blk(256);
+  switch (kw) {
+    case 1: hipLaunchKernelGGL(col_update_kernel<1>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
+    case 2: hipLaunchKernelGGL(col_update_kernel<2>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
+    case 3: hipLaunchKernelGGL(col_update_kernel<3>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
+    default: hipLaunchKernelGGL(col_update_kernel<4>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
+  }
+  return check_launch("factor update (next column)");
+}
+
+sg_status launch_rest_update(int kw, float* A, float* Y, int64_t n_pad, int k, int nblk, int64_t rest,
+                             hipStream_t st) {
+  const dim3 grid((unsigned)rest), blk(256);
+  switch (kw) {
+    case 1: hipLaunchKernelGGL(rest_update_kernel<1>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
+    case 2: hipLaunchKernelGGL(rest_update_kernel<2>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
+    case 3: hipLaunchKernelGGL(rest_update_kernel<3>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
+    default: hipLaunchKernelGGL(rest_update_kernel<4>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
+  }
+  return check_launch("factor update (rest)");
+}
+
+template <int R>
+sg_status launch_panel_rest(int kw, float* A, float* Y, int64_t n_pad, int k, int nblk, int64_t n, int32_t* info,
+                            int64_t rest, hipStream_t st) {
+  constexpr int parts = NB / R;
+  const dim3 grid((unsigned)(nblk * parts + rest)), blk(256);
+  const size_t lds = sizeof(PanelLds);
+  switch (kw) {
+    case 1: hipLaunchKernelGGL((panel_rest_kernel<R, 1>), grid, blk, lds, st, A, Y, n_pad, k, nblk, n, info); break;
+    case 2: hipLaunchKernelGGL((panel_rest_kernel<R, 2>), grid, blk, lds, st, A, Y, n_pad, k, nblk, n, info); break;
+    case 3: hipLaunchKernelGGL((panel_rest_kernel<R, 3>), grid, blk, lds, st, A, Y, n_pad, k, nblk, n, info); break;
+    default: hipLaunchKernelGGL((panel_rest_kernel<R, 4>), grid, blk, lds, st, A, Y, n_pad, k, nblk, n, info); break;
+  }
+  return check_launch("factor panel + rest of update");
+}
+
+// One stream: panel 0, then per group the next-column updates and panels of
+// the group, and one launch holding the next panel and the rest of the
+// group's update.  GROUPS = false: single panels (kw = 1).
+template <int R, bool GROUPS>
 sg_status run_factor_fused(float* A, float* Y, int64_t n_pad, int nblk, int64_t n, int32_t* info,
                            hipStream_t st) {
   constexpr int parts = NB / R;
@@ -638,7 +682,9 @@ sg_status run_factor_fused(float* A, float* Y, int64_t n_pad, int nblk, int64_t 
   // that a call on another device finds it set too
   for (const void* f : {reinterpret_cast<const void*>(panel_kernel<R>),
                         reinterpret_cast<const void*>(panel_rest_kernel<R, 1>),
-                        reinterpret_cast<const void*>(panel_rest_kernel<R, 2>)})
+                        reinterpret_cast<const void*>(panel_rest_kernel<R, 2>),
+                        reinterpret_cast<const void*>(panel_rest_kernel<R, 3>),
+                        reinterpret_cast<const void*>(panel_rest_kernel<R, 4>)})
     if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PanelLds)) !=
         hipSuccess)
       return set_error(SG_ERR_HIP, "hipFuncSetAttribute(panel kernels) failed");
@@ -646,37 +692,27 @@ sg_status run_factor_fused(float* A, float* Y, int64_t n_pad, int nblk, int64_t 
   hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, 0, n, info);
   if (sg_status e = check_launch("factor panel")) return e;
   for (int k = 0; k + 1 < nblk;) {
-    hipLaunchKernelGGL(col_update_kernel<1>, dim3((unsigned)(4 * update_tiles(k, 1, nblk, UPD_COL))), blk, 0,
-                       st, A, Y, n_pad, k, nblk);
-    if (sg_status e = check_launch("factor update (next column)")) return e;
-    if (PAIRS && k + 2 < nblk) {
-      hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, k + 1, n, info);
+    const int kw = GROUPS ? std::min(KWMAX, nblk - 1 - k) : 1;
+    for (int j = 1; j < kw; ++j) {
+      if (sg_status e = launch_col_update(j, A, Y, n_pad, k, nblk, st)) return e;
+      hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, k + j, n, info);
       if (sg_status e = check_launch("factor panel")) return e;
-      hipLaunchKernelGGL(col_update_kernel<2>, dim3((unsigned)(4 * update_tiles(k, 2, nblk, UPD_COL))), blk,
-                         0, st, A, Y, n_pad, k, nblk);
-      if (sg_status e = check_launch("factor update (next column, two panels)")) return e;
-      const int64_t rest = update_tiles(k, 2, nblk, UPD_REST);
-      hipLaunchKernelGGL((panel_rest_kernel<R, 2>), dim3((unsigned)(nblk * parts + rest)), blk,
-                         sizeof(PanelLds), st, A, Y, n_pad, k, nblk, n, info);
-      if (sg_status e = check_launch("factor panel + rest of update")) return e;
-      k += 2;
-    } else {
-      const int64_t rest = update_tiles(k, 1, nblk, UPD_REST);
-      hipLaunchKernelGGL((panel_rest_kernel<R, 1>), dim3((unsigned)(nblk * parts + rest)), blk,
-                         sizeof(PanelLds), st, A, Y, n_pad, k, nblk, n, info);
-      if (sg_status e = check_launch("factor panel + rest of update")) return e;
-      k += 1;
     }
+    if (sg_status e = launch_col_update(kw, A, Y, n_pad, k, nblk, st)) return e;
+    if (sg_status e = launch_panel_rest<R>(kw, A, Y, n_pad, k, nblk, n, info,
+                                           update_tiles(k, kw, nblk, UPD_REST), st))
+      return e;
+    k += kw;
   }
   return SG_OK;
 }
 
-// Two streams: the rest of each step's update runs on the caller's update
+// Two streams: the rest of each group's update runs on the caller's update
 // stream with two workgroups per CU instead of sharing a launch (and its
 // 135 KB of LDS per workgroup) with the panel.  The two caller events order
 // the streams: ev_panel once the panels a rest update reads are done,
-// ev_rest after each rest update.  Same steps and pairs as the one-stream
-// form, so the same result bit for bit.
+// ev_rest after each rest update.  Same groups as the one-stream form, so
+// the same result bit for bit.
 struct SideStream {
   hipStream_t s;
   hipEvent_t ev_panel, ev_rest;
@@ -693,37 +729,28 @@ sg_status run_factor_split(float* A, float* Y, int64_t n_pad, int nblk, int64_t 
     return r == hipSuccess ? SG_OK : set_error(SG_ERR_HIP, "factor: %s failed", what);
   };
   const dim3 pgrid((unsigned)(nblk * parts)), blk(256);
-  // Caller's stream: panel 0; per step (after the previous step's rest
-  // update, which covers the next block column) the next-column update(s),
-  // the pair's second panel, and the next panel.  Update stream: the rest of
-  // the step's update, once its panels are done, beside the next panel.
+  // Caller's stream: panel 0; per group (after the previous group's rest
+  // update, which covers the next block columns) the next-column updates,
+  // the group's other panels, and the next panel.  Update stream: the rest
+  // of the group's update, once its panels are done, beside the next panel.
   hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, 0, n, info);
   if (sg_status e = check_launch("factor panel")) return e;
-  if (sg_status e = api(hipEventRecord(ss->ev_panel, st), "event record")) return e;
   bool pending = false;  // a rest update was enqueued on the update stream
   for (int k = 0; k + 1 < nblk;) {
     if (pending)
       if (sg_status e = api(hipStreamWaitEvent(st, ss->ev_rest, 0), "stream wait")) return e;
-    const int kw = (k + 2 < nblk) ? 2 : 1;
-    hipLaunchKernelGGL(col_update_kernel<1>, dim3((unsigned)(4 * update_tiles(k, 1, nblk, UPD_COL))), blk, 0,
-                       st, A, Y, n_pad, k, nblk);
-    if (sg_status e = check_launch("factor update (next column)")) return e;
-    if (kw == 2) {
-      hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, k + 1, n, info);
+    const int kw = std::min(KWMAX, nblk - 1 - k);
+    for (int j = 1; j < kw; ++j) {
+      if (sg_status e = launch_col_update(j, A, Y, n_pad, k, nblk, st)) return e;
+      hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, k + j, n, info);
       if (sg_status e = check_launch("factor panel")) return e;
-      if (sg_status e = api(hipEventRecord(ss->ev_panel, st), "event record")) return e;
-      hipLaunchKernelGGL(col_update_kernel<2>, dim3((unsigned)(4 * update_tiles(k, 2, nblk, UPD_COL))), blk,
-                         0, st, A, Y, n_pad, k, nblk);
-      if (sg_status e = check_launch("factor update (next column, two panels)")) return e;
     }
+    if (sg_status e = api(hipEventRecord(ss->ev_panel, st), "event record")) return e;
+    if (sg_status e = launch_col_update(kw, A, Y, n_pad, k, nblk, st)) return e;
     const int64_t rest = update_tiles(k, kw, nblk, UPD_REST);
     if (rest > 0) {
       if (sg_status e = api(hipStreamWaitEvent(ss->s, ss->ev_panel, 0), "stream wait")) return e;
-      if (kw == 2)
-        hipLaunchKernelGGL(rest_update_kernel<2>, dim3((unsigned)rest), blk, 0, ss->s, A, Y, n_pad, k, nblk);
-      else
-        hipLaunchKernelGGL(rest_update_kernel<1>, dim3((unsigned)rest), blk, 0, ss->s, A, Y, n_pad, k, nblk);
-      if (sg_status e = check_launch("factor update (rest)")) return e;
+      if (sg_status e = launch_rest_update(kw, A, Y, n_pad, k, nblk, rest, ss->s)) return e;
       if (sg_status e = api(hipEventRecord(ss->ev_rest, ss->s), "event record")) return e;
       pending = true;
     } else {
@@ -731,7 +758,6 @@ sg_status run_factor_split(float* A, float* Y, int64_t n_pad, int nblk, int64_t 
     }
     hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, k + kw, n, info);
     if (sg_status e = check_launch("factor panel")) return e;
-    if (sg_status e = api(hipEventRecord(ss->ev_panel, st), "event record")) return e;
     k += kw;
   }
   // join: the caller's stream waits for the last trailing update

@@ -131,11 +131,11 @@ def check_in(offs, extent, what):
     assert offs.min() >= 0 and offs.max() < extent, (what, int(offs.min()), int(offs.max()), extent)
 
 
-@pytest.mark.parametrize("kw", [1, 2])
+@pytest.mark.parametrize("kw", [1, 2, 3, 4])
 @pytest.mark.parametrize("n", [200, 1000, 4096, 4224, 11008, 28672])
 def test_col_update_offsets(n, kw):
     """col_update_kernel<KW> for every panel step k: block column kl + 1 of the
-    update of panels k .. kl = k + kw - 1 (kw = 2 pairs two panels, K = 256,
+    update of panels k .. kl = k + kw - 1 (kw > 1 groups panels, K = 128 kw,
     streamed by the pipelined core; kw = 1 is the two-buffer core, K = 128):
     the C quarter and the P and Q loaders (RowsX6V<64, true>) against the
     n_pad x n_pad A and Y matrices."""
@@ -149,7 +149,10 @@ def test_col_update_offsets(n, kw):
         kl = k + kw - 1
         t = nblk - kl - 1
         tiles = t + kl + 1
-        for bid in range(4 * tiles):
+        # the first and last tiles of each kind (every other tile's offsets
+        # lie between theirs)
+        idxs = sorted({0, 1, t - 1, t, t + 1, tiles - 2, tiles - 1} & set(range(tiles)))
+        for bid in [4 * i + q for i in idxs for q in range(4)]:
             idx, qr, qc = bid >> 2, (bid >> 1) & 1, bid & 1
             if idx < t:
                 if idx == 0 and qr < qc:
@@ -163,8 +166,8 @@ def test_col_update_offsets(n, kw):
                 C = c * NB * n_pad + lb * NB           # into Y
                 P = c * NB * n_pad + k * NB            # into Y
                 Q = lb * NB * n_pad + k * NB           # into A
-            # the K = kw * 128 columns read stay in the row (and, for kw = 2,
-            # are block columns k and k + 1)
+            # the K = kw * 128 columns read stay in the row (block columns k
+            # .. k + kw - 1)
             assert (P % n_pad) + kw * NB <= n_pad and (Q % n_pad) + kw * NB <= n_pad
             Cq = C + qr * 64 * n_pad + qc * 64
             rd, wr = ctile_rows(64, 64)
@@ -177,18 +180,18 @@ def test_col_update_offsets(n, kw):
                          ("Q", n, k, bid, c))
 
 
+@pytest.mark.parametrize("kw", [2, 3, 4])
 @pytest.mark.parametrize("n", [4224, 11008, 28672])
-def test_paired_rest_update_tiles(n):
-    """update_body<2> (UPD_REST) tile map: every SYRK tile lies in A's lower
-    block triangle beyond block column k + 2, every inverse tile in Y's upper
-    block triangle, and both operands' K = 256 columns are block columns k,
-    k + 1 of the same rows."""
+def test_grouped_rest_update_tiles(n, kw):
+    """update_body<KW> (UPD_REST) tile map: every SYRK tile lies in A's lower
+    block triangle beyond block column k + kw, every inverse tile in Y's upper
+    block triangle, each tile once."""
     n_pad = cdiv(n, NB) * NB
     nblk = n_pad // NB
-    for k in [0, 1, nblk // 2, nblk - 4, nblk - 3]:
-        if k + 2 >= nblk:
+    for k in [0, 1, nblk // 2, nblk - 6, nblk - 1 - kw]:
+        if k < 0 or k + kw >= nblk:
             continue
-        kl = k + 1
+        kl = k + kw - 1
         s0 = kl + 2
         ts = nblk - s0
         nsyrk = ts * (ts + 1) // 2
