@@ -17,7 +17,10 @@ struct HessPlan {
   int64_t tok_per_split;
   int group;           // tile-panel group edge of the per-XCD tile order
   int64_t grid;        // workgroups launched (8 equal per-XCD shares)
-  size_t ws_bytes;     // partials + counters
+  size_t part_bytes;   // split counters + partial tiles (0 without splits)
+  int sync_rounds;     // lockstep rounds per XCD
+  bool sync;           // lockstep counters fit in the workspace
+  size_t ws_bytes;     // partials + split counters + lockstep counters
 };
 HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws);
 sg_status launch_hessian_bf16(float* H, int64_t n, const uint16_t* X, int64_t T,

@@ -21,9 +21,19 @@
 // with its own L2.  Tiles are enumerated in g x g groups of panels (panel =
 // 256 channels), and XCD x takes a contiguous eighth of that order, split-major:
 // the workgroups resident on one XCD then work on a compact set of tiles that
-// share few panels, over the same token range, so most X re-reads hit its L2;
+// share few panels, over the same token range, so X re-reads can hit its L2;
 // the XCDs run the same token range at the same time, which the shared
 // Infinity Cache serves once.
+// Lockstep: left alone, the 32 workgroups of one XCD drift apart by far more
+// tokens than its 4 MB L2 holds, and only about one X read in six hits there
+// (measured at n = 28672).  Each "round" of 32 workgroups of an XCD (those
+// that start together) therefore shares a progress counter: every 32 stages
+// a workgroup adds one, and before the next 32 it waits until all of its
+// round have finished the previous ones.  With that, three reads in four hit
+// the L2 and the fabric traffic falls threefold.  The wait is bounded: a
+// workgroup that polls too long (peers not resident, say, because another
+// kernel holds CUs) stops waiting for the rest of its tile; the counters
+// order nothing that the result depends on.
 #include "sg_internal.h"
 
 #include <math.h>
@@ -37,6 +47,9 @@ constexpr int HT = kHessTile;          // 256
 constexpr int HSPLIT_ALIGN = 64;     // tokens: split boundaries are multiples of this
 constexpr int HTHREADS = 512;
 constexpr int kMinTokPerSplit = 4096;
+constexpr int kCuPerXcd = kNumCU / 8;  // workgroups of one lockstep round
+constexpr int kSyncEvery = 8;          // steady-state iterations (4 stages each) per counter step
+constexpr int kSyncSpin = 400;         // polls before a workgroup stops waiting
 
 __device__ inline void tri_decode(int64_t ti, int& I, int& J) {
   int64_t r = (int64_t)((sqrt(8.0 * (double)ti + 1.0) - 1.0) * 0.5);
@@ -131,7 +144,8 @@ __device__ inline void stage_barrier() {
 __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
     float* __restrict__ H, int n, const uint16_t* __restrict__ X, int64_t T,
     int64_t ldx, int64_t tiles, int splits, int64_t tps, int group,
-    float* __restrict__ part, unsigned* __restrict__ counters) {
+    float* __restrict__ part, unsigned* __restrict__ counters, unsigned* __restrict__ sync,
+    int sync_rounds) {
   // One array per stage.
   __shared__ __attribute__((aligned(16))) unsigned char st0[DSTAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st1[DSTAGE];
@@ -265,6 +279,16 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
   };
+  // Lockstep counter of this workgroup's round (thread 0 alone touches it).
+  // Every workgroup adds qmax in total, the count of a full-length split, so
+  // that the shorter last split does not hold up the others.
+  const int64_t round = jx / kCuPerXcd;
+  const int64_t active = min<int64_t>(kCuPerXcd, cnt * splits - round * kCuPerXcd);
+  unsigned* const my_sync = sync ? sync + (int64_t)xcd * sync_rounds + round : nullptr;
+  const int64_t full_steps = ceil_div(tps, DK);
+  const int64_t qmax = (full_steps > 6 ? (full_steps - 3) / 4 : 0) / kSyncEvery;
+  bool waiting = true;
+  int64_t done = 0;
   int64_t s = 0;
   if (nsteps > 6) {
     __builtin_amdgcn_s_waitcnt(kWaitVm4);  // stages 0 and 1
@@ -272,12 +296,29 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
     Frags f;
     prefetch(st0, f);
     for (; s + 6 < nsteps; s += 4) {
+      const int64_t it = s >> 2;
+      if (my_sync && tid == 0 && waiting && it > 0 && it % kSyncEvery == 0) {
+        // the other waves wait for this one at the next stage barrier
+        const int64_t need = (it / kSyncEvery) * active;
+        int k = 0;
+        for (; k < kSyncSpin; ++k) {
+          if ((int64_t)__hip_atomic_load(my_sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+        if (k == kSyncSpin) waiting = false;
+      }
       step(st0, st1, st3, s, f);
       step(st1, st2, st0, s + 1, f);
       step(st2, st3, st1, s + 2, f);
       step(st3, st0, st2, s + 3, f);
+      if (my_sync && tid == 0 && (it + 1) % kSyncEvery == 0) {
+        __hip_atomic_fetch_add(my_sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ++done;
+      }
     }
   }
+  if (my_sync && tid == 0 && qmax > done)
+    __hip_atomic_fetch_add(my_sync, (unsigned)(qmax - done), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (; s < nsteps; ++s) {
     const int b = (int)(s & 3);
     unsigned char* cur = b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3;
@@ -480,7 +521,17 @@ HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws) {
   p.tok_per_split = round_up(ceil_div(T, best_s), HSPLIT_ALIGN);
   // Recompute the split count actually needed with the rounded split size.
   p.splits = (int)std::max<int64_t>(1, ceil_div(T, p.tok_per_split));
-  p.ws_bytes = p.splits > 1 ? cnt_bytes + tile_bytes * (size_t)p.tiles * p.splits : 0;
+  p.part_bytes = p.splits > 1 ? cnt_bytes + tile_bytes * (size_t)p.tiles * p.splits : 0;
+  // Lockstep counters (8 XCDs x rounds), after the partials, when the tokens
+  // are not split: with splits the workgroups of one round mostly cover
+  // different token ranges, which share nothing in L2 (measured: the counters
+  // then cost 1-2% at n = 4096).  Without room for them in the workspace the
+  // launch runs unsynchronised (same result, more fabric traffic).
+  p.sync_rounds = (int)ceil_div(ceil_div(p.tiles, 8) * p.splits, kCuPerXcd);
+  const size_t sync_bytes =
+      p.splits == 1 ? round_up((int64_t)8 * p.sync_rounds * sizeof(unsigned), 256) : 0;
+  p.ws_bytes = p.part_bytes + sync_bytes;
+  p.sync = sync_bytes > 0 && (!limit_by_ws || ws_avail >= p.ws_bytes);
   // Group edge: about the square root of the tiles an XCD has resident at once
   // (its 32 CUs, or its whole share when that is smaller).
   const double per_xcd = std::min<double>(32.0, (double)p.tiles * p.splits / 8.0) /
@@ -495,6 +546,7 @@ sg_status launch_hessian_bf16(float* H, int64_t n, const uint16_t* X, int64_t T,
                               hipStream_t st) {
   unsigned* counters = nullptr;
   float* part = nullptr;
+  unsigned* sync = nullptr;
   if (plan.splits > 1) {
     counters = reinterpret_cast<unsigned*>(ws);
     part = reinterpret_cast<float*>(static_cast<char*>(ws) +
@@ -503,10 +555,16 @@ sg_status launch_hessian_bf16(float* H, int64_t n, const uint16_t* X, int64_t T,
                        0, st, counters, plan.tiles);
     if (sg_status e = check_launch("hessian counters")) return e;
   }
+  if (plan.sync) {
+    const int64_t cnt = (int64_t)8 * plan.sync_rounds;
+    sync = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + plan.part_bytes);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)ceil_div(cnt, 256)), dim3(256), 0, st, sync, cnt);
+    if (sg_status e = check_launch("hessian lockstep counters")) return e;
+  }
   const int64_t grid = plan.grid;
   hipLaunchKernelGGL(hess_bf16_dma_kernel, dim3((unsigned)grid), dim3(HTHREADS), 0, st, H,
                      (int)n, X, T, ldx, plan.tiles, plan.splits, plan.tok_per_split, plan.group,
-                     part, counters);
+                     part, counters, sync, plan.sync_rounds);
   return check_launch("hessian bf16");
 }
 

@@ -63,8 +63,9 @@ def test_workspace_sizes_pure_host(sg):
     # array.
     tiles = 16 * 17 // 2
     assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 4096, 262144, 0) == 768 + tiles * 7 * 256 * 256 * 4
-    # ... and the large-n case needs no split.
-    assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 28672, 32768, 0) == 0
+    # ... and the large-n case needs no split: only the lockstep counters,
+    # 8 XCDs x ceil(ceil(6328 / 8) / 32) = 25 rounds of 32 workgroups.
+    assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 28672, 32768, 0) == 1024
     assert sg.sg_workspace_bytes(sg.SG_OP_RECON, 64, 128, 512, 0) >= 8
     # invalid arguments give 0
     assert sg.sg_workspace_bytes(sg.SG_OP_PRUNE, 10, 10, 0, 0) == 0

@@ -471,3 +471,27 @@ def test_hessian_bf16_ragged_padded_view(sg, ws):
     assert np.array_equal(Hg, Hg.T)
     Ho = oracle.hessian([Xv.double().numpy()])
     assert _rel(Hg, Ho) <= 1e-5
+
+
+@pytest.mark.gpu
+def test_hessian_lockstep_counters_change_nothing(sg):
+    """The per-XCD lockstep counters only pace the workgroups: with them (the
+    full workspace) and without (one byte short of it) the Hessian is bit for
+    bit the same, and matches the oracle on sampled channels.  24 panels, 300
+    tiles, no token split: 2 rounds of up to 32 workgroups per XCD, 7 counter
+    steps, and a ragged last stage (8000 = 250 x 32 tokens)."""
+    n, T = 6144, 8000
+    gen = torch.Generator().manual_seed(6144)
+    Xv = torch.randn(T, n, generator=gen).to(torch.bfloat16)
+    Xg = Xv.cuda()
+    need = sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, n, T, 0)
+    assert need == 256  # the counters only: 8 x 2 rounds
+    Hs = _gpu_hessian(sg, Xg, n, T, workspace_bytes=need)
+    Hn = _gpu_hessian(sg, Xg, n, T, workspace_bytes=need - 1)
+    torch.cuda.synchronize()
+    assert torch.equal(Hs, Hn)
+    Hg = Hs.cpu().double().numpy()
+    assert np.array_equal(Hg, Hg.T)
+    Xs = Xv[:, ::97].double().numpy()  # 64 sampled channels
+    cols = np.arange(0, n, 97)
+    assert _rel(Hg[np.ix_(cols, cols)], Xs.T @ Xs) <= 1e-5
