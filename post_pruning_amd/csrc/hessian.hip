@@ -27,7 +27,8 @@
 // Lockstep: left alone, the 32 workgroups of one XCD drift apart by far more
 // tokens than its 4 MB L2 holds, and only about one X read in six hits there
 // (measured at n = 28672).  Each "round" of 32 workgroups of an XCD (those
-// that start together) therefore shares a progress counter: every 32 stages
+// that start together, on one token split) therefore shares a progress
+// counter: every 32 stages
 // a workgroup adds one, and before the next 32 it waits until all of its
 // round have finished the previous ones.  With that, three reads in four hit
 // the L2 and the fabric traffic falls threefold.  The wait is bounded: a
@@ -279,16 +280,16 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Lockstep counter of this workgroup's round (thread 0 alone touches it).
-  // Every workgroup adds qmax in total, the count of a full-length split, so
-  // that the shorter last split does not hold up the others.
+  // Lockstep counter of this workgroup's group: the workgroups of its round
+  // (32 consecutive ones of the XCD) that work on the same token split.
+  // Thread 0 alone touches it.
   const int64_t round = jx / kCuPerXcd;
-  const int64_t active = min<int64_t>(kCuPerXcd, cnt * splits - round * kCuPerXcd);
-  unsigned* const my_sync = sync ? sync + (int64_t)xcd * sync_rounds + round : nullptr;
-  const int64_t full_steps = ceil_div(tps, DK);
-  const int64_t qmax = (full_steps > 6 ? (full_steps - 3) / 4 : 0) / kSyncEvery;
+  const int64_t g0 = max<int64_t>(round * kCuPerXcd, (int64_t)split * cnt);
+  const int64_t g1 = min<int64_t>((round + 1) * kCuPerXcd, (int64_t)(split + 1) * cnt);
+  const int64_t active = g1 - g0;
+  unsigned* const my_sync =
+      sync ? sync + ((int64_t)xcd * sync_rounds + round) * splits + split : nullptr;
   bool waiting = true;
-  int64_t done = 0;
   int64_t s = 0;
   if (nsteps > 6) {
     __builtin_amdgcn_s_waitcnt(kWaitVm4);  // stages 0 and 1
@@ -311,14 +312,10 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
       step(st1, st2, st0, s + 1, f);
       step(st2, st3, st1, s + 2, f);
       step(st3, st0, st2, s + 3, f);
-      if (my_sync && tid == 0 && (it + 1) % kSyncEvery == 0) {
+      if (my_sync && tid == 0 && (it + 1) % kSyncEvery == 0)
         __hip_atomic_fetch_add(my_sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ++done;
-      }
     }
   }
-  if (my_sync && tid == 0 && qmax > done)
-    __hip_atomic_fetch_add(my_sync, (unsigned)(qmax - done), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (; s < nsteps; ++s) {
     const int b = (int)(s & 3);
     unsigned char* cur = b == 0 ? st0 : b == 1 ? st1 : b == 2 ? st2 : st3;
@@ -522,14 +519,15 @@ HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws) {
   // Recompute the split count actually needed with the rounded split size.
   p.splits = (int)std::max<int64_t>(1, ceil_div(T, p.tok_per_split));
   p.part_bytes = p.splits > 1 ? cnt_bytes + tile_bytes * (size_t)p.tiles * p.splits : 0;
-  // Lockstep counters (8 XCDs x rounds), after the partials, when the tokens
-  // are not split: with splits the workgroups of one round mostly cover
-  // different token ranges, which share nothing in L2 (measured: the counters
-  // then cost 1-2% at n = 4096).  Without room for them in the workspace the
-  // launch runs unsynchronised (same result, more fabric traffic).
+  // Lockstep counters (8 XCDs x rounds x splits), after the partials, when
+  // the tokens are not split.  With splits, groups of one split per round
+  // were measured too (n = 4096, 7 splits): no gain, the tiles of a split
+  // already share their panels in L2 at about the rate the counters give.
+  // Without room for the counters in the workspace the launch runs
+  // unsynchronised (same result, more fabric traffic).
   p.sync_rounds = (int)ceil_div(ceil_div(p.tiles, 8) * p.splits, kCuPerXcd);
   const size_t sync_bytes =
-      p.splits == 1 ? round_up((int64_t)8 * p.sync_rounds * sizeof(unsigned), 256) : 0;
+      p.splits == 1 ? round_up((int64_t)8 * p.sync_rounds * p.splits * sizeof(unsigned), 256) : 0;
   p.ws_bytes = p.part_bytes + sync_bytes;
   p.sync = sync_bytes > 0 && (!limit_by_ws || ws_avail >= p.ws_bytes);
   // Group edge: about the square root of the tiles an XCD has resident at once
@@ -556,7 +554,7 @@ sg_status launch_hessian_bf16(float* H, int64_t n, const uint16_t* X, int64_t T,
     if (sg_status e = check_launch("hessian counters")) return e;
   }
   if (plan.sync) {
-    const int64_t cnt = (int64_t)8 * plan.sync_rounds;
+    const int64_t cnt = (int64_t)8 * plan.sync_rounds * plan.splits;
     sync = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + plan.part_bytes);
     hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)ceil_div(cnt, 256)), dim3(256), 0, st, sync, cnt);
     if (sg_status e = check_launch("hessian lockstep counters")) return e;
