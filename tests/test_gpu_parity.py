@@ -495,3 +495,26 @@ def test_hessian_lockstep_counters_change_nothing(sg):
     Xs = Xv[:, ::97].double().numpy()  # 64 sampled channels
     cols = np.arange(0, n, 97)
     assert _rel(Hg[np.ix_(cols, cols)], Xs.T @ Xs) <= 1e-5
+
+
+@pytest.mark.gpu
+def test_hessian_lockstep_beside_other_work(sg):
+    """The lockstep counters' waits are bounded: with matrix products on a
+    second stream holding CUs while the Hessian runs (so some of a round's
+    workgroups may not be resident together), the launch still finishes and
+    gives the same bits as the unsynchronised one."""
+    n, T = 6144, 8000
+    gen = torch.Generator().manual_seed(6145)
+    Xg = torch.randn(T, n, generator=gen).to(torch.bfloat16).cuda()
+    need = sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, n, T, 0)
+    Hn = _gpu_hessian(sg, Xg, n, T, workspace_bytes=need - 1)
+    a = torch.randn(4096, 4096, device="cuda")
+    b = torch.randn(4096, 4096, device="cuda")
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        for _ in range(40):
+            a = torch.mm(a, b) * 1e-3
+    Hs = _gpu_hessian(sg, Xg, n, T, workspace_bytes=need)
+    torch.cuda.synchronize()
+    assert torch.equal(Hs, Hn)
