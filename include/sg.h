@@ -111,11 +111,14 @@ enum {
  *          tensor or a column view of one does); the values in the padding
  *          columns do not affect H.
  *   T      tokens in the chunk, T >= 1.
- *   workspace / ws_bytes: scratch for the token-split partial tiles; the size
- *          from sg_workspace_bytes(SG_OP_HESSIAN, 0, n, T, 0) gives the
- *          intended split.  A smaller workspace (even 0 bytes) is accepted: the
- *          call then splits the tokens less (results stay deterministic for a
- *          given workspace size).
+ *   workspace / ws_bytes: scratch for the token-split partial tiles or,
+ *          without a split, for the progress counters that keep the
+ *          workgroups of one XCD on the same tokens (they order nothing the
+ *          result depends on); the size from
+ *          sg_workspace_bytes(SG_OP_HESSIAN, 0, n, T, 0) gives the intended
+ *          split.  A smaller workspace (even 0 bytes) is accepted: the call
+ *          then splits the tokens less or runs without the counters (results
+ *          stay deterministic for a given workspace size).
  * Accumulation is fp32 (bf16 x bf16 products are exact in fp32).  The result
  * is bitwise reproducible for the same inputs and workspace size.
  */
