@@ -304,20 +304,39 @@ __device__ __forceinline__ float quant_value(float x, const RowQuant& q, int v) 
   return q.s[v] * (c - q.z[v]);
 }
 
-// Sweep column j of the chunk (compile-time j: static DPP lane and indices).
-// Chain per step and row: select (pruned ? W_J : 0) on the owner lane, DPP
-// broadcast over the 16 lanes of the row, fused multiply-add.
-// 1 if member T of the group starting at lane J precedes this lane's value
-// in (saliency, position) order
+// N:M ranking of the group of MGS columns at lanes J .. J+MGS-1 of each
+// 16-lane row.  A saliency is nonnegative, so its fp32 bit pattern orders as
+// its value does: the (saliency, position) order is an unsigned compare of the
+// bits, against the lane's own bits plus one for members at earlier positions
+// (equal saliency, earlier column: ahead).  Member T's bits reach every lane
+// of the row by a DPP broadcast; no branch, so the four rows interleave.
 template <int J, int T>
-__device__ __forceinline__ int ahead_of(float my, int me) {
-  const float o = bcast16_c<J + T>(my);
-  return (o < my || (o == my && T < me)) ? 1 : 0;
+__device__ __forceinline__ unsigned ahead_u(unsigned my, unsigned my1, int lc) {
+  const unsigned o = (unsigned)__builtin_amdgcn_mov_dpp((int)my, 0x150 + J + T, 0xF, 0xF, true);
+  return o < (lc > J + T ? my1 : my) ? 1u : 0u;
 }
 
 template <int J, int... Ts>
-__device__ __forceinline__ int group_rank(std::integer_sequence<int, Ts...>, float my, int me) {
-  return (ahead_of<J, Ts>(my, me) + ... + 0);
+__device__ __forceinline__ unsigned group_rank_u(std::integer_sequence<int, Ts...>, unsigned my, int lc) {
+  const unsigned my1 = my + 1u;
+  return (ahead_u<J, Ts>(my, my1, lc) + ... + 0u);
+}
+
+// Bits v = 0..3 (the lane's rows): the lane's column is in the group and
+// ranks among its MGS - nkeep smallest, so it is pruned.
+template <int J, int MGS>
+__device__ __forceinline__ unsigned group_pruned(const floatx4& Wc, float rd, int lc, int nkeep,
+                                                 unsigned rowbits) {
+  const unsigned lim = (unsigned)(MGS - nkeep);
+  unsigned bits = 0u;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const unsigned my = __float_as_uint(saliency(Wc[v], rd));
+    const unsigned rank = group_rank_u<J>(std::make_integer_sequence<int, MGS>{}, my, lc);
+    bits |= (rank < lim ? 1u : 0u) << v;
+  }
+  const bool in = lc >= J && lc < J + MGS;
+  return in ? bits & rowbits : 0u;
 }
 
 // ---- vector-level (joint) removal of one 16-column chunk -------------------
@@ -384,16 +403,7 @@ template <int J, int MGS>
 __device__ __forceinline__ void rank_step(const floatx4& Wc, unsigned& Pc, const ChunkCtx& cx, int lc,
                                           int nkeep, unsigned rowbits) {
   if constexpr (MGS > 0) {
-    if constexpr ((J % MGS) == 0) {
-      const int me = lc - J;
-      const bool in = me >= 0 && me < MGS;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float my = saliency(Wc[v], cx.rd);
-        const int rank = group_rank<J>(std::make_integer_sequence<int, MGS>{}, my, me);
-        if (in && ((rowbits >> v) & 1u) && rank < MGS - nkeep) Pc |= 1u << v;
-      }
-    }
+    if constexpr ((J % MGS) == 0) Pc |= group_pruned<J, MGS>(Wc, cx.rd, lc, nkeep, rowbits);
   }
 }
 
@@ -443,22 +453,17 @@ __device__ __forceinline__ void joint_chunk(std::integer_sequence<int, Js...> se
   (apply_step<Js>(Wc, d, cx), ...);
 }
 
+// Sweep column J of the chunk (compile-time J: static DPP lane and indices).
+// Chain per step and row: select (pruned ? W_J : 0) on the owner lane, DPP
+// broadcast over the 16 lanes of the row, fused multiply-add.
 template <int J, int MGS, bool QUANT>
 __device__ __forceinline__ void sweep_step(floatx4& Wc, unsigned& Pc, const ChunkCtx& cx, int lc,
                                            int nkeep, unsigned rowbits, const RowQuant& q) {
   if constexpr (MGS > 0) {
     if constexpr ((J % MGS) == 0) {
-      // N:M group of MGS <= 16 columns = lanes J .. J+MGS-1 of the row: rank
-      // the current saliencies at the group start; the group's values reach
-      // every lane of the row by DPP row broadcasts
-      const int me = lc - J;
-      const bool in = me >= 0 && me < MGS;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float my = saliency(Wc[v], cx.rd);
-        const int rank = group_rank<J>(std::make_integer_sequence<int, MGS>{}, my, me);
-        if (in && ((rowbits >> v) & 1u) && rank < MGS - nkeep) Pc |= 1u << v;
-      }
+      // N:M group of MGS <= 16 columns = lanes J .. J+MGS-1 of the row,
+      // ranked from the current saliencies at the group start
+      Pc |= group_pruned<J, MGS>(Wc, cx.rd, lc, nkeep, rowbits);
     }
   }
   // owner lane's deviation from its target (0 if pruned, the grid value if
