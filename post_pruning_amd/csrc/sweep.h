@@ -750,26 +750,52 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   const bool nm_large = (MODE == MODE_NM && MGS == 0) || MODE == MODE_ROW;
   const unsigned rowbits = (rowok[0] ? 1u : 0u) | (rowok[1] ? 2u : 0u) | (rowok[2] ? 4u : 0u) |
                            (rowok[3] ? 8u : 0u);
+  // Constants of chunk c (every lane reads all 16 values: no per-lane branch
+  // around a read).  Chunks past the block read zeros of the U block.
+  auto chunk_ctx = [&](int c) {
+    ChunkCtx cx;
+    const int col = 16 * c + lc;
+    cx.ucc = S.Ub[col * SWS + col];
+    cx.rd = S.Rd[col];  // 1 / U_col,col, 0 past the block
+    float rdj[16], uj[16];
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const floatx4 t = *reinterpret_cast<const floatx4*>(&S.Rd[16 * c + 4 * j4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rdj[4 * j4 + e] = t[e];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) uj[j] = S.Ub[(16 * c + j) * SWS + col];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) cx.g[j] = (j == lc) ? 0.f : uj[j] * rdj[j];
+    return cx;
+  };
+  // Software pipeline over the chunks: the errors of chunk c update chunk
+  // c + 1 at once (its steps wait on that), and the chunks after it during
+  // chunk c + 1's steps, which touch none of them, so the matrix core works
+  // beside the serial column chain.  Modes that rank whole groups of later
+  // chunks at a chunk start need every update first and keep the plain order.
+  constexpr bool kDefer = !((MODE == MODE_NM && MGS == 0) || MODE == MODE_ROW);
+  floatx4 ead = floatx4{0.f, 0.f, 0.f, 0.f};
+  float bvd[8][4];
+  ChunkCtx cx = chunk_ctx(0);
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     if (c >= nch) break;
-    ChunkCtx cx;
-    {
-      const int col = 16 * c + lc;
-      // every lane reads all 16 values (no per-lane branch around a read)
-      cx.ucc = S.Ub[col * SWS + col];
-      cx.rd = S.Rd[col];  // 1 / U_col,col, 0 past the block
-      float rdj[16], uj[16];
+    // the next chunk's constants now: their LDS latency hides behind the steps
+    ChunkCtx cxn;
+    if (c + 1 < 8) cxn = chunk_ctx(c + 1);
+    if constexpr (kDefer) {
+      // E_{c-1} U[c-1, c'] for the chunks c' after this one
+      if (c >= 1) {
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const floatx4 t = *reinterpret_cast<const floatx4*>(&S.Rd[16 * c + 4 * j4]);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rdj[4 * j4 + e] = t[e];
+          for (int c2 = 2; c2 < 8; ++c2) {
+            if (c2 <= c) continue;
+            Wt[c2] = __builtin_amdgcn_mfma_f32_16x16x4f32(-ead[i], bvd[c2][i], Wt[c2], 0, 0, 0);
+          }
       }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) uj[j] = S.Ub[(16 * c + j) * SWS + col];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) cx.g[j] = (j == lc) ? 0.f : uj[j] * rdj[j];
     }
     if (nm_large && ((16 * c) % mgroup) == 0) {
       // group of mgroup columns = chunks c .. c + ceil(mgroup/16) - 1 (all current)
@@ -854,7 +880,18 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
         Wt[c][v] = p ? 0.f : Wt[c][v];
       }
     }
-    if (c + 1 < nch) {
+    if constexpr (kDefer) {
+      // issue order: each deferred MFMA between a few of the steps' VALU
+      // instructions, from the chunk start on
+      if (c >= 1) {
+#pragma unroll
+        for (int k = 0; k < 4 * (7 - c); ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+      }
+    }
+    if (c + 1 < 8 && c + 1 < nch) {
       // E_c to the A-operand layout: Es[row][4*(k%4) + k/4] so that lane l
       // reads E[l%16][4*i + l/16] for i = 0..3 as one 16-byte value
 #pragma unroll
@@ -863,8 +900,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
       __builtin_amdgcn_wave_barrier();
       const floatx4 ea = *reinterpret_cast<const floatx4*>(&Es[lc * ESS + 4 * lg]);
       __builtin_amdgcn_wave_barrier();
-      // B operands first (one wait), then the MFMAs with independent
-      // accumulators back to back
+      // B operands first (one wait), then the MFMAs
       float bv[8][4];
 #pragma unroll
       for (int c2 = 1; c2 < 8; ++c2) {
@@ -872,14 +908,28 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
 #pragma unroll
         for (int i = 0; i < 4; ++i) bv[c2][i] = S.Ub[(16 * c + 4 * i + lg) * SWS + 16 * c2 + lc];
       }
+      if constexpr (kDefer) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
+          Wt[c + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(-ea[i], bv[c + 1][i], Wt[c + 1], 0, 0, 0);
+        ead = ea;
 #pragma unroll
-        for (int c2 = 1; c2 < 8; ++c2) {
-          if (c2 <= c) continue;
-          Wt[c2] = __builtin_amdgcn_mfma_f32_16x16x4f32(-ea[i], bv[c2][i], Wt[c2], 0, 0, 0);
+        for (int c2 = 2; c2 < 8; ++c2) {
+          if (c2 <= c + 1) continue;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bvd[c2][i] = bv[c2][i];
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int c2 = 1; c2 < 8; ++c2) {
+            if (c2 <= c) continue;
+            Wt[c2] = __builtin_amdgcn_mfma_f32_16x16x4f32(-ea[i], bv[c2][i], Wt[c2], 0, 0, 0);
+          }
+      }
     }
+    if (c + 1 < 8) cx = cxn;
   }
 
   // retire the block: W (pruned entries +0.0), errors, mask, straight from
