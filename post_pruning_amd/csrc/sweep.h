@@ -843,7 +843,6 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
 #pragma unroll
           for (int v = 0; v < 4; ++v) sc[(4 * lg + v) * SWS + 16 * g + lc] = saliency(Wt[c + g][v], rdg);
         }
-        __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_wave_barrier();
         for (int g = 0; g < nchg && c + g < 8; ++g) {
 #pragma unroll
@@ -896,7 +895,8 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
       // reads E[l%16][4*i + l/16] for i = 0..3 as one 16-byte value
 #pragma unroll
       for (int v = 0; v < 4; ++v) Es[(4 * lg + v) * ESS + 4 * (lc & 3) + (lc >> 2)] = Et[c][v];
-      __builtin_amdgcn_s_waitcnt(0);
+      // one wave writes and reads its own tile: its LDS operations execute in
+      // order, so no wait is needed between them (as for the W staging)
       __builtin_amdgcn_wave_barrier();
       const floatx4 ea = *reinterpret_cast<const floatx4*>(&Es[lc * ESS + 4 * lg]);
       __builtin_amdgcn_wave_barrier();
