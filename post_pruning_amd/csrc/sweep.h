@@ -232,9 +232,10 @@ __device__ inline unsigned long long select_finish(const SelSet& ss, const unsig
 //     broadcast hands e to the other 15 lanes of the row, which subtract
 //     e * U[J, col] (U is zero left of the diagonal, so earlier columns are
 //     untouched);
-//   * the chunk's errors E_c (16 x 16) then update every later chunk at once,
+//   * the chunk's errors E_c (16 x 16) then update every later chunk,
 //     W[:, c'] -= E_c U[c, c'], on v_mfma_f32_16x16x4_f32 (E_c goes through a
-//     small per-wave LDS tile to reach the A-operand layout).
+//     small per-wave LDS tile to reach the A-operand layout): chunk c + 1 at
+//     once, the chunks after it during chunk c + 1's column steps.
 // This is the same computation as the column-by-column OBS sweep, with the
 // updates of later chunks batched (they only add into columns not yet
 // reached).  The U block (upper triangle, zero elsewhere) sits in LDS.
