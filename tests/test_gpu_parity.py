@@ -518,3 +518,24 @@ def test_hessian_lockstep_beside_other_work(sg):
     Hs = _gpu_hessian(sg, Xg, n, T, workspace_bytes=need)
     torch.cuda.synchronize()
     assert torch.equal(Hs, Hn)
+
+
+@pytest.mark.parametrize("pattern", ["0.5", "0.5/row", "1:4", "2:4", "4:8", "8:16", "16:32", "16:128"])
+def test_exact_saliency_ties(sg, pattern):
+    """Exact saliency ties are broken by position, as the oracle does: with
+    U = I / 2 every weight keeps its value until it is chosen (no
+    compensation), and weights drawn from {-2, -1, 1, 2} make most
+    saliencies of a group or block equal.  The mask must be the oracle's bit
+    for bit (every mode's ranking: groups inside the column steps, through the
+    staging tile, by the bitwise search, per row and block-global)."""
+    m, n = 96, 256
+    gen = torch.Generator().manual_seed(11)
+    vals = torch.tensor([-2.0, -1.0, 1.0, 2.0])
+    W = vals[torch.randint(0, 4, (m, n), generator=gen)]
+    U = 0.5 * torch.eye(n, dtype=torch.float32)
+    Wh, mask = sg.sg_prune_layer(W.cuda(), U.cuda(), pattern, 128)
+    torch.cuda.synchronize()
+    Who, Mo, _ = oracle.prune(W.double().numpy(), U.double().numpy(), pattern, 128)
+    got = mask.cpu().numpy().astype(bool)
+    assert np.array_equal(got, Mo), f"{int((got != Mo).sum())} mask entries differ"
+    assert np.array_equal(Wh.cpu().numpy(), Who.astype(np.float32))
