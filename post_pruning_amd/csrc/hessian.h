@@ -11,10 +11,17 @@ namespace sg {
 
 constexpr int kHessTile = 256;    // Hessian output tile edge
 
+constexpr int kHessMaxSplits = 64;
+
+// Token ranges of the splits: split s covers tokens [b[s], b[s + 1]).
+struct HessSplits {
+  int64_t b[kHessMaxSplits + 1];
+};
+
 struct HessPlan {
   int64_t tiles;       // lower-triangle 256x256 tiles
   int splits;          // token splits
-  int64_t tok_per_split;
+  HessSplits bounds;   // their token ranges (b[splits] = T)
   int group;           // tile-panel group edge of the per-XCD tile order
   int64_t grid;        // workgroups launched (8 equal per-XCD shares)
   size_t part_bytes;   // split counters + partial tiles (0 without splits)

@@ -58,11 +58,11 @@ def test_workspace_sizes_pure_host(sg):
     # Prune: select state + an m x 128 fp32 error block.
     assert sg.sg_workspace_bytes(sg.SG_OP_PRUNE, 4096, 4096, 0, 128) >= 4096 * 128 * 4
     # Hessian: the small-n, many-token case splits the tokens: 136 lower
-    # 256x256 tiles in 7 splits (4 full-ish rounds of 256 workgroups), one
-    # fp32 partial tile per split and tile after a 256-byte aligned counter
-    # array.
+    # 256x256 tiles in 5 splits (three of 28% of the tokens, two of 8%, the
+    # small ones last to fill the last round), one fp32 partial tile per split
+    # and tile after a 256-byte aligned counter array.
     tiles = 16 * 17 // 2
-    assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 4096, 262144, 0) == 768 + tiles * 7 * 256 * 256 * 4
+    assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 4096, 262144, 0) == 768 + tiles * 5 * 256 * 256 * 4
     # ... and the large-n case needs no split: only the lockstep counters,
     # 8 XCDs x ceil(ceil(6328 / 8) / 32) = 25 rounds of 32 workgroups.
     assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 28672, 32768, 0) == 1024
