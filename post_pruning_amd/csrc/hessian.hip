@@ -41,7 +41,6 @@
 
 #include <algorithm>
 #include <functional>
-#include <vector>
 
 namespace sg {
 namespace {
@@ -493,15 +492,15 @@ __global__ __launch_bounds__(256) void hess_f32_kernel(float* __restrict__ H, in
 // each workgroup to the first of its CUs that is free) in units of the time
 // one workgroup takes for all T tokens; c_wg: a workgroup's fixed cost
 // (pipeline fill, partial tile, the last split's sum) in the same unit.
-double split_makespan(const std::vector<double>& frac, int64_t per_xcd, double c_wg) {
-  std::vector<double> cu(kCuPerXcd, 0.0);  // min-heap of the CUs' finish times
-  for (double f : frac)
+double split_makespan(const double* frac, int nfrac, int64_t per_xcd, double c_wg) {
+  double cu[kCuPerXcd] = {};  // min-heap of the CUs' finish times
+  for (int s = 0; s < nfrac; ++s)
     for (int64_t t = 0; t < per_xcd; ++t) {
-      std::pop_heap(cu.begin(), cu.end(), std::greater<double>());
-      cu.back() += f + c_wg;
-      std::push_heap(cu.begin(), cu.end(), std::greater<double>());
+      std::pop_heap(cu, cu + kCuPerXcd, std::greater<double>());
+      cu[kCuPerXcd - 1] += frac[s] + c_wg;
+      std::push_heap(cu, cu + kCuPerXcd, std::greater<double>());
     }
-  return *std::max_element(cu.begin(), cu.end());
+  return *std::max_element(cu, cu + kCuPerXcd);
 }
 
 HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws) {
@@ -539,33 +538,35 @@ HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws) {
   // ones last to fill the tail of the last round.  Measured at n = 4096,
   // T = 262144: three splits of 28% and two of 8% take 4.37 ms against
   // 4.55-4.67 ms for 7 equal ones.
-  std::vector<double> frac(best_s, 1.0 / best_s);
+  double frac[kHessMaxSplits];
+  int nfrac = best_s;
+  for (int s = 0; s < best_s; ++s) frac[s] = 1.0 / best_s;
   if (best_s > 1) {
     const int64_t per_xcd = ceil_div(p.tiles, 8);
     const double c_wg = (double)kWgCostTok / (double)T;
-    double best_ms = split_makespan(frac, per_xcd, c_wg);
-    std::vector<double> cand;
+    double best_ms = split_makespan(frac, nfrac, per_xcd, c_wg);
+    double cand[kHessMaxSplits];
     for (int k = std::max(1, best_s - 5); k <= best_s + 1 && k < max_s; ++k)
       for (int j = 1; j <= 2 && k + j <= max_s; ++j)
         for (int r = 2; r <= 4; ++r) {
           // k splits of size a, j of size a * r / 10
           const double a = 1.0 / (k + j * r / 10.0), b = a * r / 10.0;
           if (b * (double)T < (double)kMinTokPerSplit) continue;
-          cand.assign(k, a);
-          cand.insert(cand.end(), j, b);
-          const double ms = split_makespan(cand, per_xcd, c_wg);
+          for (int s = 0; s < k + j; ++s) cand[s] = s < k ? a : b;
+          const double ms = split_makespan(cand, k + j, per_xcd, c_wg);
           if (ms < best_ms * 0.98) {
             best_ms = ms;
-            frac = cand;
+            nfrac = k + j;
+            std::copy(cand, cand + nfrac, frac);
           }
         }
   }
   p.bounds.b[0] = 0;
   int ns = 0;
   double acc = 0.0;
-  for (size_t s = 0; s < frac.size() && p.bounds.b[ns] < T; ++s) {
+  for (int s = 0; s < nfrac && p.bounds.b[ns] < T; ++s) {
     acc += frac[s];
-    const int64_t e = s + 1 == frac.size() ? T : std::min<int64_t>(T, round_up((int64_t)(acc * (double)T), HSPLIT_ALIGN));
+    const int64_t e = s + 1 == nfrac ? T : std::min<int64_t>(T, round_up((int64_t)(acc * (double)T), HSPLIT_ALIGN));
     if (e > p.bounds.b[ns]) p.bounds.b[++ns] = e;
   }
   if (p.bounds.b[ns] < T) p.bounds.b[++ns] = T;
