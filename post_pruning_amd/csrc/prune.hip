@@ -419,9 +419,20 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
     segs.row0[p] = own ? a.seg_rows[p] : 0;
     segs.row0[p + 1] = own ? a.seg_rows[p + 1] : m;
     segs.U[p] = a.seg_u ? a.Useg[p] : a.U;
-    segs.wg0[p + 1] = segs.wg0[p] + (int)ceil_div(segs.row0[p + 1] - segs.row0[p], 64);
     max_rows = std::max<int64_t>(max_rows, segs.row0[p + 1] - segs.row0[p]);
   }
+  // Rows per lane of the column sweep: two (32 rows a workgroup) when those
+  // workgroups still take one CU each, which halves each SIMD's column-step
+  // work; else four (64 rows a workgroup).  The quantized and vector-level
+  // sweeps keep four.
+  int rpl = 4;
+  if (!quant && !joint) {
+    int64_t wgs = 0;
+    for (int p = 0; p < segs.n; ++p) wgs += ceil_div(segs.row0[p + 1] - segs.row0[p], 32);
+    if (wgs <= kNumCU) rpl = 2;
+  }
+  for (int p = 0; p < segs.n; ++p)
+    segs.wg0[p + 1] = segs.wg0[p] + (int)ceil_div(segs.row0[p + 1] - segs.row0[p], 16 * rpl);
   if (mode == MODE_THRESH) {
     hipLaunchKernelGGL(sel_clear_kernel, dim3((unsigned)segs.n), dim3(256), 0, st, sel);
     if (sg_status e = check_launch("select clear")) return e;
@@ -478,6 +489,7 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
     sa.qlevels = qlevels;
     sa.mode = mode;
     sa.mgs = 0;
+    sa.rpl = rpl;
     sa.grid = sw_grid;
     sa.stream = st;
     if (mode == MODE_NM && a.m_group <= 16) sa.mgs = a.m_group;

@@ -128,7 +128,7 @@ __device__ inline void hist_locate(const unsigned* hist, long long krem, HistPic
 
 // Threshold key of the block from the two histograms and the candidates
 // (run by every sweep workgroup; `scratch` holds SEL_SORT keys of LDS).
-__device__ inline unsigned long long select_finish(const SelSet& ss, const unsigned long long* cand,
+__device__ __forceinline__ unsigned long long select_finish(const SelSet& ss, const unsigned long long* cand,
                                             long long k, unsigned long long* scratch,
                                             unsigned* s_cnt, HistPick& P) {
   const int tid = threadIdx.x;
@@ -323,15 +323,15 @@ __device__ __forceinline__ unsigned group_rank_u(std::integer_sequence<int, Ts..
   return (ahead_u<J, Ts>(my, my1, lc) + ... + 0u);
 }
 
-// Bits v = 0..3 (the lane's rows): the lane's column is in the group and
+// Bits v = 0..RPL-1 (the lane's rows): the lane's column is in the group and
 // ranks among its MGS - nkeep smallest, so it is pruned.
-template <int J, int MGS>
+template <int J, int MGS, int RPL = 4>
 __device__ __forceinline__ unsigned group_pruned(const floatx4& Wc, float rd, int lc, int nkeep,
                                                  unsigned rowbits) {
   const unsigned lim = (unsigned)(MGS - nkeep);
   unsigned bits = 0u;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
+  for (int v = 0; v < RPL; ++v) {
     const unsigned my = __float_as_uint(saliency(Wc[v], rd));
     const unsigned rank = group_rank_u<J>(std::make_integer_sequence<int, MGS>{}, my, lc);
     bits |= (rank < lim ? 1u : 0u) << v;
@@ -457,21 +457,21 @@ __device__ __forceinline__ void joint_chunk(std::integer_sequence<int, Js...> se
 // Sweep column J of the chunk (compile-time J: static DPP lane and indices).
 // Chain per step and row: select (pruned ? W_J : 0) on the owner lane, DPP
 // broadcast over the 16 lanes of the row, fused multiply-add.
-template <int J, int MGS, bool QUANT>
+template <int J, int MGS, bool QUANT, int RPL>
 __device__ __forceinline__ void sweep_step(floatx4& Wc, unsigned& Pc, const ChunkCtx& cx, int lc,
                                            int nkeep, unsigned rowbits, const RowQuant& q) {
   if constexpr (MGS > 0) {
     if constexpr ((J % MGS) == 0) {
       // N:M group of MGS <= 16 columns = lanes J .. J+MGS-1 of the row,
       // ranked from the current saliencies at the group start
-      Pc |= group_pruned<J, MGS>(Wc, cx.rd, lc, nkeep, rowbits);
+      Pc |= group_pruned<J, MGS, RPL>(Wc, cx.rd, lc, nkeep, rowbits);
     }
   }
   // owner lane's deviation from its target (0 if pruned, the grid value if
   // kept and quantized), times U_JJ: the DPP broadcast hands it to the row
   float e[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
+  for (int v = 0; v < RPL; ++v) {
     float d;
     if constexpr (QUANT)
       d = ((Pc >> v) & 1u) ? Wc[v] : Wc[v] - quant_value(Wc[v], q, v);
@@ -480,17 +480,22 @@ __device__ __forceinline__ void sweep_step(floatx4& Wc, unsigned& Pc, const Chun
     e[v] = bcast16_c<J>(d);
   }
 #pragma unroll
-  for (int v = 0; v < 4; ++v) Wc[v] = fmaf(-e[v], cx.g[J], Wc[v]);
+  for (int v = 0; v < RPL; ++v) Wc[v] = fmaf(-e[v], cx.g[J], Wc[v]);
 }
 
-template <int MGS, bool QUANT, int... Js>
+template <int MGS, bool QUANT, int RPL, int... Js>
 __device__ __forceinline__ void sweep_chunk(std::integer_sequence<int, Js...>, floatx4& Wc, unsigned& Pc,
                                             const ChunkCtx& cx, int lc, int nkeep, unsigned rowbits,
                                             const RowQuant& q) {
-  (sweep_step<Js, MGS, QUANT>(Wc, Pc, cx, lc, nkeep, rowbits, q), ...);
+  (sweep_step<Js, MGS, QUANT, RPL>(Wc, Pc, cx, lc, nkeep, rowbits, q), ...);
 }
 
-template <int MODE, int MGS, bool QUANT, bool JOINT = false>
+// RPL: rows per lane, 4 (16 rows a wave, 64 a workgroup) or 2 (8 and 32:
+// twice the workgroups, half the column-step work a SIMD, for layers whose
+// rows then still fit one workgroup per CU).  A lane's rows sit at positions
+// 4 lg + v (v < RPL) of the 16-row MFMA tiles; with RPL = 2 the other two
+// positions are idle rows of zeros.
+template <int MODE, int MGS, bool QUANT, bool JOINT = false, int RPL = 4>
 __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8_t* __restrict__ mask_out,
                                                     float* __restrict__ Err,
                                                     const uint8_t* __restrict__ mask_in,
@@ -507,23 +512,24 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   // the wave index is uniform across the wave: held in a scalar register
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lc = lane & 15;       // column inside a chunk
-  const int lg = lane >> 4;       // row group: rows 4*lg .. 4*lg+3 of the wave's 16
+  const int lg = lane >> 4;       // row group: rows RPL*lg .. RPL*lg+RPL-1 of the wave's
+  constexpr int RW = 4 * RPL;     // rows of a wave
   // this workgroup's segment (matrix): its rows end at m
   int seg = 0;
   while (seg + 1 < segs.n && (int)blockIdx.x >= segs.wg0[seg + 1]) ++seg;
   const int64_t m = segs.row0[seg + 1];
   const float* __restrict__ U = segs.U[seg];
-  const int64_t rbase = segs.row0[seg] + ((int64_t)blockIdx.x - segs.wg0[seg]) * 64;
+  const int64_t rbase = segs.row0[seg] + ((int64_t)blockIdx.x - segs.wg0[seg]) * (4 * RW);
   const long long ksel = segs.k[seg];
   const int sel_fixed = segs.fixed[seg];
   SelState* const stp = st + seg;
   const unsigned long long* const candp = cand + segs.row0[seg] * SB;
-  const int64_t r0 = rbase + wave * 16 + 4 * lg;
+  const int64_t r0 = rbase + wave * RW + RPL * lg;
   const int nch = (w + 15) >> 4;
   RowQuant q;
   if constexpr (QUANT) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < RPL; ++v) {
       const int64_t r = r0 + v < m ? r0 + v : m - 1;
       q.s[v] = qscale[r];
       q.inv[v] = 1.f / q.s[v];
@@ -578,40 +584,42 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
                    ((reinterpret_cast<uintptr_t>(codes_out) & 3) == 0) &&
                    ((reinterpret_cast<uintptr_t>(Err) & 15) == 0);
   float* Tw = S.Tw[wave];
-  const int64_t rw0 = rbase + wave * 16;
+  const int64_t rw0 = rbase + wave * RW;
   bool rowok[4];
   floatx4 Wt[8], Et[8];
   unsigned Pm[8];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) rowok[v] = r0 + v < m;
-  floatx4 wt[8];
-  unsigned mw[8];
-  if (vio && w == SB && rw0 + 16 <= m && n < (int64_t(1) << 24)) {
+  for (int v = 0; v < 4; ++v) rowok[v] = v < RPL && r0 + v < m;
+  // the wave's RW x 128 tile in RW / 2 passes of two 512-byte rows
+  constexpr int WP = RW / 2;
+  floatx4 wt[WP];
+  unsigned mw[WP];
+  if (vio && w == SB && rw0 + RW <= m && n < (int64_t(1) << 24)) {
     // full tile: pass u reads rows 2u + lane/32 from a uniform base
     const uint32_t woff = (uint32_t)((lane >> 5) * n + (lane & 31) * 4) * 4u;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < WP; ++u) {
       const char* base = reinterpret_cast<const char*>(W + (rw0 + 2 * u) * n + i1);
       wt[u] = *reinterpret_cast<const floatx4*>(base + woff);
     }
     if (MODE == MODE_FORCED) {
       const uint32_t moff = (uint32_t)((lane >> 5) * n + (lane & 31) * 4);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < WP; ++u) {
         const unsigned char* base = mask_in + (rw0 + 2 * u) * n + i1;
         mw[u] = *reinterpret_cast<const unsigned*>(base + moff);
       }
     }
   } else if (vio) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < WP; ++u) {
       const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
       const int64_t r = rw0 + rr < m ? rw0 + rr : m - 1;
       wt[u] = *reinterpret_cast<const floatx4*>(W + r * n + i1 + (c4 < w ? c4 : w - 4));
     }
     if (MODE == MODE_FORCED) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < WP; ++u) {
         const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
         const int64_t r = rw0 + rr < m ? rw0 + rr : m - 1;
         mw[u] = *reinterpret_cast<const unsigned*>(mask_in + r * n + i1 + (c4 < w ? c4 : w - 4));
@@ -646,7 +654,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
 
   if (vio) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < WP; ++u) {
       const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
       *reinterpret_cast<floatx4*>(&Tw[rr * SWS + c4]) = c4 < w ? wt[u] : floatx4{0.f, 0.f, 0.f, 0.f};
     }
@@ -654,7 +662,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) Wt[c][v] = Tw[(4 * lg + v) * SWS + 16 * c + lc];
+      for (int v = 0; v < 4; ++v) Wt[c][v] = v < RPL ? Tw[(RPL * lg + v) * SWS + 16 * c + lc] : 0.f;
     __builtin_amdgcn_wave_barrier();
   } else {
 #pragma unroll
@@ -663,7 +671,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int64_t r = rowok[v] ? r0 + v : m - 1;
-        Wt[c][v] = (col < w) ? W[r * n + i1 + (col < w ? col : 0)] : 0.f;
+        Wt[c][v] = (v < RPL && col < w) ? W[r * n + i1 + (col < w ? col : 0)] : 0.f;
       }
     }
   }
@@ -689,11 +697,11 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
   // masks known at the block start
   if (MODE == MODE_FORCED) {
     if (vio) {
-      // the wave's 16 x w mask bytes (loaded in the prologue, 4 bytes per
+      // the wave's RW x w mask bytes (loaded in the prologue, 4 bytes per
       // access) through the staging tile
       unsigned* Tb = reinterpret_cast<unsigned*>(Tw);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < WP; ++u) {
         const int f = u * 64 + lane, rr = f >> 5, c4 = (f & 31) * 4;
         Tb[rr * 32 + (c4 >> 2)] = c4 < w ? mw[u] : 0u;
       }
@@ -702,15 +710,15 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (rowok[v] && Tm[(4 * lg + v) * 128 + 16 * c + lc] != 0) Pm[c] |= 1u << v;
+        for (int v = 0; v < RPL; ++v)
+          if (rowok[v] && Tm[(RPL * lg + v) * 128 + 16 * c + lc] != 0) Pm[c] |= 1u << v;
       __builtin_amdgcn_wave_barrier();
     } else {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int col = 16 * c + lc;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < RPL; ++v)
           if (rowok[v] && col < w && mask_in[(r0 + v) * n + i1 + col] != 0) Pm[c] |= 1u << v;
       }
     }
@@ -730,7 +738,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
       for (int c = 0; c < 8; ++c) {
         unsigned bits = 0u;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < RPL; ++v) {
           const uint32_t lin = lin0 + (uint32_t)v * nn + 16u * (uint32_t)c;
           const unsigned long long key =
               ((unsigned long long)__float_as_uint(saliency(Wt[c][v], rdv[c])) << 32) | lin;
@@ -813,7 +821,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
           const bool ok = g < nchg && c + g < 8 && pos < mgroup;
           const float rdg = S.Rd[ok ? col : 0];
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
+          for (int v = 0; v < RPL; ++v)
             key[g][v] = ok ? (((unsigned long long)__float_as_uint(saliency(Wt[c + g < 8 ? c + g : 7][v], rdg))
                                << 7) | (unsigned)pos)
                            : ~0ull;
@@ -821,7 +829,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
         unsigned long long T[4] = {0ull, 0ull, 0ull, 0ull};
         for (int b = 38; b >= 0; --b) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
+          for (int v = 0; v < RPL; ++v) {
             const unsigned long long cand = T[v] | (1ull << b);
             int cnt = 0;
 #pragma unroll
@@ -833,7 +841,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
         for (int g = 0; g < 8; ++g) {
           if (c + g >= 8) continue;
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
+          for (int v = 0; v < RPL; ++v)
             if (rowok[v] && kp > 0 && key[g][v] <= T[v]) Pm[c + g] |= 1u << v;
         }
       } else {
@@ -842,13 +850,13 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
           const int col = 16 * (c + g) + lc;
           const float rdg = S.Rd[col];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) sc[(4 * lg + v) * SWS + 16 * g + lc] = saliency(Wt[c + g][v], rdg);
+          for (int v = 0; v < RPL; ++v) sc[(RPL * lg + v) * SWS + 16 * g + lc] = saliency(Wt[c + g][v], rdg);
         }
         __builtin_amdgcn_wave_barrier();
         for (int g = 0; g < nchg && c + g < 8; ++g) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float* row = sc + (4 * lg + v) * SWS;
+          for (int v = 0; v < RPL; ++v) {
+            const float* row = sc + (RPL * lg + v) * SWS;
             const int me = 16 * g + lc;
             if (rowok[v] && me < mgroup && rank_of(row, mgroup, row[me], me) < kp)
               Pm[c + g] |= 1u << v;
@@ -862,11 +870,12 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
       joint_chunk<MGS>(std::make_integer_sequence<int, 16>{}, Wt[c], Pm[c], cx, lc, lg, nkeep, rowbits,
                        S.Gc[c], &S.Ub[(16 * c + lc) * SWS + 16 * c], ev);
     else
-      sweep_chunk<MGS, QUANT>(std::make_integer_sequence<int, 16>{}, Wt[c], Pm[c], cx, lc, nkeep, rowbits, q);
+      sweep_chunk<MGS, QUANT, RPL>(std::make_integer_sequence<int, 16>{}, Wt[c], Pm[c], cx, lc, nkeep, rowbits,
+                                   q);
     // errors of the chunk: e = (W_J - target) / U_JJ, from the frozen owner
     // values; pruned entries become +0.0, quantized ones their grid value
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < RPL; ++v) {
       const bool p = (Pm[c] >> v) & 1u;
       if constexpr (JOINT) {
         Et[c][v] = ev[v];
@@ -935,15 +944,15 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
 
   // retire the block: W (pruned entries +0.0), errors, mask, straight from
   // the registers (each store instruction writes 16 consecutive values of
-  // four rows; no staging round trip through LDS).  Full blocks of full
-  // rows store from four row pointers with constant offsets.
-  if (w == SB && rw0 + 16 <= m) {
-    float* wr[4];
-    float* er[4];
-    uint8_t* mr[4];
-    uint8_t* qr[4];
+  // four row groups; no staging round trip through LDS).  Full blocks of full
+  // rows store from RPL row pointers with constant offsets.
+  if (w == SB && rw0 + RW <= m) {
+    float* wr[RPL];
+    float* er[RPL];
+    uint8_t* mr[RPL];
+    uint8_t* qr[RPL];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < RPL; ++v) {
       const int64_t r = r0 + v;
       wr[v] = W + r * n + i1 + lc;
       er[v] = Err + r * EGK + lc;
@@ -953,7 +962,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
+      for (int v = 0; v < RPL; ++v) {
         wr[v][16 * c] = Wt[c][v];
         er[v][16 * c] = Et[c][v];
       }
@@ -961,13 +970,13 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) mr[v][16 * c] = (uint8_t)((Pm[c] >> v) & 1u);
+        for (int v = 0; v < RPL; ++v) mr[v][16 * c] = (uint8_t)((Pm[c] >> v) & 1u);
     }
     if (QUANT && codes_out) {
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < RPL; ++v)
           qr[v][16 * c] = (unsigned char)fminf(fmaxf(rintf(Wt[c][v] * q.inv[v]) + q.z[v], 0.f), q.L);
     }
     return;
@@ -977,7 +986,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
     const int col = 16 * c + lc;
     if (col >= w) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < RPL; ++v) {
       if (!rowok[v]) continue;
       const int64_t r = r0 + v;
       const bool p = (Pm[c] >> v) & 1u;
@@ -1009,6 +1018,7 @@ struct SweepArgs {
   float qlevels;
   int mode;   // MODE_*
   int mgs;    // N:M groups ranked inside the column steps (1, 2, 4, 8, 16), else 0
+  int rpl;    // rows per lane (4, or 2 in the plain sweep; segs.wg0 counts 16 * rpl rows a workgroup)
   dim3 grid;
   hipStream_t stream;
 };

@@ -19,6 +19,7 @@ sg_status go(const SweepArgs& a) {
 }  // namespace
 
 sg_status launch_sweep_joint(const SweepArgs& a) {
+  if (a.rpl != 4) return set_error(SG_ERR_UNSUPPORTED, "this sweep takes four rows per lane");
   switch (a.mode) {
     case MODE_THRESH: return go<MODE_THRESH, 0>(a);
     case MODE_FORCED: return go<MODE_FORCED, 0>(a);
