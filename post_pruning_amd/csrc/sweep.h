@@ -224,9 +224,10 @@ __device__ __forceinline__ unsigned long long select_finish(const SelSet& ss, co
 }
 
 // ---- in-block sweep ---------------------------------------------------------
-// One wave per 16 rows; the block's columns are held in registers as eight
-// 16x16 tiles in the fp32 MFMA accumulator layout (lane l, register v: row
-// 4*(l/16) + v, column l%16 of the tile).  Per 16-column chunk c:
+// One wave per 16 rows (8 with two rows per lane, RPL below); the block's
+// columns are held in registers as eight 16x16 tiles in the fp32 MFMA
+// accumulator layout (lane l, register v: row 4*(l/16) + v, column l%16 of
+// the tile).  Per 16-column chunk c:
 //   * the 16 columns are swept in order: the owner lanes (column j of the
 //     chunk) compute e = W[r,J] / U_JJ for pruned entries, a DPP row
 //     broadcast hands e to the other 15 lanes of the row, which subtract
