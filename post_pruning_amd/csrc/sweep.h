@@ -31,9 +31,9 @@ struct SelState {
 
 // Row segments of one prune call (kernel argument): segment p is rows
 // [row0[p], row0[p+1]) with the factor U[p]; its sweep workgroups are
-// [wg0[p], wg0[p+1]) (64 rows each); k[p] keys of each block are pruned under
-// block-global selection (fixed[p]: 2 none, 3 all, 0 selected by the radix
-// passes).
+// [wg0[p], wg0[p+1]) (16 times the rows per lane, 32 or 64 rows each); k[p]
+// keys of each block are pruned under block-global selection (fixed[p]: 2
+// none, 3 all, 0 selected by the radix passes).
 struct Segs {
   int n;
   int64_t row0[SG_MAX_SEGMENTS + 1];
