@@ -504,7 +504,7 @@ double split_makespan(const double* frac, int nfrac, int64_t per_xcd, double c_w
 }
 
 HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws) {
-  HessPlan p;
+  HessPlan p{};
   const int64_t nt = ceil_div(n, HT);
   p.tiles = nt * (nt + 1) / 2;
   const size_t tile_bytes = (size_t)HT * HT * sizeof(float);
@@ -569,8 +569,8 @@ HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws) {
     const int64_t e = s + 1 == nfrac ? T : std::min<int64_t>(T, round_up((int64_t)(acc * (double)T), HSPLIT_ALIGN));
     if (e > p.bounds.b[ns]) p.bounds.b[++ns] = e;
   }
-  if (p.bounds.b[ns] < T) p.bounds.b[++ns] = T;
-  p.splits = std::max(1, ns);
+  if (ns == 0 || p.bounds.b[ns] < T) p.bounds.b[++ns] = T;  // (no tokens: one empty split)
+  p.splits = ns;
   p.part_bytes = p.splits > 1 ? cnt_bytes + tile_bytes * (size_t)p.tiles * p.splits : 0;
   // Lockstep counters (8 XCDs x rounds x splits), after the partials, when
   // the tokens are not split.  With splits, groups of one split per round
