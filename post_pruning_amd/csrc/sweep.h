@@ -1019,7 +1019,7 @@ struct SweepArgs {
   float qlevels;
   int mode;   // MODE_*
   int mgs;    // N:M groups ranked inside the column steps (1, 2, 4, 8, 16), else 0
-  int rpl;    // rows per lane (4, or 2 in the plain sweep; segs.wg0 counts 16 * rpl rows a workgroup)
+  int rpl;    // rows per lane (4, or 2 but in the vector-level sweep; segs.wg0 counts 16 * rpl rows a workgroup)
   dim3 grid;
   hipStream_t stream;
 };
