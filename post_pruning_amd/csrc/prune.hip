@@ -423,9 +423,9 @@ sg_status launch_prune(const PruneArgs& a, void* ws, hipStream_t st) {
   }
   // Rows per lane of the column sweep: two (32 rows a workgroup) when those
   // workgroups still take one CU each, which halves each SIMD's column-step
-  // work; else four (64 rows a workgroup).  The vector-level sweep keeps four.
+  // work; else four (64 rows a workgroup).
   int rpl = 4;
-  if (!joint) {
+  {
     int64_t wgs = 0;
     for (int p = 0; p < segs.n; ++p) wgs += ceil_div(segs.row0[p + 1] - segs.row0[p], 32);
     if (wgs <= kNumCU) rpl = 2;

@@ -401,40 +401,40 @@ __device__ __forceinline__ void joint_solve(std::integer_sequence<int, Ss...>, f
   (bwd_step<15 - Ss>(acc, a, z, rj, lc, e, urow[15 - Ss]), ...);
 }
 
-template <int J, int MGS>
+template <int J, int MGS, int RPL>
 __device__ __forceinline__ void rank_step(const floatx4& Wc, unsigned& Pc, const ChunkCtx& cx, int lc,
                                           int nkeep, unsigned rowbits) {
   if constexpr (MGS > 0) {
-    if constexpr ((J % MGS) == 0) Pc |= group_pruned<J, MGS>(Wc, cx.rd, lc, nkeep, rowbits);
+    if constexpr ((J % MGS) == 0) Pc |= group_pruned<J, MGS, RPL>(Wc, cx.rd, lc, nkeep, rowbits);
   }
 }
 
-template <int J>
+template <int J, int RPL>
 __device__ __forceinline__ void apply_step(floatx4& Wc, const float (&d)[4], const ChunkCtx& cx) {
   float e[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) e[v] = bcast16_c<J>(d[v]);
+  for (int v = 0; v < RPL; ++v) e[v] = bcast16_c<J>(d[v]);
 #pragma unroll
-  for (int v = 0; v < 4; ++v) Wc[v] = fmaf(-e[v], cx.g[J], Wc[v]);
+  for (int v = 0; v < RPL; ++v) Wc[v] = fmaf(-e[v], cx.g[J], Wc[v]);
 }
 
 // The chunk's vector-level step: groups of M <= 16 ranked at the chunk start,
 // then the joint solve per row, then the chunk's own columns moved by -e U16
 // (the owner lane's own term is taken at the chunk end).  Returns e per row.
-template <int MGS, int... Js>
+template <int MGS, int RPL, int... Js>
 __device__ __forceinline__ void joint_chunk(std::integer_sequence<int, Js...> seq, floatx4& Wc, unsigned& Pc,
                                             const ChunkCtx& cx, int lc, int lg, int nkeep, unsigned rowbits,
                                             const float* Gc, const float* Urow, float (&ev)[4]) {
-  (rank_step<Js, MGS>(Wc, Pc, cx, lc, nkeep, rowbits), ...);
+  (rank_step<Js, MGS, RPL>(Wc, Pc, cx, lc, nkeep, rowbits), ...);
   float gcol[16], urow[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     gcol[i] = Gc[i * GCS + lc];
     urow[i] = Urow[i];
   }
-  // the four rows one after another (one copy of the solve in the code)
+  // the lane's rows one after another (one copy of the solve in the code)
 #pragma unroll 1
-  for (int v = 0; v < 4; ++v) {
+  for (int v = 0; v < RPL; ++v) {
     const float wv = v == 0 ? Wc[0] : (v == 1 ? Wc[1] : (v == 2 ? Wc[2] : Wc[3]));
     const unsigned long long bal = __ballot((Pc >> v) & 1u);
     const unsigned rowP = (unsigned)(bal >> (16 * lg)) & 0xFFFFu;
@@ -451,8 +451,8 @@ __device__ __forceinline__ void joint_chunk(std::integer_sequence<int, Js...> se
   }
   float d[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) d[v] = ev[v] * cx.ucc;
-  (apply_step<Js>(Wc, d, cx), ...);
+  for (int v = 0; v < RPL; ++v) d[v] = ev[v] * cx.ucc;
+  (apply_step<Js, RPL>(Wc, d, cx), ...);
 }
 
 // Sweep column J of the chunk (compile-time J: static DPP lane and indices).
@@ -868,7 +868,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(float* __restrict__ W, uint8
     }
     float ev[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (JOINT)
-      joint_chunk<MGS>(std::make_integer_sequence<int, 16>{}, Wt[c], Pm[c], cx, lc, lg, nkeep, rowbits,
+      joint_chunk<MGS, RPL>(std::make_integer_sequence<int, 16>{}, Wt[c], Pm[c], cx, lc, lg, nkeep, rowbits,
                        S.Gc[c], &S.Ub[(16 * c + lc) * SWS + 16 * c], ev);
     else
       sweep_chunk<MGS, QUANT, RPL>(std::make_integer_sequence<int, 16>{}, Wt[c], Pm[c], cx, lc, nkeep, rowbits,
@@ -1019,7 +1019,7 @@ struct SweepArgs {
   float qlevels;
   int mode;   // MODE_*
   int mgs;    // N:M groups ranked inside the column steps (1, 2, 4, 8, 16), else 0
-  int rpl;    // rows per lane (4, or 2 but in the vector-level sweep; segs.wg0 counts 16 * rpl rows a workgroup)
+  int rpl;    // rows per lane, 4 or 2 (segs.wg0 counts 16 * rpl rows a workgroup)
   dim3 grid;
   hipStream_t stream;
 };
