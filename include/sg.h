@@ -105,7 +105,8 @@ enum {
  *   n      number of input channels, 1 <= n <= 65536.
  *   X      token-major chunk Xc[t, c] (t < T, c < n) with leading dimension
  *          ldx >= n; x_dtype SG_BF16 or SG_F32.  For SG_BF16 the pointer must
- *          be 16-byte aligned and ldx a multiple of 8; rows are read in
+ *          be 16-byte aligned and ldx a multiple of 8 below 2^28 (one copy
+ *          instruction spans up to four rows with 32-bit offsets); rows are read in
  *          16-byte pieces up to n rounded up to a multiple of 8, so the buffer
  *          must hold (T - 1) * ldx + round_up(n, 8) elements (a [T, ldx]
  *          tensor or a column view of one does); the values in the padding

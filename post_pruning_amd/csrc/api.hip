@@ -108,6 +108,8 @@ sg_status sg_hessian_accumulate(float* H, int64_t n, const void* X, int32_t x_dt
     return set_error(SG_ERR_UNSUPPORTED, "x_dtype %d not supported", x_dtype);
   if (x_dtype == SG_BF16 && (!aligned(X, 16) || (ldx % 8) != 0))
     return set_error(SG_ERR_UNSUPPORTED, "bf16 X must be 16-byte aligned with ldx %% 8 == 0");
+  if (x_dtype == SG_BF16 && ldx >= ((int64_t)1 << 28))
+    return set_error(SG_ERR_UNSUPPORTED, "bf16 X rows must lie fewer than 2^28 elements apart");
   if (ws_bytes > 0 && !workspace)
     return set_error(SG_ERR_INVALID_ARGUMENT, "workspace is NULL but ws_bytes > 0");
   if (workspace && !aligned(workspace, 256))

@@ -9,7 +9,8 @@
 
 namespace sg {
 
-constexpr int kHessTile = 256;    // Hessian output tile edge
+constexpr int kHessTileRows = 256;  // Hessian output tile: rows (one row panel)
+constexpr int kHessTileCols = 384;  // and columns (one column panel)
 
 constexpr int kHessMaxSplits = 64;
 
@@ -19,7 +20,7 @@ struct HessSplits {
 };
 
 struct HessPlan {
-  int64_t tiles;       // lower-triangle 256x256 tiles
+  int64_t tiles;       // 256x384 tiles covering the lower triangle
   int splits;          // token splits
   HessSplits bounds;   // their token ranges (b[splits] = T)
   int group;           // tile-panel group edge of the per-XCD tile order

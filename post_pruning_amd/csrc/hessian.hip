@@ -5,25 +5,26 @@
 // token-major, Xc[t, c], so H[i][j] = sum_t Xc[t][i] Xc[t][j]: a symmetric
 // rank-T update whose reduction axis (tokens) is the strided one.
 //
-// bf16 path: 256x256 output tiles of the lower triangle only (the symmetric
-// result is mirrored on store), 8 waves per workgroup, each wave a 128x64
-// sub-tile of v_mfma_f32_16x16x32_bf16 (two waves per SIMD).  Token rows are
-// copied as they lie in X straight from global memory into LDS by the LDS-DMA
-// loads, and the operands are gathered by the transposing LDS read.  Rows are
-// read in 16-byte chunks up to n rounded up to 8 channels (inside the row:
-// the ABI asks for ldx % 8 == 0); channels past n only feed outputs past n,
-// which are never stored.
+// bf16 path: output tiles of 256 rows x 384 columns covering the lower
+// triangle (row panel I takes the column panels that reach its last row; the
+// symmetric result is mirrored on store), 8 waves per workgroup, each wave a
+// 128x96 sub-tile of v_mfma_f32_16x16x32_bf16 (two waves per SIMD, 192
+// accumulators a lane).  Token rows are copied as they lie in X straight from
+// global memory into LDS by the LDS-DMA loads, and the operands are gathered
+// by the transposing LDS read.  Rows are read in 16-byte chunks up to n
+// rounded up to 8 channels (inside the row: the ABI asks for ldx % 8 == 0);
+// channels past n only feed outputs past n, which are never stored.
 // When there are too few tiles to fill the 256 CUs the tokens are split; every
 // split writes its partial tile to the workspace and the last split to finish
 // sums all partials in split order (bitwise reproducible), then adds into H.
 //
 // Tile order: the hardware deals workgroups round-robin over the 8 XCDs, each
-// with its own L2.  Tiles are enumerated in g x g groups of panels (panel =
-// 256 channels), and XCD x takes a contiguous eighth of that order, split-major:
-// the workgroups resident on one XCD then work on a compact set of tiles that
-// share few panels, over the same token range, so X re-reads can hit its L2;
-// the XCDs run the same token range at the same time, which the shared
-// Infinity Cache serves once.
+// with its own L2.  Tiles are enumerated in g x g groups of panels (row panel
+// = 256 channels, column panel = 384), and XCD x takes a contiguous eighth of
+// that order, split-major: the workgroups resident on one XCD then work on a
+// compact set of tiles that share few panels, over the same token range, so X
+// re-reads can hit its L2; the XCDs run the same token range at the same time,
+// which the shared Infinity Cache serves once.
 // Lockstep: left alone, the 32 workgroups of one XCD drift apart by far more
 // tokens than its 4 MB L2 holds, and only about one X read in six hits there
 // (measured at n = 28672).  Each "round" of 32 workgroups of an XCD (those
@@ -45,17 +46,20 @@
 namespace sg {
 namespace {
 
-constexpr int HT = kHessTile;          // 256
+constexpr int HTI = kHessTileRows;     // 256
+constexpr int HTJ = kHessTileCols;     // 384
 constexpr int HSPLIT_ALIGN = 64;     // tokens: split boundaries are multiples of this
 constexpr int HTHREADS = 512;
 constexpr int kMinTokPerSplit = 4096;
-// A workgroup's fixed cost in tokens' worth of its time (measured at n = 4096,
-// 262,144 tokens: 15 equal splits were 3% slower than 7)
-constexpr int kWgCostTok = 3700;
+// A workgroup's fixed cost in tokens' worth of its time: 3,700 for 256x256
+// tiles (measured at n = 4096, 262,144 tokens: 15 equal splits were 3%
+// slower than 7), scaled by the 1.5x work per token of a 256x384 tile
+constexpr int kWgCostTok = 2500;
 constexpr int kCuPerXcd = kNumCU / 8;  // workgroups of one lockstep round
 constexpr int kSyncEvery = 8;          // steady-state iterations (4 stages each) per counter step
 constexpr int kSyncSpin = 400;         // polls before a workgroup stops waiting
 
+// ti-th tile (I, J), J <= I, of a lower triangle of square tiles, row-major.
 __device__ inline void tri_decode(int64_t ti, int& I, int& J) {
   int64_t r = (int64_t)((sqrt(8.0 * (double)ti + 1.0) - 1.0) * 0.5);
   while ((r + 1) * (r + 2) / 2 <= ti) ++r;
@@ -64,33 +68,49 @@ __device__ inline void tri_decode(int64_t ti, int& I, int& J) {
   J = (int)(ti - r * (r + 1) / 2);
 }
 
-// k-th tile of the grouped order: panel rows in blocks of g; inside a block
-// row BI, the off-diagonal g x g groups (BJ < BI) row-major, then the
-// diagonal group's lower triangle.
-__device__ inline void grouped_decode(int64_t k, int nt, int g, int& I, int& J) {
-  int64_t base = 0;
-  for (int BI = 0;; ++BI) {
-    const int r0 = BI * g;
-    const int gi = min(g, nt - r0);
-    const int64_t off = (int64_t)BI * gi * g;
-    const int64_t row = off + (int64_t)gi * (gi + 1) / 2;
-    if (k < base + row || r0 + gi >= nt) {
-      const int64_t rem = k - base;
-      if (rem < off) {
-        const int64_t per = (int64_t)gi * g;
-        const int BJ = (int)(rem / per);
-        const int r2 = (int)(rem - BJ * per);
-        I = r0 + r2 / g;
-        J = BJ * g + r2 % g;
-      } else {
-        int a, b;
-        tri_decode(rem - off, a, b);
-        I = r0 + a;
-        J = r0 + b;
-      }
-      return;
+// Column panels of row panel I: those holding a column <= its last row.
+__host__ __device__ inline int tile_cols(int I, int n) {
+  const int r = min(n - 1, I * HTI + HTI - 1);
+  return r / HTJ + 1;
+}
+
+// k-th tile of the grouped order: row panels in blocks of g; inside a block,
+// the column panels in groups of g, and inside a group the block's rows one
+// after another, each with its columns of the group.
+__host__ __device__ inline void tile_decode(int64_t k, int n, int g, int& I, int& J) {
+  const int nI = (n + HTI - 1) / HTI;
+  I = 0;
+  J = 0;
+  for (int r0 = 0; r0 < nI; r0 += g) {
+    const int gi = min(g, nI - r0);
+    int64_t blk = 0;
+    int maxJ = 0;
+    for (int i = 0; i < gi; ++i) {
+      const int c = tile_cols(r0 + i, n);
+      blk += c;
+      maxJ = max(maxJ, c);
     }
-    base += row;
+    if (k >= blk) {
+      k -= blk;
+      continue;
+    }
+    for (int c0 = 0; c0 < maxJ; c0 += g) {
+      int64_t grp = 0;
+      for (int i = 0; i < gi; ++i) grp += min(g, max(0, tile_cols(r0 + i, n) - c0));
+      if (k >= grp) {
+        k -= grp;
+        continue;
+      }
+      for (int i = 0; i < gi; ++i) {
+        const int w = min(g, max(0, tile_cols(r0 + i, n) - c0));
+        if (k < w) {
+          I = r0 + i;
+          J = c0 + (int)k;
+          return;
+        }
+        k -= w;
+      }
+    }
   }
 }
 
@@ -100,16 +120,22 @@ __global__ void zero_u32_kernel(unsigned* p, int64_t cnt) {
 }
 
 // The X stages are copied straight from global memory into LDS by the
-// LDS-DMA loads (no register staging, no transposes in VALU).  A stage is 32 tokens; in
-// LDS each token is one 1040-byte row holding the tile's I-panel (256
-// channels) and J-panel (256 channels) as they lie in X, plus 16 bytes of
-// padding so that consecutive tokens start 16 bytes apart in the LDS banks.
+// LDS-DMA loads (no register staging, no transposes in VALU).  A stage is 32
+// tokens; in LDS each token is one 1280-byte row holding the tile's row panel
+// (256 channels) and column panel (384 channels), 80 chunks of 16 bytes.  Rows
+// are not padded (four stages fill the 160 KB): instead chunk p of token row
+// t holds the row's chunk p ^ 2 tau(t), tau(t) = (t & 3) | ((t & 8) >> 1), a
+// swap of whole 32-byte pairs inside aligned 256-byte groups, so that the 8
+// token rows one half-wave of a transposing read touches (t = 0..3 and 8..11,
+// or 4..7 and 12..15, plus 16) fall on 8 different bank groups.
 // MFMA operands (8 consecutive tokens of one channel per lane) are read with
 // the transposing LDS read, which gathers 4 tokens x 4 channels across 16
 // lanes.  Four stages rotate, three in flight while the fourth is multiplied.
 constexpr int DK = 32;                       // tokens per stage
-constexpr int DROW = 2 * HT * 2 + 16;        // LDS bytes per token row
-constexpr int DSTAGE = DK * DROW;            // 33280 bytes per stage
+constexpr int DROW = (HTI + HTJ) * 2;        // 1280 LDS bytes per token row
+constexpr int DCH = DROW / 16;               // 80 chunks per token row
+constexpr int DSTAGE = DK * DROW;            // 40960 bytes per stage
+constexpr int kNB = 6;                       // 16-column fragments of a wave's 96 columns
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
@@ -117,10 +143,11 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
 
-// s_waitcnt immediates that wait for the vector-memory counter only.
+// s_waitcnt immediates that wait for the vector-memory counter only (a wave
+// issues 5 copies per stage).
 constexpr unsigned kWaitVm0 = 0x0F70u;
-constexpr unsigned kWaitVm4 = 0x0F74u;
-constexpr unsigned kWaitVm8 = 0x0F78u;
+constexpr unsigned kWaitVm5 = 0x0F75u;
+constexpr unsigned kWaitVm10 = 0x0F7Au;
 
 // One LDS-DMA copy: lane l moves 16 bytes from gbase + voff (its own offset)
 // to LDS byte address lds_addr + 16 * l.  Issued from inline assembly so that
@@ -151,12 +178,11 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
     int64_t ldx, int64_t tiles, int splits, const HessSplits bounds, int group,
     float* __restrict__ part, unsigned* __restrict__ counters, unsigned* __restrict__ sync,
     int sync_rounds) {
-  // One array per stage.
+  // One array per stage (together the whole 160 KB).
   __shared__ __attribute__((aligned(16))) unsigned char st0[DSTAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st1[DSTAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st2[DSTAGE];
   __shared__ __attribute__((aligned(16))) unsigned char st3[DSTAGE];
-  __shared__ int s_last;
 
   const int xcd = blockIdx.x & 7;
   const int64_t jx = blockIdx.x >> 3;
@@ -167,9 +193,8 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
   const int64_t ti = k0 + (jx - (int64_t)split * cnt);
   const int64_t item = (int64_t)split * tiles + ti;
   int I, J;
-  grouped_decode(ti, (int)ceil_div((int64_t)n, HT), group, I, J);
-  const bool diag = (I == J);
-  const int i0 = I * HT, j0 = J * HT;
+  tile_decode(ti, n, group, I, J);
+  const int i0 = I * HTI, j0 = J * HTJ;
   const int64_t t_begin = bounds.b[split];
   const int64_t t_end = min(T, bounds.b[split + 1]);
 
@@ -179,43 +204,76 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
   const int wi = wave >> 2;
   const int wj = wave & 3;
 
-  floatx4 acc[8][4];
+  floatx4 acc[8][kNB];
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < kNB; ++c) acc[a][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Copy role: wave w copies token rows 4w..4w+3 of every stage, one row per
-  // instruction; lanes 0..31 fetch the I-panel's 32 16-byte chunks, lanes
-  // 32..63 the J-panel's (on diagonal tiles a second copy of the I-panel).
-  // Chunks past n8 (n rounded up to 8, still inside the row since ldx is a
-  // multiple of 8) re-read the last chunk: channels past n only feed outputs
-  // beyond n, which are never stored.
+  // Copy role: wave w fills token rows 4w..4w+3 of every stage, 320 chunks in
+  // 5 instructions of 64 lanes (lane l of instruction k writes LDS chunk
+  // 64k + l of those rows, so it reads row r = (64k + l) / 80, chunk
+  // p ^ 2 tau with p = (64k + l) % 80).  Chunks past n8 (n rounded up to 8,
+  // still inside the row since ldx is a multiple of 8) re-read the last chunk:
+  // channels past n only feed outputs beyond n, which are never stored.
   const int n8 = (n + 7) & ~7;
-  int col = ((lane >> 5) ? j0 : i0) + (lane & 31) * 8;
-  col = col < n8 ? col : n8 - 8;
-  const uint32_t dcol = (uint32_t)col * 2u;
-  auto copy_stage = [&](unsigned char* buf, int64_t s) {
+  auto chunk_src = [&](int idx, int& r) {
+    r = idx / DCH;
+    const int p = idx - r * DCH;
+    const int g = p ^ (2 * (r | ((wave & 2) << 1)));  // tau of token row 4 wave + r
+    const int col = g < 32 ? i0 + 8 * g : j0 + 8 * (g - 32);
+    return col < n8 ? col : n8 - 8;
+  };
+  uint32_t voff[5];  // the host keeps 4 * ldx * 2 bytes below 2^31
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    int r;
+    const int col = chunk_src(64 * k + lane, r);
+    voff[k] = (uint32_t)((int64_t)r * ldx * 2 + (int64_t)col * 2);
+  }
+  // every stage but the last is full
+  auto copy_full = [&](unsigned char* buf, int64_t s) {
     const int64_t tok0 = t_begin + s * DK + wave * 4;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)buf + (uint32_t)(wave * 4 * DROW);
+    const char* base = reinterpret_cast<const char*>(X) + tok0 * ldx * 2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int64_t t = tok0 + j;
-      t = t < t_end ? t : t_end - 1;  // rows past the end are zeroed later
-      const char* row = reinterpret_cast<const char*>(X) + t * ldx * 2;
-      lds_dma16(row, dcol, __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(j * DROW)));
+    for (int k = 0; k < 5; ++k)
+      lds_dma16(base, voff[k], __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(k * 1024)));
+  };
+  // any stage: token rows past the end re-read the last row (zeroed before use)
+  auto copy_stage = [&](unsigned char* buf, int64_t s) {
+    const int64_t tok0 = t_begin + s * DK + wave * 4;
+    if (tok0 + 3 < t_end) {
+      copy_full(buf, s);
+      return;
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)buf + (uint32_t)(wave * 4 * DROW);
+    const int64_t rmax = t_end - 1 - tok0;
+    const int64_t tb = rmax >= 0 ? tok0 : t_end - 1;
+    const char* base = reinterpret_cast<const char*>(X) + tb * ldx * 2;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      int r;
+      const int col = chunk_src(64 * k + lane, r);
+      const int64_t re = rmax >= 0 ? min<int64_t>(r, rmax) : 0;
+      lds_dma16(base, (uint32_t)(re * ldx * 2 + (int64_t)col * 2),
+                __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(k * 1024)));
     }
   };
 
   // Operand addresses: lane l of a transposing read points at token row
-  // 8*(l/16) + (l%16)/4 (+4 for the second read) and channel quad l%4 of the
-  // 16-channel fragment; lane i of the result then holds channel i of the
-  // fragment over those 4 tokens.
+  // trow = 8*(l/16) + (l%16)/4 (+4 for the second read, same tau) and channel
+  // quad l%4 of the 16-channel fragment; lane i of the result then holds
+  // channel i of the fragment over those 4 tokens.  Fragment a of the row
+  // panel is pair 8 wi + a of the row, fragment c of the column panel pair
+  // 16 + 6 wj + c; the swizzle moves pair q to q ^ tau.
   const int s16 = lane & 15;
   const int trow = 8 * (lane >> 4) + (s16 >> 2);
-  const int q4 = 4 * (s16 & 3);
-  const uint32_t a_off = (uint32_t)(trow * DROW + (wi * 128 + q4) * 2);
-  const uint32_t b_off = (uint32_t)(trow * DROW + HT * 2 + (wj * 64 + q4) * 2);
+  int tau = (trow & 3) | ((trow & 8) >> 1);
+  const int hq = s16 & 3;
+  uint32_t lbase = (uint32_t)(trow * DROW + (hq >> 1) * 16 + (hq & 1) * 8);
+  auto a_off = [&](int a) { return lbase + 32u * (uint32_t)(8 * wi + (a ^ tau)); };
+  auto b_off = [&](int c) { return lbase + 32u * (uint32_t)((16 + 6 * wj + c) ^ tau); };
 
   auto frag = [&](const unsigned char* buf, uint32_t off) {
     const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(buf + off));
@@ -225,14 +283,14 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
   };
 
   auto compute = [&](const unsigned char* buf) {
-    bf16x8 fb[4];
+    bf16x8 fb[kNB];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) fb[c] = frag(buf, b_off + c * 32);
+    for (int c = 0; c < kNB; ++c) fb[c] = frag(buf, b_off(c));
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
-      const bf16x8 fa = frag(buf, a_off + a * 32);
+      const bf16x8 fa = frag(buf, a_off(a));
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < kNB; ++c)
         acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[c], acc[a][c], 0, 0, 0);
     }
   };
@@ -247,41 +305,48 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
   // complete in LDS): wait for this wave's copies of stage s+1 (stage s+2 may
   // stay in flight), barrier (stage s+1 complete; every wave is done with
   // stage s-1), start copying stage s+3 into the buffer of stage s-1,
-  // multiply stage s, and read the first fragments of stage s+1, so that the
-  // next step's MFMAs start right after its barrier.
+  // multiply stage s with each row-panel fragment read one ahead of its
+  // products, and read the first fragments of stage s+1 after the last
+  // products that use the current ones (192 accumulators leave no room to
+  // hold both sets).
   struct Frags {
-    bf16x8 fb[4];
+    bf16x8 fb[kNB];
     bf16x8 fa0;
   };
   auto prefetch = [&](const unsigned char* buf, Frags& f) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) f.fb[c] = frag(buf, b_off + c * 32);
-    f.fa0 = frag(buf, a_off);
+    for (int c = 0; c < kNB; ++c) f.fb[c] = frag(buf, b_off(c));
+    f.fa0 = frag(buf, a_off(0));
   };
   auto step = [&](const unsigned char* cur, const unsigned char* nxt, unsigned char* refill,
                   int64_t s, Frags& f) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    __builtin_amdgcn_s_waitcnt(kWaitVm5);
     stage_barrier();
-    copy_stage(refill, s + 3);
+    copy_full(refill, s + 3);
     __builtin_amdgcn_sched_barrier(0);
+    // the swizzled operand addresses are recomputed every step rather than
+    // held in registers across the loop
+    asm volatile("" : "+v"(tau), "+v"(lbase));
     bf16x8 fa = f.fa0;
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
-      const bf16x8 fan = a < 7 ? frag(cur, a_off + (a + 1) * 32) : fa;
+      const bf16x8 fan = a < 7 ? frag(cur, a_off(a + 1)) : frag(nxt, a_off(0));
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < kNB; ++c)
         acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f.fb[c], acc[a][c], 0, 0, 0);
       fa = fan;
     }
-    prefetch(nxt, f);
-    // two operand reads ahead of the MFMAs; the next stage's fragments are
-    // read during the last MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    f.fa0 = fa;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    for (int c = 0; c < kNB; ++c) f.fb[c] = frag(nxt, b_off(c));
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int g = 0; g < 7; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kNB, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, kNB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kNB, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
   // Lockstep counter of this workgroup's group: the workgroups of its round
@@ -296,7 +361,7 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
   bool waiting = true;
   int64_t s = 0;
   if (nsteps > 6) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm4);  // stages 0 and 1
+    __builtin_amdgcn_s_waitcnt(kWaitVm5);  // stages 0 and 1
     stage_barrier();
     Frags f;
     prefetch(st0, f);
@@ -326,18 +391,18 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
     unsigned char* refill = b == 0 ? st3 : b == 1 ? st0 : b == 2 ? st1 : st2;
     const int64_t later = nsteps - 1 - s;
     if (later >= 2)
-      __builtin_amdgcn_s_waitcnt(kWaitVm8);
+      __builtin_amdgcn_s_waitcnt(kWaitVm10);
     else if (later == 1)
-      __builtin_amdgcn_s_waitcnt(kWaitVm4);
+      __builtin_amdgcn_s_waitcnt(kWaitVm5);
     else
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
     stage_barrier();
     const int valid = (int)min<int64_t>(DK, ntok - s * DK);
     if (valid < DK) {
       // last, partial stage: zero the token rows past the end
-      for (int e = tid; e < (DK - valid) * (DROW / 16); e += HTHREADS) {
-        const int row = valid + e / (DROW / 16);
-        *reinterpret_cast<u32x4*>(cur + row * DROW + (e % (DROW / 16)) * 16) = u32x4{0u, 0u, 0u, 0u};
+      for (int e = tid; e < (DK - valid) * DCH; e += HTHREADS) {
+        const int row = valid + e / DCH;
+        *reinterpret_cast<u32x4*>(cur + row * DROW + (e % DCH) * 16) = u32x4{0u, 0u, 0u, 0u};
       }
       __syncthreads();
     }
@@ -351,45 +416,48 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
   // order (its own re-read too, so the result does not depend on which split
   // finished last) and adds into H.
   if (splits > 1) {
-    floatx4* mine = reinterpret_cast<floatx4*>(part + (size_t)item * (HT * HT));
+    floatx4* mine = reinterpret_cast<floatx4*>(part + (size_t)item * (HTI * HTJ));
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) mine[(wave * 32 + a * 4 + c) * 64 + lane] = acc[a][c];
+      for (int c = 0; c < kNB; ++c) mine[(wave * 8 * kNB + a * kNB + c) * 64 + lane] = acc[a][c];
     __threadfence();
     __syncthreads();
+    // every wave is past its last read of the stages: the flag uses stage 0
+    int* const s_last = reinterpret_cast<int*>(st0);
     if (tid == 0) {
       const unsigned old = atomicAdd(&counters[ti], 1u);
-      s_last = (old == (unsigned)(splits - 1)) ? 1 : 0;
+      *s_last = (old == (unsigned)(splits - 1)) ? 1 : 0;
     }
     __syncthreads();
-    if (!s_last) return;
+    if (!*s_last) return;
     __threadfence();
     for (int sp = 0; sp < splits; ++sp) {
       const floatx4* other =
-          reinterpret_cast<const floatx4*>(part + ((size_t)sp * tiles + ti) * (HT * HT));
+          reinterpret_cast<const floatx4*>(part + ((size_t)sp * tiles + ti) * (HTI * HTJ));
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
-        floatx4 pv[4];
+        floatx4 pv[kNB];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) pv[c] = other[(wave * 32 + a * 4 + c) * 64 + lane];
+        for (int c = 0; c < kNB; ++c) pv[c] = other[(wave * 8 * kNB + a * kNB + c) * 64 + lane];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = (sp == 0) ? pv[c] : acc[a][c] + pv[c];
+        for (int c = 0; c < kNB; ++c) acc[a][c] = (sp == 0) ? pv[c] : acc[a][c] + pv[c];
       }
     }
     if (tid == 0) counters[ti] = 0u;
   }
 
+  // lower triangle only (tiles that cross the diagonal hold upper entries
+  // too, which the mirror of the lower ones writes)
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < kNB; ++c)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = i0 + wi * 128 + a * 16 + (lane >> 4) * 4 + v;
-        const int col2 = j0 + wj * 64 + c * 16 + (lane & 15);
-        if (row >= n || col2 >= n) continue;
-        if (diag && row < col2) continue;
+        const int col2 = j0 + wj * 96 + c * 16 + (lane & 15);
+        if (row >= n || col2 >= n || row < col2) continue;
         const size_t lo = (size_t)row * n + col2;
         const float val = H[lo] + acc[a][c][v];
         H[lo] = val;
@@ -505,9 +573,10 @@ double split_makespan(const double* frac, int nfrac, int64_t per_xcd, double c_w
 
 HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws) {
   HessPlan p{};
-  const int64_t nt = ceil_div(n, HT);
-  p.tiles = nt * (nt + 1) / 2;
-  const size_t tile_bytes = (size_t)HT * HT * sizeof(float);
+  const int64_t nI = ceil_div(n, HTI);
+  p.tiles = 0;
+  for (int I = 0; I < nI; ++I) p.tiles += tile_cols(I, (int)n);
+  const size_t tile_bytes = (size_t)HTI * HTJ * sizeof(float);
   const size_t cnt_bytes = round_up(p.tiles * sizeof(unsigned), 256);
   int max_s = (int)std::max<int64_t>(1, std::min<int64_t>(kHessMaxSplits, T / kMinTokPerSplit));
   if (limit_by_ws) {
@@ -521,8 +590,9 @@ HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws) {
   // Pick the split count that best fills whole waves of workgroups (one
   // 512-thread workgroup per CU), with a penalty of 2% per split for the
   // partial tiles (their writes, and the serial sum in the last split).
-  // Measured at n = 4096, T = 262144: 7 splits (4 rounds, 93% full) take
-  // 4.50-4.60 ms, 15 splits (8 rounds, 99.6% full) 4.63-4.73 ms.
+  // Measured at n = 4096, T = 262144 with 256x256 tiles: 7 splits (4
+  // rounds, 93% full) take 4.50-4.60 ms, 15 splits (8 rounds, 99.6% full)
+  // 4.63-4.73 ms.
   double best = 1e300;
   int best_s = 1;
   for (int s = 1; s <= max_s; ++s) {
@@ -536,8 +606,8 @@ HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws) {
   // Equal splits, then (when the tokens are split at all) unequal ones if a
   // simulated schedule finishes sooner: big splits first, a few smaller
   // ones last to fill the tail of the last round.  Measured at n = 4096,
-  // T = 262144: three splits of 28% and two of 8% take 4.37 ms against
-  // 4.55-4.67 ms for 7 equal ones.
+  // T = 262144 with 256x256 tiles: three splits of 28% and two of 8% take
+  // 4.37 ms against 4.55-4.67 ms for 7 equal ones.
   double frac[kHessMaxSplits];
   int nfrac = best_s;
   for (int s = 0; s < best_s; ++s) frac[s] = 1.0 / best_s;
@@ -587,7 +657,7 @@ HessPlan hessian_plan(int64_t n, int64_t T, size_t ws_avail, bool limit_by_ws) {
   // (its 32 CUs, or its whole share when that is smaller).
   const double per_xcd = std::min<double>(32.0, (double)p.tiles * p.splits / 8.0) /
                          std::max(1, std::min(p.splits, 2));
-  p.group = (int)std::max<int64_t>(1, std::min<int64_t>(nt, (int64_t)std::lround(std::sqrt(per_xcd))));
+  p.group = (int)std::max<int64_t>(1, std::min<int64_t>(nI, (int64_t)std::lround(std::sqrt(per_xcd))));
   p.grid = 8 * ceil_div(p.tiles, 8) * p.splits;
   return p;
 }

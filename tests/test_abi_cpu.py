@@ -57,15 +57,17 @@ def test_workspace_sizes_pure_host(sg):
     assert sg.sg_workspace_bytes(sg.SG_OP_PREPARE_HINV, 0, 1000) >= 2 * 1024 * 1024 * 4
     # Prune: select state + an m x 128 fp32 error block.
     assert sg.sg_workspace_bytes(sg.SG_OP_PRUNE, 4096, 4096, 0, 128) >= 4096 * 128 * 4
-    # Hessian: the small-n, many-token case splits the tokens: 136 lower
-    # 256x256 tiles in 5 splits (three of 28% of the tokens, two of 8%, the
-    # small ones last to fill the last round), one fp32 partial tile per split
-    # and tile after a 256-byte aligned counter array.
-    tiles = 16 * 17 // 2
-    assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 4096, 262144, 0) == 768 + tiles * 5 * 256 * 256 * 4
+    # Hessian: the small-n, many-token case splits the tokens: 96 tiles of
+    # 256 x 384 cover the lower triangle (row panel I takes the column panels
+    # up to its last row: 1, 2, 2, 3, 4, 4, ... for 16 row panels), in 8
+    # equal splits (768 workgroups, three full rounds of 256 CUs); one fp32
+    # partial tile per split and tile after a 256-byte aligned counter array.
+    tiles = sum(min(4095, 256 * i + 255) // 384 + 1 for i in range(16))
+    assert tiles == 96
+    assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 4096, 262144, 0) == 512 + tiles * 8 * 256 * 384 * 4
     # ... and the large-n case needs no split: only the lockstep counters,
-    # 8 XCDs x ceil(ceil(6328 / 8) / 32) = 25 rounds of 32 workgroups.
-    assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 28672, 32768, 0) == 1024
+    # 8 XCDs x ceil(ceil(4256 / 8) / 32) = 17 rounds of 32 workgroups.
+    assert sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, 28672, 32768, 0) == 768
     assert sg.sg_workspace_bytes(sg.SG_OP_RECON, 64, 128, 512, 0) >= 8
     # invalid arguments give 0
     assert sg.sg_workspace_bytes(sg.SG_OP_PRUNE, 10, 10, 0, 0) == 0
@@ -111,6 +113,8 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validatio
     # n out of range, T < 1, ldx < n, unknown dtype, misaligned bf16 pointer
     (dict(n=0), 1), (dict(T=0), 1), (dict(ldx=8), 1), (dict(dt=7), 2),
     (dict(X=ctypes.c_void_p(0x1002)), 2), (dict(ldx=20), 2),
+    # bf16 rows 2^28 elements apart or more
+    (dict(ldx=1 << 28), 2),
 ])
 def test_hessian_validation(sg, args, code):
     a = dict(H=FAKE, n=16, X=FAKE, dt=sg.SG_BF16, T=8, ldx=16)

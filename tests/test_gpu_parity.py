@@ -477,10 +477,10 @@ def test_hessian_bf16_ragged_padded_view(sg, ws):
 def test_hessian_lockstep_counters_change_nothing(sg):
     """The per-XCD lockstep counters only pace the workgroups: with them (the
     full workspace) and without (one byte short of it) the Hessian is bit for
-    bit the same, and matches the oracle on sampled channels.  24 panels, 300
-    tiles, no token split: 2 rounds of up to 32 workgroups per XCD, 7 counter
-    steps, and a ragged last stage (8000 = 250 x 32 tokens)."""
-    n, T = 6144, 8000
+    bit the same, and matches the oracle on sampled channels.  28 row panels,
+    280 tiles, no token split: 2 rounds of up to 32 workgroups per XCD, 7
+    counter steps, and 250 stages of 32 tokens."""
+    n, T = 7168, 8000
     gen = torch.Generator().manual_seed(6144)
     Xv = torch.randn(T, n, generator=gen).to(torch.bfloat16)
     Xg = Xv.cuda()
@@ -503,7 +503,7 @@ def test_hessian_lockstep_beside_other_work(sg):
     second stream holding CUs while the Hessian runs (so some of a round's
     workgroups may not be resident together), the launch still finishes and
     gives the same bits as the unsynchronised one."""
-    n, T = 6144, 8000
+    n, T = 7168, 8000
     gen = torch.Generator().manual_seed(6145)
     Xg = torch.randn(T, n, generator=gen).to(torch.bfloat16).cuda()
     need = sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, n, T, 0)
