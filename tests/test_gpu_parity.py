@@ -473,6 +473,28 @@ def test_hessian_bf16_ragged_padded_view(sg, ws):
     assert _rel(Hg, Ho) <= 1e-5
 
 
+@pytest.mark.parametrize("T", [1, 5, 8295])
+@pytest.mark.parametrize("ws", ["split", "none"])
+def test_hessian_bf16_partial_token_rows(sg, T, ws):
+    """Token counts that leave a copying wave with 1 to 3 of its 4 token rows
+    in the last stage of a split (the rest re-read the last row and are
+    zeroed): T = 1 and 5 fit in one partial stage; T = 8295 = 259 x 32 + 7
+    ends on 7 tokens unsplit, and with its workspace splits at token 4160,
+    leaving 4135 = 129 x 32 + 7.  n = 776 covers 4 row panels and 3 column
+    panels, the last of each partial."""
+    n = 776
+    gen = torch.Generator().manual_seed(776 + T)
+    Xv = torch.randn(T, n, generator=gen).to(torch.bfloat16)
+    Xg = Xv.cuda()
+    need = sg.sg_workspace_bytes(sg.SG_OP_HESSIAN, 0, n, T, 0)
+    H = _gpu_hessian(sg, Xg, n, T, workspace_bytes=need if ws == "split" else 0)
+    torch.cuda.synchronize()
+    Hg = H.cpu().double().numpy()
+    assert np.array_equal(Hg, Hg.T)
+    Ho = oracle.hessian([Xv.double().numpy()])
+    assert _rel(Hg, Ho) <= 1e-5
+
+
 @pytest.mark.gpu
 def test_hessian_lockstep_counters_change_nothing(sg):
     """The per-XCD lockstep counters only pace the workgroups: with them (the
