@@ -9,6 +9,9 @@
 // below 2^-24 relative), each exact in the fp32 accumulator of
 // v_mfma_f32_16x16x32_bf16.  Six bf16 MFMAs of K = 32 replace eight fp32
 // MFMAs of K = 4, at twice the rate each: 2.7x the fp32 MFMA throughput.
+// This is the six-product ("bf16x6") scheme of Henry, Tang and Heinecke,
+// "Leveraging the bfloat16 Artificial Intelligence Datatype For
+// Higher-Precision Computations" (ARITH 2019), here on gfx950's bf16 MFMA.
 //
 // Layout as in gemm_f32.h (one 256-thread workgroup per T x T output tile,
 // 4 waves in a 2 x 2 grid of (T/2) x (T/2) sub-tiles, 32 k-values per chunk,
