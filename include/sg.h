@@ -169,6 +169,36 @@ sg_status sg_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp,
                           void* event_b);
 
 /*
+ * sg_prepare_hinv_batched -- sg_prepare_hinv for several matrices of the same
+ * order n (the Hessians of layers pruned side by side), factored together.
+ *
+ * "Vector-Based SparseGPT" (voc.com.cn), part 02: the dense inputs of each
+ * layer are recorded, so that several layers can be pruned in parallel.  Each
+ * matrix goes through exactly the computation of sg_prepare_hinv (the same
+ * result, bit for bit); the calls share their launches, so that the
+ * latency-bound panel steps of one matrix run on the CUs the others leave
+ * idle.
+ *
+ *   Hinv, H    HOST arrays of num_layers DEVICE pointers, each as in
+ *              sg_prepare_hinv ([n x n] fp32, leading dimension n).  No Hinv[L]
+ *              may alias any H[M] or another Hinv[M].
+ *   num_layers 1 <= num_layers <= SG_MAX_SEGMENTS.
+ *   info       DEVICE array of num_layers int32: info[L] is layer L's status,
+ *              with the meanings of sg_prepare_hinv.
+ *   workspace  num_layers * sg_workspace_bytes(SG_OP_PREPARE_HINV, 0, n, 0, 0)
+ *              bytes, 256-byte aligned (layer L uses the L-th equal part).
+ *   stream, update_stream, event_a, event_b: as in sg_prepare_hinv (one
+ *              update stream serves all layers).
+ * Errors as sg_prepare_hinv, plus SG_ERR_INVALID_ARGUMENT for num_layers out
+ * of range or aliased outputs.
+ */
+sg_status sg_prepare_hinv_batched(float* const* Hinv, const float* const* H,
+                                  int32_t num_layers, int64_t n, double damp,
+                                  int32_t* info, void* workspace, size_t ws_bytes,
+                                  void* stream, void* update_stream,
+                                  void* event_a, void* event_b);
+
+/*
  * sg_prune_layer -- sparse W_hat with W_hat X ~ W X.
  *
  * [SGR] section 8 (OBS: choose a weight, estimate its error from the inverse

@@ -73,12 +73,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sg_prune_layers_batched.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i64,
                                             c_i64, c_i64, c_vp, c_i32, c_vp, c_i32, c_dbl, c_i32,
                                             c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]
+    lib.sg_prepare_hinv_batched.argtypes = [c_vp, c_vp, c_i32, c_i64, c_dbl, c_vp, c_vp, c_sz, c_vp, c_vp,
+                                            c_vp, c_vp]
     lib.sg_prune_layer_vector.argtypes = [c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_i32,
                                           c_dbl, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]
     for f in ("sg_hessian_accumulate", "sg_prepare_hinv", "sg_prune_layer",
               "sg_reconstruction_error", "sg_pack_two_four", "sg_prune_quantize_layer",
               "sg_prune_layers_shared", "sg_prune_layer_vector", "sg_prune_layer_noalloc",
-              "sg_prune_layers_batched"):
+              "sg_prune_layers_batched", "sg_prepare_hinv_batched"):
         getattr(lib, f).restype = c_i32
     lib.sg_workspace_bytes.argtypes = [c_i32, c_i64, c_i64, c_i64, c_i32]
     lib.sg_workspace_bytes.restype = c_sz
@@ -218,6 +220,52 @@ def sg_prepare_hinv(H: torch.Tensor, damp: float = 0.01, Hinv: Optional[torch.Te
                                None if ev_b is None else ctypes.c_void_p(ev_b.cuda_event)),
            "sg_prepare_hinv")
     return Hinv, info
+
+
+def sg_prepare_hinv_batched(Hs, damp: float = 0.01, Hinvs=None, info: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None,
+                            update_stream: Union[str, None, "torch.cuda.Stream"] = "auto"):
+    """sg_prepare_hinv for several [n, n] matrices of one order n in one call;
+    returns (Hinvs, info) with info an int32 tensor of one status per matrix.
+    Each factor equals sg_prepare_hinv's of the same matrix, bit for bit."""
+    lib = load_library()
+    Hs = list(Hs)
+    if not Hs:
+        raise ValueError("at least one matrix")
+    _require_cuda(*Hs)
+    n = Hs[0].shape[0]
+    for H in Hs:
+        if H.dtype != torch.float32 or not H.is_contiguous() or H.shape != (n, n):
+            raise ValueError("every H must be a contiguous square float32 tensor of the same order")
+    nl = len(Hs)
+    dev = Hs[0].device
+    if Hinvs is None:
+        Hinvs = [torch.empty_like(H) for H in Hs]
+    if info is None:
+        info = torch.empty(nl, dtype=torch.int32, device=dev)
+    need = nl * sg_workspace_bytes(SG_OP_PREPARE_HINV, 0, n, 0, 0)
+    ws, nb = _workspace(need, dev, workspace)
+    side = ev_a = ev_b = None
+    if isinstance(update_stream, str):
+        if update_stream != "auto":
+            raise ValueError("update_stream must be 'auto', None or a torch.cuda.Stream")
+        if n >= FACTOR_SPLIT_MIN_N:
+            side = torch.cuda.Stream(device=dev)
+    else:
+        side = update_stream
+    if side is not None:
+        ev_a, ev_b = torch.cuda.Event(), torch.cuda.Event()
+        ev_a.record(side)
+        ev_b.record(side)
+    hp = (ctypes.c_void_p * nl)(*[h.data_ptr() for h in Hs])
+    up = (ctypes.c_void_p * nl)(*[u.data_ptr() for u in Hinvs])
+    _check(lib.sg_prepare_hinv_batched(ctypes.cast(up, ctypes.c_void_p), ctypes.cast(hp, ctypes.c_void_p), nl, n,
+                                       float(damp), _ptr(info), _ptr(ws), nb, ctypes.c_void_p(_stream(dev)),
+                                       None if side is None else ctypes.c_void_p(side.cuda_stream),
+                                       None if ev_a is None else ctypes.c_void_p(ev_a.cuda_event),
+                                       None if ev_b is None else ctypes.c_void_p(ev_b.cuda_event)),
+           "sg_prepare_hinv_batched")
+    return Hinvs, info
 
 
 def parse_pattern(pattern: Union[float, str]):

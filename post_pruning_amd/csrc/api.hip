@@ -150,6 +150,44 @@ sg_status sg_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp, i
                              static_cast<hipEvent_t>(event_b));
 }
 
+sg_status sg_prepare_hinv_batched(float* const* Hinv, const float* const* H, int32_t num_layers, int64_t n,
+                                  double damp, int32_t* info, void* workspace, size_t ws_bytes, void* stream,
+                                  void* update_stream, void* event_a, void* event_b) {
+  g_last_error.clear();
+  if (!Hinv || !H || !info) return set_error(SG_ERR_INVALID_ARGUMENT, "Hinv, H and info must not be NULL");
+  if (num_layers < 1 || num_layers > SG_MAX_SEGMENTS)
+    return set_error(SG_ERR_INVALID_ARGUMENT, "num_layers=%d out of [1, %d]", num_layers, SG_MAX_SEGMENTS);
+  if (n < 1 || n > 65536) return set_error(SG_ERR_INVALID_ARGUMENT, "n=%lld out of [1, 65536]", (long long)n);
+  if (!(damp >= 0.0) || !isfinite(damp))
+    return set_error(SG_ERR_INVALID_ARGUMENT, "damp must be finite and >= 0");
+  for (int L = 0; L < num_layers; ++L) {
+    if (!Hinv[L] || !H[L]) return set_error(SG_ERR_INVALID_ARGUMENT, "Hinv[%d] and H[%d] must not be NULL", L, L);
+    for (int M = 0; M < num_layers; ++M)
+      if (static_cast<const void*>(Hinv[L]) == static_cast<const void*>(H[M]))
+        return set_error(SG_ERR_INVALID_ARGUMENT, "Hinv[%d] must not alias H[%d]", L, M);
+    for (int M = 0; M < L; ++M)
+      if (Hinv[L] == Hinv[M]) return set_error(SG_ERR_INVALID_ARGUMENT, "Hinv[%d] and Hinv[%d] are the same", M, L);
+  }
+  const size_t per = factor_ws_bytes(n);
+  if (per > SIZE_MAX / (size_t)num_layers)
+    return set_error(SG_ERR_WORKSPACE, "workspace size overflows size_t");
+  const size_t need = per * (size_t)num_layers;
+  if (!workspace || ws_bytes < need)
+    return set_error(SG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (!aligned(workspace, 256))
+    return set_error(SG_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  const int given = (update_stream != nullptr) + (event_a != nullptr) + (event_b != nullptr);
+  if (given != 0 && given != 3)
+    return set_error(SG_ERR_INVALID_ARGUMENT, "update_stream, event_a and event_b go together (all or none)");
+  if (given == 3 && (update_stream == stream || event_a == event_b))
+    return set_error(SG_ERR_INVALID_ARGUMENT,
+                     "update_stream must differ from stream, and event_a from event_b");
+  if (sg_status e = check_device()) return e;
+  return launch_prepare_hinv_batched(Hinv, H, num_layers, n, damp, info, workspace,
+                                     static_cast<hipStream_t>(stream), static_cast<hipStream_t>(update_stream),
+                                     static_cast<hipEvent_t>(event_a), static_cast<hipEvent_t>(event_b));
+}
+
 static sg_status prune_common(float* W_out, uint8_t* mask_out, uint8_t* codes_out, float* scale_out,
                               float* zero_out, int32_t bits, const void* W, int32_t w_dtype, int64_t m,
                               int64_t n, int64_t ldw, const int64_t* row_splits, int32_t nseg,

@@ -43,12 +43,28 @@ namespace {
 
 constexpr int NB = kFactorNB;  // 128
 
+// The matrices of one call, all of order n.  Layer L works in its own part of
+// the workspace (ls floats apart): A and Y of n_pad x n_pad, then lambda.
+// Every kernel below handles all layers of a call in one launch: its grid is
+// the single-layer grid repeated once per layer (or, for the damping and the
+// flip copies, one more grid dimension).
+struct FactorLayers {
+  int nl;
+  int64_t ls;
+  const float* H[SG_MAX_SEGMENTS];
+  float* Hinv[SG_MAX_SEGMENTS];
+  int32_t* info[SG_MAX_SEGMENTS];
+};
+
 // ---- damping --------------------------------------------------------------
 // One workgroup of 1024 threads; each thread's diagonal entries (one cache
 // line apiece) are requested eight at a time before they are summed.
-__global__ __launch_bounds__(1024) void damp_lambda_kernel(const float* __restrict__ H, int64_t n,
-                                                           double damp, float* lam_out,
-                                                           int32_t* info) {
+__global__ __launch_bounds__(1024) void damp_lambda_kernel(const FactorLayers fl, float* ws, int64_t n,
+                                                           int64_t n_pad, double damp) {
+  const int L = blockIdx.x;
+  const float* __restrict__ H = fl.H[L];
+  float* lam_out = ws + L * fl.ls + 2 * n_pad * n_pad;
+  int32_t* info = fl.info[L];
   __shared__ double red[1024];
   double s = 0.0;
   for (int64_t i0 = threadIdx.x; i0 < n; i0 += 8 * 1024) {
@@ -79,11 +95,13 @@ __global__ __launch_bounds__(1024) void damp_lambda_kernel(const float* __restri
 // A = J (H + lam I) J on the lower block triangle (identity tail for padding);
 // Y = I (zero below the diagonal, so its lower block triangle is zero too:
 // the grouped updates read Y[c][k .. c-1]).  64x64 tiles.
-__global__ __launch_bounds__(256) void flip_init_kernel(const float* __restrict__ H, int64_t n,
-                                                        int64_t n_pad,
-                                                        const float* __restrict__ lam_p,
-                                                        float* __restrict__ A,
-                                                        float* __restrict__ Y) {
+__global__ __launch_bounds__(256) void flip_init_kernel(const FactorLayers fl, float* ws, int64_t n,
+                                                        int64_t n_pad) {
+  const int L = blockIdx.z;
+  const float* __restrict__ H = fl.H[L];
+  float* __restrict__ A = ws + L * fl.ls;
+  float* __restrict__ Y = A + n_pad * n_pad;
+  const float* __restrict__ lam_p = Y + n_pad * n_pad;
   const int64_t ti = blockIdx.y, tj = blockIdx.x;
   const float lam = *lam_p;
   const int c = threadIdx.x & 63;
@@ -536,12 +554,15 @@ __device__ __forceinline__ void update_body(float* lds, float* __restrict__ A, f
 }
 
 template <int R>
-__global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float* __restrict__ Y,
-                                                    int64_t n_pad, int k, int64_t n, int32_t* info) {
+__global__ __launch_bounds__(256) void panel_kernel(const FactorLayers fl, float* ws, int64_t n_pad, int k,
+                                                    int nblk, int64_t n) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int parts = NB / R;
-  panel_body<R>(*reinterpret_cast<PanelLds*>(smem), A, Y, n_pad, k, n, info, blockIdx.x / parts,
-                blockIdx.x % parts);
+  const int npl = nblk * parts;  // workgroups per layer
+  const int L = (int)blockIdx.x / npl, j = (int)blockIdx.x - L * npl;
+  float* A = ws + L * fl.ls;
+  panel_body<R>(*reinterpret_cast<PanelLds*>(smem), A, A + n_pad * n_pad, n_pad, k, n, fl.info[L], j / parts,
+                j % parts);
 }
 
 // Block column kl+1 of the update of panels k .. kl = k + KW - 1 (what panel
@@ -549,14 +570,18 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
 // workgroups of the tile grid, which is only t + kl + 1 tiles, for a short
 // latency-bound launch.
 template <int KW>
-__global__ __launch_bounds__(256) void col_update_kernel(float* __restrict__ A, float* __restrict__ Y,
-                                                         int64_t n_pad, int k, int nblk) {
+__global__ __launch_bounds__(256) void col_update_kernel(float* ws, int64_t ls, int64_t n_pad, int k, int nblk,
+                                                         int64_t ncl) {
   __shared__ __attribute__((aligned(16))) unsigned char ldsb[X6Lds<64>::SHORT];
   float* lds = reinterpret_cast<float*>(ldsb);
+  // layer L's part of the grid: ncl workgroups
+  const int64_t L = blockIdx.x / ncl, bid = blockIdx.x - L * ncl;
+  float* __restrict__ A = ws + L * ls;
+  float* __restrict__ Y = A + n_pad * n_pad;
   const int kl = k + KW - 1;
   const int64_t t = nblk - kl - 1;
-  int64_t idx = blockIdx.x >> 2;
-  const int qr = (blockIdx.x >> 1) & 1, qc = blockIdx.x & 1;
+  int64_t idx = bid >> 2;
+  const int qr = (int)(bid >> 1) & 1, qc = (int)bid & 1;
   float* C;
   const float *P, *Q;
   if (idx < t) {
@@ -595,27 +620,36 @@ __global__ __launch_bounds__(256) void col_update_kernel(float* __restrict__ A, 
 // panel kl+1 does not read).  The panel's workgroups come first in the grid,
 // so they are dispatched first.
 template <int R, int KW>
-__global__ __launch_bounds__(256) void panel_rest_kernel(float* __restrict__ A, float* __restrict__ Y,
-                                                         int64_t n_pad, int k, int nblk, int64_t n,
-                                                         int32_t* info) {
+__global__ __launch_bounds__(256) void panel_rest_kernel(const FactorLayers fl, float* ws, int64_t n_pad, int k,
+                                                         int nblk, int64_t n, int64_t nrest) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int parts = NB / R;
-  if ((int)blockIdx.x < nblk * parts)
-    panel_body<R>(*reinterpret_cast<PanelLds*>(smem), A, Y, n_pad, k + KW, n, info, blockIdx.x / parts,
-                  blockIdx.x % parts);
-  else
-    update_body<KW>(reinterpret_cast<float*>(smem), A, Y, n_pad, k, nblk, UPD_REST,
-                    (int64_t)blockIdx.x - nblk * parts);
+  // every layer's panel workgroups first, then every layer's update tiles
+  const int64_t npl = (int64_t)nblk * parts, bid = blockIdx.x;
+  if (bid < fl.nl * npl) {
+    const int L = (int)(bid / npl), j = (int)(bid - L * npl);
+    float* A = ws + L * fl.ls;
+    panel_body<R>(*reinterpret_cast<PanelLds*>(smem), A, A + n_pad * n_pad, n_pad, k + KW, n, fl.info[L],
+                  j / parts, j % parts);
+  } else {
+    const int64_t r = bid - fl.nl * npl, L = r / nrest;
+    float* A = ws + L * fl.ls;
+    update_body<KW>(reinterpret_cast<float*>(smem), A, A + n_pad * n_pad, n_pad, k, nblk, UPD_REST,
+                    r - L * nrest);
+  }
 }
 
 // The rest of the update of panels k .. k + KW - 1 on its own (the panel
 // launch runs beside it on a second stream): 66 KB of LDS per workgroup, two
 // per CU.
 template <int KW>
-__global__ __launch_bounds__(256, 2) void rest_update_kernel(float* __restrict__ A, float* __restrict__ Y,
-                                                             int64_t n_pad, int k, int nblk) {
+__global__ __launch_bounds__(256, 2) void rest_update_kernel(float* ws, int64_t ls, int64_t n_pad, int k, int nblk,
+                                                             int64_t nrest) {
   __shared__ __attribute__((aligned(16))) unsigned char ldsb[X6Lds<NB>::SIZE];
-  update_body<KW>(reinterpret_cast<float*>(ldsb), A, Y, n_pad, k, nblk, UPD_REST, blockIdx.x);
+  const int64_t L = blockIdx.x / nrest;
+  float* A = ws + L * ls;
+  update_body<KW>(reinterpret_cast<float*>(ldsb), A, A + n_pad * n_pad, n_pad, k, nblk, UPD_REST,
+                  (int64_t)blockIdx.x - L * nrest);
 }
 
 // The panel chain (factor A_kk, invert it, transform the block column) is
@@ -633,40 +667,44 @@ __global__ __launch_bounds__(256, 2) void rest_update_kernel(float* __restrict__
 constexpr int KWMAX = 4;
 
 // host launchers of the templates by group width (1 .. KWMAX)
-sg_status launch_col_update(int kw, float* A, float* Y, int64_t n_pad, int k, int nblk, hipStream_t st) {
-  const dim3 grid((unsigned)(4 * update_tiles(k, kw, nblk, UPD_COL))), blk(256);
+sg_status launch_col_update(int kw, const FactorLayers& fl, float* ws, int64_t n_pad, int k, int nblk,
+                            hipStream_t st) {
+  const int64_t ncl = 4 * update_tiles(k, kw, nblk, UPD_COL);
+  const dim3 grid((unsigned)(fl.nl * ncl)), blk(256);
+  const int64_t ls = fl.ls;
   switch (kw) {
-    case 1: hipLaunchKernelGGL(col_update_kernel<1>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
-    case 2: hipLaunchKernelGGL(col_update_kernel<2>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
-    case 3: hipLaunchKernelGGL(col_update_kernel<3>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
-    default: hipLaunchKernelGGL(col_update_kernel<4>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
+    case 1: hipLaunchKernelGGL(col_update_kernel<1>, grid, blk, 0, st, ws, ls, n_pad, k, nblk, ncl); break;
+    case 2: hipLaunchKernelGGL(col_update_kernel<2>, grid, blk, 0, st, ws, ls, n_pad, k, nblk, ncl); break;
+    case 3: hipLaunchKernelGGL(col_update_kernel<3>, grid, blk, 0, st, ws, ls, n_pad, k, nblk, ncl); break;
+    default: hipLaunchKernelGGL(col_update_kernel<4>, grid, blk, 0, st, ws, ls, n_pad, k, nblk, ncl); break;
   }
   return check_launch("factor update (next column)");
 }
 
-sg_status launch_rest_update(int kw, float* A, float* Y, int64_t n_pad, int k, int nblk, int64_t rest,
-                             hipStream_t st) {
-  const dim3 grid((unsigned)rest), blk(256);
+sg_status launch_rest_update(int kw, const FactorLayers& fl, float* ws, int64_t n_pad, int k, int nblk,
+                             int64_t rest, hipStream_t st) {
+  const dim3 grid((unsigned)(fl.nl * rest)), blk(256);
+  const int64_t ls = fl.ls;
   switch (kw) {
-    case 1: hipLaunchKernelGGL(rest_update_kernel<1>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
-    case 2: hipLaunchKernelGGL(rest_update_kernel<2>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
-    case 3: hipLaunchKernelGGL(rest_update_kernel<3>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
-    default: hipLaunchKernelGGL(rest_update_kernel<4>, grid, blk, 0, st, A, Y, n_pad, k, nblk); break;
+    case 1: hipLaunchKernelGGL(rest_update_kernel<1>, grid, blk, 0, st, ws, ls, n_pad, k, nblk, rest); break;
+    case 2: hipLaunchKernelGGL(rest_update_kernel<2>, grid, blk, 0, st, ws, ls, n_pad, k, nblk, rest); break;
+    case 3: hipLaunchKernelGGL(rest_update_kernel<3>, grid, blk, 0, st, ws, ls, n_pad, k, nblk, rest); break;
+    default: hipLaunchKernelGGL(rest_update_kernel<4>, grid, blk, 0, st, ws, ls, n_pad, k, nblk, rest); break;
   }
   return check_launch("factor update (rest)");
 }
 
 template <int R>
-sg_status launch_panel_rest(int kw, float* A, float* Y, int64_t n_pad, int k, int nblk, int64_t n, int32_t* info,
+sg_status launch_panel_rest(int kw, const FactorLayers& fl, float* ws, int64_t n_pad, int k, int nblk, int64_t n,
                             int64_t rest, hipStream_t st) {
   constexpr int parts = NB / R;
-  const dim3 grid((unsigned)(nblk * parts + rest)), blk(256);
+  const dim3 grid((unsigned)(fl.nl * ((int64_t)nblk * parts + rest))), blk(256);
   const size_t lds = sizeof(PanelLds);
   switch (kw) {
-    case 1: hipLaunchKernelGGL((panel_rest_kernel<R, 1>), grid, blk, lds, st, A, Y, n_pad, k, nblk, n, info); break;
-    case 2: hipLaunchKernelGGL((panel_rest_kernel<R, 2>), grid, blk, lds, st, A, Y, n_pad, k, nblk, n, info); break;
-    case 3: hipLaunchKernelGGL((panel_rest_kernel<R, 3>), grid, blk, lds, st, A, Y, n_pad, k, nblk, n, info); break;
-    default: hipLaunchKernelGGL((panel_rest_kernel<R, 4>), grid, blk, lds, st, A, Y, n_pad, k, nblk, n, info); break;
+    case 1: hipLaunchKernelGGL((panel_rest_kernel<R, 1>), grid, blk, lds, st, fl, ws, n_pad, k, nblk, n, rest); break;
+    case 2: hipLaunchKernelGGL((panel_rest_kernel<R, 2>), grid, blk, lds, st, fl, ws, n_pad, k, nblk, n, rest); break;
+    case 3: hipLaunchKernelGGL((panel_rest_kernel<R, 3>), grid, blk, lds, st, fl, ws, n_pad, k, nblk, n, rest); break;
+    default: hipLaunchKernelGGL((panel_rest_kernel<R, 4>), grid, blk, lds, st, fl, ws, n_pad, k, nblk, n, rest); break;
   }
   return check_launch("factor panel + rest of update");
 }
@@ -675,7 +713,7 @@ sg_status launch_panel_rest(int kw, float* A, float* Y, int64_t n_pad, int k, in
 // the group, and one launch holding the next panel and the rest of the
 // group's update.  GROUPS = false: single panels (kw = 1).
 template <int R, bool GROUPS>
-sg_status run_factor_fused(float* A, float* Y, int64_t n_pad, int nblk, int64_t n, int32_t* info,
+sg_status run_factor_fused(const FactorLayers& fl, float* ws, int64_t n_pad, int nblk, int64_t n,
                            hipStream_t st) {
   constexpr int parts = NB / R;
   // the LDS limit is a per-device attribute: set on every call (cheap), so
@@ -688,18 +726,18 @@ sg_status run_factor_fused(float* A, float* Y, int64_t n_pad, int nblk, int64_t 
     if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PanelLds)) !=
         hipSuccess)
       return set_error(SG_ERR_HIP, "hipFuncSetAttribute(panel kernels) failed");
-  const dim3 pgrid((unsigned)(nblk * parts)), blk(256);
-  hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, 0, n, info);
+  const dim3 pgrid((unsigned)(fl.nl * nblk * parts)), blk(256);
+  hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, fl, ws, n_pad, 0, nblk, n);
   if (sg_status e = check_launch("factor panel")) return e;
   for (int k = 0; k + 1 < nblk;) {
     const int kw = GROUPS ? std::min(KWMAX, nblk - 1 - k) : 1;
     for (int j = 1; j < kw; ++j) {
-      if (sg_status e = launch_col_update(j, A, Y, n_pad, k, nblk, st)) return e;
-      hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, k + j, n, info);
+      if (sg_status e = launch_col_update(j, fl, ws, n_pad, k, nblk, st)) return e;
+      hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, fl, ws, n_pad, k + j, nblk, n);
       if (sg_status e = check_launch("factor panel")) return e;
     }
-    if (sg_status e = launch_col_update(kw, A, Y, n_pad, k, nblk, st)) return e;
-    if (sg_status e = launch_panel_rest<R>(kw, A, Y, n_pad, k, nblk, n, info,
+    if (sg_status e = launch_col_update(kw, fl, ws, n_pad, k, nblk, st)) return e;
+    if (sg_status e = launch_panel_rest<R>(kw, fl, ws, n_pad, k, nblk, n,
                                            update_tiles(k, kw, nblk, UPD_REST), st))
       return e;
     k += kw;
@@ -719,7 +757,7 @@ struct SideStream {
 };
 
 template <int R>
-sg_status run_factor_split(float* A, float* Y, int64_t n_pad, int nblk, int64_t n, int32_t* info,
+sg_status run_factor_split(const FactorLayers& fl, float* ws, int64_t n_pad, int nblk, int64_t n,
                            hipStream_t st, const SideStream* ss) {
   constexpr int parts = NB / R;
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(panel_kernel<R>),
@@ -728,12 +766,12 @@ sg_status run_factor_split(float* A, float* Y, int64_t n_pad, int nblk, int64_t 
   const auto api = [](hipError_t r, const char* what) -> sg_status {
     return r == hipSuccess ? SG_OK : set_error(SG_ERR_HIP, "factor: %s failed", what);
   };
-  const dim3 pgrid((unsigned)(nblk * parts)), blk(256);
+  const dim3 pgrid((unsigned)(fl.nl * nblk * parts)), blk(256);
   // Caller's stream: panel 0; per group (after the previous group's rest
   // update, which covers the next block columns) the next-column updates,
   // the group's other panels, and the next panel.  Update stream: the rest
   // of the group's update, once its panels are done, beside the next panel.
-  hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, 0, n, info);
+  hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, fl, ws, n_pad, 0, nblk, n);
   if (sg_status e = check_launch("factor panel")) return e;
   bool pending = false;  // a rest update was enqueued on the update stream
   for (int k = 0; k + 1 < nblk;) {
@@ -741,22 +779,22 @@ sg_status run_factor_split(float* A, float* Y, int64_t n_pad, int nblk, int64_t 
       if (sg_status e = api(hipStreamWaitEvent(st, ss->ev_rest, 0), "stream wait")) return e;
     const int kw = std::min(KWMAX, nblk - 1 - k);
     for (int j = 1; j < kw; ++j) {
-      if (sg_status e = launch_col_update(j, A, Y, n_pad, k, nblk, st)) return e;
-      hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, k + j, n, info);
+      if (sg_status e = launch_col_update(j, fl, ws, n_pad, k, nblk, st)) return e;
+      hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, fl, ws, n_pad, k + j, nblk, n);
       if (sg_status e = check_launch("factor panel")) return e;
     }
     if (sg_status e = api(hipEventRecord(ss->ev_panel, st), "event record")) return e;
-    if (sg_status e = launch_col_update(kw, A, Y, n_pad, k, nblk, st)) return e;
+    if (sg_status e = launch_col_update(kw, fl, ws, n_pad, k, nblk, st)) return e;
     const int64_t rest = update_tiles(k, kw, nblk, UPD_REST);
     if (rest > 0) {
       if (sg_status e = api(hipStreamWaitEvent(ss->s, ss->ev_panel, 0), "stream wait")) return e;
-      if (sg_status e = launch_rest_update(kw, A, Y, n_pad, k, nblk, rest, ss->s)) return e;
+      if (sg_status e = launch_rest_update(kw, fl, ws, n_pad, k, nblk, rest, ss->s)) return e;
       if (sg_status e = api(hipEventRecord(ss->ev_rest, ss->s), "event record")) return e;
       pending = true;
     } else {
       pending = false;
     }
-    hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, A, Y, n_pad, k + kw, n, info);
+    hipLaunchKernelGGL(panel_kernel<R>, pgrid, blk, sizeof(PanelLds), st, fl, ws, n_pad, k + kw, nblk, n);
     if (sg_status e = check_launch("factor panel")) return e;
     k += kw;
   }
@@ -767,8 +805,11 @@ sg_status run_factor_split(float* A, float* Y, int64_t n_pad, int nblk, int64_t 
 }
 
 // ---- flip out: U[i][j] = Y[n-1-j][n-1-i] (i <= j), 0 below ------------------
-__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ Y, int64_t n,
-                                                       int64_t n_pad, float* __restrict__ U) {
+__global__ __launch_bounds__(256) void finalize_kernel(const FactorLayers fl, const float* ws, int64_t n,
+                                                       int64_t n_pad) {
+  const int L = blockIdx.z;
+  const float* __restrict__ Y = ws + L * fl.ls + n_pad * n_pad;
+  float* __restrict__ U = fl.Hinv[L];
   __shared__ float tile[64][65];
   const int64_t I0 = blockIdx.y * 64, J0 = blockIdx.x * 64;
   const int c = threadIdx.x & 63, r0 = threadIdx.x >> 6;
@@ -801,19 +842,18 @@ size_t factor_ws_bytes(int64_t n) {
   return 2 * (size_t)n_pad * n_pad * sizeof(float) + 256;
 }
 
-sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp, int32_t* info,
-                              void* ws, hipStream_t st, hipStream_t side, hipEvent_t ev_a,
-                              hipEvent_t ev_b) {
+namespace {
+
+sg_status prepare_layers(const FactorLayers& fl, int64_t n, double damp, void* ws_v, hipStream_t st,
+                         hipStream_t side, hipEvent_t ev_a, hipEvent_t ev_b) {
   const int64_t n_pad = round_up(n, NB);
   const int nblk = (int)(n_pad / NB);
-  float* A = static_cast<float*>(ws);
-  float* Y = A + n_pad * n_pad;
-  float* lam = Y + n_pad * n_pad;
+  float* ws = static_cast<float*>(ws_v);
 
-  hipLaunchKernelGGL(damp_lambda_kernel, dim3(1), dim3(1024), 0, st, H, n, damp, lam, info);
+  hipLaunchKernelGGL(damp_lambda_kernel, dim3((unsigned)fl.nl), dim3(1024), 0, st, fl, ws, n, n_pad, damp);
   if (sg_status e = check_launch("damping")) return e;
   const unsigned t64 = (unsigned)(n_pad / 64);
-  hipLaunchKernelGGL(flip_init_kernel, dim3(t64, t64), dim3(256), 0, st, H, n, n_pad, lam, A, Y);
+  hipLaunchKernelGGL(flip_init_kernel, dim3(t64, t64, (unsigned)fl.nl), dim3(256), 0, st, fl, ws, n, n_pad);
   if (sg_status e = check_launch("flip/init")) return e;
   // Up to n = 4096 the panel chain sets the time: the panel takes four
   // workgroups per block (128 of the 256 CUs) and shares one launch with the
@@ -823,20 +863,44 @@ sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double dam
   // trailing update sets the time: one panel workgroup per block, and the
   // update on its own stream at two workgroups per CU (n = 28672: 150 ms
   // against 182 ms in the shared launch).  Without a caller update stream
-  // the single-stream fused form serves every n.
+  // the single-stream fused form serves every n.  Several layers share each
+  // launch (their panels first), so the latency-bound steps of one fill the
+  // CUs the others leave idle.
   sg_status e;
   if (nblk * 8 <= kNumCU) {
-    e = run_factor_fused<32, false>(A, Y, n_pad, nblk, n, info, st);
+    e = run_factor_fused<32, false>(fl, ws, n_pad, nblk, n, st);
   } else if (side != nullptr) {
     const SideStream ss{side, ev_a, ev_b};
-    e = run_factor_split<128>(A, Y, n_pad, nblk, n, info, st, &ss);
+    e = run_factor_split<128>(fl, ws, n_pad, nblk, n, st, &ss);
   } else {
-    e = run_factor_fused<128, true>(A, Y, n_pad, nblk, n, info, st);
+    e = run_factor_fused<128, true>(fl, ws, n_pad, nblk, n, st);
   }
   if (e != SG_OK) return e;
   const unsigned tn = (unsigned)ceil_div(n, 64);
-  hipLaunchKernelGGL(finalize_kernel, dim3(tn, tn), dim3(256), 0, st, Y, n, n_pad, Hinv);
+  hipLaunchKernelGGL(finalize_kernel, dim3(tn, tn, (unsigned)fl.nl), dim3(256), 0, st, fl, ws, n, n_pad);
   return check_launch("factor finalize");
+}
+
+}  // namespace
+
+sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp, int32_t* info,
+                              void* ws, hipStream_t st, hipStream_t side, hipEvent_t ev_a,
+                              hipEvent_t ev_b) {
+  return launch_prepare_hinv_batched(&Hinv, &H, 1, n, damp, info, ws, st, side, ev_a, ev_b);
+}
+
+sg_status launch_prepare_hinv_batched(float* const* Hinv, const float* const* H, int nl, int64_t n,
+                                      double damp, int32_t* info, void* ws, hipStream_t st,
+                                      hipStream_t side, hipEvent_t ev_a, hipEvent_t ev_b) {
+  FactorLayers fl{};
+  fl.nl = nl;
+  fl.ls = (int64_t)(factor_ws_bytes(n) / sizeof(float));
+  for (int L = 0; L < nl; ++L) {
+    fl.H[L] = H[L];
+    fl.Hinv[L] = Hinv[L];
+    fl.info[L] = info + L;
+  }
+  return prepare_layers(fl, n, damp, ws, st, side, ev_a, ev_b);
 }
 
 }  // namespace sg

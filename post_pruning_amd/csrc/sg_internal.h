@@ -40,6 +40,11 @@ size_t factor_ws_bytes(int64_t n);
 sg_status launch_prepare_hinv(float* Hinv, const float* H, int64_t n, double damp,
                               int32_t* info, void* ws, hipStream_t st, hipStream_t side,
                               hipEvent_t ev_a, hipEvent_t ev_b);
+// nl layers of order n in one set of launches; layer L's part of the workspace
+// starts factor_ws_bytes(n) * L bytes in; info[L] is its status.
+sg_status launch_prepare_hinv_batched(float* const* Hinv, const float* const* H, int nl, int64_t n,
+                                      double damp, int32_t* info, void* ws, hipStream_t st,
+                                      hipStream_t side, hipEvent_t ev_a, hipEvent_t ev_b);
 
 // ---------------------------------------------------------------------------
 // Prune

@@ -284,3 +284,40 @@ def test_batched_null_factor_rejected(sg):
                                           128, 128, 128, arr, 2, hv, 0, 0.5, 0, 1, 128, None,
                                           ctypes.c_void_p(0x10000), 10 ** 9, None)
     assert st == sg.SG_ERR_INVALID_ARGUMENT and "Hinv[1]" in sg.sg_last_error_message()
+
+
+def _ptr_array(vals):
+    return ctypes.cast((ctypes.c_void_p * len(vals))(*vals), ctypes.c_void_p)
+
+
+@pytest.mark.parametrize("case", ["nl0", "nl17", "null_entry", "alias_h", "same_out", "small_ws", "events"])
+def test_prepare_hinv_batched_validation(sg, case):
+    """sg_prepare_hinv_batched rejects bad arguments before anything is enqueued."""
+    n = 256
+    per = sg.sg_workspace_bytes(sg.SG_OP_PREPARE_HINV, 0, n)
+    nl = 2
+    hin = [0x10000, 0x20000]
+    out = [0x30000, 0x40000]
+    ws_bytes = nl * per
+    upd = ev = None
+    expect = sg.SG_ERR_INVALID_ARGUMENT
+    if case == "nl0":
+        nl = 0
+    elif case == "nl17":
+        nl = 17
+        hin, out = [0x10000 + i for i in range(17)], [0x90000 + i for i in range(17)]
+    elif case == "null_entry":
+        hin = [0x10000, None]
+    elif case == "alias_h":
+        out = [0x30000, 0x10000]
+    elif case == "same_out":
+        out = [0x30000, 0x30000]
+    elif case == "small_ws":
+        ws_bytes = nl * per - 1
+        expect = sg.SG_ERR_WORKSPACE
+    elif case == "events":
+        upd = ctypes.c_void_p(0x5000)  # a stream without the two events
+    st = _lib(sg).sg_prepare_hinv_batched(_ptr_array(out), _ptr_array(hin), nl, n, 0.01,
+                                          ctypes.c_void_p(0x6000), ctypes.c_void_p(0x100000), ws_bytes,
+                                          None, upd, ev, ev)
+    assert st == expect, (case, sg.sg_last_error_message())
