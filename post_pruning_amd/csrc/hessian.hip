@@ -411,6 +411,24 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
   }
 
   // ---- epilogue -----------------------------------------------------------
+  // Row fragment a of the wave's sub-tile (16 rows x 96 columns, held as
+  // kNB float4 per lane) added into H's lower triangle, and mirrored (tiles
+  // that cross the diagonal hold upper entries too, which the mirror of the
+  // lower ones writes).
+  auto store_frag = [&](int a, const floatx4 (&v4)[kNB]) {
+#pragma unroll
+    for (int c = 0; c < kNB; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = i0 + wi * 128 + a * 16 + (lane >> 4) * 4 + v;
+        const int col2 = j0 + wj * 96 + c * 16 + (lane & 15);
+        if (row >= n || col2 >= n || row < col2) continue;
+        const size_t lo = (size_t)row * n + col2;
+        const float val = H[lo] + v4[c][v];
+        H[lo] = val;
+        if (row != col2) H[(size_t)col2 * n + row] = val;
+      }
+  };
   // Token splits: each split writes its partial tile (per (wave, a, c) slot,
   // 64 lanes x float4); the last split to arrive sums every partial in split
   // order (its own re-read too, so the result does not depend on which split
@@ -432,37 +450,39 @@ __global__ __launch_bounds__(HTHREADS) void hess_bf16_dma_kernel(
     __syncthreads();
     if (!*s_last) return;
     __threadfence();
-    for (int sp = 0; sp < splits; ++sp) {
-      const floatx4* other =
-          reinterpret_cast<const floatx4*>(part + ((size_t)sp * tiles + ti) * (HTI * HTJ));
+    // The register tile is not needed any more (this split's partial is read
+    // back like the others), so the registers hold loads instead: for each
+    // row fragment, the slots of up to eight splits are requested together
+    // (a serial sum with few loads in flight was bound by their latency).
+    constexpr int SG = 8;
+    const floatx4* const base = reinterpret_cast<const floatx4*>(part + (size_t)ti * (HTI * HTJ));
+    const size_t sstride = (size_t)tiles * (HTI * HTJ / 4);  // float4 between splits of a tile
+    for (int a = 0; a < 8; ++a) {
+      floatx4 sum[kNB];
+      const floatx4* slot = base + (size_t)(wave * 8 * kNB + a * kNB) * 64 + lane;
+      for (int sp0 = 0; sp0 < splits; sp0 += SG) {
+        floatx4 pv[SG][kNB];
 #pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        floatx4 pv[kNB];
+        for (int q = 0; q < SG; ++q)
+          if (sp0 + q < splits) {
 #pragma unroll
-        for (int c = 0; c < kNB; ++c) pv[c] = other[(wave * 8 * kNB + a * kNB + c) * 64 + lane];
+            for (int c = 0; c < kNB; ++c) pv[q][c] = slot[(size_t)(sp0 + q) * sstride + c * 64];
+          }
 #pragma unroll
-        for (int c = 0; c < kNB; ++c) acc[a][c] = (sp == 0) ? pv[c] : acc[a][c] + pv[c];
+        for (int q = 0; q < SG; ++q)
+          if (sp0 + q < splits) {
+#pragma unroll
+            for (int c = 0; c < kNB; ++c) sum[c] = (sp0 + q == 0) ? pv[q][c] : sum[c] + pv[q][c];
+          }
       }
+      store_frag(a, sum);
     }
     if (tid == 0) counters[ti] = 0u;
+    return;
   }
 
-  // lower triangle only (tiles that cross the diagonal hold upper entries
-  // too, which the mirror of the lower ones writes)
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int c = 0; c < kNB; ++c)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = i0 + wi * 128 + a * 16 + (lane >> 4) * 4 + v;
-        const int col2 = j0 + wj * 96 + c * 16 + (lane & 15);
-        if (row >= n || col2 >= n || row < col2) continue;
-        const size_t lo = (size_t)row * n + col2;
-        const float val = H[lo] + acc[a][c][v];
-        H[lo] = val;
-        if (row != col2) H[(size_t)col2 * n + row] = val;
-      }
+  for (int a = 0; a < 8; ++a) store_frag(a, acc[a]);
 }
 
 // fp32 inputs: 64x64 lower-triangle tiles on v_mfma_f32_16x16x4_f32.  A
