@@ -58,6 +58,7 @@ def _bits_equal(a, b):
     (4096, 16384, 2, "auto"),     # the attention layers' order
     (4224, 8192, 2, "auto"),      # caller update stream
     (4224, 8192, 3, None),        # grouped panels on one stream
+    (256, 1024, 16, "auto"),      # the most layers one call takes
 ])
 def test_batched_factor_equals_single_calls(sg, n, T, count, route):
     Hs = _hessians(sg, n, T, count, 7000 + n)
