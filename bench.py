@@ -6,7 +6,8 @@ factor (H + lambda I)^{-1} -> U, prune W (mask selection, OBS compensation,
 lazy updates).  Default workload: the 8192 x 28672 down-projection layer
 (bf16 W and X, 524,288 calibration tokens, 50% unstructured, block 128), the
 largest of the layer shapes; the 4096- and 11008-wide layers are timed in the
-same run after it (key "configs").
+same run after it (key "configs"), and four 4096 x 4096 layers with their own
+inputs, factored and pruned together and one after another (key "layers").
 
 Prints ONE JSON line.  ``value`` is the per-layer wall time in seconds (lower
 is better).  Along with it: per-phase times, algorithmic TFLOP/s, each
@@ -678,6 +679,19 @@ def main():
             torch.cuda.empty_cache()
         keepX = None
         cache.clear()
+        # several layers with their own inputs (4 x attn_4096): one batched
+        # factor and one batched prune against one layer after another
+        la = argparse.Namespace(**{**vars(args), "steps": 3, "warmup": 1, "pattern": None})
+        lres, lbase, lpat = bench_layers(sg, 4, la, dev)
+        layers = {
+            "workload": f"4 x attn_4096 layers with their own inputs, pattern {lpat}, blocksize {lbase.blocksize}",
+            "sequential_layers_per_s": 4 / (lres["sequential"] * 1e-3),
+            "batched_prune_layers_per_s": 4 / (lres["batched"] * 1e-3),
+            "batched_factor_and_prune_layers_per_s": 4 / (lres["batched_factor"] * 1e-3),
+            "factors_ms": {"batched": lres["factors_batched_ms"], "one_by_one": lres["factors_sequential_ms"]},
+            "prune_ms": {"batched": lres["batched_prune_ms"], "one_by_one": lres["sequential_prune_ms"]},
+        }
+        torch.cuda.empty_cache()
 
     line = {
         "metric": METRIC,
@@ -726,6 +740,7 @@ def main():
                                      sorted(attr_factor.items(), key=lambda kv: -kv[1][1])[:6]}
     if extra:
         line["configs"] = extra
+        line["layers"] = layers
     if export is not None:
         line["two_four_export"] = export
     if args.shared > 1:
